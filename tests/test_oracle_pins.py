@@ -1,0 +1,484 @@
+"""Pins of the CPU oracle against facts other than itself.
+
+Each test checks one oracle function against a closed form, a published
+known-answer vector, a library routine (torch / numpy / scipy) on a small
+case, a hand-worked example from the pages, or an invariant the method
+implies.  These run on the CPU only.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.stats
+import torch
+import torch.nn.functional as Fn
+
+import oracle
+from uniform_state_discrete_dg_amd import workloads as W
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- Philox ----
+def test_philox_known_answer_vectors():
+    kat = json.load(open(os.path.join(GOLD, "philox4x32_10_kat.json")))
+    for v in kat["vectors"]:
+        ctr = [int(x, 16) for x in v["ctr"]]
+        key = [int(x, 16) for x in v["key"]]
+        out = oracle.philox4x32_10(ctr, key)
+        assert [int(x) for x in out] == [int(x, 16) for x in v["out"]]
+
+
+def test_uniform_token_is_top_bits_of_word0():
+    seed = 0x123456789ABCDEF0
+    for V in (2, 512, 32768, 262144):
+        b = int(math.log2(V))
+        for pos, step, cid, stream in [(0, 0, 0, 0), (5, 3, 2, 1), (255, 63, 7, 1)]:
+            w = oracle.philox4x32_10([pos, step, cid, stream],
+                                     [seed & 0xFFFFFFFF, seed >> 32])
+            assert oracle.uniform_token(seed, pos, step, cid, stream, V) == int(w[0]) >> (32 - b)
+
+
+def test_canvas_init_uses_stream0_step0():
+    N, V, seed, cid = 64, 32768, 7, 3
+    c = oracle.canvas_init(seed, cid, N, V)
+    assert c.dtype == np.int32 and c.shape == (N,)
+    for i in range(N):
+        assert c[i] == oracle.uniform_token(seed, i, 0, cid, 0, V)
+    assert (c >= 0).all() and (c < V).all()
+    # a different canvas id gives an independent stream
+    assert (oracle.canvas_init(seed, cid + 1, N, V) != c).mean() > 0.9
+
+
+def test_uniform_token_chi_square():
+    """Re-noise tokens are uniform over [0, V): chi-square over 64 bins."""
+    V, n = 262144, 1 << 16
+    toks = np.array([oracle.uniform_token(42, i % 256, i // 256, 1, 1, V) for i in range(n)])
+    assert toks.min() >= 0 and toks.max() < V
+    counts = np.bincount(toks * 64 // V, minlength=64)
+    stat, p = scipy.stats.chisquare(counts)
+    assert p > 1e-4, (stat, p)
+
+
+# ---------------------------------------------------------- small blocks ----
+def test_gelu_matches_torch_exact_gelu():
+    xs = np.linspace(-8, 8, 257)
+    ref = Fn.gelu(torch.tensor(xs, dtype=torch.float64), approximate="none").numpy()
+    got = np.array([oracle.gelu(x) for x in xs])
+    np.testing.assert_allclose(got, ref, rtol=1e-14, atol=1e-15)
+    assert oracle.gelu(0.0) == 0.0
+    # gelu(x) - gelu(-x) = x
+    for x in (0.3, 1.7, 4.2):
+        assert abs(oracle.gelu(x) - oracle.gelu(-x) - x) < 1e-14
+
+
+def test_rmsnorm_matches_torch_and_closed_form():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(96)
+    g = rng.standard_normal(96).astype(np.float32)
+    eps = 1e-6
+    ref = Fn.rms_norm(torch.tensor(x), (96,), weight=torch.tensor(g, dtype=torch.float64),
+                      eps=eps).numpy()
+    np.testing.assert_allclose(oracle.rmsnorm(x, g, eps), ref, rtol=1e-13)
+    # constant vector c*1 with unit gain: c / sqrt(c^2 + eps)
+    c = 2.5
+    out = oracle.rmsnorm(np.full(64, c), np.ones(64, np.float32), eps)
+    np.testing.assert_allclose(out, c / math.sqrt(c * c + eps), rtol=1e-15)
+
+
+def test_matmul_nt_matches_numpy():
+    rng = np.random.default_rng(1)
+    a = rng.standard_normal((7, 33))
+    b = rng.standard_normal((19, 33)).astype(np.float32)
+    np.testing.assert_allclose(oracle.matmul_nt(a, b), a @ b.astype(np.float64).T, rtol=1e-12,
+                               atol=1e-12)
+
+
+@pytest.mark.parametrize("V", [512, 32768, 262144])
+def test_entropy_uniform_is_lnV(V):
+    p, H = oracle.softmax_entropy(np.full(V, 0.37))
+    assert abs(H - math.log(V)) < 1e-9
+    assert abs(p.sum() - 1.0) < 1e-12
+
+
+def test_entropy_one_hot_is_zero_and_two_way_tie_is_ln2():
+    y = np.zeros(1000)
+    y[17] = 800.0  # exp(-800) underflows to 0 in double
+    p, H = oracle.softmax_entropy(y)
+    assert H == 0.0 and p[17] == 1.0
+    y = np.full(1000, -900.0)
+    y[3] = y[500] = 1.0
+    p, H = oracle.softmax_entropy(y)
+    assert abs(H - math.log(2.0)) < 1e-15
+    assert p[3] == p[500] == 0.5
+
+
+def test_entropy_matches_library_routines():
+    rng = np.random.default_rng(2)
+    for V, s in [(5, 1.0), (64, 3.0), (4096, 0.7)]:
+        y = rng.standard_normal(V) * s
+        p, H = oracle.softmax_entropy(y)
+        ref_H = torch.distributions.Categorical(logits=torch.tensor(y)).entropy().item()
+        assert abs(H - ref_H) < 1e-12
+        np.testing.assert_allclose(p, torch.softmax(torch.tensor(y), 0).numpy(), rtol=1e-12)
+        assert abs(H - scipy.stats.entropy(p)) < 1e-12
+
+
+def test_argmax_lowest_index_on_ties():
+    z = np.array([1.0, 3.0, -2.0, 3.0, 3.0])
+    assert oracle.argmax(z) == 1
+    assert oracle.argmax(z.astype(np.float32)) == 1
+    assert oracle.argmax(np.array([-1.0, -1.0])) == 0
+
+
+# ------------------------------------------------------------- attention ----
+def _sdpa_ref(q, k, v, Hq, Hkv, causal_offset=None):
+    """torch scaled_dot_product_attention in float64 with KV heads repeated."""
+    nq, nk, hd = q.shape[0], k.shape[1], k.shape[2]
+    Q = torch.tensor(q).view(nq, Hq, hd).transpose(0, 1)           # [Hq][nq][hd]
+    K = torch.tensor(k).repeat_interleave(Hq // Hkv, dim=0)          # [Hq][nk][hd]
+    Vt = torch.tensor(v).repeat_interleave(Hq // Hkv, dim=0)
+    mask = None
+    if causal_offset is not None:
+        i = torch.arange(nq)[:, None]
+        j = torch.arange(nk)[None, :]
+        mask = j <= (i + causal_offset)
+    o = Fn.scaled_dot_product_attention(Q, K, Vt, attn_mask=mask)
+    return o.transpose(0, 1).reshape(nq, Hq * hd).numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (8, 1)])
+def test_attention_matches_sdpa(Hq, Hkv):
+    rng = np.random.default_rng(3)
+    nq, nk, hd = 5, 11, 16
+    q = rng.standard_normal((nq, Hq * hd))
+    k = rng.standard_normal((Hkv, nk, hd))
+    v = rng.standard_normal((Hkv, nk, hd))
+    np.testing.assert_allclose(oracle.attention(q, k, v, Hq, Hkv), _sdpa_ref(q, k, v, Hq, Hkv),
+                               rtol=1e-12, atol=1e-12)
+    got = oracle.attention(q, k, v, Hq, Hkv, causal=True, q_pos0=nk - nq)
+    np.testing.assert_allclose(got, _sdpa_ref(q, k, v, Hq, Hkv, causal_offset=nk - nq),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(4)
+    Hq = Hkv = 2
+    hd = 8
+    q = rng.standard_normal((3, Hq * hd))
+    # one key: output is its value
+    k1 = rng.standard_normal((Hkv, 1, hd))
+    v1 = rng.standard_normal((Hkv, 1, hd))
+    o = oracle.attention(q, k1, v1, Hq, Hkv)
+    for h in range(Hq):
+        np.testing.assert_allclose(o[:, h * hd:(h + 1) * hd], np.broadcast_to(v1[h, 0], (3, hd)),
+                                   rtol=1e-14)
+    # identical keys: output is the mean of the values
+    kk = np.broadcast_to(rng.standard_normal((Hkv, 1, hd)), (Hkv, 6, hd)).copy()
+    vv = rng.standard_normal((Hkv, 6, hd))
+    o = oracle.attention(q, kk, vv, Hq, Hkv)
+    for h in range(Hq):
+        np.testing.assert_allclose(o[:, h * hd:(h + 1) * hd],
+                                   np.broadcast_to(vv[h].mean(0), (3, hd)), rtol=1e-12)
+    # GQA with every query head of a group equal to MHA on repeated KV heads
+    k = rng.standard_normal((1, 6, hd))
+    v = rng.standard_normal((1, 6, hd))
+    o_gqa = oracle.attention(q, k, v, Hq, 1)
+    o_mha = oracle.attention(q, np.repeat(k, Hq, 0), np.repeat(v, Hq, 0), Hq, Hq)
+    np.testing.assert_array_equal(o_gqa, o_mha)
+
+
+# ------------------------------------------------------------- selection ----
+def _run_select(H, gamma, rule, N=None, V=1024, seed=9, cid=0, step=0, tokens_in=None,
+                argmax_tokens=None, stable_in=0):
+    H = np.asarray(H, dtype=np.float32)
+    N = H.shape[0]
+    am = np.arange(N, dtype=np.int32) + 100 if argmax_tokens is None else argmax_tokens
+    tin = np.zeros(N, np.int32) if tokens_in is None else tokens_in
+    return oracle.select(H, am, tin, V, gamma, rule, seed, cid, step, stable_in)
+
+
+def test_select_hand_worked_cases():
+    gold = json.load(open(os.path.join(GOLD, "select_cases.json")))
+    for case in gold["cases"]:
+        H = [float("nan") if h == "nan" else h for h in case["H"]]
+        for rule, name in [(oracle.ACCEPT_SUM_MINUS_MAX, "sum_minus_max"),
+                           (oracle.ACCEPT_CUMSUM, "cumsum")]:
+            acc, _, fl = _run_select(H, case["gamma"], rule)
+            assert acc.tolist() == case[name], (case, name)
+            assert fl["accepted"] == sum(case[name])
+
+
+def _brute_force_accept(H, gamma, rule):
+    """Largest admissible prefix of the (H, index) order, each prefix checked on
+    its own with exact rational arithmetic (no fixed point, no early exit)."""
+    N = len(H)
+    Hc = [0.0 if not (h > 0) and not math.isnan(h) else float(np.float32(h)) for h in H]
+    order = sorted(range(N), key=lambda i: (math.isnan(Hc[i]), Hc[i], i))
+    best = 0
+    for k in range(N + 1):
+        pre = [Hc[i] for i in order[:k]]
+        if any(math.isnan(h) for h in pre):
+            continue
+        s = sum(Fraction(h) for h in pre)
+        val = s - (max(Fraction(h) for h in pre) if pre else 0) if rule == 0 else s
+        if val <= Fraction(gamma):
+            best = k
+    acc = np.zeros(N, np.uint8)
+    acc[order[:best]] = 1
+    return acc
+
+
+def test_select_brute_force_small_N():
+    rng = np.random.default_rng(5)
+    for trial in range(300):
+        N = int(rng.integers(1, 13))
+        H = (rng.random(N) * 3).astype(np.float32)
+        if trial % 7 == 0:
+            H[rng.integers(N)] = H[0]  # ties
+        gamma = float(rng.random() * 6)
+        for rule in (0, 1):
+            acc, _, _ = _run_select(H, gamma, rule)
+            ref = _brute_force_accept(H.tolist(), gamma, rule)
+            # fixed point may only differ from exact reals within N * 2^-32 of gamma
+            if not np.array_equal(acc, ref):
+                s = np.sort(H.astype(np.float64))
+                sums = np.concatenate([[0.0], np.cumsum(s)])
+                assert np.min(np.abs(sums - gamma)) < N * 2.0 ** -32
+            # invariants: prefix of the order, bound, maximality, >=1 for rule 0
+            order = sorted(range(N), key=lambda i: (float(H[i]), i))
+            k = int(acc.sum())
+            assert acc[order[:k]].all() and not acc[order[k:]].any()
+            if rule == 0:
+                assert k >= 1
+
+
+def test_select_exhaustive_over_all_subsets_tiny():
+    """For N <= 6, among ALL subsets that satisfy the bound and are closed under
+    'lower (H, index) first', the oracle returns the largest one."""
+    rng = np.random.default_rng(6)
+    for _ in range(60):
+        N = int(rng.integers(1, 7))
+        H = (np.floor(rng.random(N) * 8) / 4).astype(np.float32)  # dyadic, many ties
+        gamma = float(np.floor(rng.random() * 12) / 4)
+        key = {i: (float(H[i]), i) for i in range(N)}
+        for rule in (0, 1):
+            best = ()
+            for r in range(N + 1):
+                for sub in itertools.combinations(range(N), r):
+                    closed = all(key[j] > key[i] or j in sub for i in sub for j in range(N)
+                                 if key[j] < key[i])
+                    if not closed:
+                        continue
+                    hs = [float(H[i]) for i in sub]
+                    val = (sum(hs) - (max(hs) if hs else 0)) if rule == 0 else sum(hs)
+                    if val <= gamma and len(sub) > len(best):
+                        best = sub
+            acc, _, _ = _run_select(H, gamma, rule)
+            assert sorted(np.nonzero(acc)[0].tolist()) == sorted(best)
+
+
+def test_select_renoise_and_flags():
+    N, V, seed, cid, step = 12, 4096, 77, 5, 9
+    rng = np.random.default_rng(7)
+    H = (rng.random(N) * 2 + 1).astype(np.float32)
+    am = rng.integers(0, V, N).astype(np.int32)
+    tin = rng.integers(0, V, N).astype(np.int32)
+    acc, tout, fl = oracle.select(H, am, tin, V, 3.0, 0, seed, cid, step, 4)
+    for i in range(N):
+        if acc[i]:
+            assert tout[i] == am[i]
+        else:
+            assert tout[i] == oracle.uniform_token(seed, i, step, cid, 1, V)
+    assert fl["changed"] == 1 and fl["stable"] == 0 and fl["allconf"] == 0
+    # every position accepted with argmax == canvas: unchanged, stable counter grows
+    acc, tout, fl = oracle.select(np.zeros(N, np.float32), am, am, V, 1.0, 0, seed, cid, step, 4)
+    assert acc.all() and (tout == am).all()
+    assert fl == dict(allconf=1, changed=0, stable=5, accepted=N)
+    # confidence is strict: H == eps is not confident; NaN is never confident
+    Hc = np.full(N, 0.004, np.float32)
+    Hc[0] = np.float32(0.005)
+    _, _, fl = oracle.select(Hc, am, am, V, 1.0, 0, seed, cid, step, 0, conf_eps=float(np.float32(0.005)))
+    assert fl["allconf"] == 0
+    Hc[0] = np.nan
+    _, _, fl = oracle.select(Hc, am, am, V, 1.0, 0, seed, cid, step, 0)
+    assert fl["allconf"] == 0
+
+
+def test_select_permutation_equivariant():
+    rng = np.random.default_rng(8)
+    N = 40
+    H = (rng.random(N) * 4).astype(np.float32)
+    perm = rng.permutation(N)
+    a1, _, _ = _run_select(H, 9.0, 0)
+    a2, _, _ = _run_select(H[perm], 9.0, 0)
+    np.testing.assert_array_equal(a1[perm], a2)
+
+
+def test_should_stop():
+    assert oracle.should_stop(dict(allconf=1, changed=1, stable=0), 3)
+    assert not oracle.should_stop(dict(allconf=0, changed=0, stable=2), 3)
+    assert oracle.should_stop(dict(allconf=0, changed=0, stable=3), 3)
+    assert not oracle.should_stop(dict(allconf=0, changed=0, stable=99), 0)
+
+
+# ------------------------------------------------------------- schedule ----
+def test_temperature_schedules():
+    for kind in ("linear", "cosine"):
+        assert oracle.temperature(kind, 1.5, 0.3, 0, 32) == pytest.approx(1.5, abs=1e-15)
+        assert oracle.temperature(kind, 1.5, 0.3, 31, 32) == pytest.approx(0.3, abs=1e-15)
+        assert oracle.temperature(kind, 1.5, 0.3, 8, 17) == pytest.approx(0.9, abs=1e-15)
+        ts = [oracle.temperature(kind, 1.5, 0.3, s, 32) for s in range(32)]
+        assert all(a > b for a, b in zip(ts, ts[1:]))
+    assert oracle.temperature("cosine", 1.5, 0.3, 0, 1) == 1.5
+    assert oracle.temperature("const", 1.0, 1.0, 3, 4) == 1.0
+    # cosine at a quarter: T1 + (T0-T1)(1+cos(pi/4))/2
+    assert oracle.temperature("cosine", 2.0, 0.0, 1, 5) == pytest.approx(1 + math.cos(math.pi / 4))
+
+
+# ------------------------------------------------------- self-conditioning ----
+def _small_model(N=6, V=64, d=16, Hq=4, Hkv=2, hd=8, F=24, seed=11, L=5, dtype="f32"):
+    cfg = dict(N=N, V=V, d=d, Hq=Hq, Hkv=Hkv, hd=hd, F=F, L=L, dtype=dtype, prompt=0)
+    inp = W.make_inputs(cfg, seed)
+    return cfg, inp, oracle.model_from_inputs(inp)
+
+
+def test_selfcond_one_hot_gathers_row_and_is_linear():
+    cfg, inp, m = _small_model()
+    E = inp["E"].numpy().astype(np.float64)
+    for t in (0, 17, 63):
+        p = np.zeros(cfg["V"])
+        p[t] = 1.0
+        np.testing.assert_array_equal(m.selfcond_row(p), E[t])
+    p = np.full(cfg["V"], 1.0 / cfg["V"])
+    np.testing.assert_allclose(m.selfcond_row(p), E.mean(0), rtol=1e-12, atol=1e-15)
+    rng = np.random.default_rng(9)
+    p1, p2 = rng.random(cfg["V"]), rng.random(cfg["V"])
+    np.testing.assert_allclose(m.selfcond_row(p1 + 2 * p2),
+                               m.selfcond_row(p1) + 2 * m.selfcond_row(p2), rtol=1e-12)
+
+
+# -------------------------------------------------------- whole forward ----
+def _torch_forward(inp, tokens, p_prev, kp, vp, T):
+    """The denoising forward composed from torch library routines in float64."""
+    c = inp["cfg"]
+    f = lambda x: x.double()
+    E = f(inp["E"])
+    h0 = E[torch.tensor(tokens, dtype=torch.long)]
+    if p_prev is not None:
+        a = torch.tensor(p_prev) @ E
+        h0 = h0 + Fn.linear(Fn.gelu(Fn.linear(a, f(inp["w1"]))), f(inp["w2"]))
+    n = Fn.rms_norm(h0, (c["d"],), weight=f(inp["g_attn"]), eps=1e-6)
+    q = Fn.linear(n, f(inp["wq"]))
+    k = Fn.linear(n, f(inp["wk"]))
+    v = Fn.linear(n, f(inp["wv"]))
+    N, Hq, Hkv, hd = c["N"], c["Hq"], c["Hkv"], c["hd"]
+    K = torch.cat([torch.tensor(kp), k.view(N, Hkv, hd).transpose(0, 1)], 1)
+    Vt = torch.cat([torch.tensor(vp), v.view(N, Hkv, hd).transpose(0, 1)], 1)
+    o = Fn.scaled_dot_product_attention(q.view(N, Hq, hd).transpose(0, 1),
+                                        K.repeat_interleave(Hq // Hkv, 0),
+                                        Vt.repeat_interleave(Hq // Hkv, 0))
+    o = o.transpose(0, 1).reshape(N, Hq * hd)
+    h1 = h0 + Fn.linear(o, f(inp["wo"]))
+    z = Fn.linear(Fn.rms_norm(h1, (c["d"],), weight=f(inp["g_final"]), eps=1e-6), E)
+    dist = torch.distributions.Categorical(logits=z / T)
+    return dict(h0=h0, attn=o, h1=h1, logits=z, probs=dist.probs, entropy=dist.entropy())
+
+
+@pytest.mark.parametrize("with_prev", [False, True])
+def test_forward_matches_torch_composition(with_prev):
+    cfg, inp, m = _small_model()
+    rng = np.random.default_rng(10)
+    tokens = rng.integers(0, cfg["V"], cfg["N"]).astype(np.int32)
+    kp = inp["k_prefix"].double().numpy()
+    vp = inp["v_prefix"].double().numpy()
+    p_prev = None
+    if with_prev:
+        p_prev = rng.random((cfg["N"], cfg["V"]))
+        p_prev /= p_prev.sum(1, keepdims=True)
+    T = 0.7
+    got = m.denoise_forward(tokens, p_prev, kp, vp, cfg["L"], T)
+    ref = _torch_forward(inp, tokens, p_prev, kp, vp, T)
+    for k in ("h0", "attn", "h1", "logits", "probs", "entropy"):
+        np.testing.assert_allclose(got[k], ref[k].numpy(), rtol=1e-10, atol=1e-12, err_msg=k)
+    np.testing.assert_array_equal(got["argmax"], ref["logits"].argmax(1).numpy())
+
+
+def test_forward_is_permutation_equivariant_and_leaves_cache():
+    """No positional signal and no mask inside the canvas: permuting the canvas
+    permutes every per-position output (a causal mask would break this)."""
+    cfg, inp, m = _small_model(N=9)
+    rng = np.random.default_rng(11)
+    tokens = rng.integers(0, cfg["V"], cfg["N"]).astype(np.int32)
+    kp = inp["k_prefix"].double().numpy().copy()
+    vp = inp["v_prefix"].double().numpy().copy()
+    kp0, vp0 = kp.copy(), vp.copy()
+    perm = rng.permutation(cfg["N"])
+    a = m.denoise_forward(tokens, None, kp, vp, cfg["L"], 1.0)
+    b = m.denoise_forward(tokens[perm], None, kp, vp, cfg["L"], 1.0)
+    for k in ("h1", "logits", "entropy", "argmax"):
+        np.testing.assert_allclose(a[k][perm], b[k], rtol=1e-12, atol=1e-13, err_msg=k)
+    np.testing.assert_array_equal(kp, kp0)
+    np.testing.assert_array_equal(vp, vp0)
+
+
+def test_forward_row_selection_matches_full():
+    cfg, inp, m = _small_model(N=8)
+    rng = np.random.default_rng(12)
+    tokens = rng.integers(0, cfg["V"], cfg["N"]).astype(np.int32)
+    kp = inp["k_prefix"].double().numpy()
+    vp = inp["v_prefix"].double().numpy()
+    full = m.denoise_forward(tokens, None, kp, vp, cfg["L"], 0.9)
+    sel = np.zeros(cfg["N"], np.uint8)
+    sel[[1, 6]] = 1
+    part = m.denoise_forward(tokens, None, kp, vp, cfg["L"], 0.9, row_sel=sel)
+    for k in ("attn", "h1", "logits", "entropy", "argmax"):
+        np.testing.assert_array_equal(part[k][[1, 6]], full[k][[1, 6]])
+
+
+def test_high_temperature_entropy_tends_to_lnV():
+    cfg, inp, m = _small_model()
+    tokens = np.arange(cfg["N"], dtype=np.int32)
+    kp = inp["k_prefix"].double().numpy()
+    vp = inp["v_prefix"].double().numpy()
+    out = m.denoise_forward(tokens, None, kp, vp, cfg["L"], 1e6)
+    np.testing.assert_allclose(out["entropy"], math.log(cfg["V"]), atol=1e-9)
+
+
+# --------------------------------------------------------------- prefill ----
+def test_prefill_incremental_equals_one_shot_and_is_causal():
+    cfg, inp, m = _small_model(N=4, L=0)
+    Hkv, hd, d, Hq = cfg["Hkv"], cfg["hd"], cfg["d"], cfg["Hq"]
+    cap = 20
+    rng = np.random.default_rng(13)
+    toks = rng.integers(0, cfg["V"], 14).astype(np.int32)
+    k1, v1 = np.zeros((Hkv, cap, hd)), np.zeros((Hkv, cap, hd))
+    a1 = m.prefill_append(toks, k1, v1, 0)
+    k2, v2 = np.zeros((Hkv, cap, hd)), np.zeros((Hkv, cap, hd))
+    a2a = m.prefill_append(toks[:9], k2, v2, 0)
+    a2b = m.prefill_append(toks[9:], k2, v2, 9)
+    np.testing.assert_array_equal(k1, k2)
+    np.testing.assert_array_equal(v1, v2)
+    np.testing.assert_allclose(np.concatenate([a2a, a2b]), a1, rtol=1e-12, atol=1e-14)
+    # causality: changing the last token does not change earlier outputs
+    toks2 = toks.copy()
+    toks2[-1] = (toks2[-1] + 1) % cfg["V"]
+    k3, v3 = np.zeros((Hkv, cap, hd)), np.zeros((Hkv, cap, hd))
+    a3 = m.prefill_append(toks2, k3, v3, 0)
+    np.testing.assert_array_equal(a3[:-1], a1[:-1])
+    assert not np.allclose(a3[-1], a1[-1])
+    # appended K/V = projections of RMSNorm(E[t]) (torch library routines)
+    E = inp["E"].double()
+    n = Fn.rms_norm(E[torch.tensor(toks, dtype=torch.long)], (d,),
+                    weight=inp["g_attn"].double(), eps=1e-6)
+    kref = Fn.linear(n, inp["wk"].double()).view(14, Hkv, hd).transpose(0, 1).numpy()
+    np.testing.assert_allclose(k1[:, :14], kref, rtol=1e-12, atol=1e-13)
+    q = Fn.linear(n, inp["wq"].double()).numpy()
+    ref = _sdpa_ref(q, k1[:, :14], v1[:, :14], Hq, Hkv, causal_offset=0)
+    np.testing.assert_allclose(a1, ref, rtol=1e-11, atol=1e-12)
+    # positions beyond the append are untouched
+    assert not k1[:, 14:].any()
