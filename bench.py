@@ -1,0 +1,167 @@
+#!/usr/bin/env python3
+"""Benchmark of the uniform-state denoising step on one MI355X.
+
+A step is one dg_denoise_step over one 256-token canvas (embedding +
+self-conditioning, bidirectional attention over the 2048-token prefix and
+the canvas, tied LM head with the softmax/entropy epilogue, entropy-bounded
+accept and re-noise, stop flags) followed by the host's dg_should_stop
+check, exactly the loop a generator runs.  Inputs are seeded synthetic
+weights already resident in HBM before the timed region.
+
+Prints one JSON line.  --gpus above 1 is rejected: this build measures one
+GPU's share (the sharded design is described in the documentation).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E
+
+
+def step_flops(c: dict, selfcond: bool = True) -> float:
+    """Algorithmic matmul flops of one step (2 flops per multiply-add)."""
+    N, V, d, F, Hq, Hkv, hd = c["N"], c["V"], c["d"], c["F"], c["Hq"], c["Hkv"], c["hd"]
+    nk = c["L"] + N
+    f = 2 * N * V * d                          # tied LM head
+    f += 2 * N * d * (Hq + 2 * Hkv) * hd       # Q, K, V
+    f += 2 * 2 * N * Hq * hd * nk              # attention scores + values
+    f += 2 * N * Hq * hd * d                   # output projection
+    if selfcond:
+        f += 2 * N * V * d                     # p_prev E
+        f += 2 * 2 * N * d * F                 # self-conditioning FFN
+    return float(f)
+
+
+def lm_head_bytes(c: dict) -> float:
+    """Algorithmic HBM bytes of one LM-head launch: E once (bf16), the
+    normalised hidden rows, the bf16 probability numerators written once and
+    the per-(row, 256-column tile) statistics."""
+    N, V, d = c["N"], c["V"], c["d"]
+    return float(V * d * 2 + N * d * 2 + N * V * 2 + N * (V // 256) * 16)
+
+
+def selfcond_bytes(c: dict) -> float:
+    N, V, d = c["N"], c["V"], c["d"]
+    return float(V * d * 2 + N * V * 2 + N * (V // 256) * 4)
+
+
+def cpu_baseline(c: dict, inp: dict, rows=(2, 6)) -> dict:
+    """The oracle timed on a bounded sample: one step at rows[0] and rows[1]
+    evaluated canvas rows (embedding and canvas K/V always use every row),
+    plus self-conditioning rows, extrapolated linearly to all rows."""
+    import numpy as np
+
+    import oracle
+    om = oracle.model_from_inputs(inp)
+    kp = inp["k_prefix"].double().numpy()
+    vp = inp["v_prefix"].double().numpy()
+    N, V = c["N"], c["V"]
+    tok = oracle.canvas_init(1, 0, N, V)
+    times = []
+    for r in rows:
+        sel = np.zeros(N, np.uint8)
+        sel[:r] = 1
+        t0 = time.perf_counter()
+        om.denoise_forward(tok, None, kp, vp, c["L"], 1.0, row_sel=sel, want_logits=False,
+                           want_probs=False)
+        times.append(time.perf_counter() - t0)
+    per_row = (times[1] - times[0]) / (rows[1] - rows[0])
+    fixed = max(times[0] - per_row * rows[0], 0.0)
+    p = np.full(V, 1.0 / V)
+    t0 = time.perf_counter()
+    for _ in range(2):
+        om.selfcond_row(p)
+    sc_row = (time.perf_counter() - t0) / 2
+    t_step = fixed + N * (per_row + sc_row)
+    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": (f"{c['name']}: oracle step with {rows[0]} and {rows[1]} of {N} rows through "
+                       f"attention/LM head plus 2 self-conditioning rows, extrapolated linearly to "
+                       f"{N} rows (s/step = {t_step:.2f})")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload table entry (3: N256 V262144)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        return 2
+
+    import torch
+
+    from uniform_state_discrete_dg_amd import binding as B
+    from uniform_state_discrete_dg_amd import driver as D
+    from uniform_state_discrete_dg_amd import workloads as W
+
+    c = W.config(args.config)
+    inp = W.make_inputs(c)
+    den = D.Denoiser(c, inp)
+    seed = W.canvas_seed(args.config)
+    torch.cuda.synchronize()
+
+    def run(nsteps: int, canvas_id: int):
+        den.init_canvas(seed, canvas_id)
+        for s in range(nsteps):
+            den.step(D.temperature(c["sched"], c["T0"], c["T1"], s % c["steps"], c["steps"]),
+                     c["gamma"])
+            stop, _ = den.should_stop(c["stable_n"])
+            if stop:  # never with random weights; restart so every step is full work
+                den.init_canvas(seed, canvas_id + 1000 + s)
+
+    run(args.warmup, 0)
+    torch.cuda.synchronize()
+    B.dg_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(args.steps, 1)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    B.dg_profile_enable(False)
+    lm_ms, lm_n, sc_ms, sc_n = B.dg_profile_read()
+
+    steps_per_s = args.steps / dt
+    # every timed step but the first of the canvas uses self-conditioning
+    flops = step_flops(c, True) * (args.steps - 1) + step_flops(c, False)
+    lm_avg_s = lm_ms / 1e3 / max(lm_n, 1)
+    lm_gbs = lm_head_bytes(c) / lm_avg_s / 1e9
+    sc_avg_s = sc_ms / 1e3 / max(sc_n, 1)
+    out = {
+        "metric": "denoise steps/s", "value": steps_per_s, "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random-init one-layer denoiser, random prefix K/V)",
+        "config": {"workload": f"denoise step, {c['name']}", "canvas_tokens": c["N"],
+                   "vocab": c["V"], "d_model": c["d"], "q_heads": c["Hq"], "kv_heads": c["Hkv"],
+                   "head_dim": c["hd"], "ffn_hidden": c["F"], "prefix": c["L"],
+                   "accept_threshold_nats": c["gamma"], "schedule": c["sched"]},
+        "canvas_tokens_per_s": steps_per_s * c["N"],
+        "mfma_frac_of_bf16_peak": flops / dt / PEAK_BF16_FLOPS,
+        "roofline": {"bound": "hbm", "kernel": "lm_head (tied head + softmax/entropy epilogue)",
+                     "achieved": lm_gbs, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                     "frac": lm_gbs * 1e9 / PEAK_HBM_BYTES, "traffic": None,
+                     "avg_launch_us": lm_avg_s * 1e6, "launches": lm_n,
+                     "bytes_per_launch": lm_head_bytes(c)},
+        "selfcond_kernel": {"avg_launch_us": sc_avg_s * 1e6, "launches": sc_n,
+                            "achieved_GBps": selfcond_bytes(c) / max(sc_avg_s, 1e-12) / 1e9},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(c, inp)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

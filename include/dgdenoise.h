@@ -1,0 +1,259 @@
+/*
+ * dgdenoise.h -- C ABI of libdgdenoise: the uniform-state text-diffusion
+ * denoising step on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the DiffusionGemma pages:
+ *   [P1] "文字生成中的擴散模型解析" (DiffusionGemma explained, zh-TW mirror)
+ *   [P2] "DiffusionGemma——把文字生成從自迴歸換成擴散去噪" (deep-dive blog)
+ *   [P3] "DiffusionGemma 图解" (A Visual Guide to DiffusionGemma, zh-CN)
+ *   [P4] DiffusionGemma explained (ai.google.dev, Japanese)
+ *   [P5] DiffusionGemma local-deployment workshop (yomxxx.com)
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are device (HBM) addresses owned by the caller;
+ *    the library never frees or retains them.  Pointers marked "host" are
+ *    read or written before the call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Entry points are asynchronous on that stream unless stated otherwise.
+ *  - Every argument is validated on the host before the first launch.  A call
+ *    that returns anything other than DG_OK has launched nothing and changed
+ *    no buffer (cache, canvas or workspace).  DG_ERR_HIP means a launch was
+ *    rejected by the runtime after validation; device faults surface at the
+ *    caller's next synchronisation.
+ *  - Dense matrices are row-major.  bf16 values are IEEE binary32 truncated
+ *    to the upper 16 bits after round-to-nearest-even.
+ *  - The library allocates no device memory on the compute path: scratch
+ *    lives in a caller-provided workspace of dg_workspace_bytes() bytes.
+ *  - Calls that share a workspace or a canvas must be ordered (same stream or
+ *    explicit events); concurrent calls on them race.
+ */
+#ifndef DGDENOISE_H
+#define DGDENOISE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DG_ABI_VERSION 1
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad enum, NaN/negative threshold */
+  DG_ERR_UNSUPPORTED = 2,   /* shape outside what the kernels implement */
+  DG_ERR_CAPACITY = 3,      /* KV cache would overflow */
+  DG_ERR_WORKSPACE = 4,     /* workspace smaller than dg_workspace_bytes() */
+  DG_ERR_HIP = 5            /* the HIP runtime rejected a launch or copy */
+} dg_status;
+
+typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+
+/* Acceptance rule of the entropy-bounded sampler.
+ * SUM_MINUS_MAX: [P3] §5.4 -- walking positions from lowest entropy upward, a
+ *   position is accepted while (sum of entropies walked so far) minus (their
+ *   maximum) stays <= the threshold.  Always accepts at least one position.
+ * CUMSUM: [P5] entropy-constrained sampler -- the plain running sum must stay
+ *   <= the threshold. */
+typedef enum { DG_ACCEPT_SUM_MINUS_MAX = 0, DG_ACCEPT_CUMSUM = 1 } dg_accept_rule;
+
+/* Model and canvas shape.
+ * Supported: 1 <= canvas_len <= 256; vocab a power of two in [256, 2^24];
+ * n_q_heads a multiple of n_kv_heads.  DG_BF16 additionally needs head_dim ==
+ * 128 and d_model, ffn_hidden multiples of 64; DG_F32 needs head_dim <= 128. */
+typedef struct {
+  int32_t canvas_len;   /* N: tokens per canvas ([P1]: 256; [P5] table: 128) */
+  int32_t vocab;        /* V */
+  int32_t d_model;      /* d */
+  int32_t n_q_heads;    /* Hq */
+  int32_t n_kv_heads;   /* Hkv (grouped-query attention when < Hq) */
+  int32_t head_dim;     /* hd */
+  int32_t ffn_hidden;   /* F: hidden width of the self-conditioning FFN */
+  dg_dtype dtype;       /* storage/operand type of weights, cache, activations */
+  float rms_eps;        /* RMSNorm epsilon (1e-6 in the shipped configurations) */
+  float conf_eps;       /* adaptive-stop confidence threshold on entropy, nats
+                           ([P3] §5.3: 0.005) */
+  dg_accept_rule accept_rule;
+} dg_config;
+
+/* Weights (device, dtype of the config, caller-owned, read-only).
+ * E [V][d] is the token-embedding table, tied to the LM head ([P3] §4.1).
+ * E_t [d][V] is E transposed, produced once by dg_pack_embedding(); the
+ * self-conditioning contraction streams it (required for DG_BF16, ignored
+ * for DG_F32).  w_sc1 [F][d], w_sc2 [d][F]: self-conditioning FFN ([P3] §5.1).
+ * wq [Hq*hd][d], wk/wv [Hkv*hd][d], wo [d][Hq*hd]: attention projections.
+ * g_attn, g_final [d]: RMSNorm gains (pre-attention, pre-LM-head). */
+typedef struct {
+  const void *E, *E_t, *w_sc1, *w_sc2, *wq, *wk, *wv, *wo, *g_attn, *g_final;
+} dg_weights;
+
+/* Prefix KV cache ([P1]/[P4]: written causally by prefill, read by denoise).
+ * k, v: device float32 [Hkv][capacity][hd] for both dtypes (a bf16 model's
+ * keys/values are kept at full precision; the attention kernel splits them
+ * into bf16 pairs for the matrix cores).  Positions
+ * [0, length) are valid.  dg_denoise_step never writes the cache
+ * ([P3] §4.2); dg_prefill_append writes [length, length+n) and then
+ * advances `length` (host field) by n. */
+typedef struct {
+  void *k, *v;
+  int32_t length;
+  int32_t capacity;
+} dg_kv_cache;
+
+/* Per-canvas state.  Device buffers are caller-owned:
+ *   tokens  int32 [N]            current canvas
+ *   probs   dtype [N][V]         softmax numerators of the last step, per
+ *                                256-column tile: exp(y - m_tile) (the
+ *                                self-conditioning input of the next step)
+ *   stats   bytes dg_stats_bytes(): per-(row, tile) softmax statistics,
+ *                                normalisers and each row's dominant token
+ *                                with its exact probability; opaque
+ *   entropy float [N]            nats, clamped >= +0 (NaN propagates)
+ *   argmax  int32 [N]            highest logit, lowest index on ties
+ *   accept  uint8 [N]            1 = accepted in the last step
+ *   status  int32 [DG_STATUS_WORDS]  see DG_ST_* below
+ * Host fields: step (index of the next step), has_prev (the next step uses
+ * self-conditioning), seed and canvas_id (Philox key and counter word). */
+#define DG_STATUS_WORDS 16
+enum {
+  DG_ST_ALLCONF = 0,   /* every entropy < conf_eps */
+  DG_ST_CHANGED = 1,   /* last step changed the canvas */
+  DG_ST_STABLE = 2,    /* consecutive steps without change */
+  DG_ST_ACCEPTED = 3,  /* positions accepted in the last step */
+  DG_ST_NAN = 4,       /* positions whose entropy was NaN */
+  DG_ST_STEP = 5,      /* index of the last completed step */
+  DG_ST_HMIN = 6,      /* float bits: min entropy */
+  DG_ST_HMAX = 7,      /* float bits: max entropy */
+  DG_ST_HMEAN = 8      /* float bits: mean entropy */
+};
+typedef struct {
+  int32_t *tokens;
+  void *probs;
+  void *stats;
+  float *entropy;
+  int32_t *argmax;
+  uint8_t *accept;
+  int32_t *status;
+  int32_t step;
+  int32_t has_prev;
+  uint64_t seed;
+  uint32_t canvas_id;
+} dg_canvas;
+
+typedef struct {
+  int32_t accepted;
+  int32_t stable;
+  int32_t allconf;
+  int32_t changed;
+  float h_min, h_mean, h_max;
+} dg_step_stats;
+
+/* ---- sizes and checks (host only, no device work) ---------------------- */
+int32_t dg_abi_version(void);
+const char *dg_status_string(dg_status s);
+/* DG_OK if the configuration is supported; otherwise why not. */
+dg_status dg_validate_config(const dg_config *cfg);
+/* Workspace bytes for dg_denoise_step and for dg_prefill_append of up to
+ * max_prefill_tokens tokens (0 if unsupported configuration). */
+size_t dg_workspace_bytes(const dg_config *cfg, int32_t max_prefill_tokens);
+/* Bytes of the canvas `stats` buffer (0 if unsupported configuration). */
+size_t dg_stats_bytes(const dg_config *cfg);
+
+/* ---- one-time preparation ----------------------------------------------- */
+/* Writes E_t [d][V] = transpose of E [V][d] (device, caller-allocated
+ * V*d elements of the config dtype).  A layout copy only: E_t holds the same
+ * values as E. */
+dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_t, void *stream);
+
+/* [P3] §5.4 canvas initialisation: tokens[i] = the top log2(V) bits of word 0
+ * of Philox4x32-10(key = seed, counter = (i, 0, canvas_id, 0)) -- uniform
+ * vocabulary tokens.  Resets status (stable = 0) and the host fields
+ * step = 0, has_prev = 0, seed, canvas_id. */
+dg_status dg_canvas_init(const dg_config *cfg, dg_canvas *canvas, uint64_t seed,
+                         uint32_t canvas_id, void *stream);
+
+/* ---- the hot path --------------------------------------------------------- */
+/* Causal (incremental) prefill, [P1]/[P4] architecture and [P3] §5.2: for the
+ * n_tokens device tokens at absolute positions length..length+n-1,
+ *   x = E[t]; h = RMSNorm(x) * g_attn; K = h Wk^T, V = h Wv^T  -> cache
+ * and, if attn_out (device, float32 [n][Hq*hd]) is non-NULL, the causal
+ * attention output of the new tokens over keys [0, length+i].  No LM head.
+ * Then cache->length += n_tokens (host field).
+ * Errors: DG_ERR_CAPACITY if length + n_tokens > capacity; DG_ERR_WORKSPACE
+ * if ws_bytes < dg_workspace_bytes(cfg, n_tokens); tokens must be in [0, V)
+ * (not checked on the device: out-of-range ids are clamped). */
+dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cache *cache,
+                            const int32_t *tokens, int32_t n_tokens, void *attn_out,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* One denoising step over the canvas ([P2] update loop; [P3] §4.1, §5.1-§5.4):
+ *  1. h0 = E[c] (+ W2 GELU(W1 (p_prev E)) when has_prev: self-conditioning)
+ *  2. bidirectional attention (no mask) of every canvas query over
+ *     [cache 0..length) || canvas keys; h1 = h0 + O Wo^T
+ *  3. z = RMSNorm(h1) E^T (tied head); y = z / temperature; p = softmax(y);
+ *     entropy (nats) and argmax per position; probs/stats keep p for the
+ *     next step
+ *  4. accept by `accept_rule` under `accept_threshold_nats`; accepted
+ *     positions take the argmax token, every rejected one a fresh uniform
+ *     token (Philox counter (i, step, canvas_id, 1)); status flags updated
+ * Then canvas->step += 1 and canvas->has_prev = 1 (host fields).
+ * Errors: temperature must be finite and > 0; the threshold >= 0 and not NaN;
+ * DG_ERR_WORKSPACE if ws_bytes < dg_workspace_bytes(cfg, 0). */
+dg_status dg_denoise_step(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache,
+                          dg_canvas *canvas, float temperature, float accept_threshold_nats,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* Adaptive stop, [P3] §5.3 and [P5] scheduler: stop when every entropy is
+ * below conf_eps, or when the canvas has been unchanged for stable_steps
+ * consecutive steps (stable_steps <= 0 disables the stability test).
+ * Synchronises `stream`, then writes *stop_host (0/1) and, if non-NULL,
+ * *stats_host.  This is the only device-to-host transfer of a step. */
+dg_status dg_should_stop(const dg_config *cfg, const dg_canvas *canvas, int32_t stable_steps,
+                         int32_t *stop_host, dg_step_stats *stats_host, void *stream);
+
+/* ---- test and measurement exports -------------------------------------------
+ * Not part of the generation path; they expose single kernels for parity
+ * tests and timing.  Same validation rules as above. */
+
+/* Byte offsets inside the workspace of the step's intermediates, all f32:
+ * h0 [N][d], attn [N][Hq*hd], h1 [N][d], selfcond [N][d] (p_prev E),
+ * logits [N][V] (the LM head's fp32 accumulators; bf16 configurations
+ * write them only when dg_test_set_logits_dump(1)). */
+typedef struct {
+  size_t h0, attn, h1, selfcond, logits;
+} dg_ws_offsets;
+dg_status dg_test_ws_offsets(const dg_config *cfg, dg_ws_offsets *out);
+/* 1: dg_denoise_step also writes the fp32 logits z into the workspace (the
+ * workspace must then be dg_test_logits_ws_bytes() large).  Global switch. */
+void dg_test_set_logits_dump(int32_t on);
+size_t dg_test_logits_ws_bytes(const dg_config *cfg);
+
+/* Self-conditioning contraction alone: S (f32 [N][d]) = P E, with P given
+ * directly as dtype [N][V] (no tile normalisers, no correction). */
+dg_status dg_test_selfcond(const dg_config *cfg, const dg_weights *w, const void *P, void *S,
+                           void *ws, size_t ws_bytes, void *stream);
+/* Selection kernel alone on given entropies/argmax/tokens (device):
+ * writes tokens (in place), accept and status exactly as dg_denoise_step. */
+dg_status dg_test_select(const dg_config *cfg, dg_canvas *canvas, float accept_threshold_nats,
+                         void *stream);
+/* Philox4x32-10 on the device: out[4*i .. 4*i+3] for counters ctr[4*i..]
+ * and key (k0, k1); n counters; all device pointers. */
+dg_status dg_test_philox(const uint32_t *ctr, uint32_t k0, uint32_t k1, uint32_t *out, int32_t n,
+                         void *stream);
+/* Plain device copy of `bytes` bytes (multiple of 16) used to calibrate
+ * memory-traffic counters. */
+dg_status dg_test_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/* Timing of the kernels inside dg_denoise_step: when enabled, HIP events are
+ * recorded on the step's stream around the LM-head kernel and the
+ * self-conditioning contraction.  dg_profile_read synchronises on the last
+ * recorded events and returns the summed milliseconds and launch counts. */
+void dg_profile_enable(int32_t on);
+dg_status dg_profile_read(float *lm_head_ms, int32_t *lm_head_count, float *selfcond_ms,
+                          int32_t *selfcond_count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DGDENOISE_H */

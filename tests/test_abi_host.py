@@ -1,0 +1,176 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch
+(the rejected calls change no host-visible state)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from uniform_state_discrete_dg_amd import binding as B
+from uniform_state_discrete_dg_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dgdenoise.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from uniform_state_discrete_dg_amd import build
+        build.build()
+    return B.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    # the binding wraps every declared entry point under the same name
+    assert set(names) == set(B.SIGNATURES)
+
+
+def test_abi_version_and_strings(lib):
+    assert B.dg_abi_version() == 1
+    for s in range(6):
+        assert lib.dg_status_string(s)
+
+
+def cfg_of(i, **kw):
+    c = W.config(i)
+    c.update(kw)
+    return B.make_config(c)
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+def test_shipped_configs_supported(lib, i):
+    cfg = cfg_of(i)
+    assert B.dg_validate_config(cfg) == B.DG_OK
+    assert B.dg_workspace_bytes(cfg, 0) > 0
+    assert B.dg_workspace_bytes(cfg, 1024) >= B.dg_workspace_bytes(cfg, 0)
+    assert B.dg_stats_bytes(cfg) == cfg.canvas_len * ((cfg.vocab // 256) * 20 + 8)
+
+
+@pytest.mark.parametrize("kw,st", [
+    (dict(V=1000), B.DG_ERR_UNSUPPORTED),        # vocabulary not a power of two
+    (dict(V=128), B.DG_ERR_UNSUPPORTED),         # smaller than one statistics tile
+    (dict(N=257), B.DG_ERR_UNSUPPORTED),         # canvas longer than one workgroup
+    (dict(hd=64), B.DG_ERR_UNSUPPORTED),         # bf16 kernels are head_dim 128
+    (dict(d=1000), B.DG_ERR_UNSUPPORTED),        # K slices of 64
+    (dict(Hq=12, Hkv=8), B.DG_ERR_UNSUPPORTED),  # GQA groups must divide
+    (dict(N=0), B.DG_ERR_INVALID_ARG),
+    (dict(rms_eps=-1.0), B.DG_ERR_INVALID_ARG),
+])
+def test_config_rejections(lib, kw, st):
+    c = W.config(2)
+    c.update(kw)
+    assert B.dg_validate_config(B.make_config(c)) == st
+    assert B.dg_workspace_bytes(B.make_config(c), 0) == 0
+
+
+def test_bad_enums(lib):
+    cfg = cfg_of(2)
+    cfg.dtype = 7
+    assert B.dg_validate_config(cfg) == B.DG_ERR_INVALID_ARG
+    cfg = cfg_of(2)
+    cfg.accept_rule = 9
+    assert B.dg_validate_config(cfg) == B.DG_ERR_INVALID_ARG
+
+
+FAKE = 0x10000  # a non-null address; validation must fail before it is used
+
+
+def fake_weights():
+    return B.dg_weights(*([FAKE] * 10))
+
+
+def fake_canvas():
+    return B.dg_canvas(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 1, 5, 0)
+
+
+def call_step(cfg, w, cache, cv, T, g, ws_bytes):
+    return B.lib().dg_denoise_step(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache),
+                                   ctypes.byref(cv), T, g, ctypes.c_void_p(FAKE), ws_bytes, None)
+
+
+def test_denoise_step_validation(lib):
+    cfg = cfg_of(2)
+    need = B.dg_workspace_bytes(cfg, 0)
+    cache = B.dg_kv_cache(FAKE, FAKE, 512, 512)
+    cv = fake_canvas()
+    w = fake_weights()
+    cases = [
+        (dict(T=0.0), B.DG_ERR_INVALID_ARG),
+        (dict(T=-1.0), B.DG_ERR_INVALID_ARG),
+        (dict(T=float("nan")), B.DG_ERR_INVALID_ARG),
+        (dict(T=float("inf")), B.DG_ERR_INVALID_ARG),
+        (dict(g=-0.5), B.DG_ERR_INVALID_ARG),
+        (dict(g=float("nan")), B.DG_ERR_INVALID_ARG),
+        (dict(ws=need - 1), B.DG_ERR_WORKSPACE),
+    ]
+    for kw, st in cases:
+        r = call_step(cfg, w, cache, cv, kw.get("T", 1.0), kw.get("g", 8.0), kw.get("ws", need))
+        assert r == st, (kw, r)
+        assert (cv.step, cv.has_prev) == (3, 1)
+    w2 = fake_weights()
+    w2.E_t = None
+    assert call_step(cfg, w2, cache, cv, 1.0, 8.0, need) == B.DG_ERR_INVALID_ARG
+    cv2 = fake_canvas()
+    cv2.status = None
+    assert call_step(cfg, w, cache, cv2, 1.0, 8.0, need) == B.DG_ERR_INVALID_ARG
+    bad_cache = B.dg_kv_cache(FAKE, FAKE, 600, 512)
+    assert call_step(cfg, w, bad_cache, cv, 1.0, 8.0, need) == B.DG_ERR_INVALID_ARG
+    assert (cv.step, cv.has_prev) == (3, 1)
+
+
+def test_prefill_validation(lib):
+    cfg = cfg_of(5)
+    w = fake_weights()
+    L = B.lib()
+    cache = B.dg_kv_cache(FAKE, FAKE, 3000, 3072)
+    r = L.dg_prefill_append(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache),
+                            ctypes.c_void_p(FAKE), 256, None, ctypes.c_void_p(FAKE), 1 << 40, None)
+    assert r == B.DG_ERR_CAPACITY and cache.length == 3000
+    cache = B.dg_kv_cache(FAKE, FAKE, 0, 3072)
+    need = B.dg_workspace_bytes(cfg, 1024)
+    r = L.dg_prefill_append(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache),
+                            ctypes.c_void_p(FAKE), 1024, None, ctypes.c_void_p(FAKE), need // 4, None)
+    assert r == B.DG_ERR_WORKSPACE and cache.length == 0
+    r = L.dg_prefill_append(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), None, 4, None,
+                            ctypes.c_void_p(FAKE), need, None)
+    assert r == B.DG_ERR_INVALID_ARG
+    r = L.dg_prefill_append(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache),
+                            ctypes.c_void_p(FAKE), -1, None, ctypes.c_void_p(FAKE), need, None)
+    assert r == B.DG_ERR_INVALID_ARG
+    # zero tokens is a no-op that succeeds without touching the device
+    r = L.dg_prefill_append(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache),
+                            None, 0, None, None, 0, None)
+    assert r == B.DG_OK and cache.length == 0
+
+
+def test_other_entry_point_validation(lib):
+    L = B.lib()
+    cfg = cfg_of(2)
+    cv = fake_canvas()
+    stop = ctypes.c_int32(0)
+    assert L.dg_should_stop(ctypes.byref(cfg), ctypes.byref(cv), 3, None, None, None) == \
+        B.DG_ERR_INVALID_ARG
+    assert L.dg_pack_embedding(ctypes.byref(cfg), None, ctypes.c_void_p(FAKE), None) == \
+        B.DG_ERR_INVALID_ARG
+    cv.tokens = None
+    assert L.dg_canvas_init(ctypes.byref(cfg), ctypes.byref(cv), 1, 0, None) == \
+        B.DG_ERR_INVALID_ARG
+    assert L.dg_test_copy(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 15, None) == \
+        B.DG_ERR_INVALID_ARG
+    assert L.dg_test_philox(None, 0, 0, None, -1, None) == B.DG_ERR_INVALID_ARG
+    bad = cfg_of(2)
+    bad.vocab = 1000
+    assert L.dg_should_stop(ctypes.byref(bad), ctypes.byref(fake_canvas()), 3,
+                            ctypes.byref(stop), None, None) == B.DG_ERR_UNSUPPORTED

@@ -1,0 +1,321 @@
+"""Whole-step parity of dg_denoise_step / dg_prefill_append (GPU) against the
+oracle, lock-step: each step the oracle is given the canvas the GPU produced
+(integer state already verified by the replay of the previous step) and its
+own previous-step probabilities.
+
+Floats: fp32 configuration <= 1e-4 relative Frobenius; bf16 configurations
+<= 1e-2 on logits and attention output, <= 2e-3 nats on every entropy.
+Decisions (accept set, re-noised tokens, flags): bit-exact when the oracle
+replays the selection on the GPU's entropy vector and argmax.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from uniform_state_discrete_dg_amd import binding as B
+from uniform_state_discrete_dg_amd import driver as D
+from uniform_state_discrete_dg_amd import workloads as W
+from parity_util import (CONF_EPS_F32, check_argmax, gpu_probs, oracle_cache, rel_frob,
+                         replay_select, ws_view)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture
+def logits_dump():
+    """The bf16 path writes its fp32 LM-head accumulators to the workspace."""
+    B.dg_test_set_logits_dump(True)
+    yield
+    B.dg_test_set_logits_dump(False)
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.empty_cache()
+
+
+def lockstep(c, inp, nsteps, rule=0, seed=None, cid=0):
+    """Runs nsteps GPU steps and checks each against the oracle (all rows)."""
+    f32 = c["dtype"] == "f32"
+    tol = 1e-4 if f32 else 1e-2
+    den = D.Denoiser(c, inp, accept_rule=rule, logits_dump=True)
+    om = oracle.model_from_inputs(inp)
+    kc, vc = oracle_cache(inp)
+    N, V, d, qw = c["N"], c["V"], c["d"], c["Hq"] * c["hd"]
+    seed = W.canvas_seed(c.get("id", 0)) if seed is None else seed
+    den.init_canvas(seed, cid)
+    np.testing.assert_array_equal(den.canvas.tokens.cpu().numpy(),
+                                  oracle.canvas_init(seed, cid, N, V))
+    p_prev = None
+    stable = 0
+    report = []
+    for s in range(nsteps):
+        T = D.temperature(c["sched"], c["T0"], c["T1"], s, c["steps"])
+        assert abs(T - oracle.temperature(c["sched"], c["T0"], c["T1"], s, c["steps"])) < 1e-12
+        tokens_in = den.canvas.tokens.cpu().numpy()
+        den.step(T, c["gamma"])
+        torch.cuda.synchronize()
+        o = om.denoise_forward(tokens_in, p_prev, kc, vc, c["L"], float(np.float32(T)))
+        h0 = ws_view(den, "h0", torch.float32, (N, d)).cpu().numpy()
+        h1 = ws_view(den, "h1", torch.float32, (N, d)).cpu().numpy()
+        attn = ws_view(den, "attn", torch.float32, (N, qw)).cpu().numpy()
+        z = ws_view(den, "logits", torch.float32, (N, V)).cpu().numpy()
+        H = den.canvas.entropy.cpu().numpy()
+        am = den.canvas.argmax.cpu().numpy()
+        errs = dict(h0=rel_frob(h0, o["h0"]), attn=rel_frob(attn, o["attn"]),
+                    h1=rel_frob(h1, o["h1"]), logits=rel_frob(z, o["logits"]),
+                    probs=rel_frob(gpu_probs(den), o["probs"]),
+                    dH=float(np.max(np.abs(H - o["entropy"]))))
+        report.append(errs)
+        for k in ("h0", "attn", "h1", "logits", "probs"):
+            assert errs[k] <= tol, (s, k, errs)
+        if f32:
+            assert rel_frob(H, o["entropy"]) <= 1e-4, (s, errs)
+        else:
+            assert errs["dH"] <= 2e-3, (s, errs)
+        # argmax: replayed on the GPU's own fp32 logits (exact), and against
+        # the oracle's wherever the oracle's top-2 gap exceeds the float error
+        for r in range(N):
+            assert oracle.argmax(np.ascontiguousarray(z[r])) == am[r]
+        gap = 1e-4 if f32 else 2e-2
+        check_argmax(o["logits"], o["argmax"], am, range(N), gap)
+        fl = replay_select(den, tokens_in, stable, s, c["gamma"], rule)
+        stable = fl["stable"]
+        p_prev = o["probs"]
+    return den, report
+
+
+@pytest.mark.usefixtures("logits_dump")
+def test_config1_fp32_lockstep():
+    c = W.config(1)
+    inp = W.make_inputs(c)
+    den, rep = lockstep(c, inp, c["steps"])
+    print(rep)
+
+
+def test_config1_fp32_independent_decisions():
+    """fp32 config: the oracle's own decisions equal the GPU's when no two
+    entropies (or a prefix sum and the threshold) are within float error."""
+    c = W.config(1)
+    inp = W.make_inputs(c)
+    den = D.Denoiser(c, inp)
+    om = oracle.model_from_inputs(inp)
+    kc, vc = oracle_cache(inp)
+    seed = W.canvas_seed(1)
+    den.init_canvas(seed, 0)
+    tok_o = oracle.canvas_init(seed, 0, c["N"], c["V"])
+    p_prev, stable = None, 0
+    for s in range(c["steps"]):
+        T = D.temperature(c["sched"], c["T0"], c["T1"], s, c["steps"])
+        den.step(T, c["gamma"])
+        o = om.denoise_forward(tok_o, p_prev, kc, vc, c["L"], T)
+        Hs = np.sort(o["entropy"])
+        sums = np.concatenate([[0.0], np.cumsum(Hs)])
+        if np.min(np.diff(Hs)) < 1e-5 or np.min(np.abs(sums - c["gamma"])) < 1e-5:
+            pytest.skip("near-tie in the oracle's entropies")
+        acc, tok_o, fl = oracle.select(o["entropy"].astype(np.float32), o["argmax"], tok_o, c["V"],
+                                       c["gamma"], 0, seed, 0, s, stable, CONF_EPS_F32)
+        stable = fl["stable"]
+        p_prev = o["probs"]
+        np.testing.assert_array_equal(den.canvas.accept.cpu().numpy(), acc)
+        np.testing.assert_array_equal(den.canvas.tokens.cpu().numpy(), tok_o)
+
+
+@pytest.mark.usefixtures("logits_dump")
+@pytest.mark.parametrize("rule", [0, 1])
+def test_config2_bf16_lockstep(rule):
+    c = W.config(2)
+    inp = W.make_inputs(c)
+    den, rep = lockstep(c, inp, 3, rule=rule)
+    print(rep)
+
+
+@pytest.mark.usefixtures("logits_dump")
+def test_config3_dims_reduced_vocab_lockstep():
+    """Config-3 model dims (d 2816, GQA 16/8, F 2816, L 2048, N 256) with a
+    16384-token vocabulary so the oracle finishes in seconds."""
+    c = W.config(3, V=16384)
+    inp = W.make_inputs(c, seed=W.weight_seed(3))
+    den, rep = lockstep(c, inp, 2)
+    print(rep)
+
+
+@pytest.mark.usefixtures("logits_dump")
+def test_ragged_canvas_lockstep():
+    """A canvas that is not a multiple of any tile (N = 200, 40 rows past the
+    last 32-row block), short prefix not a multiple of 64."""
+    c = W.config(2, N=200, L=100, V=8192, d=1024, F=1024)
+    inp = W.make_inputs(c, seed=77)
+    den, rep = lockstep(c, inp, 2)
+    print(rep)
+
+
+@pytest.mark.usefixtures("logits_dump")
+@pytest.mark.parametrize("cfg_id", [3, 4])
+def test_full_size_step_sampled(cfg_id):
+    """Full vocabulary (262144) at the configuration's canvas and prefix:
+    first step checked on sampled rows (attention keys use every row), then
+    three more self-conditioned steps checked by decision replay and by the
+    argmax replay on the logits dump."""
+    c = W.config(cfg_id)
+    inp = W.make_inputs(c)
+    den = D.Denoiser(c, inp, logits_dump=True)
+    om = oracle.model_from_inputs(inp)
+    kc, vc = oracle_cache(inp)
+    N, V, d = c["N"], c["V"], c["d"]
+    seed = W.canvas_seed(cfg_id)
+    den.init_canvas(seed, 0)
+    rows = sorted({0, 1, N // 3, N // 2 + 1, N - 1})
+    sel = np.zeros(N, np.uint8)
+    sel[rows] = 1
+    stable = 0
+    for s in range(4):
+        T = D.temperature(c["sched"], c["T0"], c["T1"], s, c["steps"])
+        tokens_in = den.canvas.tokens.cpu().numpy()
+        den.step(T, c["gamma"])
+        torch.cuda.synchronize()
+        zg = ws_view(den, "logits", torch.float32, (N, V))
+        am = den.canvas.argmax.cpu().numpy()
+        zr = zg[rows].cpu().numpy()
+        for k, r in enumerate(rows):
+            assert oracle.argmax(np.ascontiguousarray(zr[k])) == am[r]
+        if s == 0:
+            o = om.denoise_forward(tokens_in, None, kc, vc, c["L"], float(np.float32(T)),
+                                   row_sel=sel, want_probs=False)
+            qw = c["Hq"] * c["hd"]
+            attn = ws_view(den, "attn", torch.float32, (N, qw)).cpu().numpy()
+            h1 = ws_view(den, "h1", torch.float32, (N, d)).cpu().numpy()
+            h0 = ws_view(den, "h0", torch.float32, (N, d)).cpu().numpy()
+            assert rel_frob(h0, o["h0"]) == 0.0  # embedding rows are exact
+            assert rel_frob(attn[rows], o["attn"][rows]) <= 1e-2
+            assert rel_frob(h1[rows], o["h1"][rows]) <= 1e-2
+            assert rel_frob(zr, o["logits"][rows]) <= 1e-2
+            H = den.canvas.entropy.cpu().numpy()
+            assert np.max(np.abs(H[rows] - o["entropy"][rows])) <= 2e-3
+            check_argmax([o["logits"][r] for r in rows], o["argmax"], am, rows, 2e-2)
+        fl = replay_select(den, tokens_in, stable, s, c["gamma"], 0)
+        stable = fl["stable"]
+
+
+def test_determinism_bitwise():
+    c = W.config(2)
+    inp = W.make_inputs(c)
+    outs = []
+    for _ in range(2):
+        den = D.Denoiser(c, inp)
+        den.init_canvas(3, 1)
+        for s in range(3):
+            den.step(D.temperature("cosine", 1.5, 0.3, s, 16), 8.0)
+        torch.cuda.synchronize()
+        outs.append((den.canvas.entropy.clone(), den.canvas.probs.clone(),
+                     den.canvas.tokens.clone(), den.canvas.stats.clone()))
+        del den
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_cache_untouched_by_denoise():
+    c = W.config(2)
+    inp = W.make_inputs(c)
+    den = D.Denoiser(c, inp, capacity=c["L"] + 64)
+    k0, v0 = den.cache.k.clone(), den.cache.v.clone()
+    den.init_canvas(1, 0)
+    for s in range(2):
+        den.step(1.0, 8.0)
+    torch.cuda.synchronize()
+    assert torch.equal(den.cache.k, k0) and torch.equal(den.cache.v, v0)
+    assert den.cache.length == c["L"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_append_incremental(dtype):
+    """Causal prefill of 300 tokens then 77 more (ragged), against the oracle."""
+    if dtype == "bf16":
+        c = W.config(2, L=0, V=8192, d=1024, F=1024, Hq=8, Hkv=4)
+    else:
+        c = W.config(1, L=0)
+    cap = 400
+    inp = W.make_inputs(c, seed=11)
+    den = D.Denoiser(c, inp, capacity=cap, max_prefill=300)
+    om = oracle.model_from_inputs(inp)
+    Hkv, hd, qw = c["Hkv"], c["hd"], c["Hq"] * c["hd"]
+    kc, vc = np.zeros((Hkv, cap, hd)), np.zeros((Hkv, cap, hd))
+    g = torch.Generator().manual_seed(5)
+    toks = torch.randint(0, c["V"], (377,), generator=g, dtype=torch.int32)
+    tol = 1e-4
+    L = 0
+    for lo, hi in [(0, 300), (300, 377)]:
+        n = hi - lo
+        attn = torch.zeros((n, qw), dtype=torch.float32, device="cuda")
+        den.prefill(toks[lo:hi].cuda(), attn)
+        torch.cuda.synchronize()
+        a_ref = om.prefill_append(toks[lo:hi].numpy(), kc, vc, L)
+        L += n
+        assert den.cache.length == L
+        assert rel_frob(den.cache.k[:, :L].float().cpu().numpy(), kc[:, :L]) <= tol
+        assert rel_frob(den.cache.v[:, :L].float().cpu().numpy(), vc[:, :L]) <= tol
+        assert rel_frob(attn.float().cpu().numpy(), a_ref) <= tol
+    assert not den.cache.k[:, L:].any()
+    # keys/values of a token depend on the token only: one-shot append is bitwise equal
+    den2 = D.Denoiser(c, inp, capacity=cap, max_prefill=377)
+    den2.prefill(toks.cuda())
+    assert torch.equal(den2.cache.k, den.cache.k) and torch.equal(den2.cache.v, den.cache.v)
+    # capacity overflow is rejected without touching the cache
+    with pytest.raises(B.DgError) as e:
+        den.prefill(toks[:cap].cuda())
+    assert e.value.status == B.DG_ERR_CAPACITY and den.cache.length == L
+
+
+def test_block_diffusion_reduced_vocab():
+    """Block diffusion (prompt 1024, chained canvases of 256) at config-5 model
+    dims with a 16384-token vocabulary: each step replayed bit-exactly, each
+    finished canvas appended causally and checked against the oracle."""
+    c = W.config(5, V=16384)
+    inp = W.make_inputs(c, seed=W.weight_seed(5))
+    cap = 1024 + 2 * 256
+    den = D.Denoiser(c, inp, capacity=cap, max_prefill=1024)
+    om = oracle.model_from_inputs(inp)
+    Hkv, hd = c["Hkv"], c["hd"]
+    kc, vc = np.zeros((Hkv, cap, hd)), np.zeros((Hkv, cap, hd))
+    prompt = inp["prompt"]
+    den.prefill(prompt.cuda())
+    om.prefill_append(prompt.numpy(), kc, vc, 0, want_attn=False)
+    seed = W.canvas_seed(5)
+    for b in range(2):
+        den.init_canvas(seed, b)
+        stable = 0
+        for s in range(2):
+            T = D.temperature(c["sched"], c["T0"], c["T1"], s, c["steps"])
+            tokens_in = den.canvas.tokens.cpu().numpy()
+            den.step(T, c["gamma"])
+            fl = replay_select(den, tokens_in, stable, s, c["gamma"], 0)
+            stable = fl["stable"]
+        L0 = den.cache.length
+        fin = den.canvas.tokens.clone()
+        den.prefill(fin)
+        om.prefill_append(fin.cpu().numpy(), kc, vc, L0, want_attn=False)
+        L1 = den.cache.length
+        assert L1 == L0 + 256
+        assert rel_frob(den.cache.k[:, :L1].float().cpu().numpy(), kc[:, :L1]) <= 1e-2
+        assert rel_frob(den.cache.v[:, :L1].float().cpu().numpy(), vc[:, :L1]) <= 1e-2
+
+
+def test_block_diffusion_full_size_short():
+    """Config 5 at full size: prompt 1024 prefilled, one canvas of 256 for three
+    steps (decisions replayed bit-exactly), appended (cache 1024 -> 1280)."""
+    c = W.config(5)
+    inp = W.make_inputs(c)
+    den = D.Denoiser(c, inp, capacity=c["cap"], max_prefill=1024)
+    den.prefill(inp["prompt"].cuda())
+    assert den.cache.length == 1024
+    den.init_canvas(W.canvas_seed(5), 0)
+    stable = 0
+    for s in range(3):
+        T = D.temperature(c["sched"], c["T0"], c["T1"], s, c["steps"])
+        tokens_in = den.canvas.tokens.cpu().numpy()
+        den.step(T, c["gamma"])
+        stable = replay_select(den, tokens_in, stable, s, c["gamma"], 0)["stable"]
+    den.prefill(den.canvas.tokens.clone())
+    assert den.cache.length == 1280

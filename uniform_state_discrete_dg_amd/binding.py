@@ -1,0 +1,310 @@
+"""ctypes binding of libdgdenoise (include/dgdenoise.h): same entry-point
+names, argument marshalling only.  PyTorch supplies device memory (tensors
+whose data_ptr() is passed down) and streams; every step of the compute
+path runs in the library's HIP kernels.
+
+The library must have been built (``python -m uniform_state_discrete_dg_amd.build``
+or ``__graft_entry__.build()``); loading fails loudly otherwise -- there is
+no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdgdenoise.so")
+
+c_i32, c_u32, c_u64, c_f32, c_sz, vp = (ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64,
+                                        ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p)
+
+DG_OK, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_CAPACITY, DG_ERR_WORKSPACE, DG_ERR_HIP = range(6)
+DG_F32, DG_BF16 = 0, 1
+DG_ACCEPT_SUM_MINUS_MAX, DG_ACCEPT_CUMSUM = 0, 1
+DG_STATUS_WORDS = 16
+(DG_ST_ALLCONF, DG_ST_CHANGED, DG_ST_STABLE, DG_ST_ACCEPTED, DG_ST_NAN, DG_ST_STEP, DG_ST_HMIN,
+ DG_ST_HMAX, DG_ST_HMEAN) = range(9)
+TILE_V = 256
+
+
+class dg_config(ctypes.Structure):
+    _fields_ = [("canvas_len", c_i32), ("vocab", c_i32), ("d_model", c_i32), ("n_q_heads", c_i32),
+                ("n_kv_heads", c_i32), ("head_dim", c_i32), ("ffn_hidden", c_i32), ("dtype", c_i32),
+                ("rms_eps", c_f32), ("conf_eps", c_f32), ("accept_rule", c_i32)]
+
+
+class dg_weights(ctypes.Structure):
+    _fields_ = [(n, vp) for n in ("E", "E_t", "w_sc1", "w_sc2", "wq", "wk", "wv", "wo", "g_attn",
+                                  "g_final")]
+
+
+class dg_kv_cache(ctypes.Structure):
+    _fields_ = [("k", vp), ("v", vp), ("length", c_i32), ("capacity", c_i32)]
+
+
+class dg_canvas(ctypes.Structure):
+    _fields_ = [("tokens", vp), ("probs", vp), ("stats", vp), ("entropy", vp), ("argmax", vp),
+                ("accept", vp), ("status", vp), ("step", c_i32), ("has_prev", c_i32),
+                ("seed", c_u64), ("canvas_id", c_u32)]
+
+
+class dg_step_stats(ctypes.Structure):
+    _fields_ = [("accepted", c_i32), ("stable", c_i32), ("allconf", c_i32), ("changed", c_i32),
+                ("h_min", c_f32), ("h_mean", c_f32), ("h_max", c_f32)]
+
+
+class dg_ws_offsets(ctypes.Structure):
+    _fields_ = [("h0", c_sz), ("attn", c_sz), ("h1", c_sz), ("selfcond", c_sz), ("logits", c_sz)]
+
+
+P = ctypes.POINTER
+# name -> (restype, argtypes); mirrors include/dgdenoise.h
+SIGNATURES = {
+    "dg_abi_version": (c_i32, []),
+    "dg_status_string": (ctypes.c_char_p, [c_i32]),
+    "dg_validate_config": (c_i32, [P(dg_config)]),
+    "dg_workspace_bytes": (c_sz, [P(dg_config), c_i32]),
+    "dg_stats_bytes": (c_sz, [P(dg_config)]),
+    "dg_pack_embedding": (c_i32, [P(dg_config), vp, vp, vp]),
+    "dg_canvas_init": (c_i32, [P(dg_config), P(dg_canvas), c_u64, c_u32, vp]),
+    "dg_prefill_append": (c_i32, [P(dg_config), P(dg_weights), P(dg_kv_cache), vp, c_i32, vp, vp,
+                                  c_sz, vp]),
+    "dg_denoise_step": (c_i32, [P(dg_config), P(dg_weights), P(dg_kv_cache), P(dg_canvas), c_f32,
+                                c_f32, vp, c_sz, vp]),
+    "dg_should_stop": (c_i32, [P(dg_config), P(dg_canvas), c_i32, P(c_i32), P(dg_step_stats), vp]),
+    "dg_test_ws_offsets": (c_i32, [P(dg_config), P(dg_ws_offsets)]),
+    "dg_test_set_logits_dump": (None, [c_i32]),
+    "dg_test_logits_ws_bytes": (c_sz, [P(dg_config)]),
+    "dg_test_selfcond": (c_i32, [P(dg_config), P(dg_weights), vp, vp, vp, c_sz, vp]),
+    "dg_test_select": (c_i32, [P(dg_config), P(dg_canvas), c_f32, vp]),
+    "dg_test_philox": (c_i32, [vp, c_u32, c_u32, vp, c_i32, vp]),
+    "dg_test_copy": (c_i32, [vp, vp, c_sz, vp]),
+    "dg_profile_enable": (None, [c_i32]),
+    "dg_profile_read": (c_i32, [P(c_f32), P(c_i32), P(c_f32), P(c_i32)]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libdgdenoise.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m uniform_state_discrete_dg_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+class DgError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {lib().dg_status_string(status).decode()} ({status})")
+
+
+def _check(fn: str, st: int) -> None:
+    if st != DG_OK:
+        raise DgError(fn, st)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def dg_abi_version() -> int:
+    return int(lib().dg_abi_version())
+
+
+def dg_validate_config(cfg: dg_config) -> int:
+    return int(lib().dg_validate_config(ctypes.byref(cfg)))
+
+
+def dg_workspace_bytes(cfg: dg_config, max_prefill_tokens: int = 0) -> int:
+    return int(lib().dg_workspace_bytes(ctypes.byref(cfg), max_prefill_tokens))
+
+
+def dg_stats_bytes(cfg: dg_config) -> int:
+    return int(lib().dg_stats_bytes(ctypes.byref(cfg)))
+
+
+def dg_pack_embedding(cfg: dg_config, E: torch.Tensor, E_t: torch.Tensor, stream=None) -> None:
+    _check("dg_pack_embedding", lib().dg_pack_embedding(ctypes.byref(cfg), _ptr(E), _ptr(E_t),
+                                                        _stream(stream)))
+
+
+def dg_canvas_init(cfg: dg_config, canvas: dg_canvas, seed: int, canvas_id: int, stream=None) -> None:
+    _check("dg_canvas_init", lib().dg_canvas_init(ctypes.byref(cfg), ctypes.byref(canvas), seed,
+                                                  canvas_id, _stream(stream)))
+
+
+def dg_prefill_append(cfg: dg_config, w: dg_weights, cache: dg_kv_cache, tokens: torch.Tensor,
+                      n_tokens: int, attn_out: torch.Tensor | None, ws: torch.Tensor,
+                      stream=None) -> None:
+    _check("dg_prefill_append", lib().dg_prefill_append(
+        ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), _ptr(tokens), n_tokens,
+        _ptr(attn_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dg_denoise_step(cfg: dg_config, w: dg_weights, cache: dg_kv_cache, canvas: dg_canvas,
+                    temperature: float, accept_threshold_nats: float, ws: torch.Tensor,
+                    stream=None) -> None:
+    _check("dg_denoise_step", lib().dg_denoise_step(
+        ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), ctypes.byref(canvas),
+        temperature, accept_threshold_nats, _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def dg_should_stop(cfg: dg_config, canvas: dg_canvas, stable_steps: int, stream=None):
+    stop = c_i32(0)
+    stats = dg_step_stats()
+    _check("dg_should_stop", lib().dg_should_stop(ctypes.byref(cfg), ctypes.byref(canvas),
+                                                  stable_steps, ctypes.byref(stop),
+                                                  ctypes.byref(stats), _stream(stream)))
+    return bool(stop.value), stats
+
+
+def dg_test_ws_offsets(cfg: dg_config) -> dg_ws_offsets:
+    o = dg_ws_offsets()
+    _check("dg_test_ws_offsets", lib().dg_test_ws_offsets(ctypes.byref(cfg), ctypes.byref(o)))
+    return o
+
+
+def dg_test_set_logits_dump(on: bool) -> None:
+    lib().dg_test_set_logits_dump(1 if on else 0)
+
+
+def dg_test_logits_ws_bytes(cfg: dg_config) -> int:
+    return int(lib().dg_test_logits_ws_bytes(ctypes.byref(cfg)))
+
+
+def dg_test_selfcond(cfg: dg_config, w: dg_weights, Pm: torch.Tensor, S: torch.Tensor,
+                     ws: torch.Tensor, stream=None) -> None:
+    _check("dg_test_selfcond", lib().dg_test_selfcond(
+        ctypes.byref(cfg), ctypes.byref(w), _ptr(Pm), _ptr(S), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dg_test_select(cfg: dg_config, canvas: dg_canvas, accept_threshold_nats: float,
+                   stream=None) -> None:
+    _check("dg_test_select", lib().dg_test_select(ctypes.byref(cfg), ctypes.byref(canvas),
+                                                  accept_threshold_nats, _stream(stream)))
+
+
+def dg_test_philox(ctr: torch.Tensor, k0: int, k1: int, out: torch.Tensor, n: int,
+                   stream=None) -> None:
+    _check("dg_test_philox", lib().dg_test_philox(_ptr(ctr), k0, k1, _ptr(out), n, _stream(stream)))
+
+
+def dg_test_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None) -> None:
+    _check("dg_test_copy", lib().dg_test_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def dg_profile_enable(on: bool) -> None:
+    lib().dg_profile_enable(1 if on else 0)
+
+
+def dg_profile_read():
+    a, b = c_f32(0), c_f32(0)
+    na, nb = c_i32(0), c_i32(0)
+    _check("dg_profile_read", lib().dg_profile_read(ctypes.byref(a), ctypes.byref(na),
+                                                    ctypes.byref(b), ctypes.byref(nb)))
+    return a.value, na.value, b.value, nb.value
+
+
+# ---------------------------------------------------------------------------
+# device-side holders (torch allocations wrapped in the C structs)
+# ---------------------------------------------------------------------------
+def make_config(c: dict, accept_rule: int = DG_ACCEPT_SUM_MINUS_MAX,
+                conf_eps: float = 0.005) -> dg_config:
+    return dg_config(c["N"], c["V"], c["d"], c["Hq"], c["Hkv"], c["hd"], c["F"],
+                     DG_BF16 if c["dtype"] == "bf16" else DG_F32, c.get("rms_eps", 1e-6),
+                     conf_eps, accept_rule)
+
+
+def torch_dtype(cfg: dg_config):
+    return torch.bfloat16 if cfg.dtype == DG_BF16 else torch.float32
+
+
+class DeviceWeights:
+    """Moves a workload's weights to the GPU and packs E^T once."""
+
+    def __init__(self, cfg: dg_config, inp: dict, device="cuda", stream=None):
+        dt = torch_dtype(cfg)
+        t = {k: inp[k].to(device=device, dtype=dt).contiguous()
+             for k in ("E", "w1", "w2", "wq", "wk", "wv", "wo", "g_attn", "g_final")}
+        t["E_t"] = torch.empty((cfg.d_model, cfg.vocab), dtype=dt, device=device)
+        dg_pack_embedding(cfg, t["E"], t["E_t"], stream)
+        self.t = t
+        self.s = dg_weights(*(t[k].data_ptr() for k in ("E", "E_t", "w1", "w2", "wq", "wk", "wv",
+                                                        "wo", "g_attn", "g_final")))
+
+
+class DeviceCache:
+    """fp32 [Hkv][capacity][hd] keys and values (both dtypes)."""
+
+    def __init__(self, cfg: dg_config, capacity: int, device="cuda", k_prefix=None, v_prefix=None):
+        dt = torch.float32
+        self.k = torch.zeros((cfg.n_kv_heads, capacity, cfg.head_dim), dtype=dt, device=device)
+        self.v = torch.zeros_like(self.k)
+        L = 0
+        if k_prefix is not None:
+            L = k_prefix.shape[1]
+            self.k[:, :L] = k_prefix.to(device=device, dtype=dt)
+            self.v[:, :L] = v_prefix.to(device=device, dtype=dt)
+        self.s = dg_kv_cache(self.k.data_ptr(), self.v.data_ptr(), L, capacity)
+
+    @property
+    def length(self) -> int:
+        return self.s.length
+
+
+class DeviceCanvas:
+    def __init__(self, cfg: dg_config, device="cuda"):
+        N, V = cfg.canvas_len, cfg.vocab
+        dt = torch_dtype(cfg)
+        self.tokens = torch.zeros(N, dtype=torch.int32, device=device)
+        self.probs = torch.zeros((N, V), dtype=dt, device=device)
+        self.stats = torch.zeros(dg_stats_bytes(cfg), dtype=torch.uint8, device=device)
+        self.entropy = torch.zeros(N, dtype=torch.float32, device=device)
+        self.argmax = torch.zeros(N, dtype=torch.int32, device=device)
+        self.accept = torch.zeros(N, dtype=torch.uint8, device=device)
+        self.status = torch.zeros(DG_STATUS_WORDS, dtype=torch.int32, device=device)
+        self.s = dg_canvas(self.tokens.data_ptr(), self.probs.data_ptr(), self.stats.data_ptr(),
+                           self.entropy.data_ptr(), self.argmax.data_ptr(),
+                           self.accept.data_ptr(), self.status.data_ptr(), 0, 0, 0, 0)
+
+    def tile_scale(self, cfg: dg_config) -> torch.Tensor:
+        """Per-(row, tile) normalisers written by the last step ([N][V/256] f32)."""
+        N, nt = cfg.canvas_len, cfg.vocab // TILE_V
+        return self.stats[N * nt * 16:N * nt * 20].view(torch.float32).view(N, nt)
+
+    def top(self, cfg: dg_config):
+        """Each row's dominant token and its exact probability (last step)."""
+        N, nt = cfg.canvas_len, cfg.vocab // TILE_V
+        t = self.stats[N * nt * 20:N * nt * 20 + N * 8].view(torch.float32).view(N, 2)
+        return t[:, 0].contiguous().view(torch.int32), t[:, 1].contiguous()
+
+
+def workspace(cfg: dg_config, max_prefill: int = 0, device="cuda", logits_dump=False):
+    n = dg_workspace_bytes(cfg, max_prefill)
+    if logits_dump:
+        n = max(n, dg_test_logits_ws_bytes(cfg))
+    if n == 0:
+        raise DgError("dg_workspace_bytes", dg_validate_config(cfg))
+    return torch.empty(n, dtype=torch.uint8, device=device)

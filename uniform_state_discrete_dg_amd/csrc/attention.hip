@@ -1,0 +1,327 @@
+// attention.hip -- attention of canvas (or prompt) queries over the prefix KV
+// cache and the canvas, head_dim 128, on CDNA4 matrix cores.
+//
+// Denoise mode reads every key (bidirectional, no mask); prefill mode masks
+// keys beyond each query's absolute position (causal).  Keys come from two
+// segments, the committed cache [0, nA) and the step's own canvas keys
+// [0, nB), so the cache is never written by a denoising step.
+//
+// Queries, keys and values are fp32 in memory.  While they are staged, each
+// value is split into two bf16 terms (hi + lo), and every product of two
+// split operands is formed from three bf16 MFMAs (hi*hi + hi*lo + lo*hi),
+// which keeps the scores and the output within ~1e-5 of fp32.
+//
+// Flash-style: a workgroup owns 128 queries of one query head (32 per wave)
+// and a contiguous range of keys (split-KV, partial results merged by a
+// second kernel).  64-key tiles of K and V go through LDS.  The wave
+// computes S^T = K Q^T so that each lane ends up holding one query's scores,
+// keeps the running max / sum per lane, and computes O^T = V^T P^T with the
+// probabilities taken straight from registers; V is transposed while it is
+// staged into LDS.  Grouped-query attention maps query head h to KV head
+// h / (Hq / Hkv).
+#include "dg_device.h"
+#include "dg_kernels.h"
+
+namespace dg {
+
+namespace {
+constexpr int HD = 128;
+constexpr int BQ = 128;   // queries per workgroup
+constexpr int KT = 64;    // keys per tile
+constexpr int NTH = 256;  // 4 waves
+constexpr float LOG2E = 1.4426950408889634f;
+}  // namespace
+
+__device__ __forceinline__ int kswz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
+
+__global__ void __launch_bounds__(NTH) attn_split_kernel(AttnArgs a) {
+  __shared__ uint4 Ks[2][KT * HD / 8];     // hi, lo: [64 keys][16 chunks of 8]
+  __shared__ uint2 Vt[2][HD * KT / 4];     // hi, lo: [128 hd][16 units of 4 keys]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 5;
+  const int h = blockIdx.y, z = blockIdx.z;
+  const int g = h / (a.Hq / a.Hkv);
+  const int q = blockIdx.x * BQ + wave * 32 + (lane & 31);
+  const int nk = a.nA + a.nB;
+  const int kbeg = z * a.keys_per_split;
+  const int kend = min(nk, kbeg + a.keys_per_split);
+  const float *Q = static_cast<const float *>(a.q);
+  const float *kA = static_cast<const float *>(a.kA), *vA = static_cast<const float *>(a.vA);
+  const float *kB = static_cast<const float *>(a.kB), *vB = static_cast<const float *>(a.vB);
+
+  // This lane's query fragments (B operand of S^T = K Q^T), hi and lo.
+  bf16x8_t qh[HD / 16], ql[HD / 16];
+#pragma unroll
+  for (int s = 0; s < HD / 16; ++s) {
+    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+    if (q < a.nq) {
+      const float4 *src = reinterpret_cast<const float4 *>(Q + ((int64_t)h * a.nq + q) * HD + s * 16 + g4 * 8);
+      x0 = src[0];
+      x1 = src[1];
+    }
+    uint4 hi, lo;
+    split8(x0, x1, hi, lo);
+    qh[s] = __builtin_bit_cast(bf16x8_t, hi);
+    ql[s] = __builtin_bit_cast(bf16x8_t, lo);
+  }
+
+  const float sc = rsqrtf((float)HD) * LOG2E;
+  const int qlimit = a.causal ? a.q_pos0 + q : INT32_MAX;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16_t oacc[HD / 32];
+#pragma unroll
+  for (int nb = 0; nb < HD / 32; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.f;
+
+  // 64 keys x 128 = 1024 chunks of 8 floats per tile; 4 chunks per thread.
+  float4 rk[4][2], rv[4][2];
+  auto load = [&](int kt0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int idx = tid + t * NTH;
+      const int key = idx >> 4, ch = idx & 15;
+      const int kabs = kt0 + key;
+      float4 k0 = make_float4(0.f, 0.f, 0.f, 0.f), k1 = k0, v0 = k0, v1 = k0;
+      if (kabs < kend) {
+        int64_t off;
+        const float *kp, *vp;
+        if (kabs < a.nA) {
+          off = ((int64_t)g * a.capA + kabs) * HD + ch * 8;
+          kp = kA;
+          vp = vA;
+        } else {
+          off = ((int64_t)g * a.capB + (kabs - a.nA)) * HD + ch * 8;
+          kp = kB;
+          vp = vB;
+        }
+        k0 = *reinterpret_cast<const float4 *>(kp + off);
+        k1 = *reinterpret_cast<const float4 *>(kp + off + 4);
+        v0 = *reinterpret_cast<const float4 *>(vp + off);
+        v1 = *reinterpret_cast<const float4 *>(vp + off + 4);
+      }
+      rk[t][0] = k0;
+      rk[t][1] = k1;
+      rv[t][0] = v0;
+      rv[t][1] = v1;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int idx = tid + t * NTH;
+      const int key = idx >> 4, ch = idx & 15;
+      uint4 hi, lo;
+      split8(rk[t][0], rk[t][1], hi, lo);
+      Ks[0][kswz(key, ch)] = hi;
+      Ks[1][kswz(key, ch)] = lo;
+      split8(rv[t][0], rv[t][1], hi, lo);
+      const uint32_t wh[4] = {hi.x, hi.y, hi.z, hi.w}, wl[4] = {lo.x, lo.y, lo.z, lo.w};
+      bf16 *vth = reinterpret_cast<bf16 *>(Vt[0]);
+      bf16 *vtl = reinterpret_cast<bf16 *>(Vt[1]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int hd = ch * 8 + e;
+        const int pos = hd * KT + (((key >> 2) ^ (hd & 15)) << 2) + (key & 3);
+        vth[pos] = (bf16)((e & 1) ? (wh[e >> 1] >> 16) : (wh[e >> 1] & 0xffffu));
+        vtl[pos] = (bf16)((e & 1) ? (wl[e >> 1] >> 16) : (wl[e >> 1] & 0xffffu));
+      }
+    }
+  };
+
+  if (kbeg < kend) {
+    load(kbeg);
+    store();
+    __syncthreads();
+  }
+  for (int kt0 = kbeg; kt0 < kend; kt0 += KT) {
+    const bool more = kt0 + KT < kend;
+    if (more) load(kt0 + KT);
+
+    // S^T for two 32-key blocks: K_hi Q_hi + K_lo Q_hi + K_hi Q_lo.
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[b][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < HD / 16; ++s) {
+        const int li = kswz(b * 32 + (lane & 31), 2 * s + g4);
+        const bf16x8_t kh = __builtin_bit_cast(bf16x8_t, Ks[0][li]);
+        const bf16x8_t kl = __builtin_bit_cast(bf16x8_t, Ks[1][li]);
+        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[s], sacc[b], 0, 0, 0);
+        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[s], sacc[b], 0, 0, 0);
+        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[s], sacc[b], 0, 0, 0);
+      }
+    }
+    // mask, scale, running max
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kabs = kt0 + b * 32 + (r & 3) + 4 * g4 + 8 * (r >> 2);
+        float v = sacc[b][r] * sc;
+        if (kabs >= kend || kabs > qlimit) v = -INFINITY;
+        sacc[b][r] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = (m_new == -INFINITY) ? 0.f : exp2f(sacc[b][r] - m_new);
+        sacc[b][r] = p;
+        psum += p;
+      }
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int nb = 0; nb < HD / 32; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
+
+    // O^T += V^T P^T over the four 16-key steps of the tile (3 products each).
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint4 ph4, pl4;
+        split8(make_float4(sacc[b][8 * hh + 0], sacc[b][8 * hh + 1], sacc[b][8 * hh + 2], sacc[b][8 * hh + 3]),
+               make_float4(sacc[b][8 * hh + 4], sacc[b][8 * hh + 5], sacc[b][8 * hh + 6], sacc[b][8 * hh + 7]),
+               ph4, pl4);
+        const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, ph4);
+        const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, pl4);
+        const int u1 = 8 * b + 4 * hh + g4, u2 = u1 + 2;
+#pragma unroll
+        for (int nb = 0; nb < HD / 32; ++nb) {
+          const int hd = nb * 32 + (lane & 31);
+          const int i1 = hd * 16 + (u1 ^ (hd & 15)), i2 = hd * 16 + (u2 ^ (hd & 15));
+          const uint2 a1 = Vt[0][i1], a2 = Vt[0][i2], b1 = Vt[1][i1], b2 = Vt[1][i2];
+          const bf16x8_t vh = __builtin_bit_cast(bf16x8_t, make_uint4(a1.x, a1.y, a2.x, a2.y));
+          const bf16x8_t vl = __builtin_bit_cast(bf16x8_t, make_uint4(b1.x, b1.y, b2.x, b2.y));
+          oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, ph, oacc[nb], 0, 0, 0);
+          oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pl, oacc[nb], 0, 0, 0);
+          oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, ph, oacc[nb], 0, 0, 0);
+        }
+      }
+    __syncthreads();
+    if (more) {
+      store();
+      __syncthreads();
+    }
+  }
+
+  if (q < a.nq) {
+    float *po = a.part_o + (((int64_t)z * a.Hq + h) * a.nq + q) * HD;
+#pragma unroll
+    for (int nb = 0; nb < HD / 32; ++nb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int hd = nb * 32 + 4 * g4 + 8 * rr;
+        *reinterpret_cast<float4 *>(po + hd) =
+            make_float4(oacc[nb][4 * rr], oacc[nb][4 * rr + 1], oacc[nb][4 * rr + 2], oacc[nb][4 * rr + 3]);
+      }
+    if (g4 == 0) {
+      float *pml = a.part_ml + (((int64_t)z * a.Hq + h) * a.nq + q) * 2;
+      pml[0] = m_run;
+      pml[1] = l_run;
+    }
+  }
+}
+
+// Merge of the split-KV partial results (both dtypes).
+template <typename T>
+__global__ void attn_combine_kernel(const float *__restrict__ part_o, const float *__restrict__ part_ml,
+                                    int splits, int nq, int Hq, int hd, T *__restrict__ out) {
+  const int qh = blockIdx.x;
+  const int q = qh / Hq, h = qh % Hq;
+  const int e = threadIdx.x;
+  float M = -INFINITY;
+  for (int z = 0; z < splits; ++z) M = fmaxf(M, part_ml[(((int64_t)z * Hq + h) * nq + q) * 2]);
+  float num = 0.f, den = 0.f;
+  for (int z = 0; z < splits; ++z) {
+    const float m = part_ml[(((int64_t)z * Hq + h) * nq + q) * 2];
+    const float l = part_ml[(((int64_t)z * Hq + h) * nq + q) * 2 + 1];
+    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    den += w * l;
+    if (e < hd) num += w * part_o[(((int64_t)z * Hq + h) * nq + q) * hd + e];
+  }
+  if (e < hd) Elem<T>::store(out, (int64_t)q * Hq * hd + (int64_t)h * hd + e, num / den);
+}
+
+void attention_plan(int nq, int Hq, int nk, int *splits, int *keys_per_split) {
+  const int qb = (nq + BQ - 1) / BQ;
+  int want = (512 + qb * Hq - 1) / (qb * Hq);  // aim for ~2 workgroups per CU
+  const int max_splits = (nk + KT - 1) / KT;
+  if (want > max_splits) want = max_splits;
+  if (want < 1) want = 1;
+  int kps = (nk + want - 1) / want;
+  kps = (kps + KT - 1) / KT * KT;
+  if (kps < KT) kps = KT;
+  *keys_per_split = kps;
+  *splits = (nk + kps - 1) / kps;
+  if (*splits < 1) *splits = 1;
+}
+
+hipError_t attention_mfma(const AttnArgs &a, hipStream_t s) {
+  dim3 grid((a.nq + BQ - 1) / BQ, a.Hq, a.splits);
+  hipLaunchKernelGGL(attn_split_kernel, grid, dim3(NTH), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(attn_combine_kernel<float>, dim3(a.nq * a.Hq), dim3(HD), 0, s, a.part_o,
+                     a.part_ml, a.splits, a.nq, a.Hq, HD, static_cast<float *>(a.out));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path (small head dims): one thread per (query, head), online softmax.
+// ---------------------------------------------------------------------------
+__global__ void attn_f32_kernel(AttnArgs a) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.nq * a.Hq) return;
+  const int q = t / a.Hq, h = t % a.Hq;
+  const int g = h / (a.Hq / a.Hkv);
+  const int hd = a.hd;
+  const float *Q = static_cast<const float *>(a.q) + ((int64_t)h * a.nq + q) * hd;
+  const int nk = a.nA + a.nB;
+  const int lim = a.causal ? min(nk, a.q_pos0 + q + 1) : nk;
+  const float scale = rsqrtf((float)hd);
+  float acc[128];
+  for (int e = 0; e < hd; ++e) acc[e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j < lim; ++j) {
+    const float *kp, *vp;
+    if (j < a.nA) {
+      kp = static_cast<const float *>(a.kA) + ((int64_t)g * a.capA + j) * hd;
+      vp = static_cast<const float *>(a.vA) + ((int64_t)g * a.capA + j) * hd;
+    } else {
+      kp = static_cast<const float *>(a.kB) + ((int64_t)g * a.capB + (j - a.nA)) * hd;
+      vp = static_cast<const float *>(a.vB) + ((int64_t)g * a.capB + (j - a.nA)) * hd;
+    }
+    float s = 0.f;
+    for (int e = 0; e < hd; ++e) s = fmaf(Q[e], kp[e], s);
+    s *= scale;
+    const float mn = fmaxf(m, s);
+    const float al = expf(m - mn);
+    const float p = expf(s - mn);
+    l = l * al + p;
+    for (int e = 0; e < hd; ++e) acc[e] = acc[e] * al + p * vp[e];
+    m = mn;
+  }
+  float *o = static_cast<float *>(a.out) + (int64_t)q * a.Hq * hd + (int64_t)h * hd;
+  for (int e = 0; e < hd; ++e) o[e] = acc[e] / l;
+}
+
+hipError_t attention_f32(const AttnArgs &a, hipStream_t s) {
+  const int n = a.nq * a.Hq;
+  hipLaunchKernelGGL(attn_f32_kernel, dim3((n + 63) / 64), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dg

@@ -1,0 +1,574 @@
+// dg_api.cpp -- the C ABI of libdgdenoise (declared in include/dgdenoise.h):
+// host-side validation, workspace carving and the launch sequence of one
+// denoising step / one prefill append.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "dg_kernels.h"
+#include "dgdenoise.h"
+
+using dg::bf16;
+
+namespace {
+
+constexpr int kTile = 256;  // vocabulary columns per softmax-statistics tile
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+int ilog2(int64_t v) {
+  int b = 0;
+  while ((int64_t(1) << b) < v) ++b;
+  return b;
+}
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+size_t dsize(const dg_config *c) { return c->dtype == DG_BF16 ? 2 : 4; }
+
+dg_status check_config(const dg_config *c) {
+  if (!c) return DG_ERR_INVALID_ARG;
+  if (c->dtype != DG_F32 && c->dtype != DG_BF16) return DG_ERR_INVALID_ARG;
+  if (c->accept_rule != DG_ACCEPT_SUM_MINUS_MAX && c->accept_rule != DG_ACCEPT_CUMSUM)
+    return DG_ERR_INVALID_ARG;
+  if (c->canvas_len < 1 || c->vocab < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
+      c->head_dim < 1 || c->ffn_hidden < 1)
+    return DG_ERR_INVALID_ARG;
+  if (!(std::isfinite(c->rms_eps) && c->rms_eps >= 0.f) || !std::isfinite(c->conf_eps))
+    return DG_ERR_INVALID_ARG;
+  if (c->canvas_len > 256) return DG_ERR_UNSUPPORTED;
+  if (!is_pow2(c->vocab) || c->vocab < kTile || c->vocab > (1 << 24)) return DG_ERR_UNSUPPORTED;
+  if (c->n_q_heads % c->n_kv_heads != 0) return DG_ERR_UNSUPPORTED;
+  if (c->dtype == DG_BF16) {
+    if (c->head_dim != 128 || c->d_model % 64 != 0 || c->ffn_hidden % 64 != 0) return DG_ERR_UNSUPPORTED;
+  } else {
+    if (c->head_dim > 128) return DG_ERR_UNSUPPORTED;
+  }
+  return DG_OK;
+}
+
+// Self-conditioning split of K = V over workgroups (bf16 path).
+int selfcond_ksplit(const dg_config *c) {
+  const int bm = c->canvas_len <= 128 ? 128 : 256;
+  const int ntile = (c->d_model + 255) / 256 * ((c->canvas_len + bm - 1) / bm);
+  int ks = 256 / ntile;
+  if (ks < 1) ks = 1;
+  const int slices = c->vocab / 64;
+  if (ks > slices) ks = slices;
+  return ks;
+}
+
+struct Layout {
+  size_t h0, h1, nrm, nrm16, sc, g, q, kc, vc, o, ap_o, ap_ml, sc_part, logits, total;
+  // prefill view (same region)
+  size_t p_x, p_nrm, p_q, p_ap_o, p_ap_ml, p_total;
+};
+
+// Activations are fp32 in the workspace for both dtypes (the bf16 path
+// feeds them to the matrix cores as split bf16 pairs); nrm16 is the bf16
+// copy of the final normalised state used by the LM head.
+Layout layout(const dg_config *c, int32_t nprefill, bool with_logits) {
+  Layout L{};
+  const size_t N = c->canvas_len, V = c->vocab, d = c->d_model, F = c->ffn_hidden;
+  const size_t Hq = c->n_q_heads, Hkv = c->n_kv_heads, hd = c->head_dim;
+  const bool bf = c->dtype == DG_BF16;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  L.h0 = take(N * d * 4);
+  L.h1 = take(N * d * 4);
+  L.nrm = take(N * d * 4);
+  L.nrm16 = take(bf ? N * d * 2 : 0);
+  L.sc = take(N * d * 4);
+  L.g = take(N * F * 4);
+  L.q = take(Hq * N * hd * 4);
+  L.kc = take(Hkv * N * hd * 4);
+  L.vc = take(Hkv * N * hd * 4);
+  L.o = take(N * Hq * hd * 4);
+  int splits = 1, kps = 0;
+  // the plan for any key count never uses more splits than for 2^20 keys
+  dg::attention_plan((int)N, (int)Hq, 1 << 20, &splits, &kps);
+  L.ap_o = take((size_t)splits * Hq * N * hd * 4);
+  L.ap_ml = take((size_t)splits * Hq * N * 2 * 4);
+  L.sc_part = take(bf ? (size_t)selfcond_ksplit(c) * N * d * 4 : 0);
+  L.logits = take((!bf || with_logits) ? N * V * 4 : 0);
+  L.total = off;
+  // prefill
+  off = 0;
+  const size_t n = nprefill > 0 ? (size_t)nprefill : 0;
+  L.p_x = take(n * d * 4);
+  L.p_nrm = take(n * d * 4);
+  L.p_q = take(Hq * n * hd * 4);
+  dg::attention_plan((int)(n ? n : 1), (int)Hq, 1 << 20, &splits, &kps);
+  L.p_ap_o = take((size_t)splits * Hq * n * hd * 4);
+  L.p_ap_ml = take((size_t)splits * Hq * n * 2 * 4);
+  L.p_total = off;
+  return L;
+}
+
+bool g_logits_dump = false;
+
+// profiling (events around the two E-streaming contractions)
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_prof_lm, g_prof_sc;
+
+struct ProfScope {
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> *vec = nullptr;
+  hipEvent_t e0{}, e1{};
+  hipStream_t s;
+  ProfScope(std::vector<std::pair<hipEvent_t, hipEvent_t>> &v, hipStream_t st) : s(st) {
+    if (!g_prof_on) return;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return;
+    vec = &v;
+    (void)hipEventRecord(e0, s);
+  }
+  ~ProfScope() {
+    if (!vec) return;
+    (void)hipEventRecord(e1, s);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    vec->emplace_back(e0, e1);
+  }
+};
+
+#define DG_TRY(x)                                  \
+  do {                                             \
+    if ((x) != hipSuccess) return DG_ERR_HIP;      \
+  } while (0)
+
+dg::Epi epi_store(void *out, bool f32, int64_t rstride, int cdiv, int64_t chi) {
+  dg::Epi e{};
+  e.kind = dg::EPI_STORE;
+  e.out = out;
+  e.out_f32 = f32 ? 1 : 0;
+  e.rstride = rstride;
+  e.cdiv = cdiv;
+  e.chi = chi;
+  return e;
+}
+
+bool weights_ok(const dg_config *c, const dg_weights *w) {
+  if (!w || !w->E || !w->w_sc1 || !w->w_sc2 || !w->wq || !w->wk || !w->wv || !w->wo || !w->g_attn ||
+      !w->g_final)
+    return false;
+  if (c->dtype == DG_BF16 && !w->E_t) return false;
+  return true;
+}
+
+bool canvas_ok(const dg_canvas *cv) {
+  return cv && cv->tokens && cv->probs && cv->stats && cv->entropy && cv->argmax && cv->accept && cv->status;
+}
+
+// Dense projections C_i[M][N_i] = A[M][K] W_i[N_i][K]^T (fp32 activation A,
+// up to three weight matrices sharing it) with epilogues e_i.
+hipError_t proj(const dg_config *c, const float *A, int64_t lda, int M, int K, int count, const void *const *W,
+                const int *Nout, const dg::Epi *e, hipStream_t s) {
+  if (c->dtype == DG_BF16) {
+    dg::SplitGemm g{};
+    g.A = A;
+    g.lda = lda;
+    g.M = M;
+    g.K = K;
+    g.count = count;
+    for (int i = 0; i < count; ++i) {
+      g.B[i] = W[i];
+      g.N[i] = Nout[i];
+      g.e[i] = e[i];
+    }
+    return dg::gemm_split(g, s);
+  }
+  for (int i = 0; i < count; ++i) {
+    dg::GemmShapeF32 g{A, lda, 1, static_cast<const float *>(W[i]), K, 1, M, Nout[i], K, nullptr, 0};
+    const hipError_t err = dg::gemm_f32(g, e[i], s);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t proj1(const dg_config *c, const float *A, int64_t lda, int M, int K, const void *W, int Nout,
+                 const dg::Epi &e, hipStream_t s) {
+  return proj(c, A, lda, M, K, 1, &W, &Nout, &e, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dg_abi_version(void) { return DG_ABI_VERSION; }
+
+const char *dg_status_string(dg_status s) {
+  switch (s) {
+    case DG_OK: return "ok";
+    case DG_ERR_INVALID_ARG: return "invalid argument";
+    case DG_ERR_UNSUPPORTED: return "unsupported shape or configuration";
+    case DG_ERR_CAPACITY: return "KV cache capacity exceeded";
+    case DG_ERR_WORKSPACE: return "workspace too small";
+    case DG_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+dg_status dg_validate_config(const dg_config *cfg) { return check_config(cfg); }
+
+size_t dg_workspace_bytes(const dg_config *cfg, int32_t max_prefill_tokens) {
+  if (check_config(cfg) != DG_OK || max_prefill_tokens < 0) return 0;
+  const Layout L = layout(cfg, max_prefill_tokens, false);
+  return L.total > L.p_total ? L.total : L.p_total;
+}
+
+size_t dg_stats_bytes(const dg_config *cfg) {
+  if (check_config(cfg) != DG_OK) return 0;
+  const size_t nt = (size_t)cfg->vocab / kTile;
+  return (size_t)cfg->canvas_len * (nt * (sizeof(float4) + sizeof(float)) + sizeof(float2));
+}
+
+dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_t, void *stream) {
+  dg_status st = check_config(cfg);
+  if (st != DG_OK) return st;
+  if (!E || !E_t) return DG_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cfg->dtype == DG_BF16)
+    DG_TRY(dg::transpose<bf16>(static_cast<const bf16 *>(E), cfg->vocab, cfg->d_model, static_cast<bf16 *>(E_t), s));
+  else
+    DG_TRY(dg::transpose<float>(static_cast<const float *>(E), cfg->vocab, cfg->d_model,
+                                static_cast<float *>(E_t), s));
+  return DG_OK;
+}
+
+dg_status dg_canvas_init(const dg_config *cfg, dg_canvas *cv, uint64_t seed, uint32_t canvas_id, void *stream) {
+  dg_status st = check_config(cfg);
+  if (st != DG_OK) return st;
+  if (!canvas_ok(cv)) return DG_ERR_INVALID_ARG;
+  DG_TRY(dg::canvas_init(cv->tokens, cv->status, cfg->canvas_len, ilog2(cfg->vocab), seed, canvas_id,
+                         static_cast<hipStream_t>(stream)));
+  cv->step = 0;
+  cv->has_prev = 0;
+  cv->seed = seed;
+  cv->canvas_id = canvas_id;
+  return DG_OK;
+}
+
+dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cache *cache, const int32_t *tokens,
+                            int32_t n_tokens, void *attn_out, void *ws, size_t ws_bytes, void *stream) {
+  dg_status st = check_config(cfg);
+  if (st != DG_OK) return st;
+  if (!weights_ok(cfg, w) || !cache || !cache->k || !cache->v || n_tokens < 0) return DG_ERR_INVALID_ARG;
+  if (cache->length < 0 || cache->capacity < 0 || cache->length > cache->capacity) return DG_ERR_INVALID_ARG;
+  if (n_tokens > 0 && !tokens) return DG_ERR_INVALID_ARG;
+  if ((int64_t)cache->length + n_tokens > cache->capacity) return DG_ERR_CAPACITY;
+  if (n_tokens == 0) return DG_OK;
+  const Layout L = layout(cfg, n_tokens, false);
+  if (!ws || ws_bytes < L.p_total) return DG_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int n = n_tokens, d = cfg->d_model, Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads, hd = cfg->head_dim;
+  const int V = cfg->vocab, cap = cache->capacity, Lp = cache->length;
+  const bool bf = cfg->dtype == DG_BF16;
+  char *base = static_cast<char *>(ws);
+  float *x = reinterpret_cast<float *>(base + L.p_x);
+  float *nrm = reinterpret_cast<float *>(base + L.p_nrm);
+
+  if (bf) {
+    DG_TRY(dg::gather_rows<bf16>(static_cast<const bf16 *>(w->E), tokens, n, d, V, x, s));
+    DG_TRY(dg::rmsnorm_rows<bf16>(x, static_cast<const bf16 *>(w->g_attn), n, d, cfg->rms_eps, nrm, nullptr, s));
+  } else {
+    DG_TRY(dg::gather_rows<float>(static_cast<const float *>(w->E), tokens, n, d, V, x, s));
+    DG_TRY(dg::rmsnorm_rows<float>(x, static_cast<const float *>(w->g_attn), n, d, cfg->rms_eps, nrm, nullptr, s));
+  }
+  // keys/values of the new tokens straight into the (fp32) cache at [length, length+n)
+  float *kbase = static_cast<float *>(cache->k) + (size_t)Lp * hd;
+  float *vbase = static_cast<float *>(cache->v) + (size_t)Lp * hd;
+  float *q = reinterpret_cast<float *>(base + L.p_q);
+  const void *W[3] = {w->wk, w->wv, w->wq};
+  const int No[3] = {Hkv * hd, Hkv * hd, Hq * hd};
+  const dg::Epi E3[3] = {epi_store(kbase, true, hd, hd, (int64_t)cap * hd),
+                         epi_store(vbase, true, hd, hd, (int64_t)cap * hd),
+                         epi_store(q, true, hd, hd, (int64_t)n * hd)};
+  DG_TRY(proj(cfg, nrm, d, n, d, attn_out ? 3 : 2, W, No, E3, s));
+  if (attn_out) {
+    dg::AttnArgs a{};
+    a.q = q;
+    a.nq = n;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.hd = hd;
+    a.kA = cache->k;
+    a.vA = cache->v;
+    a.nA = Lp + n;
+    a.capA = cap;
+    a.kB = nullptr;
+    a.vB = nullptr;
+    a.nB = 0;
+    a.capB = 0;
+    a.causal = 1;
+    a.q_pos0 = Lp;
+    a.out = attn_out;
+    a.part_o = reinterpret_cast<float *>(base + L.p_ap_o);
+    a.part_ml = reinterpret_cast<float *>(base + L.p_ap_ml);
+    dg::attention_plan(n, Hq, Lp + n, &a.splits, &a.keys_per_split);
+    DG_TRY(bf ? dg::attention_mfma(a, s) : dg::attention_f32(a, s));
+  }
+  cache->length = Lp + n;
+  return DG_OK;
+}
+
+static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache, dg_canvas *cv,
+                              float temperature, float gamma, void *ws, size_t ws_bytes, void *stream,
+                              bool logits_dump) {
+  dg_status st = check_config(cfg);
+  if (st != DG_OK) return st;
+  if (!weights_ok(cfg, w) || !cache || !cache->k || !cache->v || !canvas_ok(cv)) return DG_ERR_INVALID_ARG;
+  if (cache->length < 0 || cache->length > cache->capacity) return DG_ERR_INVALID_ARG;
+  if (!(std::isfinite(temperature) && temperature > 0.f)) return DG_ERR_INVALID_ARG;
+  if (std::isnan(gamma) || gamma < 0.f) return DG_ERR_INVALID_ARG;
+  if (cv->step < 0) return DG_ERR_INVALID_ARG;
+  const bool bf = cfg->dtype == DG_BF16;
+  const bool dump = logits_dump && bf;
+  const Layout L = layout(cfg, 0, dump);
+  if (!ws || ws_bytes < L.total) return DG_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int N = cfg->canvas_len, V = cfg->vocab, d = cfg->d_model, F = cfg->ffn_hidden;
+  const int Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads, hd = cfg->head_dim;
+  const int ntiles = V / kTile;
+  const float inv_T = 1.0f / temperature;
+  char *base = static_cast<char *>(ws);
+  float *h0 = reinterpret_cast<float *>(base + L.h0);
+  float *h1 = reinterpret_cast<float *>(base + L.h1);
+  float *nrm = reinterpret_cast<float *>(base + L.nrm);
+  bf16 *nrm16 = reinterpret_cast<bf16 *>(base + L.nrm16);
+  float *sc = reinterpret_cast<float *>(base + L.sc), *G = reinterpret_cast<float *>(base + L.g);
+  float *q = reinterpret_cast<float *>(base + L.q), *kc = reinterpret_cast<float *>(base + L.kc);
+  float *vc = reinterpret_cast<float *>(base + L.vc), *o = reinterpret_cast<float *>(base + L.o);
+  char *stats = static_cast<char *>(cv->stats);
+  float4 *tstats = reinterpret_cast<float4 *>(stats);
+  float *tscale = reinterpret_cast<float *>(stats + (size_t)N * ntiles * sizeof(float4));
+  float2 *top = reinterpret_cast<float2 *>(stats + (size_t)N * ntiles * (sizeof(float4) + sizeof(float)));
+
+  // 1. embeddings (+ self-conditioning from the previous step's probabilities)
+  if (bf)
+    DG_TRY(dg::gather_rows<bf16>(static_cast<const bf16 *>(w->E), cv->tokens, N, d, V, h0, s));
+  else
+    DG_TRY(dg::gather_rows<float>(static_cast<const float *>(w->E), cv->tokens, N, d, V, h0, s));
+  if (cv->has_prev) {
+    if (bf) {
+      const int ks = selfcond_ksplit(cfg);
+      float *part = reinterpret_cast<float *>(base + L.sc_part);
+      dg::GemmShape g{cv->probs, V, w->E_t, V, N, d, V, tscale, ntiles};
+      {
+        ProfScope ps(g_prof_sc, s);
+        DG_TRY(dg::selfcond_bf16(g, part, ks, s));
+      }
+      DG_TRY(dg::selfcond_reduce(part, ks, N, d, top, static_cast<const uint16_t *>(cv->probs), tscale, ntiles, V,
+                                 static_cast<const uint16_t *>(w->E), sc, s));
+    } else {
+      dg::GemmShapeF32 g{static_cast<const float *>(cv->probs), V, 1, static_cast<const float *>(w->E), 1, d,
+                         N, d, V, tscale, ntiles};
+      DG_TRY(dg::gemm_f32(g, epi_store(sc, true, d, d, 0), s));
+    }
+    dg::Epi eg = epi_store(G, true, F, F, 0);
+    eg.kind = dg::EPI_GELU;
+    DG_TRY(proj1(cfg, sc, d, N, d, w->w_sc1, F, eg, s));
+    dg::Epi ea = epi_store(h0, true, d, d, 0);
+    ea.kind = dg::EPI_ADD;
+    ea.resid = h0;
+    DG_TRY(proj1(cfg, G, F, N, F, w->w_sc2, d, ea, s));
+  }
+  // 2. RMSNorm, Q/K/V of the canvas (the canvas keys stay in the workspace)
+  if (bf)
+    DG_TRY(dg::rmsnorm_rows<bf16>(h0, static_cast<const bf16 *>(w->g_attn), N, d, cfg->rms_eps, nrm, nullptr, s));
+  else
+    DG_TRY(dg::rmsnorm_rows<float>(h0, static_cast<const float *>(w->g_attn), N, d, cfg->rms_eps, nrm, nullptr, s));
+  {
+    const void *W[3] = {w->wq, w->wk, w->wv};
+    const int No[3] = {Hq * hd, Hkv * hd, Hkv * hd};
+    const dg::Epi E3[3] = {epi_store(q, true, hd, hd, (int64_t)N * hd), epi_store(kc, true, hd, hd, (int64_t)N * hd),
+                           epi_store(vc, true, hd, hd, (int64_t)N * hd)};
+    DG_TRY(proj(cfg, nrm, d, N, d, 3, W, No, E3, s));
+  }
+  // 3. bidirectional attention over [cache || canvas], output projection
+  dg::AttnArgs a{};
+  a.q = q;
+  a.nq = N;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.hd = hd;
+  a.kA = cache->k;
+  a.vA = cache->v;
+  a.nA = cache->length;
+  a.capA = cache->capacity;
+  a.kB = kc;
+  a.vB = vc;
+  a.nB = N;
+  a.capB = N;
+  a.causal = 0;
+  a.q_pos0 = 0;
+  a.out = o;
+  a.part_o = reinterpret_cast<float *>(base + L.ap_o);
+  a.part_ml = reinterpret_cast<float *>(base + L.ap_ml);
+  dg::attention_plan(N, Hq, cache->length + N, &a.splits, &a.keys_per_split);
+  DG_TRY(bf ? dg::attention_mfma(a, s) : dg::attention_f32(a, s));
+  {
+    dg::Epi ea = epi_store(h1, true, d, d, 0);
+    ea.kind = dg::EPI_ADD;
+    ea.resid = h0;
+    DG_TRY(proj1(cfg, o, Hq * hd, N, Hq * hd, w->wo, d, ea, s));
+  }
+  // 4. final RMSNorm, tied LM head with the softmax/entropy statistics
+  float *logits = reinterpret_cast<float *>(base + L.logits);
+  if (bf) {
+    DG_TRY(dg::rmsnorm_rows<bf16>(h1, static_cast<const bf16 *>(w->g_final), N, d, cfg->rms_eps, nrm, nrm16, s));
+    {
+      ProfScope ps(g_prof_lm, s);
+      DG_TRY(dg::lm_head_bf16(nrm16, N, d, static_cast<const uint16_t *>(w->E), V, inv_T,
+                              static_cast<uint16_t *>(cv->probs), tstats, dump ? logits : nullptr, s));
+    }
+    DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, tscale, nrm,
+                           static_cast<const uint16_t *>(w->E), d, top, s));
+  } else {
+    DG_TRY(dg::rmsnorm_rows<float>(h1, static_cast<const float *>(w->g_final), N, d, cfg->rms_eps, nrm, nullptr, s));
+    dg::GemmShapeF32 g{nrm, d, 1, static_cast<const float *>(w->E), d, 1, N, V, d, nullptr, 0};
+    DG_TRY(dg::gemm_f32(g, epi_store(logits, true, V, V, 0), s));
+    DG_TRY(dg::tile_stats_f32(logits, N, V, inv_T, static_cast<float *>(cv->probs), tstats, s));
+    DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, tscale, nullptr, nullptr, d, top, s));
+  }
+  // 5. accept / re-noise / stop flags
+  DG_TRY(dg::select_step(cv->entropy, cv->argmax, cv->tokens, cv->accept, cv->status, N, ilog2(V), (double)gamma,
+                         (int)cfg->accept_rule, cfg->conf_eps, cv->seed, cv->canvas_id, (uint32_t)cv->step, s));
+  cv->step += 1;
+  cv->has_prev = 1;
+  return DG_OK;
+}
+
+dg_status dg_denoise_step(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache, dg_canvas *cv,
+                          float temperature, float accept_threshold_nats, void *ws, size_t ws_bytes, void *stream) {
+  return denoise_impl(cfg, w, cache, cv, temperature, accept_threshold_nats, ws, ws_bytes, stream, g_logits_dump);
+}
+
+dg_status dg_should_stop(const dg_config *cfg, const dg_canvas *cv, int32_t stable_steps, int32_t *stop_host,
+                         dg_step_stats *stats_host, void *stream) {
+  dg_status st = check_config(cfg);
+  if (st != DG_OK) return st;
+  if (!canvas_ok(cv) || !stop_host) return DG_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t w[DG_STATUS_WORDS];
+  DG_TRY(hipMemcpyAsync(w, cv->status, sizeof(w), hipMemcpyDeviceToHost, s));
+  DG_TRY(hipStreamSynchronize(s));
+  int32_t stop = w[DG_ST_ALLCONF] ? 1 : 0;
+  if (stable_steps > 0 && w[DG_ST_STABLE] >= stable_steps) stop = 1;
+  *stop_host = stop;
+  if (stats_host) {
+    stats_host->accepted = w[DG_ST_ACCEPTED];
+    stats_host->stable = w[DG_ST_STABLE];
+    stats_host->allconf = w[DG_ST_ALLCONF];
+    stats_host->changed = w[DG_ST_CHANGED];
+    float f;
+    std::memcpy(&f, &w[DG_ST_HMIN], 4);
+    stats_host->h_min = f;
+    std::memcpy(&f, &w[DG_ST_HMEAN], 4);
+    stats_host->h_mean = f;
+    std::memcpy(&f, &w[DG_ST_HMAX], 4);
+    stats_host->h_max = f;
+  }
+  return DG_OK;
+}
+
+// ---- test and measurement exports --------------------------------------------
+dg_status dg_test_ws_offsets(const dg_config *cfg, dg_ws_offsets *out) {
+  dg_status st = check_config(cfg);
+  if (st != DG_OK) return st;
+  if (!out) return DG_ERR_INVALID_ARG;
+  const Layout L = layout(cfg, 0, true);
+  out->h0 = L.h0;
+  out->attn = L.o;
+  out->h1 = L.h1;
+  out->selfcond = L.sc;
+  out->logits = L.logits;
+  return DG_OK;
+}
+
+void dg_test_set_logits_dump(int32_t on) { g_logits_dump = on != 0; }
+
+size_t dg_test_logits_ws_bytes(const dg_config *cfg) {
+  if (check_config(cfg) != DG_OK) return 0;
+  return layout(cfg, 0, true).total;
+}
+
+dg_status dg_test_selfcond(const dg_config *cfg, const dg_weights *w, const void *P, void *S, void *ws,
+                           size_t ws_bytes, void *stream) {
+  dg_status st = check_config(cfg);
+  if (st != DG_OK) return st;
+  if (!weights_ok(cfg, w) || !P || !S) return DG_ERR_INVALID_ARG;
+  const Layout L = layout(cfg, 0, false);
+  if (!ws || ws_bytes < L.total) return DG_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int N = cfg->canvas_len, V = cfg->vocab, d = cfg->d_model;
+  if (cfg->dtype == DG_BF16) {
+    const int ks = selfcond_ksplit(cfg);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + L.sc_part);
+    dg::GemmShape g{P, V, w->E_t, V, N, d, V, nullptr, 0};
+    DG_TRY(dg::selfcond_bf16(g, part, ks, s));
+    DG_TRY(dg::selfcond_reduce(part, ks, N, d, nullptr, nullptr, nullptr, 0, V, nullptr, static_cast<float *>(S), s));
+  } else {
+    dg::GemmShapeF32 g{static_cast<const float *>(P), V, 1, static_cast<const float *>(w->E), 1, d, N, d, V,
+                       nullptr, 0};
+    DG_TRY(dg::gemm_f32(g, epi_store(S, true, d, d, 0), s));
+  }
+  return DG_OK;
+}
+
+dg_status dg_test_select(const dg_config *cfg, dg_canvas *cv, float gamma, void *stream) {
+  dg_status st = check_config(cfg);
+  if (st != DG_OK) return st;
+  if (!canvas_ok(cv) || std::isnan(gamma) || gamma < 0.f || cv->step < 0) return DG_ERR_INVALID_ARG;
+  DG_TRY(dg::select_step(cv->entropy, cv->argmax, cv->tokens, cv->accept, cv->status, cfg->canvas_len,
+                         ilog2(cfg->vocab), (double)gamma, (int)cfg->accept_rule, cfg->conf_eps, cv->seed,
+                         cv->canvas_id, (uint32_t)cv->step, static_cast<hipStream_t>(stream)));
+  return DG_OK;
+}
+
+dg_status dg_test_philox(const uint32_t *ctr, uint32_t k0, uint32_t k1, uint32_t *out, int32_t n, void *stream) {
+  if (n < 0 || (n > 0 && (!ctr || !out))) return DG_ERR_INVALID_ARG;
+  DG_TRY(dg::philox_test(ctr, k0, k1, out, n, static_cast<hipStream_t>(stream)));
+  return DG_OK;
+}
+
+dg_status dg_test_copy(const void *src, void *dst, size_t bytes, void *stream) {
+  if (!src || !dst || bytes % 16 != 0) return DG_ERR_INVALID_ARG;
+  DG_TRY(dg::copy_bytes(src, dst, bytes, static_cast<hipStream_t>(stream)));
+  return DG_OK;
+}
+
+void dg_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+}
+
+dg_status dg_profile_read(float *lm_ms, int32_t *lm_n, float *sc_ms, int32_t *sc_n) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  auto drain = [](std::vector<std::pair<hipEvent_t, hipEvent_t>> &v, float *ms, int32_t *n) -> bool {
+    float tot = 0.f;
+    bool ok = true;
+    for (auto &pr : v) {
+      if (hipEventSynchronize(pr.second) != hipSuccess) ok = false;
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, pr.first, pr.second) != hipSuccess) ok = false;
+      tot += t;
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
+    }
+    if (ms) *ms = tot;
+    if (n) *n = (int32_t)v.size();
+    v.clear();
+    return ok;
+  };
+  const bool a = drain(g_prof_lm, lm_ms, lm_n);
+  const bool b = drain(g_prof_sc, sc_ms, sc_n);
+  return (a && b) ? DG_OK : DG_ERR_HIP;
+}
+
+}  // extern "C"

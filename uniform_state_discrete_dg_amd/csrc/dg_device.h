@@ -1,0 +1,107 @@
+// dg_device.h -- device-side helpers shared by the libdgdenoise kernels
+// (gfx950 / CDNA4).  bf16 is carried as raw 16-bit words; conversions are
+// written out so that every kernel rounds the same way (round to nearest
+// even, NaN kept quiet).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+typedef uint16_t bf16;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16 h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+__device__ __forceinline__ bf16 f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16)(u >> 16);
+}
+
+// Two floats -> packed pair of bf16 (low word = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// Split of eight floats into two bf16 octets, x = hi + lo with hi = bf16(x)
+// and lo = bf16(x - hi): 16 significant bits, so a product against an exact
+// bf16 operand costs two MFMAs and stays within ~1e-5 of fp32.
+__device__ __forceinline__ void split8(const float4 a, const float4 b, uint4 &hi, uint4 &lo) {
+  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16 h0 = f32_to_bf16(x[2 * i]), h1 = f32_to_bf16(x[2 * i + 1]);
+    h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    l[i] = pack_bf16x2(x[2 * i] - bf16_to_f32(h0), x[2 * i + 1] - bf16_to_f32(h1));
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float *p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float *p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<bf16> {
+  static __device__ __forceinline__ float load(const bf16 *p, int64_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void store(bf16 *p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds, each two
+// 32x32 -> 64-bit products (multipliers 0xD2511F53, 0xCD9E8D57) mixed with
+// the key, which is bumped by the Weyl increments 0x9E3779B9 / 0xBB67AE85
+// between rounds.
+struct Philox4 {
+  uint32_t v[4];
+};
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0;
+    const uint32_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  Philox4 o;
+  o.v[0] = c0;
+  o.v[1] = c1;
+  o.v[2] = c2;
+  o.v[3] = c3;
+  return o;
+}
+
+// Uniform token in [0, 2^log2v): top bits of Philox word 0, key = seed,
+// counter = (pos, step, canvas, stream).
+__device__ __forceinline__ int32_t uniform_token(uint64_t seed, uint32_t pos, uint32_t step,
+                                                 uint32_t canvas, uint32_t stream, int log2v) {
+  const Philox4 o = philox4x32_10(pos, step, canvas, stream, (uint32_t)seed, (uint32_t)(seed >> 32));
+  return (int32_t)(o.v[0] >> (32 - log2v));
+}
+
+__device__ __forceinline__ float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace dg

@@ -1,0 +1,132 @@
+// dg_kernels.h -- host-side launchers of the libdgdenoise kernels.  Every
+// launcher enqueues on `s` and returns the launch status; shapes have been
+// validated by the caller (dg_api.cpp).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+typedef uint16_t bf16;  // raw bfloat16 bits
+
+// Epilogue of the dense GEMMs: how an output element (row, col) is stored.
+//   index(row, col) = row * rstride + (col / cdiv) * chi + (col % cdiv)
+// which covers plain row-major outputs (cdiv >= N) and the head-split
+// layouts of Q/K/V ([head][row][hd]: cdiv = hd, chi = head stride).
+enum EpiKind { EPI_STORE = 0, EPI_GELU = 1, EPI_ADD = 2, EPI_PARTIAL = 3 };
+struct Epi {
+  int kind;
+  void *out;
+  int out_f32;           // 1: float output, 0: bf16 output
+  int64_t rstride;
+  int cdiv;
+  int64_t chi;
+  const float *resid;    // EPI_ADD: out = resid + acc (f32, same index)
+  int64_t split_stride;  // EPI_PARTIAL: f32 out + blockIdx.z * split_stride
+};
+
+struct GemmShape {
+  const void *A;          // [M][K] (lda)
+  int64_t lda;
+  const void *B;          // [N][K] (ldb)
+  int64_t ldb;
+  int M, N, K;
+  // optional per-(row, 256-column tile of K) multiplier of A (nullable)
+  const float *a_scale;
+  int64_t a_scale_ld;
+};
+
+// fp32 activation x bf16 weight GEMM on the bf16 MFMA with the activation
+// split in two bf16 terms: C_seg[M][N_seg] = A[M][K] B_seg[N_seg][K]^T for up
+// to three weight matrices sharing A (grid.z); K % 64 == 0.
+struct SplitGemm {
+  const float *A;
+  int64_t lda;
+  int M, K;
+  const void *B[3];
+  int N[3];
+  Epi e[3];
+  int count;
+};
+hipError_t gemm_split(const SplitGemm &g, hipStream_t s);
+// The self-conditioning contraction: A = probs (scaled per tile), B = E^T,
+// K = V split in ksplit ranges; writes f32 partials [ksplit][M][N].
+hipError_t selfcond_bf16(const GemmShape &g, float *partials, int ksplit, hipStream_t s);
+// fp32 SIMT GEMM: C[m][n] = sum_k A[m*sam + k*sak] * B[n*sbn + k*sbk].
+struct GemmShapeF32 {
+  const float *A;
+  int64_t sam, sak;
+  const float *B;
+  int64_t sbn, sbk;
+  int M, N, K;
+  const float *a_scale;
+  int64_t a_scale_ld;
+};
+hipError_t gemm_f32(const GemmShapeF32 &g, const Epi &e, hipStream_t s);
+
+// Tied LM head + temperature softmax statistics (bf16 operands): for each
+// row and 256-column tile t of z = A E^T: zmax_t, argmax_t, and with
+// y = z * inv_T, m_t = zmax_t * inv_T: l_t = sum exp(y - m_t),
+// s_t = sum exp(y - m_t) (y - m_t); probs = bf16(exp(y - m_t)).
+// tile_stats: float4 [M][V/256] = (zmax, l, s, argmax as int bits).
+hipError_t lm_head_bf16(const uint16_t *A, int M, int K, const uint16_t *E, int V, float inv_T,
+                        uint16_t *probs, float4 *tile_stats, float *logits_dump, hipStream_t s);
+// Same statistics from fp32 logits already in memory (fp32 path).
+hipError_t tile_stats_f32(const float *logits, int M, int V, float inv_T, float *probs,
+                          float4 *tile_stats, hipStream_t s);
+// Row combine: entropy (nats), argmax, and the per-tile normalisers
+// c[row][t] = exp(m_t - M_row) / L_row used by the next self-conditioning.
+// With n2 (fp32 [M][d]) and E given, the argmax token's logit is recomputed
+// exactly and top[row] = (argmax as int bits, its exact probability).
+hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,
+                       int32_t *argmax, float *tile_scale, const float *n2, const uint16_t *E, int d,
+                       float2 *top, hipStream_t s);
+
+// Attention over two key segments [A: nA keys][B: nB keys] per KV head, all
+// fp32 in memory.  q: [Hq][nq][hd]; k/v segment X: base + (g * capX + j) * hd.
+// out: fp32 [nq][Hq*hd].  causal: query i may read keys <= q_pos0 + i.
+struct AttnArgs {
+  const void *q;
+  int nq, Hq, Hkv, hd;
+  const void *kA, *vA;
+  int nA, capA;
+  const void *kB, *vB;
+  int nB, capB;
+  int causal, q_pos0;
+  void *out;
+  float *part_o;   // workspace [splits][Hq][nq][hd]
+  float *part_ml;  // workspace [splits][Hq][nq][2]
+  int splits, keys_per_split;
+};
+// head_dim 128 on the MFMA (split-bf16 products), split-KV + merge
+hipError_t attention_mfma(const AttnArgs &a, hipStream_t s);
+hipError_t attention_f32(const AttnArgs &a, hipStream_t s);
+void attention_plan(int nq, int Hq, int nk, int *splits, int *keys_per_split);
+
+// Small ops.
+template <typename T>
+hipError_t gather_rows(const T *E, const int32_t *tokens, int n, int d, int V, float *out,
+                       hipStream_t s);
+template <typename T>
+hipError_t rmsnorm_rows(const float *x, const T *g, int n, int d, float eps, float *out, bf16 *out_bf16,
+                        hipStream_t s);
+// S (fp32 [N][d]) = sum of the ksplit partials + exact correction of each
+// row's dominant token (top = (token bits, exact p); nullable).
+hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top,
+                           const uint16_t *probs, const float *tile_scale, int ntiles, int V,
+                           const uint16_t *E, float *out, hipStream_t s);
+template <typename T>
+hipError_t transpose(const T *in, int rows, int cols, T *out, hipStream_t s);
+hipError_t copy_bytes(const void *src, void *dst, size_t bytes, hipStream_t s);
+
+// Selection and canvas.
+hipError_t canvas_init(int32_t *tokens, int32_t *status, int N, int log2v, uint64_t seed,
+                       uint32_t canvas_id, hipStream_t s);
+hipError_t select_step(const float *entropy, const int32_t *argmax, int32_t *tokens,
+                       uint8_t *accept, int32_t *status, int N, int log2v, double gamma,
+                       int rule, float conf_eps, uint64_t seed, uint32_t canvas_id,
+                       uint32_t step, hipStream_t s);
+hipError_t philox_test(const uint32_t *ctr, uint32_t k0, uint32_t k1, uint32_t *out, int n,
+                       hipStream_t s);
+
+}  // namespace dg

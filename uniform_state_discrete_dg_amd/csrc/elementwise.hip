@@ -1,0 +1,299 @@
+// elementwise.hip -- the small kernels around the contractions: embedding
+// gather, RMSNorm, split-K merge, the one-time E transpose, per-tile softmax
+// statistics for the fp32 path, and the per-row entropy/argmax combine.
+// Every reduction is a fixed tree, so results do not depend on timing.
+#include "dg_device.h"
+#include "dg_kernels.h"
+
+namespace dg {
+
+namespace {
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr int TILE = 256;
+}  // namespace
+
+// Block-wide (256 threads) sum with a fixed reduction tree.
+__device__ __forceinline__ float block_sum256(float v, float *sh) {
+  sh[threadIdx.x] = v;
+  __syncthreads();
+#pragma unroll
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  const float r = sh[0];
+  __syncthreads();
+  return r;
+}
+
+// [P3] §5.1: the token embeddings of the canvas (rows of the tied table).
+template <typename T>
+__global__ void gather_kernel(const T *__restrict__ E, const int32_t *__restrict__ tokens, int d, int V,
+                              float *__restrict__ out) {
+  const int i = blockIdx.x;
+  int t = tokens[i];
+  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
+  for (int k = threadIdx.x; k < d; k += blockDim.x)
+    out[(int64_t)i * d + k] = Elem<T>::load(E, (int64_t)t * d + k);
+}
+
+template <typename T>
+hipError_t gather_rows(const T *E, const int32_t *tokens, int n, int d, int V, float *out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_kernel<T>, dim3(n), dim3(256), 0, s, E, tokens, d, V, out);
+  return hipGetLastError();
+}
+template hipError_t gather_rows<float>(const float *, const int32_t *, int, int, int, float *, hipStream_t);
+template hipError_t gather_rows<bf16>(const bf16 *, const int32_t *, int, int, int, float *, hipStream_t);
+
+// RMSNorm: out = x / sqrt(mean(x^2) + eps) * g, written in fp32 and, when
+// requested, also rounded to bf16 (the operand of the tied LM head).
+template <typename T>
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ x, const T *__restrict__ g,
+                                                      int d, float eps, float *__restrict__ out,
+                                                      bf16 *__restrict__ out_bf16) {
+  __shared__ float sh[256];
+  const int i = blockIdx.x;
+  const float *xi = x + (int64_t)i * d;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < d; k += 256) ss += xi[k] * xi[k];
+  ss = block_sum256(ss, sh);
+  const float inv = rsqrtf(ss / (float)d + eps);
+  for (int k = threadIdx.x; k < d; k += 256) {
+    const float v = xi[k] * inv * Elem<T>::load(g, k);
+    out[(int64_t)i * d + k] = v;
+    if (out_bf16) out_bf16[(int64_t)i * d + k] = f32_to_bf16(v);
+  }
+}
+
+template <typename T>
+hipError_t rmsnorm_rows(const float *x, const T *g, int n, int d, float eps, float *out, bf16 *out_bf16,
+                        hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(n), dim3(256), 0, s, x, g, d, eps, out, out_bf16);
+  return hipGetLastError();
+}
+template hipError_t rmsnorm_rows<float>(const float *, const float *, int, int, float, float *, bf16 *,
+                                        hipStream_t);
+template hipError_t rmsnorm_rows<bf16>(const float *, const bf16 *, int, int, float, float *, bf16 *,
+                                       hipStream_t);
+
+// Merge of the self-conditioning split-K partials into S (fp32), plus the
+// exact correction of each row's dominant token: the contraction used
+// p~ = bf16(bf16(num_a) * c_t) for token a, the previous step's exact
+// probability of a is p_a, so S += (p_a - p~) E[a].
+__global__ void selfcond_reduce_kernel(const float *__restrict__ part, int ksplit, int N, int d,
+                                       const float2 *__restrict__ top, const bf16 *__restrict__ probs,
+                                       const float *__restrict__ tile_scale, int ntiles, int V,
+                                       const bf16 *__restrict__ E, float *__restrict__ out) {
+  const int row = blockIdx.y;
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= d) return;
+  const int64_t i = (int64_t)row * d + k;
+  const int64_t count = (int64_t)N * d;
+  float acc = 0.f;
+  for (int z = 0; z < ksplit; ++z) acc += part[(int64_t)z * count + i];
+  if (top) {
+    const float2 tp = top[row];
+    const int a = __float_as_int(tp.x);
+    const float used = bf16_to_f32(f32_to_bf16(bf16_to_f32(probs[(int64_t)row * V + a]) *
+                                               tile_scale[(int64_t)row * ntiles + (a >> 8)]));
+    acc += (tp.y - used) * bf16_to_f32(E[(int64_t)a * d + k]);
+  }
+  out[i] = acc;
+}
+
+hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top, const uint16_t *probs,
+                           const float *tile_scale, int ntiles, int V, const uint16_t *E, float *out,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((d + 255) / 256, N), dim3(256), 0, s, part, ksplit, N, d,
+                     top, probs, tile_scale, ntiles, V, E, out);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ void transpose_kernel(const T *__restrict__ in, int rows, int cols, T *__restrict__ out) {
+  __shared__ T tile[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int k = ty; k < 32; k += 8) {
+    const int r = r0 + k, c = c0 + tx;
+    if (r < rows && c < cols) tile[k][tx] = in[(int64_t)r * cols + c];
+  }
+  __syncthreads();
+  for (int k = ty; k < 32; k += 8) {
+    const int c = c0 + k, r = r0 + tx;
+    if (r < rows && c < cols) out[(int64_t)c * rows + r] = tile[tx][k];
+  }
+}
+
+template <typename T>
+hipError_t transpose(const T *in, int rows, int cols, T *out, hipStream_t s) {
+  dim3 grid((cols + 31) / 32, (rows + 31) / 32);
+  hipLaunchKernelGGL(transpose_kernel<T>, grid, dim3(256), 0, s, in, rows, cols, out);
+  return hipGetLastError();
+}
+template hipError_t transpose<float>(const float *, int, int, float *, hipStream_t);
+template hipError_t transpose<bf16>(const bf16 *, int, int, bf16 *, hipStream_t);
+
+__global__ void copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+hipError_t copy_bytes(const void *src, void *dst, size_t bytes, hipStream_t s) {
+  const int64_t n = (int64_t)(bytes / 16);
+  hipLaunchKernelGGL(copy_kernel, dim3(2048), dim3(256), 0, s, static_cast<const uint4 *>(src),
+                     static_cast<uint4 *>(dst), n);
+  return hipGetLastError();
+}
+
+// Per-(row, 256-column tile) softmax statistics from fp32 logits; the same
+// quantities the bf16 LM-head epilogue produces.
+__global__ void __launch_bounds__(256) tile_stats_f32_kernel(const float *__restrict__ logits, int V,
+                                                             float inv_T, float *__restrict__ probs,
+                                                             float4 *__restrict__ stats) {
+  __shared__ float sv[256];
+  __shared__ int si[256];
+  __shared__ float sh[256];
+  const int row = blockIdx.y, tile = blockIdx.x;
+  const int col = tile * TILE + threadIdx.x;
+  const float z = logits[(int64_t)row * V + col];
+  sv[threadIdx.x] = z;
+  si[threadIdx.x] = col;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      const float v2 = sv[threadIdx.x + o];
+      const int i2 = si[threadIdx.x + o];
+      if (v2 > sv[threadIdx.x] || (v2 == sv[threadIdx.x] && i2 < si[threadIdx.x])) {
+        sv[threadIdx.x] = v2;
+        si[threadIdx.x] = i2;
+      }
+    }
+    __syncthreads();
+  }
+  const float zmax = sv[0];
+  const int amax = si[0];
+  const float m = zmax * inv_T;
+  const float t = z * inv_T - m;
+  const float e = exp2f(t * LOG2E);
+  probs[(int64_t)row * V + col] = e;
+  const float l = block_sum256(e, sh);
+  const float sacc = block_sum256(e * t, sh);
+  if (threadIdx.x == 0)
+    stats[(int64_t)row * (V / TILE) + tile] = make_float4(zmax, l, sacc, __int_as_float(amax));
+}
+
+hipError_t tile_stats_f32(const float *logits, int M, int V, float inv_T, float *probs, float4 *stats,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(tile_stats_f32_kernel, dim3(V / TILE, M), dim3(256), 0, s, logits, V, inv_T, probs,
+                     stats);
+  return hipGetLastError();
+}
+
+// Entropy of softmax(y) from the tile statistics ([P3] §5.4 measures
+// confidence by the entropy of each position's distribution):
+//   M = max_t m_t, L = sum_t l_t e^{m_t - M},
+//   S = sum_t e^{m_t - M} (s_t + (m_t - M) l_t),  H = ln L - S / L  (nats),
+// clamped at +0 (NaN propagates).  Also the argmax (lowest index on ties)
+// and the normaliser c_t = e^{m_t - M} / L of each tile, which turns the
+// stored numerators into probabilities for the next self-conditioning.
+//
+// With n2 given (bf16 path) the logit of the row's argmax token a is first
+// recomputed exactly from the fp32 normalised hidden state (the LM head used
+// its bf16 rounding), and a's term in its tile's sums is replaced: the
+// dominant token carries most of the entropy's sensitivity to logit error.
+// The exact probability of a is kept in top[row] = (a, p_a) for the next
+// step's self-conditioning.  The argmax itself stays the LM head's.
+__global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restrict__ stats, int ntiles,
+                                                          float inv_T, float *__restrict__ entropy,
+                                                          int32_t *__restrict__ argmax,
+                                                          float *__restrict__ tile_scale,
+                                                          const float *__restrict__ n2, const bf16 *__restrict__ E,
+                                                          int d, float2 *__restrict__ top) {
+  __shared__ float sv[256];
+  __shared__ int si[256];
+  __shared__ float sh[256];
+  const int row = blockIdx.x;
+  const float4 *st = stats + (int64_t)row * ntiles;
+  float best = -INFINITY;
+  int bidx = INT32_MAX;
+  for (int t = threadIdx.x; t < ntiles; t += 256) {
+    const float4 v = st[t];
+    const int idx = __float_as_int(v.w);
+    if (v.x > best || (v.x == best && idx < bidx)) {
+      best = v.x;
+      bidx = idx;
+    }
+  }
+  sv[threadIdx.x] = best;
+  si[threadIdx.x] = bidx;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      const float v2 = sv[threadIdx.x + o];
+      const int i2 = si[threadIdx.x + o];
+      if (v2 > sv[threadIdx.x] || (v2 == sv[threadIdx.x] && i2 < si[threadIdx.x])) {
+        sv[threadIdx.x] = v2;
+        si[threadIdx.x] = i2;
+      }
+    }
+    __syncthreads();
+  }
+  const float Mz = sv[0];
+  const int amax = si[0];
+  __syncthreads();
+  const float My = Mz * inv_T;
+  const int ta = amax >> 8;
+  // corrected terms of the argmax token inside its tile (reference m_ta = My)
+  float l_fix = 0.f, s_fix = 0.f, d_top = 0.f;
+  const bool fix = n2 != nullptr;
+  if (fix) {
+    float part = 0.f;
+    for (int k = threadIdx.x; k < d; k += 256)
+      part += n2[(int64_t)row * d + k] * bf16_to_f32(E[(int64_t)amax * d + k]);
+    const float z_exact = block_sum256(part, sh);
+    d_top = z_exact * inv_T - My;
+    const float e = exp2f(d_top * LOG2E);
+    l_fix = e - 1.f;
+    s_fix = e * d_top;
+  }
+  float L = 0.f, S = 0.f;
+  for (int t = threadIdx.x; t < ntiles; t += 256) {
+    const float4 v = st[t];
+    const float dd = v.x * inv_T - My;
+    const float w = exp2f(dd * LOG2E);
+    float l = v.y, sacc = v.z;
+    if (fix && t == ta) {
+      l += l_fix;
+      sacc += s_fix;
+    }
+    L += l * w;
+    S += w * (sacc + dd * l);
+  }
+  L = block_sum256(L, sh);
+  S = block_sum256(S, sh);
+  const float invL = 1.f / L;
+  for (int t = threadIdx.x; t < ntiles; t += 256) {
+    const float dd = st[t].x * inv_T - My;
+    tile_scale[(int64_t)row * ntiles + t] = exp2f(dd * LOG2E) * invL;
+  }
+  if (threadIdx.x == 0) {
+    float H = logf(L) - S * invL;
+    if (H <= 0.f) H = 0.f;
+    entropy[row] = H;
+    argmax[row] = amax;
+    if (top) top[row] = make_float2(__int_as_float(amax), exp2f(d_top * LOG2E) * invL);
+  }
+}
+
+hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,
+                       int32_t *argmax, float *tile_scale, const float *n2, const uint16_t *E, int d,
+                       float2 *top, hipStream_t s) {
+  hipLaunchKernelGGL(row_combine_kernel, dim3(M), dim3(256), 0, s, tile_stats, ntiles, inv_T, entropy,
+                     argmax, tile_scale, n2, E, d, top);
+  return hipGetLastError();
+}
+
+}  // namespace dg
