@@ -104,7 +104,7 @@ typedef struct {
 /* Per-canvas state.  Device buffers are caller-owned:
  *   tokens  int32 [N]            current canvas
  *   probs   dtype [N][V]         softmax numerators of the last step, per
- *                                256-column tile: exp(y - m_tile) (the
+ *                                64-column tile: exp(y - m_tile) (the
  *                                self-conditioning input of the next step)
  *   stats   bytes dg_stats_bytes(): per-(row, tile) softmax statistics,
  *                                normalisers and each row's dominant token

@@ -55,7 +55,7 @@ def test_shipped_configs_supported(lib, i):
     assert B.dg_validate_config(cfg) == B.DG_OK
     assert B.dg_workspace_bytes(cfg, 0) > 0
     assert B.dg_workspace_bytes(cfg, 1024) >= B.dg_workspace_bytes(cfg, 0)
-    assert B.dg_stats_bytes(cfg) == cfg.canvas_len * ((cfg.vocab // 256) * 20 + 8)
+    assert B.dg_stats_bytes(cfg) == cfg.canvas_len * ((cfg.vocab // 64) * 20 + 8)
 
 
 @pytest.mark.parametrize("kw,st", [

@@ -26,7 +26,7 @@ DG_ACCEPT_SUM_MINUS_MAX, DG_ACCEPT_CUMSUM = 0, 1
 DG_STATUS_WORDS = 16
 (DG_ST_ALLCONF, DG_ST_CHANGED, DG_ST_STABLE, DG_ST_ACCEPTED, DG_ST_NAN, DG_ST_STEP, DG_ST_HMIN,
  DG_ST_HMAX, DG_ST_HMEAN) = range(9)
-TILE_V = 256
+TILE_V = 64  # vocabulary columns per softmax-statistics tile
 
 
 class dg_config(ctypes.Structure):
@@ -290,7 +290,7 @@ class DeviceCanvas:
                            self.accept.data_ptr(), self.status.data_ptr(), 0, 0, 0, 0)
 
     def tile_scale(self, cfg: dg_config) -> torch.Tensor:
-        """Per-(row, tile) normalisers written by the last step ([N][V/256] f32)."""
+        """Per-(row, tile) normalisers written by the last step ([N][V/64] f32)."""
         N, nt = cfg.canvas_len, cfg.vocab // TILE_V
         return self.stats[N * nt * 16:N * nt * 20].view(torch.float32).view(N, nt)
 

@@ -16,7 +16,7 @@ using dg::bf16;
 
 namespace {
 
-constexpr int kTile = 256;  // vocabulary columns per softmax-statistics tile
+constexpr int kTile = 64;  // vocabulary columns per softmax-statistics tile
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 int ilog2(int64_t v) {
@@ -38,7 +38,7 @@ dg_status check_config(const dg_config *c) {
   if (!(std::isfinite(c->rms_eps) && c->rms_eps >= 0.f) || !std::isfinite(c->conf_eps))
     return DG_ERR_INVALID_ARG;
   if (c->canvas_len > 256) return DG_ERR_UNSUPPORTED;
-  if (!is_pow2(c->vocab) || c->vocab < kTile || c->vocab > (1 << 24)) return DG_ERR_UNSUPPORTED;
+  if (!is_pow2(c->vocab) || c->vocab < 256 || c->vocab > (1 << 24)) return DG_ERR_UNSUPPORTED;
   if (c->n_q_heads % c->n_kv_heads != 0) return DG_ERR_UNSUPPORTED;
   if (c->dtype == DG_BF16) {
     if (c->head_dim != 128 || c->d_model % 64 != 0 || c->ffn_hidden % 64 != 0) return DG_ERR_UNSUPPORTED;
@@ -48,9 +48,10 @@ dg_status check_config(const dg_config *c) {
   return DG_OK;
 }
 
-// Self-conditioning split of K = V over workgroups (bf16 path).
+// Self-conditioning split of K = V over workgroups (bf16 path): about one
+// work item per CU.
 int selfcond_ksplit(const dg_config *c) {
-  const int bm = c->canvas_len <= 128 ? 128 : 256;
+  const int bm = dg::estream_bm(c->canvas_len);
   const int ntile = (c->d_model + 255) / 256 * ((c->canvas_len + bm - 1) / bm);
   int ks = 256 / ntile;
   if (ks < 1) ks = 1;

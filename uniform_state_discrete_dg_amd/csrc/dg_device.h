@@ -15,17 +15,17 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(bf16 h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-__device__ __forceinline__ bf16 f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16)(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed pair of bf16 (low word = a), round to nearest even,
+// one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-// Two floats -> packed pair of bf16 (low word = a).
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
+__device__ __forceinline__ bf16 f32_to_bf16(float f) { return (bf16)(pack_bf16x2(f, 0.f) & 0xffffu); }
 
 // Split of eight floats into two bf16 octets, x = hi + lo with hi = bf16(x)
 // and lo = bf16(x - hi): 16 significant bits, so a product against an exact
@@ -35,9 +35,8 @@ __device__ __forceinline__ void split8(const float4 a, const float4 b, uint4 &hi
   uint32_t h[4], l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const bf16 h0 = f32_to_bf16(x[2 * i]), h1 = f32_to_bf16(x[2 * i + 1]);
-    h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    l[i] = pack_bf16x2(x[2 * i] - bf16_to_f32(h0), x[2 * i + 1] - bf16_to_f32(h1));
+    h[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    l[i] = pack_bf16x2(x[2 * i] - __uint_as_float(h[i] << 16), x[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u));
   }
   hi = make_uint4(h[0], h[1], h[2], h[3]);
   lo = make_uint4(l[0], l[1], l[2], l[3]);

@@ -31,7 +31,7 @@ struct GemmShape {
   const void *B;          // [N][K] (ldb)
   int64_t ldb;
   int M, N, K;
-  // optional per-(row, 256-column tile of K) multiplier of A (nullable)
+  // optional per-(row, 64-column tile of K) multiplier of A (nullable)
   const float *a_scale;
   int64_t a_scale_ld;
 };
@@ -49,6 +49,8 @@ struct SplitGemm {
   int count;
 };
 hipError_t gemm_split(const SplitGemm &g, hipStream_t s);
+// Canvas rows per workgroup of the two table-streaming kernels (128 or 256).
+int estream_bm(int M);
 // The self-conditioning contraction: A = probs (scaled per tile), B = E^T,
 // K = V split in ksplit ranges; writes f32 partials [ksplit][M][N].
 hipError_t selfcond_bf16(const GemmShape &g, float *partials, int ksplit, hipStream_t s);
@@ -65,10 +67,10 @@ struct GemmShapeF32 {
 hipError_t gemm_f32(const GemmShapeF32 &g, const Epi &e, hipStream_t s);
 
 // Tied LM head + temperature softmax statistics (bf16 operands): for each
-// row and 256-column tile t of z = A E^T: zmax_t, argmax_t, and with
+// row and 64-column tile t of z = A E^T: zmax_t, argmax_t, and with
 // y = z * inv_T, m_t = zmax_t * inv_T: l_t = sum exp(y - m_t),
 // s_t = sum exp(y - m_t) (y - m_t); probs = bf16(exp(y - m_t)).
-// tile_stats: float4 [M][V/256] = (zmax, l, s, argmax as int bits).
+// tile_stats: float4 [M][V/64] = (zmax, l, s, argmax as int bits).
 hipError_t lm_head_bf16(const uint16_t *A, int M, int K, const uint16_t *E, int V, float inv_T,
                         uint16_t *probs, float4 *tile_stats, float *logits_dump, hipStream_t s);
 // Same statistics from fp32 logits already in memory (fp32 path).

@@ -9,7 +9,7 @@ namespace dg {
 
 namespace {
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr int TILE = 256;
+constexpr int TILE = 64;  // vocabulary columns per softmax-statistics tile
 }  // namespace
 
 // Block-wide (256 threads) sum with a fixed reduction tree.
@@ -97,7 +97,7 @@ __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int kspli
     const float2 tp = top[row];
     const int a = __float_as_int(tp.x);
     const float used = bf16_to_f32(f32_to_bf16(bf16_to_f32(probs[(int64_t)row * V + a]) *
-                                               tile_scale[(int64_t)row * ntiles + (a >> 8)]));
+                                               tile_scale[(int64_t)row * ntiles + a / TILE]));
     acc += (tp.y - used) * bf16_to_f32(E[(int64_t)a * d + k]);
   }
   out[i] = acc;
@@ -148,47 +148,37 @@ hipError_t copy_bytes(const void *src, void *dst, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Per-(row, 256-column tile) softmax statistics from fp32 logits; the same
-// quantities the bf16 LM-head epilogue produces.
-__global__ void __launch_bounds__(256) tile_stats_f32_kernel(const float *__restrict__ logits, int V,
-                                                             float inv_T, float *__restrict__ probs,
-                                                             float4 *__restrict__ stats) {
-  __shared__ float sv[256];
-  __shared__ int si[256];
-  __shared__ float sh[256];
+// Per-(row, 64-column tile) softmax statistics from fp32 logits (the fp32
+// configuration); the same quantities the bf16 LM-head epilogue produces.
+// One wave per tile.
+__global__ void __launch_bounds__(64) tile_stats_f32_kernel(const float *__restrict__ logits, int V, float inv_T,
+                                                            float *__restrict__ probs, float4 *__restrict__ stats) {
   const int row = blockIdx.y, tile = blockIdx.x;
   const int col = tile * TILE + threadIdx.x;
   const float z = logits[(int64_t)row * V + col];
-  sv[threadIdx.x] = z;
-  si[threadIdx.x] = col;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) {
-      const float v2 = sv[threadIdx.x + o];
-      const int i2 = si[threadIdx.x + o];
-      if (v2 > sv[threadIdx.x] || (v2 == sv[threadIdx.x] && i2 < si[threadIdx.x])) {
-        sv[threadIdx.x] = v2;
-        si[threadIdx.x] = i2;
-      }
+  float best = z;
+  int bcol = col;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o);
+    const int oc = __shfl_xor(bcol, o);
+    if (ov > best || (ov == best && oc < bcol)) {
+      best = ov;
+      bcol = oc;
     }
-    __syncthreads();
   }
-  const float zmax = sv[0];
-  const int amax = si[0];
-  const float m = zmax * inv_T;
+  const float m = best * inv_T;
   const float t = z * inv_T - m;
   const float e = exp2f(t * LOG2E);
   probs[(int64_t)row * V + col] = e;
-  const float l = block_sum256(e, sh);
-  const float sacc = block_sum256(e * t, sh);
-  if (threadIdx.x == 0)
-    stats[(int64_t)row * (V / TILE) + tile] = make_float4(zmax, l, sacc, __int_as_float(amax));
+  const float l = warp_sum(e);
+  const float sacc = warp_sum(e * t);
+  if (threadIdx.x == 0) stats[(int64_t)row * (V / TILE) + tile] = make_float4(best, l, sacc, __int_as_float(bcol));
 }
 
 hipError_t tile_stats_f32(const float *logits, int M, int V, float inv_T, float *probs, float4 *stats,
                           hipStream_t s) {
-  hipLaunchKernelGGL(tile_stats_f32_kernel, dim3(V / TILE, M), dim3(256), 0, s, logits, V, inv_T, probs,
-                     stats);
+  hipLaunchKernelGGL(tile_stats_f32_kernel, dim3(V / TILE, M), dim3(64), 0, s, logits, V, inv_T, probs, stats);
   return hipGetLastError();
 }
 
@@ -245,7 +235,7 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
   const int amax = si[0];
   __syncthreads();
   const float My = Mz * inv_T;
-  const int ta = amax >> 8;
+  const int ta = amax / TILE;
   // corrected terms of the argmax token inside its tile (reference m_ta = My)
   float l_fix = 0.f, s_fix = 0.f, d_top = 0.f;
   const bool fix = n2 != nullptr;

@@ -1,0 +1,301 @@
+// estream.hip -- the two contractions that stream the token-embedding table
+// (V x d, 1.5 GB at V = 262144, d = 2816) once per step each:
+//   * the tied LM head z = RMSNorm(h1) E^T, with the softmax/entropy
+//     statistics fused into its epilogue (the logits never reach memory; the
+//     probability numerators are written once in bf16), and
+//   * the self-conditioning contraction S = p_prev E, streaming E^T and
+//     split over V.
+// At a 256-row canvas both are bound by HBM (256 flop per byte of the
+// table), so the design goal is bytes in flight.  A workgroup owns all
+// canvas rows x 256 table rows.  k advances in 32-wide slices; each slice of
+// both operands (16 KB + 16 KB) is copied global -> LDS by the DMA form of
+// the vector load (global_load_lds_dwordx4, no registers involved) into one
+// of four LDS stages, three slices ahead of the MFMAs.  The waits are
+// explicit (s_waitcnt vmcnt + s_barrier, one barrier per slice): a plain
+// __syncthreads would carry a release fence that drains every DMA in flight.
+// 8 waves (2 per SIMD), each 64 canvas rows x 128 table rows.
+//
+// LDS layout of a slice: row-major, 64 bytes per row = four 16-byte chunks;
+// chunk c of row r lives at position c ^ ((r >> 1) & 3), which keeps the 32
+// rows read by one MFMA fragment load in distinct banks.  The DMA writes
+// 64 lanes x 16 bytes contiguously, so the swizzle is applied by choosing
+// each lane's source address.
+#include "dg_device.h"
+#include "dg_kernels.h"
+
+
+namespace dg {
+
+namespace {
+constexpr int ES_NT = 512;        // 8 waves
+constexpr int ES_BM = 256;        // canvas rows per workgroup
+constexpr int ES_BN = 256;        // table rows per workgroup
+constexpr int ES_BK = 32;         // k per slice
+constexpr int ES_STAGES = 4;      // LDS stages (3 slices in flight)
+constexpr int ES_SLICE = ES_BM * ES_BK * 2;  // bytes of one operand slice (16 KB)
+constexpr float LOG2E = 1.4426950408889634f;
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= n, no wait on exp/lgkm.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ int slot16(int row, int c) { return row * 4 + (c ^ ((row >> 1) & 3)); }
+
+__device__ __forceinline__ bf16x8_t scale_frag(uint4 v, float s) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(w[i] << 16) * s;
+    const float hi = __uint_as_float(w[i] & 0xffff0000u) * s;
+    w[i] = pack_bf16x2(lo, hi);
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+__device__ __forceinline__ int acc_r(int r, int lane) { return (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2); }
+}  // namespace
+
+// Accumulates acc[i][j] (wave tile: rows wm*64 + 32i, columns wn*128 + 32j)
+// over k in [kb, ke) (multiples of 32).  A: [M][lda] canvas rows m0..,
+// B: [N][ldb] table rows n0..; rows past M / N read a clamped valid row and
+// only feed accumulators the epilogues discard.  With SCALE_A, A[m][k] is
+// multiplied by a_scale[m][k / 64] (a 64-column tile) as it is read.
+template <bool SCALE_A>
+__device__ __forceinline__ void estream_tile(const bf16 *__restrict__ A, int64_t lda, int M, int m0,
+                                             const bf16 *__restrict__ B, int64_t ldb, int N, int n0, int kb,
+                                             int ke, const float *__restrict__ a_scale, int64_t a_scale_ld,
+                                             char *lds, f32x16_t (&acc)[2][4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r32 = lane & 31, g = lane >> 5;
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // DMA sources: this wave fills 2 KB of each operand slice (2 instructions
+  // of 64 lanes x 16 bytes); position p -> row p / 4, logical chunk.
+  const bf16 *asrc[2], *bsrc[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int p = (wave * 2 + u) * 64 + lane;
+    const int row = p >> 2;
+    const int c = (p & 3) ^ ((row >> 1) & 3);
+    const int ar = m0 + row, br = n0 + row;
+    asrc[u] = A + (int64_t)(ar < M ? ar : M - 1) * lda + c * 8;
+    bsrc[u] = B + (int64_t)(br < N ? br : N - 1) * ldb + c * 8;
+  }
+  // per-lane rows of the two A fragments (for the scale lookup)
+  int srow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rr = m0 + wm * 64 + i * 32 + r32;
+    srow[i] = rr < M ? rr : M - 1;
+  }
+
+  const int nk = (ke - kb) / ES_BK;
+  if (nk <= 0) return;
+  const int klast = kb + ES_BK * (nk - 1);
+  float sc[ES_STAGES][2];
+  auto issue = [&](int slice, int stage) {
+    const int k0 = min(kb + ES_BK * slice, klast);
+    char *st = lds + stage * 2 * ES_SLICE;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      __builtin_amdgcn_global_load_lds(asrc[u] + k0, st + (wave * 2 + u) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bsrc[u] + k0, st + ES_SLICE + (wave * 2 + u) * 1024, 16, 0, 0);
+    }
+    if (SCALE_A) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) sc[stage][i] = a_scale[(int64_t)srow[i] * a_scale_ld + (k0 >> 6)];
+    }
+  };
+  // loads per slice per wave: 4 DMA (+2 scale loads)
+  constexpr int PER = SCALE_A ? 6 : 4;
+
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  for (int it = 0; it < nk; ++it) {
+    const int stage = it & 3;
+    wait_vmcnt<2 * PER>();          // this wave's loads for slice `it` are done
+    __builtin_amdgcn_s_barrier();   // ... and every wave's; slice it-1 is consumed
+    issue(it + 3, (it + 3) & 3);    // refill the stage slice it-1 used
+    const uint4 *sa = reinterpret_cast<const uint4 *>(lds + stage * 2 * ES_SLICE);
+    const uint4 *sb = reinterpret_cast<const uint4 *>(lds + stage * 2 * ES_SLICE + ES_SLICE);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = kk * 2 + g;
+      bf16x8_t fa[2], fb[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint4 v = sa[slot16(wm * 64 + i * 32 + r32, c)];
+        fa[i] = SCALE_A ? scale_frag(v, sc[stage][i]) : __builtin_bit_cast(bf16x8_t, v);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, sb[slot16(wn * 128 + j * 32 + r32, c)]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  wait_vmcnt<0>();  // retire the trailing (unused) prefetches before LDS is reused
+  __builtin_amdgcn_s_barrier();
+}
+
+// ---------------------------------------------------------------------------
+// LM head: workgroup = canvas rows x 256 vocabulary columns; a wave holds 64
+// rows x 128 columns = two 64-column tiles of the softmax statistics, so the
+// epilogue is local to the wave: per row and tile, the max of z and its
+// lowest column, exp(y - m) written once as bf16, l = sum exp(y - m) and
+// s = sum exp(y - m)(y - m), with y = z / T and m = zmax / T.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__restrict__ A, int M, int K,
+                                                              const bf16 *__restrict__ E, int V, float inv_T,
+                                                              bf16 *__restrict__ probs, float4 *__restrict__ tile_stats,
+                                                              float *__restrict__ logits) {
+  extern __shared__ __align__(16) char lds[];
+  const int n0 = blockIdx.x * ES_BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * ES_BM;
+  f32x16_t acc[2][4];
+  estream_tile<false>(A, K, M, m0, E, K, V, n0, 0, K, nullptr, 0, lds, acc);
+  const int ntiles = V / 64;
+
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int tile = (n0 + wn * 128 + h * 64) / 64;
+    const int c0 = tile * 64 + (lane & 31);  // global column of fragment 2h
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float z0 = acc[i][2 * h][r], z1 = acc[i][2 * h + 1][r];
+        float best = z0;
+        int bcol = c0;
+        if (z1 > best) {
+          best = z1;
+          bcol = c0 + 32;
+        }
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) {
+          const float ov = __shfl_xor(best, o);
+          const int oc = __shfl_xor(bcol, o);
+          if (ov > best || (ov == best && oc < bcol)) {
+            best = ov;
+            bcol = oc;
+          }
+        }
+        const float m = best * inv_T;
+        const float t0 = z0 * inv_T - m, t1 = z1 * inv_T - m;
+        const float e0 = exp2f(t0 * LOG2E), e1 = exp2f(t1 * LOG2E);
+        float l = e0 + e1, sacc = e0 * t0 + e1 * t1;
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) {
+          l += __shfl_xor(l, o);
+          sacc += __shfl_xor(sacc, o);
+        }
+        const int row = m0 + wm * 64 + i * 32 + acc_r(r, lane);
+        if (row < M) {
+          const int64_t o = (int64_t)row * V + c0;
+          probs[o] = f32_to_bf16(e0);
+          probs[o + 32] = f32_to_bf16(e1);
+          if (logits) {
+            logits[o] = z0;
+            logits[o + 32] = z1;
+          }
+          if ((lane & 31) == 0) tile_stats[(int64_t)row * ntiles + tile] = make_float4(best, l, sacc, __int_as_float(bcol));
+        }
+      }
+  }
+}
+
+int estream_bm(int) { return ES_BM; }
+
+static size_t es_lds_bytes() { return (size_t)ES_STAGES * 2 * ES_SLICE; }
+
+hipError_t lm_head_bf16(const uint16_t *A, int M, int K, const uint16_t *E, int V, float inv_T, uint16_t *probs,
+                        float4 *tile_stats, float *logits_dump, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(lm_head_es_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess)
+      return hipErrorInvalidValue;
+    attr = true;
+  }
+  dim3 grid(V / ES_BN, (M + ES_BM - 1) / ES_BM);
+  hipLaunchKernelGGL(lm_head_es_kernel, grid, dim3(ES_NT), es_lds_bytes(), s, A, M, K, E, V, inv_T, probs,
+                     tile_stats, logits_dump);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Self-conditioning contraction, split over K = V: work item (kc, nt) =
+// K-chunk kc of the canvas x 256 columns of d.  The hardware hands
+// consecutive workgroups to the 8 XCDs in turn; the mapping below gives the
+// work items of one K-chunk to workgroups of one XCD where it can, so the
+// chunk of probabilities they share is fetched into that XCD's L2 once.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(GemmShape g, float *__restrict__ part, int ksplit,
+                                                               int ntn, int items) {
+  extern __shared__ __align__(16) char lds[];
+  const int b = blockIdx.x, nb = gridDim.x;
+  const int per_xcd = nb / 8;  // grid is a multiple of 8
+  const int item = (b % 8) * per_xcd + b / 8;
+  if (item >= items) return;
+  const int mblocks = (g.M + ES_BM - 1) / ES_BM;
+  const int mb = item % mblocks;
+  const int kc = (item / mblocks) / ntn, nt = (item / mblocks) % ntn;
+  const int m0 = mb * ES_BM;
+  const int nslices = g.K / 64;  // 64-aligned chunks keep every chunk inside whole scale tiles
+  const int kb = (int)((int64_t)nslices * kc / ksplit) * 64;
+  const int ke = (int)((int64_t)nslices * (kc + 1) / ksplit) * 64;
+  const int n0 = nt * ES_BN;
+  f32x16_t acc[2][4];
+  if (g.a_scale)
+    estream_tile<true>(static_cast<const bf16 *>(g.A), g.lda, g.M, m0, static_cast<const bf16 *>(g.B), g.ldb, g.N,
+                       n0, kb, ke, g.a_scale, g.a_scale_ld, lds, acc);
+  else
+    estream_tile<false>(static_cast<const bf16 *>(g.A), g.lda, g.M, m0, static_cast<const bf16 *>(g.B), g.ldb, g.N,
+                        n0, kb, ke, nullptr, 0, lds, acc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  float *out = part + (int64_t)kc * g.M * g.N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + i * 32 + acc_r(r, lane);
+        const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+        if (row < g.M && col < g.N) out[(int64_t)row * g.N + col] = acc[i][j][r];
+      }
+}
+
+hipError_t selfcond_bf16(const GemmShape &g, float *partials, int ksplit, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(selfcond_es_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess)
+      return hipErrorInvalidValue;
+    attr = true;
+  }
+  const int ntn = (g.N + ES_BN - 1) / ES_BN;
+  const int items = ntn * ksplit * ((g.M + ES_BM - 1) / ES_BM);
+  const int grid = (items + 7) / 8 * 8;
+  hipLaunchKernelGGL(selfcond_es_kernel, dim3(grid), dim3(ES_NT), es_lds_bytes(), s, g, partials, ksplit, ntn,
+                     items);
+  return hipGetLastError();
+}
+
+}  // namespace dg
