@@ -43,14 +43,38 @@ def step_flops(c: dict, selfcond: bool = True) -> float:
 def lm_head_bytes(c: dict) -> float:
     """Algorithmic HBM bytes of one LM-head launch: E once (bf16), the
     normalised hidden rows, the bf16 probability numerators written once and
-    the per-(row, 256-column tile) statistics."""
+    the per-(row, 64-column tile) statistics (float4)."""
     N, V, d = c["N"], c["V"], c["d"]
-    return float(V * d * 2 + N * d * 2 + N * V * 2 + N * (V // 256) * 16)
+    return float(V * d * 2 + N * d * 2 + N * V * 2 + N * (V // 64) * 16)
 
 
 def selfcond_bytes(c: dict) -> float:
+    """E^T once, the bf16 numerators, the per-tile normalisers."""
     N, V, d = c["N"], c["V"], c["d"]
-    return float(V * d * 2 + N * V * 2 + N * (V // 256) * 4)
+    return float(V * d * 2 + N * V * 2 + N * (V // 64) * 4)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lm_head_n256_v262k_d2816.txt")
+KERNEL_SRC = os.path.join(ROOT, "uniform_state_discrete_dg_amd", "csrc", "estream.hip")
+
+
+def measured_traffic():
+    """HBM bytes per LM-head launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration),
+    or None when the kernel source has changed since it was taken."""
+    import hashlib
+    try:
+        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if kv.get("kernel_source_sha256") != src:
+        return None
+    try:
+        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(c: dict, inp: dict, rows=(2, 6)) -> dict:
@@ -95,6 +119,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload table entry (3: N256 V262144)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run the library's plain copy kernel over 1 GiB three times "
+                         "(reference for memory-traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -105,6 +132,15 @@ def main() -> int:
     from uniform_state_discrete_dg_amd import binding as B
     from uniform_state_discrete_dg_amd import driver as D
     from uniform_state_discrete_dg_amd import workloads as W
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            B.dg_test_copy(src, dst, n)
+        torch.cuda.synchronize()
+        del src, dst
 
     c = W.config(args.config)
     inp = W.make_inputs(c)
@@ -159,7 +195,7 @@ def main() -> int:
         "mfma_frac_of_bf16_peak": flops / dt / PEAK_BF16_FLOPS,
         "roofline": {"bound": "hbm", "kernel": "lm_head (tied head + softmax/entropy epilogue)",
                      "achieved": lm_gbs, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
-                     "frac": lm_gbs * 1e9 / PEAK_HBM_BYTES, "traffic": None,
+                     "frac": lm_gbs * 1e9 / PEAK_HBM_BYTES, "traffic": measured_traffic(),
                      "avg_launch_us": lm_avg_s * 1e6, "launches": lm_n,
                      "bytes_per_launch": lm_head_bytes(c)},
         "selfcond_kernel": {"avg_launch_us": sc_avg_s * 1e6, "launches": sc_n,
