@@ -15,11 +15,17 @@
 // __syncthreads would carry a release fence that drains every DMA in flight.
 // 8 waves (2 per SIMD), each 64 canvas rows x 128 table rows.
 //
+// The MFMA takes the table fragment as its first operand, so a lane's
+// accumulators hold one canvas row and 16 of the 32 table rows of a
+// fragment (its partner lane, lane ^ 32, holds the other 16): the softmax
+// statistics over a 64-column tile are reduced in registers, with a single
+// exchange between the two partner lanes.
+//
 // LDS layout of a slice: row-major, 64 bytes per row = four 16-byte chunks;
-// chunk c of row r lives at position c ^ ((r >> 1) & 3), which keeps the 32
-// rows read by one MFMA fragment load in distinct banks.  The DMA writes
-// 64 lanes x 16 bytes contiguously, so the swizzle is applied by choosing
-// each lane's source address.
+// chunk c of row r lives at position c ^ ((r >> 2) & 3).  A fragment load
+// reads 32 rows at one chunk; any 16 consecutive lanes then cover the 64
+// banks once.  The DMA writes 64 lanes x 16 bytes contiguously, so the
+// swizzle is applied by choosing each lane's source address.
 #include "dg_device.h"
 #include "dg_kernels.h"
 
@@ -42,7 +48,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__device__ __forceinline__ int slot16(int row, int c) { return row * 4 + (c ^ ((row >> 1) & 3)); }
+__device__ __forceinline__ int slot16(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
 
 __device__ __forceinline__ bf16x8_t scale_frag(uint4 v, float s) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -55,11 +61,12 @@ __device__ __forceinline__ bf16x8_t scale_frag(uint4 v, float s) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-__device__ __forceinline__ int acc_r(int r, int lane) { return (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2); }
 }  // namespace
 
-// Accumulates acc[i][j] (wave tile: rows wm*64 + 32i, columns wn*128 + 32j)
-// over k in [kb, ke) (multiples of 32).  A: [M][lda] canvas rows m0..,
+// Accumulates acc[i][j] (wave tile: canvas rows wm*64 + 32i, table rows
+// wn*128 + 32j) over k in [kb, ke) (multiples of 32).  Layout of acc[i][j]:
+// lane holds canvas row 32i + (lane & 31) and, in register r, table row
+// 8 (r >> 2) + 4 (lane >> 5) + (r & 3) of the fragment.  A: [M][lda] canvas rows m0..,
 // B: [N][ldb] table rows n0..; rows past M / N read a clamped valid row and
 // only feed accumulators the epilogues discard.  With SCALE_A, A[m][k] is
 // multiplied by a_scale[m][k / 64] (a 64-column tile) as it is read.
@@ -86,7 +93,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ A, int64_t
   for (int u = 0; u < 2; ++u) {
     const int p = (wave * 2 + u) * 64 + lane;
     const int row = p >> 2;
-    const int c = (p & 3) ^ ((row >> 1) & 3);
+    const int c = (p & 3) ^ ((row >> 2) & 3);
     const int ar = m0 + row, br = n0 + row;
     asrc[u] = A + (int64_t)(ar < M ? ar : M - 1) * lda + c * 8;
     bsrc[u] = B + (int64_t)(br < N ? br : N - 1) * ldb + c * 8;
@@ -144,7 +151,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ A, int64_t
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
   }
   wait_vmcnt<0>();  // retire the trailing (unused) prefetches before LDS is reused
@@ -153,10 +160,11 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ A, int64_t
 
 // ---------------------------------------------------------------------------
 // LM head: workgroup = canvas rows x 256 vocabulary columns; a wave holds 64
-// rows x 128 columns = two 64-column tiles of the softmax statistics, so the
-// epilogue is local to the wave: per row and tile, the max of z and its
-// lowest column, exp(y - m) written once as bf16, l = sum exp(y - m) and
-// s = sum exp(y - m)(y - m), with y = z / T and m = zmax / T.
+// rows x 128 columns = two 64-column tiles of the softmax statistics.  Per
+// canvas row and tile a lane holds 32 of the 64 logits (its partner lane the
+// other 32): the max of z and its lowest column, exp(y - m) written once as
+// bf16, l = sum exp(y - m) and s = sum exp(y - m)(y - m), with y = z / T and
+// m = zmax / T, are reduced in registers plus one exchange with the partner.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__restrict__ A, int M, int K,
                                                               const bf16 *__restrict__ E, int V, float inv_T,
@@ -165,57 +173,72 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
   extern __shared__ __align__(16) char lds[];
   const int n0 = blockIdx.x * ES_BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
   const int m0 = blockIdx.y * ES_BM;
   f32x16_t acc[2][4];
   estream_tile<false>(A, K, M, m0, E, K, V, n0, 0, K, nullptr, 0, lds, acc);
   const int ntiles = V / 64;
 
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int tile = (n0 + wn * 128 + h * 64) / 64;
-    const int c0 = tile * 64 + (lane & 31);  // global column of fragment 2h
+  for (int i = 0; i < 2; ++i) {
+    const int row = m0 + wm * 64 + i * 32 + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int h = 0; h < 2; ++h) {
+      const int tile = (n0 + wn * 128 + h * 64) / 64;
+      // lane's columns: tile*64 + 32jj + 8q + 4g + t for jj < 2, q < 4, t < 4
+      // (register r = 4q + t of fragment 2h + jj), increasing in (jj, r)
+      const int cbase = tile * 64 + 4 * g;
+      float best = acc[i][2 * h][0];
+      int bcol = cbase;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float z0 = acc[i][2 * h][r], z1 = acc[i][2 * h + 1][r];
-        float best = z0;
-        int bcol = c0;
-        if (z1 > best) {
-          best = z1;
-          bcol = c0 + 32;
-        }
+      for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int o = 16; o > 0; o >>= 1) {
-          const float ov = __shfl_xor(best, o);
-          const int oc = __shfl_xor(bcol, o);
-          if (ov > best || (ov == best && oc < bcol)) {
-            best = ov;
-            bcol = oc;
+        for (int r = 0; r < 16; ++r) {
+          const float z = acc[i][2 * h + jj][r];
+          if (z > best) {
+            best = z;
+            bcol = cbase + 32 * jj + 8 * (r >> 2) + (r & 3);
           }
         }
-        const float m = best * inv_T;
-        const float t0 = z0 * inv_T - m, t1 = z1 * inv_T - m;
-        const float e0 = exp2f(t0 * LOG2E), e1 = exp2f(t1 * LOG2E);
-        float l = e0 + e1, sacc = e0 * t0 + e1 * t1;
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) {
-          l += __shfl_xor(l, o);
-          sacc += __shfl_xor(sacc, o);
-        }
-        const int row = m0 + wm * 64 + i * 32 + acc_r(r, lane);
-        if (row < M) {
-          const int64_t o = (int64_t)row * V + c0;
-          probs[o] = f32_to_bf16(e0);
-          probs[o + 32] = f32_to_bf16(e1);
-          if (logits) {
-            logits[o] = z0;
-            logits[o + 32] = z1;
-          }
-          if ((lane & 31) == 0) tile_stats[(int64_t)row * ntiles + tile] = make_float4(best, l, sacc, __int_as_float(bcol));
+      {
+        const float ov = __shfl_xor(best, 32);
+        const int oc = __shfl_xor(bcol, 32);
+        if (ov > best || (ov == best && oc < bcol)) {
+          best = ov;
+          bcol = oc;
         }
       }
+      const float m = best * inv_T;
+      float l = 0.f, sacc = 0.f;
+      uint32_t pk[2][8];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float t0 = acc[i][2 * h + jj][r] * inv_T - m, t1 = acc[i][2 * h + jj][r + 1] * inv_T - m;
+          const float e0 = exp2f(t0 * LOG2E), e1 = exp2f(t1 * LOG2E);
+          l += e0 + e1;
+          sacc += e0 * t0 + e1 * t1;
+          pk[jj][r >> 1] = pack_bf16x2(e0, e1);
+        }
+      l += __shfl_xor(l, 32);
+      sacc += __shfl_xor(sacc, 32);
+      if (row < M) {
+        const int64_t o = (int64_t)row * V + cbase;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            *reinterpret_cast<uint2 *>(probs + o + 32 * jj + 8 * q) = make_uint2(pk[jj][2 * q], pk[jj][2 * q + 1]);
+            if (logits) {
+              const f32x16_t &z = acc[i][2 * h + jj];
+              *reinterpret_cast<float4 *>(logits + o + 32 * jj + 8 * q) =
+                  make_float4(z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]);
+            }
+          }
+        if (g == 0) tile_stats[(int64_t)row * ntiles + tile] = make_float4(best, l, sacc, __int_as_float(bcol));
+      }
+    }
   }
 }
 
@@ -271,15 +294,20 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(GemmShape g, floa
   const int wm = wave >> 1, wn = wave & 1;
   float *out = part + (int64_t)kc * g.M * g.N;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) {
+    const int row = m0 + wm * 64 + i * 32 + (lane & 31);
+    if (row >= g.M) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 64 + i * 32 + acc_r(r, lane);
-        const int col = n0 + wn * 128 + j * 32 + (lane & 31);
-        if (row < g.M && col < g.N) out[(int64_t)row * g.N + col] = acc[i][j][r];
+      for (int q = 0; q < 4; ++q) {
+        // registers 4q..4q+3 are four consecutive columns
+        const int col = n0 + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+        if (col < g.N)
+          *reinterpret_cast<float4 *>(out + (int64_t)row * g.N + col) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
       }
+  }
 }
 
 hipError_t selfcond_bf16(const GemmShape &g, float *partials, int ksplit, hipStream_t s) {
