@@ -49,9 +49,9 @@ def lm_head_bytes(c: dict) -> float:
 
 
 def selfcond_bytes(c: dict) -> float:
-    """E^T once, the bf16 numerators, the per-tile normalisers."""
+    """E^T once and the bf16 probabilities once."""
     N, V, d = c["N"], c["V"], c["d"]
-    return float(V * d * 2 + N * V * 2 + N * (V // 64) * 4)
+    return float(V * d * 2 + N * V * 2)
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lm_head_n256_v262k_d2816.txt")

@@ -79,9 +79,9 @@ typedef struct {
 
 /* Weights (device, dtype of the config, caller-owned, read-only).
  * E [V][d] is the token-embedding table, tied to the LM head ([P3] §4.1).
- * E_t [d][V] is E transposed, produced once by dg_pack_embedding(); the
- * self-conditioning contraction streams it (required for DG_BF16, ignored
- * for DG_F32).  w_sc1 [F][d], w_sc2 [d][F]: self-conditioning FFN ([P3] §5.1).
+ * E_t [d][P] (P = dg_embedding_t_pitch(cfg) >= V) is E transposed,
+ * produced once by dg_pack_embedding(); the self-conditioning contraction
+ * streams it (required for DG_BF16, ignored for DG_F32).  w_sc1 [F][d], w_sc2 [d][F]: self-conditioning FFN ([P3] §5.1).
  * wq [Hq*hd][d], wk/wv [Hkv*hd][d], wo [d][Hq*hd]: attention projections.
  * g_attn, g_final [d]: RMSNorm gains (pre-attention, pre-LM-head). */
 typedef struct {
@@ -103,9 +103,11 @@ typedef struct {
 
 /* Per-canvas state.  Device buffers are caller-owned:
  *   tokens  int32 [N]            current canvas
- *   probs   dtype [N][V]         softmax numerators of the last step, per
- *                                64-column tile: exp(y - m_tile) (the
- *                                self-conditioning input of the next step)
+ *   probs   dtype [N][V]         softmax probabilities of the last step
+ *                                (DG_BF16: rounded to nearest even; the
+ *                                dominant token's exact value is kept in
+ *                                stats), the self-conditioning input of
+ *                                the next step
  *   stats   bytes dg_stats_bytes(): per-(row, tile) softmax statistics,
  *                                normalisers and each row's dominant token
  *                                with its exact probability; opaque
@@ -161,9 +163,16 @@ size_t dg_workspace_bytes(const dg_config *cfg, int32_t max_prefill_tokens);
 size_t dg_stats_bytes(const dg_config *cfg);
 
 /* ---- one-time preparation ----------------------------------------------- */
-/* Writes E_t [d][V] = transpose of E [V][d] (device, caller-allocated
- * V*d elements of the config dtype).  A layout copy only: E_t holds the same
- * values as E. */
+/* Row pitch, in elements, of E_t: V + 64.  At a power-of-two vocabulary the
+ * rows of an unpadded E_t lie a power of two of bytes apart, so the 256 rows
+ * one workgroup of the contraction reads together would share one cache set
+ * and memory channel.  0 if the configuration is unsupported. */
+int64_t dg_embedding_t_pitch(const dg_config *cfg);
+
+/* Writes E_t[c][r] = E[r][c] for r < V, c < d (device; E_t caller-allocated
+ * with d * dg_embedding_t_pitch(cfg) elements of the config dtype).  A layout
+ * copy only: E_t holds the same values as E; the pad columns [V, pitch) are
+ * neither written nor read. */
 dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_t, void *stream);
 
 /* [P3] §5.4 canvas initialisation: tokens[i] = the top log2(V) bits of word 0

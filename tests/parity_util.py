@@ -27,9 +27,8 @@ def ws_view(den: D.Denoiser, name: str, dtype, shape):
 
 def gpu_probs(den: D.Denoiser) -> np.ndarray:
     cfg = den.cfg
-    N, V = cfg.canvas_len, cfg.vocab
-    num = den.canvas.probs.float().view(N, V // B.TILE_V, B.TILE_V)
-    p = (num * den.canvas.tile_scale(cfg)[:, :, None]).view(N, V)
+    N = cfg.canvas_len
+    p = den.canvas.probs.float().clone()
     if cfg.dtype == B.DG_BF16:  # the dominant token's probability is kept exactly
         a, pa = den.canvas.top(cfg)
         p[torch.arange(N, device=p.device), a.long()] = pa

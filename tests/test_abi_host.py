@@ -174,3 +174,17 @@ def test_other_entry_point_validation(lib):
     bad.vocab = 1000
     assert L.dg_should_stop(ctypes.byref(bad), ctypes.byref(fake_canvas()), 3,
                             ctypes.byref(stop), None, None) == B.DG_ERR_UNSUPPORTED
+
+
+def test_embedding_t_pitch(lib):
+    """The transposed table's row pitch is V + 64 elements, so its rows are
+    never a power of two of bytes apart; unsupported configurations give 0."""
+    for i in (1, 2, 3):
+        cfg = cfg_of(i)
+        p = B.dg_embedding_t_pitch(cfg)
+        assert p == cfg.vocab + 64
+        row_bytes = p * (2 if cfg.dtype == B.DG_BF16 else 4)
+        assert row_bytes & (row_bytes - 1) != 0
+    bad = cfg_of(2)
+    bad.vocab = 1000
+    assert B.dg_embedding_t_pitch(bad) == 0

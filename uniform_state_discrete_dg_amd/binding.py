@@ -67,6 +67,7 @@ SIGNATURES = {
     "dg_validate_config": (c_i32, [P(dg_config)]),
     "dg_workspace_bytes": (c_sz, [P(dg_config), c_i32]),
     "dg_stats_bytes": (c_sz, [P(dg_config)]),
+    "dg_embedding_t_pitch": (ctypes.c_int64, [P(dg_config)]),
     "dg_pack_embedding": (c_i32, [P(dg_config), vp, vp, vp]),
     "dg_canvas_init": (c_i32, [P(dg_config), P(dg_canvas), c_u64, c_u32, vp]),
     "dg_prefill_append": (c_i32, [P(dg_config), P(dg_weights), P(dg_kv_cache), vp, c_i32, vp, vp,
@@ -141,6 +142,10 @@ def dg_workspace_bytes(cfg: dg_config, max_prefill_tokens: int = 0) -> int:
 
 def dg_stats_bytes(cfg: dg_config) -> int:
     return int(lib().dg_stats_bytes(ctypes.byref(cfg)))
+
+
+def dg_embedding_t_pitch(cfg: dg_config) -> int:
+    return int(lib().dg_embedding_t_pitch(ctypes.byref(cfg)))
 
 
 def dg_pack_embedding(cfg: dg_config, E: torch.Tensor, E_t: torch.Tensor, stream=None) -> None:
@@ -248,7 +253,7 @@ class DeviceWeights:
         dt = torch_dtype(cfg)
         t = {k: inp[k].to(device=device, dtype=dt).contiguous()
              for k in ("E", "w1", "w2", "wq", "wk", "wv", "wo", "g_attn", "g_final")}
-        t["E_t"] = torch.empty((cfg.d_model, cfg.vocab), dtype=dt, device=device)
+        t["E_t"] = torch.empty((cfg.d_model, dg_embedding_t_pitch(cfg)), dtype=dt, device=device)
         dg_pack_embedding(cfg, t["E"], t["E_t"], stream)
         self.t = t
         self.s = dg_weights(*(t[k].data_ptr() for k in ("E", "E_t", "w1", "w2", "wq", "wk", "wv",
@@ -290,7 +295,8 @@ class DeviceCanvas:
                            self.accept.data_ptr(), self.status.data_ptr(), 0, 0, 0, 0)
 
     def tile_scale(self, cfg: dg_config) -> torch.Tensor:
-        """Per-(row, tile) normalisers written by the last step ([N][V/64] f32)."""
+        """Per-(row, tile) normalisers of the last step ([N][V/64] f32): the
+        factors that turned the tile-local numerators into probabilities."""
         N, nt = cfg.canvas_len, cfg.vocab // TILE_V
         return self.stats[N * nt * 16:N * nt * 20].view(torch.float32).view(N, nt)
 

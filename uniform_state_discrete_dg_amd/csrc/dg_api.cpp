@@ -50,6 +50,8 @@ dg_status check_config(const dg_config *c) {
 
 // Self-conditioning split of K = V over workgroups (bf16 path): about one
 // work item per CU.
+int64_t et_pitch(const dg_config *c) { return (int64_t)c->vocab + 64; }
+
 int selfcond_ksplit(const dg_config *c) {
   const int bm = dg::estream_bm(c->canvas_len);
   const int ntile = (c->d_model + 255) / 256 * ((c->canvas_len + bm - 1) / bm);
@@ -227,16 +229,22 @@ size_t dg_stats_bytes(const dg_config *cfg) {
   return (size_t)cfg->canvas_len * (nt * (sizeof(float4) + sizeof(float)) + sizeof(float2));
 }
 
+int64_t dg_embedding_t_pitch(const dg_config *cfg) {
+  if (check_config(cfg) != DG_OK) return 0;
+  return et_pitch(cfg);
+}
+
 dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_t, void *stream) {
   dg_status st = check_config(cfg);
   if (st != DG_OK) return st;
   if (!E || !E_t) return DG_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (cfg->dtype == DG_BF16)
-    DG_TRY(dg::transpose<bf16>(static_cast<const bf16 *>(E), cfg->vocab, cfg->d_model, static_cast<bf16 *>(E_t), s));
+    DG_TRY(dg::transpose<bf16>(static_cast<const bf16 *>(E), cfg->vocab, cfg->d_model, static_cast<bf16 *>(E_t),
+                               et_pitch(cfg), s));
   else
     DG_TRY(dg::transpose<float>(static_cast<const float *>(E), cfg->vocab, cfg->d_model,
-                                static_cast<float *>(E_t), s));
+                                static_cast<float *>(E_t), et_pitch(cfg), s));
   return DG_OK;
 }
 
@@ -359,16 +367,16 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     if (bf) {
       const int ks = selfcond_ksplit(cfg);
       float *part = reinterpret_cast<float *>(base + L.sc_part);
-      dg::GemmShape g{cv->probs, V, w->E_t, V, N, d, V, tscale, ntiles};
+      dg::GemmShape g{cv->probs, V, w->E_t, et_pitch(cfg), N, d, V};
       {
         ProfScope ps(g_prof_sc, s);
         DG_TRY(dg::selfcond_bf16(g, part, ks, s));
       }
-      DG_TRY(dg::selfcond_reduce(part, ks, N, d, top, static_cast<const uint16_t *>(cv->probs), tscale, ntiles, V,
+      DG_TRY(dg::selfcond_reduce(part, ks, N, d, top, static_cast<const uint16_t *>(cv->probs), V,
                                  static_cast<const uint16_t *>(w->E), sc, s));
     } else {
       dg::GemmShapeF32 g{static_cast<const float *>(cv->probs), V, 1, static_cast<const float *>(w->E), 1, d,
-                         N, d, V, tscale, ntiles};
+                         N, d, V, nullptr, 0};
       DG_TRY(dg::gemm_f32(g, epi_store(sc, true, d, d, 0), s));
     }
     dg::Epi eg = epi_store(G, true, F, F, 0);
@@ -430,12 +438,14 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     }
     DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, tscale, nrm,
                            static_cast<const uint16_t *>(w->E), d, top, s));
+    DG_TRY(dg::normalize_probs<bf16>(static_cast<bf16 *>(cv->probs), tscale, N, V, s));
   } else {
     DG_TRY(dg::rmsnorm_rows<float>(h1, static_cast<const float *>(w->g_final), N, d, cfg->rms_eps, nrm, nullptr, s));
     dg::GemmShapeF32 g{nrm, d, 1, static_cast<const float *>(w->E), d, 1, N, V, d, nullptr, 0};
     DG_TRY(dg::gemm_f32(g, epi_store(logits, true, V, V, 0), s));
     DG_TRY(dg::tile_stats_f32(logits, N, V, inv_T, static_cast<float *>(cv->probs), tstats, s));
     DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, tscale, nullptr, nullptr, d, top, s));
+    DG_TRY(dg::normalize_probs<float>(static_cast<float *>(cv->probs), tscale, N, V, s));
   }
   // 5. accept / re-noise / stop flags
   DG_TRY(dg::select_step(cv->entropy, cv->argmax, cv->tokens, cv->accept, cv->status, N, ilog2(V), (double)gamma,
@@ -511,9 +521,9 @@ dg_status dg_test_selfcond(const dg_config *cfg, const dg_weights *w, const void
   if (cfg->dtype == DG_BF16) {
     const int ks = selfcond_ksplit(cfg);
     float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + L.sc_part);
-    dg::GemmShape g{P, V, w->E_t, V, N, d, V, nullptr, 0};
+    dg::GemmShape g{P, V, w->E_t, et_pitch(cfg), N, d, V};
     DG_TRY(dg::selfcond_bf16(g, part, ks, s));
-    DG_TRY(dg::selfcond_reduce(part, ks, N, d, nullptr, nullptr, nullptr, 0, V, nullptr, static_cast<float *>(S), s));
+    DG_TRY(dg::selfcond_reduce(part, ks, N, d, nullptr, nullptr, V, nullptr, static_cast<float *>(S), s));
   } else {
     dg::GemmShapeF32 g{static_cast<const float *>(P), V, 1, static_cast<const float *>(w->E), 1, d, N, d, V,
                        nullptr, 0};

@@ -31,9 +31,6 @@ struct GemmShape {
   const void *B;          // [N][K] (ldb)
   int64_t ldb;
   int M, N, K;
-  // optional per-(row, 64-column tile of K) multiplier of A (nullable)
-  const float *a_scale;
-  int64_t a_scale_ld;
 };
 
 // fp32 activation x bf16 weight GEMM on the bf16 MFMA with the activation
@@ -51,8 +48,9 @@ struct SplitGemm {
 hipError_t gemm_split(const SplitGemm &g, hipStream_t s);
 // Canvas rows per workgroup of the two table-streaming kernels (128 or 256).
 int estream_bm(int M);
-// The self-conditioning contraction: A = probs (scaled per tile), B = E^T,
-// K = V split in ksplit ranges; writes f32 partials [ksplit][M][N].
+// The self-conditioning contraction: A = probs (bf16 probabilities, [M][lda]),
+// B = E^T ([N][ldb]), K = V split in ksplit ranges; writes f32 partials
+// [ksplit][M][N].
 hipError_t selfcond_bf16(const GemmShape &g, float *partials, int ksplit, hipStream_t s);
 // fp32 SIMT GEMM: C[m][n] = sum_k A[m*sam + k*sak] * B[n*sbn + k*sbk].
 struct GemmShapeF32 {
@@ -113,12 +111,17 @@ template <typename T>
 hipError_t rmsnorm_rows(const float *x, const T *g, int n, int d, float eps, float *out, bf16 *out_bf16,
                         hipStream_t s);
 // S (fp32 [N][d]) = sum of the ksplit partials + exact correction of each
-// row's dominant token (top = (token bits, exact p); nullable).
+// row's dominant token (top = (token bits, exact p); nullable): the
+// contraction used the bf16 value probs[row][a].
 hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top,
-                           const uint16_t *probs, const float *tile_scale, int ntiles, int V,
-                           const uint16_t *E, float *out, hipStream_t s);
+                           const uint16_t *probs, int V, const uint16_t *E, float *out, hipStream_t s);
+// In place: probs[row][v] = round(probs[row][v] * tile_scale[row][v / 64]),
+// numerators -> probabilities (bf16: round to nearest even).
 template <typename T>
-hipError_t transpose(const T *in, int rows, int cols, T *out, hipStream_t s);
+hipError_t normalize_probs(T *probs, const float *tile_scale, int N, int V, hipStream_t s);
+// out[c * ld_out + r] = in[r * cols + c]
+template <typename T>
+hipError_t transpose(const T *in, int rows, int cols, T *out, int64_t ld_out, hipStream_t s);
 hipError_t copy_bytes(const void *src, void *dst, size_t bytes, hipStream_t s);
 
 // Selection and canvas.

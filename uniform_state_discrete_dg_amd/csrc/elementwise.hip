@@ -79,12 +79,11 @@ template hipError_t rmsnorm_rows<bf16>(const float *, const bf16 *, int, int, fl
                                        hipStream_t);
 
 // Merge of the self-conditioning split-K partials into S (fp32), plus the
-// exact correction of each row's dominant token: the contraction used
-// p~ = bf16(bf16(num_a) * c_t) for token a, the previous step's exact
+// exact correction of each row's dominant token: the contraction used the
+// bf16 probability p~ = probs[row][a] for token a, the previous step's exact
 // probability of a is p_a, so S += (p_a - p~) E[a].
 __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int ksplit, int N, int d,
-                                       const float2 *__restrict__ top, const bf16 *__restrict__ probs,
-                                       const float *__restrict__ tile_scale, int ntiles, int V,
+                                       const float2 *__restrict__ top, const bf16 *__restrict__ probs, int V,
                                        const bf16 *__restrict__ E, float *__restrict__ out) {
   const int row = blockIdx.y;
   const int k = blockIdx.x * blockDim.x + threadIdx.x;
@@ -96,23 +95,71 @@ __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int kspli
   if (top) {
     const float2 tp = top[row];
     const int a = __float_as_int(tp.x);
-    const float used = bf16_to_f32(f32_to_bf16(bf16_to_f32(probs[(int64_t)row * V + a]) *
-                                               tile_scale[(int64_t)row * ntiles + a / TILE]));
+    const float used = bf16_to_f32(probs[(int64_t)row * V + a]);
     acc += (tp.y - used) * bf16_to_f32(E[(int64_t)a * d + k]);
   }
   out[i] = acc;
 }
 
 hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top, const uint16_t *probs,
-                           const float *tile_scale, int ntiles, int V, const uint16_t *E, float *out,
-                           hipStream_t s) {
+                           int V, const uint16_t *E, float *out, hipStream_t s) {
   hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((d + 255) / 256, N), dim3(256), 0, s, part, ksplit, N, d,
-                     top, probs, tile_scale, ntiles, V, E, out);
+                     top, probs, V, E, out);
+  return hipGetLastError();
+}
+
+// Numerators -> probabilities, in place: 8 consecutive columns (one 64-column
+// tile's multiplier) per thread.
+__global__ void normalize_bf16_kernel(bf16 *__restrict__ probs, const float *__restrict__ tile_scale, int64_t chunks,
+                                      int V) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = i * 8;
+    const int64_t row = e / V;
+    const int col = (int)(e - row * V);
+    const float c = tile_scale[row * (V / TILE) + col / TILE];
+    uint4 v = reinterpret_cast<const uint4 *>(probs)[i];
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = pack_bf16x2(__uint_as_float(w[k] << 16) * c, __uint_as_float(w[k] & 0xffff0000u) * c);
+    reinterpret_cast<uint4 *>(probs)[i] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+__global__ void normalize_f32_kernel(float *__restrict__ probs, const float *__restrict__ tile_scale, int64_t chunks,
+                                     int V) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = i * 4;
+    const int64_t row = e / V;
+    const int col = (int)(e - row * V);
+    const float c = tile_scale[row * (V / TILE) + col / TILE];
+    float4 v = reinterpret_cast<const float4 *>(probs)[i];
+    v.x *= c;
+    v.y *= c;
+    v.z *= c;
+    v.w *= c;
+    reinterpret_cast<float4 *>(probs)[i] = v;
+  }
+}
+
+template <>
+hipError_t normalize_probs<bf16>(bf16 *probs, const float *tile_scale, int N, int V, hipStream_t s) {
+  const int64_t chunks = (int64_t)N * V / 8;
+  const int64_t blocks = (chunks + 255) / 256;
+  hipLaunchKernelGGL(normalize_bf16_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s,
+                     probs, tile_scale, chunks, V);
+  return hipGetLastError();
+}
+template <>
+hipError_t normalize_probs<float>(float *probs, const float *tile_scale, int N, int V, hipStream_t s) {
+  const int64_t chunks = (int64_t)N * V / 4;
+  const int64_t blocks = (chunks + 255) / 256;
+  hipLaunchKernelGGL(normalize_f32_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s,
+                     probs, tile_scale, chunks, V);
   return hipGetLastError();
 }
 
 template <typename T>
-__global__ void transpose_kernel(const T *__restrict__ in, int rows, int cols, T *__restrict__ out) {
+__global__ void transpose_kernel(const T *__restrict__ in, int rows, int cols, T *__restrict__ out, int64_t ld_out) {
   __shared__ T tile[32][33];
   const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
@@ -123,18 +170,18 @@ __global__ void transpose_kernel(const T *__restrict__ in, int rows, int cols, T
   __syncthreads();
   for (int k = ty; k < 32; k += 8) {
     const int c = c0 + k, r = r0 + tx;
-    if (r < rows && c < cols) out[(int64_t)c * rows + r] = tile[tx][k];
+    if (r < rows && c < cols) out[(int64_t)c * ld_out + r] = tile[tx][k];
   }
 }
 
 template <typename T>
-hipError_t transpose(const T *in, int rows, int cols, T *out, hipStream_t s) {
+hipError_t transpose(const T *in, int rows, int cols, T *out, int64_t ld_out, hipStream_t s) {
   dim3 grid((cols + 31) / 32, (rows + 31) / 32);
-  hipLaunchKernelGGL(transpose_kernel<T>, grid, dim3(256), 0, s, in, rows, cols, out);
+  hipLaunchKernelGGL(transpose_kernel<T>, grid, dim3(256), 0, s, in, rows, cols, out, ld_out);
   return hipGetLastError();
 }
-template hipError_t transpose<float>(const float *, int, int, float *, hipStream_t);
-template hipError_t transpose<bf16>(const bf16 *, int, int, bf16 *, hipStream_t);
+template hipError_t transpose<float>(const float *, int, int, float *, int64_t, hipStream_t);
+template hipError_t transpose<bf16>(const bf16 *, int, int, bf16 *, int64_t, hipStream_t);
 
 __global__ void copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)

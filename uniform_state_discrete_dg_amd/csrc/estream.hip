@@ -50,17 +50,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ int slot16(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
 
-__device__ __forceinline__ bf16x8_t scale_frag(uint4 v, float s) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = __uint_as_float(w[i] << 16) * s;
-    const float hi = __uint_as_float(w[i] & 0xffff0000u) * s;
-    w[i] = pack_bf16x2(lo, hi);
-  }
-  return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-}
-
 }  // namespace
 
 // Accumulates acc[i][j] (wave tile: canvas rows wm*64 + 32i, table rows
@@ -68,13 +57,10 @@ __device__ __forceinline__ bf16x8_t scale_frag(uint4 v, float s) {
 // lane holds canvas row 32i + (lane & 31) and, in register r, table row
 // 8 (r >> 2) + 4 (lane >> 5) + (r & 3) of the fragment.  A: [M][lda] canvas rows m0..,
 // B: [N][ldb] table rows n0..; rows past M / N read a clamped valid row and
-// only feed accumulators the epilogues discard.  With SCALE_A, A[m][k] is
-// multiplied by a_scale[m][k / 64] (a 64-column tile) as it is read.
-template <bool SCALE_A>
+// only feed accumulators the epilogues discard.
 __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ A, int64_t lda, int M, int m0,
                                              const bf16 *__restrict__ B, int64_t ldb, int N, int n0, int kb,
-                                             int ke, const float *__restrict__ a_scale, int64_t a_scale_ld,
-                                             char *lds, f32x16_t (&acc)[2][4]) {
+                                             int ke, char *lds, f32x16_t (&acc)[2][4]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r32 = lane & 31, g = lane >> 5;
@@ -98,18 +84,9 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ A, int64_t
     asrc[u] = A + (int64_t)(ar < M ? ar : M - 1) * lda + c * 8;
     bsrc[u] = B + (int64_t)(br < N ? br : N - 1) * ldb + c * 8;
   }
-  // per-lane rows of the two A fragments (for the scale lookup)
-  int srow[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rr = m0 + wm * 64 + i * 32 + r32;
-    srow[i] = rr < M ? rr : M - 1;
-  }
-
   const int nk = (ke - kb) / ES_BK;
   if (nk <= 0) return;
   const int klast = kb + ES_BK * (nk - 1);
-  float sc[ES_STAGES][2];
   auto issue = [&](int slice, int stage) {
     const int k0 = min(kb + ES_BK * slice, klast);
     char *st = lds + stage * 2 * ES_SLICE;
@@ -118,13 +95,9 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ A, int64_t
       __builtin_amdgcn_global_load_lds(asrc[u] + k0, st + (wave * 2 + u) * 1024, 16, 0, 0);
       __builtin_amdgcn_global_load_lds(bsrc[u] + k0, st + ES_SLICE + (wave * 2 + u) * 1024, 16, 0, 0);
     }
-    if (SCALE_A) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) sc[stage][i] = a_scale[(int64_t)srow[i] * a_scale_ld + (k0 >> 6)];
-    }
   };
-  // loads per slice per wave: 4 DMA (+2 scale loads)
-  constexpr int PER = SCALE_A ? 6 : 4;
+  // loads per slice per wave: 4 DMA
+  constexpr int PER = 4;
 
   issue(0, 0);
   issue(1, 1);
@@ -141,10 +114,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ A, int64_t
       const int c = kk * 2 + g;
       bf16x8_t fa[2], fb[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint4 v = sa[slot16(wm * 64 + i * 32 + r32, c)];
-        fa[i] = SCALE_A ? scale_frag(v, sc[stage][i]) : __builtin_bit_cast(bf16x8_t, v);
-      }
+      for (int i = 0; i < 2; ++i) fa[i] = __builtin_bit_cast(bf16x8_t, sa[slot16(wm * 64 + i * 32 + r32, c)]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, sb[slot16(wn * 128 + j * 32 + r32, c)]);
 #pragma unroll
@@ -176,7 +146,7 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
   const int m0 = blockIdx.y * ES_BM;
   f32x16_t acc[2][4];
-  estream_tile<false>(A, K, M, m0, E, K, V, n0, 0, K, nullptr, 0, lds, acc);
+  estream_tile(A, K, M, m0, E, K, V, n0, 0, K, lds, acc);
   const int ntiles = V / 64;
 
 #pragma unroll
@@ -279,17 +249,13 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(GemmShape g, floa
   const int mb = item % mblocks;
   const int kc = (item / mblocks) / ntn, nt = (item / mblocks) % ntn;
   const int m0 = mb * ES_BM;
-  const int nslices = g.K / 64;  // 64-aligned chunks keep every chunk inside whole scale tiles
+  const int nslices = g.K / 64;  // chunks of whole 64-column units (two slices)
   const int kb = (int)((int64_t)nslices * kc / ksplit) * 64;
   const int ke = (int)((int64_t)nslices * (kc + 1) / ksplit) * 64;
   const int n0 = nt * ES_BN;
   f32x16_t acc[2][4];
-  if (g.a_scale)
-    estream_tile<true>(static_cast<const bf16 *>(g.A), g.lda, g.M, m0, static_cast<const bf16 *>(g.B), g.ldb, g.N,
-                       n0, kb, ke, g.a_scale, g.a_scale_ld, lds, acc);
-  else
-    estream_tile<false>(static_cast<const bf16 *>(g.A), g.lda, g.M, m0, static_cast<const bf16 *>(g.B), g.ldb, g.N,
-                        n0, kb, ke, nullptr, 0, lds, acc);
+  estream_tile(static_cast<const bf16 *>(g.A), g.lda, g.M, m0, static_cast<const bf16 *>(g.B), g.ldb, g.N, n0, kb,
+               ke, lds, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   float *out = part + (int64_t)kc * g.M * g.N;
