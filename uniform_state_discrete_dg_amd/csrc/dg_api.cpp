@@ -3,6 +3,7 @@
 // denoising step / one prefill append.  No device memory is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -63,9 +64,9 @@ int selfcond_ksplit(const dg_config *c) {
 }
 
 struct Layout {
-  size_t h0, h1, nrm, nrm16, sc, g, q, kc, vc, o, ap_o, ap_ml, sc_part, logits, total;
+  size_t h0, h1, nrm, nrm16, sc, g, q, kc, vc, o, ap_o, ap_ml, sc_part, gpart, logits, total;
   // prefill view (same region)
-  size_t p_x, p_nrm, p_q, p_ap_o, p_ap_ml, p_total;
+  size_t p_x, p_nrm, p_q, p_ap_o, p_ap_ml, p_gpart, p_total;
 };
 
 // Activations are fp32 in the workspace for both dtypes (the bf16 path
@@ -98,6 +99,15 @@ Layout layout(const dg_config *c, int32_t nprefill, bool with_logits) {
   L.ap_o = take((size_t)splits * Hq * N * hd * 4);
   L.ap_ml = take((size_t)splits * Hq * N * 2 * 4);
   L.sc_part = take(bf ? (size_t)selfcond_ksplit(c) * N * d * 4 : 0);
+  if (bf) {  // K-split partials of the projections, the largest of the step's four
+    const int nqkv[3] = {(int)(Hq * hd), (int)(Hkv * hd), (int)(Hkv * hd)};
+    const int nd[1] = {(int)d}, nf[1] = {(int)F};
+    size_t m = dg::gemm_split_part_bytes((int)N, (int)d, nqkv, 3);
+    m = std::max(m, dg::gemm_split_part_bytes((int)N, (int)(Hq * hd), nd, 1));
+    m = std::max(m, dg::gemm_split_part_bytes((int)N, (int)d, nf, 1));
+    m = std::max(m, dg::gemm_split_part_bytes((int)N, (int)F, nd, 1));
+    L.gpart = take(m);
+  }
   L.logits = take((!bf || with_logits) ? N * V * 4 : 0);
   L.total = off;
   // prefill
@@ -109,6 +119,11 @@ Layout layout(const dg_config *c, int32_t nprefill, bool with_logits) {
   dg::attention_plan((int)(n ? n : 1), (int)Hq, 1 << 20, &splits, &kps);
   L.p_ap_o = take((size_t)splits * Hq * n * hd * 4);
   L.p_ap_ml = take((size_t)splits * Hq * n * 2 * 4);
+  if (bf && n) {
+    const int nkvq[3] = {(int)(Hkv * hd), (int)(Hkv * hd), (int)(Hq * hd)};
+    L.p_gpart = take(std::max(dg::gemm_split_part_bytes((int)n, (int)d, nkvq, 3),
+                              dg::gemm_split_part_bytes((int)n, (int)d, nkvq, 2)));
+  }
   L.p_total = off;
   return L;
 }
@@ -168,8 +183,9 @@ bool canvas_ok(const dg_canvas *cv) {
 
 // Dense projections C_i[M][N_i] = A[M][K] W_i[N_i][K]^T (fp32 activation A,
 // up to three weight matrices sharing it) with epilogues e_i.
+// `part` holds the K-split partials (gemm_split_part_bytes; bf16 only).
 hipError_t proj(const dg_config *c, const float *A, int64_t lda, int M, int K, int count, const void *const *W,
-                const int *Nout, const dg::Epi *e, hipStream_t s) {
+                const int *Nout, const dg::Epi *e, float *part, hipStream_t s) {
   if (c->dtype == DG_BF16) {
     dg::SplitGemm g{};
     g.A = A;
@@ -182,6 +198,8 @@ hipError_t proj(const dg_config *c, const float *A, int64_t lda, int M, int K, i
       g.N[i] = Nout[i];
       g.e[i] = e[i];
     }
+    g.part = part;
+    g.ksplit = dg::gemm_split_plan(M, K, Nout, count);
     return dg::gemm_split(g, s);
   }
   for (int i = 0; i < count; ++i) {
@@ -193,8 +211,8 @@ hipError_t proj(const dg_config *c, const float *A, int64_t lda, int M, int K, i
 }
 
 hipError_t proj1(const dg_config *c, const float *A, int64_t lda, int M, int K, const void *W, int Nout,
-                 const dg::Epi &e, hipStream_t s) {
-  return proj(c, A, lda, M, K, 1, &W, &Nout, &e, s);
+                 const dg::Epi &e, float *part, hipStream_t s) {
+  return proj(c, A, lda, M, K, 1, &W, &Nout, &e, part, s);
 }
 
 }  // namespace
@@ -297,7 +315,7 @@ dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cac
   const dg::Epi E3[3] = {epi_store(kbase, true, hd, hd, (int64_t)cap * hd),
                          epi_store(vbase, true, hd, hd, (int64_t)cap * hd),
                          epi_store(q, true, hd, hd, (int64_t)n * hd)};
-  DG_TRY(proj(cfg, nrm, d, n, d, attn_out ? 3 : 2, W, No, E3, s));
+  DG_TRY(proj(cfg, nrm, d, n, d, attn_out ? 3 : 2, W, No, E3, reinterpret_cast<float *>(base + L.p_gpart), s));
   if (attn_out) {
     dg::AttnArgs a{};
     a.q = q;
@@ -357,6 +375,7 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
   float4 *tstats = reinterpret_cast<float4 *>(stats);
   float *tscale = reinterpret_cast<float *>(stats + (size_t)N * ntiles * sizeof(float4));
   float2 *top = reinterpret_cast<float2 *>(stats + (size_t)N * ntiles * (sizeof(float4) + sizeof(float)));
+  float *gpart = reinterpret_cast<float *>(base + L.gpart);
 
   // 1. embeddings (+ self-conditioning from the previous step's probabilities)
   if (bf)
@@ -381,11 +400,11 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     }
     dg::Epi eg = epi_store(G, true, F, F, 0);
     eg.kind = dg::EPI_GELU;
-    DG_TRY(proj1(cfg, sc, d, N, d, w->w_sc1, F, eg, s));
+    DG_TRY(proj1(cfg, sc, d, N, d, w->w_sc1, F, eg, gpart, s));
     dg::Epi ea = epi_store(h0, true, d, d, 0);
     ea.kind = dg::EPI_ADD;
     ea.resid = h0;
-    DG_TRY(proj1(cfg, G, F, N, F, w->w_sc2, d, ea, s));
+    DG_TRY(proj1(cfg, G, F, N, F, w->w_sc2, d, ea, gpart, s));
   }
   // 2. RMSNorm, Q/K/V of the canvas (the canvas keys stay in the workspace)
   if (bf)
@@ -397,7 +416,7 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     const int No[3] = {Hq * hd, Hkv * hd, Hkv * hd};
     const dg::Epi E3[3] = {epi_store(q, true, hd, hd, (int64_t)N * hd), epi_store(kc, true, hd, hd, (int64_t)N * hd),
                            epi_store(vc, true, hd, hd, (int64_t)N * hd)};
-    DG_TRY(proj(cfg, nrm, d, N, d, 3, W, No, E3, s));
+    DG_TRY(proj(cfg, nrm, d, N, d, 3, W, No, E3, gpart, s));
   }
   // 3. bidirectional attention over [cache || canvas], output projection
   dg::AttnArgs a{};
@@ -425,7 +444,7 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     dg::Epi ea = epi_store(h1, true, d, d, 0);
     ea.kind = dg::EPI_ADD;
     ea.resid = h0;
-    DG_TRY(proj1(cfg, o, Hq * hd, N, Hq * hd, w->wo, d, ea, s));
+    DG_TRY(proj1(cfg, o, Hq * hd, N, Hq * hd, w->wo, d, ea, gpart, s));
   }
   // 4. final RMSNorm, tied LM head with the softmax/entropy statistics
   float *logits = reinterpret_cast<float *>(base + L.logits);

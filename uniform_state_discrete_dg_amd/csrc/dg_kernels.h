@@ -13,7 +13,7 @@ typedef uint16_t bf16;  // raw bfloat16 bits
 //   index(row, col) = row * rstride + (col / cdiv) * chi + (col % cdiv)
 // which covers plain row-major outputs (cdiv >= N) and the head-split
 // layouts of Q/K/V ([head][row][hd]: cdiv = hd, chi = head stride).
-enum EpiKind { EPI_STORE = 0, EPI_GELU = 1, EPI_ADD = 2, EPI_PARTIAL = 3 };
+enum EpiKind { EPI_STORE = 0, EPI_GELU = 1, EPI_ADD = 2 };
 struct Epi {
   int kind;
   void *out;
@@ -22,7 +22,6 @@ struct Epi {
   int cdiv;
   int64_t chi;
   const float *resid;    // EPI_ADD: out = resid + acc (f32, same index)
-  int64_t split_stride;  // EPI_PARTIAL: f32 out + blockIdx.z * split_stride
 };
 
 struct GemmShape {
@@ -35,7 +34,9 @@ struct GemmShape {
 
 // fp32 activation x bf16 weight GEMM on the bf16 MFMA with the activation
 // split in two bf16 terms: C_seg[M][N_seg] = A[M][K] B_seg[N_seg][K]^T for up
-// to three weight matrices sharing A (grid.z); K % 64 == 0.
+// to three weight matrices sharing A; K % 32 == 0.  With ksplit > 1 the K
+// range is split over workgroups whose fp32 partials ([seg][ksplit][M][N_seg]
+// in `part`) are summed by a second kernel that applies the epilogue.
 struct SplitGemm {
   const float *A;
   int64_t lda;
@@ -44,7 +45,13 @@ struct SplitGemm {
   int N[3];
   Epi e[3];
   int count;
+  float *part;
+  int ksplit;
 };
+// K-split the planner picks for a shape (a function of K only).
+int gemm_split_plan(int M, int K, const int *N, int count);
+// Bytes of partials gemm_split needs for that plan (0 when ksplit == 1).
+size_t gemm_split_part_bytes(int M, int K, const int *N, int count);
 hipError_t gemm_split(const SplitGemm &g, hipStream_t s);
 // Canvas rows per workgroup of the two table-streaming kernels (128 or 256).
 int estream_bm(int M);

@@ -4,39 +4,11 @@
 // self-conditioning FFN) on the gfx950 32x32x16 bf16 MFMA with fp32
 // accumulation, plus the fp32 SIMT GEMM of the fp32 configuration.  (The
 // two table-streaming contractions live in estream.hip.)
-// All operands are K-contiguous ("NT"): A[M][K] and B[N][K].  K is staged
-// through LDS in 64-wide slices (two buffers, global loads for slice k+1 in
-// flight while slice k feeds the MFMAs); 16-byte chunks of each LDS row are
-// XOR-swizzled by the row index so the 32 rows a fragment read touches fall
-// in distinct banks.
+// All operands are K-contiguous ("NT"): A[M][K] and B[N][K].
 #include "dg_device.h"
 #include "dg_kernels.h"
 
 namespace dg {
-
-template <int BM_, int BN_, int WGM_, int WGN_>
-struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
-  static constexpr int BK = 64;
-  static constexpr int NT = WGM * WGN * 64;
-  static constexpr int WM = BM / WGM, WN = BN / WGN;
-  static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int A_VEC = BM * BK / 8;  // 16-byte vectors per slice
-  static constexpr int B_VEC = BN * BK / 8;
-  static constexpr int A_PT = A_VEC / NT, B_PT = B_VEC / NT;
-  static constexpr int LDS_VEC = 2 * (A_VEC + B_VEC);
-  static_assert(A_VEC % NT == 0 && B_VEC % NT == 0, "tile/thread mismatch");
-  static_assert(FM >= 1 && FN >= 1, "wave tile too small");
-};
-
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
-
-// Row/column of accumulator element r of lane `lane` in fragment (i, j),
-// relative to the wave tile origin (32x32 MFMA output layout).
-__device__ __forceinline__ int acc_row(int i, int r, int lane) {
-  return i * 32 + (r & 3) + 4 * (lane >> 5) + 8 * (r >> 2);
-}
-__device__ __forceinline__ int acc_col(int j, int lane) { return j * 32 + (lane & 31); }
 
 __device__ __forceinline__ void epi_store(const Epi &e, int row, int col, float v) {
   const int64_t idx = (int64_t)row * e.rstride + (int64_t)(col / e.cdiv) * e.chi + (col % e.cdiv);
@@ -45,9 +17,7 @@ __device__ __forceinline__ void epi_store(const Epi &e, int row, int col, float 
     case EPI_ADD: v += e.resid[idx]; break;
     default: break;
   }
-  if (e.kind == EPI_PARTIAL) {
-    static_cast<float *>(e.out)[(int64_t)blockIdx.z * e.split_stride + idx] = v;
-  } else if (e.out_f32) {
+  if (e.out_f32) {
     static_cast<float *>(e.out)[idx] = v;
   } else {
     static_cast<bf16 *>(e.out)[idx] = f32_to_bf16(v);
@@ -59,130 +29,220 @@ __device__ __forceinline__ void epi_store(const Epi &e, int row, int col, float 
 // weights.  Each activation is split into two bf16 terms, a = hi + lo with
 // hi = bf16(a) and lo = bf16(a - hi) (16 significant bits), so one fp32
 // product costs two MFMAs and keeps ~1e-5 relative accuracy; the weights
-// are exact in bf16.  64x64 tiles, 4 waves; up to three weight matrices
-// (Q, K, V) share the activation operand in one launch (blockIdx.z).
+// are exact in bf16.
+//
+// At a 256-row canvas these contractions are small (M = 256, N and K a few
+// thousand), so the work is cut into 64 x 128 output tiles and, along K,
+// into ranges of 512 (a 256 x 2816 x 2816 product: 88 tiles x 6 ranges =
+// 528 workgroups, two per compute unit).  Each workgroup
+// (4 waves, wave tile 32 rows x 64 columns) streams its A rows (fp32) and
+// B rows (bf16) through a 4-stage LDS ring fed by the DMA form of the
+// vector load, 32 k per slice, three slices ahead of the MFMAs; the split of
+// A into hi/lo happens on the fragment read.  The MFMA takes the weight
+// fragment first, so a lane's accumulators are one output row and runs of
+// four consecutive output columns.
 // ---------------------------------------------------------------------------
-using SmallTile = TileCfg<64, 64, 2, 2>;
+namespace {
+constexpr int PG_NT = 256;
+constexpr int PG_BM = 64, PG_BN = 128, PG_BK = 32, PG_STAGES = 4;
+constexpr int PG_ASLICE = PG_BM * PG_BK * 4;  // fp32 A slice: 8 KB
+constexpr int PG_BSLICE = PG_BN * PG_BK * 2;  // bf16 B slice: 8 KB
+constexpr int PG_STAGE = PG_ASLICE + PG_BSLICE;
 
-template <class C>
-__global__ void __launch_bounds__(C::NT) gemm_split_kernel(SplitGemm g) {
-  __shared__ uint4 lds[2 * (2 * C::A_VEC + C::B_VEC)];
-  const int seg = blockIdx.z;
-  const bf16 *__restrict__ B = static_cast<const bf16 *>(g.B[seg]);
+template <int n>
+__device__ __forceinline__ void pg_wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// A slice: 64 rows x 8 chunks of 4 floats; chunk c of row r at c ^ ((r >> 1) & 7)
+__device__ __forceinline__ int a_slot(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
+// B slice: 128 rows x 4 chunks of 8 bf16; chunk c of row r at c ^ ((r >> 2) & 3)
+__device__ __forceinline__ int b_slot(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
+}  // namespace
+
+// Accumulates acc[j] (wave tile rows wm*32 + [0, 32), columns wn*64 + 32 j +
+// [0, 32)) over the slices [sb, sb + nk) of K.  The operands come in as
+// restrict-qualified parameters: that tells the compiler the LDS reads do not
+// depend on the DMA copies in flight (the s_waitcnt / s_barrier pair before
+// each slice orders them), so it adds no wait of its own.
+__device__ __forceinline__ void pg_tile(const float *__restrict__ A, int64_t lda, int M, int m0,
+                                        const bf16 *__restrict__ B, int K, int N, int n0, int sb, int nk, char *lds,
+                                        f32x16_t (&acc)[2]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, gq = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  if (nk <= 0) return;
+
+  // DMA sources: per slice each wave copies 2 KB of A and 2 KB of B
+  // (2 + 2 instructions of 64 lanes x 16 bytes); rows past M / N read a
+  // clamped valid row and only feed discarded accumulators.
+  const float *asrc[2];
+  const bf16 *bsrc[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int p = (wave * 2 + u) * 64 + lane;
+    {
+      const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+      const int gr = m0 + row < M ? m0 + row : M - 1;
+      asrc[u] = A + (int64_t)gr * lda + c * 4;
+    }
+    {
+      const int row = p >> 2, c = (p & 3) ^ ((row >> 2) & 3);
+      const int gn = n0 + row < N ? n0 + row : N - 1;
+      bsrc[u] = B + (int64_t)gn * K + c * 8;
+    }
+  }
+  auto issue = [&](int slice, int stage) {
+    const int k0 = (sb + min(slice, nk - 1)) * PG_BK;
+    char *st = lds + stage * PG_STAGE;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      __builtin_amdgcn_global_load_lds(asrc[u] + k0, st + (wave * 2 + u) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bsrc[u] + k0, st + PG_ASLICE + (wave * 2 + u) * 1024, 16, 0, 0);
+    }
+  };
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  for (int it = 0; it < nk; ++it) {
+    const int stage = it & 3;
+    pg_wait_vmcnt<8>();             // this wave's copies of slice `it` landed
+    __builtin_amdgcn_s_barrier();   // ... and every wave's; slice it-1 is consumed
+    issue(it + 3, (it + 3) & 3);
+    const float4 *sa = reinterpret_cast<const float4 *>(lds + stage * PG_STAGE);
+    const uint4 *sbq = reinterpret_cast<const uint4 *>(lds + stage * PG_STAGE + PG_ASLICE);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      // k of this lane: 16 kk + 8 gq + [0, 8) for both operands
+      const int arow = wm * 32 + r32;
+      const float4 x0 = sa[a_slot(arow, 4 * kk + 2 * gq)];
+      const float4 x1 = sa[a_slot(arow, 4 * kk + 2 * gq + 1)];
+      uint4 hi, lo;
+      split8(x0, x1, hi, lo);
+      const bf16x8_t fh = __builtin_bit_cast(bf16x8_t, hi), fl = __builtin_bit_cast(bf16x8_t, lo);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, sbq[b_slot(wn * 64 + j * 32 + r32, 2 * kk + gq)]);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fl, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fh, acc[j], 0, 0, 0);
+      }
+    }
+  }
+  pg_wait_vmcnt<0>();  // retire the trailing (unused) prefetches
+}
+
+__global__ void __launch_bounds__(PG_NT) gemm_split_kernel(SplitGemm g) {
+  extern __shared__ __align__(16) char lds[];
+  const int seg = blockIdx.z / g.ksplit, kc = blockIdx.z % g.ksplit;
   const int N = g.N[seg];
-  const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
+  const int m0 = blockIdx.y * PG_BM, n0 = blockIdx.x * PG_BN;
   if (n0 >= N) return;  // uniform per block
   const int M = g.M, K = g.K;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WGN, wn = wave % C::WGN;
-  constexpr int STAGE = 2 * C::A_VEC + C::B_VEC;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, gq = lane >> 5;
+  const int nsl = K / PG_BK;
+  const int sb = (int)((int64_t)nsl * kc / g.ksplit), se = (int)((int64_t)nsl * (kc + 1) / g.ksplit);
+  f32x16_t acc[2];
+  pg_tile(g.A, g.lda, M, m0, static_cast<const bf16 *>(g.B[seg]), K, N, n0, sb, se - sb, lds, acc);
 
-  f32x16_t acc[C::FM][C::FN];
+  // lane: output row m0 + wm*32 + r32; register r of fragment j is column
+  // n0 + wn*64 + 32 j + 8 (r >> 2) + 4 gq + (r & 3)
+  const int row = m0 + wm * 32 + r32;
+  if (row >= M) return;
+  if (g.ksplit > 1) {
+    size_t base = 0;
+    for (int t = 0; t < seg; ++t) base += (size_t)g.ksplit * M * g.N[t];
+    float *out = g.part + base + ((size_t)kc * M + row) * N;
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  float4 ra[C::A_PT][2];
-  uint4 rb[C::B_PT];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int t = 0; t < C::A_PT; ++t) {
-      const int idx = tid + t * C::NT;
-      const int row = idx >> 3, ch = idx & 7;
-      const int gr = m0 + row;
-      float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
-      if (gr < M) {
-        const float4 *src = reinterpret_cast<const float4 *>(g.A + (int64_t)gr * g.lda + k0 + ch * 8);
-        a0 = src[0];
-        a1 = src[1];
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn * 64 + 32 * j + 8 * q + 4 * gq;
+        if (col < N)
+          *reinterpret_cast<float4 *>(out + col) =
+              make_float4(acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]);
       }
-      ra[t][0] = a0;
-      ra[t][1] = a1;
-    }
-#pragma unroll
-    for (int t = 0; t < C::B_PT; ++t) {
-      const int idx = tid + t * C::NT;
-      const int row = idx >> 3, ch = idx & 7;
-      const int gn = n0 + row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (gn < N) v = *reinterpret_cast<const uint4 *>(B + (int64_t)gn * K + k0 + ch * 8);
-      rb[t] = v;
-    }
-  };
-  auto store = [&](int buf) {
-    uint4 *st = lds + buf * STAGE;
-#pragma unroll
-    for (int t = 0; t < C::A_PT; ++t) {
-      const int idx = tid + t * C::NT;
-      uint4 hi, lo;
-      split8(ra[t][0], ra[t][1], hi, lo);
-      st[swz(idx >> 3, idx & 7)] = hi;
-      st[C::A_VEC + swz(idx >> 3, idx & 7)] = lo;
-    }
-#pragma unroll
-    for (int t = 0; t < C::B_PT; ++t) {
-      const int idx = tid + t * C::NT;
-      st[2 * C::A_VEC + swz(idx >> 3, idx & 7)] = rb[t];
-    }
-  };
-
-  const int nk = K / C::BK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int it = 0; it < nk; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < nk) load((it + 1) * C::BK);
-    const uint4 *st = lds + buf * STAGE;
-#pragma unroll
-    for (int kk = 0; kk < C::BK / 16; ++kk) {
-      const int ch = kk * 2 + (lane >> 5);
-      bf16x8_t fh[C::FM], fl[C::FM], fb[C::FN];
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
-        const int row = wm * C::WM + i * 32 + (lane & 31);
-        fh[i] = __builtin_bit_cast(bf16x8_t, st[swz(row, ch)]);
-        fl[i] = __builtin_bit_cast(bf16x8_t, st[C::A_VEC + swz(row, ch)]);
-      }
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int row = wn * C::WN + j * 32 + (lane & 31);
-        fb[j] = __builtin_bit_cast(bf16x8_t, st[2 * C::A_VEC + swz(row, ch)]);
-      }
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl[i], fb[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-    }
-    if (it + 1 < nk) store(buf ^ 1);
-    __syncthreads();
+    return;
   }
-
   const Epi e = g.e[seg];
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * C::WM + acc_row(i, r, lane);
-        const int col = n0 + wn * C::WN + acc_col(j, lane);
-        if (row < M && col < N) epi_store(e, row, col, acc[i][j][r]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int col = n0 + wn * 64 + 32 * j + 8 * (r >> 2) + 4 * gq + (r & 3);
+      if (col < N) epi_store(e, row, col, acc[j][r]);
+    }
+}
+
+// Sum of the K-split partials + epilogue: one thread per 4 consecutive
+// columns of one output row (N % 4 == 0).
+__global__ void __launch_bounds__(256) gemm_splitk_epilogue_kernel(SplitGemm g) {
+  const int seg = blockIdx.y;
+  const int M = g.M, N = g.N[seg];
+  const int64_t quads = (int64_t)M * N / 4;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= quads) return;
+  size_t base = 0;
+  for (int s = 0; s < seg; ++s) base += (size_t)g.ksplit * M * g.N[s];
+  const float4 *p = reinterpret_cast<const float4 *>(g.part + base) + t;
+  const int64_t stride = (int64_t)M * N / 4;
+  float4 v = p[0];
+  for (int z = 1; z < g.ksplit; ++z) {
+    const float4 w = p[z * stride];
+    v.x += w.x;
+    v.y += w.y;
+    v.z += w.z;
+    v.w += w.w;
+  }
+  const int row = (int)(t * 4 / N), col = (int)(t * 4 - (int64_t)row * N);
+  const Epi e = g.e[seg];
+  epi_store(e, row, col, v.x);
+  epi_store(e, row, col + 1, v.y);
+  epi_store(e, row, col + 2, v.z);
+  epi_store(e, row, col + 3, v.w);
+}
+
+// The K ranges depend on K alone (16 slices = 512 k each): a row's result
+// then does not depend on how many rows are computed with it, which keeps
+// an incremental prefill bitwise equal to a one-shot one.
+int gemm_split_plan(int M, int K, const int *N, int count) {
+  (void)M;
+  (void)N;
+  (void)count;
+  const int nsl = K / PG_BK;
+  return nsl >= 32 ? (nsl + 15) / 16 : 1;
+}
+
+size_t gemm_split_part_bytes(int M, int K, const int *N, int count) {
+  const int ks = gemm_split_plan(M, K, N, count);
+  if (ks <= 1) return 0;
+  size_t n = 0;
+  for (int i = 0; i < count; ++i) n += (size_t)ks * M * N[i];
+  return n * 4;
 }
 
 hipError_t gemm_split(const SplitGemm &g, hipStream_t s) {
-  using C = SmallTile;
+  if (g.ksplit < 1 || (g.ksplit > 1 && !g.part) || g.K % PG_BK) return hipErrorInvalidValue;
+  for (int i = 0; i < g.count; ++i)
+    if (g.N[i] % 4) return hipErrorInvalidValue;
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_split_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, PG_STAGES * PG_STAGE) != hipSuccess)
+      return hipErrorInvalidValue;
+    attr = true;
+  }
   int maxN = 0;
   for (int i = 0; i < g.count; ++i) maxN = g.N[i] > maxN ? g.N[i] : maxN;
-  dim3 grid((maxN + C::BN - 1) / C::BN, (g.M + C::BM - 1) / C::BM, g.count);
-  hipLaunchKernelGGL(gemm_split_kernel<C>, grid, dim3(C::NT), 0, s, g);
+  dim3 grid((maxN + PG_BN - 1) / PG_BN, (g.M + PG_BM - 1) / PG_BM, g.count * g.ksplit);
+  hipLaunchKernelGGL(gemm_split_kernel, grid, dim3(PG_NT), PG_STAGES * PG_STAGE, s, g);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || g.ksplit == 1) return err;
+  const int64_t quads = (int64_t)g.M * maxN / 4;
+  hipLaunchKernelGGL(gemm_splitk_epilogue_kernel, dim3((unsigned)((quads + 255) / 256), g.count), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
