@@ -79,13 +79,15 @@ typedef struct {
 
 /* Weights (device, dtype of the config, caller-owned, read-only).
  * E [V][d] is the token-embedding table, tied to the LM head ([P3] §4.1).
- * E_t [d][P] (P = dg_embedding_t_pitch(cfg) >= V) is E transposed,
- * produced once by dg_pack_embedding(); the self-conditioning contraction
- * streams it (required for DG_BF16, ignored for DG_F32).  w_sc1 [F][d], w_sc2 [d][F]: self-conditioning FFN ([P3] §5.1).
+ * E_pack (DG_BF16; ignored for DG_F32) holds E twice in the tiled layout
+ * below, written once by dg_pack_embedding(): E itself, then E^T (d rows,
+ * V columns); the LM head streams the first, the self-conditioning
+ * contraction the second.
+ * w_sc1 [F][d], w_sc2 [d][F]: self-conditioning FFN ([P3] §5.1).
  * wq [Hq*hd][d], wk/wv [Hkv*hd][d], wo [d][Hq*hd]: attention projections.
  * g_attn, g_final [d]: RMSNorm gains (pre-attention, pre-LM-head). */
 typedef struct {
-  const void *E, *E_t, *w_sc1, *w_sc2, *wq, *wk, *wv, *wo, *g_attn, *g_final;
+  const void *E, *E_pack, *w_sc1, *w_sc2, *wq, *wk, *wv, *wo, *g_attn, *g_final;
 } dg_weights;
 
 /* Prefix KV cache ([P1]/[P4]: written causally by prefill, read by denoise).
@@ -103,11 +105,12 @@ typedef struct {
 
 /* Per-canvas state.  Device buffers are caller-owned:
  *   tokens  int32 [N]            current canvas
- *   probs   dtype [N][V]         softmax probabilities of the last step
- *                                (DG_BF16: rounded to nearest even; the
- *                                dominant token's exact value is kept in
- *                                stats), the self-conditioning input of
- *                                the next step
+ *   probs   bytes dg_probs_bytes(): softmax probabilities of the last step,
+ *                                the self-conditioning input of the next.
+ *                                DG_F32: float [N][V].  DG_BF16: bf16 in
+ *                                the tiled layout (rounded to nearest even;
+ *                                the dominant token's exact value is kept
+ *                                in stats)
  *   stats   bytes dg_stats_bytes(): per-(row, tile) softmax statistics,
  *                                normalisers and each row's dominant token
  *                                with its exact probability; opaque
@@ -163,17 +166,26 @@ size_t dg_workspace_bytes(const dg_config *cfg, int32_t max_prefill_tokens);
 size_t dg_stats_bytes(const dg_config *cfg);
 
 /* ---- one-time preparation ----------------------------------------------- */
-/* Row pitch, in elements, of E_t: V + 64.  At a power-of-two vocabulary the
- * rows of an unpadded E_t lie a power of two of bytes apart, so the 256 rows
- * one workgroup of the contraction reads together would share one cache set
- * and memory channel.  0 if the configuration is unsupported. */
-int64_t dg_embedding_t_pitch(const dg_config *cfg);
+/* Tiled layout of a bf16 matrix X [R][K] (K a multiple of 32): blocks of 256
+ * rows x 32 columns, 16 KB each, block (b, s) at index b * (K / 32) + s;
+ * inside a block, 16-byte chunk p = 0..1023 holds the eight values
+ * X[256 b + r][32 s + 8 c .. 32 s + 8 c + 7] with r = p / 4 and
+ * c = (p % 4) ^ ((r / 4) % 4).  Rows past R up to a multiple of 256 are
+ * padding.  This is the order in which the two table-streaming kernels stage
+ * a 32-wide slice in LDS, so each of their copy instructions reads 1 KB of
+ * consecutive memory. */
 
-/* Writes E_t[c][r] = E[r][c] for r < V, c < d (device; E_t caller-allocated
- * with d * dg_embedding_t_pitch(cfg) elements of the config dtype).  A layout
- * copy only: E_t holds the same values as E; the pad columns [V, pitch) are
- * neither written nor read. */
-dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_t, void *stream);
+/* Bytes of dg_weights.E_pack (0 for DG_F32 or an unsupported config). */
+size_t dg_embedding_pack_bytes(const dg_config *cfg);
+
+/* Bytes of dg_canvas.probs (0 if unsupported). */
+size_t dg_probs_bytes(const dg_config *cfg);
+
+/* Writes E_pack (device, caller-allocated dg_embedding_pack_bytes(cfg)
+ * bytes): E [V][d] in the tiled layout, followed by E^T [d][V] in the tiled
+ * layout (padding rows zero).  A layout copy only: the same values as E.
+ * Does nothing for DG_F32. */
+dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_pack, void *stream);
 
 /* [P3] §5.4 canvas initialisation: tokens[i] = the top log2(V) bits of word 0
  * of Philox4x32-10(key = seed, counter = (i, 0, canvas_id, 0)) -- uniform
@@ -239,7 +251,8 @@ void dg_test_set_logits_dump(int32_t on);
 size_t dg_test_logits_ws_bytes(const dg_config *cfg);
 
 /* Self-conditioning contraction alone: S (f32 [N][d]) = P E, with P given
- * directly as dtype [N][V] (no tile normalisers, no correction). */
+ * in the layout of dg_canvas.probs (DG_BF16: tiled bf16 [N][V]; DG_F32:
+ * float [N][V]); no correction of the dominant token. */
 dg_status dg_test_selfcond(const dg_config *cfg, const dg_weights *w, const void *P, void *S,
                            void *ws, size_t ws_bytes, void *stream);
 /* Selection kernel alone on given entropies/argmax/tokens (device):

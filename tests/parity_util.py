@@ -28,7 +28,7 @@ def ws_view(den: D.Denoiser, name: str, dtype, shape):
 def gpu_probs(den: D.Denoiser) -> np.ndarray:
     cfg = den.cfg
     N = cfg.canvas_len
-    p = den.canvas.probs.float().clone()
+    p = den.canvas.probabilities(cfg).float().clone()
     if cfg.dtype == B.DG_BF16:  # the dominant token's probability is kept exactly
         a, pa = den.canvas.top(cfg)
         p[torch.arange(N, device=p.device), a.long()] = pa

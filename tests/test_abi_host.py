@@ -120,7 +120,7 @@ def test_denoise_step_validation(lib):
         assert r == st, (kw, r)
         assert (cv.step, cv.has_prev) == (3, 1)
     w2 = fake_weights()
-    w2.E_t = None
+    w2.E_pack = None
     assert call_step(cfg, w2, cache, cv, 1.0, 8.0, need) == B.DG_ERR_INVALID_ARG
     cv2 = fake_canvas()
     cv2.status = None
@@ -176,15 +176,41 @@ def test_other_entry_point_validation(lib):
                             ctypes.byref(stop), None, None) == B.DG_ERR_UNSUPPORTED
 
 
-def test_embedding_t_pitch(lib):
-    """The transposed table's row pitch is V + 64 elements, so its rows are
-    never a power of two of bytes apart; unsupported configurations give 0."""
-    for i in (1, 2, 3):
+def test_pack_and_probs_bytes(lib):
+    """Packed table = E and E^T, each tiled (rows padded to 256); bf16 probs
+    are one tiled block of 256 rows; fp32 probs are row-major; unsupported
+    configurations give 0."""
+    def tl(R, K):
+        return (R + 255) // 256 * 256 * K
+    for i in (2, 3):
         cfg = cfg_of(i)
-        p = B.dg_embedding_t_pitch(cfg)
-        assert p == cfg.vocab + 64
-        row_bytes = p * (2 if cfg.dtype == B.DG_BF16 else 4)
-        assert row_bytes & (row_bytes - 1) != 0
+        V, d = cfg.vocab, cfg.d_model
+        assert B.dg_embedding_pack_bytes(cfg) == 2 * (tl(V, d) + tl(d, V))
+        assert B.dg_probs_bytes(cfg) == 2 * tl(cfg.canvas_len, V)
+    cfg = cfg_of(1)
+    assert B.dg_embedding_pack_bytes(cfg) == 0
+    assert B.dg_probs_bytes(cfg) == 4 * cfg.canvas_len * cfg.vocab
     bad = cfg_of(2)
     bad.vocab = 1000
-    assert B.dg_embedding_t_pitch(bad) == 0
+    assert B.dg_embedding_pack_bytes(bad) == 0 and B.dg_probs_bytes(bad) == 0
+
+
+def test_tiled_layout_helpers():
+    """rows_to_tiled / tiled_to_rows follow the documented formula: element
+    (row, col) of X [R][K] sits at ((b * K/32 + s) * 1024 + p) * 8 + col % 8
+    with b, r = divmod(row, 256), s = col // 32, c = (col % 32) // 8 and
+    p = 4 r + (c ^ ((r // 4) % 4)); padding rows are zero."""
+    import torch
+    g = torch.Generator().manual_seed(0)
+    X = torch.randn(300, 96, generator=g)
+    T = B.rows_to_tiled(X)
+    assert T.numel() == 512 * 96
+    assert torch.equal(B.tiled_to_rows(T, 300, 96), X)
+    for row in (0, 1, 5, 17, 255, 256, 299):
+        for col in (0, 7, 8, 31, 32, 63, 95):
+            b, r = divmod(row, 256)
+            s, c = col // 32, (col % 32) // 8
+            p = 4 * r + (c ^ ((r // 4) % 4))
+            assert T[((b * 3 + s) * 1024 + p) * 8 + col % 8] == X[row, col]
+    pad = B.tiled_to_rows(T, 512, 96)[300:]
+    assert not pad.any()

@@ -127,7 +127,8 @@ def test_selfcond_contraction(cfg_id, N):
     Pm = W.random_row_weights(N, c["V"], seed=7).to(torch.bfloat16)
     S = torch.zeros((N, c["d"]), dtype=torch.float32, device="cuda")
     ws = B.workspace(cfg)
-    B.dg_test_selfcond(cfg, w.s, Pm.cuda(), S, ws)
+    Pt = B.rows_to_tiled(Pm.cuda())
+    B.dg_test_selfcond(cfg, w.s, Pt, S, ws)
     torch.cuda.synchronize()
     om = oracle.model_from_inputs(inp)
     Pf = Pm.float().numpy()
@@ -137,7 +138,7 @@ def test_selfcond_contraction(cfg_id, N):
     assert rel_frob(got, ref) <= 1e-2
     # determinism: a second run is bit-identical
     S2 = torch.zeros_like(S)
-    B.dg_test_selfcond(cfg, w.s, Pm.cuda(), S2, ws)
+    B.dg_test_selfcond(cfg, w.s, Pt, S2, ws)
     assert torch.equal(S, S2)
 
 
@@ -152,7 +153,7 @@ def test_selfcond_one_hot_gathers_rows():
     Pm = torch.zeros((N, V), dtype=torch.bfloat16)
     Pm[torch.arange(N), t] = 1.0
     S = torch.zeros((N, c["d"]), dtype=torch.float32, device="cuda")
-    B.dg_test_selfcond(cfg, w.s, Pm.cuda(), S, B.workspace(cfg))
+    B.dg_test_selfcond(cfg, w.s, B.rows_to_tiled(Pm.cuda()), S, B.workspace(cfg))
     assert torch.equal(S.cpu(), inp["E"][t].float())
 
 

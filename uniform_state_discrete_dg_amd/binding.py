@@ -36,7 +36,7 @@ class dg_config(ctypes.Structure):
 
 
 class dg_weights(ctypes.Structure):
-    _fields_ = [(n, vp) for n in ("E", "E_t", "w_sc1", "w_sc2", "wq", "wk", "wv", "wo", "g_attn",
+    _fields_ = [(n, vp) for n in ("E", "E_pack", "w_sc1", "w_sc2", "wq", "wk", "wv", "wo", "g_attn",
                                   "g_final")]
 
 
@@ -67,7 +67,8 @@ SIGNATURES = {
     "dg_validate_config": (c_i32, [P(dg_config)]),
     "dg_workspace_bytes": (c_sz, [P(dg_config), c_i32]),
     "dg_stats_bytes": (c_sz, [P(dg_config)]),
-    "dg_embedding_t_pitch": (ctypes.c_int64, [P(dg_config)]),
+    "dg_embedding_pack_bytes": (c_sz, [P(dg_config)]),
+    "dg_probs_bytes": (c_sz, [P(dg_config)]),
     "dg_pack_embedding": (c_i32, [P(dg_config), vp, vp, vp]),
     "dg_canvas_init": (c_i32, [P(dg_config), P(dg_canvas), c_u64, c_u32, vp]),
     "dg_prefill_append": (c_i32, [P(dg_config), P(dg_weights), P(dg_kv_cache), vp, c_i32, vp, vp,
@@ -144,12 +145,16 @@ def dg_stats_bytes(cfg: dg_config) -> int:
     return int(lib().dg_stats_bytes(ctypes.byref(cfg)))
 
 
-def dg_embedding_t_pitch(cfg: dg_config) -> int:
-    return int(lib().dg_embedding_t_pitch(ctypes.byref(cfg)))
+def dg_embedding_pack_bytes(cfg: dg_config) -> int:
+    return int(lib().dg_embedding_pack_bytes(ctypes.byref(cfg)))
 
 
-def dg_pack_embedding(cfg: dg_config, E: torch.Tensor, E_t: torch.Tensor, stream=None) -> None:
-    _check("dg_pack_embedding", lib().dg_pack_embedding(ctypes.byref(cfg), _ptr(E), _ptr(E_t),
+def dg_probs_bytes(cfg: dg_config) -> int:
+    return int(lib().dg_probs_bytes(ctypes.byref(cfg)))
+
+
+def dg_pack_embedding(cfg: dg_config, E: torch.Tensor, E_pack: torch.Tensor | None, stream=None) -> None:
+    _check("dg_pack_embedding", lib().dg_pack_embedding(ctypes.byref(cfg), _ptr(E), _ptr(E_pack),
                                                         _stream(stream)))
 
 
@@ -246,18 +251,49 @@ def torch_dtype(cfg: dg_config):
     return torch.bfloat16 if cfg.dtype == DG_BF16 else torch.float32
 
 
+def _tiled_perm(device):
+    """Chunk positions of the tiled layout: position p holds block row p // 4
+    and logical 8-column chunk (p % 4) ^ ((p // 16) % 4)."""
+    p = torch.arange(1024, device=device)
+    r = p // 4
+    return r, (p % 4) ^ ((r // 4) % 4)
+
+
+def rows_to_tiled(X: torch.Tensor) -> torch.Tensor:
+    """Row-major [R][K] -> the tiled layout (flat, rows padded to 256 with zeros)."""
+    R, K = X.shape
+    Rp = (R + 255) // 256 * 256
+    Xp = torch.zeros((Rp, K), dtype=X.dtype, device=X.device)
+    Xp[:R] = X
+    r, c = _tiled_perm(X.device)
+    Y = Xp.view(Rp // 256, 256, K // 32, 4, 8).permute(0, 2, 1, 3, 4)[:, :, r, c, :]
+    return Y.contiguous().view(-1)
+
+
+def tiled_to_rows(T: torch.Tensor, R: int, K: int) -> torch.Tensor:
+    """The tiled layout (flat) -> row-major [R][K]."""
+    Rp = (R + 255) // 256 * 256
+    r, c = _tiled_perm(T.device)
+    Y = T.view(Rp // 256, K // 32, 1024, 8)
+    out = torch.empty((Rp // 256, K // 32, 256, 4, 8), dtype=T.dtype, device=T.device)
+    out[:, :, r, c, :] = Y
+    return out.permute(0, 2, 1, 3, 4).reshape(Rp, K)[:R]
+
+
 class DeviceWeights:
-    """Moves a workload's weights to the GPU and packs E^T once."""
+    """Moves a workload's weights to the GPU and packs the tiled tables once."""
 
     def __init__(self, cfg: dg_config, inp: dict, device="cuda", stream=None):
         dt = torch_dtype(cfg)
         t = {k: inp[k].to(device=device, dtype=dt).contiguous()
              for k in ("E", "w1", "w2", "wq", "wk", "wv", "wo", "g_attn", "g_final")}
-        t["E_t"] = torch.empty((cfg.d_model, dg_embedding_t_pitch(cfg)), dtype=dt, device=device)
-        dg_pack_embedding(cfg, t["E"], t["E_t"], stream)
+        nb = dg_embedding_pack_bytes(cfg)
+        t["E_pack"] = torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
+        dg_pack_embedding(cfg, t["E"], t["E_pack"] if nb else None, stream)
         self.t = t
-        self.s = dg_weights(*(t[k].data_ptr() for k in ("E", "E_t", "w1", "w2", "wq", "wk", "wv",
-                                                        "wo", "g_attn", "g_final")))
+        self.s = dg_weights(*(t[k].data_ptr() if (k != "E_pack" or nb) else None
+                              for k in ("E", "E_pack", "w1", "w2", "wq", "wk", "wv", "wo", "g_attn",
+                                        "g_final")))
 
 
 class DeviceCache:
@@ -284,7 +320,7 @@ class DeviceCanvas:
         N, V = cfg.canvas_len, cfg.vocab
         dt = torch_dtype(cfg)
         self.tokens = torch.zeros(N, dtype=torch.int32, device=device)
-        self.probs = torch.zeros((N, V), dtype=dt, device=device)
+        self.probs = torch.zeros(dg_probs_bytes(cfg), dtype=torch.uint8, device=device)
         self.stats = torch.zeros(dg_stats_bytes(cfg), dtype=torch.uint8, device=device)
         self.entropy = torch.zeros(N, dtype=torch.float32, device=device)
         self.argmax = torch.zeros(N, dtype=torch.int32, device=device)
@@ -293,6 +329,13 @@ class DeviceCanvas:
         self.s = dg_canvas(self.tokens.data_ptr(), self.probs.data_ptr(), self.stats.data_ptr(),
                            self.entropy.data_ptr(), self.argmax.data_ptr(),
                            self.accept.data_ptr(), self.status.data_ptr(), 0, 0, 0, 0)
+
+    def probabilities(self, cfg: dg_config) -> torch.Tensor:
+        """The last step's probabilities as [N][V] (bf16 or f32, row-major)."""
+        N, V = cfg.canvas_len, cfg.vocab
+        if cfg.dtype == DG_BF16:
+            return tiled_to_rows(self.probs.view(torch.bfloat16), N, V)
+        return self.probs.view(torch.float32).view(N, V)
 
     def tile_scale(self, cfg: dg_config) -> torch.Tensor:
         """Per-(row, tile) normalisers of the last step ([N][V/64] f32): the

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "dg_kernels.h"
+#include "dg_tiled.h"
 #include "dgdenoise.h"
 
 using dg::bf16;
@@ -51,7 +52,9 @@ dg_status check_config(const dg_config *c) {
 
 // Self-conditioning split of K = V over workgroups (bf16 path): about one
 // work item per CU.
-int64_t et_pitch(const dg_config *c) { return (int64_t)c->vocab + 64; }
+// The packed table (DG_BF16): E tiled ([V][d]) followed by E^T tiled ([d][V]).
+size_t pack_te_elems(const dg_config *c) { return dg::tl_elems(c->vocab, c->d_model); }
+size_t pack_elems(const dg_config *c) { return pack_te_elems(c) + dg::tl_elems(c->d_model, c->vocab); }
 
 int selfcond_ksplit(const dg_config *c) {
   const int bm = dg::estream_bm(c->canvas_len);
@@ -86,7 +89,7 @@ Layout layout(const dg_config *c, int32_t nprefill, bool with_logits) {
   L.h0 = take(N * d * 4);
   L.h1 = take(N * d * 4);
   L.nrm = take(N * d * 4);
-  L.nrm16 = take(bf ? N * d * 2 : 0);
+  L.nrm16 = take(bf ? dg::tl_elems((int)N, (int)d) * 2 : 0);
   L.sc = take(N * d * 4);
   L.g = take(N * F * 4);
   L.q = take(Hq * N * hd * 4);
@@ -173,7 +176,7 @@ bool weights_ok(const dg_config *c, const dg_weights *w) {
   if (!w || !w->E || !w->w_sc1 || !w->w_sc2 || !w->wq || !w->wk || !w->wv || !w->wo || !w->g_attn ||
       !w->g_final)
     return false;
-  if (c->dtype == DG_BF16 && !w->E_t) return false;
+  if (c->dtype == DG_BF16 && !w->E_pack) return false;
   return true;
 }
 
@@ -247,22 +250,29 @@ size_t dg_stats_bytes(const dg_config *cfg) {
   return (size_t)cfg->canvas_len * (nt * (sizeof(float4) + sizeof(float)) + sizeof(float2));
 }
 
-int64_t dg_embedding_t_pitch(const dg_config *cfg) {
-  if (check_config(cfg) != DG_OK) return 0;
-  return et_pitch(cfg);
+size_t dg_embedding_pack_bytes(const dg_config *cfg) {
+  if (check_config(cfg) != DG_OK || cfg->dtype != DG_BF16) return 0;
+  return pack_elems(cfg) * 2;
 }
 
-dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_t, void *stream) {
+size_t dg_probs_bytes(const dg_config *cfg) {
+  if (check_config(cfg) != DG_OK) return 0;
+  if (cfg->dtype == DG_BF16) return dg::tl_elems(cfg->canvas_len, cfg->vocab) * 2;
+  return (size_t)cfg->canvas_len * cfg->vocab * 4;
+}
+
+dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_pack, void *stream) {
   dg_status st = check_config(cfg);
   if (st != DG_OK) return st;
-  if (!E || !E_t) return DG_ERR_INVALID_ARG;
+  if (cfg->dtype != DG_BF16) return DG_OK;  // the fp32 path reads E directly
+  if (!E || !E_pack) return DG_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (cfg->dtype == DG_BF16)
-    DG_TRY(dg::transpose<bf16>(static_cast<const bf16 *>(E), cfg->vocab, cfg->d_model, static_cast<bf16 *>(E_t),
-                               et_pitch(cfg), s));
-  else
-    DG_TRY(dg::transpose<float>(static_cast<const float *>(E), cfg->vocab, cfg->d_model,
-                                static_cast<float *>(E_t), et_pitch(cfg), s));
+  const int V = cfg->vocab, d = cfg->d_model;
+  bf16 *te = static_cast<bf16 *>(E_pack), *tet = te + pack_te_elems(cfg);
+  // E^T row-major goes through the first region (V*d elements) as scratch
+  DG_TRY(dg::transpose<bf16>(static_cast<const bf16 *>(E), V, d, te, V, s));
+  DG_TRY(dg::tile_rows(te, d, V, V, tet, s));
+  DG_TRY(dg::tile_rows(static_cast<const bf16 *>(E), V, d, d, te, s));
   return DG_OK;
 }
 
@@ -386,7 +396,8 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     if (bf) {
       const int ks = selfcond_ksplit(cfg);
       float *part = reinterpret_cast<float *>(base + L.sc_part);
-      dg::GemmShape g{cv->probs, V, w->E_t, et_pitch(cfg), N, d, V};
+      const bf16 *tet = static_cast<const bf16 *>(w->E_pack) + pack_te_elems(cfg);
+      dg::TiledGemm g{static_cast<const uint16_t *>(cv->probs), tet, N, d, V};
       {
         ProfScope ps(g_prof_sc, s);
         DG_TRY(dg::selfcond_bf16(g, part, ks, s));
@@ -452,19 +463,19 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     DG_TRY(dg::rmsnorm_rows<bf16>(h1, static_cast<const bf16 *>(w->g_final), N, d, cfg->rms_eps, nrm, nrm16, s));
     {
       ProfScope ps(g_prof_lm, s);
-      DG_TRY(dg::lm_head_bf16(nrm16, N, d, static_cast<const uint16_t *>(w->E), V, inv_T,
+      DG_TRY(dg::lm_head_bf16(nrm16, N, d, static_cast<const uint16_t *>(w->E_pack), V, inv_T,
                               static_cast<uint16_t *>(cv->probs), tstats, dump ? logits : nullptr, s));
     }
     DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, tscale, nrm,
                            static_cast<const uint16_t *>(w->E), d, top, s));
-    DG_TRY(dg::normalize_probs<bf16>(static_cast<bf16 *>(cv->probs), tscale, N, V, s));
+    DG_TRY(dg::normalize_probs_bf16(static_cast<uint16_t *>(cv->probs), tscale, N, V, s));
   } else {
     DG_TRY(dg::rmsnorm_rows<float>(h1, static_cast<const float *>(w->g_final), N, d, cfg->rms_eps, nrm, nullptr, s));
     dg::GemmShapeF32 g{nrm, d, 1, static_cast<const float *>(w->E), d, 1, N, V, d, nullptr, 0};
     DG_TRY(dg::gemm_f32(g, epi_store(logits, true, V, V, 0), s));
     DG_TRY(dg::tile_stats_f32(logits, N, V, inv_T, static_cast<float *>(cv->probs), tstats, s));
     DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, tscale, nullptr, nullptr, d, top, s));
-    DG_TRY(dg::normalize_probs<float>(static_cast<float *>(cv->probs), tscale, N, V, s));
+    DG_TRY(dg::normalize_probs_f32(static_cast<float *>(cv->probs), tscale, N, V, s));
   }
   // 5. accept / re-noise / stop flags
   DG_TRY(dg::select_step(cv->entropy, cv->argmax, cv->tokens, cv->accept, cv->status, N, ilog2(V), (double)gamma,
@@ -540,7 +551,8 @@ dg_status dg_test_selfcond(const dg_config *cfg, const dg_weights *w, const void
   if (cfg->dtype == DG_BF16) {
     const int ks = selfcond_ksplit(cfg);
     float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + L.sc_part);
-    dg::GemmShape g{P, V, w->E_t, et_pitch(cfg), N, d, V};
+    const bf16 *tet = static_cast<const bf16 *>(w->E_pack) + pack_te_elems(cfg);
+    dg::TiledGemm g{static_cast<const uint16_t *>(P), tet, N, d, V};
     DG_TRY(dg::selfcond_bf16(g, part, ks, s));
     DG_TRY(dg::selfcond_reduce(part, ks, N, d, nullptr, nullptr, V, nullptr, static_cast<float *>(S), s));
   } else {

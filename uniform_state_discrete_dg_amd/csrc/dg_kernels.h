@@ -24,11 +24,12 @@ struct Epi {
   const float *resid;    // EPI_ADD: out = resid + acc (f32, same index)
 };
 
-struct GemmShape {
-  const void *A;          // [M][K] (lda)
-  int64_t lda;
-  const void *B;          // [N][K] (ldb)
-  int64_t ldb;
+// Operands of a table-streaming contraction in the tiled layout of
+// dg_tiled.h: A = one block of (up to) 256 canvas rows, B = ceil(N/256)
+// blocks of table rows, both with K columns.  C[M][N] = A B^T.
+struct TiledGemm {
+  const uint16_t *A;
+  const uint16_t *B;
   int M, N, K;
 };
 
@@ -55,10 +56,10 @@ size_t gemm_split_part_bytes(int M, int K, const int *N, int count);
 hipError_t gemm_split(const SplitGemm &g, hipStream_t s);
 // Canvas rows per workgroup of the two table-streaming kernels (128 or 256).
 int estream_bm(int M);
-// The self-conditioning contraction: A = probs (bf16 probabilities, [M][lda]),
-// B = E^T ([N][ldb]), K = V split in ksplit ranges; writes f32 partials
+// The self-conditioning contraction: A = probs (tiled bf16 probabilities),
+// B = E^T (tiled, d rows), K = V split in ksplit ranges; writes f32 partials
 // [ksplit][M][N].
-hipError_t selfcond_bf16(const GemmShape &g, float *partials, int ksplit, hipStream_t s);
+hipError_t selfcond_bf16(const TiledGemm &g, float *partials, int ksplit, hipStream_t s);
 // fp32 SIMT GEMM: C[m][n] = sum_k A[m*sam + k*sak] * B[n*sbn + k*sbk].
 struct GemmShapeF32 {
   const float *A;
@@ -76,8 +77,10 @@ hipError_t gemm_f32(const GemmShapeF32 &g, const Epi &e, hipStream_t s);
 // y = z * inv_T, m_t = zmax_t * inv_T: l_t = sum exp(y - m_t),
 // s_t = sum exp(y - m_t) (y - m_t); probs = bf16(exp(y - m_t)).
 // tile_stats: float4 [M][V/64] = (zmax, l, s, argmax as int bits).
-hipError_t lm_head_bf16(const uint16_t *A, int M, int K, const uint16_t *E, int V, float inv_T,
-                        uint16_t *probs, float4 *tile_stats, float *logits_dump, hipStream_t s);
+// A_tiled: the normalised canvas rows (M <= 256, one tiled block); E_tiled:
+// E in the tiled layout; probs_tiled: the numerators, tiled ([M][V]).
+hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E_tiled, int V, float inv_T,
+                        uint16_t *probs_tiled, float4 *tile_stats, float *logits_dump, hipStream_t s);
 // Same statistics from fp32 logits already in memory (fp32 path).
 hipError_t tile_stats_f32(const float *logits, int M, int V, float inv_T, float *probs,
                           float4 *tile_stats, hipStream_t s);
@@ -114,21 +117,27 @@ void attention_plan(int nq, int Hq, int nk, int *splits, int *keys_per_split);
 template <typename T>
 hipError_t gather_rows(const T *E, const int32_t *tokens, int n, int d, int V, float *out,
                        hipStream_t s);
+// out (fp32 [n][d], nullable) and/or out_tiled (bf16, tiled block(s) of the
+// rows, the rows past n up to the block end written as zeros; nullable).
 template <typename T>
-hipError_t rmsnorm_rows(const float *x, const T *g, int n, int d, float eps, float *out, bf16 *out_bf16,
+hipError_t rmsnorm_rows(const float *x, const T *g, int n, int d, float eps, float *out, bf16 *out_tiled,
                         hipStream_t s);
 // S (fp32 [N][d]) = sum of the ksplit partials + exact correction of each
 // row's dominant token (top = (token bits, exact p); nullable): the
-// contraction used the bf16 value probs[row][a].
+// contraction used the bf16 value of probs (tiled) at (row, a).
 hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top,
-                           const uint16_t *probs, int V, const uint16_t *E, float *out, hipStream_t s);
-// In place: probs[row][v] = round(probs[row][v] * tile_scale[row][v / 64]),
-// numerators -> probabilities (bf16: round to nearest even).
-template <typename T>
-hipError_t normalize_probs(T *probs, const float *tile_scale, int N, int V, hipStream_t s);
+                           const uint16_t *probs_tiled, int V, const uint16_t *E, float *out, hipStream_t s);
+// In place: p(row, v) = round(p(row, v) * tile_scale[row][v / 64]),
+// numerators -> probabilities.  bf16: tiled layout, round to nearest even;
+// fp32: row-major [N][V].
+hipError_t normalize_probs_bf16(uint16_t *probs_tiled, const float *tile_scale, int N, int V, hipStream_t s);
+hipError_t normalize_probs_f32(float *probs, const float *tile_scale, int N, int V, hipStream_t s);
 // out[c * ld_out + r] = in[r * cols + c]
 template <typename T>
 hipError_t transpose(const T *in, int rows, int cols, T *out, int64_t ld_out, hipStream_t s);
+// Tiled copy of a row-major bf16 matrix X [R][K] (leading dimension ldx):
+// out = the tiled layout of dg_tiled.h, rows past R zero-filled.
+hipError_t tile_rows(const uint16_t *X, int R, int K, int64_t ldx, uint16_t *out, hipStream_t s);
 hipError_t copy_bytes(const void *src, void *dst, size_t bytes, hipStream_t s);
 
 // Selection and canvas.

@@ -1,0 +1,35 @@
+// dg_tiled.h -- the tiled bf16 layout of the two table-streaming
+// contractions' operands (host and device).
+//
+// A bf16 matrix X [R][K] (K a multiple of 32) is stored as blocks of 256 rows
+// x 32 columns, 16 KB each, block (b, s) at index b * (K / 32) + s.  Inside a
+// block, 16-byte chunk p (p = 0..1023) holds the 8 values
+// X[256 b + r][32 s + 8 c .. 32 s + 8 c + 7] with r = p / 4 and
+// c = (p % 4) ^ ((r / 4) % 4): exactly the order of an LDS slice of the
+// streaming kernels, so each 64-lane DMA instruction copies 1 KB of
+// consecutive memory.  Rows past R (up to the next multiple of 256) are
+// padding.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace dg {
+
+constexpr int TL_ROWS = 256;    // rows per block
+constexpr int TL_K = 32;        // columns per block
+constexpr int TL_CHUNKS = 1024; // 16-byte chunks per block
+constexpr int TL_ELEMS = 8192;  // bf16 values per block
+
+// position of logical chunk c (columns 8c..8c+7 of the block) of block row r
+__host__ __device__ inline int tl_pos(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+
+// element index of X[row][col] in the tiled layout of a matrix with K columns
+__host__ __device__ inline int64_t tl_index(int row, int col, int K) {
+  const int b = row >> 8, r = row & 255, s = col >> 5, k = col & 31;
+  return (((int64_t)b * (K >> 5) + s) * TL_CHUNKS + tl_pos(r, k >> 3)) * 8 + (k & 7);
+}
+
+inline size_t tl_elems(int R, int K) { return (size_t)((R + TL_ROWS - 1) / TL_ROWS) * TL_ROWS * (size_t)K; }
+
+}  // namespace dg

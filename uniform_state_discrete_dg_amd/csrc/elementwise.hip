@@ -4,6 +4,7 @@
 // Every reduction is a fixed tree, so results do not depend on timing.
 #include "dg_device.h"
 #include "dg_kernels.h"
+#include "dg_tiled.h"
 
 namespace dg {
 
@@ -49,11 +50,15 @@ template hipError_t gather_rows<bf16>(const bf16 *, const int32_t *, int, int, i
 // RMSNorm: out = x / sqrt(mean(x^2) + eps) * g, written in fp32 and, when
 // requested, also rounded to bf16 (the operand of the tied LM head).
 template <typename T>
-__global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ x, const T *__restrict__ g,
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ x, const T *__restrict__ g, int n,
                                                       int d, float eps, float *__restrict__ out,
-                                                      bf16 *__restrict__ out_bf16) {
+                                                      bf16 *__restrict__ out_tiled) {
   __shared__ float sh[256];
   const int i = blockIdx.x;
+  if (i >= n) {  // padding rows of the tiled block
+    for (int k = threadIdx.x; k < d; k += 256) out_tiled[tl_index(i, k, d)] = 0;
+    return;
+  }
   const float *xi = x + (int64_t)i * d;
   float ss = 0.f;
   for (int k = threadIdx.x; k < d; k += 256) ss += xi[k] * xi[k];
@@ -61,16 +66,18 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ 
   const float inv = rsqrtf(ss / (float)d + eps);
   for (int k = threadIdx.x; k < d; k += 256) {
     const float v = xi[k] * inv * Elem<T>::load(g, k);
-    out[(int64_t)i * d + k] = v;
-    if (out_bf16) out_bf16[(int64_t)i * d + k] = f32_to_bf16(v);
+    if (out) out[(int64_t)i * d + k] = v;
+    if (out_tiled) out_tiled[tl_index(i, k, d)] = f32_to_bf16(v);
   }
 }
 
 template <typename T>
-hipError_t rmsnorm_rows(const float *x, const T *g, int n, int d, float eps, float *out, bf16 *out_bf16,
+hipError_t rmsnorm_rows(const float *x, const T *g, int n, int d, float eps, float *out, bf16 *out_tiled,
                         hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(n), dim3(256), 0, s, x, g, d, eps, out, out_bf16);
+  if (out_tiled && d % TL_K) return hipErrorInvalidValue;
+  const int rows = out_tiled ? (n + TL_ROWS - 1) / TL_ROWS * TL_ROWS : n;
+  hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(rows), dim3(256), 0, s, x, g, n, d, eps, out, out_tiled);
   return hipGetLastError();
 }
 template hipError_t rmsnorm_rows<float>(const float *, const float *, int, int, float, float *, bf16 *,
@@ -80,8 +87,8 @@ template hipError_t rmsnorm_rows<bf16>(const float *, const bf16 *, int, int, fl
 
 // Merge of the self-conditioning split-K partials into S (fp32), plus the
 // exact correction of each row's dominant token: the contraction used the
-// bf16 probability p~ = probs[row][a] for token a, the previous step's exact
-// probability of a is p_a, so S += (p_a - p~) E[a].
+// bf16 probability p~ at (row, a) of the tiled probabilities for token a,
+// the previous step's exact probability of a is p_a, so S += (p_a - p~) E[a].
 __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int ksplit, int N, int d,
                                        const float2 *__restrict__ top, const bf16 *__restrict__ probs, int V,
                                        const bf16 *__restrict__ E, float *__restrict__ out) {
@@ -95,7 +102,7 @@ __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int kspli
   if (top) {
     const float2 tp = top[row];
     const int a = __float_as_int(tp.x);
-    const float used = bf16_to_f32(probs[(int64_t)row * V + a]);
+    const float used = bf16_to_f32(probs[tl_index(row, a, V)]);
     acc += (tp.y - used) * bf16_to_f32(E[(int64_t)a * d + k]);
   }
   out[i] = acc;
@@ -108,15 +115,18 @@ hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const fl
   return hipGetLastError();
 }
 
-// Numerators -> probabilities, in place: 8 consecutive columns (one 64-column
-// tile's multiplier) per thread.
+// Numerators -> probabilities, in place.  bf16: one thread per 16-byte
+// chunk of the tiled layout (8 columns of one row, inside one 64-column
+// tile); chunks of padding rows are left alone.
 __global__ void normalize_bf16_kernel(bf16 *__restrict__ probs, const float *__restrict__ tile_scale, int64_t chunks,
-                                      int V) {
+                                      int N, int V) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e = i * 8;
-    const int64_t row = e / V;
-    const int col = (int)(e - row * V);
-    const float c = tile_scale[row * (V / TILE) + col / TILE];
+    const int p = (int)(i & (TL_CHUNKS - 1));
+    const int64_t bs = i >> 10;  // block * (V / 32) + slice; one block (N <= 256)
+    const int row = p >> 2;
+    if (row >= N) continue;
+    const int slice = (int)(bs % (V / TL_K));
+    const float c = tile_scale[(int64_t)row * (V / 64) + slice / 2];
     uint4 v = reinterpret_cast<const uint4 *>(probs)[i];
     uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -141,20 +151,50 @@ __global__ void normalize_f32_kernel(float *__restrict__ probs, const float *__r
   }
 }
 
-template <>
-hipError_t normalize_probs<bf16>(bf16 *probs, const float *tile_scale, int N, int V, hipStream_t s) {
-  const int64_t chunks = (int64_t)N * V / 8;
+hipError_t normalize_probs_bf16(uint16_t *probs, const float *tile_scale, int N, int V, hipStream_t s) {
+  if (N > TL_ROWS) return hipErrorInvalidValue;
+  const int64_t chunks = (int64_t)(V / TL_K) * TL_CHUNKS;
   const int64_t blocks = (chunks + 255) / 256;
   hipLaunchKernelGGL(normalize_bf16_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s,
-                     probs, tile_scale, chunks, V);
+                     probs, tile_scale, chunks, N, V);
   return hipGetLastError();
 }
-template <>
-hipError_t normalize_probs<float>(float *probs, const float *tile_scale, int N, int V, hipStream_t s) {
+hipError_t normalize_probs_f32(float *probs, const float *tile_scale, int N, int V, hipStream_t s) {
   const int64_t chunks = (int64_t)N * V / 4;
   const int64_t blocks = (chunks + 255) / 256;
   hipLaunchKernelGGL(normalize_f32_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s,
                      probs, tile_scale, chunks, V);
+  return hipGetLastError();
+}
+
+// Tiled copy: one thread per 16-byte chunk of the output.
+__global__ void tile_rows_kernel(const bf16 *__restrict__ X, int R, int K, int64_t ldx, bf16 *__restrict__ out,
+                                 int64_t chunks) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * blockDim.x) {
+    const int p = (int)(i & (TL_CHUNKS - 1));
+    const int64_t bs = i >> 10;
+    const int ks = K / TL_K;
+    const int b = (int)(bs / ks), slice = (int)(bs % ks);
+    const int r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
+    const int row = b * TL_ROWS + r;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < R) {
+      const bf16 *src = X + (int64_t)row * ldx + slice * TL_K + c * 8;
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = (uint32_t)src[2 * k] | ((uint32_t)src[2 * k + 1] << 16);
+      v = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    reinterpret_cast<uint4 *>(out)[i] = v;
+  }
+}
+
+hipError_t tile_rows(const uint16_t *X, int R, int K, int64_t ldx, uint16_t *out, hipStream_t s) {
+  if (K % TL_K) return hipErrorInvalidValue;
+  const int64_t chunks = (int64_t)tl_elems(R, K) / 8;
+  const int64_t blocks = (chunks + 255) / 256;
+  hipLaunchKernelGGL(tile_rows_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s, X, R, K,
+                     ldx, out, chunks);
   return hipGetLastError();
 }
 

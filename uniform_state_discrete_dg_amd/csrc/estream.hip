@@ -15,20 +15,20 @@
 // __syncthreads would carry a release fence that drains every DMA in flight.
 // 8 waves (2 per SIMD), each 64 canvas rows x 128 table rows.
 //
+// Both operands are in the tiled layout of dg_tiled.h: a slice of a 256-row
+// block is 16 KB of consecutive memory already in LDS order (chunk c of row
+// r at position c ^ ((r >> 2) & 3), which keeps the 32 rows a fragment read
+// touches, 16 lanes at a time, on distinct banks), so every DMA instruction
+// copies 1 KB of consecutive bytes.
+//
 // The MFMA takes the table fragment as its first operand, so a lane's
 // accumulators hold one canvas row and 16 of the 32 table rows of a
 // fragment (its partner lane, lane ^ 32, holds the other 16): the softmax
 // statistics over a 64-column tile are reduced in registers, with a single
 // exchange between the two partner lanes.
-//
-// LDS layout of a slice: row-major, 64 bytes per row = four 16-byte chunks;
-// chunk c of row r lives at position c ^ ((r >> 2) & 3).  A fragment load
-// reads 32 rows at one chunk; any 16 consecutive lanes then cover the 64
-// banks once.  The DMA writes 64 lanes x 16 bytes contiguously, so the
-// swizzle is applied by choosing each lane's source address.
 #include "dg_device.h"
 #include "dg_kernels.h"
-
+#include "dg_tiled.h"
 
 namespace dg {
 
@@ -40,6 +40,7 @@ constexpr int ES_BK = 32;         // k per slice
 constexpr int ES_STAGES = 4;      // LDS stages (3 slices in flight)
 constexpr int ES_SLICE = ES_BM * ES_BK * 2;  // bytes of one operand slice (16 KB)
 constexpr float LOG2E = 1.4426950408889634f;
+static_assert(ES_BM == TL_ROWS && ES_BN == TL_ROWS && ES_BK == TL_K, "slices are tiled-layout blocks");
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= n, no wait on exp/lgkm.
 template <int n>
@@ -48,19 +49,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__device__ __forceinline__ int slot16(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
-
 }  // namespace
 
 // Accumulates acc[i][j] (wave tile: canvas rows wm*64 + 32i, table rows
-// wn*128 + 32j) over k in [kb, ke) (multiples of 32).  Layout of acc[i][j]:
-// lane holds canvas row 32i + (lane & 31) and, in register r, table row
-// 8 (r >> 2) + 4 (lane >> 5) + (r & 3) of the fragment.  A: [M][lda] canvas rows m0..,
-// B: [N][ldb] table rows n0..; rows past M / N read a clamped valid row and
-// only feed accumulators the epilogues discard.
-__device__ __forceinline__ void estream_tile(const bf16 *__restrict__ A, int64_t lda, int M, int m0,
-                                             const bf16 *__restrict__ B, int64_t ldb, int N, int n0, int kb,
-                                             int ke, char *lds, f32x16_t (&acc)[2][4]) {
+// wn*128 + 32j) over the slices [sb, se) of two tiled blocks: At is the
+// canvas block, Bt the table block (each 256 rows, slice s at + s * 8192).
+// Layout of acc[i][j]: lane holds canvas row 32i + (lane & 31) and, in
+// register r, table row 8 (r >> 2) + 4 (lane >> 5) + (r & 3) of the fragment.
+// The operands are restrict-qualified parameters: the compiler then adds no
+// wait of its own between the DMA copies and the LDS reads (the s_waitcnt /
+// s_barrier pairs order them).
+__device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const bf16 *__restrict__ Bt, int sb,
+                                             int se, char *lds, f32x16_t (&acc)[2][4]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r32 = lane & 31, g = lane >> 5;
@@ -72,86 +72,90 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ A, int64_t
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // DMA sources: this wave fills 2 KB of each operand slice (2 instructions
-  // of 64 lanes x 16 bytes); position p -> row p / 4, logical chunk.
-  const bf16 *asrc[2], *bsrc[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int p = (wave * 2 + u) * 64 + lane;
-    const int row = p >> 2;
-    const int c = (p & 3) ^ ((row >> 2) & 3);
-    const int ar = m0 + row, br = n0 + row;
-    asrc[u] = A + (int64_t)(ar < M ? ar : M - 1) * lda + c * 8;
-    bsrc[u] = B + (int64_t)(br < N ? br : N - 1) * ldb + c * 8;
-  }
-  const int nk = (ke - kb) / ES_BK;
+  const int nk = se - sb;
   if (nk <= 0) return;
-  const int klast = kb + ES_BK * (nk - 1);
+  // DMA: this wave copies 2 KB of each operand slice (2 instructions of 64
+  // lanes x 16 bytes), chunks p = (2 wave + u) * 64 + lane.
+  const bf16 *asrc = At + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
+  const bf16 *bsrc = Bt + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
   auto issue = [&](int slice, int stage) {
-    const int k0 = min(kb + ES_BK * slice, klast);
+    const int64_t off = (int64_t)min(slice, nk - 1) * TL_ELEMS;  // past the end: a repeat, never read
     char *st = lds + stage * 2 * ES_SLICE;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      __builtin_amdgcn_global_load_lds(asrc[u] + k0, st + (wave * 2 + u) * 1024, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(bsrc[u] + k0, st + ES_SLICE + (wave * 2 + u) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(asrc + off + u * 512, st + (wave * 2 + u) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bsrc + off + u * 512, st + ES_SLICE + (wave * 2 + u) * 1024, 16, 0, 0);
     }
   };
-  // loads per slice per wave: 4 DMA
-  constexpr int PER = 4;
+  constexpr int PER = 4;  // DMA instructions per slice per wave
 
+  // Fragments of one 16-wide k step: 2 canvas + 4 table 16-byte reads.
+  auto frags = [&](int stage, int kk, bf16x8_t (&fa)[2], bf16x8_t (&fb)[4]) {
+    const uint4 *sa = reinterpret_cast<const uint4 *>(lds + stage * 2 * ES_SLICE);
+    const uint4 *sbq = reinterpret_cast<const uint4 *>(lds + stage * 2 * ES_SLICE + ES_SLICE);
+    const int c = kk * 2 + g;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fa[i] = __builtin_bit_cast(bf16x8_t, sa[tl_pos(wm * 64 + i * 32 + r32, c)]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, sbq[tl_pos(wn * 128 + j * 32 + r32, c)]);
+  };
+  auto mfmas = [&](const bf16x8_t (&fa)[2], const bf16x8_t (&fb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  };
+
+  // Software pipeline: the barrier sits between the two k halves of a slice,
+  // so the first-half fragments of slice it+1 are read while the second-half
+  // MFMAs of slice it run.  At the barrier of iteration it every wave has
+  // consumed slice it-1 (its second half ran before), so the DMA of slice
+  // it+3 may refill that stage.
   issue(0, 0);
   issue(1, 1);
   issue(2, 2);
+  bf16x8_t fa0[2], fb0[4], fa1[2], fb1[4];
+  wait_vmcnt<2 * PER>();
+  __builtin_amdgcn_s_barrier();
+  frags(0, 0, fa0, fb0);
   for (int it = 0; it < nk; ++it) {
-    const int stage = it & 3;
-    wait_vmcnt<2 * PER>();          // this wave's loads for slice `it` are done
-    __builtin_amdgcn_s_barrier();   // ... and every wave's; slice it-1 is consumed
-    issue(it + 3, (it + 3) & 3);    // refill the stage slice it-1 used
-    const uint4 *sa = reinterpret_cast<const uint4 *>(lds + stage * 2 * ES_SLICE);
-    const uint4 *sb = reinterpret_cast<const uint4 *>(lds + stage * 2 * ES_SLICE + ES_SLICE);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = kk * 2 + g;
-      bf16x8_t fa[2], fb[4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = __builtin_bit_cast(bf16x8_t, sa[slot16(wm * 64 + i * 32 + r32, c)]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, sb[slot16(wn * 128 + j * 32 + r32, c)]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-    }
+    frags(it & 3, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    wait_vmcnt<PER>();             // this wave's copies of slice it+1 landed
+    __builtin_amdgcn_s_barrier();  // ... every wave's; every wave is done with slice it-1
+    issue(it + 3, (it + 3) & 3);
+    frags((it + 1) & 3, 0, fa0, fb0);  // past the last slice: a repeat, unused
+    mfmas(fa1, fb1);
   }
   wait_vmcnt<0>();  // retire the trailing (unused) prefetches before LDS is reused
   __builtin_amdgcn_s_barrier();
 }
 
 // ---------------------------------------------------------------------------
-// LM head: workgroup = canvas rows x 256 vocabulary columns; a wave holds 64
-// rows x 128 columns = two 64-column tiles of the softmax statistics.  Per
-// canvas row and tile a lane holds 32 of the 64 logits (its partner lane the
-// other 32): the max of z and its lowest column, exp(y - m) written once as
-// bf16, l = sum exp(y - m) and s = sum exp(y - m)(y - m), with y = z / T and
-// m = zmax / T, are reduced in registers plus one exchange with the partner.
+// LM head: workgroup = the canvas block x 256 vocabulary columns; a wave
+// holds 64 rows x 128 columns = two 64-column tiles of the softmax
+// statistics.  Per canvas row and tile a lane holds 32 of the 64 logits (its
+// partner lane the other 32): the max of z and its lowest column, exp(y - m)
+// written once as bf16 (tiled layout), l = sum exp(y - m) and
+// s = sum exp(y - m)(y - m), with y = z / T and m = zmax / T, are reduced in
+// registers plus one exchange with the partner.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__restrict__ A, int M, int K,
-                                                              const bf16 *__restrict__ E, int V, float inv_T,
+__global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__restrict__ At, int M, int K,
+                                                              const bf16 *__restrict__ Et, int V, float inv_T,
                                                               bf16 *__restrict__ probs, float4 *__restrict__ tile_stats,
                                                               float *__restrict__ logits) {
   extern __shared__ __align__(16) char lds[];
   const int n0 = blockIdx.x * ES_BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
-  const int m0 = blockIdx.y * ES_BM;
+  const int ksl = K / ES_BK;
   f32x16_t acc[2][4];
-  estream_tile(A, K, M, m0, E, K, V, n0, 0, K, lds, acc);
+  estream_tile(At, Et + (int64_t)blockIdx.x * ksl * TL_ELEMS, 0, ksl, lds, acc);
   const int ntiles = V / 64;
 
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int row = m0 + wm * 64 + i * 32 + (lane & 31);
+    const int row = wm * 64 + i * 32 + (lane & 31);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int tile = (n0 + wn * 128 + h * 64) / 64;
@@ -194,18 +198,20 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
       l += __shfl_xor(l, 32);
       sacc += __shfl_xor(sacc, 32);
       if (row < M) {
-        const int64_t o = (int64_t)row * V + cbase;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+        for (int jj = 0; jj < 2; ++jj) {
+          // slice 2 tile + jj; the lane's four values of chunk q are elements 4g..4g+3
+          bf16 *blk = probs + (int64_t)(2 * tile + jj) * TL_ELEMS + 4 * g;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<uint2 *>(probs + o + 32 * jj + 8 * q) = make_uint2(pk[jj][2 * q], pk[jj][2 * q + 1]);
+            *reinterpret_cast<uint2 *>(blk + tl_pos(row, q) * 8) = make_uint2(pk[jj][2 * q], pk[jj][2 * q + 1]);
             if (logits) {
               const f32x16_t &z = acc[i][2 * h + jj];
-              *reinterpret_cast<float4 *>(logits + o + 32 * jj + 8 * q) =
+              *reinterpret_cast<float4 *>(logits + (int64_t)row * V + cbase + 32 * jj + 8 * q) =
                   make_float4(z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]);
             }
           }
+        }
         if (g == 0) tile_stats[(int64_t)row * ntiles + tile] = make_float4(best, l, sacc, __int_as_float(bcol));
       }
     }
@@ -216,8 +222,9 @@ int estream_bm(int) { return ES_BM; }
 
 static size_t es_lds_bytes() { return (size_t)ES_STAGES * 2 * ES_SLICE; }
 
-hipError_t lm_head_bf16(const uint16_t *A, int M, int K, const uint16_t *E, int V, float inv_T, uint16_t *probs,
-                        float4 *tile_stats, float *logits_dump, hipStream_t s) {
+hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E_tiled, int V, float inv_T,
+                        uint16_t *probs_tiled, float4 *tile_stats, float *logits_dump, hipStream_t s) {
+  if (M > ES_BM || K % ES_BK || V % ES_BN) return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(lm_head_es_kernel),
@@ -225,9 +232,8 @@ hipError_t lm_head_bf16(const uint16_t *A, int M, int K, const uint16_t *E, int 
       return hipErrorInvalidValue;
     attr = true;
   }
-  dim3 grid(V / ES_BN, (M + ES_BM - 1) / ES_BM);
-  hipLaunchKernelGGL(lm_head_es_kernel, grid, dim3(ES_NT), es_lds_bytes(), s, A, M, K, E, V, inv_T, probs,
-                     tile_stats, logits_dump);
+  hipLaunchKernelGGL(lm_head_es_kernel, dim3(V / ES_BN), dim3(ES_NT), es_lds_bytes(), s, A_tiled, M, K, E_tiled, V,
+                     inv_T, probs_tiled, tile_stats, logits_dump);
   return hipGetLastError();
 }
 
@@ -238,30 +244,25 @@ hipError_t lm_head_bf16(const uint16_t *A, int M, int K, const uint16_t *E, int 
 // work items of one K-chunk to workgroups of one XCD where it can, so the
 // chunk of probabilities they share is fetched into that XCD's L2 once.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(GemmShape g, float *__restrict__ part, int ksplit,
+__global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(TiledGemm g, float *__restrict__ part, int ksplit,
                                                                int ntn, int items) {
   extern __shared__ __align__(16) char lds[];
   const int b = blockIdx.x, nb = gridDim.x;
   const int per_xcd = nb / 8;  // grid is a multiple of 8
   const int item = (b % 8) * per_xcd + b / 8;
   if (item >= items) return;
-  const int mblocks = (g.M + ES_BM - 1) / ES_BM;
-  const int mb = item % mblocks;
-  const int kc = (item / mblocks) / ntn, nt = (item / mblocks) % ntn;
-  const int m0 = mb * ES_BM;
-  const int nslices = g.K / 64;  // chunks of whole 64-column units (two slices)
-  const int kb = (int)((int64_t)nslices * kc / ksplit) * 64;
-  const int ke = (int)((int64_t)nslices * (kc + 1) / ksplit) * 64;
+  const int kc = item / ntn, nt = item % ntn;
+  const int ksl = g.K / ES_BK;
+  const int sb = (int)((int64_t)ksl * kc / ksplit), se = (int)((int64_t)ksl * (kc + 1) / ksplit);
   const int n0 = nt * ES_BN;
   f32x16_t acc[2][4];
-  estream_tile(static_cast<const bf16 *>(g.A), g.lda, g.M, m0, static_cast<const bf16 *>(g.B), g.ldb, g.N, n0, kb,
-               ke, lds, acc);
+  estream_tile(g.A, g.B + (int64_t)nt * ksl * TL_ELEMS, sb, se, lds, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   float *out = part + (int64_t)kc * g.M * g.N;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int row = m0 + wm * 64 + i * 32 + (lane & 31);
+    const int row = wm * 64 + i * 32 + (lane & 31);
     if (row >= g.M) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -276,7 +277,8 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(GemmShape g, floa
   }
 }
 
-hipError_t selfcond_bf16(const GemmShape &g, float *partials, int ksplit, hipStream_t s) {
+hipError_t selfcond_bf16(const TiledGemm &g, float *partials, int ksplit, hipStream_t s) {
+  if (g.M > ES_BM || g.K % ES_BK || g.N % 4 || ksplit < 1 || ksplit > g.K / ES_BK) return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(selfcond_es_kernel),
@@ -285,7 +287,7 @@ hipError_t selfcond_bf16(const GemmShape &g, float *partials, int ksplit, hipStr
     attr = true;
   }
   const int ntn = (g.N + ES_BN - 1) / ES_BN;
-  const int items = ntn * ksplit * ((g.M + ES_BM - 1) / ES_BM);
+  const int items = ntn * ksplit;
   const int grid = (items + 7) / 8 * 8;
   hipLaunchKernelGGL(selfcond_es_kernel, dim3(grid), dim3(ES_NT), es_lds_bytes(), s, g, partials, ksplit, ntn,
                      items);

@@ -44,137 +44,186 @@ __device__ __forceinline__ void epi_store(const Epi &e, int row, int col, float 
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int PG_NT = 256;
-constexpr int PG_BM = 64, PG_BN = 128, PG_BK = 32, PG_STAGES = 4;
-constexpr int PG_ASLICE = PG_BM * PG_BK * 4;  // fp32 A slice: 8 KB
-constexpr int PG_BSLICE = PG_BN * PG_BK * 2;  // bf16 B slice: 8 KB
-constexpr int PG_STAGE = PG_ASLICE + PG_BSLICE;
+constexpr int PG_BK = 32;
+// default tile: rows x columns per workgroup, LDS stages
+constexpr int PG_BM = 128, PG_BN = 128, PG_STAGES = 6;
 
 template <int n>
 __device__ __forceinline__ void pg_wait_vmcnt() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
-// A slice: 64 rows x 8 chunks of 4 floats; chunk c of row r at c ^ ((r >> 1) & 7)
+// A slice: rows x 8 chunks of 4 floats; chunk c of row r at c ^ ((r >> 1) & 7)
 __device__ __forceinline__ int a_slot(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
-// B slice: 128 rows x 4 chunks of 8 bf16; chunk c of row r at c ^ ((r >> 2) & 3)
+// B slice: rows x 4 chunks of 8 bf16; chunk c of row r at c ^ ((r >> 2) & 3)
 __device__ __forceinline__ int b_slot(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
+
+template <int BM, int BN, int STAGES>
+struct PgCfg {
+  static constexpr int ASLICE = BM * PG_BK * 4;  // fp32 A slice
+  static constexpr int BSLICE = BN * PG_BK * 2;  // bf16 B slice
+  static constexpr int STAGE = ASLICE + BSLICE;
+  static constexpr int LDS = STAGES * STAGE;
+  static constexpr int UA = BM / 32, UB = BN / 64;  // DMA instructions per wave per slice
+  static constexpr int PER = UA + UB;
+  static constexpr int FM = BM / 64, FN = BN / 64;  // 32-wide fragments per wave (2 x 2 waves)
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && STAGES >= 3, "tile");
+  static_assert((STAGES - 2) * PER < 64, "vmcnt range");
+};
 }  // namespace
 
-// Accumulates acc[j] (wave tile rows wm*32 + [0, 32), columns wn*64 + 32 j +
-// [0, 32)) over the slices [sb, sb + nk) of K.  The operands come in as
-// restrict-qualified parameters: that tells the compiler the LDS reads do not
-// depend on the DMA copies in flight (the s_waitcnt / s_barrier pair before
-// each slice orders them), so it adds no wait of its own.
+// Accumulates acc[i][j] (wave tile rows wm*BM/2 + 32 i + [0, 32), columns
+// wn*BN/2 + 32 j + [0, 32)) over the slices [sb, sb + nk) of K.  The
+// operands come in as restrict-qualified parameters: that tells the
+// compiler the LDS reads do not depend on the DMA copies in flight (the
+// s_waitcnt / s_barrier pair before each slice orders them), so it adds no
+// wait of its own.
+template <int BM, int BN, int STAGES>
 __device__ __forceinline__ void pg_tile(const float *__restrict__ A, int64_t lda, int M, int m0,
                                         const bf16 *__restrict__ B, int K, int N, int n0, int sb, int nk, char *lds,
-                                        f32x16_t (&acc)[2]) {
+                                        f32x16_t (&acc)[BM / 64][BN / 64]) {
+  using C = PgCfg<BM, BN, STAGES>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, gq = lane >> 5;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   if (nk <= 0) return;
 
-  // DMA sources: per slice each wave copies 2 KB of A and 2 KB of B
-  // (2 + 2 instructions of 64 lanes x 16 bytes); rows past M / N read a
-  // clamped valid row and only feed discarded accumulators.
-  const float *asrc[2];
-  const bf16 *bsrc[2];
+  // DMA sources: per slice each wave copies its share of the A slice and of
+  // the B slice in instructions of 64 lanes x 16 bytes; rows past M / N read
+  // a clamped valid row and only feed discarded accumulators.
+  const float *asrc[C::UA];
+  const bf16 *bsrc[C::UB];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int p = (wave * 2 + u) * 64 + lane;
-    {
-      const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
-      const int gr = m0 + row < M ? m0 + row : M - 1;
-      asrc[u] = A + (int64_t)gr * lda + c * 4;
-    }
-    {
-      const int row = p >> 2, c = (p & 3) ^ ((row >> 2) & 3);
-      const int gn = n0 + row < N ? n0 + row : N - 1;
-      bsrc[u] = B + (int64_t)gn * K + c * 8;
-    }
+  for (int u = 0; u < C::UA; ++u) {
+    const int p = (wave * C::UA + u) * 64 + lane;
+    const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+    const int gr = m0 + row < M ? m0 + row : M - 1;
+    asrc[u] = A + (int64_t)gr * lda + c * 4;
+  }
+#pragma unroll
+  for (int u = 0; u < C::UB; ++u) {
+    const int p = (wave * C::UB + u) * 64 + lane;
+    const int row = p >> 2, c = (p & 3) ^ ((row >> 2) & 3);
+    const int gn = n0 + row < N ? n0 + row : N - 1;
+    bsrc[u] = B + (int64_t)gn * K + c * 8;
   }
   auto issue = [&](int slice, int stage) {
     const int k0 = (sb + min(slice, nk - 1)) * PG_BK;
-    char *st = lds + stage * PG_STAGE;
+    char *st = lds + stage * C::STAGE;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      __builtin_amdgcn_global_load_lds(asrc[u] + k0, st + (wave * 2 + u) * 1024, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(bsrc[u] + k0, st + PG_ASLICE + (wave * 2 + u) * 1024, 16, 0, 0);
-    }
+    for (int u = 0; u < C::UA; ++u)
+      __builtin_amdgcn_global_load_lds(asrc[u] + k0, st + (wave * C::UA + u) * 1024, 16, 0, 0);
+#pragma unroll
+    for (int u = 0; u < C::UB; ++u)
+      __builtin_amdgcn_global_load_lds(bsrc[u] + k0, st + C::ASLICE + (wave * C::UB + u) * 1024, 16, 0, 0);
   };
-  issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t) issue(t, t);
+  int stage = 0, nstage = STAGES - 1;  // stage of slice it, stage slice it + STAGES - 1 goes to
   for (int it = 0; it < nk; ++it) {
-    const int stage = it & 3;
-    pg_wait_vmcnt<8>();             // this wave's copies of slice `it` landed
-    __builtin_amdgcn_s_barrier();   // ... and every wave's; slice it-1 is consumed
-    issue(it + 3, (it + 3) & 3);
-    const float4 *sa = reinterpret_cast<const float4 *>(lds + stage * PG_STAGE);
-    const uint4 *sbq = reinterpret_cast<const uint4 *>(lds + stage * PG_STAGE + PG_ASLICE);
+    pg_wait_vmcnt<(STAGES - 2) * C::PER>();  // this wave's copies of slice `it` landed
+    __builtin_amdgcn_s_barrier();             // ... and every wave's; slice it-1 is consumed
+    issue(it + STAGES - 1, nstage);
+    const float4 *sa = reinterpret_cast<const float4 *>(lds + stage * C::STAGE);
+    const uint4 *sbq = reinterpret_cast<const uint4 *>(lds + stage * C::STAGE + C::ASLICE);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       // k of this lane: 16 kk + 8 gq + [0, 8) for both operands
-      const int arow = wm * 32 + r32;
-      const float4 x0 = sa[a_slot(arow, 4 * kk + 2 * gq)];
-      const float4 x1 = sa[a_slot(arow, 4 * kk + 2 * gq + 1)];
-      uint4 hi, lo;
-      split8(x0, x1, hi, lo);
-      const bf16x8_t fh = __builtin_bit_cast(bf16x8_t, hi), fl = __builtin_bit_cast(bf16x8_t, lo);
+      bf16x8_t fh[C::FM], fl[C::FM];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, sbq[b_slot(wn * 64 + j * 32 + r32, 2 * kk + gq)]);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fl, acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fh, acc[j], 0, 0, 0);
+      for (int i = 0; i < C::FM; ++i) {
+        const int arow = wm * (BM / 2) + 32 * i + r32;
+        const float4 x0 = sa[a_slot(arow, 4 * kk + 2 * gq)];
+        const float4 x1 = sa[a_slot(arow, 4 * kk + 2 * gq + 1)];
+        uint4 hi, lo;
+        split8(x0, x1, hi, lo);
+        fh[i] = __builtin_bit_cast(bf16x8_t, hi);
+        fl[i] = __builtin_bit_cast(bf16x8_t, lo);
+      }
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const bf16x8_t fb =
+            __builtin_bit_cast(bf16x8_t, sbq[b_slot(wn * (BN / 2) + 32 * j + r32, 2 * kk + gq)]);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fl[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fh[i], acc[i][j], 0, 0, 0);
+        }
       }
     }
+    stage = stage + 1 == STAGES ? 0 : stage + 1;
+    nstage = nstage + 1 == STAGES ? 0 : nstage + 1;
   }
   pg_wait_vmcnt<0>();  // retire the trailing (unused) prefetches
 }
 
+// Work items are (column tile p, row tile, K range), the column tiles of all
+// segments numbered one after the other.  The hardware hands consecutive
+// workgroups to the 8 XCDs in turn; workgroup b serves column tiles
+// p = b % 8 (mod 8), so each weight tile is fetched into one XCD's L2 and
+// shared there by the row tiles and K ranges that use it.
+template <int BM, int BN, int STAGES>
 __global__ void __launch_bounds__(PG_NT) gemm_split_kernel(SplitGemm g) {
+  using C = PgCfg<BM, BN, STAGES>;
   extern __shared__ __align__(16) char lds[];
-  const int seg = blockIdx.z / g.ksplit, kc = blockIdx.z % g.ksplit;
-  const int N = g.N[seg];
-  const int m0 = blockIdx.y * PG_BM, n0 = blockIdx.x * PG_BN;
-  if (n0 >= N) return;  // uniform per block
   const int M = g.M, K = g.K;
+  const int mt = (M + BM - 1) / BM;
+  int P = 0;
+  for (int t = 0; t < g.count; ++t) P += (g.N[t] + BN - 1) / BN;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int per = mt * g.ksplit;
+  if (xcd >= P || local >= ((P - xcd + 7) >> 3) * per) return;  // uniform per block
+  int p = xcd + 8 * (local / per);
+  const int kc = (local % per) / mt, m0 = (local % per % mt) * BM;
+  int seg = 0;
+  while (p >= (g.N[seg] + BN - 1) / BN) {
+    p -= (g.N[seg] + BN - 1) / BN;
+    ++seg;
+  }
+  const int N = g.N[seg], n0 = p * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, gq = lane >> 5;
   const int nsl = K / PG_BK;
   const int sb = (int)((int64_t)nsl * kc / g.ksplit), se = (int)((int64_t)nsl * (kc + 1) / g.ksplit);
-  f32x16_t acc[2];
-  pg_tile(g.A, g.lda, M, m0, static_cast<const bf16 *>(g.B[seg]), K, N, n0, sb, se - sb, lds, acc);
+  f32x16_t acc[C::FM][C::FN];
+  pg_tile<BM, BN, STAGES>(g.A, g.lda, M, m0, static_cast<const bf16 *>(g.B[seg]), K, N, n0, sb, se - sb, lds, acc);
 
-  // lane: output row m0 + wm*32 + r32; register r of fragment j is column
-  // n0 + wn*64 + 32 j + 8 (r >> 2) + 4 gq + (r & 3)
-  const int row = m0 + wm * 32 + r32;
-  if (row >= M) return;
-  if (g.ksplit > 1) {
-    size_t base = 0;
+  // lane: output rows m0 + wm*BM/2 + 32 i + r32; register r of fragment j is
+  // column n0 + wn*BN/2 + 32 j + 8 (r >> 2) + 4 gq + (r & 3)
+  size_t base = 0;
+  if (g.ksplit > 1)
     for (int t = 0; t < seg; ++t) base += (size_t)g.ksplit * M * g.N[t];
-    float *out = g.part + base + ((size_t)kc * M + row) * N;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = n0 + wn * 64 + 32 * j + 8 * q + 4 * gq;
-        if (col < N)
-          *reinterpret_cast<float4 *>(out + col) =
-              make_float4(acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]);
-      }
-    return;
-  }
   const Epi e = g.e[seg];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < C::FM; ++i) {
+    const int row = m0 + wm * (BM / 2) + 32 * i + r32;
+    if (row >= M) continue;
+    if (g.ksplit > 1) {
+      float *out = g.part + base + ((size_t)kc * M + row) * N;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int col = n0 + wn * 64 + 32 * j + 8 * (r >> 2) + 4 * gq + (r & 3);
-      if (col < N) epi_store(e, row, col, acc[j][r]);
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * (BN / 2) + 32 * j + 8 * q + 4 * gq;
+          if (col < N)
+            *reinterpret_cast<float4 *>(out + col) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int col = n0 + wn * (BN / 2) + 32 * j + 8 * (r >> 2) + 4 * gq + (r & 3);
+          if (col < N) epi_store(e, row, col, acc[i][j][r]);
+        }
     }
+  }
 }
 
 // Sum of the K-split partials + epilogue: one thread per 4 consecutive
@@ -224,27 +273,35 @@ size_t gemm_split_part_bytes(int M, int K, const int *N, int count) {
   return n * 4;
 }
 
-hipError_t gemm_split(const SplitGemm &g, hipStream_t s) {
+template <int BM, int BN, int STAGES>
+hipError_t gemm_split_launch(const SplitGemm &g, hipStream_t s) {
+  using C = PgCfg<BM, BN, STAGES>;
   if (g.ksplit < 1 || (g.ksplit > 1 && !g.part) || g.K % PG_BK) return hipErrorInvalidValue;
   for (int i = 0; i < g.count; ++i)
     if (g.N[i] % 4) return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_split_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, PG_STAGES * PG_STAGE) != hipSuccess)
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_split_kernel<BM, BN, STAGES>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess)
       return hipErrorInvalidValue;
     attr = true;
   }
-  int maxN = 0;
-  for (int i = 0; i < g.count; ++i) maxN = g.N[i] > maxN ? g.N[i] : maxN;
-  dim3 grid((maxN + PG_BN - 1) / PG_BN, (g.M + PG_BM - 1) / PG_BM, g.count * g.ksplit);
-  hipLaunchKernelGGL(gemm_split_kernel, grid, dim3(PG_NT), PG_STAGES * PG_STAGE, s, g);
+  int maxN = 0, P = 0;
+  for (int i = 0; i < g.count; ++i) {
+    maxN = g.N[i] > maxN ? g.N[i] : maxN;
+    P += (g.N[i] + BN - 1) / BN;
+  }
+  const int per = (g.M + BM - 1) / BM * g.ksplit;
+  const int grid = 8 * ((P + 7) / 8) * per;  // XCD 0 serves the most column tiles
+  hipLaunchKernelGGL((gemm_split_kernel<BM, BN, STAGES>), dim3(grid), dim3(PG_NT), C::LDS, s, g);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || g.ksplit == 1) return err;
   const int64_t quads = (int64_t)g.M * maxN / 4;
   hipLaunchKernelGGL(gemm_splitk_epilogue_kernel, dim3((unsigned)((quads + 255) / 256), g.count), dim3(256), 0, s, g);
   return hipGetLastError();
 }
+
+hipError_t gemm_split(const SplitGemm &g, hipStream_t s) { return gemm_split_launch<PG_BM, PG_BN, PG_STAGES>(g, s); }
 
 // ---------------------------------------------------------------------------
 // fp32 SIMT GEMM (the fp32 configuration): 16x16 outputs per workgroup,
