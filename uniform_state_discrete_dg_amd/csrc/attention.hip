@@ -33,10 +33,13 @@ constexpr float LOG2E = 1.4426950408889634f;
 }  // namespace
 
 __device__ __forceinline__ int kswz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
+// V^T in LDS: [128 hd][8 groups of 8 keys], group u of row hd at u ^ ((hd >> 1) & 7),
+// so the 16 rows a fragment read touches at one group fall on distinct banks.
+__device__ __forceinline__ int vswz(int hd, int u) { return hd * 8 + (u ^ ((hd >> 1) & 7)); }
 
 __global__ void __launch_bounds__(NTH) attn_split_kernel(AttnArgs a) {
   __shared__ uint4 Ks[2][KT * HD / 8];     // hi, lo: [64 keys][16 chunks of 8]
-  __shared__ uint2 Vt[2][HD * KT / 4];     // hi, lo: [128 hd][16 units of 4 keys]
+  __shared__ uint4 Vt[2][HD * KT / 8];     // hi, lo: [128 hd][8 chunks of 8 keys]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 5;
   const int h = blockIdx.y, z = blockIdx.z;
@@ -74,36 +77,53 @@ __global__ void __launch_bounds__(NTH) attn_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.f;
 
-  // 64 keys x 128 = 1024 chunks of 8 floats per tile; 4 chunks per thread.
-  float4 rk[4][2], rv[4][2];
+  // A tile is 64 keys x 128.  K: 1024 chunks of 8 floats, 4 per thread
+  // (thread -> key idx / 16, chunk idx % 16).  V: thread -> 4 dims
+  // (4 (tid % 32) ..) x the 8 keys of group u = tid / 32, which it writes as
+  // 8-key vectors of V^T.  Group u holds, in MFMA k order, the keys that a
+  // lane's probabilities cover in the P^T fragment: with c = u / 2 and
+  // g = u % 2, keys 16 c + 4 g + {0..3} then 16 c + 8 + 4 g + {0..3}.
+  float4 rk[4][2], rv[8];
+  auto kv_src = [&](int kabs, int col, const float *&kp, const float *&vp, int64_t &off) {
+    if (kabs < a.nA) {
+      off = ((int64_t)g * a.capA + kabs) * HD + col;
+      kp = kA;
+      vp = vA;
+    } else {
+      off = ((int64_t)g * a.capB + (kabs - a.nA)) * HD + col;
+      kp = kB;
+      vp = vB;
+    }
+  };
   auto load = [&](int kt0) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int idx = tid + t * NTH;
       const int key = idx >> 4, ch = idx & 15;
       const int kabs = kt0 + key;
-      float4 k0 = make_float4(0.f, 0.f, 0.f, 0.f), k1 = k0, v0 = k0, v1 = k0;
+      float4 k0 = make_float4(0.f, 0.f, 0.f, 0.f), k1 = k0;
       if (kabs < kend) {
         int64_t off;
         const float *kp, *vp;
-        if (kabs < a.nA) {
-          off = ((int64_t)g * a.capA + kabs) * HD + ch * 8;
-          kp = kA;
-          vp = vA;
-        } else {
-          off = ((int64_t)g * a.capB + (kabs - a.nA)) * HD + ch * 8;
-          kp = kB;
-          vp = vB;
-        }
+        kv_src(kabs, ch * 8, kp, vp, off);
         k0 = *reinterpret_cast<const float4 *>(kp + off);
         k1 = *reinterpret_cast<const float4 *>(kp + off + 4);
-        v0 = *reinterpret_cast<const float4 *>(vp + off);
-        v1 = *reinterpret_cast<const float4 *>(vp + off + 4);
       }
       rk[t][0] = k0;
       rk[t][1] = k1;
-      rv[t][0] = v0;
-      rv[t][1] = v1;
+    }
+    const int d4 = tid & 31, kg = tid >> 5;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kabs = kt0 + 16 * (kg >> 1) + 4 * (kg & 1) + (j & 3) + 8 * (j >> 2);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (kabs < kend) {
+        int64_t off;
+        const float *kp, *vp;
+        kv_src(kabs, d4 * 4, kp, vp, off);
+        v = *reinterpret_cast<const float4 *>(vp + off);
+      }
+      rv[j] = v;
     }
   };
   auto store = [&]() {
@@ -115,17 +135,16 @@ __global__ void __launch_bounds__(NTH) attn_split_kernel(AttnArgs a) {
       split8(rk[t][0], rk[t][1], hi, lo);
       Ks[0][kswz(key, ch)] = hi;
       Ks[1][kswz(key, ch)] = lo;
-      split8(rv[t][0], rv[t][1], hi, lo);
-      const uint32_t wh[4] = {hi.x, hi.y, hi.z, hi.w}, wl[4] = {lo.x, lo.y, lo.z, lo.w};
-      bf16 *vth = reinterpret_cast<bf16 *>(Vt[0]);
-      bf16 *vtl = reinterpret_cast<bf16 *>(Vt[1]);
+    }
+    const int d4 = tid & 31, kg = tid >> 5;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int hd = ch * 8 + e;
-        const int pos = hd * KT + (((key >> 2) ^ (hd & 15)) << 2) + (key & 3);
-        vth[pos] = (bf16)((e & 1) ? (wh[e >> 1] >> 16) : (wh[e >> 1] & 0xffffu));
-        vtl[pos] = (bf16)((e & 1) ? (wl[e >> 1] >> 16) : (wl[e >> 1] & 0xffffu));
-      }
+    for (int e = 0; e < 4; ++e) {
+      const float x[8] = {(&rv[0].x)[e], (&rv[1].x)[e], (&rv[2].x)[e], (&rv[3].x)[e],
+                          (&rv[4].x)[e], (&rv[5].x)[e], (&rv[6].x)[e], (&rv[7].x)[e]};
+      uint4 hi, lo;
+      split8(make_float4(x[0], x[1], x[2], x[3]), make_float4(x[4], x[5], x[6], x[7]), hi, lo);
+      Vt[0][vswz(d4 * 4 + e, kg)] = hi;
+      Vt[1][vswz(d4 * 4 + e, kg)] = lo;
     }
   };
 
@@ -197,14 +216,12 @@ __global__ void __launch_bounds__(NTH) attn_split_kernel(AttnArgs a) {
                ph4, pl4);
         const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, ph4);
         const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, pl4);
-        const int u1 = 8 * b + 4 * hh + g4, u2 = u1 + 2;
+        const int u = 4 * b + 2 * hh + g4;  // the lane's 8 keys of this 16-key step
 #pragma unroll
         for (int nb = 0; nb < HD / 32; ++nb) {
           const int hd = nb * 32 + (lane & 31);
-          const int i1 = hd * 16 + (u1 ^ (hd & 15)), i2 = hd * 16 + (u2 ^ (hd & 15));
-          const uint2 a1 = Vt[0][i1], a2 = Vt[0][i2], b1 = Vt[1][i1], b2 = Vt[1][i2];
-          const bf16x8_t vh = __builtin_bit_cast(bf16x8_t, make_uint4(a1.x, a1.y, a2.x, a2.y));
-          const bf16x8_t vl = __builtin_bit_cast(bf16x8_t, make_uint4(b1.x, b1.y, b2.x, b2.y));
+          const bf16x8_t vh = __builtin_bit_cast(bf16x8_t, Vt[0][vswz(hd, u)]);
+          const bf16x8_t vl = __builtin_bit_cast(bf16x8_t, Vt[1][vswz(hd, u)]);
           oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, ph, oacc[nb], 0, 0, 0);
           oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pl, oacc[nb], 0, 0, 0);
           oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, ph, oacc[nb], 0, 0, 0);

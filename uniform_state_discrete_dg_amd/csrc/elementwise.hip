@@ -269,6 +269,43 @@ hipError_t tile_stats_f32(const float *logits, int M, int V, float inv_T, float 
   return hipGetLastError();
 }
 
+// Reductions over the 256 threads of a row: within each wave by lane
+// exchanges, then across the 4 waves through LDS (two barriers).
+__device__ __forceinline__ float rc_sum(float v, float *sh) {
+  v = warp_sum(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  __syncthreads();
+  return r;
+}
+// max of (value, lowest index on ties)
+__device__ __forceinline__ void rc_argmax(float &v, int &i, float *shv, int *shi) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(v, o);
+    const int i2 = __shfl_xor(i, o);
+    if (v2 > v || (v2 == v && i2 < i)) {
+      v = v2;
+      i = i2;
+    }
+  }
+  if ((threadIdx.x & 63) == 0) {
+    shv[threadIdx.x >> 6] = v;
+    shi[threadIdx.x >> 6] = i;
+  }
+  __syncthreads();
+  v = shv[0];
+  i = shi[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w)
+    if (shv[w] > v || (shv[w] == v && shi[w] < i)) {
+      v = shv[w];
+      i = shi[w];
+    }
+  __syncthreads();
+}
+
 // Entropy of softmax(y) from the tile statistics ([P3] §5.4 measures
 // confidence by the entropy of each position's distribution):
 //   M = max_t m_t, L = sum_t l_t e^{m_t - M},
@@ -289,9 +326,8 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
                                                           float *__restrict__ tile_scale,
                                                           const float *__restrict__ n2, const bf16 *__restrict__ E,
                                                           int d, float2 *__restrict__ top) {
-  __shared__ float sv[256];
-  __shared__ int si[256];
-  __shared__ float sh[256];
+  __shared__ float shv[4];
+  __shared__ int shi[4];
   const int row = blockIdx.x;
   const float4 *st = stats + (int64_t)row * ntiles;
   float best = -INFINITY;
@@ -304,23 +340,9 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
       bidx = idx;
     }
   }
-  sv[threadIdx.x] = best;
-  si[threadIdx.x] = bidx;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) {
-      const float v2 = sv[threadIdx.x + o];
-      const int i2 = si[threadIdx.x + o];
-      if (v2 > sv[threadIdx.x] || (v2 == sv[threadIdx.x] && i2 < si[threadIdx.x])) {
-        sv[threadIdx.x] = v2;
-        si[threadIdx.x] = i2;
-      }
-    }
-    __syncthreads();
-  }
-  const float Mz = sv[0];
-  const int amax = si[0];
-  __syncthreads();
+  rc_argmax(best, bidx, shv, shi);
+  const float Mz = best;
+  const int amax = bidx;
   const float My = Mz * inv_T;
   const int ta = amax / TILE;
   // corrected terms of the argmax token inside its tile (reference m_ta = My)
@@ -330,7 +352,7 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
     float part = 0.f;
     for (int k = threadIdx.x; k < d; k += 256)
       part += n2[(int64_t)row * d + k] * bf16_to_f32(E[(int64_t)amax * d + k]);
-    const float z_exact = block_sum256(part, sh);
+    const float z_exact = rc_sum(part, shv);
     d_top = z_exact * inv_T - My;
     const float e = exp2f(d_top * LOG2E);
     l_fix = e - 1.f;
@@ -349,8 +371,8 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
     L += l * w;
     S += w * (sacc + dd * l);
   }
-  L = block_sum256(L, sh);
-  S = block_sum256(S, sh);
+  L = rc_sum(L, shv);
+  S = rc_sum(S, shv);
   const float invL = 1.f / L;
   for (int t = threadIdx.x; t < ntiles; t += 256) {
     const float dd = st[t].x * inv_T - My;

@@ -33,8 +33,8 @@ __device__ __forceinline__ void epi_store(const Epi &e, int row, int col, float 
 //
 // At a 256-row canvas these contractions are small (M = 256, N and K a few
 // thousand), so the work is cut into 64 x 128 output tiles and, along K,
-// into ranges of 512 (a 256 x 2816 x 2816 product: 88 tiles x 6 ranges =
-// 528 workgroups, two per compute unit).  Each workgroup
+// into ranges of about 704 (a 256 x 2816 x 2816 product: 88 tiles x 4
+// ranges = 352 workgroups).  Each workgroup
 // (4 waves, wave tile 32 rows x 64 columns) streams its A rows (fp32) and
 // B rows (bf16) through a 4-stage LDS ring fed by the DMA form of the
 // vector load, 32 k per slice, three slices ahead of the MFMAs; the split of
@@ -46,7 +46,7 @@ namespace {
 constexpr int PG_NT = 256;
 constexpr int PG_BK = 32;
 // default tile: rows x columns per workgroup, LDS stages
-constexpr int PG_BM = 128, PG_BN = 128, PG_STAGES = 6;
+constexpr int PG_BM = 64, PG_BN = 128, PG_STAGES = 4;
 
 template <int n>
 __device__ __forceinline__ void pg_wait_vmcnt() {
@@ -254,15 +254,16 @@ __global__ void __launch_bounds__(256) gemm_splitk_epilogue_kernel(SplitGemm g) 
   epi_store(e, row, col + 3, v.w);
 }
 
-// The K ranges depend on K alone (16 slices = 512 k each): a row's result
-// then does not depend on how many rows are computed with it, which keeps
-// an incremental prefill bitwise equal to a one-shot one.
+// The K ranges depend on K alone (about 22 slices = 704 k each): a row's
+// result then does not depend on how many rows are computed with it, which
+// keeps an incremental prefill bitwise equal to a one-shot one.
 int gemm_split_plan(int M, int K, const int *N, int count) {
   (void)M;
   (void)N;
   (void)count;
   const int nsl = K / PG_BK;
-  return nsl >= 32 ? (nsl + 15) / 16 : 1;
+  const int ks = (nsl + 11) / 22;
+  return ks > 1 ? ks : 1;
 }
 
 size_t gemm_split_part_bytes(int M, int K, const int *N, int count) {
