@@ -1,11 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the uniform-state denoising step on one MI355X.
 
-A step is one dg_denoise_step over one 256-token canvas (embedding +
+A step is one denoising step over one 256-token canvas (embedding +
 self-conditioning, bidirectional attention over the 2048-token prefix and
 the canvas, tied LM head with the softmax/entropy epilogue, entropy-bounded
-accept and re-noise, stop flags) followed by the host's dg_should_stop
-check, exactly the loop a generator runs.  Inputs are seeded synthetic
+accept and re-noise, stop flags) followed by the adaptive-stop test, run by
+the library's canvas loop (dg_run_canvas), exactly the loop a generator
+runs.  Inputs are seeded synthetic
 weights already resident in HBM before the timed region.
 
 Prints one JSON line.  --gpus above 1 is rejected: this build measures one
@@ -148,25 +149,28 @@ def main() -> int:
     seed = W.canvas_seed(args.config)
     torch.cuda.synchronize()
 
-    stop_at = []
+    # The adaptive stop as configured (all positions below conf_eps, or the
+    # canvas unchanged for stable_n steps): the random-init model echoes its
+    # input through the tied head and stops after a few steps.
+    probe = den.run_canvas_native(seed, 0, c["steps"], c["sched"], c["T0"], c["T1"], c["gamma"], True,
+                                  c["stable_n"])
+    probe_steps, probe_stopped = probe.steps, probe.stop_reason != "budget"
+    torch.cuda.synchronize()
+
+    # Timed: the library's canvas loop (dg_run_canvas) with the per-step stop
+    # test and its status readback kept, but unable to fire (conf_eps = 0,
+    # stability test off), so every step is a full self-conditioned step.
+    den.cfg.conf_eps = 0.0
+    temps = [D.temperature(c["sched"], c["T0"], c["T1"], s % c["steps"], c["steps"]) for s in
+             range(max(args.steps, args.warmup))]
 
     def run(nsteps: int, canvas_id: int):
-        # One canvas, nsteps consecutive denoising steps, each followed by the
-        # host's stop check.  The check's verdict is recorded, not acted on:
-        # the random-init model echoes its input through the tied head and
-        # would stop after a few steps, and the measurement is of the full,
-        # self-conditioned step.
-        den.init_canvas(seed, canvas_id)
-        for s in range(nsteps):
-            den.step(D.temperature(c["sched"], c["T0"], c["T1"], s % c["steps"], c["steps"]),
-                     c["gamma"])
-            stop, _ = den.should_stop(c["stable_n"])
-            if stop and not stop_at:
-                stop_at.append(s + 1)
+        n, stopped = B.dg_run_canvas(den.cfg, den.w.s, den.cache.s, den.canvas.s, seed, canvas_id,
+                                     temps[:nsteps], c["gamma"], True, 0, den.ws)
+        assert n == nsteps and not stopped
 
     run(args.warmup, 0)
     torch.cuda.synchronize()
-    stop_at.clear()
     B.dg_profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -200,7 +204,8 @@ def main() -> int:
                      "bytes_per_launch": lm_head_bytes(c)},
         "selfcond_kernel": {"avg_launch_us": sc_avg_s * 1e6, "launches": sc_n,
                             "achieved_GBps": selfcond_bytes(c) / max(sc_avg_s, 1e-12) / 1e9},
-        "adaptive_stop_would_fire_at_step": stop_at[0] if stop_at else None,
+        "adaptive_stop": {"fires_at_step": probe_steps if probe_stopped else None,
+                          "timed_loop": "stop test run after every step, thresholds set so it cannot fire"},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c, inp)

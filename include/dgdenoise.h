@@ -233,6 +233,24 @@ dg_status dg_denoise_step(const dg_config *cfg, const dg_weights *w, const dg_kv
 dg_status dg_should_stop(const dg_config *cfg, const dg_canvas *canvas, int32_t stable_steps,
                          int32_t *stop_host, dg_step_stats *stats_host, void *stream);
 
+/* The denoising loop of one canvas ([P3] §5.4, the [P5] scheduler): the
+ * canvas is initialised as by dg_canvas_init(seed, canvas_id), then steps
+ * s = 0, 1, ... run as dg_denoise_step at temperature temps[s] (host array
+ * of max_steps values, the caller's schedule) and accept threshold
+ * accept_threshold_nats.  With adaptive_stop != 0 each step is followed by
+ * the dg_should_stop test (stable_steps as there) and the loop ends at the
+ * first step where it holds; that test is the only device-to-host transfer
+ * (a few bytes into pinned host memory the library keeps per host thread).
+ * Writes *steps_run and *stopped (1 if the adaptive stop ended the loop).
+ * Errors as dg_denoise_step, checked before the first launch; max_steps >= 0.
+ * Returns with the stream synchronised when adaptive_stop != 0, otherwise
+ * with the steps enqueued. */
+dg_status dg_run_canvas(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache,
+                        dg_canvas *canvas, uint64_t seed, uint32_t canvas_id, const float *temps,
+                        int32_t max_steps, float accept_threshold_nats, int32_t adaptive_stop,
+                        int32_t stable_steps, void *ws, size_t ws_bytes, void *stream,
+                        int32_t *steps_run, int32_t *stopped);
+
 /* ---- test and measurement exports -------------------------------------------
  * Not part of the generation path; they expose single kernels for parity
  * tests and timing.  Same validation rules as above. */

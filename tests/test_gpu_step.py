@@ -319,3 +319,32 @@ def test_block_diffusion_full_size_short():
         stable = replay_select(den, tokens_in, stable, s, c["gamma"], 0)["stable"]
     den.prefill(den.canvas.tokens.clone())
     assert den.cache.length == 1280
+
+
+@pytest.mark.parametrize("cfg_id,stop", [(2, True), (2, False), (1, True)])
+def test_run_canvas_native_matches_host_loop(cfg_id, stop):
+    """dg_run_canvas (the loop inside the library, one status readback per
+    step) gives the same canvas, step count and stop as the host loop of
+    dg_denoise_step + dg_should_stop, bit for bit."""
+    c = W.config(cfg_id)
+    inp = W.make_inputs(c)
+    den = D.Denoiser(c, inp)
+    seed = W.canvas_seed(cfg_id)
+    steps = min(c["steps"], 12)
+    a = den.run_canvas(seed, 3, steps, c["sched"], c["T0"], c["T1"], c["gamma"], stop, c["stable_n"])
+    ent_a = den.canvas.entropy.clone()
+    b = den.run_canvas_native(seed, 3, steps, c["sched"], c["T0"], c["T1"], c["gamma"], stop,
+                              c["stable_n"])
+    torch.cuda.synchronize()
+    assert (a.steps, a.stop_reason) == (b.steps, b.stop_reason)
+    assert torch.equal(a.tokens, b.tokens)
+    assert torch.equal(ent_a, den.canvas.entropy)
+    assert den.canvas.s.step == b.steps and den.canvas.s.has_prev == (1 if b.steps else 0)
+    # a zero-step call only initialises the canvas
+    n, stopped = B.dg_run_canvas(den.cfg, den.w.s, den.cache.s, den.canvas.s, seed, 4, [], c["gamma"],
+                                 True, 3, den.ws)
+    assert (n, stopped) == (0, False) and den.canvas.s.step == 0
+    with pytest.raises(B.DgError) as e:
+        B.dg_run_canvas(den.cfg, den.w.s, den.cache.s, den.canvas.s, seed, 4, [1.0, float("nan")],
+                        c["gamma"], True, 3, den.ws)
+    assert e.value.status == B.DG_ERR_INVALID_ARG

@@ -76,6 +76,8 @@ SIGNATURES = {
     "dg_denoise_step": (c_i32, [P(dg_config), P(dg_weights), P(dg_kv_cache), P(dg_canvas), c_f32,
                                 c_f32, vp, c_sz, vp]),
     "dg_should_stop": (c_i32, [P(dg_config), P(dg_canvas), c_i32, P(c_i32), P(dg_step_stats), vp]),
+    "dg_run_canvas": (c_i32, [P(dg_config), P(dg_weights), P(dg_kv_cache), P(dg_canvas), c_u64, c_u32,
+                              P(c_f32), c_i32, c_f32, c_i32, c_i32, vp, c_sz, vp, P(c_i32), P(c_i32)]),
     "dg_test_ws_offsets": (c_i32, [P(dg_config), P(dg_ws_offsets)]),
     "dg_test_set_logits_dump": (None, [c_i32]),
     "dg_test_logits_ws_bytes": (c_sz, [P(dg_config)]),
@@ -187,6 +189,20 @@ def dg_should_stop(cfg: dg_config, canvas: dg_canvas, stable_steps: int, stream=
                                                   stable_steps, ctypes.byref(stop),
                                                   ctypes.byref(stats), _stream(stream)))
     return bool(stop.value), stats
+
+
+def dg_run_canvas(cfg: dg_config, w: dg_weights, cache: dg_kv_cache, canvas: dg_canvas, seed: int,
+                  canvas_id: int, temps, accept_threshold_nats: float, adaptive_stop: bool,
+                  stable_steps: int, ws: torch.Tensor, stream=None):
+    """Returns (steps run, whether the adaptive stop ended the loop)."""
+    n = len(temps)
+    arr = (c_f32 * max(n, 1))(*temps)
+    steps, stopped = c_i32(0), c_i32(0)
+    _check("dg_run_canvas", lib().dg_run_canvas(
+        ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), ctypes.byref(canvas), seed, canvas_id,
+        arr, n, accept_threshold_nats, 1 if adaptive_stop else 0, stable_steps, _ptr(ws), ws.numel(),
+        _stream(stream), ctypes.byref(steps), ctypes.byref(stopped)))
+    return int(steps.value), bool(stopped.value)
 
 
 def dg_test_ws_offsets(cfg: dg_config) -> dg_ws_offsets:

@@ -518,6 +518,50 @@ dg_status dg_should_stop(const dg_config *cfg, const dg_canvas *cv, int32_t stab
   return DG_OK;
 }
 
+dg_status dg_run_canvas(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache, dg_canvas *cv,
+                        uint64_t seed, uint32_t canvas_id, const float *temps, int32_t max_steps,
+                        float accept_threshold_nats, int32_t adaptive_stop, int32_t stable_steps, void *ws,
+                        size_t ws_bytes, void *stream, int32_t *steps_run, int32_t *stopped) {
+  dg_status st = check_config(cfg);
+  if (st != DG_OK) return st;
+  if (!weights_ok(cfg, w) || !cache || !cache->k || !cache->v || !canvas_ok(cv) || !steps_run || !stopped)
+    return DG_ERR_INVALID_ARG;
+  if (cache->length < 0 || cache->length > cache->capacity) return DG_ERR_INVALID_ARG;
+  if (max_steps < 0 || (max_steps > 0 && !temps)) return DG_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < max_steps; ++i)
+    if (!(std::isfinite(temps[i]) && temps[i] > 0.f)) return DG_ERR_INVALID_ARG;
+  if (std::isnan(accept_threshold_nats) || accept_threshold_nats < 0.f) return DG_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < layout(cfg, 0, g_logits_dump && cfg->dtype == DG_BF16).total) return DG_ERR_WORKSPACE;
+  // pinned landing area of the status words, one per host thread (kept for the process)
+  thread_local int32_t *pinned = nullptr;
+  if (adaptive_stop && !pinned) {
+    if (hipHostMalloc(reinterpret_cast<void **>(&pinned), DG_STATUS_WORDS * sizeof(int32_t), hipHostMallocDefault) !=
+        hipSuccess) {
+      pinned = nullptr;
+      return DG_ERR_HIP;
+    }
+  }
+  *steps_run = 0;
+  *stopped = 0;
+  st = dg_canvas_init(cfg, cv, seed, canvas_id, stream);
+  if (st != DG_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t i = 0; i < max_steps; ++i) {
+    st = denoise_impl(cfg, w, cache, cv, temps[i], accept_threshold_nats, ws, ws_bytes, stream, g_logits_dump);
+    if (st != DG_OK) return st;
+    *steps_run = i + 1;
+    if (adaptive_stop) {
+      DG_TRY(hipMemcpyAsync(pinned, cv->status, DG_STATUS_WORDS * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+      DG_TRY(hipStreamSynchronize(s));
+      if (pinned[DG_ST_ALLCONF] || (stable_steps > 0 && pinned[DG_ST_STABLE] >= stable_steps)) {
+        *stopped = 1;
+        break;
+      }
+    }
+  }
+  return DG_OK;
+}
+
 // ---- test and measurement exports --------------------------------------------
 dg_status dg_test_ws_offsets(const dg_config *cfg, dg_ws_offsets *out) {
   dg_status st = check_config(cfg);

@@ -320,6 +320,11 @@ __device__ __forceinline__ void rc_argmax(float &v, int &i, float *shv, int *shi
 // dominant token carries most of the entropy's sensitivity to logit error.
 // The exact probability of a is kept in top[row] = (a, p_a) for the next
 // step's self-conditioning.  The argmax itself stays the LM head's.
+// RC_CACHE tiles per thread are held in registers (one read of the row's
+// statistics) when ntiles <= 256 * RC_CACHE; otherwise the passes re-read.
+constexpr int RC_CACHE = 16;
+
+template <bool CACHED>
 __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restrict__ stats, int ntiles,
                                                           float inv_T, float *__restrict__ entropy,
                                                           int32_t *__restrict__ argmax,
@@ -330,10 +335,23 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
   __shared__ int shi[4];
   const int row = blockIdx.x;
   const float4 *st = stats + (int64_t)row * ntiles;
+  float4 c[CACHED ? RC_CACHE : 1];
+  auto tile = [&](int i, int t) -> float4 { return CACHED ? c[i] : st[t]; };
+  if (CACHED) {
+#pragma unroll
+    for (int i = 0; i < RC_CACHE; ++i) {
+      const int t = threadIdx.x + 256 * i;
+      c[i] = t < ntiles ? st[t] : make_float4(-INFINITY, 0.f, 0.f, __int_as_float(INT32_MAX));
+    }
+  }
+  const int nper = CACHED ? RC_CACHE : (ntiles + 255) / 256;
   float best = -INFINITY;
   int bidx = INT32_MAX;
-  for (int t = threadIdx.x; t < ntiles; t += 256) {
-    const float4 v = st[t];
+#pragma unroll
+  for (int i = 0; i < nper; ++i) {
+    const int t = threadIdx.x + 256 * i;
+    if (t >= ntiles) break;
+    const float4 v = tile(i, t);
     const int idx = __float_as_int(v.w);
     if (v.x > best || (v.x == best && idx < bidx)) {
       best = v.x;
@@ -359,8 +377,11 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
     s_fix = e * d_top;
   }
   float L = 0.f, S = 0.f;
-  for (int t = threadIdx.x; t < ntiles; t += 256) {
-    const float4 v = st[t];
+#pragma unroll
+  for (int i = 0; i < nper; ++i) {
+    const int t = threadIdx.x + 256 * i;
+    if (t >= ntiles) break;
+    const float4 v = tile(i, t);
     const float dd = v.x * inv_T - My;
     const float w = exp2f(dd * LOG2E);
     float l = v.y, sacc = v.z;
@@ -374,8 +395,11 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
   L = rc_sum(L, shv);
   S = rc_sum(S, shv);
   const float invL = 1.f / L;
-  for (int t = threadIdx.x; t < ntiles; t += 256) {
-    const float dd = st[t].x * inv_T - My;
+#pragma unroll
+  for (int i = 0; i < nper; ++i) {
+    const int t = threadIdx.x + 256 * i;
+    if (t >= ntiles) break;
+    const float dd = tile(i, t).x * inv_T - My;
     tile_scale[(int64_t)row * ntiles + t] = exp2f(dd * LOG2E) * invL;
   }
   if (threadIdx.x == 0) {
@@ -390,8 +414,12 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
 hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,
                        int32_t *argmax, float *tile_scale, const float *n2, const uint16_t *E, int d,
                        float2 *top, hipStream_t s) {
-  hipLaunchKernelGGL(row_combine_kernel, dim3(M), dim3(256), 0, s, tile_stats, ntiles, inv_T, entropy,
-                     argmax, tile_scale, n2, E, d, top);
+  if (ntiles <= 256 * RC_CACHE)
+    hipLaunchKernelGGL(row_combine_kernel<true>, dim3(M), dim3(256), 0, s, tile_stats, ntiles, inv_T, entropy,
+                       argmax, tile_scale, n2, E, d, top);
+  else
+    hipLaunchKernelGGL(row_combine_kernel<false>, dim3(M), dim3(256), 0, s, tile_stats, ntiles, inv_T, entropy,
+                       argmax, tile_scale, n2, E, d, top);
   return hipGetLastError();
 }
 

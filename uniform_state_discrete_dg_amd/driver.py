@@ -92,6 +92,18 @@ class Denoiser:
                     break
         return CanvasResult(self.canvas.tokens.clone(), n, reason, stats)
 
+    def run_canvas_native(self, seed: int, canvas_id: int, steps: int, sched: str, T0: float,
+                          T1: float, gamma: float, stop: bool, stable_n: int) -> CanvasResult:
+        """The same loop inside the library (dg_run_canvas): one call, one
+        status readback per step when the adaptive stop is on."""
+        temps = [temperature(sched, T0, T1, s, steps) for s in range(steps)]
+        n, stopped = B.dg_run_canvas(self.cfg, self.w.s, self.cache.s, self.canvas.s, seed, canvas_id,
+                                     temps, gamma, stop, stable_n, self.ws)
+        reason = "budget"
+        if stopped:
+            reason = "confident" if int(self.canvas.status[B.DG_ST_ALLCONF]) else "stable"
+        return CanvasResult(self.canvas.tokens.clone(), n, reason, [])
+
     def block_diffusion(self, prompt: torch.Tensor, canvases: int, seed: int, steps: int,
                         sched: str, T0: float, T1: float, gamma: float, stop: bool,
                         stable_n: int) -> list[CanvasResult]:
