@@ -113,6 +113,32 @@ def cpu_baseline(c: dict, inp: dict, rows=(2, 6)) -> dict:
                        f"{N} rows (s/step = {t_step:.2f})")}
 
 
+def block_diffusion(cfg_id: int = 5) -> dict:
+    """Finished tokens per second of block diffusion: the prompt prefilled
+    causally, then canvases denoised one after another (adaptive stop as
+    configured) and each appended to the cache; wall time includes every
+    prefill and the per-step stop tests."""
+    import torch
+
+    from uniform_state_discrete_dg_amd import driver as D
+    from uniform_state_discrete_dg_amd import workloads as W
+    c = W.config(cfg_id)
+    inp = W.make_inputs(c)
+    den = D.Denoiser(c, inp, capacity=c["cap"], max_prefill=max(c["prompt"], c["N"]))
+    prompt = inp["prompt"].cuda()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res = den.block_diffusion(prompt, c["canvases"], W.canvas_seed(cfg_id), c["steps"], c["sched"], c["T0"],
+                              c["T1"], c["gamma"], c["stop"], c["stable_n"])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    n_tok = c["canvases"] * c["N"]
+    return {"workload": c["name"], "finished_tokens_per_s": n_tok / dt, "wall_ms": dt * 1e3,
+            "canvases": c["canvases"], "steps_per_canvas": [r.steps for r in res],
+            "stop_reasons": sorted(set(r.stop_reason for r in res)), "prompt_tokens": c["prompt"],
+            "cache_tokens_at_end": den.cache.length}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +146,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload table entry (3: N256 V262144)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block-diffusion", action="store_true",
+                    help="skip the block-diffusion run (prompt prefill + chained canvases)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run the library's plain copy kernel over 1 GiB three times "
                          "(reference for memory-traffic counters)")
@@ -207,6 +235,10 @@ def main() -> int:
         "adaptive_stop": {"fires_at_step": probe_steps if probe_stopped else None,
                           "timed_loop": "stop test run after every step, thresholds set so it cannot fire"},
     }
+    if not args.no_block_diffusion:
+        del den
+        torch.cuda.empty_cache()
+        out["block_diffusion"] = block_diffusion()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c, inp)
     print(json.dumps(out), flush=True)

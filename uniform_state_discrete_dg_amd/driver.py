@@ -113,7 +113,7 @@ class Denoiser:
             self.prefill(prompt)
         out = []
         for b in range(canvases):
-            r = self.run_canvas(seed, b, steps, sched, T0, T1, gamma, stop, stable_n)
+            r = self.run_canvas_native(seed, b, steps, sched, T0, T1, gamma, stop, stable_n)
             self.prefill(self.canvas.tokens)
             out.append(r)
         return out
