@@ -173,37 +173,51 @@ __global__ void __launch_bounds__(NTH) attn_split_kernel(AttnArgs a) {
         sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[s], sacc[b], 0, 0, 0);
       }
     }
-    // mask, scale, running max
+    // mask (only a partial tile or causal mode needs it), scale, running max
     float tmax = -INFINITY;
+    if (kt0 + KT > kend || a.causal) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kabs = kt0 + b * 32 + (r & 3) + 4 * g4 + 8 * (r >> 2);
-        float v = sacc[b][r] * sc;
-        if (kabs >= kend || kabs > qlimit) v = -INFINITY;
-        sacc[b][r] = v;
-        tmax = fmaxf(tmax, v);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int kabs = kt0 + b * 32 + (r & 3) + 4 * g4 + 8 * (r >> 2);
+          float v = sacc[b][r] * sc;
+          if (kabs >= kend || kabs > qlimit) v = -INFINITY;
+          sacc[b][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+    } else {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sacc[b][r] *= sc;
+          tmax = fmaxf(tmax, sacc[b][r]);
+        }
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    // with m_new = -inf every score is -inf and exp2(-inf - 0) = 0
+    const float msub = (m_new == -INFINITY) ? 0.f : m_new;
     float psum = 0.f;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = (m_new == -INFINITY) ? 0.f : exp2f(sacc[b][r] - m_new);
+        const float p = exp2f(sacc[b][r] - msub);
         sacc[b][r] = p;
         psum += p;
       }
     psum += __shfl_xor(psum, 32);
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    if (__any(alpha != 1.f)) {  // the running max moved for some query of the wave
 #pragma unroll
-    for (int nb = 0; nb < HD / 32; ++nb)
+      for (int nb = 0; nb < HD / 32; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
+    }
 
     // O^T += V^T P^T over the four 16-key steps of the tile (3 products each).
 #pragma unroll
