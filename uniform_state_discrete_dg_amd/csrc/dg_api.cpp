@@ -218,6 +218,35 @@ hipError_t proj1(const dg_config *c, const float *A, int64_t lda, int M, int K, 
   return proj(c, A, lda, M, K, 1, &W, &Nout, &e, part, s);
 }
 
+// proj1 whose output rows (fp32 [M][Nout], row-major) then go through
+// RMSNorm(gain) into norm_out (fp32) and/or norm_tiled (bf16 tiled): for the
+// bf16 path with a K split the norm is fused into the split-K merge.
+hipError_t proj1_norm(const dg_config *c, const float *A, int64_t lda, int M, int K, const void *W, int Nout,
+                      const dg::Epi &e, float *part, const void *gain, float *norm_out, bf16 *norm_tiled,
+                      hipStream_t s) {
+  if (c->dtype == DG_BF16 && dg::gemm_split_plan(M, K, &Nout, 1) > 1) {
+    dg::SplitGemm g{};
+    g.A = A;
+    g.lda = lda;
+    g.M = M;
+    g.K = K;
+    g.count = 1;
+    g.B[0] = W;
+    g.N[0] = Nout;
+    g.e[0] = e;
+    g.part = part;
+    g.ksplit = dg::gemm_split_plan(M, K, &Nout, 1);
+    const dg::RowNorm rn{static_cast<const uint16_t *>(gain), c->rms_eps, norm_out, norm_tiled};
+    return dg::gemm_split_norm(g, rn, s);
+  }
+  hipError_t err = proj1(c, A, lda, M, K, W, Nout, e, part, s);
+  if (err != hipSuccess) return err;
+  const float *y = static_cast<const float *>(e.out);
+  if (c->dtype == DG_BF16)
+    return dg::rmsnorm_rows<bf16>(y, static_cast<const bf16 *>(gain), M, Nout, c->rms_eps, norm_out, norm_tiled, s);
+  return dg::rmsnorm_rows<float>(y, static_cast<const float *>(gain), M, Nout, c->rms_eps, norm_out, norm_tiled, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -415,13 +444,16 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     dg::Epi ea = epi_store(h0, true, d, d, 0);
     ea.kind = dg::EPI_ADD;
     ea.resid = h0;
-    DG_TRY(proj1(cfg, G, F, N, F, w->w_sc2, d, ea, gpart, s));
+    // h0 += W2 G, then 2. the pre-attention RMSNorm of h0 (fused when the GEMM splits K)
+    DG_TRY(proj1_norm(cfg, G, F, N, F, w->w_sc2, d, ea, gpart, w->g_attn, nrm, nullptr, s));
+  } else {
+    // 2. RMSNorm of the embeddings (no self-conditioning at a canvas's first step)
+    if (bf)
+      DG_TRY(dg::rmsnorm_rows<bf16>(h0, static_cast<const bf16 *>(w->g_attn), N, d, cfg->rms_eps, nrm, nullptr, s));
+    else
+      DG_TRY(dg::rmsnorm_rows<float>(h0, static_cast<const float *>(w->g_attn), N, d, cfg->rms_eps, nrm, nullptr, s));
   }
-  // 2. RMSNorm, Q/K/V of the canvas (the canvas keys stay in the workspace)
-  if (bf)
-    DG_TRY(dg::rmsnorm_rows<bf16>(h0, static_cast<const bf16 *>(w->g_attn), N, d, cfg->rms_eps, nrm, nullptr, s));
-  else
-    DG_TRY(dg::rmsnorm_rows<float>(h0, static_cast<const float *>(w->g_attn), N, d, cfg->rms_eps, nrm, nullptr, s));
+  // Q/K/V of the canvas (the canvas keys stay in the workspace)
   {
     const void *W[3] = {w->wq, w->wk, w->wv};
     const int No[3] = {Hq * hd, Hkv * hd, Hkv * hd};
@@ -455,12 +487,13 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     dg::Epi ea = epi_store(h1, true, d, d, 0);
     ea.kind = dg::EPI_ADD;
     ea.resid = h0;
-    DG_TRY(proj1(cfg, o, Hq * hd, N, Hq * hd, w->wo, d, ea, gpart, s));
+    // h1 = h0 + O Wo^T, then 4. the final RMSNorm (fp32 for the exact top logit,
+    // tiled bf16 for the LM head; fused when the GEMM splits K)
+    DG_TRY(proj1_norm(cfg, o, Hq * hd, N, Hq * hd, w->wo, d, ea, gpart, w->g_final, nrm, bf ? nrm16 : nullptr, s));
   }
-  // 4. final RMSNorm, tied LM head with the softmax/entropy statistics
+  // tied LM head with the softmax/entropy statistics
   float *logits = reinterpret_cast<float *>(base + L.logits);
   if (bf) {
-    DG_TRY(dg::rmsnorm_rows<bf16>(h1, static_cast<const bf16 *>(w->g_final), N, d, cfg->rms_eps, nrm, nrm16, s));
     {
       ProfScope ps(g_prof_lm, s);
       DG_TRY(dg::lm_head_bf16(nrm16, N, d, static_cast<const uint16_t *>(w->E_pack), V, inv_T,
@@ -470,7 +503,6 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
                            static_cast<const uint16_t *>(w->E), d, top, s));
     DG_TRY(dg::normalize_probs_bf16(static_cast<uint16_t *>(cv->probs), tscale, N, V, s));
   } else {
-    DG_TRY(dg::rmsnorm_rows<float>(h1, static_cast<const float *>(w->g_final), N, d, cfg->rms_eps, nrm, nullptr, s));
     dg::GemmShapeF32 g{nrm, d, 1, static_cast<const float *>(w->E), d, 1, N, V, d, nullptr, 0};
     DG_TRY(dg::gemm_f32(g, epi_store(logits, true, V, V, 0), s));
     DG_TRY(dg::tile_stats_f32(logits, N, V, inv_T, static_cast<float *>(cv->probs), tstats, s));

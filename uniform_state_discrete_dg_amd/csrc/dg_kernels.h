@@ -54,6 +54,18 @@ int gemm_split_plan(int M, int K, const int *N, int count);
 // Bytes of partials gemm_split needs for that plan (0 when ksplit == 1).
 size_t gemm_split_part_bytes(int M, int K, const int *N, int count);
 hipError_t gemm_split(const SplitGemm &g, hipStream_t s);
+// RMSNorm of a projection's output rows, fused into its split-K merge:
+// y = epilogue(sum of partials) (EPI_STORE or EPI_ADD, fp32, row-major),
+// then out = y / sqrt(mean(y^2) + eps) * gain (fp32 [M][N], nullable) and
+// out_tiled (bf16 tiled block(s), rows past M zero; nullable).  One
+// segment; with ksplit == 1 it runs the GEMM and a separate RMSNorm.
+struct RowNorm {
+  const uint16_t *gain;  // bf16 [N]
+  float eps;
+  float *out;
+  uint16_t *out_tiled;
+};
+hipError_t gemm_split_norm(const SplitGemm &g, const RowNorm &rn, hipStream_t s);
 // Canvas rows per workgroup of the two table-streaming kernels (128 or 256).
 int estream_bm(int M);
 // The self-conditioning contraction: A = probs (tiled bf16 probabilities),

@@ -7,6 +7,7 @@
 // All operands are K-contiguous ("NT"): A[M][K] and B[N][K].
 #include "dg_device.h"
 #include "dg_kernels.h"
+#include "dg_tiled.h"
 
 namespace dg {
 
@@ -254,6 +255,68 @@ __global__ void __launch_bounds__(256) gemm_splitk_epilogue_kernel(SplitGemm g) 
   epi_store(e, row, col + 3, v.w);
 }
 
+// Split-K merge + epilogue + RMSNorm, one workgroup per output row: the row
+// (N <= 4096 columns, 4 per thread per pass) stays in registers between the
+// sum of squares and the normalised store.
+constexpr int RN_MAXQ = 4;  // float4 per thread: N <= 256 * 4 * RN_MAXQ
+__global__ void __launch_bounds__(256) gemm_splitk_norm_kernel(SplitGemm g, RowNorm rn) {
+  __shared__ float sh[4];
+  const int row = blockIdx.x, M = g.M, N = g.N[0];
+  if (row >= M) {  // padding rows of the tiled output block
+    for (int c = threadIdx.x; c < N; c += 256) rn.out_tiled[tl_index(row, c, N)] = 0;
+    return;
+  }
+  const Epi e = g.e[0];
+  const int64_t stride = (int64_t)M * N;
+  const float *p0 = g.part + (int64_t)row * N;
+  float4 y[RN_MAXQ];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < RN_MAXQ; ++k) {
+    const int c = (threadIdx.x + 256 * k) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < N) {
+      v = *reinterpret_cast<const float4 *>(p0 + c);
+      for (int z = 1; z < g.ksplit; ++z) {
+        const float4 w = *reinterpret_cast<const float4 *>(p0 + z * stride + c);
+        v.x += w.x;
+        v.y += w.y;
+        v.z += w.z;
+        v.w += w.w;
+      }
+      float *o = static_cast<float *>(e.out) + (int64_t)row * e.rstride + c;
+      if (e.kind == EPI_ADD) {
+        const float4 r = *reinterpret_cast<const float4 *>(e.resid + (int64_t)row * e.rstride + c);
+        v.x += r.x;
+        v.y += r.y;
+        v.z += r.z;
+        v.w += r.w;
+      }
+      *reinterpret_cast<float4 *>(o) = v;
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    y[k] = v;
+  }
+  ss = warp_sum(ss);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  ss = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  const float inv = rsqrtf(ss / (float)N + rn.eps);
+#pragma unroll
+  for (int k = 0; k < RN_MAXQ; ++k) {
+    const int c = (threadIdx.x + 256 * k) * 4;
+    if (c >= N) continue;
+    const float q[4] = {y[k].x * inv * bf16_to_f32(rn.gain[c]), y[k].y * inv * bf16_to_f32(rn.gain[c + 1]),
+                        y[k].z * inv * bf16_to_f32(rn.gain[c + 2]), y[k].w * inv * bf16_to_f32(rn.gain[c + 3])};
+    if (rn.out) *reinterpret_cast<float4 *>(rn.out + (int64_t)row * N + c) = make_float4(q[0], q[1], q[2], q[3]);
+    if (rn.out_tiled) {
+      // four consecutive columns of one 8-column chunk: one 8-byte store
+      *reinterpret_cast<uint2 *>(rn.out_tiled + tl_index(row, c, N)) =
+          make_uint2(pack_bf16x2(q[0], q[1]), pack_bf16x2(q[2], q[3]));
+    }
+  }
+}
+
 // The K ranges depend on K alone (about 22 slices = 704 k each): a row's
 // result then does not depend on how many rows are computed with it, which
 // keeps an incremental prefill bitwise equal to a one-shot one.
@@ -275,7 +338,7 @@ size_t gemm_split_part_bytes(int M, int K, const int *N, int count) {
 }
 
 template <int BM, int BN, int STAGES>
-hipError_t gemm_split_launch(const SplitGemm &g, hipStream_t s) {
+hipError_t gemm_split_launch(const SplitGemm &g, hipStream_t s, bool partials_only = false) {
   using C = PgCfg<BM, BN, STAGES>;
   if (g.ksplit < 1 || (g.ksplit > 1 && !g.part) || g.K % PG_BK) return hipErrorInvalidValue;
   for (int i = 0; i < g.count; ++i)
@@ -296,13 +359,30 @@ hipError_t gemm_split_launch(const SplitGemm &g, hipStream_t s) {
   const int grid = 8 * ((P + 7) / 8) * per;  // XCD 0 serves the most column tiles
   hipLaunchKernelGGL((gemm_split_kernel<BM, BN, STAGES>), dim3(grid), dim3(PG_NT), C::LDS, s, g);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || g.ksplit == 1) return err;
+  if (err != hipSuccess || g.ksplit == 1 || partials_only) return err;
   const int64_t quads = (int64_t)g.M * maxN / 4;
   hipLaunchKernelGGL(gemm_splitk_epilogue_kernel, dim3((unsigned)((quads + 255) / 256), g.count), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
 hipError_t gemm_split(const SplitGemm &g, hipStream_t s) { return gemm_split_launch<PG_BM, PG_BN, PG_STAGES>(g, s); }
+
+static hipError_t gemm_split_kernel_launch(const SplitGemm &g, hipStream_t s) {
+  return gemm_split_launch<PG_BM, PG_BN, PG_STAGES>(g, s, true);
+}
+
+hipError_t gemm_split_norm(const SplitGemm &g, const RowNorm &rn, hipStream_t s) {
+  const Epi &e = g.e[0];
+  if (g.count != 1 || g.ksplit < 2 || !g.part || !e.out_f32 || e.cdiv < g.N[0] || g.N[0] % 4 ||
+      g.N[0] > 256 * 4 * RN_MAXQ || (e.kind != EPI_STORE && e.kind != EPI_ADD) || e.rstride % 4 ||
+      (rn.out_tiled && g.N[0] % TL_K))
+    return hipErrorInvalidValue;
+  hipError_t err = gemm_split_kernel_launch(g, s);  // partials only; the merge applies the epilogue
+  if (err != hipSuccess) return err;
+  const int rows = rn.out_tiled ? (g.M + TL_ROWS - 1) / TL_ROWS * TL_ROWS : g.M;
+  hipLaunchKernelGGL(gemm_splitk_norm_kernel, dim3(rows), dim3(256), 0, s, g, rn);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
 // fp32 SIMT GEMM (the fp32 configuration): 16x16 outputs per workgroup,
