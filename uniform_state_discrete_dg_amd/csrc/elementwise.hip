@@ -92,25 +92,38 @@ template hipError_t rmsnorm_rows<bf16>(const float *, const bf16 *, int, int, fl
 __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int ksplit, int N, int d,
                                        const float2 *__restrict__ top, const bf16 *__restrict__ probs, int V,
                                        const bf16 *__restrict__ E, float *__restrict__ out) {
+  // one thread per 4 consecutive columns of one row; d % 4 == 0
   const int row = blockIdx.y;
-  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  const int k = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (k >= d) return;
   const int64_t i = (int64_t)row * d + k;
   const int64_t count = (int64_t)N * d;
-  float acc = 0.f;
-  for (int z = 0; z < ksplit; ++z) acc += part[(int64_t)z * count + i];
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int z = 0; z < ksplit; ++z) {
+    const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)z * count + i);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
   if (top) {
     const float2 tp = top[row];
     const int a = __float_as_int(tp.x);
-    const float used = bf16_to_f32(probs[tl_index(row, a, V)]);
-    acc += (tp.y - used) * bf16_to_f32(E[(int64_t)a * d + k]);
+    const float c = tp.y - bf16_to_f32(probs[tl_index(row, a, V)]);
+    const bf16 *e = E + (int64_t)a * d + k;
+    acc.x += c * bf16_to_f32(e[0]);
+    acc.y += c * bf16_to_f32(e[1]);
+    acc.z += c * bf16_to_f32(e[2]);
+    acc.w += c * bf16_to_f32(e[3]);
   }
-  out[i] = acc;
+  *reinterpret_cast<float4 *>(out + i) = acc;
 }
 
 hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top, const uint16_t *probs,
                            int V, const uint16_t *E, float *out, hipStream_t s) {
-  hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((d + 255) / 256, N), dim3(256), 0, s, part, ksplit, N, d,
+  if (d % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((d / 4 + 255) / 256, N), dim3(256), 0, s, part, ksplit, N, d,
                      top, probs, V, E, out);
   return hipGetLastError();
 }
