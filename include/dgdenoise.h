@@ -107,13 +107,17 @@ typedef struct {
  *   tokens  int32 [N]            current canvas
  *   probs   bytes dg_probs_bytes(): softmax probabilities of the last step,
  *                                the self-conditioning input of the next.
- *                                DG_F32: float [N][V].  DG_BF16: bf16 in
- *                                the tiled layout (rounded to nearest even;
- *                                the dominant token's exact value is kept
- *                                in stats)
+ *                                DG_F32: float [N][V].  DG_BF16: bf16
+ *                                numerators in the tiled layout, each
+ *                                relative to a power-of-two reference of
+ *                                its (row, 64-column tile); the probability
+ *                                is the stored value times the tile's
+ *                                factor kept in stats (the dominant token's
+ *                                exact probability is kept there too)
  *   stats   bytes dg_stats_bytes(): per-(row, tile) softmax statistics,
- *                                normalisers and each row's dominant token
- *                                with its exact probability; opaque
+ *                                factors and exponents, per-row factors
+ *                                and each row's dominant token with its
+ *                                exact probability; opaque
  *   entropy float [N]            nats, clamped >= +0 (NaN propagates)
  *   argmax  int32 [N]            highest logit, lowest index on ties
  *   accept  uint8 [N]            1 = accepted in the last step

@@ -55,7 +55,11 @@ def test_shipped_configs_supported(lib, i):
     assert B.dg_validate_config(cfg) == B.DG_OK
     assert B.dg_workspace_bytes(cfg, 0) > 0
     assert B.dg_workspace_bytes(cfg, 1024) >= B.dg_workspace_bytes(cfg, 0)
-    assert B.dg_stats_bytes(cfg) == cfg.canvas_len * ((cfg.vocab // 64) * 20 + 8)
+    # float4 tile stats + float tile scale per (row, tile), float2 top and float
+    # row scale per row, then (256-byte aligned) a uint8 exponent per (tile, 256 rows)
+    nt = cfg.vocab // 64
+    head = cfg.canvas_len * (nt * 20 + 8 + 4)
+    assert B.dg_stats_bytes(cfg) == (head + 255) // 256 * 256 + nt * 256
 
 
 @pytest.mark.parametrize("kw,st", [

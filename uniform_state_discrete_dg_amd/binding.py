@@ -347,15 +347,17 @@ class DeviceCanvas:
                            self.accept.data_ptr(), self.status.data_ptr(), 0, 0, 0, 0)
 
     def probabilities(self, cfg: dg_config) -> torch.Tensor:
-        """The last step's probabilities as [N][V] (bf16 or f32, row-major)."""
+        """The last step's probabilities as float32 [N][V] (row-major).  The
+        bf16 path keeps numerators; p = stored value x tile_scale."""
         N, V = cfg.canvas_len, cfg.vocab
         if cfg.dtype == DG_BF16:
-            return tiled_to_rows(self.probs.view(torch.bfloat16), N, V)
+            num = tiled_to_rows(self.probs.view(torch.bfloat16), N, V).float()
+            return (num.view(N, V // TILE_V, TILE_V) * self.tile_scale(cfg).unsqueeze(-1)).view(N, V)
         return self.probs.view(torch.float32).view(N, V)
 
     def tile_scale(self, cfg: dg_config) -> torch.Tensor:
-        """Per-(row, tile) normalisers of the last step ([N][V/64] f32): the
-        factors that turned the tile-local numerators into probabilities."""
+        """Per-(row, tile) factors of the last step ([N][V/64] f32) that turn
+        the stored numerators into probabilities."""
         N, nt = cfg.canvas_len, cfg.vocab // TILE_V
         return self.stats[N * nt * 16:N * nt * 20].view(torch.float32).view(N, nt)
 

@@ -269,7 +269,8 @@ __global__ void __launch_bounds__(NTH) attn_split_kernel(AttnArgs a) {
 // Merge of the split-KV partial results (both dtypes).
 template <typename T>
 __global__ void attn_combine_kernel(const float *__restrict__ part_o, const float *__restrict__ part_ml,
-                                    int splits, int nq, int Hq, int hd, T *__restrict__ out) {
+                                    int splits, int nq, int Hq, int hd, T *__restrict__ out,
+                                    bf16 *__restrict__ out_split) {
   const int qh = blockIdx.x;
   const int q = qh / Hq, h = qh % Hq;
   const int e = threadIdx.x;
@@ -283,7 +284,16 @@ __global__ void attn_combine_kernel(const float *__restrict__ part_o, const floa
     den += w * l;
     if (e < hd) num += w * part_o[(((int64_t)z * Hq + h) * nq + q) * hd + e];
   }
-  if (e < hd) Elem<T>::store(out, (int64_t)q * Hq * hd + (int64_t)h * hd + e, num / den);
+  if (e < hd) {
+    const int64_t i = (int64_t)q * Hq * hd + (int64_t)h * hd + e;
+    const float v = num / den;
+    Elem<T>::store(out, i, v);
+    if (out_split) {  // the output projection's operand: hi + lo terms
+      const bf16 hi = f32_to_bf16(v);
+      out_split[i] = hi;
+      out_split[(int64_t)nq * Hq * hd + i] = f32_to_bf16(v - bf16_to_f32(hi));
+    }
+  }
 }
 
 void attention_plan(int nq, int Hq, int nk, int *splits, int *keys_per_split) {
@@ -306,7 +316,7 @@ hipError_t attention_mfma(const AttnArgs &a, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(attn_combine_kernel<float>, dim3(a.nq * a.Hq), dim3(HD), 0, s, a.part_o,
-                     a.part_ml, a.splits, a.nq, a.Hq, HD, static_cast<float *>(a.out));
+                     a.part_ml, a.splits, a.nq, a.Hq, HD, static_cast<float *>(a.out), a.out_split);
   return hipGetLastError();
 }
 

@@ -66,15 +66,35 @@ int selfcond_ksplit(const dg_config *c) {
   return ks;
 }
 
+// The canvas `stats` buffer: float4 tile statistics [N][V/64], float
+// tile_scale [N][V/64], float2 top [N], float row_scale [N], then (256-byte
+// aligned) the uint8 tile exponents [V/64][256].
+struct StatsLayout {
+  size_t tstats, tscale, top, rscale, shift, total;
+};
+StatsLayout stats_layout(const dg_config *c) {
+  StatsLayout S{};
+  const size_t N = c->canvas_len, nt = (size_t)c->vocab / kTile;
+  S.tstats = 0;
+  S.tscale = N * nt * sizeof(float4);
+  S.top = S.tscale + N * nt * sizeof(float);
+  S.rscale = S.top + N * sizeof(float2);
+  S.shift = align256(S.rscale + N * sizeof(float));
+  S.total = S.shift + nt * 256;
+  return S;
+}
+
 struct Layout {
-  size_t h0, h1, nrm, nrm16, sc, g, q, kc, vc, o, ap_o, ap_ml, sc_part, gpart, logits, total;
+  size_t h0, h1, nrm, nrm16, nrm_s, sc, sc_s, g, q, kc, vc, o, o_s, ap_o, ap_ml, sc_part, gpart, logits, total;
   // prefill view (same region)
   size_t p_x, p_nrm, p_q, p_ap_o, p_ap_ml, p_gpart, p_total;
 };
 
-// Activations are fp32 in the workspace for both dtypes (the bf16 path
-// feeds them to the matrix cores as split bf16 pairs); nrm16 is the bf16
-// copy of the final normalised state used by the LM head.
+// Activations are fp32 in the workspace for both dtypes; the bf16 path also
+// keeps each projection operand as a split pair (hi and lo bf16 terms, the
+// lo array after the hi array, 4 bytes per value: nrm_s, sc_s, o_s, and g,
+// which holds only that form there); nrm16 is the bf16 copy of the final
+// normalised state used by the LM head.
 Layout layout(const dg_config *c, int32_t nprefill, bool with_logits) {
   Layout L{};
   const size_t N = c->canvas_len, V = c->vocab, d = c->d_model, F = c->ffn_hidden;
@@ -90,12 +110,15 @@ Layout layout(const dg_config *c, int32_t nprefill, bool with_logits) {
   L.h1 = take(N * d * 4);
   L.nrm = take(N * d * 4);
   L.nrm16 = take(bf ? dg::tl_elems((int)N, (int)d) * 2 : 0);
+  L.nrm_s = take(bf ? N * d * 4 : 0);
   L.sc = take(N * d * 4);
+  L.sc_s = take(bf ? N * d * 4 : 0);
   L.g = take(N * F * 4);
   L.q = take(Hq * N * hd * 4);
   L.kc = take(Hkv * N * hd * 4);
   L.vc = take(Hkv * N * hd * 4);
   L.o = take(N * Hq * hd * 4);
+  L.o_s = take(bf ? N * Hq * hd * 4 : 0);
   int splits = 1, kps = 0;
   // the plan for any key count never uses more splits than for 2^20 keys
   dg::attention_plan((int)N, (int)Hq, 1 << 20, &splits, &kps);
@@ -117,7 +140,7 @@ Layout layout(const dg_config *c, int32_t nprefill, bool with_logits) {
   off = 0;
   const size_t n = nprefill > 0 ? (size_t)nprefill : 0;
   L.p_x = take(n * d * 4);
-  L.p_nrm = take(n * d * 4);
+  L.p_nrm = take(n * d * 4);  // fp32, or the split pair of the bf16 path
   L.p_q = take(Hq * n * hd * 4);
   dg::attention_plan((int)(n ? n : 1), (int)Hq, 1 << 20, &splits, &kps);
   L.p_ap_o = take((size_t)splits * Hq * n * hd * 4);
@@ -184,17 +207,25 @@ bool canvas_ok(const dg_canvas *cv) {
   return cv && cv->tokens && cv->probs && cv->stats && cv->entropy && cv->argmax && cv->accept && cv->status;
 }
 
-// Dense projections C_i[M][N_i] = A[M][K] W_i[N_i][K]^T (fp32 activation A,
-// up to three weight matrices sharing it) with epilogues e_i.
-// `part` holds the K-split partials (gemm_split_part_bytes; bf16 only).
-hipError_t proj(const dg_config *c, const float *A, int64_t lda, int M, int K, int count, const void *const *W,
-                const int *Nout, const dg::Epi *e, float *part, hipStream_t s) {
+// Dense projections C_i[M][N_i] = A[M][K] W_i[N_i][K]^T (up to three weight
+// matrices sharing the activation A) with epilogues e_i.  A is dense
+// [M][K]: fp32 for DG_F32; for DG_BF16 the split pair (bf16 hi terms
+// [M][K], then the lo terms [M][K]).  `part` holds the K-split partials
+// (gemm_split_part_bytes; bf16 only).
+dg::SplitGemm split_gemm(const void *A, int M, int K) {
+  dg::SplitGemm g{};
+  g.A = static_cast<const uint16_t *>(A);
+  g.lda = K;
+  g.lo_off = (int64_t)M * K;
+  g.M = M;
+  g.K = K;
+  return g;
+}
+
+hipError_t proj(const dg_config *c, const void *A, int M, int K, int count, const void *const *W, const int *Nout,
+                const dg::Epi *e, float *part, hipStream_t s) {
   if (c->dtype == DG_BF16) {
-    dg::SplitGemm g{};
-    g.A = A;
-    g.lda = lda;
-    g.M = M;
-    g.K = K;
+    dg::SplitGemm g = split_gemm(A, M, K);
     g.count = count;
     for (int i = 0; i < count; ++i) {
       g.B[i] = W[i];
@@ -206,45 +237,45 @@ hipError_t proj(const dg_config *c, const float *A, int64_t lda, int M, int K, i
     return dg::gemm_split(g, s);
   }
   for (int i = 0; i < count; ++i) {
-    dg::GemmShapeF32 g{A, lda, 1, static_cast<const float *>(W[i]), K, 1, M, Nout[i], K, nullptr, 0};
+    dg::GemmShapeF32 g{static_cast<const float *>(A), K, 1, static_cast<const float *>(W[i]), K, 1, M, Nout[i], K,
+                       nullptr, 0};
     const hipError_t err = dg::gemm_f32(g, e[i], s);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
 }
 
-hipError_t proj1(const dg_config *c, const float *A, int64_t lda, int M, int K, const void *W, int Nout,
-                 const dg::Epi &e, float *part, hipStream_t s) {
-  return proj(c, A, lda, M, K, 1, &W, &Nout, &e, part, s);
+hipError_t proj1(const dg_config *c, const void *A, int M, int K, const void *W, int Nout, const dg::Epi &e,
+                 float *part, hipStream_t s) {
+  return proj(c, A, M, K, 1, &W, &Nout, &e, part, s);
 }
 
 // proj1 whose output rows (fp32 [M][Nout], row-major) then go through
-// RMSNorm(gain) into norm_out (fp32) and/or norm_tiled (bf16 tiled): for the
-// bf16 path with a K split the norm is fused into the split-K merge.
-hipError_t proj1_norm(const dg_config *c, const float *A, int64_t lda, int M, int K, const void *W, int Nout,
-                      const dg::Epi &e, float *part, const void *gain, float *norm_out, bf16 *norm_tiled,
+// RMSNorm(gain) into norm_out (fp32), norm_tiled (bf16 tiled) and/or
+// norm_split (split pair): for the bf16 path with a K split the norm is
+// fused into the split-K merge.
+hipError_t proj1_norm(const dg_config *c, const void *A, int M, int K, const void *W, int Nout, const dg::Epi &e,
+                      float *part, const void *gain, float *norm_out, bf16 *norm_tiled, bf16 *norm_split,
                       hipStream_t s) {
   if (c->dtype == DG_BF16 && dg::gemm_split_plan(M, K, &Nout, 1) > 1) {
-    dg::SplitGemm g{};
-    g.A = A;
-    g.lda = lda;
-    g.M = M;
-    g.K = K;
+    dg::SplitGemm g = split_gemm(A, M, K);
     g.count = 1;
     g.B[0] = W;
     g.N[0] = Nout;
     g.e[0] = e;
     g.part = part;
     g.ksplit = dg::gemm_split_plan(M, K, &Nout, 1);
-    const dg::RowNorm rn{static_cast<const uint16_t *>(gain), c->rms_eps, norm_out, norm_tiled};
+    const dg::RowNorm rn{static_cast<const uint16_t *>(gain), c->rms_eps, norm_out, norm_tiled, norm_split};
     return dg::gemm_split_norm(g, rn, s);
   }
-  hipError_t err = proj1(c, A, lda, M, K, W, Nout, e, part, s);
+  hipError_t err = proj1(c, A, M, K, W, Nout, e, part, s);
   if (err != hipSuccess) return err;
   const float *y = static_cast<const float *>(e.out);
   if (c->dtype == DG_BF16)
-    return dg::rmsnorm_rows<bf16>(y, static_cast<const bf16 *>(gain), M, Nout, c->rms_eps, norm_out, norm_tiled, s);
-  return dg::rmsnorm_rows<float>(y, static_cast<const float *>(gain), M, Nout, c->rms_eps, norm_out, norm_tiled, s);
+    return dg::rmsnorm_rows<bf16>(y, static_cast<const bf16 *>(gain), M, Nout, c->rms_eps, norm_out, norm_tiled,
+                                  norm_split, s);
+  return dg::rmsnorm_rows<float>(y, static_cast<const float *>(gain), M, Nout, c->rms_eps, norm_out, norm_tiled,
+                                 norm_split, s);
 }
 
 }  // namespace
@@ -275,8 +306,7 @@ size_t dg_workspace_bytes(const dg_config *cfg, int32_t max_prefill_tokens) {
 
 size_t dg_stats_bytes(const dg_config *cfg) {
   if (check_config(cfg) != DG_OK) return 0;
-  const size_t nt = (size_t)cfg->vocab / kTile;
-  return (size_t)cfg->canvas_len * (nt * (sizeof(float4) + sizeof(float)) + sizeof(float2));
+  return stats_layout(cfg).total;
 }
 
 size_t dg_embedding_pack_bytes(const dg_config *cfg) {
@@ -338,12 +368,14 @@ dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cac
   float *x = reinterpret_cast<float *>(base + L.p_x);
   float *nrm = reinterpret_cast<float *>(base + L.p_nrm);
 
-  if (bf) {
+  if (bf) {  // nrm holds the split pair
     DG_TRY(dg::gather_rows<bf16>(static_cast<const bf16 *>(w->E), tokens, n, d, V, x, s));
-    DG_TRY(dg::rmsnorm_rows<bf16>(x, static_cast<const bf16 *>(w->g_attn), n, d, cfg->rms_eps, nrm, nullptr, s));
+    DG_TRY(dg::rmsnorm_rows<bf16>(x, static_cast<const bf16 *>(w->g_attn), n, d, cfg->rms_eps, nullptr, nullptr,
+                                  reinterpret_cast<bf16 *>(nrm), s));
   } else {
     DG_TRY(dg::gather_rows<float>(static_cast<const float *>(w->E), tokens, n, d, V, x, s));
-    DG_TRY(dg::rmsnorm_rows<float>(x, static_cast<const float *>(w->g_attn), n, d, cfg->rms_eps, nrm, nullptr, s));
+    DG_TRY(dg::rmsnorm_rows<float>(x, static_cast<const float *>(w->g_attn), n, d, cfg->rms_eps, nrm, nullptr,
+                                   nullptr, s));
   }
   // keys/values of the new tokens straight into the (fp32) cache at [length, length+n)
   float *kbase = static_cast<float *>(cache->k) + (size_t)Lp * hd;
@@ -354,7 +386,7 @@ dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cac
   const dg::Epi E3[3] = {epi_store(kbase, true, hd, hd, (int64_t)cap * hd),
                          epi_store(vbase, true, hd, hd, (int64_t)cap * hd),
                          epi_store(q, true, hd, hd, (int64_t)n * hd)};
-  DG_TRY(proj(cfg, nrm, d, n, d, attn_out ? 3 : 2, W, No, E3, reinterpret_cast<float *>(base + L.p_gpart), s));
+  DG_TRY(proj(cfg, nrm, n, d, attn_out ? 3 : 2, W, No, E3, reinterpret_cast<float *>(base + L.p_gpart), s));
   if (attn_out) {
     dg::AttnArgs a{};
     a.q = q;
@@ -411,10 +443,16 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
   float *q = reinterpret_cast<float *>(base + L.q), *kc = reinterpret_cast<float *>(base + L.kc);
   float *vc = reinterpret_cast<float *>(base + L.vc), *o = reinterpret_cast<float *>(base + L.o);
   char *stats = static_cast<char *>(cv->stats);
-  float4 *tstats = reinterpret_cast<float4 *>(stats);
-  float *tscale = reinterpret_cast<float *>(stats + (size_t)N * ntiles * sizeof(float4));
-  float2 *top = reinterpret_cast<float2 *>(stats + (size_t)N * ntiles * (sizeof(float4) + sizeof(float)));
+  const StatsLayout SL = stats_layout(cfg);
+  float4 *tstats = reinterpret_cast<float4 *>(stats + SL.tstats);
+  float *tscale = reinterpret_cast<float *>(stats + SL.tscale);
+  float2 *top = reinterpret_cast<float2 *>(stats + SL.top);
+  float *rscale = reinterpret_cast<float *>(stats + SL.rscale);
+  uint8_t *shift = reinterpret_cast<uint8_t *>(stats + SL.shift);
   float *gpart = reinterpret_cast<float *>(base + L.gpart);
+  bf16 *nrm_s = reinterpret_cast<bf16 *>(base + L.nrm_s);  // split pairs (bf16 path)
+  bf16 *sc_s = reinterpret_cast<bf16 *>(base + L.sc_s);
+  bf16 *o_s = reinterpret_cast<bf16 *>(base + L.o_s);
 
   // 1. embeddings (+ self-conditioning from the previous step's probabilities)
   if (bf)
@@ -429,29 +467,34 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
       dg::TiledGemm g{static_cast<const uint16_t *>(cv->probs), tet, N, d, V};
       {
         ProfScope ps(g_prof_sc, s);
-        DG_TRY(dg::selfcond_bf16(g, part, ks, s));
+        DG_TRY(dg::selfcond_bf16(g, shift, part, ks, s));
       }
-      DG_TRY(dg::selfcond_reduce(part, ks, N, d, top, static_cast<const uint16_t *>(cv->probs), V,
-                                 static_cast<const uint16_t *>(w->E), sc, s));
+      DG_TRY(dg::selfcond_reduce(part, ks, N, d, top, static_cast<const uint16_t *>(cv->probs), V, rscale, shift,
+                                 static_cast<const uint16_t *>(w->E), sc, sc_s, s));
     } else {
       dg::GemmShapeF32 g{static_cast<const float *>(cv->probs), V, 1, static_cast<const float *>(w->E), 1, d,
                          N, d, V, nullptr, 0};
       DG_TRY(dg::gemm_f32(g, epi_store(sc, true, d, d, 0), s));
     }
-    dg::Epi eg = epi_store(G, true, F, F, 0);
+    // G = GELU(W1 S): fp32, or the split pair of the bf16 path
+    dg::Epi eg = epi_store(G, !bf, F, F, 0);
     eg.kind = dg::EPI_GELU;
-    DG_TRY(proj1(cfg, sc, d, N, d, w->w_sc1, F, eg, gpart, s));
+    if (bf) eg.lo_off = (int64_t)N * F;
+    DG_TRY(proj1(cfg, bf ? static_cast<const void *>(sc_s) : sc, N, d, w->w_sc1, F, eg, gpart, s));
     dg::Epi ea = epi_store(h0, true, d, d, 0);
     ea.kind = dg::EPI_ADD;
     ea.resid = h0;
     // h0 += W2 G, then 2. the pre-attention RMSNorm of h0 (fused when the GEMM splits K)
-    DG_TRY(proj1_norm(cfg, G, F, N, F, w->w_sc2, d, ea, gpart, w->g_attn, nrm, nullptr, s));
+    DG_TRY(proj1_norm(cfg, G, N, F, w->w_sc2, d, ea, gpart, w->g_attn, bf ? nullptr : nrm, nullptr,
+                      bf ? nrm_s : nullptr, s));
   } else {
     // 2. RMSNorm of the embeddings (no self-conditioning at a canvas's first step)
     if (bf)
-      DG_TRY(dg::rmsnorm_rows<bf16>(h0, static_cast<const bf16 *>(w->g_attn), N, d, cfg->rms_eps, nrm, nullptr, s));
+      DG_TRY(dg::rmsnorm_rows<bf16>(h0, static_cast<const bf16 *>(w->g_attn), N, d, cfg->rms_eps, nullptr, nullptr,
+                                    nrm_s, s));
     else
-      DG_TRY(dg::rmsnorm_rows<float>(h0, static_cast<const float *>(w->g_attn), N, d, cfg->rms_eps, nrm, nullptr, s));
+      DG_TRY(dg::rmsnorm_rows<float>(h0, static_cast<const float *>(w->g_attn), N, d, cfg->rms_eps, nrm, nullptr,
+                                     nullptr, s));
   }
   // Q/K/V of the canvas (the canvas keys stay in the workspace)
   {
@@ -459,7 +502,7 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     const int No[3] = {Hq * hd, Hkv * hd, Hkv * hd};
     const dg::Epi E3[3] = {epi_store(q, true, hd, hd, (int64_t)N * hd), epi_store(kc, true, hd, hd, (int64_t)N * hd),
                            epi_store(vc, true, hd, hd, (int64_t)N * hd)};
-    DG_TRY(proj(cfg, nrm, d, N, d, 3, W, No, E3, gpart, s));
+    DG_TRY(proj(cfg, bf ? static_cast<const void *>(nrm_s) : nrm, N, d, 3, W, No, E3, gpart, s));
   }
   // 3. bidirectional attention over [cache || canvas], output projection
   dg::AttnArgs a{};
@@ -479,6 +522,7 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
   a.causal = 0;
   a.q_pos0 = 0;
   a.out = o;
+  a.out_split = bf ? o_s : nullptr;
   a.part_o = reinterpret_cast<float *>(base + L.ap_o);
   a.part_ml = reinterpret_cast<float *>(base + L.ap_ml);
   dg::attention_plan(N, Hq, cache->length + N, &a.splits, &a.keys_per_split);
@@ -489,7 +533,8 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     ea.resid = h0;
     // h1 = h0 + O Wo^T, then 4. the final RMSNorm (fp32 for the exact top logit,
     // tiled bf16 for the LM head; fused when the GEMM splits K)
-    DG_TRY(proj1_norm(cfg, o, Hq * hd, N, Hq * hd, w->wo, d, ea, gpart, w->g_final, nrm, bf ? nrm16 : nullptr, s));
+    DG_TRY(proj1_norm(cfg, bf ? static_cast<const void *>(o_s) : o, N, Hq * hd, w->wo, d, ea, gpart, w->g_final, nrm,
+                      bf ? nrm16 : nullptr, nullptr, s));
   }
   // tied LM head with the softmax/entropy statistics
   float *logits = reinterpret_cast<float *>(base + L.logits);
@@ -499,14 +544,16 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
       DG_TRY(dg::lm_head_bf16(nrm16, N, d, static_cast<const uint16_t *>(w->E_pack), V, inv_T,
                               static_cast<uint16_t *>(cv->probs), tstats, dump ? logits : nullptr, s));
     }
-    DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, tscale, nrm,
+    // the numerators stay as stored: the next step's contraction applies the
+    // power-of-two tile exponents and the row factor
+    DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, tscale, rscale, shift, nrm,
                            static_cast<const uint16_t *>(w->E), d, top, s));
-    DG_TRY(dg::normalize_probs_bf16(static_cast<uint16_t *>(cv->probs), tscale, N, V, s));
   } else {
     dg::GemmShapeF32 g{nrm, d, 1, static_cast<const float *>(w->E), d, 1, N, V, d, nullptr, 0};
     DG_TRY(dg::gemm_f32(g, epi_store(logits, true, V, V, 0), s));
     DG_TRY(dg::tile_stats_f32(logits, N, V, inv_T, static_cast<float *>(cv->probs), tstats, s));
-    DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, tscale, nullptr, nullptr, d, top, s));
+    DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, tscale, nullptr, nullptr, nullptr,
+                           nullptr, d, top, s));
     DG_TRY(dg::normalize_probs_f32(static_cast<float *>(cv->probs), tscale, N, V, s));
   }
   // 5. accept / re-noise / stop flags
@@ -629,8 +676,9 @@ dg_status dg_test_selfcond(const dg_config *cfg, const dg_weights *w, const void
     float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + L.sc_part);
     const bf16 *tet = static_cast<const bf16 *>(w->E_pack) + pack_te_elems(cfg);
     dg::TiledGemm g{static_cast<const uint16_t *>(P), tet, N, d, V};
-    DG_TRY(dg::selfcond_bf16(g, part, ks, s));
-    DG_TRY(dg::selfcond_reduce(part, ks, N, d, nullptr, nullptr, V, nullptr, static_cast<float *>(S), s));
+    DG_TRY(dg::selfcond_bf16(g, nullptr, part, ks, s));
+    DG_TRY(dg::selfcond_reduce(part, ks, N, d, nullptr, nullptr, V, nullptr, nullptr, nullptr, static_cast<float *>(S),
+                               nullptr, s));
   } else {
     dg::GemmShapeF32 g{static_cast<const float *>(P), V, 1, static_cast<const float *>(w->E), 1, d, N, d, V,
                        nullptr, 0};

@@ -12,6 +12,7 @@ typedef uint16_t bf16;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(bf16 h) { return __uint_as_float(((uint32_t)h) << 16); }
 
@@ -27,19 +28,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 __device__ __forceinline__ bf16 f32_to_bf16(float f) { return (bf16)(pack_bf16x2(f, 0.f) & 0xffffu); }
 
-// Split of eight floats into two bf16 octets, x = hi + lo with hi = bf16(x)
-// and lo = bf16(x - hi): 16 significant bits, so a product against an exact
-// bf16 operand costs two MFMAs and stays within ~1e-5 of fp32.
+// Split of a float into two bf16 terms, x = hi + lo with hi = bf16(x) and
+// lo = bf16(x - hi): 16 significant bits, so a product against an exact
+// bf16 operand costs two MFMAs and stays within ~1e-5 of fp32.  The pair
+// form below packs two consecutive values per 32-bit word.
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+__device__ __forceinline__ void split4(const float4 v, uint2 &hi, uint2 &lo) {
+  split2(v.x, v.y, hi.x, lo.x);
+  split2(v.z, v.w, hi.y, lo.y);
+}
 __device__ __forceinline__ void split8(const float4 a, const float4 b, uint4 &hi, uint4 &lo) {
-  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-    l[i] = pack_bf16x2(x[2 * i] - __uint_as_float(h[i] << 16), x[2 * i + 1] - __uint_as_float(h[i] & 0xffff0000u));
-  }
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
+  split2(a.x, a.y, hi.x, lo.x);
+  split2(a.z, a.w, hi.y, lo.y);
+  split2(b.x, b.y, hi.z, lo.z);
+  split2(b.z, b.w, hi.w, lo.w);
 }
 
 template <typename T> struct Elem;

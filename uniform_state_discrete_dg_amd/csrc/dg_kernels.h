@@ -13,6 +13,8 @@ typedef uint16_t bf16;  // raw bfloat16 bits
 //   index(row, col) = row * rstride + (col / cdiv) * chi + (col % cdiv)
 // which covers plain row-major outputs (cdiv >= N) and the head-split
 // layouts of Q/K/V ([head][row][hd]: cdiv = hd, chi = head stride).
+// A bf16 output with lo_off != 0 is a split pair: hi = bf16(v) at the index,
+// lo = bf16(v - hi) at index + lo_off (the operand format of SplitGemm).
 enum EpiKind { EPI_STORE = 0, EPI_GELU = 1, EPI_ADD = 2 };
 struct Epi {
   int kind;
@@ -22,6 +24,7 @@ struct Epi {
   int cdiv;
   int64_t chi;
   const float *resid;    // EPI_ADD: out = resid + acc (f32, same index)
+  int64_t lo_off;        // bf16 output: offset of the lo term (0: plain bf16)
 };
 
 // Operands of a table-streaming contraction in the tiled layout of
@@ -33,14 +36,17 @@ struct TiledGemm {
   int M, N, K;
 };
 
-// fp32 activation x bf16 weight GEMM on the bf16 MFMA with the activation
-// split in two bf16 terms: C_seg[M][N_seg] = A[M][K] B_seg[N_seg][K]^T for up
-// to three weight matrices sharing A; K % 32 == 0.  With ksplit > 1 the K
-// range is split over workgroups whose fp32 partials ([seg][ksplit][M][N_seg]
-// in `part`) are summed by a second kernel that applies the epilogue.
+// fp32 activation x bf16 weight GEMM on the bf16 MFMA.  The activation
+// comes as a split pair (two bf16 terms a = hi + lo, hi = bf16(a),
+// lo = bf16(a - hi), written by the kernel that produced it): hi at
+// A[m * lda + k], lo at A[lo_off + m * lda + k].  C_seg[M][N_seg] =
+// A[M][K] B_seg[N_seg][K]^T for up to three weight matrices sharing A;
+// K % 32 == 0.  With ksplit > 1 the K range is split over workgroups whose
+// fp32 partials ([seg][ksplit][M][N_seg] in `part`) are summed by a second
+// kernel that applies the epilogue.
 struct SplitGemm {
-  const float *A;
-  int64_t lda;
+  const uint16_t *A;
+  int64_t lda, lo_off;
   int M, K;
   const void *B[3];
   int N[3];
@@ -57,21 +63,24 @@ hipError_t gemm_split(const SplitGemm &g, hipStream_t s);
 // RMSNorm of a projection's output rows, fused into its split-K merge:
 // y = epilogue(sum of partials) (EPI_STORE or EPI_ADD, fp32, row-major),
 // then out = y / sqrt(mean(y^2) + eps) * gain (fp32 [M][N], nullable) and
-// out_tiled (bf16 tiled block(s), rows past M zero; nullable).  One
-// segment; with ksplit == 1 it runs the GEMM and a separate RMSNorm.
+// out_tiled (bf16 tiled block(s), rows past M zero; nullable) and out_split
+// (split pair [M][N], lo term at + M * N; nullable).  One segment; with
+// ksplit == 1 it runs the GEMM and a separate RMSNorm.
 struct RowNorm {
   const uint16_t *gain;  // bf16 [N]
   float eps;
   float *out;
   uint16_t *out_tiled;
+  uint16_t *out_split;
 };
 hipError_t gemm_split_norm(const SplitGemm &g, const RowNorm &rn, hipStream_t s);
 // Canvas rows per workgroup of the two table-streaming kernels (128 or 256).
 int estream_bm(int M);
-// The self-conditioning contraction: A = probs (tiled bf16 probabilities),
-// B = E^T (tiled, d rows), K = V split in ksplit ranges; writes f32 partials
-// [ksplit][M][N].
-hipError_t selfcond_bf16(const TiledGemm &g, float *partials, int ksplit, hipStream_t s);
+// The self-conditioning contraction: A = probs (tiled bf16), B = E^T (tiled,
+// d rows), K = V split in ksplit ranges; writes f32 partials [ksplit][M][N].
+// shift (nullable; uint8 [K/64][256]): A's value at (row, k) is the stored
+// bf16 times 2^-shift[k / 64][row], applied exactly on the exponent field.
+hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partials, int ksplit, hipStream_t s);
 // fp32 SIMT GEMM: C[m][n] = sum_k A[m*sam + k*sak] * B[n*sbn + k*sbk].
 struct GemmShapeF32 {
   const float *A;
@@ -87,7 +96,9 @@ hipError_t gemm_f32(const GemmShapeF32 &g, const Epi &e, hipStream_t s);
 // Tied LM head + temperature softmax statistics (bf16 operands): for each
 // row and 64-column tile t of z = A E^T: zmax_t, argmax_t, and with
 // y = z * inv_T, m_t = zmax_t * inv_T: l_t = sum exp(y - m_t),
-// s_t = sum exp(y - m_t) (y - m_t); probs = bf16(exp(y - m_t)).
+// s_t = sum exp(y - m_t) (y - m_t); probs = bf16(exp(y - m_t) f_t) with
+// f_t = 2^(m_t log2e - r_t), r_t = ceil(m_t log2e): numerators relative to
+// a power-of-two reference 2^r_t.
 // tile_stats: float4 [M][V/64] = (zmax, l, s, argmax as int bits).
 // A_tiled: the normalised canvas rows (M <= 256, one tiled block); E_tiled:
 // E in the tiled layout; probs_tiled: the numerators, tiled ([M][V]).
@@ -96,13 +107,16 @@ hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E
 // Same statistics from fp32 logits already in memory (fp32 path).
 hipError_t tile_stats_f32(const float *logits, int M, int V, float inv_T, float *probs,
                           float4 *tile_stats, hipStream_t s);
-// Row combine: entropy (nats), argmax, and the per-tile normalisers
-// c[row][t] = exp(m_t - M_row) / L_row used by the next self-conditioning.
-// With n2 (fp32 [M][d]) and E given, the argmax token's logit is recomputed
-// exactly and top[row] = (argmax as int bits, its exact probability).
+// Row combine: entropy (nats), argmax, and the factors that turn the stored
+// numerators into probabilities.  shift == nullptr (numerators exp(y - m_t)):
+// tile_scale[row][t] = exp(m_t - M_row) / L_row.  shift given (numerators
+// relative to 2^r_t, M <= 256): p = stored * 2^-shift[t][row] * row_scale[row]
+// and tile_scale = 2^-shift * row_scale.  With n2 (fp32 [M][d]) and E given,
+// the argmax token's logit is recomputed exactly and top[row] = (argmax as
+// int bits, its exact probability).
 hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,
-                       int32_t *argmax, float *tile_scale, const float *n2, const uint16_t *E, int d,
-                       float2 *top, hipStream_t s);
+                       int32_t *argmax, float *tile_scale, float *row_scale, uint8_t *shift, const float *n2,
+                       const uint16_t *E, int d, float2 *top, hipStream_t s);
 
 // Attention over two key segments [A: nA keys][B: nB keys] per KV head, all
 // fp32 in memory.  q: [Hq][nq][hd]; k/v segment X: base + (g * capX + j) * hd.
@@ -116,6 +130,7 @@ struct AttnArgs {
   int nB, capB;
   int causal, q_pos0;
   void *out;
+  uint16_t *out_split;  // nullable: also the split pair of out (lo term at + nq * Hq * hd)
   float *part_o;   // workspace [splits][Hq][nq][hd]
   float *part_ml;  // workspace [splits][Hq][nq][2]
   int splits, keys_per_split;
@@ -129,20 +144,23 @@ void attention_plan(int nq, int Hq, int nk, int *splits, int *keys_per_split);
 template <typename T>
 hipError_t gather_rows(const T *E, const int32_t *tokens, int n, int d, int V, float *out,
                        hipStream_t s);
-// out (fp32 [n][d], nullable) and/or out_tiled (bf16, tiled block(s) of the
-// rows, the rows past n up to the block end written as zeros; nullable).
+// out (fp32 [n][d], nullable), out_tiled (bf16, tiled block(s) of the
+// rows, the rows past n up to the block end written as zeros; nullable)
+// and/or out_split (split pair [n][d], lo term at + n * d; nullable).
 template <typename T>
 hipError_t rmsnorm_rows(const float *x, const T *g, int n, int d, float eps, float *out, bf16 *out_tiled,
-                        hipStream_t s);
-// S (fp32 [N][d]) = sum of the ksplit partials + exact correction of each
-// row's dominant token (top = (token bits, exact p); nullable): the
-// contraction used the bf16 value of probs (tiled) at (row, a).
+                        bf16 *out_split, hipStream_t s);
+// S (fp32 [N][d]) = row_scale[row] (1 when null) * the sum of the ksplit
+// partials + exact correction of each row's dominant token (top = (token
+// bits, exact p); nullable): the contraction used the value of probs
+// (tiled) at (row, a), scaled by 2^-shift of a's tile when shift is given,
+// times row_scale.  out_split (nullable): S also as a split pair [N][d], lo
+// term at + N * d.
 hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top,
-                           const uint16_t *probs_tiled, int V, const uint16_t *E, float *out, hipStream_t s);
-// In place: p(row, v) = round(p(row, v) * tile_scale[row][v / 64]),
-// numerators -> probabilities.  bf16: tiled layout, round to nearest even;
-// fp32: row-major [N][V].
-hipError_t normalize_probs_bf16(uint16_t *probs_tiled, const float *tile_scale, int N, int V, hipStream_t s);
+                           const uint16_t *probs_tiled, int V, const float *row_scale, const uint8_t *shift,
+                           const uint16_t *E, float *out, uint16_t *out_split, hipStream_t s);
+// In place (fp32 path): p(row, v) *= tile_scale[row][v / 64], numerators ->
+// probabilities; row-major [N][V].
 hipError_t normalize_probs_f32(float *probs, const float *tile_scale, int N, int V, hipStream_t s);
 // out[c * ld_out + r] = in[r * cols + c]
 template <typename T>

@@ -47,12 +47,13 @@ hipError_t gather_rows(const T *E, const int32_t *tokens, int n, int d, int V, f
 template hipError_t gather_rows<float>(const float *, const int32_t *, int, int, int, float *, hipStream_t);
 template hipError_t gather_rows<bf16>(const bf16 *, const int32_t *, int, int, int, float *, hipStream_t);
 
-// RMSNorm: out = x / sqrt(mean(x^2) + eps) * g, written in fp32 and, when
-// requested, also rounded to bf16 (the operand of the tied LM head).
+// RMSNorm: out = x / sqrt(mean(x^2) + eps) * g, written in fp32 and/or, when
+// requested, rounded to bf16 (the operand of the tied LM head) and as a
+// split pair hi + lo (the operand of the projections).
 template <typename T>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ x, const T *__restrict__ g, int n,
                                                       int d, float eps, float *__restrict__ out,
-                                                      bf16 *__restrict__ out_tiled) {
+                                                      bf16 *__restrict__ out_tiled, bf16 *__restrict__ out_split) {
   __shared__ float sh[256];
   const int i = blockIdx.x;
   if (i >= n) {  // padding rows of the tiled block
@@ -68,30 +69,38 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ 
     const float v = xi[k] * inv * Elem<T>::load(g, k);
     if (out) out[(int64_t)i * d + k] = v;
     if (out_tiled) out_tiled[tl_index(i, k, d)] = f32_to_bf16(v);
+    if (out_split) {
+      const bf16 hi = f32_to_bf16(v);
+      out_split[(int64_t)i * d + k] = hi;
+      out_split[(int64_t)n * d + (int64_t)i * d + k] = f32_to_bf16(v - bf16_to_f32(hi));
+    }
   }
 }
 
 template <typename T>
 hipError_t rmsnorm_rows(const float *x, const T *g, int n, int d, float eps, float *out, bf16 *out_tiled,
-                        hipStream_t s) {
+                        bf16 *out_split, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (out_tiled && d % TL_K) return hipErrorInvalidValue;
   const int rows = out_tiled ? (n + TL_ROWS - 1) / TL_ROWS * TL_ROWS : n;
-  hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(rows), dim3(256), 0, s, x, g, n, d, eps, out, out_tiled);
+  hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(rows), dim3(256), 0, s, x, g, n, d, eps, out, out_tiled, out_split);
   return hipGetLastError();
 }
-template hipError_t rmsnorm_rows<float>(const float *, const float *, int, int, float, float *, bf16 *,
+template hipError_t rmsnorm_rows<float>(const float *, const float *, int, int, float, float *, bf16 *, bf16 *,
                                         hipStream_t);
-template hipError_t rmsnorm_rows<bf16>(const float *, const bf16 *, int, int, float, float *, bf16 *,
+template hipError_t rmsnorm_rows<bf16>(const float *, const bf16 *, int, int, float, float *, bf16 *, bf16 *,
                                        hipStream_t);
 
-// Merge of the self-conditioning split-K partials into S (fp32), plus the
-// exact correction of each row's dominant token: the contraction used the
-// bf16 probability p~ at (row, a) of the tiled probabilities for token a,
+// Merge of the self-conditioning split-K partials into S (fp32), times the
+// row factor g (row_scale; 1 when null), plus the exact correction of each
+// row's dominant token: the contraction used p~ = g * (the tiled value at
+// (row, a) scaled by 2^-shift of a's tile, as the contraction scaled it),
 // the previous step's exact probability of a is p_a, so S += (p_a - p~) E[a].
 __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int ksplit, int N, int d,
                                        const float2 *__restrict__ top, const bf16 *__restrict__ probs, int V,
-                                       const bf16 *__restrict__ E, float *__restrict__ out) {
+                                       const float *__restrict__ row_scale, const uint8_t *__restrict__ shift,
+                                       const bf16 *__restrict__ E, float *__restrict__ out,
+                                       bf16 *__restrict__ out_split) {
   // one thread per 4 consecutive columns of one row; d % 4 == 0
   const int row = blockIdx.y;
   const int k = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -107,10 +116,14 @@ __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int kspli
     acc.z += v.z;
     acc.w += v.w;
   }
+  const float g = row_scale ? row_scale[row] : 1.f;
+  acc = make_float4(acc.x * g, acc.y * g, acc.z * g, acc.w * g);
   if (top) {
     const float2 tp = top[row];
     const int a = __float_as_int(tp.x);
-    const float c = tp.y - bf16_to_f32(probs[tl_index(row, a, V)]);
+    int bits = probs[tl_index(row, a, V)];
+    if (shift) bits = max(bits - ((int)shift[(int64_t)(a >> 6) * 256 + row] << 7), 0);
+    const float c = tp.y - g * bf16_to_f32((bf16)bits);
     const bf16 *e = E + (int64_t)a * d + k;
     acc.x += c * bf16_to_f32(e[0]);
     acc.y += c * bf16_to_f32(e[1]);
@@ -118,36 +131,24 @@ __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int kspli
     acc.w += c * bf16_to_f32(e[3]);
   }
   *reinterpret_cast<float4 *>(out + i) = acc;
+  if (out_split) {
+    uint2 hi, lo;
+    split4(acc, hi, lo);
+    *reinterpret_cast<uint2 *>(out_split + i) = hi;
+    *reinterpret_cast<uint2 *>(out_split + count + i) = lo;
+  }
 }
 
 hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top, const uint16_t *probs,
-                           int V, const uint16_t *E, float *out, hipStream_t s) {
+                           int V, const float *row_scale, const uint8_t *shift, const uint16_t *E, float *out,
+                           uint16_t *out_split, hipStream_t s) {
   if (d % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((d / 4 + 255) / 256, N), dim3(256), 0, s, part, ksplit, N, d,
-                     top, probs, V, E, out);
+                     top, probs, V, row_scale, shift, E, out, out_split);
   return hipGetLastError();
 }
 
-// Numerators -> probabilities, in place.  bf16: one thread per 16-byte
-// chunk of the tiled layout (8 columns of one row, inside one 64-column
-// tile); chunks of padding rows are left alone.
-__global__ void normalize_bf16_kernel(bf16 *__restrict__ probs, const float *__restrict__ tile_scale, int64_t chunks,
-                                      int N, int V) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * blockDim.x) {
-    const int p = (int)(i & (TL_CHUNKS - 1));
-    const int64_t bs = i >> 10;  // block * (V / 32) + slice; one block (N <= 256)
-    const int row = p >> 2;
-    if (row >= N) continue;
-    const int slice = (int)(bs % (V / TL_K));
-    const float c = tile_scale[(int64_t)row * (V / 64) + slice / 2];
-    uint4 v = reinterpret_cast<const uint4 *>(probs)[i];
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      w[k] = pack_bf16x2(__uint_as_float(w[k] << 16) * c, __uint_as_float(w[k] & 0xffff0000u) * c);
-    reinterpret_cast<uint4 *>(probs)[i] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
+// Numerators -> probabilities, in place (fp32 path, row-major [N][V]).
 __global__ void normalize_f32_kernel(float *__restrict__ probs, const float *__restrict__ tile_scale, int64_t chunks,
                                      int V) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * blockDim.x) {
@@ -164,14 +165,6 @@ __global__ void normalize_f32_kernel(float *__restrict__ probs, const float *__r
   }
 }
 
-hipError_t normalize_probs_bf16(uint16_t *probs, const float *tile_scale, int N, int V, hipStream_t s) {
-  if (N > TL_ROWS) return hipErrorInvalidValue;
-  const int64_t chunks = (int64_t)(V / TL_K) * TL_CHUNKS;
-  const int64_t blocks = (chunks + 255) / 256;
-  hipLaunchKernelGGL(normalize_bf16_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s,
-                     probs, tile_scale, chunks, N, V);
-  return hipGetLastError();
-}
 hipError_t normalize_probs_f32(float *probs, const float *tile_scale, int N, int V, hipStream_t s) {
   const int64_t chunks = (int64_t)N * V / 4;
   const int64_t blocks = (chunks + 255) / 256;
@@ -333,6 +326,14 @@ __device__ __forceinline__ void rc_argmax(float &v, int &i, float *shv, int *shi
 // dominant token carries most of the entropy's sensitivity to logit error.
 // The exact probability of a is kept in top[row] = (a, p_a) for the next
 // step's self-conditioning.  The argmax itself stays the LM head's.
+//
+// With shift given (bf16 path) the stored numerators are relative to the
+// power-of-two reference 2^r_t, r_t = ceil(m_t log2e) (the LM head's
+// choice), so p = stored * 2^-(R - r_t) * g with R = ceil(M log2e) and
+// g = 2^(R - M log2e) / L: the row factor g goes to row_scale, the
+// per-tile exponent R - r_t (capped at 255) to shift ([tile][256 rows],
+// uint8) and tile_scale holds 2^-(R - r_t) g.  Without shift, tile_scale is
+// e^{m_t - M} / L for numerators relative to m_t itself.
 // RC_CACHE tiles per thread are held in registers (one read of the row's
 // statistics) when ntiles <= 256 * RC_CACHE; otherwise the passes re-read.
 constexpr int RC_CACHE = 16;
@@ -342,6 +343,7 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
                                                           float inv_T, float *__restrict__ entropy,
                                                           int32_t *__restrict__ argmax,
                                                           float *__restrict__ tile_scale,
+                                                          float *__restrict__ row_scale, uint8_t *__restrict__ shift,
                                                           const float *__restrict__ n2, const bf16 *__restrict__ E,
                                                           int d, float2 *__restrict__ top) {
   __shared__ float shv[4];
@@ -408,12 +410,20 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
   L = rc_sum(L, shv);
   S = rc_sum(S, shv);
   const float invL = 1.f / L;
+  const float R = ceilf(My * LOG2E);
+  const float g = exp2f(R - My * LOG2E) * invL;
 #pragma unroll
   for (int i = 0; i < nper; ++i) {
     const int t = threadIdx.x + 256 * i;
     if (t >= ntiles) break;
-    const float dd = tile(i, t).x * inv_T - My;
-    tile_scale[(int64_t)row * ntiles + t] = exp2f(dd * LOG2E) * invL;
+    const float mt = tile(i, t).x * inv_T;
+    if (shift) {
+      const float sh = fminf(fmaxf(R - ceilf(mt * LOG2E), 0.f), 255.f);  // NaN -> 0
+      shift[(int64_t)t * 256 + row] = (uint8_t)sh;
+      tile_scale[(int64_t)row * ntiles + t] = exp2f(-sh) * g;
+    } else {
+      tile_scale[(int64_t)row * ntiles + t] = exp2f((mt - My) * LOG2E) * invL;
+    }
   }
   if (threadIdx.x == 0) {
     float H = logf(L) - S * invL;
@@ -421,18 +431,20 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
     entropy[row] = H;
     argmax[row] = amax;
     if (top) top[row] = make_float2(__int_as_float(amax), exp2f(d_top * LOG2E) * invL);
+    if (row_scale) row_scale[row] = g;
   }
 }
 
 hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,
-                       int32_t *argmax, float *tile_scale, const float *n2, const uint16_t *E, int d,
-                       float2 *top, hipStream_t s) {
+                       int32_t *argmax, float *tile_scale, float *row_scale, uint8_t *shift, const float *n2,
+                       const uint16_t *E, int d, float2 *top, hipStream_t s) {
+  if (shift && M > 256) return hipErrorInvalidValue;
   if (ntiles <= 256 * RC_CACHE)
     hipLaunchKernelGGL(row_combine_kernel<true>, dim3(M), dim3(256), 0, s, tile_stats, ntiles, inv_T, entropy,
-                       argmax, tile_scale, n2, E, d, top);
+                       argmax, tile_scale, row_scale, shift, n2, E, d, top);
   else
     hipLaunchKernelGGL(row_combine_kernel<false>, dim3(M), dim3(256), 0, s, tile_stats, ntiles, inv_T, entropy,
-                       argmax, tile_scale, n2, E, d, top);
+                       argmax, tile_scale, row_scale, shift, n2, E, d, top);
   return hipGetLastError();
 }
 

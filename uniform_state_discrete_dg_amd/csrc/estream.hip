@@ -59,8 +59,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // The operands are restrict-qualified parameters: the compiler then adds no
 // wait of its own between the DMA copies and the LDS reads (the s_waitcnt /
 // s_barrier pairs order them).
-__device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const bf16 *__restrict__ Bt, int sb,
-                                             int se, char *lds, f32x16_t (&acc)[2][4]) {
+//
+// SCALED: the canvas operand holds numerators whose scale is a power of two
+// per (row, 64-column tile): value = stored * 2^-shift[t][row] with shift
+// (uint8, tile-major [K/64][256]) copied into LDS beside each slice s by
+// wave s % 8.  The scaling is exact integer arithmetic on the bf16 exponent
+// field: a saturating subtraction of shift << 7 from each 16-bit value
+// (positive values; anything scaled below the normal range becomes zero or
+// a denormal).
+template <bool SCALED>
+__device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const bf16 *__restrict__ Bt,
+                                             const uint8_t *__restrict__ shift, int sb, int se, char *lds,
+                                             f32x16_t (&acc)[2][4]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r32 = lane & 31, g = lane >> 5;
@@ -78,6 +88,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   // lanes x 16 bytes), chunks p = (2 wave + u) * 64 + lane.
   const bf16 *asrc = At + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
   const bf16 *bsrc = Bt + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
+  char *lds_shift = lds + ES_STAGES * 2 * ES_SLICE;  // SCALED: [stage][256] bytes
   auto issue = [&](int slice, int stage) {
     const int64_t off = (int64_t)min(slice, nk - 1) * TL_ELEMS;  // past the end: a repeat, never read
     char *st = lds + stage * 2 * ES_SLICE;
@@ -86,46 +97,99 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
       __builtin_amdgcn_global_load_lds(asrc + off + u * 512, st + (wave * 2 + u) * 1024, 16, 0, 0);
       __builtin_amdgcn_global_load_lds(bsrc + off + u * 512, st + ES_SLICE + (wave * 2 + u) * 1024, 16, 0, 0);
     }
+    if (SCALED && wave == (slice & 7))  // the slice tile's 256 row exponents, 4 bytes per lane
+      __builtin_amdgcn_global_load_lds(shift + (int64_t)((sb + min(slice, nk - 1)) >> 1) * 256 + lane * 4,
+                                       lds_shift + stage * 256, 4, 0, 0);
   };
-  constexpr int PER = 4;  // DMA instructions per slice per wave
+  // DMA instructions per slice per wave: 4, plus the exponents of slice s
+  // for wave s % 8 when SCALED
+  constexpr int PER = 4;
 
-  // Fragments of one 16-wide k step: 2 canvas + 4 table 16-byte reads.
-  auto frags = [&](int stage, int kk, bf16x8_t (&fa)[2], bf16x8_t (&fb)[4]) {
-    const uint4 *sa = reinterpret_cast<const uint4 *>(lds + stage * 2 * ES_SLICE);
-    const uint4 *sbq = reinterpret_cast<const uint4 *>(lds + stage * 2 * ES_SLICE + ES_SLICE);
-    const int c = kk * 2 + g;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) fa[i] = __builtin_bit_cast(bf16x8_t, sa[tl_pos(wm * 64 + i * 32 + r32, c)]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = __builtin_bit_cast(bf16x8_t, sbq[tl_pos(wn * 128 + j * 32 + r32, c)]);
+  // Fragment f of one 16-wide k step as stored: f < 2 a canvas fragment
+  // (rows wm*64 + 32f), else table fragment f - 2 (rows wn*128 + 32(f-2)).
+  auto frag = [&](int stage, int kk, int f) -> uint4 {
+    const uint4 *sl = reinterpret_cast<const uint4 *>(lds + stage * 2 * ES_SLICE + (f < 2 ? 0 : ES_SLICE));
+    const int row = f < 2 ? wm * 64 + f * 32 + r32 : wn * 128 + (f - 2) * 32 + r32;
+    return sl[tl_pos(row, kk * 2 + g)];
   };
-  auto mfmas = [&](const bf16x8_t (&fa)[2], const bf16x8_t (&fb)[4]) {
+  // SCALED: the exponent of canvas fragment i's row, and its packed form
+  // (shift << 7 in both 16-bit halves)
+  auto expo = [&](int stage, int i) -> uint32_t { return (uint8_t)lds_shift[stage * 256 + wm * 64 + i * 32 + r32]; };
+  auto packed = [](uint32_t sh) -> u16x2_t { return __builtin_bit_cast(u16x2_t, (sh << 7) | (sh << 23)); };
+  auto scale = [&](uint4 &v, u16x2_t e) {
+    v.x = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2_t, v.x), e));
+    v.y = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2_t, v.y), e));
+    v.z = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2_t, v.z), e));
+    v.w = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2_t, v.w), e));
+    asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));  // computed here, not sunk past the barrier
+  };
+  // The 8 MFMAs of one k half with the 6 fragment reads of the next k half
+  // interleaved (two after each of the first three MFMAs), each step pinned
+  // in place, so a fragment is read a full k half before its first use.
+  // With ex, the next half's exponents are read too (a new slice).
+  auto half = [&](const uint4 (&cur)[6], uint4 (&nxt)[6], int nstage, int nkk, bool ex, u16x2_t (&e)[2]) {
+    uint32_t sh[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    for (int m = 0; m < 8; ++m) {
+      const int i = m >> 2, j = m & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cur[2 + j]),
+                                                          __builtin_bit_cast(bf16x8_t, cur[i]), acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (m < 3) {
+        nxt[2 * m] = frag(nstage, nkk, 2 * m);
+        nxt[2 * m + 1] = frag(nstage, nkk, 2 * m + 1);
+        if (SCALED && ex && m == 0) {
+          sh[0] = expo(nstage, 0);
+          sh[1] = expo(nstage, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (SCALED) {  // while the last MFMAs run
+      if (ex) {
+        e[0] = packed(sh[0]);
+        e[1] = packed(sh[1]);
+      }
+      scale(nxt[0], e[0]);
+      scale(nxt[1], e[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  // Software pipeline: the barrier sits between the two k halves of a slice,
-  // so the first-half fragments of slice it+1 are read while the second-half
-  // MFMAs of slice it run.  At the barrier of iteration it every wave has
+  // Software pipeline: the barrier sits between the two k halves of a slice.
+  // The second-half fragments of slice it are read during the first-half
+  // MFMAs, the first-half fragments of slice it+1 (after the barrier) during
+  // the second-half MFMAs.  At the barrier of iteration it every wave has
   // consumed slice it-1 (its second half ran before), so the DMA of slice
   // it+3 may refill that stage.
   issue(0, 0);
   issue(1, 1);
   issue(2, 2);
-  bf16x8_t fa0[2], fb0[4], fa1[2], fb1[4];
-  wait_vmcnt<2 * PER>();
+  uint4 F0[6], F1[6];
+  u16x2_t ex[2];
+  if (SCALED && (wave == 1 || wave == 2))
+    wait_vmcnt<2 * PER + 1>();
+  else
+    wait_vmcnt<2 * PER>();
   __builtin_amdgcn_s_barrier();
-  frags(0, 0, fa0, fb0);
+#pragma unroll
+  for (int f = 0; f < 6; ++f) F0[f] = frag(0, 0, f);
+  if (SCALED) {
+    ex[0] = packed(expo(0, 0));
+    ex[1] = packed(expo(0, 1));
+    scale(F0[0], ex[0]);
+    scale(F0[1], ex[1]);
+  }
   for (int it = 0; it < nk; ++it) {
-    frags(it & 3, 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    wait_vmcnt<PER>();             // this wave's copies of slice it+1 landed
+    half(F0, F1, it & 3, 1, false, ex);  // second half of slice it, same exponents
+    if (SCALED && wave == ((it + 2) & 7))  // this wave's copies of slice it+1 landed ...
+      wait_vmcnt<PER + 1>();
+    else
+      wait_vmcnt<PER>();
     __builtin_amdgcn_s_barrier();  // ... every wave's; every wave is done with slice it-1
     issue(it + 3, (it + 3) & 3);
-    frags((it + 1) & 3, 0, fa0, fb0);  // past the last slice: a repeat, unused
-    mfmas(fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    half(F1, F0, (it + 1) & 3, 0, true, ex);  // past the last slice: a repeat, unused
   }
   wait_vmcnt<0>();  // retire the trailing (unused) prefetches before LDS is reused
   __builtin_amdgcn_s_barrier();
@@ -150,7 +214,7 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
   const int ksl = K / ES_BK;
   f32x16_t acc[2][4];
-  estream_tile(At, Et + (int64_t)blockIdx.x * ksl * TL_ELEMS, 0, ksl, lds, acc);
+  estream_tile<false>(At, Et + (int64_t)blockIdx.x * ksl * TL_ELEMS, nullptr, 0, ksl, lds, acc);
   const int ntiles = V / 64;
 
 #pragma unroll
@@ -183,6 +247,9 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
         }
       }
       const float m = best * inv_T;
+      // stored numerators are exp(y - m) * f = 2^(y log2e - r), r = ceil(m log2e):
+      // the tile's reference is a power of two (see row_combine)
+      const float f = exp2f(m * LOG2E - ceilf(m * LOG2E));
       float l = 0.f, sacc = 0.f;
       uint32_t pk[2][8];
 #pragma unroll
@@ -193,7 +260,7 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
           const float e0 = exp2f(t0 * LOG2E), e1 = exp2f(t1 * LOG2E);
           l += e0 + e1;
           sacc += e0 * t0 + e1 * t1;
-          pk[jj][r >> 1] = pack_bf16x2(e0, e1);
+          pk[jj][r >> 1] = pack_bf16x2(e0 * f, e1 * f);
         }
       l += __shfl_xor(l, 32);
       sacc += __shfl_xor(sacc, 32);
@@ -220,7 +287,7 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
 
 int estream_bm(int) { return ES_BM; }
 
-static size_t es_lds_bytes() { return (size_t)ES_STAGES * 2 * ES_SLICE; }
+static size_t es_lds_bytes() { return (size_t)ES_STAGES * (2 * ES_SLICE + 256); }
 
 hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E_tiled, int V, float inv_T,
                         uint16_t *probs_tiled, float4 *tile_stats, float *logits_dump, hipStream_t s) {
@@ -244,8 +311,10 @@ hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E
 // work items of one K-chunk to workgroups of one XCD where it can, so the
 // chunk of probabilities they share is fetched into that XCD's L2 once.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(TiledGemm g, float *__restrict__ part, int ksplit,
-                                                               int ntn, int items) {
+template <bool SCALED>
+__global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(TiledGemm g, const uint8_t *__restrict__ shift,
+                                                               float *__restrict__ part, int ksplit, int ntn,
+                                                               int items) {
   extern __shared__ __align__(16) char lds[];
   const int b = blockIdx.x, nb = gridDim.x;
   const int per_xcd = nb / 8;  // grid is a multiple of 8
@@ -256,7 +325,7 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(TiledGemm g, floa
   const int sb = (int)((int64_t)ksl * kc / ksplit), se = (int)((int64_t)ksl * (kc + 1) / ksplit);
   const int n0 = nt * ES_BN;
   f32x16_t acc[2][4];
-  estream_tile(g.A, g.B + (int64_t)nt * ksl * TL_ELEMS, sb, se, lds, acc);
+  estream_tile<SCALED>(g.A, g.B + (int64_t)nt * ksl * TL_ELEMS, shift, sb, se, lds, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   float *out = part + (int64_t)kc * g.M * g.N;
@@ -277,11 +346,13 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(TiledGemm g, floa
   }
 }
 
-hipError_t selfcond_bf16(const TiledGemm &g, float *partials, int ksplit, hipStream_t s) {
-  if (g.M > ES_BM || g.K % ES_BK || g.N % 4 || ksplit < 1 || ksplit > g.K / ES_BK) return hipErrorInvalidValue;
+hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partials, int ksplit, hipStream_t s) {
+  if (g.M > ES_BM || g.K % 64 || g.N % 4 || ksplit < 1 || ksplit > g.K / ES_BK) return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(selfcond_es_kernel),
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(selfcond_es_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void *>(selfcond_es_kernel<true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess)
       return hipErrorInvalidValue;
     attr = true;
@@ -289,8 +360,12 @@ hipError_t selfcond_bf16(const TiledGemm &g, float *partials, int ksplit, hipStr
   const int ntn = (g.N + ES_BN - 1) / ES_BN;
   const int items = ntn * ksplit;
   const int grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL(selfcond_es_kernel, dim3(grid), dim3(ES_NT), es_lds_bytes(), s, g, partials, ksplit, ntn,
-                     items);
+  if (shift)
+    hipLaunchKernelGGL(selfcond_es_kernel<true>, dim3(grid), dim3(ES_NT), es_lds_bytes(), s, g, shift, partials,
+                       ksplit, ntn, items);
+  else
+    hipLaunchKernelGGL(selfcond_es_kernel<false>, dim3(grid), dim3(ES_NT), es_lds_bytes(), s, g, shift, partials,
+                       ksplit, ntn, items);
   return hipGetLastError();
 }
 

@@ -21,27 +21,28 @@ __device__ __forceinline__ void epi_store(const Epi &e, int row, int col, float 
   if (e.out_f32) {
     static_cast<float *>(e.out)[idx] = v;
   } else {
-    static_cast<bf16 *>(e.out)[idx] = f32_to_bf16(v);
+    const bf16 hi = f32_to_bf16(v);
+    static_cast<bf16 *>(e.out)[idx] = hi;
+    if (e.lo_off) static_cast<bf16 *>(e.out)[idx + e.lo_off] = f32_to_bf16(v - bf16_to_f32(hi));
   }
 }
 
 // ---------------------------------------------------------------------------
 // Projections and the self-conditioning FFN: fp32 activations against bf16
-// weights.  Each activation is split into two bf16 terms, a = hi + lo with
-// hi = bf16(a) and lo = bf16(a - hi) (16 significant bits), so one fp32
-// product costs two MFMAs and keeps ~1e-5 relative accuracy; the weights
-// are exact in bf16.
+// weights.  Each activation is carried as two bf16 terms, a = hi + lo with
+// hi = bf16(a) and lo = bf16(a - hi) (16 significant bits), written in that
+// form by the kernel that produces it, so one fp32 product costs two MFMAs
+// and keeps ~1e-5 relative accuracy; the weights are exact in bf16.
 //
 // At a 256-row canvas these contractions are small (M = 256, N and K a few
 // thousand), so the work is cut into 64 x 128 output tiles and, along K,
 // into ranges of about 704 (a 256 x 2816 x 2816 product: 88 tiles x 4
 // ranges = 352 workgroups).  Each workgroup
-// (4 waves, wave tile 32 rows x 64 columns) streams its A rows (fp32) and
-// B rows (bf16) through a 4-stage LDS ring fed by the DMA form of the
-// vector load, 32 k per slice, three slices ahead of the MFMAs; the split of
-// A into hi/lo happens on the fragment read.  The MFMA takes the weight
-// fragment first, so a lane's accumulators are one output row and runs of
-// four consecutive output columns.
+// (4 waves, wave tile 32 rows x 64 columns) streams its A rows (both bf16
+// terms) and B rows (bf16) through a 4-stage LDS ring fed by the DMA form of
+// the vector load, 32 k per slice, three slices ahead of the MFMAs.  The
+// MFMA takes the weight fragment first, so a lane's accumulators are one
+// output row and runs of four consecutive output columns.
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int PG_NT = 256;
@@ -54,14 +55,13 @@ __device__ __forceinline__ void pg_wait_vmcnt() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
-// A slice: rows x 8 chunks of 4 floats; chunk c of row r at c ^ ((r >> 1) & 7)
-__device__ __forceinline__ int a_slot(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
-// B slice: rows x 4 chunks of 8 bf16; chunk c of row r at c ^ ((r >> 2) & 3)
+// B slice: rows x 4 chunks of 8 bf16; chunk c of row r at c ^ ((r >> 2) & 3).
+// The A slice is two such arrays of BM rows, the hi terms then the lo terms.
 __device__ __forceinline__ int b_slot(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
 
 template <int BM, int BN, int STAGES>
 struct PgCfg {
-  static constexpr int ASLICE = BM * PG_BK * 4;  // fp32 A slice
+  static constexpr int ASLICE = BM * PG_BK * 4;  // A slice: hi and lo bf16 terms
   static constexpr int BSLICE = BN * PG_BK * 2;  // bf16 B slice
   static constexpr int STAGE = ASLICE + BSLICE;
   static constexpr int LDS = STAGES * STAGE;
@@ -80,7 +80,7 @@ struct PgCfg {
 // s_waitcnt / s_barrier pair before each slice orders them), so it adds no
 // wait of its own.
 template <int BM, int BN, int STAGES>
-__device__ __forceinline__ void pg_tile(const float *__restrict__ A, int64_t lda, int M, int m0,
+__device__ __forceinline__ void pg_tile(const bf16 *__restrict__ A, int64_t lda, int64_t lo_off, int M, int m0,
                                         const bf16 *__restrict__ B, int K, int N, int n0, int sb, int nk, char *lds,
                                         f32x16_t (&acc)[BM / 64][BN / 64]) {
   using C = PgCfg<BM, BN, STAGES>;
@@ -97,14 +97,15 @@ __device__ __forceinline__ void pg_tile(const float *__restrict__ A, int64_t lda
   // DMA sources: per slice each wave copies its share of the A slice and of
   // the B slice in instructions of 64 lanes x 16 bytes; rows past M / N read
   // a clamped valid row and only feed discarded accumulators.
-  const float *asrc[C::UA];
+  const bf16 *asrc[C::UA];
   const bf16 *bsrc[C::UB];
 #pragma unroll
   for (int u = 0; u < C::UA; ++u) {
-    const int p = (wave * C::UA + u) * 64 + lane;
-    const int row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+    const int p = (wave * C::UA + u) * 64 + lane;  // one instruction stays inside one term's array
+    const int t = p / (BM * 4), q = p % (BM * 4);
+    const int row = q >> 2, c = (q & 3) ^ ((row >> 2) & 3);
     const int gr = m0 + row < M ? m0 + row : M - 1;
-    asrc[u] = A + (int64_t)gr * lda + c * 4;
+    asrc[u] = A + t * lo_off + (int64_t)gr * lda + c * 8;
   }
 #pragma unroll
   for (int u = 0; u < C::UB; ++u) {
@@ -130,7 +131,7 @@ __device__ __forceinline__ void pg_tile(const float *__restrict__ A, int64_t lda
     pg_wait_vmcnt<(STAGES - 2) * C::PER>();  // this wave's copies of slice `it` landed
     __builtin_amdgcn_s_barrier();             // ... and every wave's; slice it-1 is consumed
     issue(it + STAGES - 1, nstage);
-    const float4 *sa = reinterpret_cast<const float4 *>(lds + stage * C::STAGE);
+    const uint4 *sa = reinterpret_cast<const uint4 *>(lds + stage * C::STAGE);
     const uint4 *sbq = reinterpret_cast<const uint4 *>(lds + stage * C::STAGE + C::ASLICE);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -139,12 +140,8 @@ __device__ __forceinline__ void pg_tile(const float *__restrict__ A, int64_t lda
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
         const int arow = wm * (BM / 2) + 32 * i + r32;
-        const float4 x0 = sa[a_slot(arow, 4 * kk + 2 * gq)];
-        const float4 x1 = sa[a_slot(arow, 4 * kk + 2 * gq + 1)];
-        uint4 hi, lo;
-        split8(x0, x1, hi, lo);
-        fh[i] = __builtin_bit_cast(bf16x8_t, hi);
-        fl[i] = __builtin_bit_cast(bf16x8_t, lo);
+        fh[i] = __builtin_bit_cast(bf16x8_t, sa[b_slot(arow, 2 * kk + gq)]);
+        fl[i] = __builtin_bit_cast(bf16x8_t, sa[BM * 4 + b_slot(arow, 2 * kk + gq)]);
       }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
@@ -192,7 +189,8 @@ __global__ void __launch_bounds__(PG_NT) gemm_split_kernel(SplitGemm g) {
   const int nsl = K / PG_BK;
   const int sb = (int)((int64_t)nsl * kc / g.ksplit), se = (int)((int64_t)nsl * (kc + 1) / g.ksplit);
   f32x16_t acc[C::FM][C::FN];
-  pg_tile<BM, BN, STAGES>(g.A, g.lda, M, m0, static_cast<const bf16 *>(g.B[seg]), K, N, n0, sb, se - sb, lds, acc);
+  pg_tile<BM, BN, STAGES>(g.A, g.lda, g.lo_off, M, m0, static_cast<const bf16 *>(g.B[seg]), K, N, n0, sb, se - sb, lds,
+                          acc);
 
   // lane: output rows m0 + wm*BM/2 + 32 i + r32; register r of fragment j is
   // column n0 + wn*BN/2 + 32 j + 8 (r >> 2) + 4 gq + (r & 3)
@@ -249,10 +247,30 @@ __global__ void __launch_bounds__(256) gemm_splitk_epilogue_kernel(SplitGemm g) 
   }
   const int row = (int)(t * 4 / N), col = (int)(t * 4 - (int64_t)row * N);
   const Epi e = g.e[seg];
-  epi_store(e, row, col, v.x);
-  epi_store(e, row, col + 1, v.y);
-  epi_store(e, row, col + 2, v.z);
-  epi_store(e, row, col + 3, v.w);
+  const int64_t idx = (int64_t)row * e.rstride + (int64_t)(col / e.cdiv) * e.chi + (col % e.cdiv);
+  if (e.cdiv % 4 || ((idx | e.lo_off) & 3)) {  // the four outputs are not one aligned run
+    epi_store(e, row, col, v.x);
+    epi_store(e, row, col + 1, v.y);
+    epi_store(e, row, col + 2, v.z);
+    epi_store(e, row, col + 3, v.w);
+    return;
+  }
+  if (e.kind == EPI_GELU) {
+    v = make_float4(gelu_erf(v.x), gelu_erf(v.y), gelu_erf(v.z), gelu_erf(v.w));
+  } else if (e.kind == EPI_ADD) {
+    const float4 r = *reinterpret_cast<const float4 *>(e.resid + idx);
+    v = make_float4(v.x + r.x, v.y + r.y, v.z + r.z, v.w + r.w);
+  }
+  if (e.out_f32) {
+    *reinterpret_cast<float4 *>(static_cast<float *>(e.out) + idx) = v;
+  } else if (e.lo_off) {
+    uint2 hi, lo;
+    split4(v, hi, lo);
+    *reinterpret_cast<uint2 *>(static_cast<bf16 *>(e.out) + idx) = hi;
+    *reinterpret_cast<uint2 *>(static_cast<bf16 *>(e.out) + idx + e.lo_off) = lo;
+  } else {
+    *reinterpret_cast<uint2 *>(static_cast<bf16 *>(e.out) + idx) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  }
 }
 
 // Split-K merge + epilogue + RMSNorm, one workgroup per output row: the row
@@ -309,6 +327,12 @@ __global__ void __launch_bounds__(256) gemm_splitk_norm_kernel(SplitGemm g, RowN
     const float q[4] = {y[k].x * inv * bf16_to_f32(rn.gain[c]), y[k].y * inv * bf16_to_f32(rn.gain[c + 1]),
                         y[k].z * inv * bf16_to_f32(rn.gain[c + 2]), y[k].w * inv * bf16_to_f32(rn.gain[c + 3])};
     if (rn.out) *reinterpret_cast<float4 *>(rn.out + (int64_t)row * N + c) = make_float4(q[0], q[1], q[2], q[3]);
+    if (rn.out_split) {
+      uint2 hi, lo;
+      split4(make_float4(q[0], q[1], q[2], q[3]), hi, lo);
+      *reinterpret_cast<uint2 *>(rn.out_split + (int64_t)row * N + c) = hi;
+      *reinterpret_cast<uint2 *>(rn.out_split + (int64_t)M * N + (int64_t)row * N + c) = lo;
+    }
     if (rn.out_tiled) {
       // four consecutive columns of one 8-column chunk: one 8-byte store
       *reinterpret_cast<uint2 *>(rn.out_tiled + tl_index(row, c, N)) =
