@@ -133,6 +133,23 @@ def test_config2_bf16_lockstep(rule):
 
 
 @pytest.mark.usefixtures("logits_dump")
+def test_config2_bf16_lockstep_low_temperature():
+    """T = 0.05: peaked rows whose tiles sit hundreds of nats below the row
+    maximum, so the self-conditioning contraction's power-of-two tile
+    exponents span the whole uint8 range (including the cap that flushes a
+    tile to zero) at steps 1 and 2."""
+    c = W.config(2, sched="const", T0=0.05, T1=0.05)
+    inp = W.make_inputs(c)
+    den, rep = lockstep(c, inp, 3)
+    st = den.canvas.stats
+    nt = c["V"] // 64
+    head = c["N"] * (nt * 20 + 8 + 4)
+    shift = st[(head + 255) // 256 * 256:].view(nt, 256)[:, :c["N"]]
+    assert int(shift.max()) == 255 and int(shift.min()) == 0, (int(shift.min()), int(shift.max()))
+    print(rep)
+
+
+@pytest.mark.usefixtures("logits_dump")
 def test_config3_dims_reduced_vocab_lockstep():
     """Config-3 model dims (d 2816, GQA 16/8, F 2816, L 2048, N 256) with a
     16384-token vocabulary so the oracle finishes in seconds."""

@@ -11,9 +11,11 @@
 // split operands is formed from three bf16 MFMAs (hi*hi + hi*lo + lo*hi),
 // which keeps the scores and the output within ~1e-5 of fp32.
 //
-// Flash-style: a workgroup owns 128 queries of one query head (32 per wave)
-// and a contiguous range of keys (split-KV, partial results merged by a
-// second kernel).  64-key tiles of K and V go through LDS.  The wave
+// Flash-style: a workgroup owns 128 queries of G query heads that share one
+// KV head (G = 2 when the group size is even, else 1; 4 waves of 32
+// queries per head) and a contiguous range of keys (split-KV, partial
+// results merged by a second kernel), so each 64-key tile of K and V is
+// staged through LDS once for G heads.  The wave
 // computes S^T = K Q^T so that each lane ends up holding one query's scores,
 // keeps the running max / sum per lane, and computes O^T = V^T P^T with the
 // probabilities taken straight from registers; V is transposed while it is
@@ -37,14 +39,15 @@ __device__ __forceinline__ int kswz(int row, int chunk) { return row * 16 + (chu
 // so the 16 rows a fragment read touches at one group fall on distinct banks.
 __device__ __forceinline__ int vswz(int hd, int u) { return hd * 8 + (u ^ ((hd >> 1) & 7)); }
 
-__global__ void __launch_bounds__(NTH) attn_split_kernel(AttnArgs a) {
+template <int G>
+__global__ void __launch_bounds__(NTH * G) attn_split_kernel(AttnArgs a) {
   __shared__ uint4 Ks[2][KT * HD / 8];     // hi, lo: [64 keys][16 chunks of 8]
   __shared__ uint4 Vt[2][HD * KT / 8];     // hi, lo: [128 hd][8 chunks of 8 keys]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 5;
-  const int h = blockIdx.y, z = blockIdx.z;
+  const int h = blockIdx.y * G + (wave >> 2), z = blockIdx.z;
   const int g = h / (a.Hq / a.Hkv);
-  const int q = blockIdx.x * BQ + wave * 32 + (lane & 31);
+  const int q = blockIdx.x * BQ + (wave & 3) * 32 + (lane & 31);
   const int nk = a.nA + a.nB;
   const int kbeg = z * a.keys_per_split;
   const int kend = min(nk, kbeg + a.keys_per_split);
@@ -77,13 +80,16 @@ __global__ void __launch_bounds__(NTH) attn_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.f;
 
-  // A tile is 64 keys x 128.  K: 1024 chunks of 8 floats, 4 per thread
-  // (thread -> key idx / 16, chunk idx % 16).  V: thread -> 4 dims
-  // (4 (tid % 32) ..) x the 8 keys of group u = tid / 32, which it writes as
-  // 8-key vectors of V^T.  Group u holds, in MFMA k order, the keys that a
-  // lane's probabilities cover in the P^T fragment: with c = u / 2 and
+  // A tile is 64 keys x 128.  K: 1024 chunks of 8 floats, 4 / G per thread
+  // (thread -> key idx / 16, chunk idx % 16).  V: thread -> DV = 4 / G dims
+  // (DV (tid % (32 G)) ..) x the 8 keys of group u = tid / (32 G), which it
+  // writes as 8-key vectors of V^T.  Group u holds, in MFMA k order, the keys
+  // that a lane's probabilities cover in the P^T fragment: with c = u / 2 and
   // g = u % 2, keys 16 c + 4 g + {0..3} then 16 c + 8 + 4 g + {0..3}.
-  float4 rk[4][2], rv[8];
+  constexpr int KPT = 4 / G, DV = 4 / G;
+  typedef float fv_t __attribute__((ext_vector_type(DV)));
+  float4 rk[KPT][2];
+  fv_t rv[8];
   auto kv_src = [&](int kabs, int col, const float *&kp, const float *&vp, int64_t &off) {
     if (kabs < a.nA) {
       off = ((int64_t)g * a.capA + kabs) * HD + col;
@@ -97,8 +103,8 @@ __global__ void __launch_bounds__(NTH) attn_split_kernel(AttnArgs a) {
   };
   auto load = [&](int kt0) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int idx = tid + t * NTH;
+    for (int t = 0; t < KPT; ++t) {
+      const int idx = tid + t * NTH * G;
       const int key = idx >> 4, ch = idx & 15;
       const int kabs = kt0 + key;
       float4 k0 = make_float4(0.f, 0.f, 0.f, 0.f), k1 = k0;
@@ -112,39 +118,38 @@ __global__ void __launch_bounds__(NTH) attn_split_kernel(AttnArgs a) {
       rk[t][0] = k0;
       rk[t][1] = k1;
     }
-    const int d4 = tid & 31, kg = tid >> 5;
+    const int dv = tid & (32 * G - 1), kg = tid / (32 * G);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int kabs = kt0 + 16 * (kg >> 1) + 4 * (kg & 1) + (j & 3) + 8 * (j >> 2);
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      fv_t v = {};
       if (kabs < kend) {
         int64_t off;
         const float *kp, *vp;
-        kv_src(kabs, d4 * 4, kp, vp, off);
-        v = *reinterpret_cast<const float4 *>(vp + off);
+        kv_src(kabs, dv * DV, kp, vp, off);
+        v = *reinterpret_cast<const fv_t *>(vp + off);
       }
       rv[j] = v;
     }
   };
   auto store = [&]() {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int idx = tid + t * NTH;
+    for (int t = 0; t < KPT; ++t) {
+      const int idx = tid + t * NTH * G;
       const int key = idx >> 4, ch = idx & 15;
       uint4 hi, lo;
       split8(rk[t][0], rk[t][1], hi, lo);
       Ks[0][kswz(key, ch)] = hi;
       Ks[1][kswz(key, ch)] = lo;
     }
-    const int d4 = tid & 31, kg = tid >> 5;
+    const int dv = tid & (32 * G - 1), kg = tid / (32 * G);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x[8] = {(&rv[0].x)[e], (&rv[1].x)[e], (&rv[2].x)[e], (&rv[3].x)[e],
-                          (&rv[4].x)[e], (&rv[5].x)[e], (&rv[6].x)[e], (&rv[7].x)[e]};
+    for (int e = 0; e < DV; ++e) {
+      const float x[8] = {rv[0][e], rv[1][e], rv[2][e], rv[3][e], rv[4][e], rv[5][e], rv[6][e], rv[7][e]};
       uint4 hi, lo;
       split8(make_float4(x[0], x[1], x[2], x[3]), make_float4(x[4], x[5], x[6], x[7]), hi, lo);
-      Vt[0][vswz(d4 * 4 + e, kg)] = hi;
-      Vt[1][vswz(d4 * 4 + e, kg)] = lo;
+      Vt[0][vswz(dv * DV + e, kg)] = hi;
+      Vt[1][vswz(dv * DV + e, kg)] = lo;
     }
   };
 
@@ -311,8 +316,10 @@ void attention_plan(int nq, int Hq, int nk, int *splits, int *keys_per_split) {
 }
 
 hipError_t attention_mfma(const AttnArgs &a, hipStream_t s) {
-  dim3 grid((a.nq + BQ - 1) / BQ, a.Hq, a.splits);
-  hipLaunchKernelGGL(attn_split_kernel, grid, dim3(NTH), 0, s, a);
+  if ((a.Hq / a.Hkv) % 2 == 0)  // pairs of query heads share their KV head's tiles
+    hipLaunchKernelGGL(attn_split_kernel<2>, dim3((a.nq + BQ - 1) / BQ, a.Hq / 2, a.splits), dim3(NTH * 2), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_split_kernel<1>, dim3((a.nq + BQ - 1) / BQ, a.Hq, a.splits), dim3(NTH), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(attn_combine_kernel<float>, dim3(a.nq * a.Hq), dim3(HD), 0, s, a.part_o,
