@@ -61,7 +61,8 @@ typedef enum { DG_ACCEPT_SUM_MINUS_MAX = 0, DG_ACCEPT_CUMSUM = 1 } dg_accept_rul
 /* Model and canvas shape.
  * Supported: 1 <= canvas_len <= 256; vocab a power of two in [256, 2^24];
  * n_q_heads a multiple of n_kv_heads.  DG_BF16 additionally needs head_dim ==
- * 128 and d_model, ffn_hidden multiples of 64; DG_F32 needs head_dim <= 128. */
+ * 128, d_model <= 4096 and d_model, ffn_hidden multiples of 64; DG_F32 needs
+ * head_dim <= 128. */
 typedef struct {
   int32_t canvas_len;   /* N: tokens per canvas ([P1]: 256; [P5] table: 128) */
   int32_t vocab;        /* V */

@@ -68,6 +68,7 @@ def test_shipped_configs_supported(lib, i):
     (dict(N=257), B.DG_ERR_UNSUPPORTED),         # canvas longer than one workgroup
     (dict(hd=64), B.DG_ERR_UNSUPPORTED),         # bf16 kernels are head_dim 128
     (dict(d=1000), B.DG_ERR_UNSUPPORTED),        # K slices of 64
+    (dict(d=4160), B.DG_ERR_UNSUPPORTED),        # row combine holds a d-row in 16 values per thread
     (dict(Hq=12, Hkv=8), B.DG_ERR_UNSUPPORTED),  # GQA groups must divide
     (dict(N=0), B.DG_ERR_INVALID_ARG),
     (dict(rms_eps=-1.0), B.DG_ERR_INVALID_ARG),

@@ -347,8 +347,7 @@ class DeviceCanvas:
                            self.accept.data_ptr(), self.status.data_ptr(), 0, 0, 0, 0)
 
     def probabilities(self, cfg: dg_config) -> torch.Tensor:
-        """The last step's probabilities as float32 [N][V] (row-major).  The
-        bf16 path keeps numerators; p = stored value x tile_scale."""
+        """The last step's probabilities as float32 [N][V] (row-major)."""
         N, V = cfg.canvas_len, cfg.vocab
         if cfg.dtype == DG_BF16:
             num = tiled_to_rows(self.probs.view(torch.bfloat16), N, V).float()
@@ -357,8 +356,15 @@ class DeviceCanvas:
 
     def tile_scale(self, cfg: dg_config) -> torch.Tensor:
         """Per-(row, tile) factors of the last step ([N][V/64] f32) that turn
-        the stored numerators into probabilities."""
+        the stored values into probabilities.  bf16: 2^-exponent x the row
+        factor (the library keeps those two, not the product)."""
         N, nt = cfg.canvas_len, cfg.vocab // TILE_V
+        if cfg.dtype == DG_BF16:
+            head = N * (nt * 20 + 8)
+            g = self.stats[head:head + N * 4].view(torch.float32)
+            base = (head + N * 4 + 255) // 256 * 256
+            e = self.stats[base:base + nt * 256].view(nt, 256)[:, :N].t().float()
+            return torch.exp2(-e) * g.unsqueeze(1)
         return self.stats[N * nt * 16:N * nt * 20].view(torch.float32).view(N, nt)
 
     def top(self, cfg: dg_config):

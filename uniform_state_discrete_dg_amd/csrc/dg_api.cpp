@@ -43,7 +43,8 @@ dg_status check_config(const dg_config *c) {
   if (!is_pow2(c->vocab) || c->vocab < 256 || c->vocab > (1 << 24)) return DG_ERR_UNSUPPORTED;
   if (c->n_q_heads % c->n_kv_heads != 0) return DG_ERR_UNSUPPORTED;
   if (c->dtype == DG_BF16) {
-    if (c->head_dim != 128 || c->d_model % 64 != 0 || c->ffn_hidden % 64 != 0) return DG_ERR_UNSUPPORTED;
+    if (c->head_dim != 128 || c->d_model % 64 != 0 || c->ffn_hidden % 64 != 0 || c->d_model > 4096)
+      return DG_ERR_UNSUPPORTED;
   } else {
     if (c->head_dim > 128) return DG_ERR_UNSUPPORTED;
   }
@@ -454,10 +455,13 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
   bf16 *sc_s = reinterpret_cast<bf16 *>(base + L.sc_s);
   bf16 *o_s = reinterpret_cast<bf16 *>(base + L.o_s);
 
-  // 1. embeddings (+ self-conditioning from the previous step's probabilities)
-  if (bf)
+  // 1. embeddings (+ self-conditioning from the previous step's probabilities);
+  // with self-conditioning on the bf16 path the embedding rows are gathered
+  // by the FFN's output merge (its residual), so h0 is written once
+  const bool fused_embed = bf && cv->has_prev;
+  if (bf && !fused_embed)
     DG_TRY(dg::gather_rows<bf16>(static_cast<const bf16 *>(w->E), cv->tokens, N, d, V, h0, s));
-  else
+  else if (!bf)
     DG_TRY(dg::gather_rows<float>(static_cast<const float *>(w->E), cv->tokens, N, d, V, h0, s));
   if (cv->has_prev) {
     if (bf) {
@@ -482,8 +486,16 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     if (bf) eg.lo_off = (int64_t)N * F;
     DG_TRY(proj1(cfg, bf ? static_cast<const void *>(sc_s) : sc, N, d, w->w_sc1, F, eg, gpart, s));
     dg::Epi ea = epi_store(h0, true, d, d, 0);
-    ea.kind = dg::EPI_ADD;
-    ea.resid = h0;
+    if (fused_embed) {  // h0 = E[tokens] + W2 G
+      ea.kind = dg::EPI_ADD_ROW;
+      ea.gtab = static_cast<const uint16_t *>(w->E);
+      ea.gtok = cv->tokens;
+      ea.gV = V;
+      ea.gld = d;
+    } else {
+      ea.kind = dg::EPI_ADD;
+      ea.resid = h0;
+    }
     // h0 += W2 G, then 2. the pre-attention RMSNorm of h0 (fused when the GEMM splits K)
     DG_TRY(proj1_norm(cfg, G, N, F, w->w_sc2, d, ea, gpart, w->g_attn, bf ? nullptr : nrm, nullptr,
                       bf ? nrm_s : nullptr, s));
@@ -546,7 +558,7 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     }
     // the numerators stay as stored: the next step's contraction applies the
     // power-of-two tile exponents and the row factor
-    DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, tscale, rscale, shift, nrm,
+    DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, nullptr, rscale, shift, nrm,
                            static_cast<const uint16_t *>(w->E), d, top, s));
   } else {
     dg::GemmShapeF32 g{nrm, d, 1, static_cast<const float *>(w->E), d, 1, N, V, d, nullptr, 0};

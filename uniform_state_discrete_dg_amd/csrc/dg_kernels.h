@@ -15,7 +15,9 @@ typedef uint16_t bf16;  // raw bfloat16 bits
 // layouts of Q/K/V ([head][row][hd]: cdiv = hd, chi = head stride).
 // A bf16 output with lo_off != 0 is a split pair: hi = bf16(v) at the index,
 // lo = bf16(v - hi) at index + lo_off (the operand format of SplitGemm).
-enum EpiKind { EPI_STORE = 0, EPI_GELU = 1, EPI_ADD = 2 };
+// EPI_ADD_ROW: out = acc + gtab[tok[row]][col] (bf16 table rows, leading
+// dimension gld, token ids clamped to [0, gV)): a residual gathered on the fly.
+enum EpiKind { EPI_STORE = 0, EPI_GELU = 1, EPI_ADD = 2, EPI_ADD_ROW = 3 };
 struct Epi {
   int kind;
   void *out;
@@ -25,6 +27,10 @@ struct Epi {
   int64_t chi;
   const float *resid;    // EPI_ADD: out = resid + acc (f32, same index)
   int64_t lo_off;        // bf16 output: offset of the lo term (0: plain bf16)
+  const uint16_t *gtab;  // EPI_ADD_ROW
+  const int32_t *gtok;
+  int gV;
+  int64_t gld;
 };
 
 // Operands of a table-streaming contraction in the tiled layout of
@@ -61,7 +67,8 @@ int gemm_split_plan(int M, int K, const int *N, int count);
 size_t gemm_split_part_bytes(int M, int K, const int *N, int count);
 hipError_t gemm_split(const SplitGemm &g, hipStream_t s);
 // RMSNorm of a projection's output rows, fused into its split-K merge:
-// y = epilogue(sum of partials) (EPI_STORE or EPI_ADD, fp32, row-major),
+// y = epilogue(sum of partials) (EPI_STORE, EPI_ADD or EPI_ADD_ROW, fp32,
+// row-major),
 // then out = y / sqrt(mean(y^2) + eps) * gain (fp32 [M][N], nullable) and
 // out_tiled (bf16 tiled block(s), rows past M zero; nullable) and out_split
 // (split pair [M][N], lo term at + M * N; nullable).  One segment; with
@@ -111,9 +118,9 @@ hipError_t tile_stats_f32(const float *logits, int M, int V, float inv_T, float 
 // numerators into probabilities.  shift == nullptr (numerators exp(y - m_t)):
 // tile_scale[row][t] = exp(m_t - M_row) / L_row.  shift given (numerators
 // relative to 2^r_t, M <= 256): p = stored * 2^-shift[t][row] * row_scale[row]
-// and tile_scale = 2^-shift * row_scale.  With n2 (fp32 [M][d]) and E given,
-// the argmax token's logit is recomputed exactly and top[row] = (argmax as
-// int bits, its exact probability).
+// and tile_scale (nullable) = 2^-shift * row_scale.  With n2 (fp32 [M][d],
+// d <= 4096) and E given, the argmax token's logit is recomputed exactly and
+// top[row] = (argmax as int bits, its exact probability).
 hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,
                        int32_t *argmax, float *tile_scale, float *row_scale, uint8_t *shift, const float *n2,
                        const uint16_t *E, int d, float2 *top, hipStream_t s);

@@ -38,9 +38,32 @@ __global__ void gather_kernel(const T *__restrict__ E, const int32_t *__restrict
     out[(int64_t)i * d + k] = Elem<T>::load(E, (int64_t)t * d + k);
 }
 
+// bf16 rows, d % 8 == 0: eight values (16 bytes) per thread
+__global__ void gather8_kernel(const bf16 *__restrict__ E, const int32_t *__restrict__ tokens, int d, int V,
+                               float *__restrict__ out) {
+  const int i = blockIdx.x;
+  int t = tokens[i];
+  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
+  const uint4 *src = reinterpret_cast<const uint4 *>(E + (int64_t)t * d);
+  float4 *dst = reinterpret_cast<float4 *>(out + (int64_t)i * d);
+  for (int k = threadIdx.x; k < d / 8; k += blockDim.x) {
+    const uint4 v = src[k];
+    dst[2 * k] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                             __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+    dst[2 * k + 1] = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u),
+                                 __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u));
+  }
+}
+
 template <typename T>
 hipError_t gather_rows(const T *E, const int32_t *tokens, int n, int d, int V, float *out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  if constexpr (sizeof(T) == 2) {
+    if (d % 8 == 0) {
+      hipLaunchKernelGGL(gather8_kernel, dim3(n), dim3(256), 0, s, E, tokens, d, V, out);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL(gather_kernel<T>, dim3(n), dim3(256), 0, s, E, tokens, d, V, out);
   return hipGetLastError();
 }
@@ -285,6 +308,18 @@ __device__ __forceinline__ float rc_sum(float v, float *sh) {
   __syncthreads();
   return r;
 }
+__device__ __forceinline__ float2 rc_sum2(float a, float b, float *sh) {
+  a = warp_sum(a);
+  b = warp_sum(b);
+  if ((threadIdx.x & 63) == 0) {
+    sh[threadIdx.x >> 6] = a;
+    sh[4 + (threadIdx.x >> 6)] = b;
+  }
+  __syncthreads();
+  const float2 r = make_float2((sh[0] + sh[1]) + (sh[2] + sh[3]), (sh[4] + sh[5]) + (sh[6] + sh[7]));
+  __syncthreads();
+  return r;
+}
 // max of (value, lowest index on ties)
 __device__ __forceinline__ void rc_argmax(float &v, int &i, float *shv, int *shi) {
 #pragma unroll
@@ -332,8 +367,8 @@ __device__ __forceinline__ void rc_argmax(float &v, int &i, float *shv, int *shi
 // choice), so p = stored * 2^-(R - r_t) * g with R = ceil(M log2e) and
 // g = 2^(R - M log2e) / L: the row factor g goes to row_scale, the
 // per-tile exponent R - r_t (capped at 255) to shift ([tile][256 rows],
-// uint8) and tile_scale holds 2^-(R - r_t) g.  Without shift, tile_scale is
-// e^{m_t - M} / L for numerators relative to m_t itself.
+// uint8); tile_scale (nullable then) holds 2^-(R - r_t) g.  Without shift,
+// tile_scale is e^{m_t - M} / L for numerators relative to m_t itself.
 // RC_CACHE tiles per thread are held in registers (one read of the row's
 // statistics) when ntiles <= 256 * RC_CACHE; otherwise the passes re-read.
 constexpr int RC_CACHE = 16;
@@ -346,9 +381,20 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
                                                           float *__restrict__ row_scale, uint8_t *__restrict__ shift,
                                                           const float *__restrict__ n2, const bf16 *__restrict__ E,
                                                           int d, float2 *__restrict__ top) {
-  __shared__ float shv[4];
+  __shared__ float shv[8];
   __shared__ int shi[4];
   const int row = blockIdx.x;
+  // the normalised row for the exact top logit, loaded before the argmax is known
+  constexpr int RC_D = 16;  // per thread: d <= 256 * RC_D
+  float nv[RC_D];
+  const bool fix = n2 != nullptr;
+  if (fix) {
+#pragma unroll
+    for (int i = 0; i < RC_D; ++i) {
+      const int k = threadIdx.x + 256 * i;
+      nv[i] = k < d ? n2[(int64_t)row * d + k] : 0.f;
+    }
+  }
   const float4 *st = stats + (int64_t)row * ntiles;
   float4 c[CACHED ? RC_CACHE : 1];
   auto tile = [&](int i, int t) -> float4 { return CACHED ? c[i] : st[t]; };
@@ -380,11 +426,13 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
   const int ta = amax / TILE;
   // corrected terms of the argmax token inside its tile (reference m_ta = My)
   float l_fix = 0.f, s_fix = 0.f, d_top = 0.f;
-  const bool fix = n2 != nullptr;
   if (fix) {
     float part = 0.f;
-    for (int k = threadIdx.x; k < d; k += 256)
-      part += n2[(int64_t)row * d + k] * bf16_to_f32(E[(int64_t)amax * d + k]);
+#pragma unroll
+    for (int i = 0; i < RC_D; ++i) {
+      const int k = threadIdx.x + 256 * i;
+      if (k < d) part += nv[i] * bf16_to_f32(E[(int64_t)amax * d + k]);
+    }
     const float z_exact = rc_sum(part, shv);
     d_top = z_exact * inv_T - My;
     const float e = exp2f(d_top * LOG2E);
@@ -407,8 +455,11 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
     L += l * w;
     S += w * (sacc + dd * l);
   }
-  L = rc_sum(L, shv);
-  S = rc_sum(S, shv);
+  {
+    const float2 LS = rc_sum2(L, S, shv);
+    L = LS.x;
+    S = LS.y;
+  }
   const float invL = 1.f / L;
   const float R = ceilf(My * LOG2E);
   const float g = exp2f(R - My * LOG2E) * invL;
@@ -420,7 +471,7 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
     if (shift) {
       const float sh = fminf(fmaxf(R - ceilf(mt * LOG2E), 0.f), 255.f);  // NaN -> 0
       shift[(int64_t)t * 256 + row] = (uint8_t)sh;
-      tile_scale[(int64_t)row * ntiles + t] = exp2f(-sh) * g;
+      if (tile_scale) tile_scale[(int64_t)row * ntiles + t] = exp2f(-sh) * g;
     } else {
       tile_scale[(int64_t)row * ntiles + t] = exp2f((mt - My) * LOG2E) * invL;
     }
@@ -438,7 +489,7 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
 hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,
                        int32_t *argmax, float *tile_scale, float *row_scale, uint8_t *shift, const float *n2,
                        const uint16_t *E, int d, float2 *top, hipStream_t s) {
-  if (shift && M > 256) return hipErrorInvalidValue;
+  if ((shift && M > 256) || (n2 && d > 256 * 16)) return hipErrorInvalidValue;
   if (ntiles <= 256 * RC_CACHE)
     hipLaunchKernelGGL(row_combine_kernel<true>, dim3(M), dim3(256), 0, s, tile_stats, ntiles, inv_T, entropy,
                        argmax, tile_scale, row_scale, shift, n2, E, d, top);

@@ -11,11 +11,18 @@
 
 namespace dg {
 
+__device__ __forceinline__ const uint16_t *epi_row(const Epi &e, int row) {
+  int t = e.gtok[row];
+  t = t < 0 ? 0 : (t >= e.gV ? e.gV - 1 : t);
+  return e.gtab + (int64_t)t * e.gld;
+}
+
 __device__ __forceinline__ void epi_store(const Epi &e, int row, int col, float v) {
   const int64_t idx = (int64_t)row * e.rstride + (int64_t)(col / e.cdiv) * e.chi + (col % e.cdiv);
   switch (e.kind) {
     case EPI_GELU: v = gelu_erf(v); break;
     case EPI_ADD: v += e.resid[idx]; break;
+    case EPI_ADD_ROW: v += bf16_to_f32(epi_row(e, row)[col]); break;
     default: break;
   }
   if (e.out_f32) {
@@ -260,6 +267,10 @@ __global__ void __launch_bounds__(256) gemm_splitk_epilogue_kernel(SplitGemm g) 
   } else if (e.kind == EPI_ADD) {
     const float4 r = *reinterpret_cast<const float4 *>(e.resid + idx);
     v = make_float4(v.x + r.x, v.y + r.y, v.z + r.z, v.w + r.w);
+  } else if (e.kind == EPI_ADD_ROW) {
+    const uint16_t *r = epi_row(e, row) + col;
+    v = make_float4(v.x + bf16_to_f32(r[0]), v.y + bf16_to_f32(r[1]), v.z + bf16_to_f32(r[2]),
+                    v.w + bf16_to_f32(r[3]));
   }
   if (e.out_f32) {
     *reinterpret_cast<float4 *>(static_cast<float *>(e.out) + idx) = v;
@@ -309,6 +320,12 @@ __global__ void __launch_bounds__(256) gemm_splitk_norm_kernel(SplitGemm g, RowN
         v.y += r.y;
         v.z += r.z;
         v.w += r.w;
+      } else if (e.kind == EPI_ADD_ROW) {
+        const uint2 r = *reinterpret_cast<const uint2 *>(epi_row(e, row) + c);
+        v.x += __uint_as_float(r.x << 16);
+        v.y += __uint_as_float(r.x & 0xffff0000u);
+        v.z += __uint_as_float(r.y << 16);
+        v.w += __uint_as_float(r.y & 0xffff0000u);
       }
       *reinterpret_cast<float4 *>(o) = v;
       ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
@@ -398,7 +415,8 @@ static hipError_t gemm_split_kernel_launch(const SplitGemm &g, hipStream_t s) {
 hipError_t gemm_split_norm(const SplitGemm &g, const RowNorm &rn, hipStream_t s) {
   const Epi &e = g.e[0];
   if (g.count != 1 || g.ksplit < 2 || !g.part || !e.out_f32 || e.cdiv < g.N[0] || g.N[0] % 4 ||
-      g.N[0] > 256 * 4 * RN_MAXQ || (e.kind != EPI_STORE && e.kind != EPI_ADD) || e.rstride % 4 ||
+      g.N[0] > 256 * 4 * RN_MAXQ || (e.kind != EPI_STORE && e.kind != EPI_ADD && e.kind != EPI_ADD_ROW) ||
+      e.rstride % 4 || (e.kind == EPI_ADD_ROW && e.gld % 4) ||
       (rn.out_tiled && g.N[0] % TL_K))
     return hipErrorInvalidValue;
   hipError_t err = gemm_split_kernel_launch(g, s);  // partials only; the merge applies the epilogue

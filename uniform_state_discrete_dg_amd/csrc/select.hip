@@ -9,11 +9,14 @@
 // the plain running sum (rule CUMSUM).  Every rejected position is
 // re-noised with a fresh uniform token; accepted ones take the argmax.
 //
-// The walk is evaluated in parallel: keys (entropy bits << 32 | position)
-// are bitonic-sorted, the entropies are turned into 2^-32-nat fixed point
-// and prefix-summed in 64-bit integers, and rank r is accepted iff its
-// prefix test holds -- the tests are monotone in r, so this equals the
-// sequential walk, and integer sums make the result independent of order.
+// The walk is evaluated in parallel: each position's key (entropy bits << 32
+// | position) orders it among the others, its entropy is turned into
+// 2^-32-nat fixed point, and each thread sums, in 64-bit integers, the
+// fixed-point entropies of every key below its own -- the prefix sum of its
+// rank in the ascending order, without sorting.  A position is accepted iff
+// its prefix test holds: the tests are monotone in the rank, so this equals
+// the sequential walk, and integer sums make the result independent of
+// summation order.
 #include "dg_device.h"
 #include "dg_kernels.h"
 #include "dgdenoise.h"
@@ -39,10 +42,9 @@ __global__ void __launch_bounds__(256) select_kernel(const float *__restrict__ e
                                                      int32_t *__restrict__ status, int N, int log2v,
                                                      uint64_t limit, int rule, float conf_eps, uint64_t seed,
                                                      uint32_t canvas_id, uint32_t step) {
-  __shared__ uint64_t keys[256];
-  __shared__ uint64_t scan[256];
-  __shared__ uint8_t acc_pos[256];
-  __shared__ float fmin_s[256], fmax_s[256], fsum_s[256];
+  __shared__ __align__(16) uint64_t keys[256];
+  __shared__ __align__(16) uint64_t fix[256];
+  __shared__ float fmin_s[4], fmax_s[4], fsum_s[4];
   const int i = threadIdx.x;
 
   float h = 0.f;
@@ -50,50 +52,41 @@ __global__ void __launch_bounds__(256) select_kernel(const float *__restrict__ e
     h = entropy[i];
     if (h <= 0.f) h = 0.f;  // clamp; NaN passes through
   }
-  keys[i] = (i < N) ? (((uint64_t)__float_as_uint(h) << 32) | (uint32_t)i) : ~0ull;
-  acc_pos[i] = 0;
+  const uint64_t key = (i < N) ? (((uint64_t)__float_as_uint(h) << 32) | (uint32_t)i) : ~0ull;
+  // h >= +0 or NaN, so the float bits order the finite entropies; NaN, inf
+  // and absurd values sort after every finite one and end the walk
+  const bool finite = i < N && h < 1048576.0f;
+  const uint64_t q = finite ? (uint64_t)((double)h * 4294967296.0) : 0ull;
+  keys[i] = key;
+  fix[i] = q;
   __syncthreads();
 
-  // bitonic sort, ascending
-  for (int k = 2; k <= 256; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const int ixj = i ^ j;
-      if (ixj > i) {
-        const uint64_t a = keys[i], b = keys[ixj];
-        const bool up = (i & k) == 0;
-        if ((a > b) == up) {
-          keys[i] = b;
-          keys[ixj] = a;
-        }
-      }
-      __syncthreads();
+  // sum of the fixed-point entropies ranked below this position (only finite
+  // keys can be below a finite one)
+  // (eight keys per step, loaded before use; the padding keys ~0 are never below)
+  uint64_t below = 0;
+  for (int j0 = 0; j0 < N; j0 += 8) {
+    ulonglong2 kk[4], ff[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      kk[u] = reinterpret_cast<const ulonglong2 *>(keys + j0)[u];
+      ff[u] = reinterpret_cast<const ulonglong2 *>(fix + j0)[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      below += ff[u].x & (0ull - (uint64_t)(kk[u].x < key));  // masks, not branches
+      below += ff[u].y & (0ull - (uint64_t)(kk[u].y < key));
     }
   }
-
-  // fixed-point prefix sums over the sorted order (rank = i)
-  const uint64_t key = keys[i];
-  const bool real = key != ~0ull;
-  const float hr = __uint_as_float((uint32_t)(key >> 32));
-  const bool finite = real && (hr < 1048576.0f);  // NaN / inf / absurd end the walk
-  const uint64_t q = finite ? (uint64_t)((double)hr * 4294967296.0) : 0ull;
-  scan[i] = q;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const uint64_t v = (i >= o) ? scan[i - o] : 0ull;
-    __syncthreads();
-    scan[i] += v;
-    __syncthreads();
-  }
-  const uint64_t incl = scan[i];
-  const uint64_t test = (rule == DG_ACCEPT_CUMSUM) ? incl : incl - q;
-  if (finite && test <= limit) acc_pos[(uint32_t)key] = 1;
-  __syncthreads();
+  const uint64_t incl = below + q;
+  const uint64_t test = (rule == DG_ACCEPT_CUMSUM) ? incl : below;  // below = incl - this (the max so far)
+  const int acc_here = (finite && test <= limit) ? 1 : 0;
 
   // re-noise, new canvas, flags
   int changed = 0, conf = 1, acc = 0, isnan_ = 0;
   float hmin = INFINITY, hmax = -INFINITY, hsum = 0.f;
   if (i < N) {
-    acc = acc_pos[i];
+    acc = acc_here;
     const int32_t old = tokens[i];
     const int32_t t = acc ? argmax[i] : uniform_token(seed, (uint32_t)i, step, canvas_id, 1u, log2v);
     tokens[i] = t;
@@ -109,19 +102,25 @@ __global__ void __launch_bounds__(256) select_kernel(const float *__restrict__ e
   const int all_conf = __syncthreads_and(conf);
   const int n_acc = __syncthreads_count(acc);
   const int n_nan = __syncthreads_count(isnan_);
-  fmin_s[i] = hmin;
-  fmax_s[i] = hmax;
-  fsum_s[i] = hsum;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (i < o) {
-      fmin_s[i] = fminf(fmin_s[i], fmin_s[i + o]);
-      fmax_s[i] = fmaxf(fmax_s[i], fmax_s[i + o]);
-      fsum_s[i] += fsum_s[i + o];
-    }
-    __syncthreads();
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    hmin = fminf(hmin, __shfl_xor(hmin, o));
+    hmax = fmaxf(hmax, __shfl_xor(hmax, o));
+    hsum += __shfl_xor(hsum, o);
   }
+  if ((i & 63) == 0) {
+    fmin_s[i >> 6] = hmin;
+    fmax_s[i >> 6] = hmax;
+    fsum_s[i >> 6] = hsum;
+  }
+  __syncthreads();
   if (i == 0) {
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      fmin_s[0] = fminf(fmin_s[0], fmin_s[w]);
+      fmax_s[0] = fmaxf(fmax_s[0], fmax_s[w]);
+      fsum_s[0] += fsum_s[w];
+    }
     const int stable_old = status[DG_ST_STABLE];
     status[DG_ST_ALLCONF] = all_conf;
     status[DG_ST_CHANGED] = any_changed;
