@@ -43,8 +43,8 @@ __device__ __forceinline__ void epi_store(const Epi &e, int row, int col, float 
 //
 // At a 256-row canvas these contractions are small (M = 256, N and K a few
 // thousand), so the work is cut into 64 x 128 output tiles and, along K,
-// into ranges of about 704 (a 256 x 2816 x 2816 product: 88 tiles x 4
-// ranges = 352 workgroups).  Each workgroup
+// into ranges of about 1408 (a 256 x 2816 x 2816 product: 88 tiles x 2
+// ranges = 176 workgroups).  Each workgroup
 // (4 waves, wave tile 32 rows x 64 columns) streams its A rows (both bf16
 // terms) and B rows (bf16) through a 4-stage LDS ring fed by the DMA form of
 // the vector load, 32 k per slice, three slices ahead of the MFMAs.  The
@@ -358,15 +358,17 @@ __global__ void __launch_bounds__(256) gemm_splitk_norm_kernel(SplitGemm g, RowN
   }
 }
 
-// The K ranges depend on K alone (about 22 slices = 704 k each): a row's
-// result then does not depend on how many rows are computed with it, which
-// keeps an incremental prefill bitwise equal to a one-shot one.
+// The K ranges depend on K alone (about 44 slices = 1408 k each, at least
+// two ranges from 64 slices on): a row's result then does not depend on how
+// many rows are computed with it, which keeps an incremental prefill bitwise
+// equal to a one-shot one.  (Measured on the step's shapes, M = 256: two
+// ranges beat three or four once the partials' merge is counted.)
 int gemm_split_plan(int M, int K, const int *N, int count) {
   (void)M;
   (void)N;
   (void)count;
   const int nsl = K / PG_BK;
-  const int ks = (nsl + 11) / 22;
+  const int ks = (nsl + 43) / 44;
   return ks > 1 ? ks : 1;
 }
 
