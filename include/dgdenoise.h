@@ -249,7 +249,10 @@ dg_status dg_should_stop(const dg_config *cfg, const dg_canvas *canvas, int32_t 
  * Writes *steps_run and *stopped (1 if the adaptive stop ended the loop).
  * Errors as dg_denoise_step, checked before the first launch; max_steps >= 0.
  * Returns with the stream synchronised when adaptive_stop != 0, otherwise
- * with the steps enqueued. */
+ * with the steps enqueued.  With adaptive_stop (DG_BF16) the next step's
+ * self-conditioning contraction is enqueued before the host reads a step's
+ * status, guarded on the device by those status words; it writes only the
+ * workspace, and does nothing when the step stopped the canvas. */
 dg_status dg_run_canvas(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache,
                         dg_canvas *canvas, uint64_t seed, uint32_t canvas_id, const float *temps,
                         int32_t max_steps, float accept_threshold_nats, int32_t adaptive_stop,

@@ -415,9 +415,16 @@ dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cac
   return DG_OK;
 }
 
+// How a step treats its self-conditioning contraction (bf16 path):
+//   SC_INLINE  launch it in order (the whole step);
+//   SC_AHEAD   launch only it, guarded by the status words of the step
+//              before (see dg_run_canvas), and return;
+//   SC_DONE    it was launched ahead: launch the rest of the step.
+enum ScMode { SC_INLINE = 0, SC_AHEAD = 1, SC_DONE = 2 };
+
 static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache, dg_canvas *cv,
                               float temperature, float gamma, void *ws, size_t ws_bytes, void *stream,
-                              bool logits_dump) {
+                              bool logits_dump, ScMode sc_mode = SC_INLINE, int32_t stable_steps = 0) {
   dg_status st = check_config(cfg);
   if (st != DG_OK) return st;
   if (!weights_ok(cfg, w) || !cache || !cache->k || !cache->v || !canvas_ok(cv)) return DG_ERR_INVALID_ARG;
@@ -469,10 +476,12 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
       float *part = reinterpret_cast<float *>(base + L.sc_part);
       const bf16 *tet = static_cast<const bf16 *>(w->E_pack) + pack_te_elems(cfg);
       dg::TiledGemm g{static_cast<const uint16_t *>(cv->probs), tet, N, d, V};
-      {
+      if (sc_mode != SC_DONE) {
         ProfScope ps(g_prof_sc, s);
-        DG_TRY(dg::selfcond_bf16(g, shift, part, ks, s));
+        const dg::SelfcondGuard guard{sc_mode == SC_AHEAD ? cv->status : nullptr, stable_steps};
+        DG_TRY(dg::selfcond_bf16(g, shift, part, ks, s, guard));
       }
+      if (sc_mode == SC_AHEAD) return DG_OK;
       DG_TRY(dg::selfcond_reduce(part, ks, N, d, top, static_cast<const uint16_t *>(cv->probs), V, rscale, shift,
                                  static_cast<const uint16_t *>(w->E), sc, sc_s, s));
     } else {
@@ -637,15 +646,37 @@ dg_status dg_run_canvas(const dg_config *cfg, const dg_weights *w, const dg_kv_c
   st = dg_canvas_init(cfg, cv, seed, canvas_id, stream);
   if (st != DG_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // With the adaptive stop, step i+1's self-conditioning contraction (its
+  // first kernel, which writes only the workspace) is launched before the
+  // host reads step i's status, guarded by those status words on the
+  // device: the host's wait and the next launches hide behind a kernel that
+  // is running anyway, and if step i did stop the canvas, every workgroup
+  // of the guarded launch returns at once.
+  thread_local hipEvent_t status_ready = nullptr;
+  if (adaptive_stop && !status_ready && hipEventCreateWithFlags(&status_ready, hipEventDisableTiming) != hipSuccess) {
+    status_ready = nullptr;
+    return DG_ERR_HIP;
+  }
+  const bool ahead_ok = adaptive_stop && cfg->dtype == DG_BF16;
+  bool ahead = false;  // step i's contraction is already in the stream
   for (int32_t i = 0; i < max_steps; ++i) {
-    st = denoise_impl(cfg, w, cache, cv, temps[i], accept_threshold_nats, ws, ws_bytes, stream, g_logits_dump);
+    st = denoise_impl(cfg, w, cache, cv, temps[i], accept_threshold_nats, ws, ws_bytes, stream, g_logits_dump,
+                      ahead ? SC_DONE : SC_INLINE);
     if (st != DG_OK) return st;
     *steps_run = i + 1;
     if (adaptive_stop) {
       DG_TRY(hipMemcpyAsync(pinned, cv->status, DG_STATUS_WORDS * sizeof(int32_t), hipMemcpyDeviceToHost, s));
-      DG_TRY(hipStreamSynchronize(s));
+      DG_TRY(hipEventRecord(status_ready, s));
+      ahead = ahead_ok && i + 1 < max_steps;
+      if (ahead) {
+        st = denoise_impl(cfg, w, cache, cv, temps[i + 1], accept_threshold_nats, ws, ws_bytes, stream,
+                          g_logits_dump, SC_AHEAD, stable_steps);
+        if (st != DG_OK) return st;
+      }
+      DG_TRY(hipEventSynchronize(status_ready));
       if (pinned[DG_ST_ALLCONF] || (stable_steps > 0 && pinned[DG_ST_STABLE] >= stable_steps)) {
         *stopped = 1;
+        if (ahead) DG_TRY(hipStreamSynchronize(s));  // the guarded launch returns at once
         break;
       }
     }

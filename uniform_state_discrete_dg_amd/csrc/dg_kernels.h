@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dgdenoise.h"
+
 namespace dg {
 
 typedef uint16_t bf16;  // raw bfloat16 bits
@@ -87,7 +89,19 @@ int estream_bm(int M);
 // d rows), K = V split in ksplit ranges; writes f32 partials [ksplit][M][N].
 // shift (nullable; uint8 [K/64][256]): A's value at (row, k) is the stored
 // bf16 times 2^-shift[k / 64][row], applied exactly on the exponent field.
-hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partials, int ksplit, hipStream_t s);
+// guard: a launch made before the host knows whether the canvas loop stops
+// after the previous step; every workgroup returns at once when the status
+// words (written by that step's selection) say stop.
+struct SelfcondGuard {
+  const int32_t *status;  // null: unconditional
+  int stable_steps;
+  __device__ bool stopped() const {
+    if (!status) return false;
+    return status[DG_ST_ALLCONF] != 0 || (stable_steps > 0 && status[DG_ST_STABLE] >= stable_steps);
+  }
+};
+hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partials, int ksplit, hipStream_t s,
+                         SelfcondGuard guard = SelfcondGuard{nullptr, 0});
 // fp32 SIMT GEMM: C[m][n] = sum_k A[m*sam + k*sak] * B[n*sbn + k*sbk].
 struct GemmShapeF32 {
   const float *A;

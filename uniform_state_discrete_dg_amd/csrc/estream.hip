@@ -314,12 +314,12 @@ hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E
 template <bool SCALED>
 __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(TiledGemm g, const uint8_t *__restrict__ shift,
                                                                float *__restrict__ part, int ksplit, int ntn,
-                                                               int items) {
+                                                               int items, SelfcondGuard guard) {
   extern __shared__ __align__(16) char lds[];
   const int b = blockIdx.x, nb = gridDim.x;
   const int per_xcd = nb / 8;  // grid is a multiple of 8
   const int item = (b % 8) * per_xcd + b / 8;
-  if (item >= items) return;
+  if (item >= items || guard.stopped()) return;
   const int kc = item / ntn, nt = item % ntn;
   const int ksl = g.K / ES_BK;
   const int sb = (int)((int64_t)ksl * kc / ksplit), se = (int)((int64_t)ksl * (kc + 1) / ksplit);
@@ -346,7 +346,8 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(TiledGemm g, cons
   }
 }
 
-hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partials, int ksplit, hipStream_t s) {
+hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partials, int ksplit, hipStream_t s,
+                         SelfcondGuard guard) {
   if (g.M > ES_BM || g.K % 64 || g.N % 4 || ksplit < 1 || ksplit > g.K / ES_BK) return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
@@ -362,10 +363,10 @@ hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partia
   const int grid = (items + 7) / 8 * 8;
   if (shift)
     hipLaunchKernelGGL(selfcond_es_kernel<true>, dim3(grid), dim3(ES_NT), es_lds_bytes(), s, g, shift, partials,
-                       ksplit, ntn, items);
+                       ksplit, ntn, items, guard);
   else
     hipLaunchKernelGGL(selfcond_es_kernel<false>, dim3(grid), dim3(ES_NT), es_lds_bytes(), s, g, shift, partials,
-                       ksplit, ntn, items);
+                       ksplit, ntn, items, guard);
   return hipGetLastError();
 }
 
