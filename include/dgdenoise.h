@@ -277,8 +277,9 @@ void dg_test_set_logits_dump(int32_t on);
 size_t dg_test_logits_ws_bytes(const dg_config *cfg);
 
 /* Self-conditioning contraction alone: S (f32 [N][d]) = P E, with P given
- * in the layout of dg_canvas.probs (DG_BF16: tiled bf16 [N][V]; DG_F32:
- * float [N][V]); no correction of the dominant token. */
+ * as plain probabilities in the layout of dg_canvas.probs (DG_BF16: tiled
+ * bf16 [N][V], no tile exponents or row factors; DG_F32: float [N][V]); no
+ * correction of the dominant token. */
 dg_status dg_test_selfcond(const dg_config *cfg, const dg_weights *w, const void *P, void *S,
                            void *ws, size_t ws_bytes, void *stream);
 /* Selection kernel alone on given entropies/argmax/tokens (device):
