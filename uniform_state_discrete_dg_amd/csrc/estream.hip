@@ -4,9 +4,13 @@
 //     statistics fused into its epilogue (the logits never reach memory; the
 //     probability numerators are written once in bf16), and
 //   * the self-conditioning contraction S = p_prev E, streaming E^T and
-//     split over V.
-// At a 256-row canvas both are bound by HBM (256 flop per byte of the
-// table), so the design goal is bytes in flight.  A workgroup owns all
+//     split over V, with the probability numerators' power-of-two tile
+//     exponents applied as they are read.
+// At a 256-row canvas both sit at the chip's ridge point (256 flop per byte
+// of the table: HBM and matrix cores would finish together), and with both
+// busy the chip runs at its power limit (the shader clock drops to about
+// 1.4 GHz), so the design keeps bytes in flight and spends as few
+// instructions and LDS bytes per MFMA as it can.  A workgroup owns all
 // canvas rows x 256 table rows.  k advances in 32-wide slices; each slice of
 // both operands (16 KB + 16 KB) is copied global -> LDS by the DMA form of
 // the vector load (global_load_lds_dwordx4, no registers involved) into one
