@@ -65,6 +65,12 @@ def lib():
         L.orc_argmax.restype = _c_i32
         L.orc_argmax_f32.argtypes = [_vp, _c_i32]
         L.orc_argmax_f32.restype = _c_i32
+        L.orc_ln_f32.argtypes = [ctypes.c_float]
+        L.orc_ln_f32.restype = ctypes.c_float
+        L.orc_gumbel_f32.argtypes = [_c_u32]
+        L.orc_gumbel_f32.restype = ctypes.c_float
+        L.orc_gumbel_candidates.argtypes = [_vp, _c_i32, _c_i32, ctypes.c_float, _c_u64, _c_u32,
+                                            _c_u32, _vp, _vp]
         L.orc_attention.argtypes = [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                     _c_i32, _c_i32, _c_i32, _vp]
         L.orc_select.argtypes = [_c_i32, _c_i32, _vp, _vp, _vp, _c_dbl, _c_i32, _c_u64,
@@ -170,6 +176,28 @@ def argmax(z) -> int:
         return int(lib().orc_argmax_f32(_p(z), z.shape[0]))
     z = _f64(z)
     return int(lib().orc_argmax(_p(z), z.shape[0]))
+
+
+def ln_f32(x) -> np.float32:
+    """The fixed single-precision natural log of the multinomial draw."""
+    return np.float32(lib().orc_ln_f32(float(np.float32(x))))
+
+
+def gumbel_f32(w: int) -> np.float32:
+    """Standard Gumbel variable of one 32-bit Philox word (multinomial draw)."""
+    return np.float32(lib().orc_gumbel_f32(int(w) & 0xFFFFFFFF))
+
+
+def gumbel_candidates(z, inv_T, seed: int, step: int, canvas_id: int, fallback) -> np.ndarray:
+    """[P3] §5.3 multinomial candidates of float32 logits z [N][V] by
+    Gumbel-max at temperature 1/inv_T (inv_T the float32 the kernels use),
+    replayable bit for bit; fallback[i] for a row without a finite key."""
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    N, V = z.shape
+    fb = _i32(fallback)
+    out = np.zeros(N, dtype=np.int32)
+    lib().orc_gumbel_candidates(_p(z), N, V, float(np.float32(inv_T)), seed, step, canvas_id, _p(fb), _p(out))
+    return out
 
 
 def attention(q, k, v, Hq: int, Hkv: int, causal: bool = False, q_pos0: int = 0) -> np.ndarray:

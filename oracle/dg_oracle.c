@@ -134,6 +134,80 @@ int32_t orc_argmax_f32(const float *z, int32_t V) {
   return best;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Multinomial candidate ([P3] §5.3, logits scheduler: the token is drawn     */
+/* from the tempered softmax rather than always taken as the most likely).    */
+/* Drawn by the Gumbel-max method: argmax_v (y_v + G_v) with G_v independent  */
+/* standard Gumbel variables is distributed as softmax(y).  Every quantity    */
+/* is single precision and every operation a separately rounded IEEE one      */
+/* (the file is built with -ffp-contract=off), so the draw is a function of   */
+/* the float logits alone and can be replayed exactly.                        */
+/* ------------------------------------------------------------------------ */
+
+/* Natural log of a positive normal float.  x = m 2^e with m folded into     */
+/* (sqrt(1/2), sqrt(2)]; ln m = 2 atanh(s), s = (m - 1) / (m + 1), from the   */
+/* odd series 2 (s + s^3/3 + s^5/5 + s^7/7 + s^9/9) (|s| <= 0.1716, so the    */
+/* first omitted term is below 2^-27 of the result); ln 2 in two parts so     */
+/* that e ln2_hi is exact.                                                    */
+float orc_ln_f32(float x) {
+  uint32_t b;
+  memcpy(&b, &x, 4);
+  int32_t e = (int32_t)((b >> 23) & 0xFFu) - 127;
+  const uint32_t mb = (b & 0x7FFFFFu) | 0x3F800000u;
+  float m;
+  memcpy(&m, &mb, 4);
+  if (m > 1.41421353816986083984375f) { /* the float nearest sqrt(2) */
+    m = m * 0.5f;
+    e = e + 1;
+  }
+  const float f = m - 1.0f;
+  const float s = f / (2.0f + f);
+  const float z = s * s;
+  const float c3 = 2.0f / 3.0f, c5 = 2.0f / 5.0f, c7 = 2.0f / 7.0f, c9 = 2.0f / 9.0f;
+  const float P = z * (c3 + z * (c5 + z * (c7 + z * c9)));
+  const float lnm = (s + s) + s * P;
+  const float ef = (float)e;
+  const float ln2_hi = 0.693145751953125f;      /* 16 significant bits */
+  const float ln2_lo = 1.42860676533018704e-6f; /* ln 2 - ln2_hi */
+  return ef * ln2_hi + (ef * ln2_lo + lnm);
+}
+
+/* Standard Gumbel variable from a 32-bit word: u = (2 floor(w / 512) + 1)   */
+/* 2^-24 lies in (0, 1) and is exact in float; G = -ln(-ln u).                */
+float orc_gumbel_f32(uint32_t w) {
+  const float u = (float)(2u * (w >> 9) + 1u) * 5.9604644775390625e-8f; /* 2^-24 */
+  return -orc_ln_f32(-orc_ln_f32(u));
+}
+
+/* Candidates of N rows of float logits z [N][V]: per row i, the lowest v    */
+/* with the largest key fl(fl(z_v inv_T) + G_v), G_v from word (v mod 4) of  */
+/* Philox4x32-10(key = seed, counter = (i, step, canvas_id, 2 + 4 floor(v/4))). */
+/* A NaN key never wins; a row without a key above -inf takes fallback[i].   */
+void orc_gumbel_candidates(const float *z, int32_t N, int32_t V, float inv_T, uint64_t seed,
+                           uint32_t step, uint32_t canvas_id, const int32_t *fallback,
+                           int32_t *out) {
+  const uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
+#pragma omp parallel for schedule(static)
+  for (int32_t i = 0; i < N; ++i) {
+    float best = -INFINITY;
+    int32_t arg = -1;
+    uint32_t words[4];
+    for (int32_t v = 0; v < V; ++v) {
+      if ((v & 3) == 0) {
+        const uint32_t ctr[4] = {(uint32_t)i, step, canvas_id, 2u + 4u * ((uint32_t)v >> 2)};
+        orc_philox4x32_10(ctr, key, words);
+      }
+      const float y = z[(int64_t)i * V + v] * inv_T;
+      const float k = y + orc_gumbel_f32(words[v & 3]);
+      if (k > best) {
+        best = k;
+        arg = v;
+      }
+    }
+    out[i] = arg >= 0 ? arg : fallback[i];
+  }
+}
+
 void orc_attention(const double *q, const double *k, const double *v,
                    int32_t nq, int32_t nk, int32_t Hq, int32_t Hkv, int32_t hd,
                    int32_t causal, int32_t q_pos0, double *out) {

@@ -76,6 +76,18 @@ void orc_matmul_nt(const double *a, const float *b, int32_t rows, int32_t cols,
 void orc_softmax_entropy(const double *y, int32_t V, double *p, double *H);
 int32_t orc_argmax(const double *z, int32_t V);          /* lowest index on ties */
 int32_t orc_argmax_f32(const float *z, int32_t V);       /* same, float input    */
+/* Multinomial candidate by Gumbel-max ([P3] §5.3), single precision with
+ * separately rounded operations so the draw replays exactly:
+ *   orc_ln_f32: natural log of a positive normal float (fixed evaluation);
+ *   orc_gumbel_f32: -ln(-ln u), u = (2 floor(w/512) + 1) 2^-24;
+ *   orc_gumbel_candidates: per row the lowest index of the largest
+ *     fl(fl(z inv_T) + G), G from word v%4 of Philox(seed; i, step,
+ *     canvas_id, 2 + 4 floor(v/4)); fallback[i] when no key exceeds -inf. */
+float orc_ln_f32(float x);
+float orc_gumbel_f32(uint32_t w);
+void orc_gumbel_candidates(const float *z, int32_t N, int32_t V, float inv_T, uint64_t seed,
+                           uint32_t step, uint32_t canvas_id, const int32_t *fallback,
+                           int32_t *out);
 /* Multi-head attention, query head h reads KV head h / (Hq/Hkv).
  * q: [nq][Hq*hd]; keys/values: [Hkv][nk][hd] (key-major inside a head);
  * causal: query i may read keys 0 .. q_pos0 + i (absolute key positions).

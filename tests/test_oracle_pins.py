@@ -135,6 +135,79 @@ def test_argmax_lowest_index_on_ties():
     assert oracle.argmax(np.array([-1.0, -1.0])) == 0
 
 
+# ------------------------------------------- multinomial (Gumbel-max) ----
+def test_ln_f32_within_two_ulp_of_the_library_log():
+    rng = np.random.default_rng(7)
+    xs = np.concatenate([
+        np.float32(2.0) ** np.arange(-126, 128, dtype=np.float32),            # powers of two
+        np.logspace(-37, 38, 3000).astype(np.float32),
+        (1.0 + rng.uniform(-0.3, 0.5, 3000)).astype(np.float32),              # near 1 (s small)
+        np.nextafter(np.float32(1.0), np.float32(2.0)) + np.zeros(1, np.float32),
+        np.array([1.0, 1.4142135, 1.4142137, 0.70710677, 5.9604645e-8, 0.99999994, 16.635532],
+                 np.float32),
+    ])
+    for x in xs:
+        got = oracle.ln_f32(x)
+        ref = math.log(float(x))
+        ulp = float(np.spacing(np.float32(abs(ref)))) if ref != 0.0 else 0.0
+        assert abs(float(got) - ref) <= 2 * ulp, (x, got, ref)
+    assert oracle.ln_f32(1.0) == 0.0
+
+
+def test_gumbel_transform_is_standard_gumbel():
+    # the uniform's end points: (2 * 0 + 1) 2^-24 and (2 (2^23 - 1) + 1) 2^-24
+    assert oracle.gumbel_f32(0) == np.float32(-math.log(-math.log(2.0 ** -24)))
+    assert abs(float(oracle.gumbel_f32(0xFFFFFFFF)) + math.log(-math.log1p(-2.0 ** -24))) < 1e-5
+    rng = np.random.default_rng(11)
+    g = np.array([oracle.gumbel_f32(w) for w in rng.integers(0, 2 ** 32, 60000, dtype=np.uint64)],
+                 dtype=np.float64)
+    ks = scipy.stats.kstest(g, scipy.stats.gumbel_r.cdf)
+    assert ks.pvalue > 1e-3, ks
+    assert abs(g.mean() - 0.5772156649) < 0.03          # Euler-Mascheroni constant
+    assert abs(g.std() - math.pi / math.sqrt(6.0)) < 0.03
+
+
+def test_gumbel_candidates_follow_the_tempered_softmax():
+    # fixed logits, fresh noise per (row, step): draws ~ softmax(z / T)
+    z = np.array([0.0, 1.0, 2.5, -1.0, 0.3, 2.0, -3.0, 1.7], np.float32)
+    T = 0.7
+    inv_T = np.float32(1.0) / np.float32(T)
+    N, steps = 64, 600
+    counts = np.zeros(8)
+    for s in range(steps):
+        c = oracle.gumbel_candidates(np.tile(z, (N, 1)), inv_T, 0xC0FFEE, s, 3, np.zeros(N, np.int32))
+        counts += np.bincount(c, minlength=8)
+    p = torch.softmax(torch.tensor(z, dtype=torch.float64) / T, 0).numpy()
+    chi = scipy.stats.chisquare(counts, p * counts.sum())
+    assert chi.pvalue > 1e-3, (counts, p * counts.sum())
+    # and not the softmax at T = 1, nor the argmax
+    p1 = torch.softmax(torch.tensor(z, dtype=torch.float64), 0).numpy()
+    assert scipy.stats.chisquare(counts, p1 * counts.sum()).pvalue < 1e-6
+    assert counts[2] < 0.8 * counts.sum()
+
+
+def test_gumbel_candidates_counter_layout_and_fallbacks():
+    N, V, seed, step, cid = 3, 40, 0x0123456789ABCDEF, 5, 9
+    z = np.zeros((N, V), np.float32)                 # flat logits: the winner is the largest noise
+    got = oracle.gumbel_candidates(z, 1.0, seed, step, cid, np.full(N, -7, np.int32))
+    key = [seed & 0xFFFFFFFF, seed >> 32]
+    for i in range(N):
+        g = [oracle.gumbel_f32(oracle.philox4x32_10([i, step, cid, 2 + 4 * (v // 4)], key)[v % 4])
+             for v in range(V)]
+        assert got[i] == int(np.argmax(np.array(g, np.float32)))
+    # NaN keys never win; a row with no key above -inf takes its fallback
+    z2 = np.zeros((N, V), np.float32)
+    z2[0, :] = np.nan
+    z2[1, :] = -np.inf
+    z2[2, 1::2] = np.nan
+    got2 = oracle.gumbel_candidates(z2, 1.0, seed, step, cid, np.array([11, 12, 13], np.int32))
+    assert got2[0] == 11 and got2[1] == 12 and got2[2] % 2 == 0
+    # a dominant logit always wins (its key exceeds every other by more than the noise range)
+    z3 = np.zeros((N, V), np.float32)
+    z3[:, 17] = 40.0
+    assert list(oracle.gumbel_candidates(z3, 1.0, seed, step, cid, np.zeros(N, np.int32))) == [17] * N
+
+
 # ------------------------------------------------------------- attention ----
 def _sdpa_ref(q, k, v, Hq, Hkv, causal_offset=None):
     """torch scaled_dot_product_attention in float64 with KV heads repeated."""
