@@ -69,8 +69,8 @@ def lib():
         L.orc_ln_f32.restype = ctypes.c_float
         L.orc_gumbel_f32.argtypes = [_c_u32]
         L.orc_gumbel_f32.restype = ctypes.c_float
-        L.orc_gumbel_candidates.argtypes = [_vp, _c_i32, _c_i32, ctypes.c_float, _c_u64, _c_u32,
-                                            _c_u32, _vp, _vp]
+        L.orc_multinomial_candidates.argtypes = [_vp, _vp, _c_i32, _c_i32, _vp, ctypes.c_float, _c_u64,
+                                                 _c_u32, _c_u32, _vp, _vp]
         L.orc_attention.argtypes = [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                     _c_i32, _c_i32, _c_i32, _vp]
         L.orc_select.argtypes = [_c_i32, _c_i32, _vp, _vp, _vp, _c_dbl, _c_i32, _c_u64,
@@ -188,15 +188,21 @@ def gumbel_f32(w: int) -> np.float32:
     return np.float32(lib().orc_gumbel_f32(int(w) & 0xFFFFFFFF))
 
 
-def gumbel_candidates(z, inv_T, seed: int, step: int, canvas_id: int, fallback) -> np.ndarray:
-    """[P3] §5.3 multinomial candidates of float32 logits z [N][V] by
-    Gumbel-max at temperature 1/inv_T (inv_T the float32 the kernels use),
-    replayable bit for bit; fallback[i] for a row without a finite key."""
-    z = np.ascontiguousarray(z, dtype=np.float32)
-    N, V = z.shape
+def multinomial_candidates(tile_zmax, tile_l, num, inv_T, seed: int, step: int, canvas_id: int,
+                           fallback) -> np.ndarray:
+    """[P3] §5.3 multinomial candidates drawn in two levels (tile by its mass
+    l_t e^(zmax_t inv_T), then the column by its numerator) with Gumbel-max,
+    replayable bit for bit.  tile_zmax, tile_l: float32 [N][ntiles]; num:
+    float32 numerators [N][64 ntiles]; inv_T the float32 the kernels use."""
+    tz = np.ascontiguousarray(tile_zmax, dtype=np.float32)
+    tl = np.ascontiguousarray(tile_l, dtype=np.float32)
+    nm = np.ascontiguousarray(num, dtype=np.float32)
+    N, nt = tz.shape
+    assert tl.shape == (N, nt) and nm.shape == (N, 64 * nt)
     fb = _i32(fallback)
     out = np.zeros(N, dtype=np.int32)
-    lib().orc_gumbel_candidates(_p(z), N, V, float(np.float32(inv_T)), seed, step, canvas_id, _p(fb), _p(out))
+    lib().orc_multinomial_candidates(_p(tz), _p(tl), N, nt, _p(nm), float(np.float32(inv_T)), seed, step,
+                                     canvas_id, _p(fb), _p(out))
     return out
 
 

@@ -179,32 +179,64 @@ float orc_gumbel_f32(uint32_t w) {
   return -orc_ln_f32(-orc_ln_f32(u));
 }
 
-/* Candidates of N rows of float logits z [N][V]: per row i, the lowest v    */
-/* with the largest key fl(fl(z_v inv_T) + G_v), G_v from word (v mod 4) of  */
-/* Philox4x32-10(key = seed, counter = (i, step, canvas_id, 2 + 4 floor(v/4))). */
-/* A NaN key never wins; a row without a key above -inf takes fallback[i].   */
-void orc_gumbel_candidates(const float *z, int32_t N, int32_t V, float inv_T, uint64_t seed,
-                           uint32_t step, uint32_t canvas_id, const int32_t *fallback,
-                           int32_t *out) {
+/* Key of a positive weight x in the log domain plus an offset and a Gumbel  */
+/* variable: fl(fl(ln x + add) + G(word)); weights that are not positive     */
+/* finite normal floats (zero, subnormal, inf, NaN) get -inf.                 */
+static float gumbel_log_key(float x, float add, uint32_t word) {
+  if (!(x >= 1.17549435e-38f && x <= 3.40282347e38f)) return -INFINITY;
+  const float lx = orc_ln_f32(x) + add;
+  return lx + orc_gumbel_f32(word);
+}
+
+/* Multinomial candidates ([P3] §5.3) drawn in two levels from the          */
+/* distribution the step keeps, per row i (tiles of 64 columns):            */
+/*   tile masses w_t = l_t e^{m_t}: l_t the tile's sum of e^{y - m_t},      */
+/*   m_t = zmax_t inv_T; inside tile t the stored numerators num_v, which   */
+/*   are e^{y_v - m_t} times a factor common to the tile.                   */
+/* Level 1, the tile: the lowest t with the largest fl(fl(ln l_t + m_t) +   */
+/*   G), G from word t%4 of Philox(seed; i, step, canvas_id, 2 + 4 floor(t/4)). */
+/* Level 2, the column c of that tile: the lowest c with the largest        */
+/*   fl(ln num_{64t+c} + G'), G' from word c%4 of Philox(seed; i, step,      */
+/*   canvas_id, 3 + 4 floor(c/4)).                                          */
+/* Gumbel-max at each level draws exactly from its categorical law, so the  */
+/* token is drawn with probability (w_t / sum w) (num_v / sum_tile num),    */
+/* i.e. softmax(y)_v.  NaN keys never win; a row with no key above -inf at  */
+/* either level takes fallback[i].                                          */
+void orc_multinomial_candidates(const float *tile_zmax, const float *tile_l, int32_t N,
+                                int32_t ntiles, const float *num, float inv_T, uint64_t seed,
+                                uint32_t step, uint32_t canvas_id, const int32_t *fallback,
+                                int32_t *out) {
   const uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
-#pragma omp parallel for schedule(static)
   for (int32_t i = 0; i < N; ++i) {
     float best = -INFINITY;
-    int32_t arg = -1;
-    uint32_t words[4];
-    for (int32_t v = 0; v < V; ++v) {
-      if ((v & 3) == 0) {
-        const uint32_t ctr[4] = {(uint32_t)i, step, canvas_id, 2u + 4u * ((uint32_t)v >> 2)};
-        orc_philox4x32_10(ctr, key, words);
-      }
-      const float y = z[(int64_t)i * V + v] * inv_T;
-      const float k = y + orc_gumbel_f32(words[v & 3]);
+    int32_t tile = -1;
+    for (int32_t t = 0; t < ntiles; ++t) {
+      const uint32_t ctr[4] = {(uint32_t)i, step, canvas_id, 2u + 4u * ((uint32_t)t >> 2)};
+      uint32_t w[4];
+      orc_philox4x32_10(ctr, key, w);
+      const float m = tile_zmax[(int64_t)i * ntiles + t] * inv_T;
+      const float k = gumbel_log_key(tile_l[(int64_t)i * ntiles + t], m, w[t & 3]);
       if (k > best) {
         best = k;
-        arg = v;
+        tile = t;
       }
     }
-    out[i] = arg >= 0 ? arg : fallback[i];
+    int32_t col = -1;
+    if (tile >= 0) {
+      best = -INFINITY;
+      for (int32_t c = 0; c < 64; ++c) {
+        const uint32_t ctr[4] = {(uint32_t)i, step, canvas_id, 3u + 4u * ((uint32_t)c >> 2)};
+        uint32_t w[4];
+        orc_philox4x32_10(ctr, key, w);
+        const float k = gumbel_log_key(num[(int64_t)i * ntiles * 64 + (int64_t)tile * 64 + c], 0.0f,
+                                       w[c & 3]);
+        if (k > best) {
+          best = k;
+          col = c;
+        }
+      }
+    }
+    out[i] = col >= 0 ? tile * 64 + col : fallback[i];
   }
 }
 

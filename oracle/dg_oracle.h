@@ -5,7 +5,9 @@
  * Only the tests, the smoke check and the CPU-baseline leg of the benchmark
  * may load it; the product path never does.
  *
- * Arithmetic is IEEE double throughout.  Inputs arrive as float arrays whose
+ * Arithmetic is IEEE double throughout, except the multinomial draw, which
+ * is defined in single precision so that it replays exactly on the GPU's
+ * float statistics.  Inputs arrive as float arrays whose
  * values are exactly what the GPU path receives (for bf16 configurations the
  * harness rounds them to bf16 first, so they upcast exactly), which leaves
  * the arithmetic as the only difference between the two sides.
@@ -76,18 +78,23 @@ void orc_matmul_nt(const double *a, const float *b, int32_t rows, int32_t cols,
 void orc_softmax_entropy(const double *y, int32_t V, double *p, double *H);
 int32_t orc_argmax(const double *z, int32_t V);          /* lowest index on ties */
 int32_t orc_argmax_f32(const float *z, int32_t V);       /* same, float input    */
-/* Multinomial candidate by Gumbel-max ([P3] §5.3), single precision with
+/* Multinomial candidate ([P3] §5.3) by Gumbel-max, single precision with
  * separately rounded operations so the draw replays exactly:
  *   orc_ln_f32: natural log of a positive normal float (fixed evaluation);
  *   orc_gumbel_f32: -ln(-ln u), u = (2 floor(w/512) + 1) 2^-24;
- *   orc_gumbel_candidates: per row the lowest index of the largest
- *     fl(fl(z inv_T) + G), G from word v%4 of Philox(seed; i, step,
- *     canvas_id, 2 + 4 floor(v/4)); fallback[i] when no key exceeds -inf. */
+ *   orc_multinomial_candidates: two levels over 64-column tiles -- the tile
+ *     by the largest fl(fl(ln l_t + zmax_t inv_T) + G) (Philox counter
+ *     (i, step, canvas_id, 2 + 4 floor(t/4)), word t%4), then the column c
+ *     by the largest fl(ln num + G') (counter (i, step, canvas_id,
+ *     3 + 4 floor(c/4)), word c%4); lowest index on ties, NaN never wins,
+ *     fallback[i] when no key exceeds -inf.  tile_zmax, tile_l: [N][ntiles];
+ *     num: the numerators [N][64 ntiles] (row-major floats). */
 float orc_ln_f32(float x);
 float orc_gumbel_f32(uint32_t w);
-void orc_gumbel_candidates(const float *z, int32_t N, int32_t V, float inv_T, uint64_t seed,
-                           uint32_t step, uint32_t canvas_id, const int32_t *fallback,
-                           int32_t *out);
+void orc_multinomial_candidates(const float *tile_zmax, const float *tile_l, int32_t N,
+                                int32_t ntiles, const float *num, float inv_T, uint64_t seed,
+                                uint32_t step, uint32_t canvas_id, const int32_t *fallback,
+                                int32_t *out);
 /* Multi-head attention, query head h reads KV head h / (Hq/Hkv).
  * q: [nq][Hq*hd]; keys/values: [Hkv][nk][hd] (key-major inside a head);
  * causal: query i may read keys 0 .. q_pos0 + i (absolute key positions).

@@ -167,45 +167,86 @@ def test_gumbel_transform_is_standard_gumbel():
     assert abs(g.std() - math.pi / math.sqrt(6.0)) < 0.03
 
 
-def test_gumbel_candidates_follow_the_tempered_softmax():
-    # fixed logits, fresh noise per (row, step): draws ~ softmax(z / T)
-    z = np.array([0.0, 1.0, 2.5, -1.0, 0.3, 2.0, -3.0, 1.7], np.float32)
-    T = 0.7
+def _tile_view(z, inv_T):
+    """Tile statistics and numerators of float32 logits z [N][V], computed in
+    float64 from the definition: zmax_t, l_t = sum e^(y - m_t), num = e^(y - m_t)."""
+    N, V = z.shape
+    y = z.astype(np.float32) * np.float32(inv_T)
+    zt = z.reshape(N, V // 64, 64)
+    zmax = zt.max(axis=2).astype(np.float32)
+    m = (zmax * np.float32(inv_T)).astype(np.float64)
+    e = np.exp(y.reshape(N, V // 64, 64).astype(np.float64) - m[:, :, None])
+    return zmax, e.sum(axis=2).astype(np.float32), e.reshape(N, V).astype(np.float32)
+
+
+def test_multinomial_candidates_follow_the_tempered_softmax():
+    # 256 columns (4 tiles) with fixed logits, fresh noise per (row, step):
+    # the two-level draw must follow softmax(z / T) column by column
+    rng = np.random.default_rng(5)
+    z1 = rng.normal(0.0, 1.2, 256).astype(np.float32)
+    z1[[3, 70, 140, 250]] += np.float32(3.0)     # a few heavy columns in different tiles
+    T = 0.8
     inv_T = np.float32(1.0) / np.float32(T)
-    N, steps = 64, 600
-    counts = np.zeros(8)
-    for s in range(steps):
-        c = oracle.gumbel_candidates(np.tile(z, (N, 1)), inv_T, 0xC0FFEE, s, 3, np.zeros(N, np.int32))
-        counts += np.bincount(c, minlength=8)
-    p = torch.softmax(torch.tensor(z, dtype=torch.float64) / T, 0).numpy()
-    chi = scipy.stats.chisquare(counts, p * counts.sum())
-    assert chi.pvalue > 1e-3, (counts, p * counts.sum())
-    # and not the softmax at T = 1, nor the argmax
-    p1 = torch.softmax(torch.tensor(z, dtype=torch.float64), 0).numpy()
-    assert scipy.stats.chisquare(counts, p1 * counts.sum()).pvalue < 1e-6
-    assert counts[2] < 0.8 * counts.sum()
+    N, steps = 64, 500
+    z = np.tile(z1, (N, 1))
+    zmax, l, num = _tile_view(z, inv_T)
+    counts = np.zeros(256)
+    for s_ in range(steps):
+        c = oracle.multinomial_candidates(zmax, l, num, inv_T, 0xC0FFEE, s_, 3, np.zeros(N, np.int32))
+        counts += np.bincount(c, minlength=256)
+    p = torch.softmax(torch.tensor(z1, dtype=torch.float64) * float(inv_T), 0).numpy()
+    heavy = p * counts.sum() >= 5                      # chi-square over columns with enough mass
+    obs = np.append(counts[heavy], counts[~heavy].sum())
+    exp_ = np.append(p[heavy], p[~heavy].sum()) * counts.sum()
+    chi = scipy.stats.chisquare(obs, exp_)
+    assert chi.pvalue > 1e-3, chi
+    # tile level alone: frequencies of the four tiles
+    pt = p.reshape(4, 64).sum(1)
+    assert scipy.stats.chisquare(counts.reshape(4, 64).sum(1), pt * counts.sum()).pvalue > 1e-3
+    # not the softmax at T = 1
+    p1 = torch.softmax(torch.tensor(z1, dtype=torch.float64), 0).numpy()
+    obs1 = np.append(counts[heavy], counts[~heavy].sum())
+    assert scipy.stats.chisquare(obs1, np.append(p1[heavy], p1[~heavy].sum()) * counts.sum()).pvalue < 1e-6
 
 
-def test_gumbel_candidates_counter_layout_and_fallbacks():
-    N, V, seed, step, cid = 3, 40, 0x0123456789ABCDEF, 5, 9
-    z = np.zeros((N, V), np.float32)                 # flat logits: the winner is the largest noise
-    got = oracle.gumbel_candidates(z, 1.0, seed, step, cid, np.full(N, -7, np.int32))
+def test_multinomial_candidates_scale_invariance_counters_and_fallbacks():
+    N, V, seed, step, cid = 3, 192, 0x0123456789ABCDEF, 5, 9
+    rng = np.random.default_rng(2)
+    z = rng.normal(0, 1, (N, V)).astype(np.float32)
+    zmax, l, num = _tile_view(z, 1.0)
+    fb = np.full(N, -7, np.int32)
+    got = oracle.multinomial_candidates(zmax, l, num, 1.0, seed, step, cid, fb)
+    # a power-of-two factor common to a tile's numerators changes nothing
+    # (the bf16 path stores them relative to a power-of-two reference)
+    num2 = num.copy()
+    num2[:, 64:128] *= np.float32(0.5)
+    assert list(oracle.multinomial_candidates(zmax, l, num2, 1.0, seed, step, cid, fb)) == list(got)
+    # the counter layout: tile t uses word t%4 of counter (i, step, cid, 2 + 4 floor(t/4)),
+    # column c word c%4 of (i, step, cid, 3 + 4 floor(c/4))
     key = [seed & 0xFFFFFFFF, seed >> 32]
     for i in range(N):
-        g = [oracle.gumbel_f32(oracle.philox4x32_10([i, step, cid, 2 + 4 * (v // 4)], key)[v % 4])
-             for v in range(V)]
-        assert got[i] == int(np.argmax(np.array(g, np.float32)))
-    # NaN keys never win; a row with no key above -inf takes its fallback
-    z2 = np.zeros((N, V), np.float32)
-    z2[0, :] = np.nan
-    z2[1, :] = -np.inf
-    z2[2, 1::2] = np.nan
-    got2 = oracle.gumbel_candidates(z2, 1.0, seed, step, cid, np.array([11, 12, 13], np.int32))
-    assert got2[0] == 11 and got2[1] == 12 and got2[2] % 2 == 0
-    # a dominant logit always wins (its key exceeds every other by more than the noise range)
+        kt = [np.float32(np.float32(oracle.ln_f32(l[i, t]) + np.float32(zmax[i, t]))
+                         + oracle.gumbel_f32(oracle.philox4x32_10([i, step, cid, 2 + 4 * (t // 4)], key)[t % 4]))
+              for t in range(V // 64)]
+        t = int(np.argmax(kt))
+        kc = [np.float32(oracle.ln_f32(num[i, 64 * t + c])
+                         + oracle.gumbel_f32(oracle.philox4x32_10([i, step, cid, 3 + 4 * (c // 4)], key)[c % 4]))
+              for c in range(64)]
+        assert got[i] == 64 * t + int(np.argmax(kc))
+    # NaN weights never win; a row with nothing above -inf takes its fallback
+    l2 = l.copy()
+    l2[0, :] = np.nan
+    l2[1, :] = 0.0
+    num3 = num.copy()
+    num3[2, :] = 0.0
+    num3[2, 5::7] = 1.0                                   # the only drawable columns of row 2
+    got2 = oracle.multinomial_candidates(zmax, l2, num3, 1.0, seed, step, cid, np.array([11, 12, 13], np.int32))
+    assert got2[0] == 11 and got2[1] == 12 and got2[2] % 64 % 7 == 5
+    # a dominant logit always wins
     z3 = np.zeros((N, V), np.float32)
-    z3[:, 17] = 40.0
-    assert list(oracle.gumbel_candidates(z3, 1.0, seed, step, cid, np.zeros(N, np.int32))) == [17] * N
+    z3[:, 100] = 60.0
+    a, b, c = _tile_view(z3, 1.0)
+    assert list(oracle.multinomial_candidates(a, b, c, 1.0, seed, step, cid, fb)) == [100] * N
 
 
 # ------------------------------------------------------------- attention ----
