@@ -190,7 +190,7 @@ def main() -> int:
     # stability test off), so every step is a full self-conditioned step.
     den.cfg.conf_eps = 0.0
     temps = [D.temperature(c["sched"], c["T0"], c["T1"], s % c["steps"], c["steps"]) for s in
-             range(max(args.steps, args.warmup))]
+             range(max(args.steps, args.warmup, 20))]
 
     def run(nsteps: int, canvas_id: int):
         n, stopped = B.dg_run_canvas(den.cfg, den.w.s, den.cache.s, den.canvas.s, seed, canvas_id,
@@ -207,6 +207,18 @@ def main() -> int:
     dt = time.perf_counter() - t0
     B.dg_profile_enable(False)
     lm_ms, lm_n, sc_ms, sc_n = B.dg_profile_read()
+
+    # The multinomial candidate rule ([P3] §5.3): the same loop with the draw
+    # kernel after the row combine (a shorter timed run)
+    den.cfg.candidate_rule = B.DG_CANDIDATE_MULTINOMIAL
+    n_mn = max(5, min(20, args.steps))
+    run(2, 2)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    run(n_mn, 3)
+    torch.cuda.synchronize()
+    dt_mn = time.perf_counter() - t1
+    den.cfg.candidate_rule = B.DG_CANDIDATE_ARGMAX
 
     steps_per_s = args.steps / dt
     # every timed step but the first of the canvas uses self-conditioning
@@ -232,6 +244,8 @@ def main() -> int:
                      "bytes_per_launch": lm_head_bytes(c)},
         "selfcond_kernel": {"avg_launch_us": sc_avg_s * 1e6, "launches": sc_n,
                             "achieved_GBps": selfcond_bytes(c) / max(sc_avg_s, 1e-12) / 1e9},
+        "multinomial_candidates": {"steps_per_s": n_mn / dt_mn, "steps": n_mn,
+                                   "note": "same loop with the two-level Gumbel-max draw of the candidate tokens"},
         "adaptive_stop": {"fires_at_step": probe_steps if probe_stopped else None,
                           "timed_loop": "stop test run after every step, thresholds set so it cannot fire"},
     }

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define DG_ABI_VERSION 1
+#define DG_ABI_VERSION 2
 
 typedef enum {
   DG_OK = 0,
@@ -58,6 +58,29 @@ typedef enum { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
  *   <= the threshold. */
 typedef enum { DG_ACCEPT_SUM_MINUS_MAX = 0, DG_ACCEPT_CUMSUM = 1 } dg_accept_rule;
 
+/* Token placed at an accepted position.
+ * ARGMAX: the most likely token (highest logit, lowest index on ties); the
+ *   pages' figures speak of the most likely token.
+ * MULTINOMIAL: [P3] §5.3 logits scheduler -- a draw from the tempered
+ *   softmax p = softmax(z / T), made from the distribution the step keeps
+ *   (tile statistics and stored numerators, 64-column tiles) in two
+ *   Gumbel-max levels, each of which draws exactly from its categorical law:
+ *     tile t: the largest fl(fl(ln l_t + zmax_t * inv_T) + G), l_t the
+ *       tile's sum of e^(y - m_t), G from word t % 4 of Philox4x32-10(key =
+ *       seed, counter = (i, step, canvas_id, 2 + 4 floor(t / 4)));
+ *     column c of that tile: the largest fl(ln num_c + G'), num_c the stored
+ *       numerator, G' from word c % 4 of counter (i, step, canvas_id,
+ *       3 + 4 floor(c / 4));
+ *   lowest index on equal keys, NaN keys (and weights that are not positive
+ *   normal floats) never drawn, the argmax when nothing is drawable.
+ *   G = -ln(-ln u), u = (2 floor(w / 512) + 1) 2^-24, inv_T = (float)(1 / T)
+ *   as the step computes it, and ln a fixed single-precision evaluation
+ *   (x = m 2^e, m in (sqrt(1/2), sqrt(2)]; 2 atanh((m-1)/(m+1)) to the s^9
+ *   term; e ln 2 with ln 2 = 0.693145751953125 + 1.42860676533018704e-6),
+ *   every operation rounded on its own, so the draw replays exactly from the
+ *   step's float statistics. */
+typedef enum { DG_CANDIDATE_ARGMAX = 0, DG_CANDIDATE_MULTINOMIAL = 1 } dg_candidate_rule;
+
 /* Model and canvas shape.
  * Supported: 1 <= canvas_len <= 256; vocab a power of two in [256, 2^24];
  * n_q_heads a multiple of n_kv_heads.  DG_BF16 additionally needs head_dim ==
@@ -76,6 +99,7 @@ typedef struct {
   float conf_eps;       /* adaptive-stop confidence threshold on entropy, nats
                            ([P3] §5.3: 0.005) */
   dg_accept_rule accept_rule;
+  dg_candidate_rule candidate_rule;
 } dg_config;
 
 /* Weights (device, dtype of the config, caller-owned, read-only).
@@ -120,7 +144,9 @@ typedef struct {
  *                                and each row's dominant token with its
  *                                exact probability; opaque
  *   entropy float [N]            nats, clamped >= +0 (NaN propagates)
- *   argmax  int32 [N]            highest logit, lowest index on ties
+ *   argmax  int32 [N]            the candidate token of the last step: the
+ *                                highest logit (lowest index on ties), or the
+ *                                multinomial draw (candidate_rule)
  *   accept  uint8 [N]            1 = accepted in the last step
  *   status  int32 [DG_STATUS_WORDS]  see DG_ST_* below
  * Host fields: step (index of the next step), has_prev (the next step uses
@@ -218,10 +244,11 @@ dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cac
  *  2. bidirectional attention (no mask) of every canvas query over
  *     [cache 0..length) || canvas keys; h1 = h0 + O Wo^T
  *  3. z = RMSNorm(h1) E^T (tied head); y = z / temperature; p = softmax(y);
- *     entropy (nats) and argmax per position; probs/stats keep p for the
- *     next step
+ *     entropy (nats) and the candidate token per position (`candidate_rule`:
+ *     argmax, or the multinomial draw with Philox counter words 3 of
+ *     2 + 4k and 3 + 4k); probs/stats keep p for the next step
  *  4. accept by `accept_rule` under `accept_threshold_nats`; accepted
- *     positions take the argmax token, every rejected one a fresh uniform
+ *     positions take the candidate token, every rejected one a fresh uniform
  *     token (Philox counter (i, step, canvas_id, 1)); status flags updated
  * Then canvas->step += 1 and canvas->has_prev = 1 (host fields).
  * Errors: temperature must be finite and > 0; the threshold >= 0 and not NaN;
@@ -290,6 +317,11 @@ dg_status dg_test_select(const dg_config *cfg, dg_canvas *canvas, float accept_t
  * and key (k0, k1); n counters; all device pointers. */
 dg_status dg_test_philox(const uint32_t *ctr, uint32_t k0, uint32_t k1, uint32_t *out, int32_t n,
                          void *stream);
+/* The multinomial draw's single-precision pieces on the device, for n
+ * device words w: mode 0 writes out[i] = ln of the float whose bits are
+ * w[i] (positive normal floats), mode 1 the Gumbel variable of word w[i]
+ * (see DG_CANDIDATE_MULTINOMIAL); out is device float [n]. */
+dg_status dg_test_gumbel(const uint32_t *w, int32_t n, int32_t mode, float *out, void *stream);
 /* Plain device copy of `bytes` bytes (multiple of 16) used to calibrate
  * memory-traffic counters. */
 dg_status dg_test_copy(const void *src, void *dst, size_t bytes, void *stream);

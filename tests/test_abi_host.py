@@ -38,7 +38,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert B.dg_abi_version() == 1
+    assert B.dg_abi_version() == 2
     for s in range(6):
         assert lib.dg_status_string(s)
 
@@ -87,6 +87,20 @@ def test_bad_enums(lib):
     cfg = cfg_of(2)
     cfg.accept_rule = 9
     assert B.dg_validate_config(cfg) == B.DG_ERR_INVALID_ARG
+    cfg = cfg_of(2)
+    cfg.candidate_rule = 2
+    assert B.dg_validate_config(cfg) == B.DG_ERR_INVALID_ARG
+    cfg.candidate_rule = B.DG_CANDIDATE_MULTINOMIAL
+    assert B.dg_validate_config(cfg) == B.DG_OK
+    # the draw needs no buffer of its own: sizes do not depend on the rule
+    assert B.dg_stats_bytes(cfg) == B.dg_stats_bytes(cfg_of(2))
+    assert B.dg_workspace_bytes(cfg, 0) == B.dg_workspace_bytes(cfg_of(2), 0)
+
+
+def test_gumbel_export_rejects_bad_arguments(lib):
+    assert lib.dg_test_gumbel(None, 4, 1, None, None) == B.DG_ERR_INVALID_ARG
+    assert lib.dg_test_gumbel(FAKE, 4, 2, FAKE, None) == B.DG_ERR_INVALID_ARG
+    assert lib.dg_test_gumbel(FAKE, -1, 0, FAKE, None) == B.DG_ERR_INVALID_ARG
 
 
 FAKE = 0x10000  # a non-null address; validation must fail before it is used

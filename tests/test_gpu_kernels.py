@@ -35,6 +35,29 @@ def test_philox_matches_oracle_and_kat():
         np.testing.assert_array_equal(got[i], oracle.philox4x32_10(ctr[i], key))
 
 
+def test_multinomial_pieces_bit_exact():
+    """The multinomial draw's single-precision log and Gumbel transform on the
+    device equal the oracle's bit for bit (random words and edge values)."""
+    rng = np.random.default_rng(3)
+    words = np.concatenate([rng.integers(0, 2**32, 20000, dtype=np.uint64).astype(np.uint32),
+                            np.array([0, 1, 511, 512, 513, 2**31, 2**32 - 512, 2**32 - 1], np.uint32)])
+    # positive normal floats for the log: random exponents and mantissas, plus edges
+    xs = np.concatenate([
+        (rng.integers(1, 255, 20000, dtype=np.uint64).astype(np.uint32) << 23)
+        | rng.integers(0, 2**23, 20000, dtype=np.uint64).astype(np.uint32),
+        np.array([1.0, 2.0, 0.5, 1.4142135, 1.4142137, 0.70710677, 1.1754944e-38, 3.4028235e38,
+                  5.9604645e-8, 0.99999994, 16.635532], np.float32).view(np.uint32)])
+    for mode, src in ((1, words), (0, xs)):
+        n = src.size
+        w = torch.from_numpy(src.view(np.int32).copy()).cuda()
+        out = torch.zeros(n, dtype=torch.float32, device="cuda")
+        B.dg_test_gumbel(w, n, mode, out)
+        got = out.cpu().numpy()
+        fn = oracle.gumbel_f32 if mode == 1 else (lambda b: oracle.ln_f32(np.uint32(b).view(np.float32)))
+        ref = np.array([fn(int(b)) for b in src], np.float32)
+        np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("N,V", [(16, 512), (128, 262144), (256, 32768)])
 def test_canvas_init_matches_oracle(N, V):
     c = dict(N=N, V=V, d=1024, Hq=8, Hkv=8, hd=128, F=1024, dtype="bf16")

@@ -216,6 +216,56 @@ def test_full_size_step_sampled(cfg_id):
         stable = fl["stable"]
 
 
+def multinomial_steps(c, inp, nsteps, cid=5, den=None):
+    """Steps under the multinomial candidate rule ([P3] §5.3): each step's
+    candidates equal the oracle's two-level Gumbel-max draw replayed on the
+    step's own tile statistics and stored weights, bit for bit, and the
+    selection replays on them.  Returns the number of rows whose candidate
+    differs from the argmax."""
+    den = den or D.Denoiser(c, inp, candidate_rule=B.DG_CANDIDATE_MULTINOMIAL)
+    cfg = den.cfg
+    N = c["N"]
+    seed = W.canvas_seed(c.get("id", 0))
+    den.init_canvas(seed, cid)
+    stable, differ = 0, 0
+    for s in range(nsteps):
+        T = D.temperature(c["sched"], c["T0"], c["T1"], s, c["steps"])
+        tokens_in = den.canvas.tokens.cpu().numpy()
+        den.step(T, c["gamma"])
+        torch.cuda.synchronize()
+        zmax, l, _, tcol = (t.cpu().numpy() for t in den.canvas.tile_stats(cfg))
+        wgt = den.canvas.weights(cfg).cpu().numpy()
+        inv_T = np.float32(1.0) / np.float32(T)
+        cand = oracle.multinomial_candidates(zmax, l, wgt, inv_T, seed, s, cid, np.full(N, -1, np.int32))
+        gpu = den.canvas.argmax.cpu().numpy()
+        np.testing.assert_array_equal(gpu, cand, err_msg=f"step {s}")
+        # the argmax from the same statistics (lowest column among equal maxima)
+        for r in range(N):
+            best = np.flatnonzero(zmax[r] == zmax[r].max())
+            differ += int(cand[r] != tcol[r, best].min())
+        fl = replay_select(den, tokens_in, stable, s, c["gamma"], 0)
+        stable = fl["stable"]
+    return differ
+
+
+def test_config1_fp32_multinomial_draw_replays():
+    c = W.config(1)
+    differ = multinomial_steps(c, W.make_inputs(c), c["steps"])
+    assert differ > c["N"]          # T = 1 over 512 tokens: the draw mostly differs from the argmax
+
+
+def test_config2_bf16_multinomial_draw_replays():
+    c = W.config(2)
+    differ = multinomial_steps(c, W.make_inputs(c), 4)
+    assert differ > 0
+
+
+def test_full_size_multinomial_draw_replays():
+    """V = 262144, d = 2816, 256 rows: two steps (the second self-conditioned)."""
+    c = W.config(3)
+    multinomial_steps(c, W.make_inputs(c), 2)
+
+
 def test_determinism_bitwise():
     c = W.config(2)
     inp = W.make_inputs(c)

@@ -23,6 +23,7 @@ c_i32, c_u32, c_u64, c_f32, c_sz, vp = (ctypes.c_int32, ctypes.c_uint32, ctypes.
 DG_OK, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_CAPACITY, DG_ERR_WORKSPACE, DG_ERR_HIP = range(6)
 DG_F32, DG_BF16 = 0, 1
 DG_ACCEPT_SUM_MINUS_MAX, DG_ACCEPT_CUMSUM = 0, 1
+DG_CANDIDATE_ARGMAX, DG_CANDIDATE_MULTINOMIAL = 0, 1
 DG_STATUS_WORDS = 16
 (DG_ST_ALLCONF, DG_ST_CHANGED, DG_ST_STABLE, DG_ST_ACCEPTED, DG_ST_NAN, DG_ST_STEP, DG_ST_HMIN,
  DG_ST_HMAX, DG_ST_HMEAN) = range(9)
@@ -32,7 +33,7 @@ TILE_V = 64  # vocabulary columns per softmax-statistics tile
 class dg_config(ctypes.Structure):
     _fields_ = [("canvas_len", c_i32), ("vocab", c_i32), ("d_model", c_i32), ("n_q_heads", c_i32),
                 ("n_kv_heads", c_i32), ("head_dim", c_i32), ("ffn_hidden", c_i32), ("dtype", c_i32),
-                ("rms_eps", c_f32), ("conf_eps", c_f32), ("accept_rule", c_i32)]
+                ("rms_eps", c_f32), ("conf_eps", c_f32), ("accept_rule", c_i32), ("candidate_rule", c_i32)]
 
 
 class dg_weights(ctypes.Structure):
@@ -84,6 +85,7 @@ SIGNATURES = {
     "dg_test_selfcond": (c_i32, [P(dg_config), P(dg_weights), vp, vp, vp, c_sz, vp]),
     "dg_test_select": (c_i32, [P(dg_config), P(dg_canvas), c_f32, vp]),
     "dg_test_philox": (c_i32, [vp, c_u32, c_u32, vp, c_i32, vp]),
+    "dg_test_gumbel": (c_i32, [vp, c_i32, c_i32, vp, vp]),
     "dg_test_copy": (c_i32, [vp, vp, c_sz, vp]),
     "dg_profile_enable": (None, [c_i32]),
     "dg_profile_read": (c_i32, [P(c_f32), P(c_i32), P(c_f32), P(c_i32)]),
@@ -237,6 +239,10 @@ def dg_test_philox(ctr: torch.Tensor, k0: int, k1: int, out: torch.Tensor, n: in
     _check("dg_test_philox", lib().dg_test_philox(_ptr(ctr), k0, k1, _ptr(out), n, _stream(stream)))
 
 
+def dg_test_gumbel(w: torch.Tensor, n: int, mode: int, out: torch.Tensor, stream=None) -> None:
+    _check("dg_test_gumbel", lib().dg_test_gumbel(_ptr(w), n, mode, _ptr(out), _stream(stream)))
+
+
 def dg_test_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None) -> None:
     _check("dg_test_copy", lib().dg_test_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
@@ -257,10 +263,10 @@ def dg_profile_read():
 # device-side holders (torch allocations wrapped in the C structs)
 # ---------------------------------------------------------------------------
 def make_config(c: dict, accept_rule: int = DG_ACCEPT_SUM_MINUS_MAX,
-                conf_eps: float = 0.005) -> dg_config:
+                conf_eps: float = 0.005, candidate_rule: int = DG_CANDIDATE_ARGMAX) -> dg_config:
     return dg_config(c["N"], c["V"], c["d"], c["Hq"], c["Hkv"], c["hd"], c["F"],
                      DG_BF16 if c["dtype"] == "bf16" else DG_F32, c.get("rms_eps", 1e-6),
-                     conf_eps, accept_rule)
+                     conf_eps, accept_rule, candidate_rule)
 
 
 def torch_dtype(cfg: dg_config):
@@ -366,6 +372,23 @@ class DeviceCanvas:
             e = self.stats[base:base + nt * 256].view(nt, 256)[:, :N].t().float()
             return torch.exp2(-e) * g.unsqueeze(1)
         return self.stats[N * nt * 16:N * nt * 20].view(torch.float32).view(N, nt)
+
+    def tile_stats(self, cfg: dg_config):
+        """The last step's per-(row, 64-column tile) statistics as stored:
+        (zmax, l = sum e^(y - m), s = sum e^(y - m)(y - m), argmax column),
+        float32 [N][V/64] each (the argmax as int32)."""
+        N, nt = cfg.canvas_len, cfg.vocab // TILE_V
+        t = self.stats[:N * nt * 16].view(torch.float32).view(N, nt, 4)
+        return t[..., 0], t[..., 1], t[..., 2], t[..., 3].contiguous().view(torch.int32)
+
+    def weights(self, cfg: dg_config) -> torch.Tensor:
+        """The stored per-column weights as float32 [N][V] (row-major): the
+        bf16 numerators (probabilities up to a factor per (row, tile)) or the
+        fp32 configuration's probabilities."""
+        N, V = cfg.canvas_len, cfg.vocab
+        if cfg.dtype == DG_BF16:
+            return tiled_to_rows(self.probs.view(torch.bfloat16), N, V).float()
+        return self.probs.view(torch.float32).view(N, V)
 
     def top(self, cfg: dg_config):
         """Each row's dominant token and its exact probability (last step)."""

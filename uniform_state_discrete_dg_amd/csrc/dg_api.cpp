@@ -34,6 +34,8 @@ dg_status check_config(const dg_config *c) {
   if (c->dtype != DG_F32 && c->dtype != DG_BF16) return DG_ERR_INVALID_ARG;
   if (c->accept_rule != DG_ACCEPT_SUM_MINUS_MAX && c->accept_rule != DG_ACCEPT_CUMSUM)
     return DG_ERR_INVALID_ARG;
+  if (c->candidate_rule != DG_CANDIDATE_ARGMAX && c->candidate_rule != DG_CANDIDATE_MULTINOMIAL)
+    return DG_ERR_INVALID_ARG;
   if (c->canvas_len < 1 || c->vocab < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
       c->head_dim < 1 || c->ffn_hidden < 1)
     return DG_ERR_INVALID_ARG;
@@ -577,6 +579,15 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
                            nullptr, d, top, s));
     DG_TRY(dg::normalize_probs_f32(static_cast<float *>(cv->probs), tscale, N, V, s));
   }
+  // [P3] §5.3 multinomial candidates, drawn from the probabilities as kept
+  if (cfg->candidate_rule == DG_CANDIDATE_MULTINOMIAL) {
+    dg::DrawArgs draw{cv->seed, (uint32_t)cv->step, cv->canvas_id, nullptr, nullptr};
+    if (bf)
+      draw.num_tiled = static_cast<const uint16_t *>(cv->probs);
+    else
+      draw.num_f32 = static_cast<const float *>(cv->probs);
+    DG_TRY(dg::multinomial_draw(tstats, N, ntiles, inv_T, draw, cv->argmax, s));
+  }
   // 5. accept / re-noise / stop flags
   DG_TRY(dg::select_step(cv->entropy, cv->argmax, cv->tokens, cv->accept, cv->status, N, ilog2(V), (double)gamma,
                          (int)cfg->accept_rule, cfg->conf_eps, cv->seed, cv->canvas_id, (uint32_t)cv->step, s));
@@ -743,6 +754,12 @@ dg_status dg_test_select(const dg_config *cfg, dg_canvas *cv, float gamma, void 
 dg_status dg_test_philox(const uint32_t *ctr, uint32_t k0, uint32_t k1, uint32_t *out, int32_t n, void *stream) {
   if (n < 0 || (n > 0 && (!ctr || !out))) return DG_ERR_INVALID_ARG;
   DG_TRY(dg::philox_test(ctr, k0, k1, out, n, static_cast<hipStream_t>(stream)));
+  return DG_OK;
+}
+
+dg_status dg_test_gumbel(const uint32_t *w, int32_t n, int32_t mode, float *out, void *stream) {
+  if (n < 0 || (mode != 0 && mode != 1) || (n > 0 && (!w || !out))) return DG_ERR_INVALID_ARG;
+  DG_TRY(dg::gumbel_test(w, n, mode, out, static_cast<hipStream_t>(stream)));
   return DG_OK;
 }
 

@@ -97,6 +97,65 @@ __device__ __forceinline__ int32_t uniform_token(uint64_t seed, uint32_t pos, ui
   return (int32_t)(o.v[0] >> (32 - log2v));
 }
 
+// Multinomial candidate ([P3] §5.3: the token is drawn from the tempered
+// softmax) by Gumbel-max: argmax_v (ln w_v + G_v) with independent standard
+// Gumbel G_v draws v with probability w_v / sum w.  Everything below is
+// single precision with every operation rounded on its own (no fused
+// multiply-add: contraction is off in these bodies; the division is the
+// correctly rounded one), so the draw is a fixed function of its float
+// inputs and reproduces bit for bit.
+//
+// Natural log of a positive normal float: x = m 2^e with m folded into
+// (sqrt(1/2), sqrt(2)], ln m = 2 atanh(s), s = (m - 1) / (m + 1), by the odd
+// series to the s^9 term (|s| <= 0.1716), and e ln 2 with ln 2 split so that
+// e times the high part is exact.
+__device__ __forceinline__ float ln_fixed(float x) {
+#pragma clang fp contract(off)
+  const uint32_t b = __float_as_uint(x);
+  int e = (int)((b >> 23) & 0xFFu) - 127;
+  float m = __uint_as_float((b & 0x7FFFFFu) | 0x3F800000u);
+  if (m > 1.41421353816986083984375f) {  // the float nearest sqrt(2)
+    m = m * 0.5f;
+    e = e + 1;
+  }
+  const float f = m - 1.0f;
+  const float s = f / (2.0f + f);
+  const float z = s * s;
+  const float P = z * (0.666666686534881591796875f +                  // float(2/3)
+                       z * (0.4000000059604644775390625f +            // float(2/5)
+                            z * (0.2857142984867095947265625f +       // float(2/7)
+                                 z * 0.2222222238779067993164062f)));  // float(2/9)
+  const float lnm = (s + s) + s * P;
+  const float ef = (float)e;
+  return ef * 0.693145751953125f + (ef * 1.42860676533018704e-6f + lnm);  // ln 2 = hi + lo
+}
+
+// Standard Gumbel variable of a 32-bit random word: u = (2 floor(w/512) + 1)
+// 2^-24, exact in float and inside (0, 1); G = -ln(-ln u).
+__device__ __forceinline__ float gumbel_word(uint32_t w) {
+#pragma clang fp contract(off)
+  const float u = (float)(2u * (w >> 9) + 1u) * 5.9604644775390625e-8f;
+  return -ln_fixed(-ln_fixed(u));
+}
+
+// Gumbel-max keys of weights given in the linear domain; a weight that is
+// not a positive finite normal float (zero, subnormal, inf, NaN) gets -inf
+// and is never drawn.
+//   tile level: fl(fl(ln l + fl(zmax inv_T)) + G(word))  (mass l e^{zmax inv_T})
+//   column level: fl(ln w + G(word))
+__device__ __forceinline__ float gumbel_key_tile(float l, float zmax, float inv_T, uint32_t word) {
+#pragma clang fp contract(off)
+  if (!(l >= 1.17549435e-38f && l <= 3.40282347e38f)) return -INFINITY;
+  const float m = zmax * inv_T;
+  const float lx = ln_fixed(l) + m;
+  return lx + gumbel_word(word);
+}
+__device__ __forceinline__ float gumbel_key_col(float w, uint32_t word) {
+#pragma clang fp contract(off)
+  if (!(w >= 1.17549435e-38f && w <= 3.40282347e38f)) return -INFINITY;
+  return ln_fixed(w) + gumbel_word(word);
+}
+
 __device__ __forceinline__ float warp_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -128,16 +128,34 @@ hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E
 // Same statistics from fp32 logits already in memory (fp32 path).
 hipError_t tile_stats_f32(const float *logits, int M, int V, float inv_T, float *probs,
                           float4 *tile_stats, hipStream_t s);
+// Multinomial draw of one step: the canvas's Philox key and counter words,
+// and the stored weights the second level reads (one of the two pointers).
+struct DrawArgs {
+  uint64_t seed;
+  uint32_t step, canvas;
+  const uint16_t *num_tiled;  // bf16 path: numerators in the tiled layout [256][V]
+  const float *num_f32;       // fp32 path: the normalised probabilities, row-major [M][V]
+};
 // Row combine: entropy (nats), argmax, and the factors that turn the stored
 // numerators into probabilities.  shift == nullptr (numerators exp(y - m_t)):
 // tile_scale[row][t] = exp(m_t - M_row) / L_row.  shift given (numerators
 // relative to 2^r_t, M <= 256): p = stored * 2^-shift[t][row] * row_scale[row]
 // and tile_scale (nullable) = 2^-shift * row_scale.  With n2 (fp32 [M][d],
 // d <= 4096) and E given, the argmax token's logit is recomputed exactly and
-// top[row] = (argmax as int bits, its exact probability).
+// top[row] = (argmax as int bits, its exact probability).  cand receives
+// the argmax (the candidate token unless a multinomial draw follows).
 hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,
-                       int32_t *argmax, float *tile_scale, float *row_scale, uint8_t *shift, const float *n2,
+                       int32_t *cand, float *tile_scale, float *row_scale, uint8_t *shift, const float *n2,
                        const uint16_t *E, int d, float2 *top, hipStream_t s);
+// Multinomial draw of the candidate tokens (two Gumbel-max levels over the
+// tile statistics and the stored weights, dg_device.h), run once the step's
+// probabilities are final; cand holds the argmax and keeps it for a row with
+// nothing drawable.  Exactly one of draw.num_tiled / draw.num_f32 is set.
+hipError_t multinomial_draw(const float4 *tile_stats, int M, int ntiles, float inv_T, const DrawArgs &draw,
+                            int32_t *cand, hipStream_t s);
+// Test export: out[i] = ln_fixed(bits of w[i]) (mode 0) or gumbel_word(w[i])
+// (mode 1), the multinomial draw's single-precision pieces.
+hipError_t gumbel_test(const uint32_t *w, int n, int mode, float *out, hipStream_t s);
 
 // Attention over two key segments [A: nA keys][B: nB keys] per KV head, all
 // fp32 in memory.  q: [Hq][nq][hd]; k/v segment X: base + (g * capX + j) * hd.

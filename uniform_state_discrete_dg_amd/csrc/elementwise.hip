@@ -298,6 +298,17 @@ hipError_t tile_stats_f32(const float *logits, int M, int V, float inv_T, float 
   return hipGetLastError();
 }
 
+__global__ void gumbel_test_kernel(const uint32_t *__restrict__ w, int n, int mode, float *__restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = mode == 0 ? ln_fixed(__uint_as_float(w[i])) : gumbel_word(w[i]);
+}
+
+hipError_t gumbel_test(const uint32_t *w, int n, int mode, float *out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gumbel_test_kernel, dim3((n + 255) / 256), dim3(256), 0, s, w, n, mode, out);
+  return hipGetLastError();
+}
+
 // Reductions over the 256 threads of a row: within each wave by lane
 // exchanges, then across the 4 waves through LDS (two barriers).
 __device__ __forceinline__ float rc_sum(float v, float *sh) {
@@ -376,7 +387,7 @@ constexpr int RC_CACHE = 16;
 template <bool CACHED>
 __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restrict__ stats, int ntiles,
                                                           float inv_T, float *__restrict__ entropy,
-                                                          int32_t *__restrict__ argmax,
+                                                          int32_t *__restrict__ cand,
                                                           float *__restrict__ tile_scale,
                                                           float *__restrict__ row_scale, uint8_t *__restrict__ shift,
                                                           const float *__restrict__ n2, const bf16 *__restrict__ E,
@@ -421,12 +432,15 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
   }
   rc_argmax(best, bidx, shv, shi);
   const float Mz = best;
-  const int amax = bidx;
+  // every tile maximum NaN (a NaN hidden state): no argmax; token 0 stands in
+  // and nothing is recomputed (the entropy comes out NaN)
+  const bool found = bidx < ntiles * TILE;
+  const int amax = found ? bidx : 0;
   const float My = Mz * inv_T;
   const int ta = amax / TILE;
   // corrected terms of the argmax token inside its tile (reference m_ta = My)
   float l_fix = 0.f, s_fix = 0.f, d_top = 0.f;
-  if (fix) {
+  if (fix && found) {
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < RC_D; ++i) {
@@ -480,22 +494,85 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
     float H = logf(L) - S * invL;
     if (H <= 0.f) H = 0.f;
     entropy[row] = H;
-    argmax[row] = amax;
+    cand[row] = amax;
     if (top) top[row] = make_float2(__int_as_float(amax), exp2f(d_top * LOG2E) * invL);
     if (row_scale) row_scale[row] = g;
   }
 }
 
 hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,
-                       int32_t *argmax, float *tile_scale, float *row_scale, uint8_t *shift, const float *n2,
+                       int32_t *cand, float *tile_scale, float *row_scale, uint8_t *shift, const float *n2,
                        const uint16_t *E, int d, float2 *top, hipStream_t s) {
   if ((shift && M > 256) || (n2 && d > 256 * 16)) return hipErrorInvalidValue;
   if (ntiles <= 256 * RC_CACHE)
     hipLaunchKernelGGL(row_combine_kernel<true>, dim3(M), dim3(256), 0, s, tile_stats, ntiles, inv_T, entropy,
-                       argmax, tile_scale, row_scale, shift, n2, E, d, top);
+                       cand, tile_scale, row_scale, shift, n2, E, d, top);
   else
     hipLaunchKernelGGL(row_combine_kernel<false>, dim3(M), dim3(256), 0, s, tile_stats, ntiles, inv_T, entropy,
-                       argmax, tile_scale, row_scale, shift, n2, E, d, top);
+                       cand, tile_scale, row_scale, shift, n2, E, d, top);
+  return hipGetLastError();
+}
+
+// Multinomial candidate ([P3] §5.3: the token is drawn from the tempered
+// softmax), drawn from the distribution the step keeps in two Gumbel-max
+// levels (dg_device.h), one workgroup per canvas row:
+//   the tile t, by the largest fl(fl(ln l_t + zmax_t inv_T) + G), G from word
+//   t%4 of Philox(seed; row, step, canvas, 2 + 4 floor(t/4)): l_t e^{m_t} is
+//   the tile's mass up to a factor common to the row;
+//   then the column c of that tile, by the largest fl(ln w_c + G'), G' from
+//   word c%4 of Philox(seed; row, step, canvas, 3 + 4 floor(c/4)), w_c the
+//   stored weight (bf16 numerator, or the fp32 path's probability), which is
+//   e^{y_c} up to a factor common to the tile.
+// Lowest index on equal keys; a NaN key never wins.  cand holds the argmax on
+// entry and keeps it when nothing is drawable.
+__global__ void __launch_bounds__(256) draw_kernel(const float4 *__restrict__ stats, int ntiles, float inv_T,
+                                                   DrawArgs draw, int32_t *__restrict__ cand) {
+  __shared__ float shv[8];
+  __shared__ int shi[4];
+  const int row = blockIdx.x;
+  const uint32_t k0 = (uint32_t)draw.seed, k1 = (uint32_t)(draw.seed >> 32);
+  const float4 *st = stats + (int64_t)row * ntiles;
+  float kb = -INFINITY;
+  int kt = INT32_MAX;
+  for (int t = threadIdx.x; t < ntiles; t += 256) {  // ascending tiles per thread
+    const float4 v = st[t];
+    const Philox4 w = philox4x32_10((uint32_t)row, draw.step, draw.canvas, 2u + 4u * ((uint32_t)t >> 2), k0, k1);
+    const float k = gumbel_key_tile(v.y, v.x, inv_T, w.v[t & 3]);
+    if (k > kb) {
+      kb = k;
+      kt = t;
+    }
+  }
+  rc_argmax(kb, kt, shv, shi);
+  if (kt == INT32_MAX || threadIdx.x >= 64) return;
+  // one wave: lane c = column c of tile kt
+  const int c = threadIdx.x;
+  float wgt;
+  if (draw.num_tiled)  // slice 2 kt + c / 32, chunk (c % 32) / 8 of the row, element c % 8
+    wgt = bf16_to_f32(draw.num_tiled[(int64_t)(2 * kt + (c >> 5)) * TL_ELEMS + tl_pos(row, (c & 31) >> 3) * 8 +
+                                     (c & 7)]);
+  else
+    wgt = draw.num_f32[(int64_t)row * ntiles * TILE + (int64_t)kt * TILE + c];
+  const Philox4 w = philox4x32_10((uint32_t)row, draw.step, draw.canvas, 3u + 4u * ((uint32_t)c >> 2), k0, k1);
+  float kc = gumbel_key_col(wgt, w.v[c & 3]);
+  int cc = kc > -INFINITY ? c : INT32_MAX;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(kc, o);
+    const int oc = __shfl_xor(cc, o);
+    if (ov > kc || (ov == kc && oc < cc)) {
+      kc = ov;
+      cc = oc;
+    }
+  }
+  if (c == 0 && cc != INT32_MAX) cand[row] = kt * TILE + cc;
+}
+
+hipError_t multinomial_draw(const float4 *tile_stats, int M, int ntiles, float inv_T, const DrawArgs &draw,
+                            int32_t *cand, hipStream_t s) {
+  if ((draw.num_tiled == nullptr) == (draw.num_f32 == nullptr) || (draw.num_tiled && M > 256))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(draw_kernel, dim3(M), dim3(256), 0, s, tile_stats, ntiles, inv_T, draw, cand);
   return hipGetLastError();
 }
 

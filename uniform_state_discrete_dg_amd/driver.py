@@ -45,9 +45,9 @@ class Denoiser:
 
     def __init__(self, c: dict, inp: dict, capacity: int | None = None, max_prefill: int = 0,
                  accept_rule: int = B.DG_ACCEPT_SUM_MINUS_MAX, device="cuda",
-                 logits_dump: bool = False):
+                 logits_dump: bool = False, candidate_rule: int = B.DG_CANDIDATE_ARGMAX):
         self.c = c
-        self.cfg = B.make_config(c, accept_rule=accept_rule)
+        self.cfg = B.make_config(c, accept_rule=accept_rule, candidate_rule=candidate_rule)
         st = B.dg_validate_config(self.cfg)
         if st != B.DG_OK:
             raise B.DgError("dg_validate_config", st)
