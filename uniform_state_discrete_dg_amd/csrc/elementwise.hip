@@ -525,26 +525,56 @@ hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T,
 //   e^{y_c} up to a factor common to the tile.
 // Lowest index on equal keys; a NaN key never wins.  cand holds the argmax on
 // entry and keeps it when nothing is drawable.
-__global__ void __launch_bounds__(256) draw_kernel(const float4 *__restrict__ stats, int ntiles, float inv_T,
-                                                   DrawArgs draw, int32_t *__restrict__ cand) {
-  __shared__ float shv[8];
-  __shared__ int shi[4];
+// 1024 threads per row; thread k owns tiles 4k .. 4k+3 (and every 4096th
+// after), whose noise is the four words of one Philox block.
+constexpr int DRAW_NT = 1024;
+__global__ void __launch_bounds__(DRAW_NT) draw_kernel(const float4 *__restrict__ stats, int ntiles, float inv_T,
+                                                       DrawArgs draw, int32_t *__restrict__ cand) {
+  __shared__ float shv[DRAW_NT / 64];
+  __shared__ int shi[DRAW_NT / 64];
   const int row = blockIdx.x;
   const uint32_t k0 = (uint32_t)draw.seed, k1 = (uint32_t)(draw.seed >> 32);
   const float4 *st = stats + (int64_t)row * ntiles;
   float kb = -INFINITY;
   int kt = INT32_MAX;
-  for (int t = threadIdx.x; t < ntiles; t += 256) {  // ascending tiles per thread
-    const float4 v = st[t];
-    const Philox4 w = philox4x32_10((uint32_t)row, draw.step, draw.canvas, 2u + 4u * ((uint32_t)t >> 2), k0, k1);
-    const float k = gumbel_key_tile(v.y, v.x, inv_T, w.v[t & 3]);
-    if (k > kb) {
-      kb = k;
-      kt = t;
+  for (int t0 = 4 * threadIdx.x; t0 < ntiles; t0 += 4 * DRAW_NT) {  // ascending tiles per thread
+    const Philox4 w = philox4x32_10((uint32_t)row, draw.step, draw.canvas, 2u + (uint32_t)t0, k0, k1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = st[t0 + j];
+      const float k = gumbel_key_tile(v.y, v.x, inv_T, w.v[j]);
+      if (k > kb) {
+        kb = k;
+        kt = t0 + j;
+      }
     }
   }
-  rc_argmax(kb, kt, shv, shi);
-  if (kt == INT32_MAX || threadIdx.x >= 64) return;
+  // largest key, lowest tile on ties: within each wave, then across the 16 waves
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(kb, o);
+    const int i2 = __shfl_xor(kt, o);
+    if (v2 > kb || (v2 == kb && i2 < kt)) {
+      kb = v2;
+      kt = i2;
+    }
+  }
+  if ((threadIdx.x & 63) == 0) {
+    shv[threadIdx.x >> 6] = kb;
+    shi[threadIdx.x >> 6] = kt;
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  kb = shv[0];
+  kt = shi[0];
+#pragma unroll
+  for (int w = 1; w < DRAW_NT / 64; ++w)
+    if (shv[w] > kb || (shv[w] == kb && shi[w] < kt)) {
+      kb = shv[w];
+      kt = shi[w];
+    }
+  if (kt == INT32_MAX) return;
+
   // one wave: lane c = column c of tile kt
   const int c = threadIdx.x;
   float wgt;
@@ -570,9 +600,9 @@ __global__ void __launch_bounds__(256) draw_kernel(const float4 *__restrict__ st
 
 hipError_t multinomial_draw(const float4 *tile_stats, int M, int ntiles, float inv_T, const DrawArgs &draw,
                             int32_t *cand, hipStream_t s) {
-  if ((draw.num_tiled == nullptr) == (draw.num_f32 == nullptr) || (draw.num_tiled && M > 256))
+  if ((draw.num_tiled == nullptr) == (draw.num_f32 == nullptr) || (draw.num_tiled && M > 256) || ntiles % 4)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(draw_kernel, dim3(M), dim3(256), 0, s, tile_stats, ntiles, inv_T, draw, cand);
+  hipLaunchKernelGGL(draw_kernel, dim3(M), dim3(DRAW_NT), 0, s, tile_stats, ntiles, inv_T, draw, cand);
   return hipGetLastError();
 }
 
