@@ -74,7 +74,7 @@ def lib():
         L.orc_attention.argtypes = [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                     _c_i32, _c_i32, _c_i32, _vp]
         L.orc_select.argtypes = [_c_i32, _c_i32, _vp, _vp, _vp, _c_dbl, _c_i32, _c_u64,
-                                 _c_u32, _c_u32, _c_i32, _c_dbl, _vp, _vp, _vp]
+                                 _c_u32, _c_u32, _c_i32, _c_dbl, _c_i32, _vp, _vp, _vp]
         L.orc_denoise_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_dbl,
                                           _vp, _vp]
         L.orc_denoise_forward.restype = ctypes.c_int
@@ -128,8 +128,11 @@ def uniform_token(seed: int, pos: int, step: int, canvas_id: int, stream: int, V
     return int(lib().orc_uniform_token(seed, pos, step, canvas_id, stream, V))
 
 
-def canvas_init(seed: int, canvas_id: int, N: int, V: int) -> np.ndarray:
-    """[P3] §5.4 canvas initialisation: uniform tokens from Philox stream 0."""
+def canvas_init(seed: int, canvas_id: int, N: int, V: int, masked: bool = False) -> np.ndarray:
+    """[P3] §5.4 canvas initialisation: uniform tokens from Philox stream 0;
+    the masked sampler ([P3] §3.1) starts from [MASK] (id V) everywhere."""
+    if masked:
+        return np.full(N, V, dtype=np.int32)
     out = np.zeros(N, dtype=np.int32)
     lib().orc_canvas_init(seed, canvas_id, N, V, _p(out))
     return out
@@ -227,15 +230,19 @@ ACCEPT_CUMSUM = 1
 
 class _Flags(ctypes.Structure):
     _fields_ = [("allconf", _c_i32), ("changed", _c_i32), ("stable", _c_i32),
-                ("accepted", _c_i32)]
+                ("accepted", _c_i32), ("masked", _c_i32)]
 
 
 def select(H, argmax_tokens, tokens_in, V: int, gamma: float, rule: int, seed: int,
-           canvas_id: int, step: int, stable_in: int, conf_eps: float = 0.005):
+           canvas_id: int, step: int, stable_in: int, conf_eps: float = 0.005,
+           mask_id: int = -1):
     """[P3] §5.4 entropy-bounded acceptance + re-noise; [P5] stop flags.
 
     H is float32 (the decision is taken in the precision the kernel produces
-    its entropies in).  Returns (accept uint8[N], tokens_out int32[N], flags dict).
+    its entropies in).  mask_id >= 0 selects the masked sampler ([P1] §1,
+    [P3] §3.1): only positions holding mask_id take part; accepted ones lock,
+    rejected ones stay mask_id.  Returns (accept uint8[N], tokens_out int32[N],
+    flags dict).
     """
     Hf = np.ascontiguousarray(H, dtype=np.float32)
     am = _i32(argmax_tokens)
@@ -245,13 +252,15 @@ def select(H, argmax_tokens, tokens_in, V: int, gamma: float, rule: int, seed: i
     tout = np.zeros(N, dtype=np.int32)
     fl = _Flags()
     lib().orc_select(N, V, _p(Hf), _p(am), _p(tin), float(gamma), int(rule), seed, canvas_id,
-                     step, stable_in, float(conf_eps), _p(acc), _p(tout), ctypes.byref(fl))
-    flags = dict(allconf=fl.allconf, changed=fl.changed, stable=fl.stable, accepted=fl.accepted)
+                     step, stable_in, float(conf_eps), int(mask_id), _p(acc), _p(tout), ctypes.byref(fl))
+    flags = dict(allconf=fl.allconf, changed=fl.changed, stable=fl.stable, accepted=fl.accepted,
+                 masked=fl.masked)
     return acc, tout, flags
 
 
 def should_stop(flags: dict, stable_steps: int) -> bool:
-    fl = _Flags(flags["allconf"], flags["changed"], flags["stable"], flags.get("accepted", 0))
+    fl = _Flags(flags["allconf"], flags["changed"], flags["stable"], flags.get("accepted", 0),
+                flags.get("masked", -1))
     return bool(lib().orc_should_stop(ctypes.byref(fl), stable_steps))
 
 
@@ -271,7 +280,7 @@ class _Model(ctypes.Structure):
     _fields_ = [("N", _c_i32), ("V", _c_i32), ("d", _c_i32), ("Hq", _c_i32), ("Hkv", _c_i32),
                 ("hd", _c_i32), ("F", _c_i32), ("rms_eps", _c_dbl),
                 ("E", _vp), ("w1", _vp), ("w2", _vp), ("wq", _vp), ("wk", _vp), ("wv", _vp),
-                ("wo", _vp), ("g_attn", _vp), ("g_final", _vp)]
+                ("wo", _vp), ("g_attn", _vp), ("g_final", _vp), ("mask_emb", _vp)]
 
 
 class _StepOut(ctypes.Structure):
@@ -284,18 +293,22 @@ class Model:
     """Holds float32 copies of the weights (values as the GPU receives them)."""
 
     def __init__(self, N, V, d, Hq, Hkv, hd, F, E, w1, w2, wq, wk, wv, wo, g_attn, g_final,
-                 rms_eps: float = 1e-6):
+                 rms_eps: float = 1e-6, mask_emb=None):
         self.N, self.V, self.d, self.Hq, self.Hkv, self.hd, self.F = N, V, d, Hq, Hkv, hd, F
         self.rms_eps = rms_eps
         self._arrs = dict(E=_f32(E), w1=_f32(w1), w2=_f32(w2), wq=_f32(wq), wk=_f32(wk),
                           wv=_f32(wv), wo=_f32(wo), g_attn=_f32(g_attn), g_final=_f32(g_final))
+        if mask_emb is not None:       # the [MASK] token's row (id V), masked sampler
+            self._arrs["mask_emb"] = _f32(mask_emb)
+            assert self._arrs["mask_emb"].shape == (d,)
         a = self._arrs
         assert a["E"].shape == (V, d)
         assert a["w1"].shape == (F, d) and a["w2"].shape == (d, F)
         assert a["wq"].shape == (Hq * hd, d) and a["wk"].shape == (Hkv * hd, d)
         assert a["wv"].shape == (Hkv * hd, d) and a["wo"].shape == (d, Hq * hd)
         self._s = _Model(N, V, d, Hq, Hkv, hd, F, rms_eps, *(_p(a[k]) for k in
-                         ("E", "w1", "w2", "wq", "wk", "wv", "wo", "g_attn", "g_final")))
+                         ("E", "w1", "w2", "wq", "wk", "wv", "wo", "g_attn", "g_final")),
+                         _p(a.get("mask_emb")))
 
     @property
     def E(self) -> np.ndarray:
@@ -305,7 +318,7 @@ class Model:
         a = self._arrs
         return Model(N, self.V, self.d, self.Hq, self.Hkv, self.hd, self.F, a["E"], a["w1"],
                      a["w2"], a["wq"], a["wk"], a["wv"], a["wo"], a["g_attn"], a["g_final"],
-                     self.rms_eps)
+                     self.rms_eps, a.get("mask_emb"))
 
     def selfcond_row(self, p_row) -> np.ndarray:
         p = _f64(p_row)
@@ -371,4 +384,4 @@ def model_from_inputs(inp: dict, N: int | None = None) -> Model:
     return Model(N if N is not None else c["N"], c["V"], c["d"], c["Hq"], c["Hkv"], c["hd"],
                  c["F"], f(inp["E"]), f(inp["w1"]), f(inp["w2"]), f(inp["wq"]), f(inp["wk"]),
                  f(inp["wv"]), f(inp["wo"]), f(inp["g_attn"]), f(inp["g_final"]),
-                 c.get("rms_eps", 1e-6))
+                 c.get("rms_eps", 1e-6), f(inp["mask_emb"]) if "mask_emb" in inp else None)

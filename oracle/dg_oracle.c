@@ -82,6 +82,14 @@ void orc_canvas_init(uint64_t seed, uint32_t canvas_id, int32_t N, int32_t V,
 /* ------------------------------------------------------------------------ */
 /* Building blocks                                                           */
 /* ------------------------------------------------------------------------ */
+/* Embedding row of token t: E[t] for a vocabulary token, the [MASK] row for */
+/* t = V when the model has one ([P1] §1, [P3] §3.1); NULL otherwise.        */
+static const float *embed_row(const orc_model *m, int32_t t) {
+  if (t >= 0 && t < m->V) return m->E + (int64_t)t * m->d;
+  if (t == m->V && m->mask_emb) return m->mask_emb;
+  return NULL;
+}
+
 double orc_gelu(double x) { return 0.5 * x * (1.0 + erf(x / sqrt(2.0))); }
 
 void orc_rmsnorm(const double *x, const float *g, int32_t d, double eps, double *out) {
@@ -311,22 +319,26 @@ static uint64_t fixed_point_nats(double x) {
 void orc_select(int32_t N, int32_t V, const float *H, const int32_t *argmax,
                 const int32_t *tokens_in, double gamma, int32_t rule,
                 uint64_t seed, uint32_t canvas_id, uint32_t step,
-                int32_t stable_in, double conf_eps,
+                int32_t stable_in, double conf_eps, int32_t mask_id,
                 uint8_t *accept, int32_t *tokens_out, orc_flags *flags) {
+  /* the positions that take part: all of them, or (masked sampler) those */
+  /* still holding [MASK]                                                  */
   uint64_t *keys = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(N > 0 ? N : 1));
+  int32_t n = 0;
   for (int32_t i = 0; i < N; ++i) {
+    accept[i] = 0;
+    if (mask_id >= 0 && tokens_in[i] != mask_id) continue;
     const float h = clamp_entropy(H[i]);
     uint32_t bits;
     memcpy(&bits, &h, 4);
-    keys[i] = ((uint64_t)bits << 32) | (uint32_t)i;
-    accept[i] = 0;
+    keys[n++] = ((uint64_t)bits << 32) | (uint32_t)i;
   }
-  qsort(keys, (size_t)N, sizeof(uint64_t), cmp_u64);
+  qsort(keys, (size_t)n, sizeof(uint64_t), cmp_u64);
 
   const uint64_t limit = (gamma > 0.0) ? fixed_point_nats(gamma) : 0u;
   uint64_t sum_before = 0; /* sum of q over the positions already accepted */
   int32_t accepted = 0;
-  for (int32_t r = 0; r < N; ++r) {
+  for (int32_t r = 0; r < n; ++r) {
     const int32_t i = (int32_t)(keys[r] & 0xFFFFFFFFu);
     const float h = clamp_entropy(H[i]);
     if (!(h < 1048576.0f)) break; /* NaN, inf or absurd: never accepted */
@@ -341,13 +353,18 @@ void orc_select(int32_t N, int32_t V, const float *H, const int32_t *argmax,
   }
   free(keys);
 
-  int32_t allconf = 1, changed = 0;
+  int32_t allconf = 1, changed = 0, masked = 0;
   for (int32_t i = 0; i < N; ++i) {
-    const int32_t t = accept[i]
-                          ? argmax[i]
-                          : orc_uniform_token(seed, (uint32_t)i, step, canvas_id, 1u, V);
+    int32_t t;
+    if (accept[i])
+      t = argmax[i];
+    else if (mask_id >= 0)
+      t = tokens_in[i]; /* a locked token, or [MASK] staying [MASK] */
+    else
+      t = orc_uniform_token(seed, (uint32_t)i, step, canvas_id, 1u, V);
     tokens_out[i] = t;
     if (t != tokens_in[i]) changed = 1;
+    if (mask_id >= 0 && t == mask_id) ++masked;
     const float h = clamp_entropy(H[i]);
     if (!((double)h < conf_eps)) allconf = 0;
   }
@@ -355,6 +372,7 @@ void orc_select(int32_t N, int32_t V, const float *H, const int32_t *argmax,
   flags->changed = changed;
   flags->stable = changed ? 0 : stable_in + 1;
   flags->accepted = accepted;
+  flags->masked = mask_id >= 0 ? masked : -1;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -383,13 +401,13 @@ int orc_denoise_forward(const orc_model *m, const int32_t *tokens,
   const int32_t qw = Hq * hd, kw = Hkv * hd;
   if (Hq % Hkv != 0 || L < 0 || L > cap || !(T > 0.0)) return -1;
   for (int32_t i = 0; i < N; ++i)
-    if (tokens[i] < 0 || tokens[i] >= V) return -2;
+    if (!embed_row(m, tokens[i])) return -2;
 
   /* 1. token embeddings ([P3] §5.1: the self-conditioning vector is added to */
   /*    the next step's token embeddings).                                     */
   double *h0 = out->h0;
   for (int32_t i = 0; i < N; ++i)
-    for (int32_t k = 0; k < d; ++k) h0[(int64_t)i * d + k] = (double)m->E[(int64_t)tokens[i] * d + k];
+    for (int32_t k = 0; k < d; ++k) h0[(int64_t)i * d + k] = (double)embed_row(m, tokens[i])[k];
 
   /* 2. self-conditioning: p_prev @ E, then a small feed-forward network     */
   /*    (two layers, exact GELU, no biases), added to the embeddings.         */
@@ -507,14 +525,14 @@ int orc_prefill_append(const orc_model *m, const int32_t *tokens, int32_t n,
   const int32_t qw = Hq * hd, kw = Hkv * hd;
   if (n < 0 || L < 0 || L + n > cap || Hq % Hkv != 0) return -1;
   for (int32_t i = 0; i < n; ++i)
-    if (tokens[i] < 0 || tokens[i] >= m->V) return -2;
+    if (!embed_row(m, tokens[i])) return -2;
   if (n == 0) return 0;
   double *x = (double *)malloc(sizeof(double) * (size_t)n * d);
   double *nrm = (double *)malloc(sizeof(double) * (size_t)n * d);
   double *kk = (double *)malloc(sizeof(double) * (size_t)n * kw);
   double *vv = (double *)malloc(sizeof(double) * (size_t)n * kw);
   for (int32_t i = 0; i < n; ++i) {
-    for (int32_t k = 0; k < d; ++k) x[(int64_t)i * d + k] = (double)m->E[(int64_t)tokens[i] * d + k];
+    for (int32_t k = 0; k < d; ++k) x[(int64_t)i * d + k] = (double)embed_row(m, tokens[i])[k];
     orc_rmsnorm(x + (int64_t)i * d, m->g_attn, d, m->rms_eps, nrm + (int64_t)i * d);
   }
   orc_matmul_nt(nrm, m->wk, n, kw, d, kk);
@@ -567,6 +585,7 @@ double orc_temperature(int32_t kind, double T0, double T1, int32_t s, int32_t S)
 
 int32_t orc_should_stop(const orc_flags *f, int32_t stable_steps) {
   if (f->allconf) return 1;
+  if (f->masked == 0) return 1; /* masked sampler: no [MASK] left */
   if (stable_steps > 0 && f->stable >= stable_steps) return 1;
   return 0;
 }

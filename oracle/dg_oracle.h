@@ -66,6 +66,8 @@ typedef struct {
   const float *wo;      /* [d][Hq*hd]                                        */
   const float *g_attn;  /* [d] RMSNorm gain before attention                 */
   const float *g_final; /* [d] RMSNorm gain before the LM head               */
+  const float *mask_emb; /* [d] embedding of the [MASK] token, id V (masked    */
+                         /* sampler); NULL: the model has no [MASK] token      */
 } orc_model;
 
 /* ---- building blocks (exported so the tests can pin each one) ----------- */
@@ -110,15 +112,21 @@ typedef struct {
   int32_t changed;   /* canvas after != canvas before                          */
   int32_t stable;    /* consecutive unchanged steps                            */
   int32_t accepted;  /* number of accepted positions                           */
+  int32_t masked;    /* [MASK] positions after the step; -1 under re-noise      */
 } orc_flags;
 
 /* Decisions of one step from the per-position entropies H (float, as the
- * kernel produces them) and argmax tokens.  Writes accept[N] (0/1),
- * tokens_out[N] and flags. */
+ * kernel produces them) and candidate tokens.  Writes accept[N] (0/1),
+ * tokens_out[N] and flags.
+ * mask_id < 0: uniform-state sampler -- every position takes part, rejected
+ *   ones are re-noised with a uniform token.
+ * mask_id >= 0: masked sampler ([P1] §1, [P3] §3.1) -- only positions holding
+ *   mask_id take part in the walk; accepted ones take their candidate and
+ *   lock, rejected ones stay mask_id, the others keep their token. */
 void orc_select(int32_t N, int32_t V, const float *H, const int32_t *argmax,
                 const int32_t *tokens_in, double gamma, int32_t rule,
                 uint64_t seed, uint32_t canvas_id, uint32_t step,
-                int32_t stable_in, double conf_eps,
+                int32_t stable_in, double conf_eps, int32_t mask_id,
                 uint8_t *accept, int32_t *tokens_out, orc_flags *flags);
 
 /* ---- one denoising step ---------------------------------------------------- */

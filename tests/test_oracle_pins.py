@@ -371,6 +371,79 @@ def test_select_brute_force_small_N():
                 assert k >= 1
 
 
+def test_masked_select_walks_only_masked_positions():
+    """Masked sampler ([P1] §1, [P3] §3.1): the accept set is the brute-force
+    walk over the masked positions alone (exact rationals); accepted ones take
+    their candidate, rejected ones stay [MASK], every other token is kept."""
+    rng = np.random.default_rng(15)
+    V = 1024
+    for trial in range(300):
+        N = int(rng.integers(1, 13))
+        H = (rng.random(N) * 3).astype(np.float32)
+        if trial % 5 == 0:
+            H[rng.integers(N)] = H[0]
+        tin = rng.integers(0, V, N).astype(np.int32)
+        masked = rng.random(N) < 0.6
+        tin[masked] = V
+        am = rng.integers(0, V, N).astype(np.int32)
+        gamma = float(rng.random() * 4)
+        for rule in (0, 1):
+            acc, tout, fl = oracle.select(H, am, tin, V, gamma, rule, 9, 0, 0, 2, mask_id=V)
+            idx = np.flatnonzero(masked)
+            ref = np.zeros(N, np.uint8)
+            if idx.size:
+                sub = _brute_force_accept(H[idx].tolist(), gamma, rule)
+                if not np.array_equal(acc[idx], sub):
+                    s_ = np.sort(H[idx].astype(np.float64))
+                    sums = np.concatenate([[0.0], np.cumsum(s_)])
+                    assert np.min(np.abs(sums - gamma)) < N * 2.0 ** -32
+                    sub = acc[idx]
+                ref[idx] = sub
+            np.testing.assert_array_equal(acc, ref)
+            np.testing.assert_array_equal(tout, np.where(acc == 1, am, tin))
+            assert fl["masked"] == int((tout == V).sum())
+            assert fl["accepted"] == int(acc.sum())
+            assert fl["changed"] == int((tout != tin).any())
+            if rule == 0 and idx.size:
+                assert acc.sum() >= 1
+    # no [MASK] left: nothing is walked, nothing changes, and the loop stops
+    H = np.array([0.5, 0.1], np.float32)
+    acc, tout, fl = oracle.select(H, np.array([3, 4], np.int32), np.array([1, 2], np.int32), V, 5.0, 0,
+                                  9, 0, 0, 0, mask_id=V)
+    assert not acc.any() and list(tout) == [1, 2] and fl["masked"] == 0 and fl["stable"] == 1
+    assert oracle.should_stop(fl, 0)
+    # the uniform-state sampler reports no count
+    assert oracle.select(H, np.array([3, 4], np.int32), np.array([1, 2], np.int32), V, 5.0, 0,
+                         9, 0, 0, 0)[2]["masked"] == -1
+
+
+def test_masked_sampler_loop_locks_and_terminates():
+    """A loop of masked-sampler steps on random entropies: [MASK] count never
+    grows, a decided token never changes, at least one position resolves per
+    step (sum-minus-max rule), and the stop test fires when none is left."""
+    rng = np.random.default_rng(16)
+    N, V = 40, 512
+    tok = oracle.canvas_init(3, 0, N, V, masked=True)
+    assert (tok == V).all()
+    decided = {}
+    stable, prev_masked = 0, N
+    for step in range(N + 1):
+        H = (rng.random(N) * 4).astype(np.float32)
+        am = rng.integers(0, V, N).astype(np.int32)
+        acc, out, fl = oracle.select(H, am, tok, V, 2.0, 0, 3, 0, step, stable, mask_id=V)
+        for i, t in decided.items():
+            assert out[i] == t
+        for i in np.flatnonzero(out != V):
+            decided.setdefault(int(i), int(out[i]))
+        assert fl["masked"] <= prev_masked
+        if prev_masked:
+            assert fl["masked"] < prev_masked
+        prev_masked, stable, tok = fl["masked"], fl["stable"], out
+        if oracle.should_stop(fl, 0):
+            break
+    assert prev_masked == 0 and (tok < V).all()
+
+
 def test_select_exhaustive_over_all_subsets_tiny():
     """For N <= 6, among ALL subsets that satisfy the bound and are closed under
     'lower (H, index) first', the oracle returns the largest one."""
@@ -412,7 +485,7 @@ def test_select_renoise_and_flags():
     # every position accepted with argmax == canvas: unchanged, stable counter grows
     acc, tout, fl = oracle.select(np.zeros(N, np.float32), am, am, V, 1.0, 0, seed, cid, step, 4)
     assert acc.all() and (tout == am).all()
-    assert fl == dict(allconf=1, changed=0, stable=5, accepted=N)
+    assert fl == dict(allconf=1, changed=0, stable=5, accepted=N, masked=-1)
     # confidence is strict: H == eps is not confident; NaN is never confident
     Hc = np.full(N, 0.004, np.float32)
     Hc[0] = np.float32(0.005)
@@ -438,6 +511,9 @@ def test_should_stop():
     assert not oracle.should_stop(dict(allconf=0, changed=0, stable=2), 3)
     assert oracle.should_stop(dict(allconf=0, changed=0, stable=3), 3)
     assert not oracle.should_stop(dict(allconf=0, changed=0, stable=99), 0)
+    # masked sampler: stops when no [MASK] is left, not while some are
+    assert oracle.should_stop(dict(allconf=0, changed=1, stable=0, masked=0), 3)
+    assert not oracle.should_stop(dict(allconf=0, changed=1, stable=0, masked=4), 3)
 
 
 # ------------------------------------------------------------- schedule ----
@@ -482,7 +558,8 @@ def _torch_forward(inp, tokens, p_prev, kp, vp, T):
     c = inp["cfg"]
     f = lambda x: x.double()
     E = f(inp["E"])
-    h0 = E[torch.tensor(tokens, dtype=torch.long)]
+    E_in = torch.cat([E, f(inp["mask_emb"]).view(1, -1)])   # input rows: id V is [MASK]
+    h0 = E_in[torch.tensor(tokens, dtype=torch.long)]
     if p_prev is not None:
         a = torch.tensor(p_prev) @ E
         h0 = h0 + Fn.linear(Fn.gelu(Fn.linear(a, f(inp["w1"]))), f(inp["w2"]))
@@ -503,11 +580,13 @@ def _torch_forward(inp, tokens, p_prev, kp, vp, T):
     return dict(h0=h0, attn=o, h1=h1, logits=z, probs=dist.probs, entropy=dist.entropy())
 
 
-@pytest.mark.parametrize("with_prev", [False, True])
-def test_forward_matches_torch_composition(with_prev):
+@pytest.mark.parametrize("with_prev,with_mask", [(False, False), (True, False), (True, True)])
+def test_forward_matches_torch_composition(with_prev, with_mask):
     cfg, inp, m = _small_model()
     rng = np.random.default_rng(10)
     tokens = rng.integers(0, cfg["V"], cfg["N"]).astype(np.int32)
+    if with_mask:                      # masked sampler: [MASK] (id V) at every third position
+        tokens[::3] = cfg["V"]
     kp = inp["k_prefix"].double().numpy()
     vp = inp["v_prefix"].double().numpy()
     p_prev = None

@@ -78,7 +78,8 @@ def make_inputs(cfg: dict, seed: int | None = None) -> dict:
 
     Returns a dict with the config under "cfg" and tensors in the compute
     dtype (bf16 or fp32): E, w1, w2, wq, wk, wv, wo, g_attn, g_final,
-    k_prefix/v_prefix ([Hkv][L][hd], fp32 or bf16) and prompt (int32).
+    k_prefix/v_prefix ([Hkv][L][hd], fp32 or bf16), prompt (int32) and
+    mask_emb ([d], the [MASK] token's row for the masked sampler).
     """
     c = cfg
     if seed is None:
@@ -107,6 +108,9 @@ def make_inputs(cfg: dict, seed: int | None = None) -> dict:
     out["v_prefix"] = _round(torch.randn(Hkv, L, hd, generator=g), dt)
     P = c.get("prompt", 0)
     out["prompt"] = torch.randint(0, V, (P,), generator=g, dtype=torch.int64).to(torch.int32)
+    # the [MASK] token's embedding row (id V) for the masked sampler, drawn
+    # like a row of E and last, so the inputs above do not depend on it
+    out["mask_emb"] = w(1, d).view(d)
     return out
 
 
