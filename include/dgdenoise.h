@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define DG_ABI_VERSION 2
+#define DG_ABI_VERSION 3
 
 typedef enum {
   DG_OK = 0,
@@ -81,6 +81,19 @@ typedef enum { DG_ACCEPT_SUM_MINUS_MAX = 0, DG_ACCEPT_CUMSUM = 1 } dg_accept_rul
  *   step's float statistics. */
 typedef enum { DG_CANDIDATE_ARGMAX = 0, DG_CANDIDATE_MULTINOMIAL = 1 } dg_candidate_rule;
 
+/* Noise of the reverse process.
+ * UNIFORM: uniform-state diffusion ([P1] §2, [P3] §3.2, §5.4) -- the canvas
+ *   starts as uniform vocabulary tokens and every rejected position is
+ *   re-noised with a fresh one; no position is ever locked.
+ * MASKED: masked diffusion, the variant the pages contrast it with ([P1] §1,
+ *   [P3] §3.1) -- the [MASK] token, id V (one past the vocabulary, embedded
+ *   by dg_weights.mask_emb and never predicted by the tied head), stands for
+ *   the noise: the canvas starts all [MASK]; a step walks only the positions
+ *   still holding [MASK] (same order, rule and threshold), accepted ones take
+ *   their candidate and are locked from then on, rejected ones stay [MASK];
+ *   the loop also stops when no [MASK] is left. */
+typedef enum { DG_SAMPLER_UNIFORM = 0, DG_SAMPLER_MASKED = 1 } dg_sampler;
+
 /* Model and canvas shape.
  * Supported: 1 <= canvas_len <= 256; vocab a power of two in [256, 2^24];
  * n_q_heads a multiple of n_kv_heads.  DG_BF16 additionally needs head_dim ==
@@ -100,6 +113,7 @@ typedef struct {
                            ([P3] §5.3: 0.005) */
   dg_accept_rule accept_rule;
   dg_candidate_rule candidate_rule;
+  dg_sampler sampler;
 } dg_config;
 
 /* Weights (device, dtype of the config, caller-owned, read-only).
@@ -110,9 +124,11 @@ typedef struct {
  * contraction the second.
  * w_sc1 [F][d], w_sc2 [d][F]: self-conditioning FFN ([P3] §5.1).
  * wq [Hq*hd][d], wk/wv [Hkv*hd][d], wo [d][Hq*hd]: attention projections.
- * g_attn, g_final [d]: RMSNorm gains (pre-attention, pre-LM-head). */
+ * g_attn, g_final [d]: RMSNorm gains (pre-attention, pre-LM-head).
+ * mask_emb [d]: the [MASK] token's embedding (id V), required (16-byte
+ * aligned) by DG_SAMPLER_MASKED and ignored otherwise. */
 typedef struct {
-  const void *E, *E_pack, *w_sc1, *w_sc2, *wq, *wk, *wv, *wo, *g_attn, *g_final;
+  const void *E, *E_pack, *w_sc1, *w_sc2, *wq, *wk, *wv, *wo, *g_attn, *g_final, *mask_emb;
 } dg_weights;
 
 /* Prefix KV cache ([P1]/[P4]: written causally by prefill, read by denoise).
@@ -161,7 +177,8 @@ enum {
   DG_ST_STEP = 5,      /* index of the last completed step */
   DG_ST_HMIN = 6,      /* float bits: min entropy */
   DG_ST_HMAX = 7,      /* float bits: max entropy */
-  DG_ST_HMEAN = 8      /* float bits: mean entropy */
+  DG_ST_HMEAN = 8,     /* float bits: mean entropy */
+  DG_ST_MASKED = 9     /* [MASK] positions left (DG_SAMPLER_MASKED), else -1 */
 };
 typedef struct {
   int32_t *tokens;
@@ -183,6 +200,7 @@ typedef struct {
   int32_t allconf;
   int32_t changed;
   float h_min, h_mean, h_max;
+  int32_t masked;      /* [MASK] positions left; -1 under DG_SAMPLER_UNIFORM */
 } dg_step_stats;
 
 /* ---- sizes and checks (host only, no device work) ---------------------- */
@@ -220,8 +238,9 @@ dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_pack, v
 
 /* [P3] §5.4 canvas initialisation: tokens[i] = the top log2(V) bits of word 0
  * of Philox4x32-10(key = seed, counter = (i, 0, canvas_id, 0)) -- uniform
- * vocabulary tokens.  Resets status (stable = 0) and the host fields
- * step = 0, has_prev = 0, seed, canvas_id. */
+ * vocabulary tokens; DG_SAMPLER_MASKED: tokens[i] = V ([MASK]) everywhere.
+ * Resets status (stable = 0) and the host fields step = 0, has_prev = 0,
+ * seed, canvas_id. */
 dg_status dg_canvas_init(const dg_config *cfg, dg_canvas *canvas, uint64_t seed,
                          uint32_t canvas_id, void *stream);
 
@@ -233,8 +252,9 @@ dg_status dg_canvas_init(const dg_config *cfg, dg_canvas *canvas, uint64_t seed,
  * attention output of the new tokens over keys [0, length+i].  No LM head.
  * Then cache->length += n_tokens (host field).
  * Errors: DG_ERR_CAPACITY if length + n_tokens > capacity; DG_ERR_WORKSPACE
- * if ws_bytes < dg_workspace_bytes(cfg, n_tokens); tokens must be in [0, V)
- * (not checked on the device: out-of-range ids are clamped). */
+ * if ws_bytes < dg_workspace_bytes(cfg, n_tokens); tokens must be in [0, V),
+ * or [0, V] under DG_SAMPLER_MASKED where V is [MASK] (not checked on the
+ * device: out-of-range ids are clamped into that range). */
 dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cache *cache,
                             const int32_t *tokens, int32_t n_tokens, void *attn_out,
                             void *ws, size_t ws_bytes, void *stream);
@@ -249,7 +269,9 @@ dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cac
  *     2 + 4k and 3 + 4k); probs/stats keep p for the next step
  *  4. accept by `accept_rule` under `accept_threshold_nats`; accepted
  *     positions take the candidate token, every rejected one a fresh uniform
- *     token (Philox counter (i, step, canvas_id, 1)); status flags updated
+ *     token (Philox counter (i, step, canvas_id, 1)) -- or, under
+ *     DG_SAMPLER_MASKED, only [MASK] positions are walked, rejected ones
+ *     stay [MASK] and decided ones are kept; status flags updated
  * Then canvas->step += 1 and canvas->has_prev = 1 (host fields).
  * Errors: temperature must be finite and > 0; the threshold >= 0 and not NaN;
  * DG_ERR_WORKSPACE if ws_bytes < dg_workspace_bytes(cfg, 0). */
@@ -259,7 +281,8 @@ dg_status dg_denoise_step(const dg_config *cfg, const dg_weights *w, const dg_kv
 
 /* Adaptive stop, [P3] §5.3 and [P5] scheduler: stop when every entropy is
  * below conf_eps, or when the canvas has been unchanged for stable_steps
- * consecutive steps (stable_steps <= 0 disables the stability test).
+ * consecutive steps (stable_steps <= 0 disables the stability test), or,
+ * under DG_SAMPLER_MASKED, when no [MASK] is left ([P3] §3.1).
  * Synchronises `stream`, then writes *stop_host (0/1) and, if non-NULL,
  * *stats_host.  This is the only device-to-host transfer of a step. */
 dg_status dg_should_stop(const dg_config *cfg, const dg_canvas *canvas, int32_t stable_steps,

@@ -64,8 +64,9 @@ def replay_select(den: D.Denoiser, tokens_in, stable_in, step, gamma, rule):
     cfg = den.cfg
     H = den.canvas.entropy.cpu().numpy()
     am = den.canvas.argmax.cpu().numpy()
+    mask_id = cfg.vocab if cfg.sampler == B.DG_SAMPLER_MASKED else -1
     acc, tout, fl = oracle.select(H, am, tokens_in, cfg.vocab, gamma, rule, den.canvas.s.seed,
-                                  den.canvas.s.canvas_id, step, stable_in, CONF_EPS_F32)
+                                  den.canvas.s.canvas_id, step, stable_in, CONF_EPS_F32, mask_id=mask_id)
     st = den.canvas.status.cpu().numpy()
     np.testing.assert_array_equal(den.canvas.accept.cpu().numpy(), acc)
     np.testing.assert_array_equal(den.canvas.tokens.cpu().numpy(), tout)
@@ -73,4 +74,5 @@ def replay_select(den: D.Denoiser, tokens_in, stable_in, step, gamma, rule):
     assert st[B.DG_ST_CHANGED] == fl["changed"]
     assert st[B.DG_ST_STABLE] == fl["stable"]
     assert st[B.DG_ST_ACCEPTED] == fl["accepted"]
+    assert st[B.DG_ST_MASKED] == fl["masked"]
     return fl

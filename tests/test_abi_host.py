@@ -38,7 +38,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert B.dg_abi_version() == 2
+    assert B.dg_abi_version() == 3
     for s in range(6):
         assert lib.dg_status_string(s)
 
@@ -88,6 +88,11 @@ def test_bad_enums(lib):
     cfg.accept_rule = 9
     assert B.dg_validate_config(cfg) == B.DG_ERR_INVALID_ARG
     cfg = cfg_of(2)
+    cfg.sampler = 5
+    assert B.dg_validate_config(cfg) == B.DG_ERR_INVALID_ARG
+    cfg.sampler = B.DG_SAMPLER_MASKED
+    assert B.dg_validate_config(cfg) == B.DG_OK
+    cfg = cfg_of(2)
     cfg.candidate_rule = 2
     assert B.dg_validate_config(cfg) == B.DG_ERR_INVALID_ARG
     cfg.candidate_rule = B.DG_CANDIDATE_MULTINOMIAL
@@ -107,7 +112,7 @@ FAKE = 0x10000  # a non-null address; validation must fail before it is used
 
 
 def fake_weights():
-    return B.dg_weights(*([FAKE] * 10))
+    return B.dg_weights(*([FAKE] * 11))
 
 
 def fake_canvas():
@@ -146,6 +151,15 @@ def test_denoise_step_validation(lib):
     assert call_step(cfg, w, cache, cv2, 1.0, 8.0, need) == B.DG_ERR_INVALID_ARG
     bad_cache = B.dg_kv_cache(FAKE, FAKE, 600, 512)
     assert call_step(cfg, w, bad_cache, cv, 1.0, 8.0, need) == B.DG_ERR_INVALID_ARG
+    # the masked sampler needs the [MASK] row, 16-byte aligned
+    cfg_m = cfg_of(2)
+    cfg_m.sampler = B.DG_SAMPLER_MASKED
+    w3 = fake_weights()
+    w3.mask_emb = None
+    assert call_step(cfg_m, w3, cache, cv, 1.0, 8.0, need) == B.DG_ERR_INVALID_ARG
+    w3.mask_emb = FAKE + 8
+    assert call_step(cfg_m, w3, cache, cv, 1.0, 8.0, need) == B.DG_ERR_INVALID_ARG
+    assert call_step(cfg_m, w, cache, cv, 1.0, 8.0, need - 1) == B.DG_ERR_WORKSPACE
     assert (cv.step, cv.has_prev) == (3, 1)
 
 

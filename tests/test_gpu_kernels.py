@@ -67,7 +67,12 @@ def test_canvas_init_matches_oracle(N, V):
         B.dg_canvas_init(cfg, cv.s, seed, cid)
         np.testing.assert_array_equal(cv.tokens.cpu().numpy(), oracle.canvas_init(seed, cid, N, V))
         assert cv.s.step == 0 and cv.s.has_prev == 0
-        assert int(cv.status[B.DG_ST_STABLE]) == 0
+        assert int(cv.status[B.DG_ST_STABLE]) == 0 and int(cv.status[B.DG_ST_MASKED]) == -1
+    # masked sampler: [MASK] (id V) everywhere, all N counted as masked
+    cfg.sampler = B.DG_SAMPLER_MASKED
+    B.dg_canvas_init(cfg, cv.s, 5, 1)
+    np.testing.assert_array_equal(cv.tokens.cpu().numpy(), oracle.canvas_init(5, 1, N, V, masked=True))
+    assert int(cv.status[B.DG_ST_MASKED]) == N
 
 
 def _select_cases():
@@ -89,17 +94,22 @@ def _select_cases():
             yield N, H
 
 
-@pytest.mark.parametrize("rule", [0, 1])
-def test_select_kernel_bit_exact(rule):
+@pytest.mark.parametrize("rule,masked", [(0, False), (1, False), (0, True), (1, True)])
+def test_select_kernel_bit_exact(rule, masked):
+    """Selection kernel vs the oracle, bit-exact: uniform-state re-noise, and
+    the masked sampler ([MASK] = id V at ~60% of the positions, the rest locked)."""
     V = 32768
     c = dict(N=256, V=V, d=1024, Hq=8, Hkv=8, hd=128, F=1024, dtype="bf16")
-    rng = np.random.default_rng(2 + rule)
+    rng = np.random.default_rng(2 + rule + 4 * masked)
     for N, H in _select_cases():
         c["N"] = N
-        cfg = B.make_config(c, accept_rule=rule)
+        cfg = B.make_config(c, accept_rule=rule,
+                            sampler=B.DG_SAMPLER_MASKED if masked else B.DG_SAMPLER_UNIFORM)
         cv = B.DeviceCanvas(cfg)
         am = rng.integers(0, V, N).astype(np.int32)
         tin = rng.integers(0, V, N).astype(np.int32)
+        if masked:
+            tin[rng.random(N) < 0.6] = V
         for gamma in (0.0, 0.75, 3.0, 16.0, 1e30):
             step, cid, seed, stable_in = int(rng.integers(0, 64)), int(rng.integers(0, 8)), 99, 2
             cv.entropy.copy_(torch.from_numpy(H))
@@ -110,13 +120,13 @@ def test_select_kernel_bit_exact(rule):
             cv.s.step, cv.s.canvas_id, cv.s.seed = step, cid, seed
             B.dg_test_select(cfg, cv.s, gamma)
             acc, tout, fl = oracle.select(H, am, tin, V, gamma, rule, seed, cid, step, stable_in,
-                                          CONF_EPS_F32)
+                                          CONF_EPS_F32, mask_id=V if masked else -1)
             np.testing.assert_array_equal(cv.accept.cpu().numpy(), acc, err_msg=f"{N} {gamma}")
             np.testing.assert_array_equal(cv.tokens.cpu().numpy(), tout)
             st = cv.status.cpu().numpy()
             assert (st[B.DG_ST_ALLCONF], st[B.DG_ST_CHANGED], st[B.DG_ST_STABLE],
-                    st[B.DG_ST_ACCEPTED]) == (fl["allconf"], fl["changed"], fl["stable"],
-                                              fl["accepted"])
+                    st[B.DG_ST_ACCEPTED], st[B.DG_ST_MASKED]) == (fl["allconf"], fl["changed"], fl["stable"],
+                                                                  fl["accepted"], fl["masked"])
 
 
 def test_stop_flags_on_constructed_canvas():

@@ -36,18 +36,20 @@ def _free_memory():
     torch.cuda.empty_cache()
 
 
-def lockstep(c, inp, nsteps, rule=0, seed=None, cid=0):
-    """Runs nsteps GPU steps and checks each against the oracle (all rows)."""
+def lockstep(c, inp, nsteps, rule=0, seed=None, cid=0, masked=False):
+    """Runs nsteps GPU steps and checks each against the oracle (all rows);
+    masked: the masked-diffusion sampler ([MASK] = id V)."""
     f32 = c["dtype"] == "f32"
     tol = 1e-4 if f32 else 1e-2
-    den = D.Denoiser(c, inp, accept_rule=rule, logits_dump=True)
+    den = D.Denoiser(c, inp, accept_rule=rule, logits_dump=True,
+                     sampler=B.DG_SAMPLER_MASKED if masked else B.DG_SAMPLER_UNIFORM)
     om = oracle.model_from_inputs(inp)
     kc, vc = oracle_cache(inp)
     N, V, d, qw = c["N"], c["V"], c["d"], c["Hq"] * c["hd"]
     seed = W.canvas_seed(c.get("id", 0)) if seed is None else seed
     den.init_canvas(seed, cid)
     np.testing.assert_array_equal(den.canvas.tokens.cpu().numpy(),
-                                  oracle.canvas_init(seed, cid, N, V))
+                                  oracle.canvas_init(seed, cid, N, V, masked=masked))
     p_prev = None
     stable = 0
     report = []
@@ -130,6 +132,20 @@ def test_config2_bf16_lockstep(rule):
     inp = W.make_inputs(c)
     den, rep = lockstep(c, inp, 3, rule=rule)
     print(rep)
+
+
+@pytest.mark.usefixtures("logits_dump")
+def test_config1_fp32_masked_sampler_lockstep():
+    c = W.config(1)
+    den, rep = lockstep(c, W.make_inputs(c), c["steps"], masked=True)
+    tok = den.canvas.tokens.cpu().numpy()
+    assert (tok == c["V"]).sum() < c["N"]        # some positions decided, and locked
+
+
+@pytest.mark.usefixtures("logits_dump")
+def test_config2_bf16_masked_sampler_lockstep():
+    c = W.config(2)
+    lockstep(c, W.make_inputs(c), 3, masked=True)
 
 
 @pytest.mark.usefixtures("logits_dump")
@@ -415,3 +431,25 @@ def test_run_canvas_native_matches_host_loop(cfg_id, stop):
         B.dg_run_canvas(den.cfg, den.w.s, den.cache.s, den.canvas.s, seed, 4, [1.0, float("nan")],
                         c["gamma"], True, 3, den.ws)
     assert e.value.status == B.DG_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("cfg_id,budget", [(1, 40), (2, 400)])
+def test_masked_sampler_runs_until_unmasked(cfg_id, budget):
+    """Masked sampler ([P3] §3.1): the loop ends when no [MASK] is left, every
+    position then holds a vocabulary token, and the library's loop equals the
+    host loop bit for bit."""
+    c = W.config(cfg_id)
+    inp = W.make_inputs(c)
+    den = D.Denoiser(c, inp, sampler=B.DG_SAMPLER_MASKED)
+    seed = W.canvas_seed(cfg_id)
+    a = den.run_canvas(seed, 2, budget, c["sched"], c["T0"], c["T1"], c["gamma"], True, 0)
+    b = den.run_canvas_native(seed, 2, budget, c["sched"], c["T0"], c["T1"], c["gamma"], True, 0)
+    torch.cuda.synchronize()
+    assert (a.steps, a.stop_reason) == (b.steps, b.stop_reason)
+    assert torch.equal(a.tokens, b.tokens)
+    assert a.stop_reason in ("unmasked", "confident"), a.stop_reason
+    assert int((b.tokens >= c["V"]).sum()) == 0 and int((b.tokens < 0).sum()) == 0
+    assert int(den.canvas.status[B.DG_ST_MASKED]) == 0
+    # masks only ever resolve: the per-step counts of the host loop never grow
+    counts = [st.masked for st in a.stats]
+    assert all(x >= y for x, y in zip(counts, counts[1:])) and counts[-1] == 0

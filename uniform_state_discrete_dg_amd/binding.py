@@ -24,21 +24,23 @@ DG_OK, DG_ERR_INVALID_ARG, DG_ERR_UNSUPPORTED, DG_ERR_CAPACITY, DG_ERR_WORKSPACE
 DG_F32, DG_BF16 = 0, 1
 DG_ACCEPT_SUM_MINUS_MAX, DG_ACCEPT_CUMSUM = 0, 1
 DG_CANDIDATE_ARGMAX, DG_CANDIDATE_MULTINOMIAL = 0, 1
+DG_SAMPLER_UNIFORM, DG_SAMPLER_MASKED = 0, 1
 DG_STATUS_WORDS = 16
 (DG_ST_ALLCONF, DG_ST_CHANGED, DG_ST_STABLE, DG_ST_ACCEPTED, DG_ST_NAN, DG_ST_STEP, DG_ST_HMIN,
- DG_ST_HMAX, DG_ST_HMEAN) = range(9)
+ DG_ST_HMAX, DG_ST_HMEAN, DG_ST_MASKED) = range(10)
 TILE_V = 64  # vocabulary columns per softmax-statistics tile
 
 
 class dg_config(ctypes.Structure):
     _fields_ = [("canvas_len", c_i32), ("vocab", c_i32), ("d_model", c_i32), ("n_q_heads", c_i32),
                 ("n_kv_heads", c_i32), ("head_dim", c_i32), ("ffn_hidden", c_i32), ("dtype", c_i32),
-                ("rms_eps", c_f32), ("conf_eps", c_f32), ("accept_rule", c_i32), ("candidate_rule", c_i32)]
+                ("rms_eps", c_f32), ("conf_eps", c_f32), ("accept_rule", c_i32), ("candidate_rule", c_i32),
+                ("sampler", c_i32)]
 
 
 class dg_weights(ctypes.Structure):
     _fields_ = [(n, vp) for n in ("E", "E_pack", "w_sc1", "w_sc2", "wq", "wk", "wv", "wo", "g_attn",
-                                  "g_final")]
+                                  "g_final", "mask_emb")]
 
 
 class dg_kv_cache(ctypes.Structure):
@@ -53,7 +55,7 @@ class dg_canvas(ctypes.Structure):
 
 class dg_step_stats(ctypes.Structure):
     _fields_ = [("accepted", c_i32), ("stable", c_i32), ("allconf", c_i32), ("changed", c_i32),
-                ("h_min", c_f32), ("h_mean", c_f32), ("h_max", c_f32)]
+                ("h_min", c_f32), ("h_mean", c_f32), ("h_max", c_f32), ("masked", c_i32)]
 
 
 class dg_ws_offsets(ctypes.Structure):
@@ -263,10 +265,11 @@ def dg_profile_read():
 # device-side holders (torch allocations wrapped in the C structs)
 # ---------------------------------------------------------------------------
 def make_config(c: dict, accept_rule: int = DG_ACCEPT_SUM_MINUS_MAX,
-                conf_eps: float = 0.005, candidate_rule: int = DG_CANDIDATE_ARGMAX) -> dg_config:
+                conf_eps: float = 0.005, candidate_rule: int = DG_CANDIDATE_ARGMAX,
+                sampler: int = DG_SAMPLER_UNIFORM) -> dg_config:
     return dg_config(c["N"], c["V"], c["d"], c["Hq"], c["Hkv"], c["hd"], c["F"],
                      DG_BF16 if c["dtype"] == "bf16" else DG_F32, c.get("rms_eps", 1e-6),
-                     conf_eps, accept_rule, candidate_rule)
+                     conf_eps, accept_rule, candidate_rule, sampler)
 
 
 def torch_dtype(cfg: dg_config):
@@ -308,14 +311,14 @@ class DeviceWeights:
     def __init__(self, cfg: dg_config, inp: dict, device="cuda", stream=None):
         dt = torch_dtype(cfg)
         t = {k: inp[k].to(device=device, dtype=dt).contiguous()
-             for k in ("E", "w1", "w2", "wq", "wk", "wv", "wo", "g_attn", "g_final")}
+             for k in ("E", "w1", "w2", "wq", "wk", "wv", "wo", "g_attn", "g_final", "mask_emb") if k in inp}
         nb = dg_embedding_pack_bytes(cfg)
         t["E_pack"] = torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
         dg_pack_embedding(cfg, t["E"], t["E_pack"] if nb else None, stream)
         self.t = t
-        self.s = dg_weights(*(t[k].data_ptr() if (k != "E_pack" or nb) else None
+        self.s = dg_weights(*(t[k].data_ptr() if k in t and (k != "E_pack" or nb) else None
                               for k in ("E", "E_pack", "w1", "w2", "wq", "wk", "wv", "wo", "g_attn",
-                                        "g_final")))
+                                        "g_final", "mask_emb")))
 
 
 class DeviceCache:

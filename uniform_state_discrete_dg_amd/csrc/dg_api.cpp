@@ -36,6 +36,7 @@ dg_status check_config(const dg_config *c) {
     return DG_ERR_INVALID_ARG;
   if (c->candidate_rule != DG_CANDIDATE_ARGMAX && c->candidate_rule != DG_CANDIDATE_MULTINOMIAL)
     return DG_ERR_INVALID_ARG;
+  if (c->sampler != DG_SAMPLER_UNIFORM && c->sampler != DG_SAMPLER_MASKED) return DG_ERR_INVALID_ARG;
   if (c->canvas_len < 1 || c->vocab < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
       c->head_dim < 1 || c->ffn_hidden < 1)
     return DG_ERR_INVALID_ARG;
@@ -203,7 +204,23 @@ bool weights_ok(const dg_config *c, const dg_weights *w) {
       !w->g_final)
     return false;
   if (c->dtype == DG_BF16 && !w->E_pack) return false;
+  if (c->sampler == DG_SAMPLER_MASKED && (!w->mask_emb || reinterpret_cast<uintptr_t>(w->mask_emb) % 16))
+    return false;
   return true;
+}
+
+// The [MASK] token id of the masked sampler (one past the vocabulary), -1 for
+// uniform-state re-noise; and the embedding row that id reads.
+int mask_id(const dg_config *c) { return c->sampler == DG_SAMPLER_MASKED ? c->vocab : -1; }
+template <typename T>
+const T *mask_row(const dg_config *c, const dg_weights *w) {
+  return c->sampler == DG_SAMPLER_MASKED ? static_cast<const T *>(w->mask_emb) : nullptr;
+}
+
+// The adaptive stop on a step's status words: every entropy below conf_eps,
+// the canvas stable for stable_steps steps, or (masked sampler) no [MASK] left.
+bool status_stops(const int32_t *w, int32_t stable_steps) {
+  return w[DG_ST_ALLCONF] != 0 || (stable_steps > 0 && w[DG_ST_STABLE] >= stable_steps) || w[DG_ST_MASKED] == 0;
 }
 
 bool canvas_ok(const dg_canvas *cv) {
@@ -343,7 +360,7 @@ dg_status dg_canvas_init(const dg_config *cfg, dg_canvas *cv, uint64_t seed, uin
   if (st != DG_OK) return st;
   if (!canvas_ok(cv)) return DG_ERR_INVALID_ARG;
   DG_TRY(dg::canvas_init(cv->tokens, cv->status, cfg->canvas_len, ilog2(cfg->vocab), seed, canvas_id,
-                         static_cast<hipStream_t>(stream)));
+                         mask_id(cfg), static_cast<hipStream_t>(stream)));
   cv->step = 0;
   cv->has_prev = 0;
   cv->seed = seed;
@@ -372,11 +389,11 @@ dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cac
   float *nrm = reinterpret_cast<float *>(base + L.p_nrm);
 
   if (bf) {  // nrm holds the split pair
-    DG_TRY(dg::gather_rows<bf16>(static_cast<const bf16 *>(w->E), tokens, n, d, V, x, s));
+    DG_TRY(dg::gather_rows<bf16>(static_cast<const bf16 *>(w->E), tokens, n, d, V, mask_row<bf16>(cfg, w), x, s));
     DG_TRY(dg::rmsnorm_rows<bf16>(x, static_cast<const bf16 *>(w->g_attn), n, d, cfg->rms_eps, nullptr, nullptr,
                                   reinterpret_cast<bf16 *>(nrm), s));
   } else {
-    DG_TRY(dg::gather_rows<float>(static_cast<const float *>(w->E), tokens, n, d, V, x, s));
+    DG_TRY(dg::gather_rows<float>(static_cast<const float *>(w->E), tokens, n, d, V, mask_row<float>(cfg, w), x, s));
     DG_TRY(dg::rmsnorm_rows<float>(x, static_cast<const float *>(w->g_attn), n, d, cfg->rms_eps, nrm, nullptr,
                                    nullptr, s));
   }
@@ -469,9 +486,11 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
   // by the FFN's output merge (its residual), so h0 is written once
   const bool fused_embed = bf && cv->has_prev;
   if (bf && !fused_embed)
-    DG_TRY(dg::gather_rows<bf16>(static_cast<const bf16 *>(w->E), cv->tokens, N, d, V, h0, s));
+    DG_TRY(dg::gather_rows<bf16>(static_cast<const bf16 *>(w->E), cv->tokens, N, d, V, mask_row<bf16>(cfg, w), h0,
+                                 s));
   else if (!bf)
-    DG_TRY(dg::gather_rows<float>(static_cast<const float *>(w->E), cv->tokens, N, d, V, h0, s));
+    DG_TRY(dg::gather_rows<float>(static_cast<const float *>(w->E), cv->tokens, N, d, V, mask_row<float>(cfg, w),
+                                  h0, s));
   if (cv->has_prev) {
     if (bf) {
       const int ks = selfcond_ksplit(cfg);
@@ -503,6 +522,7 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
       ea.gtok = cv->tokens;
       ea.gV = V;
       ea.gld = d;
+      ea.gmask = mask_row<uint16_t>(cfg, w);
     } else {
       ea.kind = dg::EPI_ADD;
       ea.resid = h0;
@@ -590,7 +610,8 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
   }
   // 5. accept / re-noise / stop flags
   DG_TRY(dg::select_step(cv->entropy, cv->argmax, cv->tokens, cv->accept, cv->status, N, ilog2(V), (double)gamma,
-                         (int)cfg->accept_rule, cfg->conf_eps, cv->seed, cv->canvas_id, (uint32_t)cv->step, s));
+                         (int)cfg->accept_rule, cfg->conf_eps, cv->seed, cv->canvas_id, (uint32_t)cv->step,
+                         mask_id(cfg), s));
   cv->step += 1;
   cv->has_prev = 1;
   return DG_OK;
@@ -610,9 +631,7 @@ dg_status dg_should_stop(const dg_config *cfg, const dg_canvas *cv, int32_t stab
   int32_t w[DG_STATUS_WORDS];
   DG_TRY(hipMemcpyAsync(w, cv->status, sizeof(w), hipMemcpyDeviceToHost, s));
   DG_TRY(hipStreamSynchronize(s));
-  int32_t stop = w[DG_ST_ALLCONF] ? 1 : 0;
-  if (stable_steps > 0 && w[DG_ST_STABLE] >= stable_steps) stop = 1;
-  *stop_host = stop;
+  *stop_host = status_stops(w, stable_steps) ? 1 : 0;
   if (stats_host) {
     stats_host->accepted = w[DG_ST_ACCEPTED];
     stats_host->stable = w[DG_ST_STABLE];
@@ -625,6 +644,7 @@ dg_status dg_should_stop(const dg_config *cfg, const dg_canvas *cv, int32_t stab
     stats_host->h_mean = f;
     std::memcpy(&f, &w[DG_ST_HMAX], 4);
     stats_host->h_max = f;
+    stats_host->masked = w[DG_ST_MASKED];
   }
   return DG_OK;
 }
@@ -685,7 +705,7 @@ dg_status dg_run_canvas(const dg_config *cfg, const dg_weights *w, const dg_kv_c
         if (st != DG_OK) return st;
       }
       DG_TRY(hipEventSynchronize(status_ready));
-      if (pinned[DG_ST_ALLCONF] || (stable_steps > 0 && pinned[DG_ST_STABLE] >= stable_steps)) {
+      if (status_stops(pinned, stable_steps)) {
         *stopped = 1;
         if (ahead) DG_TRY(hipStreamSynchronize(s));  // the guarded launch returns at once
         break;
@@ -747,7 +767,7 @@ dg_status dg_test_select(const dg_config *cfg, dg_canvas *cv, float gamma, void 
   if (!canvas_ok(cv) || std::isnan(gamma) || gamma < 0.f || cv->step < 0) return DG_ERR_INVALID_ARG;
   DG_TRY(dg::select_step(cv->entropy, cv->argmax, cv->tokens, cv->accept, cv->status, cfg->canvas_len,
                          ilog2(cfg->vocab), (double)gamma, (int)cfg->accept_rule, cfg->conf_eps, cv->seed,
-                         cv->canvas_id, (uint32_t)cv->step, static_cast<hipStream_t>(stream)));
+                         cv->canvas_id, (uint32_t)cv->step, mask_id(cfg), static_cast<hipStream_t>(stream)));
   return DG_OK;
 }
 

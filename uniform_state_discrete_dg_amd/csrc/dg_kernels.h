@@ -18,7 +18,8 @@ typedef uint16_t bf16;  // raw bfloat16 bits
 // A bf16 output with lo_off != 0 is a split pair: hi = bf16(v) at the index,
 // lo = bf16(v - hi) at index + lo_off (the operand format of SplitGemm).
 // EPI_ADD_ROW: out = acc + gtab[tok[row]][col] (bf16 table rows, leading
-// dimension gld, token ids clamped to [0, gV)): a residual gathered on the fly.
+// dimension gld, token ids clamped to [0, gV)): a residual gathered on the fly;
+// with gmask (the [MASK] row of the masked sampler) ids >= gV read gmask.
 enum EpiKind { EPI_STORE = 0, EPI_GELU = 1, EPI_ADD = 2, EPI_ADD_ROW = 3 };
 struct Epi {
   int kind;
@@ -33,6 +34,7 @@ struct Epi {
   const int32_t *gtok;
   int gV;
   int64_t gld;
+  const uint16_t *gmask;  // EPI_ADD_ROW: row of token ids >= gV (nullable)
 };
 
 // Operands of a table-streaming contraction in the tiled layout of
@@ -97,7 +99,8 @@ struct SelfcondGuard {
   int stable_steps;
   __device__ bool stopped() const {
     if (!status) return false;
-    return status[DG_ST_ALLCONF] != 0 || (stable_steps > 0 && status[DG_ST_STABLE] >= stable_steps);
+    return status[DG_ST_ALLCONF] != 0 || (stable_steps > 0 && status[DG_ST_STABLE] >= stable_steps) ||
+           status[DG_ST_MASKED] == 0;
   }
 };
 hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partials, int ksplit, hipStream_t s,
@@ -180,8 +183,10 @@ hipError_t attention_f32(const AttnArgs &a, hipStream_t s);
 void attention_plan(int nq, int Hq, int nk, int *splits, int *keys_per_split);
 
 // Small ops.
+// out[i] = E[tokens[i]] (fp32 [n][d]); ids clamped to [0, V), except that with
+// mask_row (the [MASK] embedding, id V, masked sampler) ids >= V read mask_row.
 template <typename T>
-hipError_t gather_rows(const T *E, const int32_t *tokens, int n, int d, int V, float *out,
+hipError_t gather_rows(const T *E, const int32_t *tokens, int n, int d, int V, const T *mask_row, float *out,
                        hipStream_t s);
 // out (fp32 [n][d], nullable), out_tiled (bf16, tiled block(s) of the
 // rows, the rows past n up to the block end written as zeros; nullable)
@@ -209,13 +214,15 @@ hipError_t transpose(const T *in, int rows, int cols, T *out, int64_t ld_out, hi
 hipError_t tile_rows(const uint16_t *X, int R, int K, int64_t ldx, uint16_t *out, hipStream_t s);
 hipError_t copy_bytes(const void *src, void *dst, size_t bytes, hipStream_t s);
 
-// Selection and canvas.
+// Selection and canvas.  mask_id >= 0: the masked sampler (the canvas starts
+// as mask_id; only positions holding it are walked; rejected ones keep it,
+// decided ones are locked); mask_id < 0: uniform-state re-noise.
 hipError_t canvas_init(int32_t *tokens, int32_t *status, int N, int log2v, uint64_t seed,
-                       uint32_t canvas_id, hipStream_t s);
+                       uint32_t canvas_id, int mask_id, hipStream_t s);
 hipError_t select_step(const float *entropy, const int32_t *argmax, int32_t *tokens,
                        uint8_t *accept, int32_t *status, int N, int log2v, double gamma,
                        int rule, float conf_eps, uint64_t seed, uint32_t canvas_id,
-                       uint32_t step, hipStream_t s);
+                       uint32_t step, int mask_id, hipStream_t s);
 hipError_t philox_test(const uint32_t *ctr, uint32_t k0, uint32_t k1, uint32_t *out, int n,
                        hipStream_t s);
 

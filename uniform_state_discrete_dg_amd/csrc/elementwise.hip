@@ -27,24 +27,28 @@ __device__ __forceinline__ float block_sum256(float v, float *sh) {
   return r;
 }
 
-// [P3] §5.1: the token embeddings of the canvas (rows of the tied table).
+// [P3] §5.1: the token embeddings of the canvas (rows of the tied table);
+// under the masked sampler ([P3] §3.1) ids >= V are [MASK] and read mask_row.
+template <typename T>
+__device__ __forceinline__ const T *embed_row(const T *E, int t, int d, int V, const T *mask_row) {
+  if (t >= V && mask_row) return mask_row;
+  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
+  return E + (int64_t)t * d;
+}
+
 template <typename T>
 __global__ void gather_kernel(const T *__restrict__ E, const int32_t *__restrict__ tokens, int d, int V,
-                              float *__restrict__ out) {
+                              const T *__restrict__ mask_row, float *__restrict__ out) {
   const int i = blockIdx.x;
-  int t = tokens[i];
-  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
-  for (int k = threadIdx.x; k < d; k += blockDim.x)
-    out[(int64_t)i * d + k] = Elem<T>::load(E, (int64_t)t * d + k);
+  const T *row = embed_row(E, tokens[i], d, V, mask_row);
+  for (int k = threadIdx.x; k < d; k += blockDim.x) out[(int64_t)i * d + k] = Elem<T>::load(row, k);
 }
 
 // bf16 rows, d % 8 == 0: eight values (16 bytes) per thread
 __global__ void gather8_kernel(const bf16 *__restrict__ E, const int32_t *__restrict__ tokens, int d, int V,
-                               float *__restrict__ out) {
+                               const bf16 *__restrict__ mask_row, float *__restrict__ out) {
   const int i = blockIdx.x;
-  int t = tokens[i];
-  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
-  const uint4 *src = reinterpret_cast<const uint4 *>(E + (int64_t)t * d);
+  const uint4 *src = reinterpret_cast<const uint4 *>(embed_row(E, tokens[i], d, V, mask_row));
   float4 *dst = reinterpret_cast<float4 *>(out + (int64_t)i * d);
   for (int k = threadIdx.x; k < d / 8; k += blockDim.x) {
     const uint4 v = src[k];
@@ -56,19 +60,22 @@ __global__ void gather8_kernel(const bf16 *__restrict__ E, const int32_t *__rest
 }
 
 template <typename T>
-hipError_t gather_rows(const T *E, const int32_t *tokens, int n, int d, int V, float *out, hipStream_t s) {
+hipError_t gather_rows(const T *E, const int32_t *tokens, int n, int d, int V, const T *mask_row, float *out,
+                       hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    if (d % 8 == 0) {
-      hipLaunchKernelGGL(gather8_kernel, dim3(n), dim3(256), 0, s, E, tokens, d, V, out);
+    if (d % 8 == 0 && (reinterpret_cast<uintptr_t>(mask_row) & 15) == 0) {
+      hipLaunchKernelGGL(gather8_kernel, dim3(n), dim3(256), 0, s, E, tokens, d, V, mask_row, out);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL(gather_kernel<T>, dim3(n), dim3(256), 0, s, E, tokens, d, V, out);
+  hipLaunchKernelGGL(gather_kernel<T>, dim3(n), dim3(256), 0, s, E, tokens, d, V, mask_row, out);
   return hipGetLastError();
 }
-template hipError_t gather_rows<float>(const float *, const int32_t *, int, int, int, float *, hipStream_t);
-template hipError_t gather_rows<bf16>(const bf16 *, const int32_t *, int, int, int, float *, hipStream_t);
+template hipError_t gather_rows<float>(const float *, const int32_t *, int, int, int, const float *, float *,
+                                       hipStream_t);
+template hipError_t gather_rows<bf16>(const bf16 *, const int32_t *, int, int, int, const bf16 *, float *,
+                                      hipStream_t);
 
 // RMSNorm: out = x / sqrt(mean(x^2) + eps) * g, written in fp32 and/or, when
 // requested, rounded to bf16 (the operand of the tied LM head) and as a

@@ -13,6 +13,7 @@ namespace dg {
 
 __device__ __forceinline__ const uint16_t *epi_row(const Epi &e, int row) {
   int t = e.gtok[row];
+  if (t >= e.gV && e.gmask) return e.gmask;  // [MASK] (masked sampler)
   t = t < 0 ? 0 : (t >= e.gV ? e.gV - 1 : t);
   return e.gtab + (int64_t)t * e.gld;
 }

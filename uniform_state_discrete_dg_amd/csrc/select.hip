@@ -7,7 +7,9 @@
 // (less their maximum, which in ascending order is the current one) stays
 // within the threshold, and the first failure ends the walk.  [P5] states
 // the plain running sum (rule CUMSUM).  Every rejected position is
-// re-noised with a fresh uniform token; accepted ones take the argmax.
+// re-noised with a fresh uniform token; accepted ones take the candidate.
+// Masked sampler ([P1] §1, [P3] §3.1): only positions holding [MASK] are
+// walked, rejected ones keep [MASK] and decided ones are never revisited.
 //
 // The walk is evaluated in parallel: each position's key (entropy bits << 32
 // | position) orders it among the others, its entropy is turned into
@@ -24,15 +26,17 @@
 namespace dg {
 
 __global__ void canvas_init_kernel(int32_t *tokens, int32_t *status, int N, int log2v, uint64_t seed,
-                                   uint32_t canvas_id) {
+                                   uint32_t canvas_id, int mask_id) {
   const int i = threadIdx.x + blockIdx.x * blockDim.x;
-  if (i < N) tokens[i] = uniform_token(seed, (uint32_t)i, 0u, canvas_id, 0u, log2v);
-  if (i < DG_STATUS_WORDS) status[i] = (i == DG_ST_STEP) ? -1 : 0;
+  if (i < N) tokens[i] = mask_id >= 0 ? mask_id : uniform_token(seed, (uint32_t)i, 0u, canvas_id, 0u, log2v);
+  if (i < DG_STATUS_WORDS)
+    status[i] = (i == DG_ST_STEP) ? -1 : (i == DG_ST_MASKED) ? (mask_id >= 0 ? N : -1) : 0;
 }
 
 hipError_t canvas_init(int32_t *tokens, int32_t *status, int N, int log2v, uint64_t seed,
-                       uint32_t canvas_id, hipStream_t s) {
-  hipLaunchKernelGGL(canvas_init_kernel, dim3(1), dim3(256), 0, s, tokens, status, N, log2v, seed, canvas_id);
+                       uint32_t canvas_id, int mask_id, hipStream_t s) {
+  hipLaunchKernelGGL(canvas_init_kernel, dim3(1), dim3(256), 0, s, tokens, status, N, log2v, seed, canvas_id,
+                     mask_id);
   return hipGetLastError();
 }
 
@@ -41,21 +45,26 @@ __global__ void __launch_bounds__(256) select_kernel(const float *__restrict__ e
                                                      int32_t *__restrict__ tokens, uint8_t *__restrict__ accept,
                                                      int32_t *__restrict__ status, int N, int log2v,
                                                      uint64_t limit, int rule, float conf_eps, uint64_t seed,
-                                                     uint32_t canvas_id, uint32_t step) {
+                                                     uint32_t canvas_id, uint32_t step, int mask_id) {
   __shared__ __align__(16) uint64_t keys[256];
   __shared__ __align__(16) uint64_t fix[256];
   __shared__ float fmin_s[4], fmax_s[4], fsum_s[4];
   const int i = threadIdx.x;
 
   float h = 0.f;
+  int32_t old = 0;
   if (i < N) {
     h = entropy[i];
     if (h <= 0.f) h = 0.f;  // clamp; NaN passes through
+    old = tokens[i];
   }
-  const uint64_t key = (i < N) ? (((uint64_t)__float_as_uint(h) << 32) | (uint32_t)i) : ~0ull;
+  // masked sampler: a decided (locked) position takes no part in the walk;
+  // its key sorts after every walked one and it adds nothing to their sums
+  const bool walked = i < N && (mask_id < 0 || old == mask_id);
+  const uint64_t key = walked ? (((uint64_t)__float_as_uint(h) << 32) | (uint32_t)i) : ~0ull;
   // h >= +0 or NaN, so the float bits order the finite entropies; NaN, inf
   // and absurd values sort after every finite one and end the walk
-  const bool finite = i < N && h < 1048576.0f;
+  const bool finite = walked && h < 1048576.0f;
   const uint64_t q = finite ? (uint64_t)((double)h * 4294967296.0) : 0ull;
   keys[i] = key;
   fix[i] = q;
@@ -85,11 +94,13 @@ __global__ void __launch_bounds__(256) select_kernel(const float *__restrict__ e
   // re-noise, new canvas, flags
   int changed = 0, conf = 1, acc = 0, isnan_ = 0;
   float hmin = INFINITY, hmax = -INFINITY, hsum = 0.f;
+  int masked = 0;
   if (i < N) {
     acc = acc_here;
-    const int32_t old = tokens[i];
-    const int32_t t = acc ? argmax[i] : uniform_token(seed, (uint32_t)i, step, canvas_id, 1u, log2v);
+    const int32_t t = acc ? argmax[i]
+                          : (mask_id >= 0 ? old : uniform_token(seed, (uint32_t)i, step, canvas_id, 1u, log2v));
     tokens[i] = t;
+    masked = mask_id >= 0 && t == mask_id;
     accept[i] = (uint8_t)acc;
     changed = (t != old);
     conf = (h < conf_eps);  // false for NaN
@@ -102,6 +113,7 @@ __global__ void __launch_bounds__(256) select_kernel(const float *__restrict__ e
   const int all_conf = __syncthreads_and(conf);
   const int n_acc = __syncthreads_count(acc);
   const int n_nan = __syncthreads_count(isnan_);
+  const int n_masked = __syncthreads_count(masked);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     hmin = fminf(hmin, __shfl_xor(hmin, o));
@@ -131,19 +143,20 @@ __global__ void __launch_bounds__(256) select_kernel(const float *__restrict__ e
     status[DG_ST_HMIN] = __float_as_int(fmin_s[0]);
     status[DG_ST_HMAX] = __float_as_int(fmax_s[0]);
     status[DG_ST_HMEAN] = __float_as_int(N > n_nan ? fsum_s[0] / (float)(N - n_nan) : 0.f);
+    status[DG_ST_MASKED] = mask_id >= 0 ? n_masked : -1;
   }
 }
 
 hipError_t select_step(const float *entropy, const int32_t *argmax, int32_t *tokens, uint8_t *accept,
                        int32_t *status, int N, int log2v, double gamma, int rule, float conf_eps,
-                       uint64_t seed, uint32_t canvas_id, uint32_t step, hipStream_t s) {
+                       uint64_t seed, uint32_t canvas_id, uint32_t step, int mask_id, hipStream_t s) {
   uint64_t limit = 0;
   if (gamma > 0.0) {
     const double x = gamma * 4294967296.0;
     limit = (x >= 18446744073709551615.0) ? ~0ull : (uint64_t)x;
   }
   hipLaunchKernelGGL(select_kernel, dim3(1), dim3(256), 0, s, entropy, argmax, tokens, accept, status, N,
-                     log2v, limit, rule, conf_eps, seed, canvas_id, step);
+                     log2v, limit, rule, conf_eps, seed, canvas_id, step, mask_id);
   return hipGetLastError();
 }
 

@@ -45,9 +45,10 @@ class Denoiser:
 
     def __init__(self, c: dict, inp: dict, capacity: int | None = None, max_prefill: int = 0,
                  accept_rule: int = B.DG_ACCEPT_SUM_MINUS_MAX, device="cuda",
-                 logits_dump: bool = False, candidate_rule: int = B.DG_CANDIDATE_ARGMAX):
+                 logits_dump: bool = False, candidate_rule: int = B.DG_CANDIDATE_ARGMAX,
+                 sampler: int = B.DG_SAMPLER_UNIFORM):
         self.c = c
-        self.cfg = B.make_config(c, accept_rule=accept_rule, candidate_rule=candidate_rule)
+        self.cfg = B.make_config(c, accept_rule=accept_rule, candidate_rule=candidate_rule, sampler=sampler)
         st = B.dg_validate_config(self.cfg)
         if st != B.DG_OK:
             raise B.DgError("dg_validate_config", st)
@@ -88,7 +89,7 @@ class Denoiser:
                 halt, st = self.should_stop(stable_n)
                 stats.append(st)
                 if halt:
-                    reason = "confident" if st.allconf else "stable"
+                    reason = "confident" if st.allconf else ("unmasked" if st.masked == 0 else "stable")
                     break
         return CanvasResult(self.canvas.tokens.clone(), n, reason, stats)
 
@@ -101,7 +102,9 @@ class Denoiser:
                                      temps, gamma, stop, stable_n, self.ws)
         reason = "budget"
         if stopped:
-            reason = "confident" if int(self.canvas.status[B.DG_ST_ALLCONF]) else "stable"
+            st = self.canvas.status.cpu()
+            reason = ("confident" if int(st[B.DG_ST_ALLCONF]) else
+                      "unmasked" if int(st[B.DG_ST_MASKED]) == 0 else "stable")
         return CanvasResult(self.canvas.tokens.clone(), n, reason, [])
 
     def block_diffusion(self, prompt: torch.Tensor, canvases: int, seed: int, steps: int,
