@@ -192,10 +192,11 @@ def main() -> int:
     temps = [D.temperature(c["sched"], c["T0"], c["T1"], s % c["steps"], c["steps"]) for s in
              range(max(args.steps, args.warmup, 20))]
 
-    def run(nsteps: int, canvas_id: int):
+    def run(nsteps: int, canvas_id: int, may_stop: bool = False) -> int:
         n, stopped = B.dg_run_canvas(den.cfg, den.w.s, den.cache.s, den.canvas.s, seed, canvas_id,
                                      temps[:nsteps], c["gamma"], True, 0, den.ws)
-        assert n == nsteps and not stopped
+        assert may_stop or (n == nsteps and not stopped)
+        return n
 
     run(args.warmup, 0)
     torch.cuda.synchronize()
@@ -208,17 +209,27 @@ def main() -> int:
     B.dg_profile_enable(False)
     lm_ms, lm_n, sc_ms, sc_n = B.dg_profile_read()
 
-    # The multinomial candidate rule ([P3] §5.3): the same loop with the draw
-    # kernel after the row combine (a shorter timed run)
-    den.cfg.candidate_rule = B.DG_CANDIDATE_MULTINOMIAL
-    n_mn = max(5, min(20, args.steps))
-    run(2, 2)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    run(n_mn, 3)
-    torch.cuda.synchronize()
-    dt_mn = time.perf_counter() - t1
-    den.cfg.candidate_rule = B.DG_CANDIDATE_ARGMAX
+    # The two variants, each the same loop over a shorter timed run: the
+    # multinomial candidate rule ([P3] §5.3: the draw kernel after the row
+    # combine) and the masked-diffusion sampler ([P3] §3.1: the canvas starts
+    # all [MASK]; its own stop, no [MASK] left, cannot fire within the run).
+    n_var = max(5, min(20, args.steps))
+
+    def timed_variant(**fields):
+        for k, v in fields.items():
+            setattr(den.cfg, k, v)
+        run(2, 2, True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        n = run(n_var, 3, True)
+        torch.cuda.synchronize()
+        dt_v = time.perf_counter() - t1
+        den.cfg.candidate_rule = B.DG_CANDIDATE_ARGMAX
+        den.cfg.sampler = B.DG_SAMPLER_UNIFORM
+        return n / dt_v
+
+    mn_steps_per_s = timed_variant(candidate_rule=B.DG_CANDIDATE_MULTINOMIAL)
+    masked_steps_per_s = timed_variant(sampler=B.DG_SAMPLER_MASKED)
 
     steps_per_s = args.steps / dt
     # every timed step but the first of the canvas uses self-conditioning
@@ -244,8 +255,10 @@ def main() -> int:
                      "bytes_per_launch": lm_head_bytes(c)},
         "selfcond_kernel": {"avg_launch_us": sc_avg_s * 1e6, "launches": sc_n,
                             "achieved_GBps": selfcond_bytes(c) / max(sc_avg_s, 1e-12) / 1e9},
-        "multinomial_candidates": {"steps_per_s": n_mn / dt_mn, "steps": n_mn,
+        "multinomial_candidates": {"steps_per_s": mn_steps_per_s, "steps": n_var,
                                    "note": "same loop with the two-level Gumbel-max draw of the candidate tokens"},
+        "masked_sampler": {"steps_per_s": masked_steps_per_s, "steps": n_var,
+                           "note": "same loop with the masked-diffusion sampler ([MASK] noise, locked positions)"},
         "adaptive_stop": {"fires_at_step": probe_steps if probe_stopped else None,
                           "timed_loop": "stop test run after every step, thresholds set so it cannot fire"},
     }
