@@ -276,6 +276,15 @@ def test_config2_bf16_multinomial_draw_replays():
     assert differ > 0
 
 
+def test_masked_sampler_with_multinomial_draw_replays():
+    """The two variants together (configuration 2): masked canvas, drawn candidates."""
+    c = W.config(2)
+    inp = W.make_inputs(c)
+    den = D.Denoiser(c, inp, candidate_rule=B.DG_CANDIDATE_MULTINOMIAL, sampler=B.DG_SAMPLER_MASKED)
+    multinomial_steps(c, inp, 4, den=den)
+    assert int(den.canvas.status[B.DG_ST_MASKED]) < c["N"]
+
+
 def test_full_size_multinomial_draw_replays():
     """V = 262144, d = 2816, 256 rows: two steps (the second self-conditioned)."""
     c = W.config(3)
@@ -312,21 +321,25 @@ def test_cache_untouched_by_denoise():
     assert den.cache.length == c["L"]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_prefill_append_incremental(dtype):
-    """Causal prefill of 300 tokens then 77 more (ragged), against the oracle."""
+@pytest.mark.parametrize("dtype,masked", [("bf16", False), ("f32", False), ("bf16", True)])
+def test_prefill_append_incremental(dtype, masked):
+    """Causal prefill of 300 tokens then 77 more (ragged), against the oracle;
+    masked: the masked sampler's [MASK] id V among them reads its own row."""
     if dtype == "bf16":
         c = W.config(2, L=0, V=8192, d=1024, F=1024, Hq=8, Hkv=4)
     else:
         c = W.config(1, L=0)
     cap = 400
     inp = W.make_inputs(c, seed=11)
-    den = D.Denoiser(c, inp, capacity=cap, max_prefill=300)
+    den = D.Denoiser(c, inp, capacity=cap, max_prefill=300,
+                     sampler=B.DG_SAMPLER_MASKED if masked else B.DG_SAMPLER_UNIFORM)
     om = oracle.model_from_inputs(inp)
     Hkv, hd, qw = c["Hkv"], c["hd"], c["Hq"] * c["hd"]
     kc, vc = np.zeros((Hkv, cap, hd)), np.zeros((Hkv, cap, hd))
     g = torch.Generator().manual_seed(5)
     toks = torch.randint(0, c["V"], (377,), generator=g, dtype=torch.int32)
+    if masked:
+        toks[::7] = c["V"]
     tol = 1e-4
     L = 0
     for lo, hi in [(0, 300), (300, 377)]:
@@ -342,7 +355,7 @@ def test_prefill_append_incremental(dtype):
         assert rel_frob(attn.float().cpu().numpy(), a_ref) <= tol
     assert not den.cache.k[:, L:].any()
     # keys/values of a token depend on the token only: one-shot append is bitwise equal
-    den2 = D.Denoiser(c, inp, capacity=cap, max_prefill=377)
+    den2 = D.Denoiser(c, inp, capacity=cap, max_prefill=377, sampler=den.cfg.sampler)
     den2.prefill(toks.cuda())
     assert torch.equal(den2.cache.k, den.cache.k) and torch.equal(den2.cache.v, den.cache.v)
     # capacity overflow is rejected without touching the cache

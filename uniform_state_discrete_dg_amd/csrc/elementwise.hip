@@ -316,29 +316,39 @@ hipError_t gumbel_test(const uint32_t *w, int n, int mode, float *out, hipStream
   return hipGetLastError();
 }
 
-// Reductions over the 256 threads of a row: within each wave by lane
-// exchanges, then across the 4 waves through LDS (two barriers).
+// Reductions over the NW waves of a row's workgroup: within each wave by lane
+// exchanges, then across the waves through LDS (two barriers).
+template <int NW>
 __device__ __forceinline__ float rc_sum(float v, float *sh) {
   v = warp_sum(v);
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
-  const float r = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  float r = sh[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r += sh[w];
   __syncthreads();
   return r;
 }
+template <int NW>
 __device__ __forceinline__ float2 rc_sum2(float a, float b, float *sh) {
   a = warp_sum(a);
   b = warp_sum(b);
   if ((threadIdx.x & 63) == 0) {
     sh[threadIdx.x >> 6] = a;
-    sh[4 + (threadIdx.x >> 6)] = b;
+    sh[NW + (threadIdx.x >> 6)] = b;
   }
   __syncthreads();
-  const float2 r = make_float2((sh[0] + sh[1]) + (sh[2] + sh[3]), (sh[4] + sh[5]) + (sh[6] + sh[7]));
+  float2 r = make_float2(sh[0], sh[NW]);
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    r.x += sh[w];
+    r.y += sh[NW + w];
+  }
   __syncthreads();
   return r;
 }
 // max of (value, lowest index on ties)
+template <int NW>
 __device__ __forceinline__ void rc_argmax(float &v, int &i, float *shv, int *shi) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -357,7 +367,7 @@ __device__ __forceinline__ void rc_argmax(float &v, int &i, float *shv, int *shi
   v = shv[0];
   i = shi[0];
 #pragma unroll
-  for (int w = 1; w < 4; ++w)
+  for (int w = 1; w < NW; ++w)
     if (shv[w] > v || (shv[w] == v && shi[w] < i)) {
       v = shv[w];
       i = shi[w];
@@ -387,29 +397,32 @@ __device__ __forceinline__ void rc_argmax(float &v, int &i, float *shv, int *shi
 // per-tile exponent R - r_t (capped at 255) to shift ([tile][256 rows],
 // uint8); tile_scale (nullable then) holds 2^-(R - r_t) g.  Without shift,
 // tile_scale is e^{m_t - M} / L for numerators relative to m_t itself.
-// RC_CACHE tiles per thread are held in registers (one read of the row's
-// statistics) when ntiles <= 256 * RC_CACHE; otherwise the passes re-read.
-constexpr int RC_CACHE = 16;
+// RC_NT threads per row; RC_CACHE tiles per thread are held in registers
+// (one read of the row's statistics) when ntiles <= RC_NT * RC_CACHE;
+// otherwise the passes re-read.
+constexpr int RC_NT = 512;
+constexpr int RC_NW = RC_NT / 64;
+constexpr int RC_CACHE = 4096 / RC_NT;
+constexpr int RC_D = 4096 / RC_NT;  // normalised-row values per thread: d <= 4096
 
 template <bool CACHED>
-__global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restrict__ stats, int ntiles,
+__global__ void __launch_bounds__(RC_NT) row_combine_kernel(const float4 *__restrict__ stats, int ntiles,
                                                           float inv_T, float *__restrict__ entropy,
                                                           int32_t *__restrict__ cand,
                                                           float *__restrict__ tile_scale,
                                                           float *__restrict__ row_scale, uint8_t *__restrict__ shift,
                                                           const float *__restrict__ n2, const bf16 *__restrict__ E,
                                                           int d, float2 *__restrict__ top) {
-  __shared__ float shv[8];
-  __shared__ int shi[4];
+  __shared__ float shv[2 * RC_NW];
+  __shared__ int shi[RC_NW];
   const int row = blockIdx.x;
   // the normalised row for the exact top logit, loaded before the argmax is known
-  constexpr int RC_D = 16;  // per thread: d <= 256 * RC_D
   float nv[RC_D];
   const bool fix = n2 != nullptr;
   if (fix) {
 #pragma unroll
     for (int i = 0; i < RC_D; ++i) {
-      const int k = threadIdx.x + 256 * i;
+      const int k = threadIdx.x + RC_NT * i;
       nv[i] = k < d ? n2[(int64_t)row * d + k] : 0.f;
     }
   }
@@ -419,16 +432,16 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
   if (CACHED) {
 #pragma unroll
     for (int i = 0; i < RC_CACHE; ++i) {
-      const int t = threadIdx.x + 256 * i;
+      const int t = threadIdx.x + RC_NT * i;
       c[i] = t < ntiles ? st[t] : make_float4(-INFINITY, 0.f, 0.f, __int_as_float(INT32_MAX));
     }
   }
-  const int nper = CACHED ? RC_CACHE : (ntiles + 255) / 256;
+  const int nper = CACHED ? RC_CACHE : (ntiles + RC_NT - 1) / RC_NT;
   float best = -INFINITY;
   int bidx = INT32_MAX;
 #pragma unroll
   for (int i = 0; i < nper; ++i) {
-    const int t = threadIdx.x + 256 * i;
+    const int t = threadIdx.x + RC_NT * i;
     if (t >= ntiles) break;
     const float4 v = tile(i, t);
     const int idx = __float_as_int(v.w);
@@ -437,7 +450,7 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
       bidx = idx;
     }
   }
-  rc_argmax(best, bidx, shv, shi);
+  rc_argmax<RC_NW>(best, bidx, shv, shi);
   const float Mz = best;
   // every tile maximum NaN (a NaN hidden state): no argmax; token 0 stands in
   // and nothing is recomputed (the entropy comes out NaN)
@@ -451,10 +464,10 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < RC_D; ++i) {
-      const int k = threadIdx.x + 256 * i;
+      const int k = threadIdx.x + RC_NT * i;
       if (k < d) part += nv[i] * bf16_to_f32(E[(int64_t)amax * d + k]);
     }
-    const float z_exact = rc_sum(part, shv);
+    const float z_exact = rc_sum<RC_NW>(part, shv);
     d_top = z_exact * inv_T - My;
     const float e = exp2f(d_top * LOG2E);
     l_fix = e - 1.f;
@@ -463,7 +476,7 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
   float L = 0.f, S = 0.f;
 #pragma unroll
   for (int i = 0; i < nper; ++i) {
-    const int t = threadIdx.x + 256 * i;
+    const int t = threadIdx.x + RC_NT * i;
     if (t >= ntiles) break;
     const float4 v = tile(i, t);
     const float dd = v.x * inv_T - My;
@@ -477,7 +490,7 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
     S += w * (sacc + dd * l);
   }
   {
-    const float2 LS = rc_sum2(L, S, shv);
+    const float2 LS = rc_sum2<RC_NW>(L, S, shv);
     L = LS.x;
     S = LS.y;
   }
@@ -486,7 +499,7 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
   const float g = exp2f(R - My * LOG2E) * invL;
 #pragma unroll
   for (int i = 0; i < nper; ++i) {
-    const int t = threadIdx.x + 256 * i;
+    const int t = threadIdx.x + RC_NT * i;
     if (t >= ntiles) break;
     const float mt = tile(i, t).x * inv_T;
     if (shift) {
@@ -510,12 +523,12 @@ __global__ void __launch_bounds__(256) row_combine_kernel(const float4 *__restri
 hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,
                        int32_t *cand, float *tile_scale, float *row_scale, uint8_t *shift, const float *n2,
                        const uint16_t *E, int d, float2 *top, hipStream_t s) {
-  if ((shift && M > 256) || (n2 && d > 256 * 16)) return hipErrorInvalidValue;
-  if (ntiles <= 256 * RC_CACHE)
-    hipLaunchKernelGGL(row_combine_kernel<true>, dim3(M), dim3(256), 0, s, tile_stats, ntiles, inv_T, entropy,
+  if ((shift && M > 256) || (n2 && d > RC_NT * RC_D)) return hipErrorInvalidValue;
+  if (ntiles <= RC_NT * RC_CACHE)
+    hipLaunchKernelGGL(row_combine_kernel<true>, dim3(M), dim3(RC_NT), 0, s, tile_stats, ntiles, inv_T, entropy,
                        cand, tile_scale, row_scale, shift, n2, E, d, top);
   else
-    hipLaunchKernelGGL(row_combine_kernel<false>, dim3(M), dim3(256), 0, s, tile_stats, ntiles, inv_T, entropy,
+    hipLaunchKernelGGL(row_combine_kernel<false>, dim3(M), dim3(RC_NT), 0, s, tile_stats, ntiles, inv_T, entropy,
                        cand, tile_scale, row_scale, shift, n2, E, d, top);
   return hipGetLastError();
 }
