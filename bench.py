@@ -113,6 +113,65 @@ def cpu_baseline(c: dict, inp: dict, rows=(2, 6)) -> dict:
                        f"{N} rows (s/step = {t_step:.2f})")}
 
 
+def batched_canvases(c: dict, inp: dict, w, cfg, sizes, steps: int, warmup: int) -> dict:
+    """Several users' canvases of the same workload (each with its own
+    2048-entry prefix cache, seed and canvas id) stepped together by
+    dg_denoise_step_batch: the projections and both table-streaming
+    contractions run once per step for the whole batch.  Every timed step is
+    self-conditioned (the warm-up steps come first)."""
+    import torch
+
+    from uniform_state_discrete_dg_amd import binding as B
+    from uniform_state_discrete_dg_amd import driver as D
+    g = torch.Generator().manual_seed(5150)
+    nmax = max(sizes)
+    caches = []
+    for b in range(nmax):
+        if b == 0:
+            k, v = inp["k_prefix"], inp["v_prefix"]
+        else:
+            shape = (c["Hkv"], c["L"], c["hd"])
+            k = torch.randn(shape, generator=g).bfloat16().float()
+            v = torch.randn(shape, generator=g).bfloat16().float()
+        caches.append(B.DeviceCache(cfg, c["L"], "cuda", k, v))
+    canv = [B.DeviceCanvas(cfg) for _ in range(nmax)]
+    ws = torch.empty(B.dg_workspace_bytes_batch(cfg, nmax), dtype=torch.uint8, device="cuda")
+    res = {}
+    for nb in sizes:
+        for b in range(nb):
+            B.dg_canvas_init(cfg, canv[b].s, 1000 + b, b)
+        cs, cv = [x.s for x in caches[:nb]], [x.s for x in canv[:nb]]
+
+        def go(n, s0):
+            for s in range(n):
+                T = D.temperature(c["sched"], c["T0"], c["T1"], (s0 + s) % c["steps"], c["steps"])
+                B.dg_denoise_step_batch(cfg, w.s, cs, cv, T, c["gamma"], ws)
+
+        go(warmup, 0)
+        torch.cuda.synchronize()
+        B.dg_profile_enable(True)
+        t0 = time.perf_counter()
+        go(steps, warmup)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        B.dg_profile_enable(False)
+        lm_ms, lm_n, sc_ms, sc_n = B.dg_profile_read()
+        sps = steps / dt
+        res[str(nb)] = {
+            "steps_per_s": sps, "ms_per_step": dt / steps * 1e3,
+            "canvas_tokens_per_s": sps * nb * c["N"],
+            "mfma_frac_of_bf16_peak": nb * step_flops(c, True) * sps / PEAK_BF16_FLOPS,
+            "lm_head_us": lm_ms / max(lm_n, 1) * 1e3,
+            "lm_head_tflops": nb * 2 * c["N"] * c["V"] * c["d"] / (lm_ms / max(lm_n, 1) / 1e3) / 1e12,
+            "selfcond_us": sc_ms / max(sc_n, 1) * 1e3,
+            "selfcond_tflops": nb * 2 * c["N"] * c["V"] * c["d"] / (sc_ms / max(sc_n, 1) / 1e3) / 1e12,
+        }
+    del ws, canv, caches
+    torch.cuda.empty_cache()
+    return {"workload": f"batched canvases, {c['name']}, one prefix cache per canvas", "steps": steps,
+            "warmup": warmup, "by_canvases": res}
+
+
 def block_diffusion(cfg_id: int = 5) -> dict:
     """Finished tokens per second of block diffusion: the prompt prefilled
     causally, then canvases denoised one after another (adaptive stop as
@@ -148,6 +207,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block-diffusion", action="store_true",
                     help="skip the block-diffusion run (prompt prefill + chained canvases)")
+    ap.add_argument("--batch", default="2,4,8",
+                    help="canvas counts of the batched-canvases run (empty: skip it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run the library's plain copy kernel over 1 GiB three times "
                          "(reference for memory-traffic counters)")
@@ -262,6 +323,11 @@ def main() -> int:
         "adaptive_stop": {"fires_at_step": probe_steps if probe_stopped else None,
                           "timed_loop": "stop test run after every step, thresholds set so it cannot fire"},
     }
+    sizes = [int(x) for x in args.batch.split(",") if x.strip()]
+    if sizes:
+        den.cfg.conf_eps = 0.005
+        out["batched_canvases"] = batched_canvases(c, inp, den.w, den.cfg, sizes, max(5, min(20, args.steps)),
+                                                   3)
     if not args.no_block_diffusion:
         del den
         torch.cuda.empty_cache()

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define DG_ABI_VERSION 3
+#define DG_ABI_VERSION 4
 
 typedef enum {
   DG_OK = 0,
@@ -278,6 +278,30 @@ dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cac
 dg_status dg_denoise_step(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache,
                           dg_canvas *canvas, float temperature, float accept_threshold_nats,
                           void *ws, size_t ws_bytes, void *stream);
+
+/* Batched canvases.  [P5] (current limitations) notes that several users
+ * cannot share one denoising pass the way autoregressive decoding shares a
+ * batch: each user's canvas runs its own loop.  This call steps n_canvases
+ * such canvases (each with its own cache, tokens, probabilities, seed and
+ * step counter) at once: their rows are stacked for the projections and the
+ * two table-streaming contractions, so the embedding table is read from HBM
+ * once per step for the whole batch instead of once per canvas; attention,
+ * the row statistics and the selection run per canvas.  Every canvas ends in
+ * exactly the state dg_denoise_step would give it (bit for bit), so a batch
+ * may mix canvases at different steps of their own schedules, with one
+ * temperature and threshold for the call.
+ *   caches:   host array of n_canvases cache descriptors (several may name
+ *             the same cache: it is only read);
+ *   canvases: host array of n_canvases canvases (distinct buffers), all with
+ *             the same has_prev (all past their first step, or none);
+ *   1 <= n_canvases <= DG_MAX_BATCH; ws_bytes >= dg_workspace_bytes_batch().
+ * Each canvas's step += 1 and has_prev = 1.  Errors as dg_denoise_step, plus
+ * DG_ERR_INVALID_ARG for a count out of range or mixed has_prev. */
+#define DG_MAX_BATCH 16
+size_t dg_workspace_bytes_batch(const dg_config *cfg, int32_t n_canvases);
+dg_status dg_denoise_step_batch(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *caches,
+                                dg_canvas *canvases, int32_t n_canvases, float temperature,
+                                float accept_threshold_nats, void *ws, size_t ws_bytes, void *stream);
 
 /* Adaptive stop, [P3] §5.3 and [P5] scheduler: stop when every entropy is
  * below conf_eps, or when the canvas has been unchanged for stable_steps

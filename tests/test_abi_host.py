@@ -38,7 +38,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert B.dg_abi_version() == 3
+    assert B.dg_abi_version() == 4
     for s in range(6):
         assert lib.dg_status_string(s)
 
@@ -247,3 +247,60 @@ def test_tiled_layout_helpers():
             assert T[((b * 3 + s) * 1024 + p) * 8 + col % 8] == X[row, col]
     pad = B.tiled_to_rows(T, 512, 96)[300:]
     assert not pad.any()
+
+
+def distinct_canvas(k, step=3, has_prev=1):
+    base = FAKE * (k + 2)
+    return B.dg_canvas(base, base + 0x100, base + 0x200, base + 0x300, base + 0x400, base + 0x500,
+                       base + 0x600, step, has_prev, 5, k)
+
+
+def call_batch(cfg, w, caches, cvs, T, g, ws_bytes, n=None):
+    n = len(cvs) if n is None else n
+    ca = (B.dg_kv_cache * max(len(caches), 1))(*caches)
+    cv = (B.dg_canvas * max(len(cvs), 1))(*cvs)
+    r = B.lib().dg_denoise_step_batch(ctypes.byref(cfg), ctypes.byref(w), ca, cv, n, T, g,
+                                      ctypes.c_void_p(FAKE), ws_bytes, None)
+    return r, [(c.step, c.has_prev) for c in cv[:len(cvs)]]
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4])
+def test_batch_workspace_bytes(lib, i):
+    cfg = cfg_of(i)
+    one = B.dg_workspace_bytes(cfg, 0)
+    sizes = [B.dg_workspace_bytes_batch(cfg, n) for n in range(1, B.DG_MAX_BATCH + 1)]
+    assert sizes[0] >= one - (cfg.canvas_len * cfg.vocab * 4 if cfg.dtype == B.DG_F32 else 0)
+    assert all(b >= a for a, b in zip(sizes, sizes[1:]))
+    assert sizes[-1] > sizes[0]
+    assert B.dg_workspace_bytes_batch(cfg, 0) == 0
+    assert B.dg_workspace_bytes_batch(cfg, B.DG_MAX_BATCH + 1) == 0
+
+
+def test_batch_step_validation(lib):
+    cfg = cfg_of(2)
+    w = fake_weights()
+    need = B.dg_workspace_bytes_batch(cfg, 3)
+    caches = [B.dg_kv_cache(FAKE, FAKE, 512, 512)] * 3
+    ok = [distinct_canvas(k) for k in range(3)]
+    before = [(3, 1)] * 3
+    # a workspace one byte short: the whole call is rejected, nothing stepped
+    assert call_batch(cfg, w, caches, ok, 1.0, 8.0, need - 1) == (B.DG_ERR_WORKSPACE, before)
+    assert call_batch(cfg, w, caches, ok, 1.0, 8.0, need, n=0)[0] == B.DG_ERR_INVALID_ARG
+    assert call_batch(cfg, w, caches, ok, 0.0, 8.0, need) == (B.DG_ERR_INVALID_ARG, before)
+    assert call_batch(cfg, w, caches, ok, 1.0, float("nan"), need)[0] == B.DG_ERR_INVALID_ARG
+    # mixed has_prev: the batch shares one self-conditioning pass
+    mixed = [distinct_canvas(0), distinct_canvas(1, has_prev=0), distinct_canvas(2)]
+    assert call_batch(cfg, w, caches, mixed, 1.0, 8.0, need)[0] == B.DG_ERR_INVALID_ARG
+    # two canvases on the same buffers
+    twin = [distinct_canvas(0), distinct_canvas(1), distinct_canvas(1)]
+    assert call_batch(cfg, w, caches, twin, 1.0, 8.0, need) == (B.DG_ERR_INVALID_ARG, before)
+    bad = [distinct_canvas(0), distinct_canvas(1), distinct_canvas(2)]
+    bad[2].status = None
+    assert call_batch(cfg, w, caches, bad, 1.0, 8.0, need)[0] == B.DG_ERR_INVALID_ARG
+    over = [B.dg_kv_cache(FAKE, FAKE, 512, 512), B.dg_kv_cache(FAKE, FAKE, 600, 512),
+            B.dg_kv_cache(FAKE, FAKE, 512, 512)]
+    assert call_batch(cfg, w, over, ok, 1.0, 8.0, need)[0] == B.DG_ERR_INVALID_ARG
+    many = [distinct_canvas(k) for k in range(B.DG_MAX_BATCH + 1)]
+    many_c = [caches[0]] * len(many)
+    big = B.dg_workspace_bytes_batch(cfg, B.DG_MAX_BATCH)
+    assert call_batch(cfg, w, many_c, many, 1.0, 8.0, big)[0] == B.DG_ERR_INVALID_ARG

@@ -26,6 +26,7 @@ DG_ACCEPT_SUM_MINUS_MAX, DG_ACCEPT_CUMSUM = 0, 1
 DG_CANDIDATE_ARGMAX, DG_CANDIDATE_MULTINOMIAL = 0, 1
 DG_SAMPLER_UNIFORM, DG_SAMPLER_MASKED = 0, 1
 DG_STATUS_WORDS = 16
+DG_MAX_BATCH = 16
 (DG_ST_ALLCONF, DG_ST_CHANGED, DG_ST_STABLE, DG_ST_ACCEPTED, DG_ST_NAN, DG_ST_STEP, DG_ST_HMIN,
  DG_ST_HMAX, DG_ST_HMEAN, DG_ST_MASKED) = range(10)
 TILE_V = 64  # vocabulary columns per softmax-statistics tile
@@ -78,6 +79,9 @@ SIGNATURES = {
                                   c_sz, vp]),
     "dg_denoise_step": (c_i32, [P(dg_config), P(dg_weights), P(dg_kv_cache), P(dg_canvas), c_f32,
                                 c_f32, vp, c_sz, vp]),
+    "dg_workspace_bytes_batch": (c_sz, [P(dg_config), c_i32]),
+    "dg_denoise_step_batch": (c_i32, [P(dg_config), P(dg_weights), P(dg_kv_cache), P(dg_canvas), c_i32,
+                                      c_f32, c_f32, vp, c_sz, vp]),
     "dg_should_stop": (c_i32, [P(dg_config), P(dg_canvas), c_i32, P(c_i32), P(dg_step_stats), vp]),
     "dg_run_canvas": (c_i32, [P(dg_config), P(dg_weights), P(dg_kv_cache), P(dg_canvas), c_u64, c_u32,
                               P(c_f32), c_i32, c_f32, c_i32, c_i32, vp, c_sz, vp, P(c_i32), P(c_i32)]),
@@ -184,6 +188,27 @@ def dg_denoise_step(cfg: dg_config, w: dg_weights, cache: dg_kv_cache, canvas: d
         ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), ctypes.byref(canvas),
         temperature, accept_threshold_nats, _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def dg_workspace_bytes_batch(cfg: dg_config, n_canvases: int) -> int:
+    return int(lib().dg_workspace_bytes_batch(ctypes.byref(cfg), n_canvases))
+
+
+def dg_denoise_step_batch(cfg: dg_config, w: dg_weights, caches, canvases, temperature: float,
+                          accept_threshold_nats: float, ws: torch.Tensor, stream=None) -> None:
+    """caches, canvases: equal-length sequences of dg_kv_cache / dg_canvas.
+    The canvases' host fields (step, has_prev) are updated in place."""
+    n = len(canvases)
+    if len(caches) != n:
+        raise ValueError("one cache descriptor per canvas")
+    ca = (dg_kv_cache * max(n, 1))(*caches)
+    cv = (dg_canvas * max(n, 1))(*canvases)
+    _check("dg_denoise_step_batch", lib().dg_denoise_step_batch(
+        ctypes.byref(cfg), ctypes.byref(w), ca, cv, n, temperature, accept_threshold_nats, _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+    for i in range(n):
+        canvases[i].step = cv[i].step
+        canvases[i].has_prev = cv[i].has_prev
 
 
 def dg_should_stop(cfg: dg_config, canvas: dg_canvas, stable_steps: int, stream=None):

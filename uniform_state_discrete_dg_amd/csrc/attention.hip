@@ -52,6 +52,7 @@ __global__ void __launch_bounds__(NTH * G) attn_split_kernel(AttnArgs a) {
   const int kbeg = z * a.keys_per_split;
   const int kend = min(nk, kbeg + a.keys_per_split);
   const float *Q = static_cast<const float *>(a.q);
+  const int64_t qhs = a.q_hstride ? a.q_hstride : (int64_t)a.nq * HD;
   const float *kA = static_cast<const float *>(a.kA), *vA = static_cast<const float *>(a.vA);
   const float *kB = static_cast<const float *>(a.kB), *vB = static_cast<const float *>(a.vB);
 
@@ -61,7 +62,7 @@ __global__ void __launch_bounds__(NTH * G) attn_split_kernel(AttnArgs a) {
   for (int s = 0; s < HD / 16; ++s) {
     float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
     if (q < a.nq) {
-      const float4 *src = reinterpret_cast<const float4 *>(Q + ((int64_t)h * a.nq + q) * HD + s * 16 + g4 * 8);
+      const float4 *src = reinterpret_cast<const float4 *>(Q + (int64_t)h * qhs + (int64_t)q * HD + s * 16 + g4 * 8);
       x0 = src[0];
       x1 = src[1];
     }
@@ -275,7 +276,7 @@ __global__ void __launch_bounds__(NTH * G) attn_split_kernel(AttnArgs a) {
 template <typename T>
 __global__ void attn_combine_kernel(const float *__restrict__ part_o, const float *__restrict__ part_ml,
                                     int splits, int nq, int Hq, int hd, T *__restrict__ out,
-                                    bf16 *__restrict__ out_split) {
+                                    bf16 *__restrict__ out_split, int64_t lo_off) {
   const int qh = blockIdx.x;
   const int q = qh / Hq, h = qh % Hq;
   const int e = threadIdx.x;
@@ -296,7 +297,7 @@ __global__ void attn_combine_kernel(const float *__restrict__ part_o, const floa
     if (out_split) {  // the output projection's operand: hi + lo terms
       const bf16 hi = f32_to_bf16(v);
       out_split[i] = hi;
-      out_split[(int64_t)nq * Hq * hd + i] = f32_to_bf16(v - bf16_to_f32(hi));
+      out_split[lo_off + i] = f32_to_bf16(v - bf16_to_f32(hi));
     }
   }
 }
@@ -323,7 +324,8 @@ hipError_t attention_mfma(const AttnArgs &a, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(attn_combine_kernel<float>, dim3(a.nq * a.Hq), dim3(HD), 0, s, a.part_o,
-                     a.part_ml, a.splits, a.nq, a.Hq, HD, static_cast<float *>(a.out), a.out_split);
+                     a.part_ml, a.splits, a.nq, a.Hq, HD, static_cast<float *>(a.out), a.out_split,
+                     a.out_lo_off ? a.out_lo_off : (int64_t)a.nq * a.Hq * HD);
   return hipGetLastError();
 }
 

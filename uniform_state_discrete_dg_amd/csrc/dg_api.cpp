@@ -89,7 +89,7 @@ StatsLayout stats_layout(const dg_config *c) {
 }
 
 struct Layout {
-  size_t h0, h1, nrm, nrm16, nrm_s, sc, sc_s, g, q, kc, vc, o, o_s, ap_o, ap_ml, sc_part, gpart, logits, total;
+  size_t h0, h1, nrm, nrm16, nrm_s, sc, sc_s, g, q, kc, vc, o, o_s, ap_o, ap_ml, sc_part, gpart, logits, tok, total;
   // prefill view (same region)
   size_t p_x, p_nrm, p_q, p_ap_o, p_ap_ml, p_gpart, p_total;
 };
@@ -98,10 +98,13 @@ struct Layout {
 // keeps each projection operand as a split pair (hi and lo bf16 terms, the
 // lo array after the hi array, 4 bytes per value: nrm_s, sc_s, o_s, and g,
 // which holds only that form there); nrm16 is the bf16 copy of the final
-// normalised state used by the LM head.
-Layout layout(const dg_config *c, int32_t nprefill, bool with_logits) {
+// normalised state used by the LM head.  nb > 1: a batch of nb canvases,
+// whose rows are stacked (N = nb * canvas_len rows) in every activation; the
+// attention partials serve one canvas at a time; tok holds the stacked ids.
+Layout layout(const dg_config *c, int32_t nprefill, bool with_logits, int nb = 1) {
   Layout L{};
-  const size_t N = c->canvas_len, V = c->vocab, d = c->d_model, F = c->ffn_hidden;
+  const size_t N = (size_t)nb * c->canvas_len, V = c->vocab, d = c->d_model, F = c->ffn_hidden;
+  const int Nc = c->canvas_len;
   const size_t Hq = c->n_q_heads, Hkv = c->n_kv_heads, hd = c->head_dim;
   const bool bf = c->dtype == DG_BF16;
   size_t off = 0;
@@ -125,9 +128,9 @@ Layout layout(const dg_config *c, int32_t nprefill, bool with_logits) {
   L.o_s = take(bf ? N * Hq * hd * 4 : 0);
   int splits = 1, kps = 0;
   // the plan for any key count never uses more splits than for 2^20 keys
-  dg::attention_plan((int)N, (int)Hq, 1 << 20, &splits, &kps);
-  L.ap_o = take((size_t)splits * Hq * N * hd * 4);
-  L.ap_ml = take((size_t)splits * Hq * N * 2 * 4);
+  dg::attention_plan(Nc, (int)Hq, 1 << 20, &splits, &kps);
+  L.ap_o = take((size_t)splits * Hq * Nc * hd * 4);
+  L.ap_ml = take((size_t)splits * Hq * Nc * 2 * 4);
   L.sc_part = take(bf ? (size_t)selfcond_ksplit(c) * N * d * 4 : 0);
   if (bf) {  // K-split partials of the projections, the largest of the step's four
     const int nqkv[3] = {(int)(Hq * hd), (int)(Hkv * hd), (int)(Hkv * hd)};
@@ -138,7 +141,8 @@ Layout layout(const dg_config *c, int32_t nprefill, bool with_logits) {
     m = std::max(m, dg::gemm_split_part_bytes((int)N, (int)F, nd, 1));
     L.gpart = take(m);
   }
-  L.logits = take((!bf || with_logits) ? N * V * 4 : 0);
+  L.logits = take(nb == 1 && (!bf || with_logits) ? N * V * 4 : 0);
+  L.tok = take(N * 4);
   L.total = off;
   // prefill
   off = 0;
@@ -617,9 +621,196 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
   return DG_OK;
 }
 
+// A batch of canvases on the bf16 path ([P5] current limitations: several
+// users' canvases in one pass over the table).  Rows are stacked canvas after
+// canvas in every activation; the projections and both table-streaming
+// contractions run once for the batch (their per-row results do not depend
+// on the other rows: the projections' K ranges are a function of K, the
+// contractions accumulate each row on its own), attention, the row
+// statistics and the selection once per canvas.  Validated by the caller.
+static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *caches,
+                                    dg_canvas *cvs, int B, float temperature, float gamma, void *ws,
+                                    hipStream_t s) {
+  const Layout L = layout(cfg, 0, false, B);
+  const int N = cfg->canvas_len, V = cfg->vocab, d = cfg->d_model, F = cfg->ffn_hidden;
+  const int Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads, hd = cfg->head_dim;
+  const int BN = B * N, ntiles = V / kTile;
+  const float inv_T = 1.0f / temperature;
+  char *base = static_cast<char *>(ws);
+  float *h0 = reinterpret_cast<float *>(base + L.h0);
+  float *h1 = reinterpret_cast<float *>(base + L.h1);
+  float *nrm = reinterpret_cast<float *>(base + L.nrm);
+  bf16 *nrm16 = reinterpret_cast<bf16 *>(base + L.nrm16);
+  float *sc = reinterpret_cast<float *>(base + L.sc), *G = reinterpret_cast<float *>(base + L.g);
+  float *q = reinterpret_cast<float *>(base + L.q), *kc = reinterpret_cast<float *>(base + L.kc);
+  float *vc = reinterpret_cast<float *>(base + L.vc), *o = reinterpret_cast<float *>(base + L.o);
+  float *gpart = reinterpret_cast<float *>(base + L.gpart);
+  bf16 *nrm_s = reinterpret_cast<bf16 *>(base + L.nrm_s);
+  bf16 *sc_s = reinterpret_cast<bf16 *>(base + L.sc_s);
+  bf16 *o_s = reinterpret_cast<bf16 *>(base + L.o_s);
+  int32_t *tok = reinterpret_cast<int32_t *>(base + L.tok);
+  const StatsLayout SL = stats_layout(cfg);
+  auto st_of = [&](int b, size_t off) { return static_cast<char *>(cvs[b].stats) + off; };
+  const uint16_t *Eb = static_cast<const uint16_t *>(w->E);
+
+  dg::TokenPtrs tp{};
+  for (int b = 0; b < B; ++b) tp.p[b] = cvs[b].tokens;
+  DG_TRY(dg::stack_tokens(tp, B, N, tok, s));
+  if (cvs[0].has_prev) {
+    // S = p_prev E for every canvas in one pass over E^T, then the merges
+    const int ks = selfcond_ksplit(cfg);
+    float *part = reinterpret_cast<float *>(base + L.sc_part);
+    const bf16 *tet = static_cast<const bf16 *>(w->E_pack) + pack_te_elems(cfg);
+    dg::EsCanvasesIn cin{};
+    for (int b = 0; b < B; ++b) {
+      cin.probs[b] = static_cast<const uint16_t *>(cvs[b].probs);
+      cin.shift[b] = reinterpret_cast<const uint8_t *>(st_of(b, SL.shift));
+    }
+    {
+      ProfScope ps(g_prof_sc, s);
+      DG_TRY(dg::selfcond_bf16_batch(cin, B, tet, N, d, V, true, part, ks, s));
+    }
+    for (int b = 0; b < B; ++b)
+      DG_TRY(dg::selfcond_reduce(part + (size_t)b * ks * N * d, ks, N, d,
+                                 reinterpret_cast<const float2 *>(st_of(b, SL.top)), cin.probs[b], V,
+                                 reinterpret_cast<const float *>(st_of(b, SL.rscale)), cin.shift[b], Eb,
+                                 sc + (size_t)b * N * d, sc_s + (size_t)b * N * d, s, (int64_t)BN * d));
+    dg::Epi eg = epi_store(G, false, F, F, 0);
+    eg.kind = dg::EPI_GELU;
+    eg.lo_off = (int64_t)BN * F;
+    DG_TRY(proj1(cfg, sc_s, BN, d, w->w_sc1, F, eg, gpart, s));
+    dg::Epi ea = epi_store(h0, true, d, d, 0);  // h0 = E[tokens] + W2 G
+    ea.kind = dg::EPI_ADD_ROW;
+    ea.gtab = Eb;
+    ea.gtok = tok;
+    ea.gV = V;
+    ea.gld = d;
+    ea.gmask = mask_row<uint16_t>(cfg, w);
+    DG_TRY(proj1_norm(cfg, G, BN, F, w->w_sc2, d, ea, gpart, w->g_attn, nullptr, nullptr, nrm_s, s));
+  } else {
+    DG_TRY(dg::gather_rows<bf16>(static_cast<const bf16 *>(w->E), tok, BN, d, V, mask_row<bf16>(cfg, w), h0, s));
+    DG_TRY(dg::rmsnorm_rows<bf16>(h0, static_cast<const bf16 *>(w->g_attn), BN, d, cfg->rms_eps, nullptr, nullptr,
+                                  nrm_s, s));
+  }
+  {
+    const void *W[3] = {w->wq, w->wk, w->wv};
+    const int No[3] = {Hq * hd, Hkv * hd, Hkv * hd};
+    const dg::Epi E3[3] = {epi_store(q, true, hd, hd, (int64_t)BN * hd),
+                           epi_store(kc, true, hd, hd, (int64_t)BN * hd),
+                           epi_store(vc, true, hd, hd, (int64_t)BN * hd)};
+    DG_TRY(proj(cfg, nrm_s, BN, d, 3, W, No, E3, gpart, s));
+  }
+  for (int b = 0; b < B; ++b) {  // canvas b: its queries over [its cache || its own keys]
+    dg::AttnArgs a{};
+    a.q = q + (size_t)b * N * hd;
+    a.q_hstride = (int64_t)BN * hd;
+    a.nq = N;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.hd = hd;
+    a.kA = caches[b].k;
+    a.vA = caches[b].v;
+    a.nA = caches[b].length;
+    a.capA = caches[b].capacity;
+    a.kB = kc + (size_t)b * N * hd;
+    a.vB = vc + (size_t)b * N * hd;
+    a.nB = N;
+    a.capB = BN;
+    a.causal = 0;
+    a.q_pos0 = 0;
+    a.out = o + (size_t)b * N * Hq * hd;
+    a.out_split = o_s + (size_t)b * N * Hq * hd;
+    a.out_lo_off = (int64_t)BN * Hq * hd;
+    a.part_o = reinterpret_cast<float *>(base + L.ap_o);
+    a.part_ml = reinterpret_cast<float *>(base + L.ap_ml);
+    dg::attention_plan(N, Hq, caches[b].length + N, &a.splits, &a.keys_per_split);
+    DG_TRY(dg::attention_mfma(a, s));
+  }
+  {
+    dg::Epi ea = epi_store(h1, true, d, d, 0);
+    ea.kind = dg::EPI_ADD;
+    ea.resid = h0;
+    DG_TRY(proj1_norm(cfg, o_s, BN, Hq * hd, w->wo, d, ea, gpart, w->g_final, nrm, nrm16, nullptr, s));
+  }
+  {
+    dg::EsCanvases ec{};
+    for (int b = 0; b < B; ++b) {
+      ec.probs[b] = static_cast<uint16_t *>(cvs[b].probs);
+      ec.tile_stats[b] = reinterpret_cast<float4 *>(st_of(b, SL.tstats));
+    }
+    ProfScope ps(g_prof_lm, s);
+    DG_TRY(dg::lm_head_bf16_batch(nrm16, B, N, d, static_cast<const uint16_t *>(w->E_pack), V, inv_T, ec, nullptr,
+                                  s));
+  }
+  for (int b = 0; b < B; ++b) {
+    dg_canvas *cv = &cvs[b];
+    const float4 *tstats = reinterpret_cast<const float4 *>(st_of(b, SL.tstats));
+    DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, nullptr,
+                           reinterpret_cast<float *>(st_of(b, SL.rscale)),
+                           reinterpret_cast<uint8_t *>(st_of(b, SL.shift)), nrm + (size_t)b * N * d, Eb, d,
+                           reinterpret_cast<float2 *>(st_of(b, SL.top)), s));
+    if (cfg->candidate_rule == DG_CANDIDATE_MULTINOMIAL) {
+      dg::DrawArgs draw{cv->seed, (uint32_t)cv->step, cv->canvas_id, static_cast<const uint16_t *>(cv->probs),
+                        nullptr};
+      DG_TRY(dg::multinomial_draw(tstats, N, ntiles, inv_T, draw, cv->argmax, s));
+    }
+    DG_TRY(dg::select_step(cv->entropy, cv->argmax, cv->tokens, cv->accept, cv->status, N, ilog2(V),
+                           (double)gamma, (int)cfg->accept_rule, cfg->conf_eps, cv->seed, cv->canvas_id,
+                           (uint32_t)cv->step, mask_id(cfg), s));
+  }
+  for (int b = 0; b < B; ++b) {
+    cvs[b].step += 1;
+    cvs[b].has_prev = 1;
+  }
+  return DG_OK;
+}
+
 dg_status dg_denoise_step(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache, dg_canvas *cv,
                           float temperature, float accept_threshold_nats, void *ws, size_t ws_bytes, void *stream) {
   return denoise_impl(cfg, w, cache, cv, temperature, accept_threshold_nats, ws, ws_bytes, stream, g_logits_dump);
+}
+
+// The batch's stacked layout; at least the single step's (the fp32 path steps
+// the canvases one by one).
+static size_t batch_ws_bytes(const dg_config *cfg, int32_t n) {
+  return std::max(layout(cfg, 0, false, n).total, layout(cfg, 0, false).total);
+}
+
+size_t dg_workspace_bytes_batch(const dg_config *cfg, int32_t n_canvases) {
+  if (check_config(cfg) != DG_OK || n_canvases < 1 || n_canvases > DG_MAX_BATCH) return 0;
+  return batch_ws_bytes(cfg, n_canvases);
+}
+
+dg_status dg_denoise_step_batch(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *caches,
+                                dg_canvas *canvases, int32_t n_canvases, float temperature,
+                                float accept_threshold_nats, void *ws, size_t ws_bytes, void *stream) {
+  dg_status st = check_config(cfg);
+  if (st != DG_OK) return st;
+  if (n_canvases < 1 || n_canvases > DG_MAX_BATCH || !caches || !canvases || !weights_ok(cfg, w))
+    return DG_ERR_INVALID_ARG;
+  if (!(std::isfinite(temperature) && temperature > 0.f)) return DG_ERR_INVALID_ARG;
+  if (std::isnan(accept_threshold_nats) || accept_threshold_nats < 0.f) return DG_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < n_canvases; ++b) {
+    const dg_kv_cache &c = caches[b];
+    if (!c.k || !c.v || c.length < 0 || c.length > c.capacity) return DG_ERR_INVALID_ARG;
+    if (!canvas_ok(&canvases[b]) || canvases[b].step < 0 || canvases[b].has_prev != canvases[0].has_prev)
+      return DG_ERR_INVALID_ARG;
+    for (int32_t a = 0; a < b; ++a)  // the canvases' buffers are written: no two may share them
+      if (canvases[a].tokens == canvases[b].tokens || canvases[a].probs == canvases[b].probs ||
+          canvases[a].stats == canvases[b].stats || canvases[a].status == canvases[b].status)
+        return DG_ERR_INVALID_ARG;
+  }
+  if (!ws || ws_bytes < batch_ws_bytes(cfg, n_canvases)) return DG_ERR_WORKSPACE;
+  if (cfg->dtype != DG_BF16) {  // the fp32 path: the single-canvas step, canvas after canvas
+    for (int32_t b = 0; b < n_canvases; ++b) {
+      st = denoise_impl(cfg, w, &caches[b], &canvases[b], temperature, accept_threshold_nats, ws, ws_bytes, stream,
+                        false);
+      if (st != DG_OK) return st;
+    }
+    return DG_OK;
+  }
+  return denoise_batch_bf16(cfg, w, caches, canvases, n_canvases, temperature, accept_threshold_nats, ws,
+                            static_cast<hipStream_t>(stream));
 }
 
 dg_status dg_should_stop(const dg_config *cfg, const dg_canvas *cv, int32_t stable_steps, int32_t *stop_host,

@@ -128,6 +128,27 @@ hipError_t gemm_f32(const GemmShapeF32 &g, const Epi &e, hipStream_t s);
 // E in the tiled layout; probs_tiled: the numerators, tiled ([M][V]).
 hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E_tiled, int V, float inv_T,
                         uint16_t *probs_tiled, float4 *tile_stats, float *logits_dump, hipStream_t s);
+// A batch of B canvases of N rows each (B * N rows stacked in A_tiled, row r
+// = row r % N of canvas r / N): canvas c's numerators and statistics go to
+// cv.probs[c] and cv.tile_stats[c].  Each row's results are those of the
+// single-canvas launch bit for bit.
+constexpr int ES_MAX_BATCH = DG_MAX_BATCH;
+struct EsCanvases {
+  uint16_t *probs[ES_MAX_BATCH];
+  float4 *tile_stats[ES_MAX_BATCH];
+};
+hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, const uint16_t *E_tiled, int V,
+                              float inv_T, const EsCanvases &cv, float *logits_dump, hipStream_t s);
+// The self-conditioning contraction of B canvases at once: canvas c's
+// operand cin.probs[c] (its exponents cin.shift[c] when scaled), partials at
+// partials + c * ksplit * M * N (the single-canvas layout per canvas).
+struct EsCanvasesIn {
+  const uint16_t *probs[ES_MAX_BATCH];
+  const uint8_t *shift[ES_MAX_BATCH];
+};
+hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *Et_tiled, int M, int N, int K,
+                               bool scaled, float *partials, int ksplit, hipStream_t s,
+                               SelfcondGuard guard = SelfcondGuard{nullptr, 0});
 // Same statistics from fp32 logits already in memory (fp32 path).
 hipError_t tile_stats_f32(const float *logits, int M, int V, float inv_T, float *probs,
                           float4 *tile_stats, hipStream_t s);
@@ -161,7 +182,7 @@ hipError_t multinomial_draw(const float4 *tile_stats, int M, int ntiles, float i
 hipError_t gumbel_test(const uint32_t *w, int n, int mode, float *out, hipStream_t s);
 
 // Attention over two key segments [A: nA keys][B: nB keys] per KV head, all
-// fp32 in memory.  q: [Hq][nq][hd]; k/v segment X: base + (g * capX + j) * hd.
+// fp32 in memory.  q: [Hq][nq][hd] (heads q_hstride apart); k/v segment X: base + (g * capX + j) * hd.
 // out: fp32 [nq][Hq*hd].  causal: query i may read keys <= q_pos0 + i.
 struct AttnArgs {
   const void *q;
@@ -173,6 +194,8 @@ struct AttnArgs {
   int causal, q_pos0;
   void *out;
   uint16_t *out_split;  // nullable: also the split pair of out (lo term at + nq * Hq * hd)
+  int64_t q_hstride;   // elements between q's heads (0: nq * hd)
+  int64_t out_lo_off;  // offset of out_split's lo terms (0: nq * Hq * hd)
   float *part_o;   // workspace [splits][Hq][nq][hd]
   float *part_ml;  // workspace [splits][Hq][nq][2]
   int splits, keys_per_split;
@@ -199,10 +222,16 @@ hipError_t rmsnorm_rows(const float *x, const T *g, int n, int d, float eps, flo
 // bits, exact p); nullable): the contraction used the value of probs
 // (tiled) at (row, a), scaled by 2^-shift of a's tile when shift is given,
 // times row_scale.  out_split (nullable): S also as a split pair [N][d], lo
-// term at + N * d.
+// term at + lo_off (0: + N * d).
 hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top,
                            const uint16_t *probs_tiled, int V, const float *row_scale, const uint8_t *shift,
-                           const uint16_t *E, float *out, uint16_t *out_split, hipStream_t s);
+                           const uint16_t *E, float *out, uint16_t *out_split, hipStream_t s, int64_t lo_off = 0);
+// The token ids of B canvases (src.p[c], N each) copied into one array
+// out[B * N], canvas after canvas.
+struct TokenPtrs {
+  const int32_t *p[ES_MAX_BATCH];
+};
+hipError_t stack_tokens(const TokenPtrs &src, int B, int N, int32_t *out, hipStream_t s);
 // In place (fp32 path): p(row, v) *= tile_scale[row][v / 64], numerators ->
 // probabilities; row-major [N][V].
 hipError_t normalize_probs_f32(float *probs, const float *tile_scale, int N, int V, hipStream_t s);

@@ -130,7 +130,7 @@ __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int kspli
                                        const float2 *__restrict__ top, const bf16 *__restrict__ probs, int V,
                                        const float *__restrict__ row_scale, const uint8_t *__restrict__ shift,
                                        const bf16 *__restrict__ E, float *__restrict__ out,
-                                       bf16 *__restrict__ out_split) {
+                                       bf16 *__restrict__ out_split, int64_t lo_off) {
   // one thread per 4 consecutive columns of one row; d % 4 == 0
   const int row = blockIdx.y;
   const int k = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -165,16 +165,31 @@ __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int kspli
     uint2 hi, lo;
     split4(acc, hi, lo);
     *reinterpret_cast<uint2 *>(out_split + i) = hi;
-    *reinterpret_cast<uint2 *>(out_split + count + i) = lo;
+    *reinterpret_cast<uint2 *>(out_split + lo_off + i) = lo;
   }
+}
+
+// out[c * N + i] = canvas c's token i: the token ids of a batch of canvases
+// as the stacked rows of the batched step.
+__global__ void stack_tokens_kernel(TokenPtrs src, int N, int total, int32_t *__restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int c = i / N;
+  out[i] = src.p[c][i - c * N];
+}
+
+hipError_t stack_tokens(const TokenPtrs &src, int B, int N, int32_t *out, hipStream_t s) {
+  if (B < 1 || B > ES_MAX_BATCH || N < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(stack_tokens_kernel, dim3((B * N + 255) / 256), dim3(256), 0, s, src, N, B * N, out);
+  return hipGetLastError();
 }
 
 hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top, const uint16_t *probs,
                            int V, const float *row_scale, const uint8_t *shift, const uint16_t *E, float *out,
-                           uint16_t *out_split, hipStream_t s) {
+                           uint16_t *out_split, hipStream_t s, int64_t lo_off) {
   if (d % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((d / 4 + 255) / 256, N), dim3(256), 0, s, part, ksplit, N, d,
-                     top, probs, V, row_scale, shift, E, out, out_split);
+                     top, probs, V, row_scale, shift, E, out, out_split, lo_off ? lo_off : (int64_t)N * d);
   return hipGetLastError();
 }
 

@@ -200,30 +200,45 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
 }
 
 // ---------------------------------------------------------------------------
-// LM head: workgroup = the canvas block x 256 vocabulary columns; a wave
-// holds 64 rows x 128 columns = two 64-column tiles of the softmax
-// statistics.  Per canvas row and tile a lane holds 32 of the 64 logits (its
-// partner lane the other 32): the max of z and its lowest column, exp(y - m)
-// written once as bf16 (tiled layout), l = sum exp(y - m) and
-// s = sum exp(y - m)(y - m), with y = z / T and m = zmax / T, are reduced in
-// registers plus one exchange with the partner.
+// LM head: workgroup = one 256-row block of the (stacked) canvas rows x 256
+// vocabulary columns; a wave holds 64 rows x 128 columns = two 64-column
+// tiles of the softmax statistics.  Per canvas row and tile a lane holds 32
+// of the 64 logits (its partner lane the other 32): the max of z and its
+// lowest column, exp(y - m) written once as bf16 (tiled layout), l = sum
+// exp(y - m) and s = sum exp(y - m)(y - m), with y = z / T and m = zmax / T,
+// are reduced in registers plus one exchange with the partner.
+// Several canvases (a batch) stack their rows: stacked row r is row r % N of
+// canvas r / N, whose numerators and statistics go to that canvas's buffers.
+// With more than one row block, the blocks that read the same 256 table rows
+// run back to back on one XCD, so the table tile comes from HBM once and from
+// that XCD's L2 for the other blocks.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__restrict__ At, int M, int K,
+template <bool BATCH>
+__global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__restrict__ At, int M, int N, int K,
                                                               const bf16 *__restrict__ Et, int V, float inv_T,
-                                                              bf16 *__restrict__ probs, float4 *__restrict__ tile_stats,
+                                                              EsCanvases cv, int nblk, int items,
                                                               float *__restrict__ logits) {
   extern __shared__ __align__(16) char lds[];
-  const int n0 = blockIdx.x * ES_BN;
+  int item = blockIdx.x;
+  if (BATCH) item = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;  // grid: a multiple of 8
+  if (BATCH && item >= items) return;
+  const int jt = BATCH ? item / nblk : item, bb = BATCH ? item % nblk : 0;
+  const int n0 = jt * ES_BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
   const int ksl = K / ES_BK;
   f32x16_t acc[2][4];
-  estream_tile<false>(At, Et + (int64_t)blockIdx.x * ksl * TL_ELEMS, nullptr, 0, ksl, lds, acc);
+  estream_tile<false>(At + (int64_t)bb * ksl * TL_ELEMS, Et + (int64_t)jt * ksl * TL_ELEMS, nullptr, 0, ksl, lds,
+                      acc);
   const int ntiles = V / 64;
 
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = wm * 64 + i * 32 + (lane & 31);
+    const int grow = bb * ES_BM + row;  // stacked row
+    const int c = BATCH ? min(grow, M - 1) / N : 0, lrow = grow - c * N;  // c < M / N even past the last row
+    bf16 *__restrict__ probs = cv.probs[c];
+    float4 *__restrict__ tile_stats = cv.tile_stats[c];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int tile = (n0 + wn * 128 + h * 64) / 64;
@@ -268,22 +283,22 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
         }
       l += __shfl_xor(l, 32);
       sacc += __shfl_xor(sacc, 32);
-      if (row < M) {
+      if (grow < M) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           // slice 2 tile + jj; the lane's four values of chunk q are elements 4g..4g+3
           bf16 *blk = probs + (int64_t)(2 * tile + jj) * TL_ELEMS + 4 * g;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<uint2 *>(blk + tl_pos(row, q) * 8) = make_uint2(pk[jj][2 * q], pk[jj][2 * q + 1]);
+            *reinterpret_cast<uint2 *>(blk + tl_pos(lrow, q) * 8) = make_uint2(pk[jj][2 * q], pk[jj][2 * q + 1]);
             if (logits) {
               const f32x16_t &z = acc[i][2 * h + jj];
-              *reinterpret_cast<float4 *>(logits + (int64_t)row * V + cbase + 32 * jj + 8 * q) =
+              *reinterpret_cast<float4 *>(logits + (int64_t)grow * V + cbase + 32 * jj + 8 * q) =
                   make_float4(z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]);
             }
           }
         }
-        if (g == 0) tile_stats[(int64_t)row * ntiles + tile] = make_float4(best, l, sacc, __int_as_float(bcol));
+        if (g == 0) tile_stats[(int64_t)lrow * ntiles + tile] = make_float4(best, l, sacc, __int_as_float(bcol));
       }
     }
   }
@@ -293,85 +308,122 @@ int estream_bm(int) { return ES_BM; }
 
 static size_t es_lds_bytes() { return (size_t)ES_STAGES * (2 * ES_SLICE + 256); }
 
-hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E_tiled, int V, float inv_T,
-                        uint16_t *probs_tiled, float4 *tile_stats, float *logits_dump, hipStream_t s) {
-  if (M > ES_BM || K % ES_BK || V % ES_BN) return hipErrorInvalidValue;
+hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, const uint16_t *E_tiled, int V,
+                              float inv_T, const EsCanvases &cv, float *logits_dump, hipStream_t s) {
+  if (B < 1 || B > ES_MAX_BATCH || N < 1 || N > ES_BM || K % ES_BK || V % ES_BN) return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(lm_head_es_kernel),
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(lm_head_es_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void *>(lm_head_es_kernel<true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess)
       return hipErrorInvalidValue;
     attr = true;
   }
-  hipLaunchKernelGGL(lm_head_es_kernel, dim3(V / ES_BN), dim3(ES_NT), es_lds_bytes(), s, A_tiled, M, K, E_tiled, V,
-                     inv_T, probs_tiled, tile_stats, logits_dump);
+  const int M = B * N, nblk = (M + ES_BM - 1) / ES_BM;
+  const int items = (V / ES_BN) * nblk;
+  if (B == 1)
+    hipLaunchKernelGGL(lm_head_es_kernel<false>, dim3(items), dim3(ES_NT), es_lds_bytes(), s, A_tiled, M, N, K,
+                       E_tiled, V, inv_T, cv, nblk, items, logits_dump);
+  else
+    hipLaunchKernelGGL(lm_head_es_kernel<true>, dim3((items + 7) / 8 * 8), dim3(ES_NT), es_lds_bytes(), s, A_tiled,
+                       M, N, K, E_tiled, V, inv_T, cv, nblk, items, logits_dump);
   return hipGetLastError();
 }
 
+hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E_tiled, int V, float inv_T,
+                        uint16_t *probs_tiled, float4 *tile_stats, float *logits_dump, hipStream_t s) {
+  EsCanvases cv{};
+  cv.probs[0] = probs_tiled;
+  cv.tile_stats[0] = tile_stats;
+  return lm_head_bf16_batch(A_tiled, 1, M, K, E_tiled, V, inv_T, cv, logits_dump, s);
+}
+
 // ---------------------------------------------------------------------------
-// Self-conditioning contraction, split over K = V: work item (kc, nt) =
-// K-chunk kc of the canvas x 256 columns of d.  The hardware hands
-// consecutive workgroups to the 8 XCDs in turn; the mapping below gives the
-// work items of one K-chunk to workgroups of one XCD where it can, so the
-// chunk of probabilities they share is fetched into that XCD's L2 once.
+// Self-conditioning contraction, split over K = V: work item (kc, nt, c) =
+// K-chunk kc of canvas c x 256 columns of d.  The hardware hands consecutive
+// workgroups to the 8 XCDs in turn; the mapping below gives consecutive work
+// items to workgroups of one XCD, so the items of one K-chunk (which share
+// each canvas's chunk of probabilities, and across canvases each chunk of
+// the table) run on one XCD where they can and fetch the shared data into
+// its L2 once.
 // ---------------------------------------------------------------------------
-template <bool SCALED>
-__global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(TiledGemm g, const uint8_t *__restrict__ shift,
-                                                               float *__restrict__ part, int ksplit, int ntn,
-                                                               int items, SelfcondGuard guard) {
+template <bool SCALED, bool BATCH>
+__global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin, const bf16 *__restrict__ Bt,
+                                                               int M, int N, int K, float *__restrict__ part,
+                                                               int ksplit, int ntn, int nb, int items,
+                                                               SelfcondGuard guard) {
   extern __shared__ __align__(16) char lds[];
-  const int b = blockIdx.x, nb = gridDim.x;
-  const int per_xcd = nb / 8;  // grid is a multiple of 8
+  const int b = blockIdx.x, ng = gridDim.x;
+  const int per_xcd = ng / 8;  // grid is a multiple of 8
   const int item = (b % 8) * per_xcd + b / 8;
   if (item >= items || guard.stopped()) return;
-  const int kc = item / ntn, nt = item % ntn;
-  const int ksl = g.K / ES_BK;
+  const int c = BATCH ? item % nb : 0, kn = BATCH ? item / nb : item;
+  const int kc = kn / ntn, nt = kn % ntn;
+  const int ksl = K / ES_BK;
   const int sb = (int)((int64_t)ksl * kc / ksplit), se = (int)((int64_t)ksl * (kc + 1) / ksplit);
   const int n0 = nt * ES_BN;
   f32x16_t acc[2][4];
-  estream_tile<SCALED>(g.A, g.B + (int64_t)nt * ksl * TL_ELEMS, shift, sb, se, lds, acc);
+  estream_tile<SCALED>(cin.probs[c], Bt + (int64_t)nt * ksl * TL_ELEMS, cin.shift[c], sb, se, lds, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  float *out = part + (int64_t)kc * g.M * g.N;
+  float *out = part + ((int64_t)c * ksplit + kc) * M * N;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = wm * 64 + i * 32 + (lane & 31);
-    if (row >= g.M) continue;
+    if (row >= M) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         // registers 4q..4q+3 are four consecutive columns
         const int col = n0 + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
-        if (col < g.N)
-          *reinterpret_cast<float4 *>(out + (int64_t)row * g.N + col) =
+        if (col < N)
+          *reinterpret_cast<float4 *>(out + (int64_t)row * N + col) =
               make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
       }
   }
 }
 
-hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partials, int ksplit, hipStream_t s,
-                         SelfcondGuard guard) {
-  if (g.M > ES_BM || g.K % 64 || g.N % 4 || ksplit < 1 || ksplit > g.K / ES_BK) return hipErrorInvalidValue;
+hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *Et_tiled, int M, int N, int K,
+                               bool scaled, float *partials, int ksplit, hipStream_t s, SelfcondGuard guard) {
+  if (B < 1 || B > ES_MAX_BATCH || M > ES_BM || K % 64 || N % 4 || ksplit < 1 || ksplit > K / ES_BK)
+    return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(selfcond_es_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void *>(selfcond_es_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess)
-      return hipErrorInvalidValue;
+    const void *fns[4] = {reinterpret_cast<const void *>(selfcond_es_kernel<false, false>),
+                          reinterpret_cast<const void *>(selfcond_es_kernel<true, false>),
+                          reinterpret_cast<const void *>(selfcond_es_kernel<false, true>),
+                          reinterpret_cast<const void *>(selfcond_es_kernel<true, true>)};
+    for (const void *f : fns)
+      if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess)
+        return hipErrorInvalidValue;
     attr = true;
   }
-  const int ntn = (g.N + ES_BN - 1) / ES_BN;
-  const int items = ntn * ksplit;
-  const int grid = (items + 7) / 8 * 8;
-  if (shift)
-    hipLaunchKernelGGL(selfcond_es_kernel<true>, dim3(grid), dim3(ES_NT), es_lds_bytes(), s, g, shift, partials,
-                       ksplit, ntn, items, guard);
+  const int ntn = (N + ES_BN - 1) / ES_BN;
+  const int items = ntn * ksplit * B;
+  const dim3 grid((items + 7) / 8 * 8);
+  if (scaled && B == 1)
+    hipLaunchKernelGGL((selfcond_es_kernel<true, false>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Et_tiled, M, N,
+                       K, partials, ksplit, ntn, B, items, guard);
+  else if (scaled)
+    hipLaunchKernelGGL((selfcond_es_kernel<true, true>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Et_tiled, M, N,
+                       K, partials, ksplit, ntn, B, items, guard);
+  else if (B == 1)
+    hipLaunchKernelGGL((selfcond_es_kernel<false, false>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Et_tiled, M,
+                       N, K, partials, ksplit, ntn, B, items, guard);
   else
-    hipLaunchKernelGGL(selfcond_es_kernel<false>, dim3(grid), dim3(ES_NT), es_lds_bytes(), s, g, shift, partials,
-                       ksplit, ntn, items, guard);
+    hipLaunchKernelGGL((selfcond_es_kernel<false, true>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Et_tiled, M,
+                       N, K, partials, ksplit, ntn, B, items, guard);
   return hipGetLastError();
+}
+
+hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partials, int ksplit, hipStream_t s,
+                         SelfcondGuard guard) {
+  EsCanvasesIn cin{};
+  cin.probs[0] = reinterpret_cast<const bf16 *>(g.A);
+  cin.shift[0] = shift;
+  return selfcond_bf16_batch(cin, 1, g.B, g.M, g.N, g.K, shift != nullptr, partials, ksplit, s, guard);
 }
 
 }  // namespace dg
