@@ -114,11 +114,13 @@ def cpu_baseline(c: dict, inp: dict, rows=(2, 6)) -> dict:
 
 
 def batched_canvases(c: dict, inp: dict, w, cfg, sizes, steps: int, warmup: int) -> dict:
-    """Several users' canvases of the same workload (each with its own
-    2048-entry prefix cache, seed and canvas id) stepped together by
+    """Several users' canvases of the same shapes (each with its own prefix
+    cache of c["L"] entries, seed and canvas id) stepped together by
     dg_denoise_step_batch: the projections and both table-streaming
-    contractions run once per step for the whole batch.  Every timed step is
-    self-conditioned (the warm-up steps come first)."""
+    contractions run once per step for the whole batch (one canvas: the
+    single-canvas kernels).  Every timed step is self-conditioned (the
+    warm-up steps come first).  canvas 0's prefix is inp's when it has
+    c["L"] entries, every other one seeded N(0, 1) rounded to bf16."""
     import torch
 
     from uniform_state_discrete_dg_amd import binding as B
@@ -127,7 +129,7 @@ def batched_canvases(c: dict, inp: dict, w, cfg, sizes, steps: int, warmup: int)
     nmax = max(sizes)
     caches = []
     for b in range(nmax):
-        if b == 0:
+        if b == 0 and inp["k_prefix"].shape[1] == c["L"]:
             k, v = inp["k_prefix"], inp["v_prefix"]
         else:
             shape = (c["Hkv"], c["L"], c["hd"])
@@ -168,8 +170,8 @@ def batched_canvases(c: dict, inp: dict, w, cfg, sizes, steps: int, warmup: int)
         }
     del ws, canv, caches
     torch.cuda.empty_cache()
-    return {"workload": f"batched canvases, {c['name']}, one prefix cache per canvas", "steps": steps,
-            "warmup": warmup, "by_canvases": res}
+    return {"workload": f"batched canvases, {c['name']}, one prefix cache of {c['L']} per canvas",
+            "steps": steps, "warmup": warmup, "by_canvases": res}
 
 
 def block_diffusion(cfg_id: int = 5) -> dict:
@@ -207,8 +209,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block-diffusion", action="store_true",
                     help="skip the block-diffusion run (prompt prefill + chained canvases)")
-    ap.add_argument("--batch", default="2,4,8",
+    ap.add_argument("--batch", default="1,2,4,8",
                     help="canvas counts of the batched-canvases run (empty: skip it)")
+    ap.add_argument("--batch-small", default="1,2,4",
+                    help="canvas counts of the batched run at 128-token canvases with a 4096-entry "
+                         "prefix (the latency-sensitive shapes; empty: skip it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run the library's plain copy kernel over 1 GiB three times "
                          "(reference for memory-traffic counters)")
@@ -324,10 +329,16 @@ def main() -> int:
                           "timed_loop": "stop test run after every step, thresholds set so it cannot fire"},
     }
     sizes = [int(x) for x in args.batch.split(",") if x.strip()]
+    nb_steps = max(5, min(20, args.steps))
     if sizes:
         den.cfg.conf_eps = 0.005
-        out["batched_canvases"] = batched_canvases(c, inp, den.w, den.cfg, sizes, max(5, min(20, args.steps)),
-                                                   3)
+        out["batched_canvases"] = batched_canvases(c, inp, den.w, den.cfg, sizes, nb_steps, 3)
+    small = [int(x) for x in args.batch_small.split(",") if x.strip()]
+    if small:
+        # same table and weight shapes (V, d, heads, F) as the main workload, so its weights serve
+        c4 = W.config(4)
+        assert all(c4[k] == c[k] for k in ("V", "d", "Hq", "Hkv", "hd", "F", "dtype"))
+        out["batched_small_canvases"] = batched_canvases(c4, inp, den.w, B.make_config(c4), small, nb_steps, 3)
     if not args.no_block_diffusion:
         del den
         torch.cuda.empty_cache()

@@ -88,17 +88,23 @@ def run_equal(c, inp, nb, nsteps, **kw):
     return bt
 
 
-@pytest.mark.parametrize("case", ["cfg2_n256_b3", "cfg2_n256_b1", "n128_b3", "ragged_n200_b2", "cfg1_f32_b3"])
+@pytest.mark.parametrize("case", ["cfg2_n256_b3", "cfg2_n256_b1", "n128_b3", "n128_b2", "ragged_n100_b4",
+                                  "ragged_n200_b2", "cfg1_f32_b3"])
 def test_batch_equals_single_steps(case):
-    """N = 256 (one row block per canvas), N = 128 (two canvases share the
-    LM head's row blocks), N = 200 (canvases straddle row blocks), and the
-    fp32 configuration (canvas after canvas)."""
+    """N = 256 (one row block per canvas), N <= 128 (two canvases share a
+    256-row block in both table-streaming contractions; an odd count leaves
+    the last block half its own padding), N = 200 (canvases straddle the LM
+    head's row blocks), and the fp32 configuration (canvas after canvas)."""
     if case == "cfg2_n256_b3":
         c, nb = W.config(2), 3
     elif case == "cfg2_n256_b1":
         c, nb = W.config(2), 1
     elif case == "n128_b3":
         c, nb = W.config(2, N=128, V=16384), 3
+    elif case == "n128_b2":
+        c, nb = W.config(2, N=128, V=16384), 2
+    elif case == "ragged_n100_b4":
+        c, nb = W.config(2, N=100, L=60, V=8192, d=1024, F=1024), 4
     elif case == "ragged_n200_b2":
         c, nb = W.config(2, N=200, L=100, V=8192, d=1024, F=1024), 2
     else:
@@ -113,11 +119,14 @@ def test_batch_multinomial_and_masked_equal_single():
     run_equal(c, inp, 2, 3, sampler=B.DG_SAMPLER_MASKED)
 
 
-def test_batch_full_vocab_equal_single():
-    """V = 262144, d = 2816, GQA 16/8 (the large-vocabulary canvas), two
-    canvases with different prefixes, two steps (the second self-conditioned)."""
-    c = W.config(3)
-    run_equal(c, W.make_inputs(c), 2, 2)
+@pytest.mark.parametrize("cfg_id,nb", [(3, 2), (4, 3)])
+def test_batch_full_vocab_equal_single(cfg_id, nb):
+    """V = 262144, d = 2816, GQA 16/8: the large-vocabulary canvas (N = 256)
+    and the latency-sensitive one (N = 128, prefix 4096, canvases paired in
+    the contractions), canvases with different prefixes, two steps (the
+    second self-conditioned)."""
+    c = W.config(cfg_id)
+    run_equal(c, W.make_inputs(c), nb, 2)
 
 
 def test_batch_oracle_lockstep():

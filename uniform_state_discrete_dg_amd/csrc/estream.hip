@@ -71,10 +71,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // field: a saturating subtraction of shift << 7 from each 16-bit value
 // (positive values; anything scaled below the normal range becomes zero or
 // a denormal).
-template <bool SCALED>
+template <bool SCALED, bool PAIR = false>
 __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const bf16 *__restrict__ Bt,
                                              const uint8_t *__restrict__ shift, int sb, int se, char *lds,
-                                             f32x16_t (&acc)[2][4]) {
+                                             f32x16_t (&acc)[2][4], const bf16 *__restrict__ At2 = nullptr,
+                                             const uint8_t *__restrict__ shift2 = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r32 = lane & 31, g = lane >> 5;
@@ -90,7 +91,12 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   if (nk <= 0) return;
   // DMA: this wave copies 2 KB of each operand slice (2 instructions of 64
   // lanes x 16 bytes), chunks p = (2 wave + u) * 64 + lane.
-  const bf16 *asrc = At + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
+  // PAIR: rows 128..255 of the canvas operand (chunks 512..1023, copied by
+  // waves 4..7) are rows 0..127 of a second block At2, and their exponents
+  // (bytes 128..255 of a tile's row, lanes 32..63) rows 0..127 of shift2.
+  const bf16 *asrc = (PAIR && wave >= 4) ? At2 + (int64_t)sb * TL_ELEMS + ((wave - 4) * 2 * 64 + lane) * 8
+                                         : At + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
+  const uint8_t *ssrc = !SCALED ? nullptr : (PAIR && lane >= 32) ? shift2 + (lane - 32) * 4 : shift + lane * 4;
   const bf16 *bsrc = Bt + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
   char *lds_shift = lds + ES_STAGES * 2 * ES_SLICE;  // SCALED: [stage][256] bytes
   auto issue = [&](int slice, int stage) {
@@ -102,7 +108,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
       __builtin_amdgcn_global_load_lds(bsrc + off + u * 512, st + ES_SLICE + (wave * 2 + u) * 1024, 16, 0, 0);
     }
     if (SCALED && wave == (slice & 7))  // the slice tile's 256 row exponents, 4 bytes per lane
-      __builtin_amdgcn_global_load_lds(shift + (int64_t)((sb + min(slice, nk - 1)) >> 1) * 256 + lane * 4,
+      __builtin_amdgcn_global_load_lds(ssrc + (int64_t)((sb + min(slice, nk - 1)) >> 1) * 256,
                                        lds_shift + stage * 256, 4, 0, 0);
   };
   // DMA instructions per slice per wave: 4, plus the exponents of slice s
@@ -348,7 +354,10 @@ hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E
 // the table) run on one XCD where they can and fetch the shared data into
 // its L2 once.
 // ---------------------------------------------------------------------------
-template <bool SCALED, bool BATCH>
+// MODE: 0 one canvas; 1 a batch, one canvas per 256-row block; 2 a batch of
+// canvases of at most 128 rows, two per block (canvas 2p in rows 0..127,
+// canvas 2p + 1 in rows 128..255, read from its own buffers).
+template <bool SCALED, int MODE>
 __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin, const bf16 *__restrict__ Bt,
                                                                int M, int N, int K, float *__restrict__ part,
                                                                int ksplit, int ntn, int nb, int items,
@@ -358,20 +367,31 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin,
   const int per_xcd = ng / 8;  // grid is a multiple of 8
   const int item = (b % 8) * per_xcd + b / 8;
   if (item >= items || guard.stopped()) return;
-  const int c = BATCH ? item % nb : 0, kn = BATCH ? item / nb : item;
+  const int nblk = MODE == 2 ? (nb + 1) / 2 : nb;  // canvas operand blocks
+  const int blk = MODE == 0 ? 0 : item % nblk, kn = MODE == 0 ? item : item / nblk;
   const int kc = kn / ntn, nt = kn % ntn;
   const int ksl = K / ES_BK;
   const int sb = (int)((int64_t)ksl * kc / ksplit), se = (int)((int64_t)ksl * (kc + 1) / ksplit);
   const int n0 = nt * ES_BN;
   f32x16_t acc[2][4];
-  estream_tile<SCALED>(cin.probs[c], Bt + (int64_t)nt * ksl * TL_ELEMS, cin.shift[c], sb, se, lds, acc);
+  const bf16 *Bn = Bt + (int64_t)nt * ksl * TL_ELEMS;
+  if (MODE == 2) {
+    const int c0 = 2 * blk, c1 = c0 + 1;
+    // an odd batch's last block: its upper half is the canvas's own padding rows
+    const bf16 *A2 = c1 < nb ? cin.probs[c1] : cin.probs[c0] + 512 * 8;
+    const uint8_t *s2 = c1 < nb ? cin.shift[c1] : cin.shift[c0] + 128;
+    estream_tile<SCALED, true>(cin.probs[c0], Bn, cin.shift[c0], sb, se, lds, acc, A2, s2);
+  } else {
+    estream_tile<SCALED>(cin.probs[blk], Bn, cin.shift[blk], sb, se, lds, acc);
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  float *out = part + ((int64_t)c * ksplit + kc) * M * N;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = wm * 64 + i * 32 + (lane & 31);
-    if (row >= M) continue;
+    const int c = MODE == 2 ? 2 * blk + (row >> 7) : blk, lrow = MODE == 2 ? row & 127 : row;
+    if (lrow >= M || c >= nb) continue;
+    float *out = part + ((int64_t)c * ksplit + kc) * M * N;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -379,7 +399,7 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin,
         // registers 4q..4q+3 are four consecutive columns
         const int col = n0 + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
         if (col < N)
-          *reinterpret_cast<float4 *>(out + (int64_t)row * N + col) =
+          *reinterpret_cast<float4 *>(out + (int64_t)lrow * N + col) =
               make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
       }
   }
@@ -391,30 +411,34 @@ hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *E
     return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
-    const void *fns[4] = {reinterpret_cast<const void *>(selfcond_es_kernel<false, false>),
-                          reinterpret_cast<const void *>(selfcond_es_kernel<true, false>),
-                          reinterpret_cast<const void *>(selfcond_es_kernel<false, true>),
-                          reinterpret_cast<const void *>(selfcond_es_kernel<true, true>)};
+    const void *fns[6] = {reinterpret_cast<const void *>(selfcond_es_kernel<false, 0>),
+                          reinterpret_cast<const void *>(selfcond_es_kernel<true, 0>),
+                          reinterpret_cast<const void *>(selfcond_es_kernel<false, 1>),
+                          reinterpret_cast<const void *>(selfcond_es_kernel<true, 1>),
+                          reinterpret_cast<const void *>(selfcond_es_kernel<false, 2>),
+                          reinterpret_cast<const void *>(selfcond_es_kernel<true, 2>)};
     for (const void *f : fns)
       if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess)
         return hipErrorInvalidValue;
     attr = true;
   }
+  const int mode = B == 1 ? 0 : (M <= ES_BM / 2 ? 2 : 1);
   const int ntn = (N + ES_BN - 1) / ES_BN;
-  const int items = ntn * ksplit * B;
+  const int items = ntn * ksplit * (mode == 2 ? (B + 1) / 2 : B);
   const dim3 grid((items + 7) / 8 * 8);
-  if (scaled && B == 1)
-    hipLaunchKernelGGL((selfcond_es_kernel<true, false>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Et_tiled, M, N,
-                       K, partials, ksplit, ntn, B, items, guard);
-  else if (scaled)
-    hipLaunchKernelGGL((selfcond_es_kernel<true, true>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Et_tiled, M, N,
-                       K, partials, ksplit, ntn, B, items, guard);
-  else if (B == 1)
-    hipLaunchKernelGGL((selfcond_es_kernel<false, false>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Et_tiled, M,
-                       N, K, partials, ksplit, ntn, B, items, guard);
-  else
-    hipLaunchKernelGGL((selfcond_es_kernel<false, true>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Et_tiled, M,
-                       N, K, partials, ksplit, ntn, B, items, guard);
+#define DG_SC_LAUNCH(SC, MD)                                                                                    \
+  hipLaunchKernelGGL((selfcond_es_kernel<SC, MD>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Et_tiled, M, N, K, \
+                     partials, ksplit, ntn, B, items, guard)
+  if (scaled) {
+    if (mode == 0) DG_SC_LAUNCH(true, 0);
+    else if (mode == 1) DG_SC_LAUNCH(true, 1);
+    else DG_SC_LAUNCH(true, 2);
+  } else {
+    if (mode == 0) DG_SC_LAUNCH(false, 0);
+    else if (mode == 1) DG_SC_LAUNCH(false, 1);
+    else DG_SC_LAUNCH(false, 2);
+  }
+#undef DG_SC_LAUNCH
   return hipGetLastError();
 }
 
