@@ -89,7 +89,7 @@ def run_equal(c, inp, nb, nsteps, **kw):
 
 
 @pytest.mark.parametrize("case", ["cfg2_n256_b3", "cfg2_n256_b1", "n128_b3", "n128_b2", "ragged_n100_b4",
-                                  "ragged_n200_b2", "cfg1_f32_b3"])
+                                  "ragged_n200_b2", "cfg1_f32_b3", "n16_b16_max"])
 def test_batch_equals_single_steps(case):
     """N = 256 (one row block per canvas), N <= 128 (two canvases share a
     256-row block in both table-streaming contractions; an odd count leaves
@@ -103,6 +103,8 @@ def test_batch_equals_single_steps(case):
         c, nb = W.config(2, N=128, V=16384), 3
     elif case == "n128_b2":
         c, nb = W.config(2, N=128, V=16384), 2
+    elif case == "n16_b16_max":  # the largest batch the library takes
+        c, nb = W.config(2, N=16, L=40, V=8192, d=1024, F=1024), B.DG_MAX_BATCH
     elif case == "ragged_n100_b4":
         c, nb = W.config(2, N=100, L=60, V=8192, d=1024, F=1024), 4
     elif case == "ragged_n200_b2":
