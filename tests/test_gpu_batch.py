@@ -114,6 +114,29 @@ def test_batch_equals_single_steps(case):
     run_equal(c, W.make_inputs(c, seed=W.weight_seed(2) + len(case)), nb, 3)
 
 
+def test_batch_canvases_at_different_steps():
+    """Canvases that joined at different times: canvas b has run b + 1
+    single steps before the batch takes over (its own step counter feeds its
+    Philox counters and, under the multinomial rule, its draws); the batch
+    must still match each canvas's single-step twin bit for bit."""
+    c = W.config(2, V=16384)
+    inp = W.make_inputs(c, seed=5151)
+    bt = Batch(c, inp, 3, candidate_rule=B.DG_CANDIDATE_MULTINOMIAL)
+    bt.init()
+    for b in range(3):
+        for s in range(b + 1):
+            T = D.temperature(c["sched"], c["T0"], c["T1"], s, c["steps"])
+            for cv in (bt.cv[b], bt.twin[b]):
+                B.dg_denoise_step(bt.cfg, bt.w.s, bt.caches[b].s, cv.s, T, c["gamma"], bt.ws1)
+    torch.cuda.synchronize()
+    bt.assert_equal("joined")
+    assert [x.s.step for x in bt.cv] == [1, 2, 3]
+    for s in range(3, 6):
+        bt.step(D.temperature(c["sched"], c["T0"], c["T1"], s, c["steps"]), c["gamma"])
+        bt.assert_equal(s)
+    assert [x.s.step for x in bt.cv] == [4, 5, 6]
+
+
 def test_batch_multinomial_and_masked_equal_single():
     c = W.config(2, V=16384)
     inp = W.make_inputs(c, seed=4242)

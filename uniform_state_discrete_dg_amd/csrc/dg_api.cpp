@@ -592,9 +592,16 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
                               static_cast<uint16_t *>(cv->probs), tstats, dump ? logits : nullptr, s));
     }
     // the numerators stay as stored: the next step's contraction applies the
-    // power-of-two tile exponents and the row factor
-    DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, nullptr, rscale, shift, nrm,
-                           static_cast<const uint16_t *>(w->E), d, top, s));
+    // power-of-two tile exponents and the row factor (the batch launch with
+    // one canvas: a batched step runs this same code for each of its rows)
+    dg::RowCombineBatch rc{};
+    rc.stats[0] = tstats;
+    rc.entropy[0] = cv->entropy;
+    rc.cand[0] = cv->argmax;
+    rc.row_scale[0] = rscale;
+    rc.shift[0] = shift;
+    rc.top[0] = top;
+    DG_TRY(dg::row_combine_batch(rc, 1, N, ntiles, inv_T, nrm, static_cast<const uint16_t *>(w->E), d, s));
   } else {
     dg::GemmShapeF32 g{nrm, d, 1, static_cast<const float *>(w->E), d, 1, N, V, d, nullptr, 0};
     DG_TRY(dg::gemm_f32(g, epi_store(logits, true, V, V, 0), s));
@@ -612,10 +619,20 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
       draw.num_f32 = static_cast<const float *>(cv->probs);
     DG_TRY(dg::multinomial_draw(tstats, N, ntiles, inv_T, draw, cv->argmax, s));
   }
-  // 5. accept / re-noise / stop flags
-  DG_TRY(dg::select_step(cv->entropy, cv->argmax, cv->tokens, cv->accept, cv->status, N, ilog2(V), (double)gamma,
-                         (int)cfg->accept_rule, cfg->conf_eps, cv->seed, cv->canvas_id, (uint32_t)cv->step,
-                         mask_id(cfg), s));
+  // 5. accept / re-noise / stop flags (the batch launch with one canvas)
+  {
+    dg::SelectBatch sel{};
+    sel.entropy[0] = cv->entropy;
+    sel.argmax[0] = cv->argmax;
+    sel.tokens[0] = cv->tokens;
+    sel.accept[0] = cv->accept;
+    sel.status[0] = cv->status;
+    sel.seed[0] = cv->seed;
+    sel.canvas_id[0] = cv->canvas_id;
+    sel.step[0] = (uint32_t)cv->step;
+    DG_TRY(dg::select_step_batch(sel, 1, N, ilog2(V), (double)gamma, (int)cfg->accept_rule, cfg->conf_eps,
+                                 mask_id(cfg), s));
+  }
   cv->step += 1;
   cv->has_prev = 1;
   return DG_OK;
@@ -742,21 +759,36 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
     DG_TRY(dg::lm_head_bf16_batch(nrm16, B, N, d, static_cast<const uint16_t *>(w->E_pack), V, inv_T, ec, nullptr,
                                   s));
   }
-  for (int b = 0; b < B; ++b) {
-    dg_canvas *cv = &cvs[b];
-    const float4 *tstats = reinterpret_cast<const float4 *>(st_of(b, SL.tstats));
-    DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, nullptr,
-                           reinterpret_cast<float *>(st_of(b, SL.rscale)),
-                           reinterpret_cast<uint8_t *>(st_of(b, SL.shift)), nrm + (size_t)b * N * d, Eb, d,
-                           reinterpret_cast<float2 *>(st_of(b, SL.top)), s));
-    if (cfg->candidate_rule == DG_CANDIDATE_MULTINOMIAL) {
-      dg::DrawArgs draw{cv->seed, (uint32_t)cv->step, cv->canvas_id, static_cast<const uint16_t *>(cv->probs),
-                        nullptr};
-      DG_TRY(dg::multinomial_draw(tstats, N, ntiles, inv_T, draw, cv->argmax, s));
+  {  // row statistics of every canvas in one launch, then its candidates, then one selection launch
+    dg::RowCombineBatch rc{};
+    dg::SelectBatch sel{};
+    for (int b = 0; b < B; ++b) {
+      dg_canvas *cv = &cvs[b];
+      rc.stats[b] = reinterpret_cast<const float4 *>(st_of(b, SL.tstats));
+      rc.entropy[b] = cv->entropy;
+      rc.cand[b] = cv->argmax;
+      rc.row_scale[b] = reinterpret_cast<float *>(st_of(b, SL.rscale));
+      rc.shift[b] = reinterpret_cast<uint8_t *>(st_of(b, SL.shift));
+      rc.top[b] = reinterpret_cast<float2 *>(st_of(b, SL.top));
+      sel.entropy[b] = cv->entropy;
+      sel.argmax[b] = cv->argmax;
+      sel.tokens[b] = cv->tokens;
+      sel.accept[b] = cv->accept;
+      sel.status[b] = cv->status;
+      sel.seed[b] = cv->seed;
+      sel.canvas_id[b] = cv->canvas_id;
+      sel.step[b] = (uint32_t)cv->step;
     }
-    DG_TRY(dg::select_step(cv->entropy, cv->argmax, cv->tokens, cv->accept, cv->status, N, ilog2(V),
-                           (double)gamma, (int)cfg->accept_rule, cfg->conf_eps, cv->seed, cv->canvas_id,
-                           (uint32_t)cv->step, mask_id(cfg), s));
+    DG_TRY(dg::row_combine_batch(rc, B, N, ntiles, inv_T, nrm, Eb, d, s));
+    if (cfg->candidate_rule == DG_CANDIDATE_MULTINOMIAL)
+      for (int b = 0; b < B; ++b) {
+        dg_canvas *cv = &cvs[b];
+        dg::DrawArgs draw{cv->seed, (uint32_t)cv->step, cv->canvas_id, static_cast<const uint16_t *>(cv->probs),
+                          nullptr};
+        DG_TRY(dg::multinomial_draw(rc.stats[b], N, ntiles, inv_T, draw, cv->argmax, s));
+      }
+    DG_TRY(dg::select_step_batch(sel, B, N, ilog2(V), (double)gamma, (int)cfg->accept_rule, cfg->conf_eps,
+                                 mask_id(cfg), s));
   }
   for (int b = 0; b < B; ++b) {
     cvs[b].step += 1;
@@ -956,9 +988,17 @@ dg_status dg_test_select(const dg_config *cfg, dg_canvas *cv, float gamma, void 
   dg_status st = check_config(cfg);
   if (st != DG_OK) return st;
   if (!canvas_ok(cv) || std::isnan(gamma) || gamma < 0.f || cv->step < 0) return DG_ERR_INVALID_ARG;
-  DG_TRY(dg::select_step(cv->entropy, cv->argmax, cv->tokens, cv->accept, cv->status, cfg->canvas_len,
-                         ilog2(cfg->vocab), (double)gamma, (int)cfg->accept_rule, cfg->conf_eps, cv->seed,
-                         cv->canvas_id, (uint32_t)cv->step, mask_id(cfg), static_cast<hipStream_t>(stream)));
+  dg::SelectBatch sel{};  // the kernel the step launches
+  sel.entropy[0] = cv->entropy;
+  sel.argmax[0] = cv->argmax;
+  sel.tokens[0] = cv->tokens;
+  sel.accept[0] = cv->accept;
+  sel.status[0] = cv->status;
+  sel.seed[0] = cv->seed;
+  sel.canvas_id[0] = cv->canvas_id;
+  sel.step[0] = (uint32_t)cv->step;
+  DG_TRY(dg::select_step_batch(sel, 1, cfg->canvas_len, ilog2(cfg->vocab), (double)gamma, (int)cfg->accept_rule,
+                               cfg->conf_eps, mask_id(cfg), static_cast<hipStream_t>(stream)));
   return DG_OK;
 }
 

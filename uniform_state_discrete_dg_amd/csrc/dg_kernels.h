@@ -171,6 +171,20 @@ struct DrawArgs {
 hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,
                        int32_t *cand, float *tile_scale, float *row_scale, uint8_t *shift, const float *n2,
                        const uint16_t *E, int d, float2 *top, hipStream_t s);
+// The row combine of B canvases (bf16 path, N <= 256 rows each) in one
+// launch: canvas c's statistics, entropy, candidates, row factors, exponents
+// and top tokens at the c-th pointers; n2 the stacked normalised rows
+// ([B * N][d]).  Each row's results are the single-canvas launch's.
+struct RowCombineBatch {
+  const float4 *stats[ES_MAX_BATCH];
+  float *entropy[ES_MAX_BATCH];
+  int32_t *cand[ES_MAX_BATCH];
+  float *row_scale[ES_MAX_BATCH];
+  uint8_t *shift[ES_MAX_BATCH];
+  float2 *top[ES_MAX_BATCH];
+};
+hipError_t row_combine_batch(const RowCombineBatch &bt, int B, int N, int ntiles, float inv_T, const float *n2,
+                             const uint16_t *E, int d, hipStream_t s);
 // Multinomial draw of the candidate tokens (two Gumbel-max levels over the
 // tile statistics and the stored weights, dg_device.h), run once the step's
 // probabilities are final; cand holds the argmax and keeps it for a row with
@@ -248,10 +262,21 @@ hipError_t copy_bytes(const void *src, void *dst, size_t bytes, hipStream_t s);
 // decided ones are locked); mask_id < 0: uniform-state re-noise.
 hipError_t canvas_init(int32_t *tokens, int32_t *status, int N, int log2v, uint64_t seed,
                        uint32_t canvas_id, int mask_id, hipStream_t s);
-hipError_t select_step(const float *entropy, const int32_t *argmax, int32_t *tokens,
-                       uint8_t *accept, int32_t *status, int N, int log2v, double gamma,
-                       int rule, float conf_eps, uint64_t seed, uint32_t canvas_id,
-                       uint32_t step, int mask_id, hipStream_t s);
+// The selection of B canvases (N <= 256 each) in one launch, one workgroup
+// per canvas, each with its own buffers, seed, canvas id and step; a single
+// canvas is a batch of one.
+struct SelectBatch {
+  const float *entropy[ES_MAX_BATCH];
+  const int32_t *argmax[ES_MAX_BATCH];
+  int32_t *tokens[ES_MAX_BATCH];
+  uint8_t *accept[ES_MAX_BATCH];
+  int32_t *status[ES_MAX_BATCH];
+  uint64_t seed[ES_MAX_BATCH];
+  uint32_t canvas_id[ES_MAX_BATCH];
+  uint32_t step[ES_MAX_BATCH];
+};
+hipError_t select_step_batch(const SelectBatch &bt, int B, int N, int log2v, double gamma, int rule,
+                             float conf_eps, int mask_id, hipStream_t s);
 hipError_t philox_test(const uint32_t *ctr, uint32_t k0, uint32_t k1, uint32_t *out, int n,
                        hipStream_t s);
 

@@ -420,17 +420,15 @@ constexpr int RC_NW = RC_NT / 64;
 constexpr int RC_CACHE = 4096 / RC_NT;
 constexpr int RC_D = 4096 / RC_NT;  // normalised-row values per thread: d <= 4096
 
+// One row: row indexes the canvas's own buffers, n2 points at that row's
+// normalised state.
 template <bool CACHED>
-__global__ void __launch_bounds__(RC_NT) row_combine_kernel(const float4 *__restrict__ stats, int ntiles,
-                                                          float inv_T, float *__restrict__ entropy,
-                                                          int32_t *__restrict__ cand,
-                                                          float *__restrict__ tile_scale,
-                                                          float *__restrict__ row_scale, uint8_t *__restrict__ shift,
-                                                          const float *__restrict__ n2, const bf16 *__restrict__ E,
-                                                          int d, float2 *__restrict__ top) {
-  __shared__ float shv[2 * RC_NW];
-  __shared__ int shi[RC_NW];
-  const int row = blockIdx.x;
+__device__ __forceinline__ void row_combine_row(const int row, const float4 *__restrict__ stats, int ntiles,
+                                                float inv_T, float *__restrict__ entropy,
+                                                int32_t *__restrict__ cand, float *__restrict__ tile_scale,
+                                                float *__restrict__ row_scale, uint8_t *__restrict__ shift,
+                                                const float *__restrict__ n2, const bf16 *__restrict__ E, int d,
+                                                float2 *__restrict__ top, float *shv, int *shi) {
   // the normalised row for the exact top logit, loaded before the argmax is known
   float nv[RC_D];
   const bool fix = n2 != nullptr;
@@ -438,7 +436,7 @@ __global__ void __launch_bounds__(RC_NT) row_combine_kernel(const float4 *__rest
 #pragma unroll
     for (int i = 0; i < RC_D; ++i) {
       const int k = threadIdx.x + RC_NT * i;
-      nv[i] = k < d ? n2[(int64_t)row * d + k] : 0.f;
+      nv[i] = k < d ? n2[k] : 0.f;
     }
   }
   const float4 *st = stats + (int64_t)row * ntiles;
@@ -533,6 +531,46 @@ __global__ void __launch_bounds__(RC_NT) row_combine_kernel(const float4 *__rest
     if (top) top[row] = make_float2(__int_as_float(amax), exp2f(d_top * LOG2E) * invL);
     if (row_scale) row_scale[row] = g;
   }
+}
+
+template <bool CACHED>
+__global__ void __launch_bounds__(RC_NT) row_combine_kernel(const float4 *__restrict__ stats, int ntiles,
+                                                          float inv_T, float *__restrict__ entropy,
+                                                          int32_t *__restrict__ cand,
+                                                          float *__restrict__ tile_scale,
+                                                          float *__restrict__ row_scale, uint8_t *__restrict__ shift,
+                                                          const float *__restrict__ n2, const bf16 *__restrict__ E,
+                                                          int d, float2 *__restrict__ top) {
+  __shared__ float shv[2 * RC_NW];
+  __shared__ int shi[RC_NW];
+  const int row = blockIdx.x;
+  row_combine_row<CACHED>(row, stats, ntiles, inv_T, entropy, cand, tile_scale, row_scale, shift,
+                          n2 ? n2 + (int64_t)row * d : nullptr, E, d, top, shv, shi);
+}
+
+// A batch: workgroup r is row r % N of canvas r / N (the bf16 path's
+// buffers, exponents and top tokens per canvas); n2 holds the stacked rows.
+template <bool CACHED>
+__global__ void __launch_bounds__(RC_NT) row_combine_batch_kernel(RowCombineBatch bt, int N, int ntiles,
+                                                                float inv_T, const float *__restrict__ n2,
+                                                                const bf16 *__restrict__ E, int d) {
+  __shared__ float shv[2 * RC_NW];
+  __shared__ int shi[RC_NW];
+  const int c = blockIdx.x / N, row = blockIdx.x - c * N;
+  row_combine_row<CACHED>(row, bt.stats[c], ntiles, inv_T, bt.entropy[c], bt.cand[c], nullptr, bt.row_scale[c],
+                          bt.shift[c], n2 + (int64_t)blockIdx.x * d, E, d, bt.top[c], shv, shi);
+}
+
+hipError_t row_combine_batch(const RowCombineBatch &bt, int B, int N, int ntiles, float inv_T, const float *n2,
+                             const uint16_t *E, int d, hipStream_t s) {
+  if (B < 1 || B > ES_MAX_BATCH || N < 1 || N > 256 || !n2 || d > RC_NT * RC_D) return hipErrorInvalidValue;
+  if (ntiles <= RC_NT * RC_CACHE)
+    hipLaunchKernelGGL(row_combine_batch_kernel<true>, dim3(B * N), dim3(RC_NT), 0, s, bt, N, ntiles, inv_T, n2, E,
+                       d);
+  else
+    hipLaunchKernelGGL(row_combine_batch_kernel<false>, dim3(B * N), dim3(RC_NT), 0, s, bt, N, ntiles, inv_T, n2,
+                       E, d);
+  return hipGetLastError();
 }
 
 hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,

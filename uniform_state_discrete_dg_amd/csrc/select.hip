@@ -40,12 +40,11 @@ hipError_t canvas_init(int32_t *tokens, int32_t *status, int N, int log2v, uint6
   return hipGetLastError();
 }
 
-__global__ void __launch_bounds__(256) select_kernel(const float *__restrict__ entropy,
-                                                     const int32_t *__restrict__ argmax,
-                                                     int32_t *__restrict__ tokens, uint8_t *__restrict__ accept,
-                                                     int32_t *__restrict__ status, int N, int log2v,
-                                                     uint64_t limit, int rule, float conf_eps, uint64_t seed,
-                                                     uint32_t canvas_id, uint32_t step, int mask_id) {
+__device__ __forceinline__ void select_body(const float *__restrict__ entropy, const int32_t *__restrict__ argmax,
+                                            int32_t *__restrict__ tokens, uint8_t *__restrict__ accept,
+                                            int32_t *__restrict__ status, int N, int log2v, uint64_t limit,
+                                            int rule, float conf_eps, uint64_t seed, uint32_t canvas_id,
+                                            uint32_t step, int mask_id) {
   __shared__ __align__(16) uint64_t keys[256];
   __shared__ __align__(16) uint64_t fix[256];
   __shared__ float fmin_s[4], fmax_s[4], fsum_s[4];
@@ -147,16 +146,29 @@ __global__ void __launch_bounds__(256) select_kernel(const float *__restrict__ e
   }
 }
 
-hipError_t select_step(const float *entropy, const int32_t *argmax, int32_t *tokens, uint8_t *accept,
-                       int32_t *status, int N, int log2v, double gamma, int rule, float conf_eps,
-                       uint64_t seed, uint32_t canvas_id, uint32_t step, int mask_id, hipStream_t s) {
+// One workgroup per canvas (a single canvas is a batch of one).
+__global__ void __launch_bounds__(256) select_batch_kernel(SelectBatch bt, int N, int log2v, uint64_t limit,
+                                                           int rule, float conf_eps, int mask_id) {
+  const int c = blockIdx.x;
+  select_body(bt.entropy[c], bt.argmax[c], bt.tokens[c], bt.accept[c], bt.status[c], N, log2v, limit, rule,
+              conf_eps, bt.seed[c], bt.canvas_id[c], bt.step[c], mask_id);
+}
+
+// gamma (nats) -> the 2^-32-nat fixed-point limit, saturating
+static uint64_t select_limit(double gamma) {
   uint64_t limit = 0;
   if (gamma > 0.0) {
     const double x = gamma * 4294967296.0;
     limit = (x >= 18446744073709551615.0) ? ~0ull : (uint64_t)x;
   }
-  hipLaunchKernelGGL(select_kernel, dim3(1), dim3(256), 0, s, entropy, argmax, tokens, accept, status, N,
-                     log2v, limit, rule, conf_eps, seed, canvas_id, step, mask_id);
+  return limit;
+}
+
+hipError_t select_step_batch(const SelectBatch &bt, int B, int N, int log2v, double gamma, int rule,
+                             float conf_eps, int mask_id, hipStream_t s) {
+  if (B < 1 || B > ES_MAX_BATCH || N < 1 || N > 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(select_batch_kernel, dim3(B), dim3(256), 0, s, bt, N, log2v, select_limit(gamma), rule,
+                     conf_eps, mask_id);
   return hipGetLastError();
 }
 
