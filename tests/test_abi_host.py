@@ -294,6 +294,10 @@ def test_batch_step_validation(lib):
     # two canvases on the same buffers
     twin = [distinct_canvas(0), distinct_canvas(1), distinct_canvas(1)]
     assert call_batch(cfg, w, caches, twin, 1.0, 8.0, need) == (B.DG_ERR_INVALID_ARG, before)
+    for field in ("tokens", "probs", "stats", "entropy", "argmax", "accept", "status"):
+        shared = [distinct_canvas(0), distinct_canvas(1), distinct_canvas(2)]
+        setattr(shared[2], field, getattr(shared[0], field))
+        assert call_batch(cfg, w, caches, shared, 1.0, 8.0, need) == (B.DG_ERR_INVALID_ARG, before), field
     bad = [distinct_canvas(0), distinct_canvas(1), distinct_canvas(2)]
     bad[2].status = None
     assert call_batch(cfg, w, caches, bad, 1.0, 8.0, need)[0] == B.DG_ERR_INVALID_ARG

@@ -827,10 +827,12 @@ dg_status dg_denoise_step_batch(const dg_config *cfg, const dg_weights *w, const
     if (!c.k || !c.v || c.length < 0 || c.length > c.capacity) return DG_ERR_INVALID_ARG;
     if (!canvas_ok(&canvases[b]) || canvases[b].step < 0 || canvases[b].has_prev != canvases[0].has_prev)
       return DG_ERR_INVALID_ARG;
-    for (int32_t a = 0; a < b; ++a)  // the canvases' buffers are written: no two may share them
-      if (canvases[a].tokens == canvases[b].tokens || canvases[a].probs == canvases[b].probs ||
-          canvases[a].stats == canvases[b].stats || canvases[a].status == canvases[b].status)
+    for (int32_t a = 0; a < b; ++a) {  // the canvases' buffers are written: no two may share one
+      const dg_canvas &x = canvases[a], &y = canvases[b];
+      if (x.tokens == y.tokens || x.probs == y.probs || x.stats == y.stats || x.entropy == y.entropy ||
+          x.argmax == y.argmax || x.accept == y.accept || x.status == y.status)
         return DG_ERR_INVALID_ARG;
+    }
   }
   if (!ws || ws_bytes < batch_ws_bytes(cfg, n_canvases)) return DG_ERR_WORKSPACE;
   if (cfg->dtype != DG_BF16) {  // the fp32 path: the single-canvas step, canvas after canvas
