@@ -285,18 +285,29 @@ dg_status dg_denoise_step(const dg_config *cfg, const dg_weights *w, const dg_kv
  * such canvases (each with its own cache, tokens, probabilities, seed and
  * step counter) at once: their rows are stacked for the projections and the
  * two table-streaming contractions, so the embedding table is read from HBM
- * once per step for the whole batch instead of once per canvas; attention,
- * the row statistics and the selection run per canvas.  Every canvas ends in
- * exactly the state dg_denoise_step would give it (bit for bit), so a batch
- * may mix canvases at different steps of their own schedules, with one
- * temperature and threshold for the call.
- *   caches:   host array of n_canvases cache descriptors (several may name
- *             the same cache: it is only read);
- *   canvases: host array of n_canvases canvases (distinct buffers), all with
- *             the same has_prev (all past their first step, or none);
- *   1 <= n_canvases <= DG_MAX_BATCH; ws_bytes >= dg_workspace_bytes_batch().
- * Each canvas's step += 1 and has_prev = 1.  Errors as dg_denoise_step, plus
- * DG_ERR_INVALID_ARG for a count out of range or mixed has_prev. */
+ * about once per step for the whole batch instead of once per canvas
+ * (DG_BF16; canvases of at most 128 rows share 256-row blocks two by two).
+ * Attention runs per canvas over that canvas's own cache; the row
+ * statistics and the selection are per canvas, each computed by one launch
+ * for the batch.  Every canvas ends in exactly the state dg_denoise_step
+ * would give it (bit for bit), so a batch may mix canvases at different
+ * steps of their own schedules, with one temperature and threshold for the
+ * call.  DG_F32 runs the single-canvas step for each canvas in turn.
+ *   caches:   host array of n_canvases cache descriptors (device K/V as for
+ *             dg_denoise_step; several may name the same cache: it is only
+ *             read);
+ *   canvases: host array of n_canvases canvases, all with the same has_prev
+ *             (all past their first step, or none); no two may share any
+ *             device buffer (tokens, probs, stats, entropy, argmax, accept,
+ *             status);
+ *   ws:       device workspace of at least dg_workspace_bytes_batch(cfg,
+ *             n_canvases) bytes (0 for an unsupported config or count);
+ *   1 <= n_canvases <= DG_MAX_BATCH.
+ * Each canvas's step += 1 and has_prev = 1 (host fields of the array).
+ * Errors as dg_denoise_step, checked for every canvas before the first
+ * launch; DG_ERR_INVALID_ARG also for a count out of range, mixed has_prev
+ * or shared canvas buffers.  The test switch dg_test_set_logits_dump does
+ * not apply to this call. */
 #define DG_MAX_BATCH 16
 size_t dg_workspace_bytes_batch(const dg_config *cfg, int32_t n_canvases);
 dg_status dg_denoise_step_batch(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *caches,

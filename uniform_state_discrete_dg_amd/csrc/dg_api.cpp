@@ -643,8 +643,9 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
 // canvas in every activation; the projections and both table-streaming
 // contractions run once for the batch (their per-row results do not depend
 // on the other rows: the projections' K ranges are a function of K, the
-// contractions accumulate each row on its own), attention, the row
-// statistics and the selection once per canvas.  Validated by the caller.
+// contractions accumulate each row on its own); attention once per canvas;
+// the row statistics and the selection per canvas, one launch each for the
+// batch (the kernels the single-canvas step runs).  Validated by the caller.
 static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *caches,
                                     dg_canvas *cvs, int B, float temperature, float gamma, void *ws,
                                     hipStream_t s) {

@@ -142,6 +142,9 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
 // The self-conditioning contraction of B canvases at once: canvas c's
 // operand cin.probs[c] (its exponents cin.shift[c] when scaled), partials at
 // partials + c * ksplit * M * N (the single-canvas layout per canvas).
+// Canvases of M <= 128 rows are paired in one 256-row block (the second
+// canvas's rows read from its own buffers).  Each row's partials are those
+// of the single-canvas launch bit for bit (same K ranges, same MFMA order).
 struct EsCanvasesIn {
   const uint16_t *probs[ES_MAX_BATCH];
   const uint8_t *shift[ES_MAX_BATCH];
@@ -174,7 +177,8 @@ hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T,
 // The row combine of B canvases (bf16 path, N <= 256 rows each) in one
 // launch: canvas c's statistics, entropy, candidates, row factors, exponents
 // and top tokens at the c-th pointers; n2 the stacked normalised rows
-// ([B * N][d]).  Each row's results are the single-canvas launch's.
+// ([B * N][d]).  The single-canvas step launches it with B = 1, so a row's
+// results do not depend on the batch it is in.
 struct RowCombineBatch {
   const float4 *stats[ES_MAX_BATCH];
   float *entropy[ES_MAX_BATCH];
