@@ -329,8 +329,12 @@ dg_status dg_should_stop(const dg_config *cfg, const dg_canvas *canvas, int32_t 
  * of max_steps values, the caller's schedule) and accept threshold
  * accept_threshold_nats.  With adaptive_stop != 0 each step is followed by
  * the dg_should_stop test (stable_steps as there) and the loop ends at the
- * first step where it holds; that test is the only device-to-host transfer
- * (a few bytes into pinned host memory the library keeps per host thread).
+ * first step where it holds.  The step's selection kernel writes its status
+ * words straight into coherent pinned host memory the library keeps per host
+ * thread (the step word last, after a system-scope fence), and the host polls
+ * that word: no copy, no event.  The poll checks the stream every few
+ * thousand reads, so a stream that ends or fails without writing the word
+ * returns DG_ERR_HIP instead of waiting forever.
  * Writes *steps_run and *stopped (1 if the adaptive stop ended the loop).
  * Errors as dg_denoise_step, checked before the first launch; max_steps >= 0.
  * Returns with the stream synchronised when adaptive_stop != 0, otherwise

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -447,7 +448,8 @@ enum ScMode { SC_INLINE = 0, SC_AHEAD = 1, SC_DONE = 2 };
 
 static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache, dg_canvas *cv,
                               float temperature, float gamma, void *ws, size_t ws_bytes, void *stream,
-                              bool logits_dump, ScMode sc_mode = SC_INLINE, int32_t stable_steps = 0) {
+                              bool logits_dump, ScMode sc_mode = SC_INLINE, int32_t stable_steps = 0,
+                              int32_t *host_status = nullptr) {
   dg_status st = check_config(cfg);
   if (st != DG_OK) return st;
   if (!weights_ok(cfg, w) || !cache || !cache->k || !cache->v || !canvas_ok(cv)) return DG_ERR_INVALID_ARG;
@@ -630,6 +632,7 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     sel.seed[0] = cv->seed;
     sel.canvas_id[0] = cv->canvas_id;
     sel.step[0] = (uint32_t)cv->step;
+    sel.host_status[0] = host_status;
     DG_TRY(dg::select_step_batch(sel, 1, N, ilog2(V), (double)gamma, (int)cfg->accept_rule, cfg->conf_eps,
                                  mask_id(cfg), s));
   }
@@ -889,12 +892,21 @@ dg_status dg_run_canvas(const dg_config *cfg, const dg_weights *w, const dg_kv_c
     if (!(std::isfinite(temps[i]) && temps[i] > 0.f)) return DG_ERR_INVALID_ARG;
   if (std::isnan(accept_threshold_nats) || accept_threshold_nats < 0.f) return DG_ERR_INVALID_ARG;
   if (!ws || ws_bytes < layout(cfg, 0, g_logits_dump && cfg->dtype == DG_BF16).total) return DG_ERR_WORKSPACE;
-  // pinned landing area of the status words, one per host thread (kept for the process)
-  thread_local int32_t *pinned = nullptr;
-  if (adaptive_stop && !pinned) {
-    if (hipHostMalloc(reinterpret_cast<void **>(&pinned), DG_STATUS_WORDS * sizeof(int32_t), hipHostMallocDefault) !=
-        hipSuccess) {
-      pinned = nullptr;
+  // Host-visible copy of the status words, one per host thread (kept for the
+  // process): coherent pinned memory that the selection kernel writes
+  // directly, the step word last, so the host learns a step's outcome without
+  // a copy or an event; it polls that word.
+  thread_local int32_t *host_words = nullptr;
+  thread_local int32_t *host_words_dev = nullptr;
+  if (adaptive_stop && !host_words) {
+    if (hipHostMalloc(reinterpret_cast<void **>(&host_words), DG_STATUS_WORDS * sizeof(int32_t),
+                      hipHostMallocCoherent | hipHostMallocMapped) != hipSuccess) {
+      host_words = nullptr;
+      return DG_ERR_HIP;
+    }
+    if (hipHostGetDevicePointer(reinterpret_cast<void **>(&host_words_dev), host_words, 0) != hipSuccess) {
+      (void)hipHostFree(host_words);
+      host_words = nullptr;
       return DG_ERR_HIP;
     }
   }
@@ -909,29 +921,40 @@ dg_status dg_run_canvas(const dg_config *cfg, const dg_weights *w, const dg_kv_c
   // device: the host's wait and the next launches hide behind a kernel that
   // is running anyway, and if step i did stop the canvas, every workgroup
   // of the guarded launch returns at once.
-  thread_local hipEvent_t status_ready = nullptr;
-  if (adaptive_stop && !status_ready && hipEventCreateWithFlags(&status_ready, hipEventDisableTiming) != hipSuccess) {
-    status_ready = nullptr;
-    return DG_ERR_HIP;
-  }
   const bool ahead_ok = adaptive_stop && cfg->dtype == DG_BF16;
   bool ahead = false;  // step i's contraction is already in the stream
   for (int32_t i = 0; i < max_steps; ++i) {
+    const int32_t step_index = cv->step;
+    if (adaptive_stop) reinterpret_cast<volatile int32_t *>(host_words)[DG_ST_STEP] = -1;
     st = denoise_impl(cfg, w, cache, cv, temps[i], accept_threshold_nats, ws, ws_bytes, stream, g_logits_dump,
-                      ahead ? SC_DONE : SC_INLINE);
+                      ahead ? SC_DONE : SC_INLINE, 0, adaptive_stop ? host_words_dev : nullptr);
     if (st != DG_OK) return st;
     *steps_run = i + 1;
     if (adaptive_stop) {
-      DG_TRY(hipMemcpyAsync(pinned, cv->status, DG_STATUS_WORDS * sizeof(int32_t), hipMemcpyDeviceToHost, s));
-      DG_TRY(hipEventRecord(status_ready, s));
       ahead = ahead_ok && i + 1 < max_steps;
       if (ahead) {
         st = denoise_impl(cfg, w, cache, cv, temps[i + 1], accept_threshold_nats, ws, ws_bytes, stream,
                           g_logits_dump, SC_AHEAD, stable_steps);
         if (st != DG_OK) return st;
       }
-      DG_TRY(hipEventSynchronize(status_ready));
-      if (status_stops(pinned, stable_steps)) {
+      // wait for the step word; every 4096 polls make sure the stream is
+      // still running (a stream that finished or failed without writing it
+      // is an error, never an endless wait)
+      volatile int32_t *hw = host_words;
+      for (uint32_t polls = 1; hw[DG_ST_STEP] != step_index; ++polls) {
+        if ((polls & 4095) == 0) {
+          const hipError_t q = hipStreamQuery(s);
+          if (q == hipSuccess) {
+            if (hw[DG_ST_STEP] == step_index) break;
+            return DG_ERR_HIP;
+          }
+          if (q != hipErrorNotReady) return DG_ERR_HIP;
+        }
+      }
+      std::atomic_thread_fence(std::memory_order_acquire);
+      int32_t words[DG_STATUS_WORDS];
+      for (int k = 0; k < DG_STATUS_WORDS; ++k) words[k] = hw[k];
+      if (status_stops(words, stable_steps)) {
         *stopped = 1;
         if (ahead) DG_TRY(hipStreamSynchronize(s));  // the guarded launch returns at once
         break;

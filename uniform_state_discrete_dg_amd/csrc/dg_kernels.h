@@ -278,6 +278,9 @@ struct SelectBatch {
   uint64_t seed[ES_MAX_BATCH];
   uint32_t canvas_id[ES_MAX_BATCH];
   uint32_t step[ES_MAX_BATCH];
+  // nullable: a copy of the status words in host-visible memory, the step
+  // word written last (after a system-scope fence)
+  int32_t *host_status[ES_MAX_BATCH];
 };
 hipError_t select_step_batch(const SelectBatch &bt, int B, int N, int log2v, double gamma, int rule,
                              float conf_eps, int mask_id, hipStream_t s);

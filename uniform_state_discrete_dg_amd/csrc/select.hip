@@ -44,7 +44,7 @@ __device__ __forceinline__ void select_body(const float *__restrict__ entropy, c
                                             int32_t *__restrict__ tokens, uint8_t *__restrict__ accept,
                                             int32_t *__restrict__ status, int N, int log2v, uint64_t limit,
                                             int rule, float conf_eps, uint64_t seed, uint32_t canvas_id,
-                                            uint32_t step, int mask_id) {
+                                            uint32_t step, int mask_id, int32_t *host_status) {
   __shared__ __align__(16) uint64_t keys[256];
   __shared__ __align__(16) uint64_t fix[256];
   __shared__ float fmin_s[4], fmax_s[4], fsum_s[4];
@@ -143,6 +143,13 @@ __device__ __forceinline__ void select_body(const float *__restrict__ entropy, c
     status[DG_ST_HMAX] = __float_as_int(fmax_s[0]);
     status[DG_ST_HMEAN] = __float_as_int(N > n_nan ? fsum_s[0] / (float)(N - n_nan) : 0.f);
     status[DG_ST_MASKED] = mask_id >= 0 ? n_masked : -1;
+    if (host_status) {  // the host's copy: every other word first, the step word last
+      for (int w = 0; w < DG_STATUS_WORDS; ++w)
+        if (w != DG_ST_STEP) host_status[w] = status[w];
+      __threadfence_system();
+      host_status[DG_ST_STEP] = (int32_t)step;
+      __threadfence_system();
+    }
   }
 }
 
@@ -151,7 +158,7 @@ __global__ void __launch_bounds__(256) select_batch_kernel(SelectBatch bt, int N
                                                            int rule, float conf_eps, int mask_id) {
   const int c = blockIdx.x;
   select_body(bt.entropy[c], bt.argmax[c], bt.tokens[c], bt.accept[c], bt.status[c], N, log2v, limit, rule,
-              conf_eps, bt.seed[c], bt.canvas_id[c], bt.step[c], mask_id);
+              conf_eps, bt.seed[c], bt.canvas_id[c], bt.step[c], mask_id, bt.host_status[c]);
 }
 
 // gamma (nats) -> the 2^-32-nat fixed-point limit, saturating
