@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define DG_ABI_VERSION 4
+#define DG_ABI_VERSION 5
 
 typedef enum {
   DG_OK = 0,
@@ -94,6 +94,22 @@ typedef enum { DG_CANDIDATE_ARGMAX = 0, DG_CANDIDATE_MULTINOMIAL = 1 } dg_candid
  *   the loop also stops when no [MASK] is left. */
 typedef enum { DG_SAMPLER_UNIFORM = 0, DG_SAMPLER_MASKED = 1 } dg_sampler;
 
+/* Storage of the packed table the two table-streaming contractions read
+ * (DG_BF16 only; DG_F32 ignores it).  [P2] (local-deployment numbers) runs
+ * the model quantised (NVFP4) to fit a consumer GPU; the MI355X counterpart
+ * kept here is OCP fp8 e4m3.
+ * BF16: E_pack holds E and E^T in bf16.
+ * FP8:  E_pack holds q = E * 2^table_exp and its transpose as fp8 e4m3
+ *       (dg_pack_embedding rounds to nearest even and saturates at +-448).
+ *       The kernels turn each fragment back into bf16 as q * 2^-table_exp,
+ *       exactly, so the arithmetic is that of the bf16 path on a table whose
+ *       entries are those values; E itself (row-major bf16: the embedding
+ *       gathers and the exact top-logit recompute read it) must hold the
+ *       same values, i.e. lie on that grid (E = fp8(E * 2^table_exp) *
+ *       2^-table_exp), or the two copies disagree.  The table's bytes halve
+ *       (E_pack 2 V d bytes instead of 4 V d). */
+typedef enum { DG_TABLE_BF16 = 0, DG_TABLE_FP8 = 1 } dg_table_format;
+
 /* Model and canvas shape.
  * Supported: 1 <= canvas_len <= 256; vocab a power of two in [256, 2^24];
  * n_q_heads a multiple of n_kv_heads.  DG_BF16 additionally needs head_dim ==
@@ -114,6 +130,8 @@ typedef struct {
   dg_accept_rule accept_rule;
   dg_candidate_rule candidate_rule;
   dg_sampler sampler;
+  dg_table_format table_format;
+  int32_t table_exp;    /* DG_TABLE_FP8: q = E * 2^table_exp, in [-32, 32] */
 } dg_config;
 
 /* Weights (device, dtype of the config, caller-owned, read-only).

@@ -38,7 +38,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert B.dg_abi_version() == 4
+    assert B.dg_abi_version() == 5
     for s in range(6):
         assert lib.dg_status_string(s)
 
@@ -308,3 +308,45 @@ def test_batch_step_validation(lib):
     many_c = [caches[0]] * len(many)
     big = B.dg_workspace_bytes_batch(cfg, B.DG_MAX_BATCH)
     assert call_batch(cfg, w, many_c, many, 1.0, 8.0, big)[0] == B.DG_ERR_INVALID_ARG
+
+
+def test_fp8_table_config_and_sizes(lib):
+    """The fp8 packed table: accepted for DG_BF16 with a scale exponent in
+    [-32, 32], half the bytes of the bf16 pack, same workspace and canvas
+    buffers; bad formats and exponents rejected."""
+    for i in (2, 3, 4):
+        cfg = cfg_of(i)
+        c8 = cfg_of(i, table="fp8", table_exp=8)
+        assert c8.table_format == B.DG_TABLE_FP8 and c8.table_exp == 8
+        assert B.dg_validate_config(c8) == B.DG_OK
+        assert 2 * B.dg_embedding_pack_bytes(c8) == B.dg_embedding_pack_bytes(cfg)
+        assert B.dg_embedding_pack_bytes(c8) == 2 * cfg.vocab * cfg.d_model
+        assert B.dg_workspace_bytes(c8, 0) == B.dg_workspace_bytes(cfg, 0)
+        assert B.dg_probs_bytes(c8) == B.dg_probs_bytes(cfg)
+    c8 = cfg_of(2, table="fp8", table_exp=33)
+    assert B.dg_validate_config(c8) == B.DG_ERR_INVALID_ARG
+    c8.table_exp = -33
+    assert B.dg_validate_config(c8) == B.DG_ERR_INVALID_ARG
+    c8.table_exp = -32
+    assert B.dg_validate_config(c8) == B.DG_OK
+    c8.table_format = 2
+    assert B.dg_validate_config(c8) == B.DG_ERR_INVALID_ARG
+    # the fp32 configuration ignores the table format (it reads E directly)
+    c1 = cfg_of(1, table="fp8", table_exp=8)
+    assert B.dg_validate_config(c1) == B.DG_OK
+    assert B.dg_embedding_pack_bytes(c1) == 0
+
+
+def test_fp8_grid_quantiser():
+    """The quantised-table input: every entry is q 2^-exp with q an fp8 e4m3
+    number (nearest even, saturating), idempotent, and exact in bf16."""
+    import torch
+    g = torch.Generator().manual_seed(3)
+    E = (torch.randn(64, 256, generator=g) * 0.05).to(torch.bfloat16)
+    Q = W.fp8_grid(E, 8)
+    q = Q.float() * 256
+    assert torch.equal(q.to(torch.float8_e4m3fn).float(), q)
+    assert torch.equal(W.fp8_grid(Q, 8), Q)
+    assert (Q.float() - E.float()).abs().max().item() <= 0.0625 * E.float().abs().max().item() + 2 ** -17
+    big = torch.tensor([[1e6, -1e6, 0.0, 3.0]], dtype=torch.bfloat16)
+    assert W.fp8_grid(big, 0).float().tolist() == [[448.0, -448.0, 0.0, 3.0]]

@@ -25,6 +25,7 @@ DG_F32, DG_BF16 = 0, 1
 DG_ACCEPT_SUM_MINUS_MAX, DG_ACCEPT_CUMSUM = 0, 1
 DG_CANDIDATE_ARGMAX, DG_CANDIDATE_MULTINOMIAL = 0, 1
 DG_SAMPLER_UNIFORM, DG_SAMPLER_MASKED = 0, 1
+DG_TABLE_BF16, DG_TABLE_FP8 = 0, 1
 DG_STATUS_WORDS = 16
 DG_MAX_BATCH = 16
 (DG_ST_ALLCONF, DG_ST_CHANGED, DG_ST_STABLE, DG_ST_ACCEPTED, DG_ST_NAN, DG_ST_STEP, DG_ST_HMIN,
@@ -36,7 +37,7 @@ class dg_config(ctypes.Structure):
     _fields_ = [("canvas_len", c_i32), ("vocab", c_i32), ("d_model", c_i32), ("n_q_heads", c_i32),
                 ("n_kv_heads", c_i32), ("head_dim", c_i32), ("ffn_hidden", c_i32), ("dtype", c_i32),
                 ("rms_eps", c_f32), ("conf_eps", c_f32), ("accept_rule", c_i32), ("candidate_rule", c_i32),
-                ("sampler", c_i32)]
+                ("sampler", c_i32), ("table_format", c_i32), ("table_exp", c_i32)]
 
 
 class dg_weights(ctypes.Structure):
@@ -292,9 +293,13 @@ def dg_profile_read():
 def make_config(c: dict, accept_rule: int = DG_ACCEPT_SUM_MINUS_MAX,
                 conf_eps: float = 0.005, candidate_rule: int = DG_CANDIDATE_ARGMAX,
                 sampler: int = DG_SAMPLER_UNIFORM) -> dg_config:
+    """The C config of a workload dict; c["table"] == "fp8" selects the fp8
+    packed table with scale exponent c["table_exp"]."""
+    fp8 = c.get("table") == "fp8"
     return dg_config(c["N"], c["V"], c["d"], c["Hq"], c["Hkv"], c["hd"], c["F"],
                      DG_BF16 if c["dtype"] == "bf16" else DG_F32, c.get("rms_eps", 1e-6),
-                     conf_eps, accept_rule, candidate_rule, sampler)
+                     conf_eps, accept_rule, candidate_rule, sampler,
+                     DG_TABLE_FP8 if fp8 else DG_TABLE_BF16, c.get("table_exp", 0) if fp8 else 0)
 
 
 def torch_dtype(cfg: dg_config):

@@ -38,6 +38,8 @@ dg_status check_config(const dg_config *c) {
   if (c->candidate_rule != DG_CANDIDATE_ARGMAX && c->candidate_rule != DG_CANDIDATE_MULTINOMIAL)
     return DG_ERR_INVALID_ARG;
   if (c->sampler != DG_SAMPLER_UNIFORM && c->sampler != DG_SAMPLER_MASKED) return DG_ERR_INVALID_ARG;
+  if (c->table_format != DG_TABLE_BF16 && c->table_format != DG_TABLE_FP8) return DG_ERR_INVALID_ARG;
+  if (c->table_format == DG_TABLE_FP8 && (c->table_exp < -32 || c->table_exp > 32)) return DG_ERR_INVALID_ARG;
   if (c->canvas_len < 1 || c->vocab < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
       c->head_dim < 1 || c->ffn_hidden < 1)
     return DG_ERR_INVALID_ARG;
@@ -60,6 +62,22 @@ dg_status check_config(const dg_config *c) {
 // The packed table (DG_BF16): E tiled ([V][d]) followed by E^T tiled ([d][V]).
 size_t pack_te_elems(const dg_config *c) { return dg::tl_elems(c->vocab, c->d_model); }
 size_t pack_elems(const dg_config *c) { return pack_te_elems(c) + dg::tl_elems(c->d_model, c->vocab); }
+bool table_fp8(const dg_config *c) { return c->dtype == DG_BF16 && c->table_format == DG_TABLE_FP8; }
+
+// The packed table one streaming contraction reads: bf16 (elements) or fp8
+// (one byte per element, E = q * scale).
+struct TableRef {
+  const uint16_t *bf;
+  const uint8_t *q8;
+  float scale;
+};
+// E (the LM head's operand) or, with transposed, E^T (the self-conditioning one)
+TableRef table_ref(const dg_config *c, const dg_weights *w, bool transposed) {
+  const size_t off = transposed ? pack_te_elems(c) : 0;
+  if (table_fp8(c))
+    return {nullptr, static_cast<const uint8_t *>(w->E_pack) + off, std::ldexp(1.f, -c->table_exp)};
+  return {static_cast<const uint16_t *>(w->E_pack) + off, nullptr, 1.f};
+}
 
 int selfcond_ksplit(const dg_config *c) {
   const int bm = dg::estream_bm(c->canvas_len);
@@ -336,7 +354,7 @@ size_t dg_stats_bytes(const dg_config *cfg) {
 
 size_t dg_embedding_pack_bytes(const dg_config *cfg) {
   if (check_config(cfg) != DG_OK || cfg->dtype != DG_BF16) return 0;
-  return pack_elems(cfg) * 2;
+  return pack_elems(cfg) * (table_fp8(cfg) ? 1 : 2);
 }
 
 size_t dg_probs_bytes(const dg_config *cfg) {
@@ -352,6 +370,14 @@ dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_pack, v
   if (!E || !E_pack) return DG_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int V = cfg->vocab, d = cfg->d_model;
+  if (table_fp8(cfg)) {  // q = E * 2^table_exp as fp8: E [V][d], then E^T [d][V]
+    uint8_t *q = static_cast<uint8_t *>(E_pack);
+    const float sc = std::ldexp(1.f, cfg->table_exp);
+    const uint16_t *Eb = static_cast<const uint16_t *>(E);
+    DG_TRY(dg::tile_fp8(Eb, V, d, d, false, sc, q, s));
+    DG_TRY(dg::tile_fp8(Eb, d, V, d, true, sc, q + pack_te_elems(cfg), s));
+    return DG_OK;
+  }
   bf16 *te = static_cast<bf16 *>(E_pack), *tet = te + pack_te_elems(cfg);
   // E^T row-major goes through the first region (V*d elements) as scratch
   DG_TRY(dg::transpose<bf16>(static_cast<const bf16 *>(E), V, d, te, V, s));
@@ -501,12 +527,14 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     if (bf) {
       const int ks = selfcond_ksplit(cfg);
       float *part = reinterpret_cast<float *>(base + L.sc_part);
-      const bf16 *tet = static_cast<const bf16 *>(w->E_pack) + pack_te_elems(cfg);
-      dg::TiledGemm g{static_cast<const uint16_t *>(cv->probs), tet, N, d, V};
       if (sc_mode != SC_DONE) {
         ProfScope ps(g_prof_sc, s);
         const dg::SelfcondGuard guard{sc_mode == SC_AHEAD ? cv->status : nullptr, stable_steps};
-        DG_TRY(dg::selfcond_bf16(g, shift, part, ks, s, guard));
+        const TableRef tt = table_ref(cfg, w, true);
+        dg::EsCanvasesIn cin{};
+        cin.probs[0] = static_cast<const uint16_t *>(cv->probs);
+        cin.shift[0] = shift;
+        DG_TRY(dg::selfcond_bf16_batch(cin, 1, tt.bf, N, d, V, true, part, ks, s, guard, tt.q8, tt.scale));
       }
       if (sc_mode == SC_AHEAD) return DG_OK;
       DG_TRY(dg::selfcond_reduce(part, ks, N, d, top, static_cast<const uint16_t *>(cv->probs), V, rscale, shift,
@@ -590,8 +618,12 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
   if (bf) {
     {
       ProfScope ps(g_prof_lm, s);
-      DG_TRY(dg::lm_head_bf16(nrm16, N, d, static_cast<const uint16_t *>(w->E_pack), V, inv_T,
-                              static_cast<uint16_t *>(cv->probs), tstats, dump ? logits : nullptr, s));
+      const TableRef te = table_ref(cfg, w, false);
+      dg::EsCanvases ec{};
+      ec.probs[0] = static_cast<uint16_t *>(cv->probs);
+      ec.tile_stats[0] = tstats;
+      DG_TRY(dg::lm_head_bf16_batch(nrm16, 1, N, d, te.bf, V, inv_T, ec, dump ? logits : nullptr, s, te.q8,
+                                    te.scale));
     }
     // the numerators stay as stored: the next step's contraction applies the
     // power-of-two tile exponents and the row factor (the batch launch with
@@ -681,7 +713,7 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
     // S = p_prev E for every canvas in one pass over E^T, then the merges
     const int ks = selfcond_ksplit(cfg);
     float *part = reinterpret_cast<float *>(base + L.sc_part);
-    const bf16 *tet = static_cast<const bf16 *>(w->E_pack) + pack_te_elems(cfg);
+    const TableRef tt = table_ref(cfg, w, true);
     dg::EsCanvasesIn cin{};
     for (int b = 0; b < B; ++b) {
       cin.probs[b] = static_cast<const uint16_t *>(cvs[b].probs);
@@ -689,7 +721,8 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
     }
     {
       ProfScope ps(g_prof_sc, s);
-      DG_TRY(dg::selfcond_bf16_batch(cin, B, tet, N, d, V, true, part, ks, s));
+      DG_TRY(dg::selfcond_bf16_batch(cin, B, tt.bf, N, d, V, true, part, ks, s, dg::SelfcondGuard{nullptr, 0},
+                                     tt.q8, tt.scale));
     }
     for (int b = 0; b < B; ++b)
       DG_TRY(dg::selfcond_reduce(part + (size_t)b * ks * N * d, ks, N, d,
@@ -760,8 +793,8 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
       ec.tile_stats[b] = reinterpret_cast<float4 *>(st_of(b, SL.tstats));
     }
     ProfScope ps(g_prof_lm, s);
-    DG_TRY(dg::lm_head_bf16_batch(nrm16, B, N, d, static_cast<const uint16_t *>(w->E_pack), V, inv_T, ec, nullptr,
-                                  s));
+    const TableRef te = table_ref(cfg, w, false);
+    DG_TRY(dg::lm_head_bf16_batch(nrm16, B, N, d, te.bf, V, inv_T, ec, nullptr, s, te.q8, te.scale));
   }
   {  // row statistics of every canvas in one launch, then its candidates, then one selection launch
     dg::RowCombineBatch rc{};
@@ -997,9 +1030,11 @@ dg_status dg_test_selfcond(const dg_config *cfg, const dg_weights *w, const void
   if (cfg->dtype == DG_BF16) {
     const int ks = selfcond_ksplit(cfg);
     float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + L.sc_part);
-    const bf16 *tet = static_cast<const bf16 *>(w->E_pack) + pack_te_elems(cfg);
-    dg::TiledGemm g{static_cast<const uint16_t *>(P), tet, N, d, V};
-    DG_TRY(dg::selfcond_bf16(g, nullptr, part, ks, s));
+    const TableRef tt = table_ref(cfg, w, true);
+    dg::EsCanvasesIn cin{};
+    cin.probs[0] = static_cast<const uint16_t *>(P);
+    DG_TRY(dg::selfcond_bf16_batch(cin, 1, tt.bf, N, d, V, false, part, ks, s, dg::SelfcondGuard{nullptr, 0}, tt.q8,
+                                   tt.scale));
     DG_TRY(dg::selfcond_reduce(part, ks, N, d, nullptr, nullptr, V, nullptr, nullptr, nullptr, static_cast<float *>(S),
                                nullptr, s));
   } else {

@@ -137,8 +137,12 @@ struct EsCanvases {
   uint16_t *probs[ES_MAX_BATCH];
   float4 *tile_stats[ES_MAX_BATCH];
 };
+// The table comes in one of two forms: E_tiled (bf16) or E8_tiled (fp8
+// e4m3 in the 8-byte-chunk tiled layout, values q with E = q * e8_scale);
+// exactly one is non-null.
 hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, const uint16_t *E_tiled, int V,
-                              float inv_T, const EsCanvases &cv, float *logits_dump, hipStream_t s);
+                              float inv_T, const EsCanvases &cv, float *logits_dump, hipStream_t s,
+                              const uint8_t *E8_tiled = nullptr, float e8_scale = 1.f);
 // The self-conditioning contraction of B canvases at once: canvas c's
 // operand cin.probs[c] (its exponents cin.shift[c] when scaled), partials at
 // partials + c * ksplit * M * N (the single-canvas layout per canvas).
@@ -151,7 +155,8 @@ struct EsCanvasesIn {
 };
 hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *Et_tiled, int M, int N, int K,
                                bool scaled, float *partials, int ksplit, hipStream_t s,
-                               SelfcondGuard guard = SelfcondGuard{nullptr, 0});
+                               SelfcondGuard guard = SelfcondGuard{nullptr, 0}, const uint8_t *Et8_tiled = nullptr,
+                               float e8_scale = 1.f);
 // Same statistics from fp32 logits already in memory (fp32 path).
 hipError_t tile_stats_f32(const float *logits, int M, int V, float inv_T, float *probs,
                           float4 *tile_stats, hipStream_t s);
@@ -260,6 +265,11 @@ hipError_t transpose(const T *in, int rows, int cols, T *out, int64_t ld_out, hi
 // out = the tiled layout of dg_tiled.h, rows past R zero-filled.
 hipError_t tile_rows(const uint16_t *X, int R, int K, int64_t ldx, uint16_t *out, hipStream_t s);
 hipError_t copy_bytes(const void *src, void *dst, size_t bytes, hipStream_t s);
+// fp8 e4m3 copy in the 8-byte-chunk tiled layout (dg_tiled.h) of Y = X
+// (X [R][K]) or Y = X^T (trans: X [K][R]), leading dimension ldx: each value
+// times scale, clamped to +-448, rounded to nearest even; rows past R zero.
+hipError_t tile_fp8(const uint16_t *X, int R, int K, int64_t ldx, bool trans, float scale, uint8_t *out,
+                    hipStream_t s);
 
 // Selection and canvas.  mask_id >= 0: the masked sampler (the canvas starts
 // as mask_id; only positions holding it are walked; rejected ones keep it,

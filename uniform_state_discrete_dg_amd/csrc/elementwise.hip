@@ -184,6 +184,55 @@ hipError_t stack_tokens(const TokenPtrs &src, int B, int N, int32_t *out, hipStr
   return hipGetLastError();
 }
 
+// fp8 copy of a bf16 matrix in the 8-byte-chunk tiled layout (dg_tiled.h):
+// Y = X (X [R][K], leading dimension ldx) or, with trans, Y = X^T (X [K][R]);
+// each value y * scale rounded to fp8 e4m3 (nearest even), clamped to
+// +-448 first; rows past R are zero.  One workgroup per 256 x 32 block,
+// staged through LDS so that both forms read X along its rows.
+__global__ void __launch_bounds__(256) tile_fp8_kernel(const bf16 *__restrict__ X, int R, int K, int64_t ldx,
+                                                       int trans, float scale, uint8_t *__restrict__ out) {
+  __shared__ float tile[256][33];
+  const int nks = K / TL_K;
+  const int b = blockIdx.x / nks, s = blockIdx.x % nks;
+  const int t = threadIdx.x;
+  for (int i = 0; i < 32; ++i) {
+    const int idx = t + 256 * i;
+    int r, k;
+    float v = 0.f;
+    if (trans) {
+      k = idx >> 8;
+      r = idx & 255;
+      if (256 * b + r < R) v = bf16_to_f32(X[(int64_t)(32 * s + k) * ldx + 256 * b + r]);
+    } else {
+      r = idx >> 5;
+      k = idx & 31;
+      if (256 * b + r < R) v = bf16_to_f32(X[(int64_t)(256 * b + r) * ldx + 32 * s + k]);
+    }
+    tile[r][k] = v;
+  }
+  __syncthreads();
+  for (int j = 0; j < 4; ++j) {
+    const int p = t + 256 * j, r = p >> 2, c = (p & 3) ^ ((r >> 3) & 3);
+    uint32_t w[2] = {0u, 0u};
+    for (int h = 0; h < 2; ++h) {
+      float q[4];
+      for (int e = 0; e < 4; ++e) q[e] = fminf(fmaxf(tile[r][8 * c + 4 * h + e] * scale, -448.f), 448.f);
+      int packed = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+      packed = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], packed, true);
+      w[h] = (uint32_t)packed;
+    }
+    *reinterpret_cast<uint2 *>(out + (int64_t)blockIdx.x * TL8_BYTES + (int64_t)p * 8) = make_uint2(w[0], w[1]);
+  }
+}
+
+hipError_t tile_fp8(const uint16_t *X, int R, int K, int64_t ldx, bool trans, float scale, uint8_t *out,
+                    hipStream_t s) {
+  if (R < 1 || K % TL_K) return hipErrorInvalidValue;
+  const int blocks = (R + TL_ROWS - 1) / TL_ROWS * (K / TL_K);
+  hipLaunchKernelGGL(tile_fp8_kernel, dim3(blocks), dim3(256), 0, s, X, R, K, ldx, trans ? 1 : 0, scale, out);
+  return hipGetLastError();
+}
+
 hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top, const uint16_t *probs,
                            int V, const float *row_scale, const uint8_t *shift, const uint16_t *E, float *out,
                            uint16_t *out_split, hipStream_t s, int64_t lo_off) {

@@ -71,11 +71,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // field: a saturating subtraction of shift << 7 from each 16-bit value
 // (positive values; anything scaled below the normal range becomes zero or
 // a denormal).
-template <bool SCALED, bool PAIR = false>
+//
+// B8: the table operand is fp8 e4m3 (q = E * 2^e) in the 8-byte-chunk tiled
+// layout (8 KB per slice, one DMA instruction per wave); each table fragment
+// is read as 8 bytes and turned into bf16 q * b8_scale (b8_scale = 2^-e:
+// exact) before the MFMAs, so the accumulation is that of the bf16 table
+// holding the same values.
+template <bool SCALED, bool PAIR = false, bool B8 = false>
 __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const bf16 *__restrict__ Bt,
                                              const uint8_t *__restrict__ shift, int sb, int se, char *lds,
                                              f32x16_t (&acc)[2][4], const bf16 *__restrict__ At2 = nullptr,
-                                             const uint8_t *__restrict__ shift2 = nullptr) {
+                                             const uint8_t *__restrict__ shift2 = nullptr,
+                                             const uint8_t *__restrict__ Bt8 = nullptr, float b8_scale = 1.f) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r32 = lane & 31, g = lane >> 5;
@@ -97,7 +104,8 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   const bf16 *asrc = (PAIR && wave >= 4) ? At2 + (int64_t)sb * TL_ELEMS + ((wave - 4) * 2 * 64 + lane) * 8
                                          : At + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
   const uint8_t *ssrc = !SCALED ? nullptr : (PAIR && lane >= 32) ? shift2 + (lane - 32) * 4 : shift + lane * 4;
-  const bf16 *bsrc = Bt + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
+  const bf16 *bsrc = B8 ? nullptr : Bt + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
+  const uint8_t *bsrc8 = B8 ? Bt8 + (int64_t)sb * TL8_BYTES + (wave * 64 + lane) * 16 : nullptr;
   char *lds_shift = lds + ES_STAGES * 2 * ES_SLICE;  // SCALED: [stage][256] bytes
   auto issue = [&](int slice, int stage) {
     const int64_t off = (int64_t)min(slice, nk - 1) * TL_ELEMS;  // past the end: a repeat, never read
@@ -105,15 +113,19 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       __builtin_amdgcn_global_load_lds(asrc + off + u * 512, st + (wave * 2 + u) * 1024, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(bsrc + off + u * 512, st + ES_SLICE + (wave * 2 + u) * 1024, 16, 0, 0);
+      if (!B8)
+        __builtin_amdgcn_global_load_lds(bsrc + off + u * 512, st + ES_SLICE + (wave * 2 + u) * 1024, 16, 0, 0);
     }
+    if (B8)  // 8 KB of fp8 table: 1 KB per wave
+      __builtin_amdgcn_global_load_lds(bsrc8 + (int64_t)min(slice, nk - 1) * TL8_BYTES, st + ES_SLICE + wave * 1024,
+                                       16, 0, 0);
     if (SCALED && wave == (slice & 7))  // the slice tile's 256 row exponents, 4 bytes per lane
       __builtin_amdgcn_global_load_lds(ssrc + (int64_t)((sb + min(slice, nk - 1)) >> 1) * 256,
                                        lds_shift + stage * 256, 4, 0, 0);
   };
-  // DMA instructions per slice per wave: 4, plus the exponents of slice s
-  // for wave s % 8 when SCALED
-  constexpr int PER = 4;
+  // DMA instructions per slice per wave: 4 (3 with the fp8 table), plus the
+  // exponents of slice s for wave s % 8 when SCALED
+  constexpr int PER = B8 ? 3 : 4;
 
   // Fragment f of one 16-wide k step as stored: f < 2 a canvas fragment
   // (rows wm*64 + 32f), else table fragment f - 2 (rows wn*128 + 32(f-2)).
@@ -121,6 +133,17 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
     const uint4 *sl = reinterpret_cast<const uint4 *>(lds + stage * 2 * ES_SLICE + (f < 2 ? 0 : ES_SLICE));
     const int row = f < 2 ? wm * 64 + f * 32 + r32 : wn * 128 + (f - 2) * 32 + r32;
     return sl[tl_pos(row, kk * 2 + g)];
+  };
+  // B8: the 8 fp8 bytes of table fragment j (rows wn*128 + 32j), and their bf16 form
+  auto frag8 = [&](int stage, int kk, int j) -> uint2 {
+    const uint2 *sl = reinterpret_cast<const uint2 *>(lds + stage * 2 * ES_SLICE + ES_SLICE);
+    return sl[tl8_pos(wn * 128 + j * 32 + r32, kk * 2 + g)];
+  };
+  auto widen = [&](uint2 q) -> uint4 {
+    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, b8_scale, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, b8_scale, true)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, b8_scale, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, b8_scale, true)));
   };
   // SCALED: the exponent of canvas fragment i's row, and its packed form
   // (shift << 7 in both 16-bit halves)
@@ -139,6 +162,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   // With ex, the next half's exponents are read too (a new slice).
   auto half = [&](const uint4 (&cur)[6], uint4 (&nxt)[6], int nstage, int nkk, bool ex, u16x2_t (&e)[2]) {
     uint32_t sh[2];
+    uint2 q8[4];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int i = m >> 2, j = m & 3;
@@ -146,14 +170,24 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
                                                           __builtin_bit_cast(bf16x8_t, cur[i]), acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (m < 3) {
-        nxt[2 * m] = frag(nstage, nkk, 2 * m);
-        nxt[2 * m + 1] = frag(nstage, nkk, 2 * m + 1);
+        if (!B8 || m == 0) {
+          nxt[2 * m] = frag(nstage, nkk, 2 * m);
+          nxt[2 * m + 1] = frag(nstage, nkk, 2 * m + 1);
+        } else {
+          q8[2 * m - 2] = frag8(nstage, nkk, 2 * m - 2);
+          q8[2 * m - 1] = frag8(nstage, nkk, 2 * m - 1);
+        }
         if (SCALED && ex && m == 0) {
           sh[0] = expo(nstage, 0);
           sh[1] = expo(nstage, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    if (B8) {  // while the last MFMAs run
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nxt[2 + j] = widen(q8[j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (SCALED) {  // while the last MFMAs run
       if (ex) {
@@ -183,7 +217,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
     wait_vmcnt<2 * PER>();
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int f = 0; f < 6; ++f) F0[f] = frag(0, 0, f);
+  for (int f = 0; f < 6; ++f) F0[f] = (B8 && f >= 2) ? widen(frag8(0, 0, f - 2)) : frag(0, 0, f);
   if (SCALED) {
     ex[0] = packed(expo(0, 0));
     ex[1] = packed(expo(0, 1));
@@ -219,11 +253,12 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
 // run back to back on one XCD, so the table tile comes from HBM once and from
 // that XCD's L2 for the other blocks.
 // ---------------------------------------------------------------------------
-template <bool BATCH>
+template <bool BATCH, bool B8>
 __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__restrict__ At, int M, int N, int K,
                                                               const bf16 *__restrict__ Et, int V, float inv_T,
                                                               EsCanvases cv, int nblk, int items,
-                                                              float *__restrict__ logits) {
+                                                              float *__restrict__ logits,
+                                                              const uint8_t *__restrict__ Et8, float b8_scale) {
   extern __shared__ __align__(16) char lds[];
   int item = blockIdx.x;
   if (BATCH) item = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;  // grid: a multiple of 8
@@ -234,8 +269,9 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
   const int ksl = K / ES_BK;
   f32x16_t acc[2][4];
-  estream_tile<false>(At + (int64_t)bb * ksl * TL_ELEMS, Et + (int64_t)jt * ksl * TL_ELEMS, nullptr, 0, ksl, lds,
-                      acc);
+  estream_tile<false, false, B8>(At + (int64_t)bb * ksl * TL_ELEMS, B8 ? nullptr : Et + (int64_t)jt * ksl * TL_ELEMS,
+                                 nullptr, 0, ksl, lds, acc, nullptr, nullptr,
+                                 B8 ? Et8 + (int64_t)jt * ksl * TL8_BYTES : nullptr, b8_scale);
   const int ntiles = V / 64;
 
 #pragma unroll
@@ -315,25 +351,36 @@ int estream_bm(int) { return ES_BM; }
 static size_t es_lds_bytes() { return (size_t)ES_STAGES * (2 * ES_SLICE + 256); }
 
 hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, const uint16_t *E_tiled, int V,
-                              float inv_T, const EsCanvases &cv, float *logits_dump, hipStream_t s) {
+                              float inv_T, const EsCanvases &cv, float *logits_dump, hipStream_t s,
+                              const uint8_t *E8_tiled, float e8_scale) {
   if (B < 1 || B > ES_MAX_BATCH || N < 1 || N > ES_BM || K % ES_BK || V % ES_BN) return hipErrorInvalidValue;
+  if (!E_tiled == !E8_tiled) return hipErrorInvalidValue;  // exactly one table form
   static bool attr = false;
   if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(lm_head_es_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void *>(lm_head_es_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess)
-      return hipErrorInvalidValue;
+    const void *fns[4] = {reinterpret_cast<const void *>(lm_head_es_kernel<false, false>),
+                          reinterpret_cast<const void *>(lm_head_es_kernel<true, false>),
+                          reinterpret_cast<const void *>(lm_head_es_kernel<false, true>),
+                          reinterpret_cast<const void *>(lm_head_es_kernel<true, true>)};
+    for (const void *f : fns)
+      if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess)
+        return hipErrorInvalidValue;
     attr = true;
   }
   const int M = B * N, nblk = (M + ES_BM - 1) / ES_BM;
   const int items = (V / ES_BN) * nblk;
-  if (B == 1)
-    hipLaunchKernelGGL(lm_head_es_kernel<false>, dim3(items), dim3(ES_NT), es_lds_bytes(), s, A_tiled, M, N, K,
-                       E_tiled, V, inv_T, cv, nblk, items, logits_dump);
-  else
-    hipLaunchKernelGGL(lm_head_es_kernel<true>, dim3((items + 7) / 8 * 8), dim3(ES_NT), es_lds_bytes(), s, A_tiled,
-                       M, N, K, E_tiled, V, inv_T, cv, nblk, items, logits_dump);
+  const dim3 grid(B == 1 ? items : (items + 7) / 8 * 8);
+#define DG_LM_LAUNCH(BT, Q8)                                                                                   \
+  hipLaunchKernelGGL((lm_head_es_kernel<BT, Q8>), grid, dim3(ES_NT), es_lds_bytes(), s, A_tiled, M, N, K,      \
+                     reinterpret_cast<const bf16 *>(E_tiled), V, inv_T, cv, nblk, items, logits_dump, E8_tiled, \
+                     e8_scale)
+  if (B == 1) {
+    if (E8_tiled) DG_LM_LAUNCH(false, true);
+    else DG_LM_LAUNCH(false, false);
+  } else {
+    if (E8_tiled) DG_LM_LAUNCH(true, true);
+    else DG_LM_LAUNCH(true, false);
+  }
+#undef DG_LM_LAUNCH
   return hipGetLastError();
 }
 
@@ -342,7 +389,7 @@ hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E
   EsCanvases cv{};
   cv.probs[0] = probs_tiled;
   cv.tile_stats[0] = tile_stats;
-  return lm_head_bf16_batch(A_tiled, 1, M, K, E_tiled, V, inv_T, cv, logits_dump, s);
+  return lm_head_bf16_batch(A_tiled, 1, M, K, E_tiled, V, inv_T, cv, logits_dump, s, nullptr, 1.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -357,11 +404,12 @@ hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E
 // MODE: 0 one canvas; 1 a batch, one canvas per 256-row block; 2 a batch of
 // canvases of at most 128 rows, two per block (canvas 2p in rows 0..127,
 // canvas 2p + 1 in rows 128..255, read from its own buffers).
-template <bool SCALED, int MODE>
+template <bool SCALED, int MODE, bool B8>
 __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin, const bf16 *__restrict__ Bt,
                                                                int M, int N, int K, float *__restrict__ part,
                                                                int ksplit, int ntn, int nb, int items,
-                                                               SelfcondGuard guard) {
+                                                               SelfcondGuard guard, const uint8_t *__restrict__ Bt8,
+                                                               float b8_scale) {
   extern __shared__ __align__(16) char lds[];
   const int b = blockIdx.x, ng = gridDim.x;
   const int per_xcd = ng / 8;  // grid is a multiple of 8
@@ -374,15 +422,17 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin,
   const int sb = (int)((int64_t)ksl * kc / ksplit), se = (int)((int64_t)ksl * (kc + 1) / ksplit);
   const int n0 = nt * ES_BN;
   f32x16_t acc[2][4];
-  const bf16 *Bn = Bt + (int64_t)nt * ksl * TL_ELEMS;
+  const bf16 *Bn = B8 ? nullptr : Bt + (int64_t)nt * ksl * TL_ELEMS;
+  const uint8_t *Bn8 = B8 ? Bt8 + (int64_t)nt * ksl * TL8_BYTES : nullptr;
   if (MODE == 2) {
     const int c0 = 2 * blk, c1 = c0 + 1;
     // an odd batch's last block: its upper half is the canvas's own padding rows
     const bf16 *A2 = c1 < nb ? cin.probs[c1] : cin.probs[c0] + 512 * 8;
     const uint8_t *s2 = c1 < nb ? cin.shift[c1] : cin.shift[c0] + 128;
-    estream_tile<SCALED, true>(cin.probs[c0], Bn, cin.shift[c0], sb, se, lds, acc, A2, s2);
+    estream_tile<SCALED, true, B8>(cin.probs[c0], Bn, cin.shift[c0], sb, se, lds, acc, A2, s2, Bn8, b8_scale);
   } else {
-    estream_tile<SCALED>(cin.probs[blk], Bn, cin.shift[blk], sb, se, lds, acc);
+    estream_tile<SCALED, false, B8>(cin.probs[blk], Bn, cin.shift[blk], sb, se, lds, acc, nullptr, nullptr, Bn8,
+                                    b8_scale);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -406,17 +456,19 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin,
 }
 
 hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *Et_tiled, int M, int N, int K,
-                               bool scaled, float *partials, int ksplit, hipStream_t s, SelfcondGuard guard) {
+                               bool scaled, float *partials, int ksplit, hipStream_t s, SelfcondGuard guard,
+                               const uint8_t *Et8_tiled, float e8_scale) {
   if (B < 1 || B > ES_MAX_BATCH || M > ES_BM || K % 64 || N % 4 || ksplit < 1 || ksplit > K / ES_BK)
     return hipErrorInvalidValue;
+  if (!Et_tiled == !Et8_tiled) return hipErrorInvalidValue;  // exactly one table form
   static bool attr = false;
   if (!attr) {
-    const void *fns[6] = {reinterpret_cast<const void *>(selfcond_es_kernel<false, 0>),
-                          reinterpret_cast<const void *>(selfcond_es_kernel<true, 0>),
-                          reinterpret_cast<const void *>(selfcond_es_kernel<false, 1>),
-                          reinterpret_cast<const void *>(selfcond_es_kernel<true, 1>),
-                          reinterpret_cast<const void *>(selfcond_es_kernel<false, 2>),
-                          reinterpret_cast<const void *>(selfcond_es_kernel<true, 2>)};
+#define DG_SC_FN(SC, MD, Q8) reinterpret_cast<const void *>(selfcond_es_kernel<SC, MD, Q8>)
+    const void *fns[12] = {DG_SC_FN(false, 0, false), DG_SC_FN(true, 0, false), DG_SC_FN(false, 1, false),
+                           DG_SC_FN(true, 1, false),  DG_SC_FN(false, 2, false), DG_SC_FN(true, 2, false),
+                           DG_SC_FN(false, 0, true),  DG_SC_FN(true, 0, true),  DG_SC_FN(false, 1, true),
+                           DG_SC_FN(true, 1, true),   DG_SC_FN(false, 2, true), DG_SC_FN(true, 2, true)};
+#undef DG_SC_FN
     for (const void *f : fns)
       if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess)
         return hipErrorInvalidValue;
@@ -426,18 +478,24 @@ hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *E
   const int ntn = (N + ES_BN - 1) / ES_BN;
   const int items = ntn * ksplit * (mode == 2 ? (B + 1) / 2 : B);
   const dim3 grid((items + 7) / 8 * 8);
-#define DG_SC_LAUNCH(SC, MD)                                                                                    \
-  hipLaunchKernelGGL((selfcond_es_kernel<SC, MD>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Et_tiled, M, N, K, \
-                     partials, ksplit, ntn, B, items, guard)
-  if (scaled) {
-    if (mode == 0) DG_SC_LAUNCH(true, 0);
-    else if (mode == 1) DG_SC_LAUNCH(true, 1);
-    else DG_SC_LAUNCH(true, 2);
+  const bf16 *Bt = reinterpret_cast<const bf16 *>(Et_tiled);
+#define DG_SC_LAUNCH(SC, MD, Q8)                                                                                 \
+  hipLaunchKernelGGL((selfcond_es_kernel<SC, MD, Q8>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Bt, M, N, K,   \
+                     partials, ksplit, ntn, B, items, guard, Et8_tiled, e8_scale)
+#define DG_SC_MODES(SC, Q8)                  \
+  do {                                       \
+    if (mode == 0) DG_SC_LAUNCH(SC, 0, Q8);  \
+    else if (mode == 1) DG_SC_LAUNCH(SC, 1, Q8); \
+    else DG_SC_LAUNCH(SC, 2, Q8);            \
+  } while (0)
+  if (Et8_tiled) {
+    if (scaled) DG_SC_MODES(true, true);
+    else DG_SC_MODES(false, true);
   } else {
-    if (mode == 0) DG_SC_LAUNCH(false, 0);
-    else if (mode == 1) DG_SC_LAUNCH(false, 1);
-    else DG_SC_LAUNCH(false, 2);
+    if (scaled) DG_SC_MODES(true, false);
+    else DG_SC_MODES(false, false);
   }
+#undef DG_SC_MODES
 #undef DG_SC_LAUNCH
   return hipGetLastError();
 }
@@ -447,7 +505,8 @@ hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partia
   EsCanvasesIn cin{};
   cin.probs[0] = reinterpret_cast<const bf16 *>(g.A);
   cin.shift[0] = shift;
-  return selfcond_bf16_batch(cin, 1, g.B, g.M, g.N, g.K, shift != nullptr, partials, ksplit, s, guard);
+  return selfcond_bf16_batch(cin, 1, g.B, g.M, g.N, g.K, shift != nullptr, partials, ksplit, s, guard, nullptr,
+                             1.f);
 }
 
 }  // namespace dg

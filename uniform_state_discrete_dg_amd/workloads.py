@@ -95,6 +95,8 @@ def make_inputs(cfg: dict, seed: int | None = None) -> dict:
 
     out = dict(cfg=c)
     out["E"] = w(V, d)
+    if c.get("table") == "fp8":
+        out["E"] = fp8_grid(out["E"], c["table_exp"])
     out["w1"] = w(F, d)
     out["w2"] = w(d, F)
     out["wq"] = w(Hq * hd, d)
@@ -112,6 +114,16 @@ def make_inputs(cfg: dict, seed: int | None = None) -> dict:
     # like a row of E and last, so the inputs above do not depend on it
     out["mask_emb"] = w(1, d).view(d)
     return out
+
+
+def fp8_grid(E: torch.Tensor, exp: int) -> torch.Tensor:
+    """A quantised table: every entry replaced by the nearest value of the
+    form q * 2^-exp with q an fp8 e4m3 number (round to nearest even,
+    saturated at +-448), returned in E's dtype (exactly: such values are bf16
+    numbers).  This is an input of the fp8-table configurations, drawn before
+    either side sees it."""
+    q = (E.float() * (2.0 ** exp)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).float()
+    return (q * (2.0 ** -exp)).to(E.dtype)
 
 
 def random_row_weights(N: int, V: int, seed: int) -> torch.Tensor:
