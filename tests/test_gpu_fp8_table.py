@@ -37,12 +37,13 @@ def logits_dump():
 def tiled8_positions(R: int, K: int) -> torch.Tensor:
     """Byte index of X[r][k] in the fp8 tiled layout: blocks of 256 x 32,
     block (b, s) at (b * K/32 + s) * 8192, 8-byte chunk of row r and chunk c
-    at slot 4 r + (c ^ ((r / 8) % 4))."""
+    at slot 4 r + (c ^ w(r)), w(r) = (bit 2 xor bit 4 of r) + 2 bit 3 of r."""
     r = torch.arange(R).view(R, 1)
     k = torch.arange(K).view(1, K)
     b, rr, s, kk = r // 256, r % 256, k // 32, k % 32
     c = kk // 8
-    slot = rr * 4 + (c ^ ((rr // 8) % 4))
+    w = (((rr >> 2) ^ (rr >> 4)) & 1) | (((rr >> 3) & 1) << 1)
+    slot = rr * 4 + (c ^ w)
     return ((b * (K // 32) + s) * 1024 + slot) * 8 + kk % 8
 
 

@@ -34,12 +34,15 @@ inline size_t tl_elems(int R, int K) { return (size_t)((R + TL_ROWS - 1) / TL_RO
 
 // The fp8 form (one byte per value): the same blocks of 256 rows x 32
 // columns, 8 KB each, with 8-byte chunks: chunk p holds the 8 values
-// X[256 b + r][32 s + 8 c .. + 7], r = p / 4, c = (p % 4) ^ ((r / 8) % 4).
-// A table fragment is then one 8-byte LDS read per lane, and the 32 rows it
-// touches fall on distinct banks whether the LDS serves 16 or 32 lanes per
-// pass (rows 8 apart share a bank group and get different chunk slots).
+// X[256 b + r][32 s + 8 c .. + 7], r = p / 4, c = (p % 4) ^ w(r) with
+// w(r) = (bit 2 of r xor bit 4 of r) + 2 (bit 3 of r).  A table fragment is
+// one 8-byte LDS read per lane; with this w the reads of a fragment's 32
+// rows measured no bank conflict (the r / 4 and r / 8 swizzles measured 3 and
+// 17 M conflict cycles per LM-head launch).
 constexpr int TL8_BYTES = 8192;  // bytes per block
-__host__ __device__ inline int tl8_pos(int r, int c) { return r * 4 + (c ^ ((r >> 3) & 3)); }
+__host__ __device__ inline int tl8_pos(int r, int c) {
+  return r * 4 + (c ^ ((((r >> 2) ^ (r >> 4)) & 1) | (((r >> 3) & 1) << 1)));
+}
 __host__ __device__ inline int64_t tl8_index(int row, int col, int K) {
   const int b = row >> 8, r = row & 255, s = col >> 5, k = col & 31;
   return (((int64_t)b * (K >> 5) + s) * TL_CHUNKS + tl8_pos(r, k >> 3)) * 8 + (k & 7);
