@@ -212,7 +212,7 @@ __global__ void __launch_bounds__(256) tile_fp8_kernel(const bf16 *__restrict__ 
   }
   __syncthreads();
   for (int j = 0; j < 4; ++j) {
-    const int p = t + 256 * j, r = p >> 2, c = (p & 3) ^ ((r >> 3) & 3);
+    const int p = t + 256 * j, r = p >> 2, c = (p & 3) ^ (tl8_pos(r, 0) & 3);  // slot p holds chunk c
     uint32_t w[2] = {0u, 0u};
     for (int h = 0; h < 2; ++h) {
       float q[4];
