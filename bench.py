@@ -151,12 +151,12 @@ def batched_canvases(c: dict, inp: dict, w, cfg, sizes, steps: int, warmup: int)
 
         go(warmup, 0)
         torch.cuda.synchronize()
-        B.dg_profile_enable(True)
+        B.dg_profile_enable(3)
         t0 = time.perf_counter()
         go(steps, warmup)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
-        B.dg_profile_enable(False)
+        B.dg_profile_enable(0)
         lm_ms, lm_n, sc_ms, sc_n = B.dg_profile_read()
         sps = steps / dt
         res[str(nb)] = {
@@ -197,13 +197,13 @@ def fp8_table(c: dict, inp: dict, steps: int, warmup: int) -> dict:
     B.dg_run_canvas(den.cfg, den.w.s, den.cache.s, den.canvas.s, seed, 0, temps[:warmup], c["gamma"], True, 0,
                     den.ws)
     torch.cuda.synchronize()
-    B.dg_profile_enable(True)
+    B.dg_profile_enable(3)
     t0 = time.perf_counter()
     n, _ = B.dg_run_canvas(den.cfg, den.w.s, den.cache.s, den.canvas.s, seed, 1, temps[:steps], c["gamma"], True,
                            0, den.ws)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    B.dg_profile_enable(False)
+    B.dg_profile_enable(0)
     lm_ms, lm_n, sc_ms, sc_n = B.dg_profile_read()
     N, V, d = c["N"], c["V"], c["d"]
     lm_us = lm_ms / max(lm_n, 1) * 1e3
@@ -313,14 +313,14 @@ def main() -> int:
 
     run(args.warmup, 0)
     torch.cuda.synchronize()
-    B.dg_profile_enable(True)
+    B.dg_profile_enable(1)  # the LM head's launches, timed inside the timed region
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run(args.steps, 1)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    B.dg_profile_enable(False)
-    lm_ms, lm_n, sc_ms, sc_n = B.dg_profile_read()
+    B.dg_profile_enable(0)
+    lm_ms, lm_n, _, _ = B.dg_profile_read()
 
     # The two variants, each the same loop over a shorter timed run: the
     # multinomial candidate rule ([P3] §5.3: the draw kernel after the row
@@ -345,6 +345,21 @@ def main() -> int:
     masked_steps_per_s = timed_variant(sampler=B.DG_SAMPLER_MASKED)
 
     steps_per_s = args.steps / dt
+    # the same timed loop four more times (spread of one box; `value` stays the first)
+    repeats = [steps_per_s]
+    sc_ms, sc_n = 0.0, 0
+    for r in range(4):
+        run(3, 10 + r)
+        torch.cuda.synchronize()
+        if r == 0:  # the self-conditioning contraction's launches, timed in this repeat
+            B.dg_profile_enable(2)
+        t1 = time.perf_counter()
+        run(args.steps, 20 + r)
+        torch.cuda.synchronize()
+        repeats.append(args.steps / (time.perf_counter() - t1))
+        if r == 0:
+            B.dg_profile_enable(0)
+            _, _, sc_ms, sc_n = B.dg_profile_read()
     # every timed step but the first of the canvas uses self-conditioning
     flops = step_flops(c, True) * (args.steps - 1) + step_flops(c, False)
     lm_avg_s = lm_ms / 1e3 / max(lm_n, 1)
@@ -360,6 +375,8 @@ def main() -> int:
                    "head_dim": c["hd"], "ffn_hidden": c["F"], "prefix": c["L"],
                    "accept_threshold_nats": c["gamma"], "schedule": c["sched"]},
         "canvas_tokens_per_s": steps_per_s * c["N"],
+        "repeats": {"steps_per_s": repeats, "median": sorted(repeats)[len(repeats) // 2],
+                    "note": "the timed loop run five times back to back; value is the first"},
         "mfma_frac_of_bf16_peak": flops / dt / PEAK_BF16_FLOPS,
         "roofline": {"bound": "hbm", "kernel": "lm_head (tied head + softmax/entropy epilogue)",
                      "achieved": lm_gbs, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",

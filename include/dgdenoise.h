@@ -406,11 +406,13 @@ dg_status dg_test_gumbel(const uint32_t *w, int32_t n, int32_t mode, float *out,
  * memory-traffic counters. */
 dg_status dg_test_copy(const void *src, void *dst, size_t bytes, void *stream);
 
-/* Timing of the kernels inside dg_denoise_step: when enabled, HIP events are
- * recorded on the step's stream around the LM-head kernel and the
- * self-conditioning contraction.  dg_profile_read synchronises on the last
- * recorded events and returns the summed milliseconds and launch counts. */
-void dg_profile_enable(int32_t on);
+/* Timing of the kernels inside dg_denoise_step: HIP events are recorded on
+ * the step's stream around the LM-head kernel (mask bit 0) and the
+ * self-conditioning contraction (mask bit 1); 0 stops recording.  Each pair
+ * of records adds a marker to the stream, so a timed run records only the
+ * kernels it needs.  dg_profile_read synchronises on the last recorded
+ * events and returns the summed milliseconds and launch counts. */
+void dg_profile_enable(int32_t mask);
 dg_status dg_profile_read(float *lm_head_ms, int32_t *lm_head_count, float *selfcond_ms,
                           int32_t *selfcond_count);
 

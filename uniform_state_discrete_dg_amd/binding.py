@@ -275,8 +275,9 @@ def dg_test_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None)
     _check("dg_test_copy", lib().dg_test_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 
-def dg_profile_enable(on: bool) -> None:
-    lib().dg_profile_enable(1 if on else 0)
+def dg_profile_enable(mask: int) -> None:
+    """1: time the LM head, 2: the self-conditioning contraction, 3: both, 0: off."""
+    lib().dg_profile_enable(int(mask))
 
 
 def dg_profile_read():

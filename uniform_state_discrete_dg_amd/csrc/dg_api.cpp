@@ -185,16 +185,34 @@ bool g_logits_dump = false;
 
 // profiling (events around the two E-streaming contractions)
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+int g_prof_mask = 0;  // bit 0: LM head, bit 1: self-conditioning contraction
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_prof_lm, g_prof_sc;
+// Events created ahead (when profiling is switched on), so that a profiled
+// launch costs two event records and no event creation on the host.
+std::vector<hipEvent_t> g_prof_pool;
+constexpr size_t kProfPool = 1024;
+
+bool prof_take(hipEvent_t *e) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_pool.empty()) {
+    *e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return true;
+  }
+  return hipEventCreate(e) == hipSuccess;
+}
 
 struct ProfScope {
   std::vector<std::pair<hipEvent_t, hipEvent_t>> *vec = nullptr;
   hipEvent_t e0{}, e1{};
   hipStream_t s;
   ProfScope(std::vector<std::pair<hipEvent_t, hipEvent_t>> &v, hipStream_t st) : s(st) {
-    if (!g_prof_on) return;
-    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return;
+    if (!(g_prof_mask & (&v == &g_prof_lm ? 1 : 2))) return;
+    if (!prof_take(&e0)) return;
+    if (!prof_take(&e1)) {
+      (void)hipEventDestroy(e0);
+      return;
+    }
     vec = &v;
     (void)hipEventRecord(e0, s);
   }
@@ -1081,9 +1099,14 @@ dg_status dg_test_copy(const void *src, void *dst, size_t bytes, void *stream) {
   return DG_OK;
 }
 
-void dg_profile_enable(int32_t on) {
+void dg_profile_enable(int32_t mask) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_on = on != 0;
+  while (mask && g_prof_pool.size() < kProfPool) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) break;
+    g_prof_pool.push_back(e);
+  }
+  g_prof_mask = mask & 3;
 }
 
 dg_status dg_profile_read(float *lm_ms, int32_t *lm_n, float *sc_ms, int32_t *sc_n) {
@@ -1096,8 +1119,12 @@ dg_status dg_profile_read(float *lm_ms, int32_t *lm_n, float *sc_ms, int32_t *sc
       float t = 0.f;
       if (hipEventElapsedTime(&t, pr.first, pr.second) != hipSuccess) ok = false;
       tot += t;
-      (void)hipEventDestroy(pr.first);
-      (void)hipEventDestroy(pr.second);
+      for (hipEvent_t e : {pr.first, pr.second}) {
+        if (g_prof_pool.size() < kProfPool)
+          g_prof_pool.push_back(e);
+        else
+          (void)hipEventDestroy(e);
+      }
     }
     if (ms) *ms = tot;
     if (n) *n = (int32_t)v.size();
