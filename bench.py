@@ -249,7 +249,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", type=int, default=3, help="workload table entry (3: N256 V262144)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block-diffusion", action="store_true",
