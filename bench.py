@@ -9,7 +9,7 @@ the library's canvas loop (dg_run_canvas), exactly the loop a generator
 runs.  Inputs are seeded synthetic
 weights already resident in HBM before the timed region.
 
-Prints one JSON line.  --gpus above 1 is rejected: this build measures one
+Prints one JSON line.  --gpus above 1 is rejected: the benchmark measures one
 GPU's share (the sharded design is described in the documentation).
 """
 from __future__ import annotations
@@ -266,7 +266,7 @@ def main() -> int:
                          "(reference for memory-traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library runs on one GPU (the sharded design is not implemented); --gpus must be 1"}))
         return 2
 
     import torch
