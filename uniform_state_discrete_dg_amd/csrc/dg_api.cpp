@@ -185,7 +185,7 @@ bool g_logits_dump = false;
 
 // profiling (events around the two E-streaming contractions)
 std::mutex g_prof_mu;
-int g_prof_mask = 0;  // bit 0: LM head, bit 1: self-conditioning contraction
+std::atomic<int> g_prof_mask{0};  // bit 0: LM head, bit 1: self-conditioning contraction
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_prof_lm, g_prof_sc;
 // Events created ahead (when profiling is switched on), so that a profiled
 // launch costs two event records and no event creation on the host.
@@ -207,7 +207,7 @@ struct ProfScope {
   hipEvent_t e0{}, e1{};
   hipStream_t s;
   ProfScope(std::vector<std::pair<hipEvent_t, hipEvent_t>> &v, hipStream_t st) : s(st) {
-    if (!(g_prof_mask & (&v == &g_prof_lm ? 1 : 2))) return;
+    if (!(g_prof_mask.load(std::memory_order_relaxed) & (&v == &g_prof_lm ? 1 : 2))) return;
     if (!prof_take(&e0)) return;
     if (!prof_take(&e1)) {
       (void)hipEventDestroy(e0);
