@@ -78,7 +78,7 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(c: dict, inp: dict, rows=(2, 6)) -> dict:
+def cpu_baseline(c: dict, inp: dict, rows=(8, 56), sc_rows: int = 8) -> dict:
     """The oracle timed on a bounded sample: one step at rows[0] and rows[1]
     evaluated canvas rows (embedding and canvas K/V always use every row),
     plus self-conditioning rows, extrapolated linearly to all rows."""
@@ -91,6 +91,7 @@ def cpu_baseline(c: dict, inp: dict, rows=(2, 6)) -> dict:
     N, V = c["N"], c["V"]
     tok = oracle.canvas_init(1, 0, N, V)
     times = []
+    t_start = time.perf_counter()
     for r in rows:
         sel = np.zeros(N, np.uint8)
         sel[:r] = 1
@@ -102,15 +103,16 @@ def cpu_baseline(c: dict, inp: dict, rows=(2, 6)) -> dict:
     fixed = max(times[0] - per_row * rows[0], 0.0)
     p = np.full(V, 1.0 / V)
     t0 = time.perf_counter()
-    for _ in range(2):
+    for _ in range(sc_rows):
         om.selfcond_row(p)
-    sc_row = (time.perf_counter() - t0) / 2
+    sc_row = (time.perf_counter() - t0) / sc_rows
+    sample_s = time.perf_counter() - t_start
     t_step = fixed + N * (per_row + sc_row)
     return {"value": 1.0 / t_step, "unit": "steps/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": (f"{c['name']}: oracle step with {rows[0]} and {rows[1]} of {N} rows through "
-                       f"attention/LM head plus 2 self-conditioning rows, extrapolated linearly to "
-                       f"{N} rows (s/step = {t_step:.2f})")}
+                       f"attention/LM head plus {sc_rows} self-conditioning rows ({sample_s:.1f} s of oracle "
+                       f"time), extrapolated linearly to {N} rows (s/step = {t_step:.2f})")}
 
 
 def batched_canvases(c: dict, inp: dict, w, cfg, sizes, steps: int, warmup: int) -> dict:
