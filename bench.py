@@ -78,7 +78,7 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(c: dict, inp: dict, rows=(8, 56), sc_rows: int = 8) -> dict:
+def cpu_baseline(c: dict, inp: dict, rows=(16, 176), sc_rows: int = 24) -> dict:
     """The oracle timed on a bounded sample: one step at rows[0] and rows[1]
     evaluated canvas rows (embedding and canvas K/V always use every row),
     plus self-conditioning rows, extrapolated linearly to all rows."""
