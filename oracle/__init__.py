@@ -74,7 +74,8 @@ def lib():
         L.orc_attention.argtypes = [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                     _c_i32, _c_i32, _c_i32, _vp]
         L.orc_select.argtypes = [_c_i32, _c_i32, _vp, _vp, _vp, _c_dbl, _c_i32, _c_u64,
-                                 _c_u32, _c_u32, _c_i32, _c_dbl, _c_i32, _vp, _vp, _vp]
+                                 _c_u32, _c_u32, _c_i32, _c_dbl, _c_i32, _vp, _vp, _c_i32,
+                                 _vp, _vp, _vp]
         L.orc_denoise_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_dbl,
                                           _vp, _vp]
         L.orc_denoise_forward.restype = ctypes.c_int
@@ -226,41 +227,50 @@ def attention(q, k, v, Hq: int, Hkv: int, causal: bool = False, q_pos0: int = 0)
 # --------------------------------------------------------------------------
 ACCEPT_SUM_MINUS_MAX = 0
 ACCEPT_CUMSUM = 1
+STABLE_PREDICTIONS = 0
+STABLE_CANVAS = 1
 
 
 class _Flags(ctypes.Structure):
     _fields_ = [("allconf", _c_i32), ("changed", _c_i32), ("stable", _c_i32),
-                ("accepted", _c_i32), ("masked", _c_i32)]
+                ("accepted", _c_i32), ("masked", _c_i32), ("pred_changed", _c_i32)]
 
 
 def select(H, argmax_tokens, tokens_in, V: int, gamma: float, rule: int, seed: int,
            canvas_id: int, step: int, stable_in: int, conf_eps: float = 0.005,
-           mask_id: int = -1):
-    """[P3] §5.4 entropy-bounded acceptance + re-noise; [P5] stop flags.
+           mask_id: int = -1, stable_rule: int = STABLE_CANVAS, pred=None, pred_prev=None):
+    """[P3] §5.4 entropy-bounded acceptance + re-noise; [P3] §5.3 / [P5] stop flags.
 
     H is float32 (the decision is taken in the precision the kernel produces
-    its entropies in).  mask_id >= 0 selects the masked sampler ([P1] §1,
-    [P3] §3.1): only positions holding mask_id take part; accepted ones lock,
-    rejected ones stay mask_id.  Returns (accept uint8[N], tokens_out int32[N],
-    flags dict).
+    its entropies in; conf_eps is compared as a float32 too).  argmax_tokens:
+    the candidate token of each position.  mask_id >= 0 selects the masked
+    sampler ([P1] §1, [P3] §3.1): only positions holding mask_id take part;
+    accepted ones lock, rejected ones stay mask_id.  stable_rule: what the
+    stable counter counts -- STABLE_PREDICTIONS (the predictions `pred`, each
+    position's most likely token, equal to the previous step's `pred_prev`;
+    None at a canvas's first step) or STABLE_CANVAS (the canvas unchanged).
+    Returns (accept uint8[N], tokens_out int32[N], flags dict).
     """
     Hf = np.ascontiguousarray(H, dtype=np.float32)
     am = _i32(argmax_tokens)
     tin = _i32(tokens_in)
     N = Hf.shape[0]
+    pr = am if pred is None else _i32(pred)
+    pp = None if pred_prev is None else _i32(pred_prev)
     acc = np.zeros(N, dtype=np.uint8)
     tout = np.zeros(N, dtype=np.int32)
     fl = _Flags()
     lib().orc_select(N, V, _p(Hf), _p(am), _p(tin), float(gamma), int(rule), seed, canvas_id,
-                     step, stable_in, float(conf_eps), int(mask_id), _p(acc), _p(tout), ctypes.byref(fl))
+                     step, stable_in, float(conf_eps), int(mask_id), _p(pr), _p(pp), int(stable_rule),
+                     _p(acc), _p(tout), ctypes.byref(fl))
     flags = dict(allconf=fl.allconf, changed=fl.changed, stable=fl.stable, accepted=fl.accepted,
-                 masked=fl.masked)
+                 masked=fl.masked, pred_changed=fl.pred_changed)
     return acc, tout, flags
 
 
 def should_stop(flags: dict, stable_steps: int) -> bool:
     fl = _Flags(flags["allconf"], flags["changed"], flags["stable"], flags.get("accepted", 0),
-                flags.get("masked", -1))
+                flags.get("masked", -1), flags.get("pred_changed", 1))
     return bool(lib().orc_should_stop(ctypes.byref(fl), stable_steps))
 
 

@@ -293,7 +293,8 @@ void orc_attention(const double *q, const double *k, const double *v,
 /* the first failure ends the walk.  [P5] states the same walk with the plain */
 /* cumulative sum (ORC_ACCEPT_CUMSUM).  [P3] §5.4 re-noise: every rejected   */
 /* position receives a fresh uniform token.  [P3] §5.3 / [P5] adaptive stop: */
-/* confidence (entropies below a threshold) and stability (unchanged canvas). */
+/* confidence (entropies below a threshold) and stability (predictions, or  */
+/* the canvas, unchanged from the previous step).                            */
 /*                                                                           */
 /* Readings where the pages leave a step open:                               */
 /*  - the running sums are taken in 2^-32-nat fixed point, q = floor(H*2^32), */
@@ -320,6 +321,7 @@ void orc_select(int32_t N, int32_t V, const float *H, const int32_t *argmax,
                 const int32_t *tokens_in, double gamma, int32_t rule,
                 uint64_t seed, uint32_t canvas_id, uint32_t step,
                 int32_t stable_in, double conf_eps, int32_t mask_id,
+                const int32_t *pred, const int32_t *pred_prev, int32_t stable_rule,
                 uint8_t *accept, int32_t *tokens_out, orc_flags *flags) {
   /* the positions that take part: all of them, or (masked sampler) those */
   /* still holding [MASK]                                                  */
@@ -353,6 +355,8 @@ void orc_select(int32_t N, int32_t V, const float *H, const int32_t *argmax,
   }
   free(keys);
 
+  /* the entropies are floats, so the confidence test is a float comparison */
+  const float eps = (float)conf_eps;
   int32_t allconf = 1, changed = 0, masked = 0;
   for (int32_t i = 0; i < N; ++i) {
     int32_t t;
@@ -366,11 +370,24 @@ void orc_select(int32_t N, int32_t V, const float *H, const int32_t *argmax,
     if (t != tokens_in[i]) changed = 1;
     if (mask_id >= 0 && t == mask_id) ++masked;
     const float h = clamp_entropy(H[i]);
-    if (!((double)h < conf_eps)) allconf = 0;
+    if (!(h < eps)) allconf = 0;
+  }
+  /* [P3] §5.3 / [P5]: are the predictions those of the previous step?  Not  */
+  /* at a canvas's first step, and not when any entropy is NaN (a position  */
+  /* without a distribution has no prediction to compare).                   */
+  int32_t pred_changed = 1;
+  if (pred != NULL && pred_prev != NULL) {
+    pred_changed = 0;
+    for (int32_t i = 0; i < N; ++i)
+      if (pred[i] != pred_prev[i] || H[i] != H[i]) pred_changed = 1;
   }
   flags->allconf = allconf;
   flags->changed = changed;
-  flags->stable = changed ? 0 : stable_in + 1;
+  flags->pred_changed = pred_changed;
+  if (stable_rule == ORC_STABLE_PREDICTIONS)
+    flags->stable = pred_changed ? 0 : stable_in + 1;
+  else
+    flags->stable = changed ? 0 : stable_in + 1;
   flags->accepted = accepted;
   flags->masked = mask_id >= 0 ? masked : -1;
 }

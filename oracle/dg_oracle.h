@@ -107,17 +107,32 @@ void orc_attention(const double *q, const double *k, const double *v,
 
 /* ---- entropy-bounded selection ([P3] §5.4, [P5] entropy-constrained sampler) */
 enum { ORC_ACCEPT_SUM_MINUS_MAX = 0, ORC_ACCEPT_CUMSUM = 1 };
+/* What "stable" counts ([P3] §5.3 adaptive stop: the highest-probability    */
+/* predictions unchanged over the last N steps; [P5] scheduler: the         */
+/* predictions identical for N consecutive steps).                           */
+/*   PREDICTIONS: steps in a row whose predictions (each position's most     */
+/*     likely token) equal the previous step's at every position; a step    */
+/*     with no previous step, or with a NaN entropy anywhere, resets it.     */
+/*   CANVAS: steps in a row that left the canvas unchanged (equal to         */
+/*     PREDICTIONS whenever every position is accepted with its argmax).     */
+enum { ORC_STABLE_PREDICTIONS = 0, ORC_STABLE_CANVAS = 1 };
 typedef struct {
   int32_t allconf;   /* every entropy < conf_eps (NaN counts as not confident) */
   int32_t changed;   /* canvas after != canvas before                          */
-  int32_t stable;    /* consecutive unchanged steps                            */
+  int32_t stable;    /* consecutive stable steps, by the stability rule        */
   int32_t accepted;  /* number of accepted positions                           */
   int32_t masked;    /* [MASK] positions after the step; -1 under re-noise      */
+  int32_t pred_changed; /* predictions differ from the previous step's, or    */
+                        /* there is none, or an entropy is NaN                */
 } orc_flags;
 
 /* Decisions of one step from the per-position entropies H (float, as the
  * kernel produces them) and candidate tokens.  Writes accept[N] (0/1),
- * tokens_out[N] and flags.
+ * tokens_out[N] and flags.  pred[N]: the step's predictions (the most
+ * likely token of each position); pred_prev[N]: the previous step's, NULL at
+ * a canvas's first step; pred_changed is reported under either rule, the
+ * stable count follows stable_rule.
+ * conf_eps is compared in single precision, as the entropies are.
  * mask_id < 0: uniform-state sampler -- every position takes part, rejected
  *   ones are re-noised with a uniform token.
  * mask_id >= 0: masked sampler ([P1] §1, [P3] §3.1) -- only positions holding
@@ -127,6 +142,7 @@ void orc_select(int32_t N, int32_t V, const float *H, const int32_t *argmax,
                 const int32_t *tokens_in, double gamma, int32_t rule,
                 uint64_t seed, uint32_t canvas_id, uint32_t step,
                 int32_t stable_in, double conf_eps, int32_t mask_id,
+                const int32_t *pred, const int32_t *pred_prev, int32_t stable_rule,
                 uint8_t *accept, int32_t *tokens_out, orc_flags *flags);
 
 /* ---- one denoising step ---------------------------------------------------- */

@@ -485,7 +485,7 @@ def test_select_renoise_and_flags():
     # every position accepted with argmax == canvas: unchanged, stable counter grows
     acc, tout, fl = oracle.select(np.zeros(N, np.float32), am, am, V, 1.0, 0, seed, cid, step, 4)
     assert acc.all() and (tout == am).all()
-    assert fl == dict(allconf=1, changed=0, stable=5, accepted=N, masked=-1)
+    assert fl == dict(allconf=1, changed=0, stable=5, accepted=N, masked=-1, pred_changed=1)
     # confidence is strict: H == eps is not confident; NaN is never confident
     Hc = np.full(N, 0.004, np.float32)
     Hc[0] = np.float32(0.005)
@@ -494,6 +494,85 @@ def test_select_renoise_and_flags():
     Hc[0] = np.nan
     _, _, fl = oracle.select(Hc, am, am, V, 1.0, 0, seed, cid, step, 0)
     assert fl["allconf"] == 0
+    # the threshold is compared as a float32 (the entropies are float32): an
+    # entropy equal to float32(0.005), just below 0.005, is not below it
+    Hc[0] = np.float32(0.005)
+    assert float(Hc[0]) < 0.005
+    _, _, fl = oracle.select(Hc, am, am, V, 1.0, 0, seed, cid, step, 0, conf_eps=0.005)
+    assert fl["allconf"] == 0
+    Hc[0] = np.nextafter(np.float32(0.005), np.float32(0))
+    _, _, fl = oracle.select(Hc, am, am, V, 1.0, 0, seed, cid, step, 0, conf_eps=0.005)
+    assert fl["allconf"] == 1
+
+
+def test_select_stability_on_predictions():
+    """[P3] §5.3 / [P5]: the adaptive stop's stability counts steps whose
+    predictions (each position's most likely token) are those of the step
+    before.  Constructed sequences: predictions held while the canvas keeps
+    being re-noised count up; one differing position, a NaN entropy or a
+    canvas's first step reset the count; the canvas rule counts the other
+    thing."""
+    N, V, seed, cid = 10, 1024, 5, 2
+    rng = np.random.default_rng(11)
+    pred = rng.integers(0, V, N).astype(np.int32)
+    H = np.full(N, 3.0, np.float32)          # gamma 1: one position accepted per step,
+    tok = rng.integers(0, V, N).astype(np.int32)  # the rest re-noised -> the canvas changes
+    P, C = oracle.STABLE_PREDICTIONS, oracle.STABLE_CANVAS
+    # first step of a canvas: no previous predictions
+    _, tok1, fl = oracle.select(H, pred, tok, V, 1.0, 0, seed, cid, 0, 0, stable_rule=P, pred=pred)
+    assert fl["stable"] == 0 and fl["pred_changed"] == 1 and fl["changed"] == 1
+    stable = 0
+    for step in range(1, 6):
+        acc, tok2, fl = oracle.select(H, pred, tok1, V, 1.0, 0, seed, cid, step, stable,
+                                      stable_rule=P, pred=pred, pred_prev=pred)
+        assert acc.sum() == 1 and fl["changed"] == 1     # the canvas is not stable ...
+        assert fl["pred_changed"] == 0 and fl["stable"] == step  # ... the predictions are
+        # the canvas rule on the same step: the count resets
+        _, _, flc = oracle.select(H, pred, tok1, V, 1.0, 0, seed, cid, step, stable,
+                                  stable_rule=C, pred=pred, pred_prev=pred)
+        assert flc["stable"] == 0 and flc["pred_changed"] == 0
+        stable, tok1 = fl["stable"], tok2
+    assert oracle.should_stop(fl, 5) and not oracle.should_stop(fl, 6)
+    # one position's prediction differs: reset
+    other = pred.copy()
+    other[7] = (other[7] + 1) % V
+    _, _, fl = oracle.select(H, other, tok1, V, 1.0, 0, seed, cid, 6, stable, stable_rule=P, pred=other,
+                             pred_prev=pred)
+    assert fl["pred_changed"] == 1 and fl["stable"] == 0
+    # a NaN entropy anywhere: no stable predictions
+    Hn = H.copy()
+    Hn[3] = np.nan
+    _, _, fl = oracle.select(Hn, pred, tok1, V, 1.0, 0, seed, cid, 6, stable, stable_rule=P, pred=pred,
+                             pred_prev=pred)
+    assert fl["pred_changed"] == 1 and fl["stable"] == 0 and not oracle.should_stop(fl, 1)
+    # candidates (what an accepted position takes) and predictions are separate inputs
+    cand = (pred + 3) % V
+    acc, tok3, fl = oracle.select(np.zeros(N, np.float32), cand, tok1, V, 100.0, 0, seed, cid, 6, stable,
+                                  stable_rule=P, pred=pred, pred_prev=pred)
+    assert acc.all() and (tok3 == cand).all() and fl["stable"] == stable + 1
+
+
+def test_stability_rules_agree_when_everything_is_accepted():
+    """When every position is accepted with its prediction, the canvas after a
+    step is the prediction vector, so from the second step on the two
+    stability rules count the same steps."""
+    rng = np.random.default_rng(12)
+    N, V = 12, 64
+    tok = rng.integers(0, V, N).astype(np.int32)
+    sp = sc = 0
+    prev = None
+    for step in range(30):
+        pred = prev.copy() if prev is not None and rng.random() < 0.6 else rng.integers(0, V, N).astype(np.int32)
+        if prev is not None and rng.random() < 0.3:
+            pred[rng.integers(0, N)] = rng.integers(0, V)
+        H = np.zeros(N, np.float32)
+        _, outp, flp = oracle.select(H, pred, tok, V, 1e6, 1, 1, 0, step, sp, stable_rule=oracle.STABLE_PREDICTIONS,
+                                     pred=pred, pred_prev=prev)
+        _, outc, flc = oracle.select(H, pred, tok, V, 1e6, 1, 1, 0, step, sc, stable_rule=oracle.STABLE_CANVAS)
+        assert (outp == pred).all() and (outc == pred).all()
+        if step >= 1:
+            assert flp["stable"] == flc["stable"], step
+        sp, sc, tok, prev = flp["stable"], flc["stable"], outp, pred
 
 
 def test_select_permutation_equivariant():
