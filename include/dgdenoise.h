@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define DG_ABI_VERSION 5
+#define DG_ABI_VERSION 6
 
 typedef enum {
   DG_OK = 0,
@@ -110,6 +110,19 @@ typedef enum { DG_SAMPLER_UNIFORM = 0, DG_SAMPLER_MASKED = 1 } dg_sampler;
  *       (E_pack 2 V d bytes instead of 4 V d). */
 typedef enum { DG_TABLE_BF16 = 0, DG_TABLE_FP8 = 1 } dg_table_format;
 
+/* What the adaptive stop's stability counter counts ([P3] §5.3 adaptive
+ * stop: the most likely token predictions unchanged over the last N steps;
+ * [P5] scheduler: the predictions identical for N consecutive steps).
+ * PREDICTIONS: consecutive steps whose predictions -- each position's most
+ *   likely token (highest logit, lowest index on ties), whatever token the
+ *   candidate rule places -- equal the previous step's at every position.
+ *   A canvas's first step (step 0) and a step with any NaN entropy count as
+ *   changed.
+ * CANVAS: consecutive steps that left the canvas unchanged.  The two agree
+ *   whenever every position is accepted with its argmax; under re-noise the
+ *   canvas changes even when the predictions do not. */
+typedef enum { DG_STABLE_PREDICTIONS = 0, DG_STABLE_CANVAS = 1 } dg_stable_rule;
+
 /* Model and canvas shape.
  * Supported: 1 <= canvas_len <= 256; vocab a power of two in [256, 2^24];
  * n_q_heads a multiple of n_kv_heads.  DG_BF16 additionally needs head_dim ==
@@ -132,6 +145,7 @@ typedef struct {
   dg_sampler sampler;
   dg_table_format table_format;
   int32_t table_exp;    /* DG_TABLE_FP8: q = E * 2^table_exp, in [-32, 32] */
+  dg_stable_rule stable_rule;
 } dg_config;
 
 /* Weights (device, dtype of the config, caller-owned, read-only).
@@ -174,9 +188,10 @@ typedef struct {
  *                                factor kept in stats (the dominant token's
  *                                exact probability is kept there too)
  *   stats   bytes dg_stats_bytes(): per-(row, tile) softmax statistics,
- *                                factors and exponents, per-row factors
- *                                and each row's dominant token with its
- *                                exact probability; opaque
+ *                                factors and exponents, per-row factors,
+ *                                each row's dominant token with its exact
+ *                                probability and the previous step's
+ *                                predictions; opaque
  *   entropy float [N]            nats, clamped >= +0 (NaN propagates)
  *   argmax  int32 [N]            the candidate token of the last step: the
  *                                highest logit (lowest index on ties), or the
@@ -189,14 +204,16 @@ typedef struct {
 enum {
   DG_ST_ALLCONF = 0,   /* every entropy < conf_eps */
   DG_ST_CHANGED = 1,   /* last step changed the canvas */
-  DG_ST_STABLE = 2,    /* consecutive steps without change */
+  DG_ST_STABLE = 2,    /* consecutive stable steps (stable_rule) */
   DG_ST_ACCEPTED = 3,  /* positions accepted in the last step */
   DG_ST_NAN = 4,       /* positions whose entropy was NaN */
   DG_ST_STEP = 5,      /* index of the last completed step */
   DG_ST_HMIN = 6,      /* float bits: min entropy */
   DG_ST_HMAX = 7,      /* float bits: max entropy */
   DG_ST_HMEAN = 8,     /* float bits: mean entropy */
-  DG_ST_MASKED = 9     /* [MASK] positions left (DG_SAMPLER_MASKED), else -1 */
+  DG_ST_MASKED = 9,    /* [MASK] positions left (DG_SAMPLER_MASKED), else -1 */
+  DG_ST_PRED_CHANGED = 10  /* 1: the predictions differ from the previous
+                              step's (or step 0, or a NaN entropy), 0: same */
 };
 typedef struct {
   int32_t *tokens;
@@ -289,7 +306,9 @@ dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cac
  *     positions take the candidate token, every rejected one a fresh uniform
  *     token (Philox counter (i, step, canvas_id, 1)) -- or, under
  *     DG_SAMPLER_MASKED, only [MASK] positions are walked, rejected ones
- *     stay [MASK] and decided ones are kept; status flags updated
+ *     stay [MASK] and decided ones are kept; status flags updated, the
+ *     stability counter by cfg->stable_rule (the predictions are kept in
+ *     stats for the next step's comparison)
  * Then canvas->step += 1 and canvas->has_prev = 1 (host fields).
  * Errors: temperature must be finite and > 0; the threshold >= 0 and not NaN;
  * DG_ERR_WORKSPACE if ws_bytes < dg_workspace_bytes(cfg, 0). */
@@ -333,9 +352,10 @@ dg_status dg_denoise_step_batch(const dg_config *cfg, const dg_weights *w, const
                                 float accept_threshold_nats, void *ws, size_t ws_bytes, void *stream);
 
 /* Adaptive stop, [P3] §5.3 and [P5] scheduler: stop when every entropy is
- * below conf_eps, or when the canvas has been unchanged for stable_steps
- * consecutive steps (stable_steps <= 0 disables the stability test), or,
- * under DG_SAMPLER_MASKED, when no [MASK] is left ([P3] §3.1).
+ * below conf_eps, or when the stability counter (the predictions, or the
+ * canvas, unchanged: cfg->stable_rule) has reached stable_steps
+ * (stable_steps <= 0 disables the stability test), or, under
+ * DG_SAMPLER_MASKED, when no [MASK] is left ([P3] §3.1).
  * Synchronises `stream`, then writes *stop_host (0/1) and, if non-NULL,
  * *stats_host.  This is the only device-to-host transfer of a step. */
 dg_status dg_should_stop(const dg_config *cfg, const dg_canvas *canvas, int32_t stable_steps,
@@ -383,12 +403,21 @@ dg_status dg_test_ws_offsets(const dg_config *cfg, dg_ws_offsets *out);
 void dg_test_set_logits_dump(int32_t on);
 size_t dg_test_logits_ws_bytes(const dg_config *cfg);
 
-/* Self-conditioning contraction alone: S (f32 [N][d]) = P E, with P given
- * as plain probabilities in the layout of dg_canvas.probs (DG_BF16: tiled
- * bf16 [N][V], no tile exponents or row factors; DG_F32: float [N][V]); no
- * correction of the dominant token. */
+/* Self-conditioning contraction alone ([P3] §5.1): S (f32 [N][d]) = P E,
+ * with P given as plain probabilities in the layout of dg_canvas.probs
+ * (DG_BF16: tiled bf16 [N][V]; DG_F32: float [N][V]), run by the kernels
+ * dg_denoise_step runs, with every tile exponent 0, row factor 1 and no
+ * dominant-token correction.  ws: at least dg_test_logits_ws_bytes() bytes
+ * (the zero exponents are written there). */
 dg_status dg_test_selfcond(const dg_config *cfg, const dg_weights *w, const void *P, void *S,
                            void *ws, size_t ws_bytes, void *stream);
+/* The self-conditioning vector S (f32 [N][d], device) = p E of the canvas's
+ * kept state (its last step's probabilities: numerators, tile exponents,
+ * row factors and the dominant token's exact probability), computed exactly
+ * as the canvas's next dg_denoise_step computes it ([P3] §5.1).
+ * ws: at least dg_workspace_bytes(cfg, 0) bytes. */
+dg_status dg_test_selfcond_canvas(const dg_config *cfg, const dg_weights *w, const dg_canvas *canvas, void *S,
+                                  void *ws, size_t ws_bytes, void *stream);
 /* Selection kernel alone on given entropies/argmax/tokens (device):
  * writes tokens (in place), accept and status exactly as dg_denoise_step. */
 dg_status dg_test_select(const dg_config *cfg, dg_canvas *canvas, float accept_threshold_nats,

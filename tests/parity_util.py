@@ -60,14 +60,23 @@ def check_argmax(z_oracle_rows, am_oracle, am_gpu, rows, gap_tol):
 
 
 def replay_select(den: D.Denoiser, tokens_in, stable_in, step, gamma, rule):
-    """Oracle selection on the GPU's own entropies/argmax: must be bit-exact."""
+    """Oracle selection on the GPU's own entropies, candidates and
+    predictions: must be bit-exact.  The previous step's predictions are the
+    ones this helper saw at the canvas's previous step (call it for every
+    step of a canvas, from step 0)."""
     cfg = den.cfg
     H = den.canvas.entropy.cpu().numpy()
     am = den.canvas.argmax.cpu().numpy()
+    pred = den.canvas.predictions(cfg).cpu().numpy()
+    prev = None if step == 0 else den.canvas.replay_pred
+    assert step == 0 or prev is not None, "replay every step of the canvas from step 0"
     mask_id = cfg.vocab if cfg.sampler == B.DG_SAMPLER_MASKED else -1
     acc, tout, fl = oracle.select(H, am, tokens_in, cfg.vocab, gamma, rule, den.canvas.s.seed,
-                                  den.canvas.s.canvas_id, step, stable_in, CONF_EPS_F32, mask_id=mask_id)
+                                  den.canvas.s.canvas_id, step, stable_in, CONF_EPS_F32, mask_id=mask_id,
+                                  stable_rule=cfg.stable_rule, pred=pred, pred_prev=prev)
+    den.canvas.replay_pred = pred
     st = den.canvas.status.cpu().numpy()
+    assert st[B.DG_ST_PRED_CHANGED] == fl["pred_changed"]
     np.testing.assert_array_equal(den.canvas.accept.cpu().numpy(), acc)
     np.testing.assert_array_equal(den.canvas.tokens.cpu().numpy(), tout)
     assert st[B.DG_ST_ALLCONF] == fl["allconf"]

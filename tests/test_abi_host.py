@@ -38,7 +38,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert B.dg_abi_version() == 5
+    assert B.dg_abi_version() == 6
     for s in range(6):
         assert lib.dg_status_string(s)
 
@@ -55,11 +55,13 @@ def test_shipped_configs_supported(lib, i):
     assert B.dg_validate_config(cfg) == B.DG_OK
     assert B.dg_workspace_bytes(cfg, 0) > 0
     assert B.dg_workspace_bytes(cfg, 1024) >= B.dg_workspace_bytes(cfg, 0)
-    # float4 tile stats + float tile scale per (row, tile), float2 top and float
-    # row scale per row, then (256-byte aligned) a uint8 exponent per (tile, 256 rows)
+    # float4 tile stats + float tile scale per (row, tile), float2 top, float
+    # row scale and int32 previous prediction per row, then (256-byte aligned)
+    # a uint8 exponent per (tile, 256 rows)
     nt = cfg.vocab // 64
-    head = cfg.canvas_len * (nt * 20 + 8 + 4)
+    head = cfg.canvas_len * (nt * 20 + 8 + 4 + 4)
     assert B.dg_stats_bytes(cfg) == (head + 255) // 256 * 256 + nt * 256
+    assert B.stats_offsets(cfg)["shift"] == (head + 255) // 256 * 256
 
 
 @pytest.mark.parametrize("kw,st", [
@@ -71,6 +73,7 @@ def test_shipped_configs_supported(lib, i):
     (dict(d=4160), B.DG_ERR_UNSUPPORTED),        # row combine holds a d-row in 16 values per thread
     (dict(Hq=12, Hkv=8), B.DG_ERR_UNSUPPORTED),  # GQA groups must divide
     (dict(N=0), B.DG_ERR_INVALID_ARG),
+    (dict(stable_rule=2), B.DG_ERR_INVALID_ARG),   # no such stability rule
     (dict(rms_eps=-1.0), B.DG_ERR_INVALID_ARG),
 ])
 def test_config_rejections(lib, kw, st):

@@ -36,9 +36,12 @@ def _free_memory():
     torch.cuda.empty_cache()
 
 
-def lockstep(c, inp, nsteps, rule=0, seed=None, cid=0, masked=False):
+def lockstep(c, inp, nsteps, rule=0, seed=None, cid=0, masked=False, stop=False):
     """Runs nsteps GPU steps and checks each against the oracle (all rows);
-    masked: the masked-diffusion sampler ([MASK] = id V)."""
+    masked: the masked-diffusion sampler ([MASK] = id V); stop: after every
+    step the library's adaptive-stop test (dg_should_stop, c["stable_n"])
+    must agree with the oracle's on the replayed flags, and the loop ends
+    when it fires."""
     f32 = c["dtype"] == "f32"
     tol = 1e-4 if f32 else 1e-2
     den = D.Denoiser(c, inp, accept_rule=rule, logits_dump=True,
@@ -86,6 +89,12 @@ def lockstep(c, inp, nsteps, rule=0, seed=None, cid=0, masked=False):
         fl = replay_select(den, tokens_in, stable, s, c["gamma"], rule)
         stable = fl["stable"]
         p_prev = o["probs"]
+        if stop:
+            halt, st = den.should_stop(c["stable_n"])
+            assert halt == oracle.should_stop(fl, c["stable_n"]), (s, fl)
+            report[-1]["stop"] = halt
+            if halt:
+                break
     return den, report
 
 
@@ -135,6 +144,17 @@ def test_config2_bf16_lockstep(rule):
 
 
 @pytest.mark.usefixtures("logits_dump")
+def test_config2_bf16_lockstep_full_budget_adaptive_stop():
+    """Configuration 2 over its whole 16-step budget (cosine 1.5 -> 0.3), every
+    step in lock-step with the oracle, with the adaptive stop (all entropies
+    below 0.005, or the predictions stable for 3 steps) tested after each
+    step against the oracle's decision on the replayed flags."""
+    c = W.config(2)
+    den, rep = lockstep(c, W.make_inputs(c), c["steps"], stop=True)
+    print(len(rep), "steps;", rep[-1])
+
+
+@pytest.mark.usefixtures("logits_dump")
 def test_config1_fp32_masked_sampler_lockstep():
     c = W.config(1)
     den, rep = lockstep(c, W.make_inputs(c), c["steps"], masked=True)
@@ -157,10 +177,7 @@ def test_config2_bf16_lockstep_low_temperature():
     c = W.config(2, sched="const", T0=0.05, T1=0.05)
     inp = W.make_inputs(c)
     den, rep = lockstep(c, inp, 3)
-    st = den.canvas.stats
-    nt = c["V"] // 64
-    head = c["N"] * (nt * 20 + 8 + 4)
-    shift = st[(head + 255) // 256 * 256:].view(nt, 256)[:, :c["N"]]
+    shift = den.canvas.exponents(den.cfg)
     assert int(shift.max()) == 255 and int(shift.min()) == 0, (int(shift.min()), int(shift.max()))
     print(rep)
 
@@ -466,3 +483,98 @@ def test_masked_sampler_runs_until_unmasked(cfg_id, budget):
     # masks only ever resolve: the per-step counts of the host loop never grow
     counts = [st.masked for st in a.stats]
     assert all(x >= y for x, y in zip(counts, counts[1:])) and counts[-1] == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_multinomial_draw_law(dtype):
+    """[P3] §5.3 logits scheduler: the candidate drawn at each position follows
+    softmax(z / T) -- the law, not just the replay.  The canvas is held fixed
+    (every step a first step, so the logits are fixed) while the step counter,
+    which keys the draw's Philox counters, runs over K values; the K draws of
+    each row are tested by chi-square against the probabilities the oracle
+    computes from its own float64 logits (bins of expected count >= 5, the
+    tail merged), and the same counts must reject the untempered softmax(z)."""
+    from scipy import stats
+    # temperatures at which the own-token logit the random-init model echoes
+    # back does not swamp the row (a broad law, many chi-square bins)
+    if dtype == "f32":
+        c = W.config(1, sched="const", T0=1.5, T1=1.5)
+    else:
+        c = W.config(2, N=32, V=1024, d=256, Hq=2, Hkv=2, F=256, L=64, sched="const", T0=2.0, T1=2.0)
+    inp = W.make_inputs(c, seed=404)
+    den = D.Denoiser(c, inp, candidate_rule=B.DG_CANDIDATE_MULTINOMIAL)
+    N, V, T = c["N"], c["V"], c["T0"]
+    den.init_canvas(W.canvas_seed(1), 9)
+    tok = den.canvas.tokens.clone()
+    K = 4000
+    draws = torch.empty((K, N), dtype=torch.int32, device="cuda")
+    for k in range(K):
+        den.canvas.tokens.copy_(tok)
+        den.canvas.s.step, den.canvas.s.has_prev = k, 0
+        den.step(T, c["gamma"])
+        draws[k].copy_(den.canvas.argmax)
+    torch.cuda.synchronize()
+    d_np = draws.cpu().numpy()
+    om = oracle.model_from_inputs(inp)
+    kc, vc = oracle_cache(inp)
+    o = om.denoise_forward(tok.cpu().numpy(), None, kc, vc, c["L"], T)
+    o1 = om.denoise_forward(tok.cpu().numpy(), None, kc, vc, c["L"], 1.0)
+
+    def chi2(probs):
+        x2, dof = 0.0, 0
+        for i in range(N):
+            cnt = np.bincount(d_np[:, i], minlength=V).astype(np.float64)
+            e = K * probs[i]
+            order = np.argsort(-e)
+            big = order[e[order] >= 5.0]
+            rest = np.setdiff1d(np.arange(V), big)
+            obs = list(cnt[big]) + ([cnt[rest].sum()] if rest.size else [])
+            exp = list(e[big]) + ([e[rest].sum()] if rest.size else [])
+            obs, exp = np.array(obs), np.array(exp)
+            if exp.size < 2:
+                continue
+            x2 += float(((obs - exp) ** 2 / np.maximum(exp, 1e-300)).sum())
+            dof += exp.size - 1
+        return x2, dof
+
+    x2, dof = chi2(o["probs"])
+    p_val = stats.chi2.sf(x2, dof)
+    assert p_val > 1e-4, (x2, dof, p_val)
+    x2w, dofw = chi2(o1["probs"])
+    assert stats.chi2.sf(x2w, dofw) < 1e-6, (x2w, dofw)
+    # the draw differs from the argmax often: it is a draw
+    assert (d_np != o["argmax"][None, :]).mean() > 0.2
+    print(dtype, "chi2", x2, "dof", dof, "p", p_val)
+
+
+def test_nan_weights_never_accepted_or_stop():
+    """A NaN in the self-conditioning FFN's output weights (w_sc2): the first
+    step is unaffected; from the first self-conditioned step every entropy is
+    NaN, and then no position is accepted (every one is re-noised), none
+    counts as confident, the stability counter stays 0 under both rules and
+    the adaptive stop never fires; the decisions replay bit-exactly."""
+    for srule in (B.DG_STABLE_PREDICTIONS, B.DG_STABLE_CANVAS):
+        c = W.config(2, N=64, V=4096, d=512, Hq=4, Hkv=4, F=512, L=64, stable_rule=srule)
+        inp = W.make_inputs(c, seed=31)
+        inp["w2"] = inp["w2"].clone()
+        inp["w2"][3, 7] = float("nan")
+        den = D.Denoiser(c, inp)
+        N = c["N"]
+        den.init_canvas(5, 0)
+        stable = 0
+        for s in range(4):
+            tok = den.canvas.tokens.cpu().numpy()
+            den.step(1.0, 1e6)
+            torch.cuda.synchronize()
+            H = den.canvas.entropy.cpu().numpy()
+            fl = replay_select(den, tok, stable, s, 1e6, 0)
+            stable = fl["stable"]
+            halt, st = den.should_stop(1)
+            if s == 0:
+                assert np.isfinite(H).all() and st.accepted == N
+                continue
+            assert np.isnan(H).all()
+            assert st.accepted == 0 and st.allconf == 0 and st.stable == 0 and not halt
+            assert int(den.canvas.status[B.DG_ST_NAN]) == N
+            expect = [oracle.uniform_token(5, i, s, 0, 1, c["V"]) for i in range(N)]
+            np.testing.assert_array_equal(den.canvas.tokens.cpu().numpy(), expect)

@@ -26,10 +26,11 @@ DG_ACCEPT_SUM_MINUS_MAX, DG_ACCEPT_CUMSUM = 0, 1
 DG_CANDIDATE_ARGMAX, DG_CANDIDATE_MULTINOMIAL = 0, 1
 DG_SAMPLER_UNIFORM, DG_SAMPLER_MASKED = 0, 1
 DG_TABLE_BF16, DG_TABLE_FP8 = 0, 1
+DG_STABLE_PREDICTIONS, DG_STABLE_CANVAS = 0, 1
 DG_STATUS_WORDS = 16
 DG_MAX_BATCH = 16
 (DG_ST_ALLCONF, DG_ST_CHANGED, DG_ST_STABLE, DG_ST_ACCEPTED, DG_ST_NAN, DG_ST_STEP, DG_ST_HMIN,
- DG_ST_HMAX, DG_ST_HMEAN, DG_ST_MASKED) = range(10)
+ DG_ST_HMAX, DG_ST_HMEAN, DG_ST_MASKED, DG_ST_PRED_CHANGED) = range(11)
 TILE_V = 64  # vocabulary columns per softmax-statistics tile
 
 
@@ -37,7 +38,7 @@ class dg_config(ctypes.Structure):
     _fields_ = [("canvas_len", c_i32), ("vocab", c_i32), ("d_model", c_i32), ("n_q_heads", c_i32),
                 ("n_kv_heads", c_i32), ("head_dim", c_i32), ("ffn_hidden", c_i32), ("dtype", c_i32),
                 ("rms_eps", c_f32), ("conf_eps", c_f32), ("accept_rule", c_i32), ("candidate_rule", c_i32),
-                ("sampler", c_i32), ("table_format", c_i32), ("table_exp", c_i32)]
+                ("sampler", c_i32), ("table_format", c_i32), ("table_exp", c_i32), ("stable_rule", c_i32)]
 
 
 class dg_weights(ctypes.Structure):
@@ -90,6 +91,7 @@ SIGNATURES = {
     "dg_test_set_logits_dump": (None, [c_i32]),
     "dg_test_logits_ws_bytes": (c_sz, [P(dg_config)]),
     "dg_test_selfcond": (c_i32, [P(dg_config), P(dg_weights), vp, vp, vp, c_sz, vp]),
+    "dg_test_selfcond_canvas": (c_i32, [P(dg_config), P(dg_weights), P(dg_canvas), vp, vp, c_sz, vp]),
     "dg_test_select": (c_i32, [P(dg_config), P(dg_canvas), c_f32, vp]),
     "dg_test_philox": (c_i32, [vp, c_u32, c_u32, vp, c_i32, vp]),
     "dg_test_gumbel": (c_i32, [vp, c_i32, c_i32, vp, vp]),
@@ -256,6 +258,13 @@ def dg_test_selfcond(cfg: dg_config, w: dg_weights, Pm: torch.Tensor, S: torch.T
         ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def dg_test_selfcond_canvas(cfg: dg_config, w: dg_weights, canvas: dg_canvas, S: torch.Tensor,
+                            ws: torch.Tensor, stream=None) -> None:
+    _check("dg_test_selfcond_canvas", lib().dg_test_selfcond_canvas(
+        ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(canvas), _ptr(S), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def dg_test_select(cfg: dg_config, canvas: dg_canvas, accept_threshold_nats: float,
                    stream=None) -> None:
     _check("dg_test_select", lib().dg_test_select(ctypes.byref(cfg), ctypes.byref(canvas),
@@ -293,14 +302,30 @@ def dg_profile_read():
 # ---------------------------------------------------------------------------
 def make_config(c: dict, accept_rule: int = DG_ACCEPT_SUM_MINUS_MAX,
                 conf_eps: float = 0.005, candidate_rule: int = DG_CANDIDATE_ARGMAX,
-                sampler: int = DG_SAMPLER_UNIFORM) -> dg_config:
+                sampler: int = DG_SAMPLER_UNIFORM, stable_rule: int = DG_STABLE_PREDICTIONS) -> dg_config:
     """The C config of a workload dict; c["table"] == "fp8" selects the fp8
-    packed table with scale exponent c["table_exp"]."""
+    packed table with scale exponent c["table_exp"]; c["stable_rule"], when
+    present, overrides stable_rule."""
     fp8 = c.get("table") == "fp8"
     return dg_config(c["N"], c["V"], c["d"], c["Hq"], c["Hkv"], c["hd"], c["F"],
                      DG_BF16 if c["dtype"] == "bf16" else DG_F32, c.get("rms_eps", 1e-6),
                      conf_eps, accept_rule, candidate_rule, sampler,
-                     DG_TABLE_FP8 if fp8 else DG_TABLE_BF16, c.get("table_exp", 0) if fp8 else 0)
+                     DG_TABLE_FP8 if fp8 else DG_TABLE_BF16, c.get("table_exp", 0) if fp8 else 0,
+                     c.get("stable_rule", stable_rule))
+
+
+def stats_offsets(cfg: dg_config) -> dict:
+    """Byte offsets inside a canvas's `stats` buffer (the library's layout):
+    float4 tile statistics [N][V/64], float tile factors [N][V/64] (fp32
+    path), float2 top [N], float row factor [N], int32 previous predictions
+    [N], then, 256-byte aligned, uint8 tile exponents [V/64][256]."""
+    N, nt = cfg.canvas_len, cfg.vocab // TILE_V
+    o = dict(tstats=0, tscale=N * nt * 16)
+    o["top"] = o["tscale"] + N * nt * 4
+    o["rscale"] = o["top"] + N * 8
+    o["pred"] = o["rscale"] + N * 4
+    o["shift"] = (o["pred"] + N * 4 + 255) // 256 * 256
+    return o
 
 
 def torch_dtype(cfg: dg_config):
@@ -382,6 +407,7 @@ class DeviceCanvas:
         self.argmax = torch.zeros(N, dtype=torch.int32, device=device)
         self.accept = torch.zeros(N, dtype=torch.uint8, device=device)
         self.status = torch.zeros(DG_STATUS_WORDS, dtype=torch.int32, device=device)
+        self.replay_pred = None  # host-side note of the tests' decision replay
         self.s = dg_canvas(self.tokens.data_ptr(), self.probs.data_ptr(), self.stats.data_ptr(),
                            self.entropy.data_ptr(), self.argmax.data_ptr(),
                            self.accept.data_ptr(), self.status.data_ptr(), 0, 0, 0, 0)
@@ -399,13 +425,29 @@ class DeviceCanvas:
         the stored values into probabilities.  bf16: 2^-exponent x the row
         factor (the library keeps those two, not the product)."""
         N, nt = cfg.canvas_len, cfg.vocab // TILE_V
+        o = stats_offsets(cfg)
         if cfg.dtype == DG_BF16:
-            head = N * (nt * 20 + 8)
-            g = self.stats[head:head + N * 4].view(torch.float32)
-            base = (head + N * 4 + 255) // 256 * 256
-            e = self.stats[base:base + nt * 256].view(nt, 256)[:, :N].t().float()
+            g = self.stats[o["rscale"]:o["rscale"] + N * 4].view(torch.float32)
+            e = self.exponents(cfg).t().float()
             return torch.exp2(-e) * g.unsqueeze(1)
-        return self.stats[N * nt * 16:N * nt * 20].view(torch.float32).view(N, nt)
+        return self.stats[o["tscale"]:o["top"]].view(torch.float32).view(N, nt)
+
+    def exponents(self, cfg: dg_config) -> torch.Tensor:
+        """bf16 path: the per-(tile, row) power-of-two exponents R - r_t
+        (uint8 [V/64][N]) the next step's contraction applies."""
+        N, nt = cfg.canvas_len, cfg.vocab // TILE_V
+        base = stats_offsets(cfg)["shift"]
+        return self.stats[base:base + nt * 256].view(nt, 256)[:, :N]
+
+    def predictions(self, cfg: dg_config) -> torch.Tensor:
+        """The step's predictions (each position's most likely token), int32 [N]."""
+        return self.top(cfg)[0]
+
+    def pred_prev(self, cfg: dg_config) -> torch.Tensor:
+        """The predictions the stability test compares against (int32 [N],
+        rewritten by every step's selection)."""
+        o = stats_offsets(cfg)
+        return self.stats[o["pred"]:o["pred"] + cfg.canvas_len * 4].view(torch.int32)
 
     def tile_stats(self, cfg: dg_config):
         """The last step's per-(row, 64-column tile) statistics as stored:
@@ -426,8 +468,9 @@ class DeviceCanvas:
 
     def top(self, cfg: dg_config):
         """Each row's dominant token and its exact probability (last step)."""
-        N, nt = cfg.canvas_len, cfg.vocab // TILE_V
-        t = self.stats[N * nt * 20:N * nt * 20 + N * 8].view(torch.float32).view(N, 2)
+        N = cfg.canvas_len
+        o = stats_offsets(cfg)["top"]
+        t = self.stats[o:o + N * 8].view(torch.float32).view(N, 2)
         return t[:, 0].contiguous().view(torch.int32), t[:, 1].contiguous()
 
 

@@ -30,15 +30,27 @@ int ilog2(int64_t v) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 size_t dsize(const dg_config *c) { return c->dtype == DG_BF16 ? 2 : 4; }
 
+// The integer a caller stored in an enum-typed field of the ABI.  A C caller
+// may store any int there; reading it through the enum type would be
+// undefined for values outside the enum's range, so the bytes are copied.
+template <typename E>
+int32_t enum_value(const E &e) {
+  static_assert(sizeof(E) == sizeof(int32_t), "ABI enums are 32-bit");
+  int32_t v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+bool in_range(int32_t v, int32_t lo, int32_t hi) { return v >= lo && v <= hi; }
+
 dg_status check_config(const dg_config *c) {
   if (!c) return DG_ERR_INVALID_ARG;
-  if (c->dtype != DG_F32 && c->dtype != DG_BF16) return DG_ERR_INVALID_ARG;
-  if (c->accept_rule != DG_ACCEPT_SUM_MINUS_MAX && c->accept_rule != DG_ACCEPT_CUMSUM)
+  if (!in_range(enum_value(c->dtype), DG_F32, DG_BF16) ||
+      !in_range(enum_value(c->accept_rule), DG_ACCEPT_SUM_MINUS_MAX, DG_ACCEPT_CUMSUM) ||
+      !in_range(enum_value(c->candidate_rule), DG_CANDIDATE_ARGMAX, DG_CANDIDATE_MULTINOMIAL) ||
+      !in_range(enum_value(c->sampler), DG_SAMPLER_UNIFORM, DG_SAMPLER_MASKED) ||
+      !in_range(enum_value(c->table_format), DG_TABLE_BF16, DG_TABLE_FP8) ||
+      !in_range(enum_value(c->stable_rule), DG_STABLE_PREDICTIONS, DG_STABLE_CANVAS))
     return DG_ERR_INVALID_ARG;
-  if (c->candidate_rule != DG_CANDIDATE_ARGMAX && c->candidate_rule != DG_CANDIDATE_MULTINOMIAL)
-    return DG_ERR_INVALID_ARG;
-  if (c->sampler != DG_SAMPLER_UNIFORM && c->sampler != DG_SAMPLER_MASKED) return DG_ERR_INVALID_ARG;
-  if (c->table_format != DG_TABLE_BF16 && c->table_format != DG_TABLE_FP8) return DG_ERR_INVALID_ARG;
   if (c->table_format == DG_TABLE_FP8 && (c->table_exp < -32 || c->table_exp > 32)) return DG_ERR_INVALID_ARG;
   if (c->canvas_len < 1 || c->vocab < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
       c->head_dim < 1 || c->ffn_hidden < 1)
@@ -90,10 +102,11 @@ int selfcond_ksplit(const dg_config *c) {
 }
 
 // The canvas `stats` buffer: float4 tile statistics [N][V/64], float
-// tile_scale [N][V/64], float2 top [N], float row_scale [N], then (256-byte
+// tile_scale [N][V/64], float2 top [N], float row_scale [N], int32 pred [N]
+// (the last step's predictions, for the stability test), then (256-byte
 // aligned) the uint8 tile exponents [V/64][256].
 struct StatsLayout {
-  size_t tstats, tscale, top, rscale, shift, total;
+  size_t tstats, tscale, top, rscale, pred, shift, total;
 };
 StatsLayout stats_layout(const dg_config *c) {
   StatsLayout S{};
@@ -102,7 +115,8 @@ StatsLayout stats_layout(const dg_config *c) {
   S.tscale = N * nt * sizeof(float4);
   S.top = S.tscale + N * nt * sizeof(float);
   S.rscale = S.top + N * sizeof(float2);
-  S.shift = align256(S.rscale + N * sizeof(float));
+  S.pred = S.rscale + N * sizeof(float);
+  S.shift = align256(S.pred + N * sizeof(int32_t));
   S.total = S.shift + nt * 256;
   return S;
 }
@@ -181,7 +195,7 @@ Layout layout(const dg_config *c, int32_t nprefill, bool with_logits, int nb = 1
   return L;
 }
 
-bool g_logits_dump = false;
+std::atomic<bool> g_logits_dump{false};
 
 // profiling (events around the two E-streaming contractions)
 std::mutex g_prof_mu;
@@ -345,8 +359,8 @@ extern "C" {
 
 int32_t dg_abi_version(void) { return DG_ABI_VERSION; }
 
-const char *dg_status_string(dg_status s) {
-  switch (s) {
+const char *dg_status_string(dg_status status) {
+  switch (enum_value(status)) {
     case DG_OK: return "ok";
     case DG_ERR_INVALID_ARG: return "invalid argument";
     case DG_ERR_UNSUPPORTED: return "unsupported shape or configuration";
@@ -683,8 +697,10 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     sel.canvas_id[0] = cv->canvas_id;
     sel.step[0] = (uint32_t)cv->step;
     sel.host_status[0] = host_status;
+    sel.pred[0] = top;
+    sel.pred_prev[0] = reinterpret_cast<int32_t *>(stats + SL.pred);
     DG_TRY(dg::select_step_batch(sel, 1, N, ilog2(V), (double)gamma, (int)cfg->accept_rule, cfg->conf_eps,
-                                 mask_id(cfg), s));
+                                 mask_id(cfg), (int)cfg->stable_rule, s));
   }
   cv->step += 1;
   cv->has_prev = 1;
@@ -833,6 +849,8 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
       sel.seed[b] = cv->seed;
       sel.canvas_id[b] = cv->canvas_id;
       sel.step[b] = (uint32_t)cv->step;
+      sel.pred[b] = reinterpret_cast<const float2 *>(st_of(b, SL.top));
+      sel.pred_prev[b] = reinterpret_cast<int32_t *>(st_of(b, SL.pred));
     }
     DG_TRY(dg::row_combine_batch(rc, B, N, ntiles, inv_T, nrm, Eb, d, s));
     if (cfg->candidate_rule == DG_CANDIDATE_MULTINOMIAL)
@@ -843,7 +861,7 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
         DG_TRY(dg::multinomial_draw(rc.stats[b], N, ntiles, inv_T, draw, cv->argmax, s));
       }
     DG_TRY(dg::select_step_batch(sel, B, N, ilog2(V), (double)gamma, (int)cfg->accept_rule, cfg->conf_eps,
-                                 mask_id(cfg), s));
+                                 mask_id(cfg), (int)cfg->stable_rule, s));
   }
   for (int b = 0; b < B; ++b) {
     cvs[b].step += 1;
@@ -854,7 +872,8 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
 
 dg_status dg_denoise_step(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache, dg_canvas *cv,
                           float temperature, float accept_threshold_nats, void *ws, size_t ws_bytes, void *stream) {
-  return denoise_impl(cfg, w, cache, cv, temperature, accept_threshold_nats, ws, ws_bytes, stream, g_logits_dump);
+  return denoise_impl(cfg, w, cache, cv, temperature, accept_threshold_nats, ws, ws_bytes, stream,
+                      g_logits_dump.load());
 }
 
 // The batch's stacked layout; at least the single step's (the fp32 path steps
@@ -942,7 +961,8 @@ dg_status dg_run_canvas(const dg_config *cfg, const dg_weights *w, const dg_kv_c
   for (int32_t i = 0; i < max_steps; ++i)
     if (!(std::isfinite(temps[i]) && temps[i] > 0.f)) return DG_ERR_INVALID_ARG;
   if (std::isnan(accept_threshold_nats) || accept_threshold_nats < 0.f) return DG_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < layout(cfg, 0, g_logits_dump && cfg->dtype == DG_BF16).total) return DG_ERR_WORKSPACE;
+  const bool dump = g_logits_dump.load();
+  if (!ws || ws_bytes < layout(cfg, 0, dump && cfg->dtype == DG_BF16).total) return DG_ERR_WORKSPACE;
   // Host-visible copy of the status words, one per host thread (kept for the
   // process): coherent pinned memory that the selection kernel writes
   // directly, the step word last, so the host learns a step's outcome without
@@ -977,15 +997,15 @@ dg_status dg_run_canvas(const dg_config *cfg, const dg_weights *w, const dg_kv_c
   for (int32_t i = 0; i < max_steps; ++i) {
     const int32_t step_index = cv->step;
     if (adaptive_stop) reinterpret_cast<volatile int32_t *>(host_words)[DG_ST_STEP] = -1;
-    st = denoise_impl(cfg, w, cache, cv, temps[i], accept_threshold_nats, ws, ws_bytes, stream, g_logits_dump,
+    st = denoise_impl(cfg, w, cache, cv, temps[i], accept_threshold_nats, ws, ws_bytes, stream, dump,
                       ahead ? SC_DONE : SC_INLINE, 0, adaptive_stop ? host_words_dev : nullptr);
     if (st != DG_OK) return st;
     *steps_run = i + 1;
     if (adaptive_stop) {
       ahead = ahead_ok && i + 1 < max_steps;
       if (ahead) {
-        st = denoise_impl(cfg, w, cache, cv, temps[i + 1], accept_threshold_nats, ws, ws_bytes, stream,
-                          g_logits_dump, SC_AHEAD, stable_steps);
+        st = denoise_impl(cfg, w, cache, cv, temps[i + 1], accept_threshold_nats, ws, ws_bytes, stream, dump,
+                          SC_AHEAD, stable_steps);
         if (st != DG_OK) return st;
       }
       // wait for the step word; every 4096 polls make sure the stream is
@@ -1029,11 +1049,35 @@ dg_status dg_test_ws_offsets(const dg_config *cfg, dg_ws_offsets *out) {
   return DG_OK;
 }
 
-void dg_test_set_logits_dump(int32_t on) { g_logits_dump = on != 0; }
+void dg_test_set_logits_dump(int32_t on) { g_logits_dump.store(on != 0); }
 
 size_t dg_test_logits_ws_bytes(const dg_config *cfg) {
   if (check_config(cfg) != DG_OK) return 0;
   return layout(cfg, 0, true).total;
+}
+
+// The step's self-conditioning vector S = p E as dg_denoise_step computes
+// it (bf16: the production contraction with per-tile exponents, then the
+// merge with the row factor and the dominant-token correction; f32: the
+// fp32 GEMM).  probs, shift, rscale, top as in the canvas state; S fp32.
+static hipError_t selfcond_vector(const dg_config *cfg, const dg_weights *w, const void *probs, const uint8_t *shift,
+                                  const float *rscale, const float2 *top, float *S, float *part, hipStream_t s) {
+  const int N = cfg->canvas_len, V = cfg->vocab, d = cfg->d_model;
+  if (cfg->dtype == DG_BF16) {
+    const int ks = selfcond_ksplit(cfg);
+    const TableRef tt = table_ref(cfg, w, true);
+    dg::EsCanvasesIn cin{};
+    cin.probs[0] = static_cast<const uint16_t *>(probs);
+    cin.shift[0] = shift;
+    hipError_t e = dg::selfcond_bf16_batch(cin, 1, tt.bf, N, d, V, true, part, ks, s, dg::SelfcondGuard{nullptr, 0},
+                                           tt.q8, tt.scale);
+    if (e != hipSuccess) return e;
+    return dg::selfcond_reduce(part, ks, N, d, top, static_cast<const uint16_t *>(probs), V, rscale, shift,
+                               static_cast<const uint16_t *>(w->E), S, nullptr, s);
+  }
+  dg::GemmShapeF32 g{static_cast<const float *>(probs), V, 1, static_cast<const float *>(w->E), 1, d, N, d, V,
+                     nullptr, 0};
+  return dg::gemm_f32(g, epi_store(S, true, d, d, 0), s);
 }
 
 dg_status dg_test_selfcond(const dg_config *cfg, const dg_weights *w, const void *P, void *S, void *ws,
@@ -1041,25 +1085,35 @@ dg_status dg_test_selfcond(const dg_config *cfg, const dg_weights *w, const void
   dg_status st = check_config(cfg);
   if (st != DG_OK) return st;
   if (!weights_ok(cfg, w) || !P || !S) return DG_ERR_INVALID_ARG;
-  const Layout L = layout(cfg, 0, false);
+  const Layout L = layout(cfg, 0, true);  // the dump layout: room for zero exponents
   if (!ws || ws_bytes < L.total) return DG_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int N = cfg->canvas_len, V = cfg->vocab, d = cfg->d_model;
-  if (cfg->dtype == DG_BF16) {
-    const int ks = selfcond_ksplit(cfg);
-    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + L.sc_part);
-    const TableRef tt = table_ref(cfg, w, true);
-    dg::EsCanvasesIn cin{};
-    cin.probs[0] = static_cast<const uint16_t *>(P);
-    DG_TRY(dg::selfcond_bf16_batch(cin, 1, tt.bf, N, d, V, false, part, ks, s, dg::SelfcondGuard{nullptr, 0}, tt.q8,
-                                   tt.scale));
-    DG_TRY(dg::selfcond_reduce(part, ks, N, d, nullptr, nullptr, V, nullptr, nullptr, nullptr, static_cast<float *>(S),
-                               nullptr, s));
-  } else {
-    dg::GemmShapeF32 g{static_cast<const float *>(P), V, 1, static_cast<const float *>(w->E), 1, d, N, d, V,
-                       nullptr, 0};
-    DG_TRY(dg::gemm_f32(g, epi_store(S, true, d, d, 0), s));
+  char *base = static_cast<char *>(ws);
+  uint8_t *zero_shift = nullptr;
+  if (cfg->dtype == DG_BF16) {  // exponents 0 (plain probabilities) in the logits region
+    zero_shift = reinterpret_cast<uint8_t *>(base + L.logits);
+    DG_TRY(hipMemsetAsync(zero_shift, 0, (size_t)(cfg->vocab / kTile) * 256, s));
   }
+  DG_TRY(selfcond_vector(cfg, w, P, zero_shift, nullptr, nullptr, static_cast<float *>(S),
+                         reinterpret_cast<float *>(base + L.sc_part), s));
+  return DG_OK;
+}
+
+dg_status dg_test_selfcond_canvas(const dg_config *cfg, const dg_weights *w, const dg_canvas *cv, void *S, void *ws,
+                                  size_t ws_bytes, void *stream) {
+  dg_status st = check_config(cfg);
+  if (st != DG_OK) return st;
+  if (!weights_ok(cfg, w) || !canvas_ok(cv) || !S) return DG_ERR_INVALID_ARG;
+  const Layout L = layout(cfg, 0, false);
+  if (!ws || ws_bytes < L.total) return DG_ERR_WORKSPACE;
+  const StatsLayout SL = stats_layout(cfg);
+  const char *stats = static_cast<const char *>(cv->stats);
+  const bool bf = cfg->dtype == DG_BF16;
+  DG_TRY(selfcond_vector(cfg, w, cv->probs, bf ? reinterpret_cast<const uint8_t *>(stats + SL.shift) : nullptr,
+                         bf ? reinterpret_cast<const float *>(stats + SL.rscale) : nullptr,
+                         bf ? reinterpret_cast<const float2 *>(stats + SL.top) : nullptr, static_cast<float *>(S),
+                         reinterpret_cast<float *>(static_cast<char *>(ws) + L.sc_part),
+                         static_cast<hipStream_t>(stream)));
   return DG_OK;
 }
 
@@ -1076,8 +1130,12 @@ dg_status dg_test_select(const dg_config *cfg, dg_canvas *cv, float gamma, void 
   sel.seed[0] = cv->seed;
   sel.canvas_id[0] = cv->canvas_id;
   sel.step[0] = (uint32_t)cv->step;
+  const StatsLayout SL = stats_layout(cfg);
+  sel.pred[0] = reinterpret_cast<const float2 *>(static_cast<char *>(cv->stats) + SL.top);
+  sel.pred_prev[0] = reinterpret_cast<int32_t *>(static_cast<char *>(cv->stats) + SL.pred);
   DG_TRY(dg::select_step_batch(sel, 1, cfg->canvas_len, ilog2(cfg->vocab), (double)gamma, (int)cfg->accept_rule,
-                               cfg->conf_eps, mask_id(cfg), static_cast<hipStream_t>(stream)));
+                               cfg->conf_eps, mask_id(cfg), (int)cfg->stable_rule,
+                               static_cast<hipStream_t>(stream)));
   return DG_OK;
 }
 

@@ -5,11 +5,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "dgdenoise.h"
 
 namespace dg {
 
 typedef uint16_t bf16;  // raw bfloat16 bits
+
+// One-time per-device set-up of a launcher (raising a kernel's dynamic LDS
+// limit): `done` keeps one bit per device; set_up() is idempotent, so two
+// host threads that race on the first launch both run it, harmlessly.
+template <typename F>
+hipError_t once_per_device(std::atomic<uint64_t> &done, F &&set_up) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const uint64_t bit = uint64_t(1) << dev;
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  const hipError_t err = set_up();
+  if (err == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  return err;
+}
 
 // Epilogue of the dense GEMMs: how an output element (row, col) is stored.
 //   index(row, col) = row * rstride + (col / cdiv) * chi + (col % cdiv)
@@ -291,9 +307,14 @@ struct SelectBatch {
   // nullable: a copy of the status words in host-visible memory, the step
   // word written last (after a system-scope fence)
   int32_t *host_status[ES_MAX_BATCH];
+  // the step's predictions (the row combine's top tokens, as int bits of
+  // .x) and the previous step's, which the kernel replaces (int32 [N])
+  const float2 *pred[ES_MAX_BATCH];
+  int32_t *pred_prev[ES_MAX_BATCH];
 };
+// stable_rule: dg_stable_rule (what DG_ST_STABLE counts).
 hipError_t select_step_batch(const SelectBatch &bt, int B, int N, int log2v, double gamma, int rule,
-                             float conf_eps, int mask_id, hipStream_t s);
+                             float conf_eps, int mask_id, int stable_rule, hipStream_t s);
 hipError_t philox_test(const uint32_t *ctr, uint32_t k0, uint32_t k1, uint32_t *out, int n,
                        hipStream_t s);
 

@@ -355,17 +355,19 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
                               const uint8_t *E8_tiled, float e8_scale) {
   if (B < 1 || B > ES_MAX_BATCH || N < 1 || N > ES_BM || K % ES_BK || V % ES_BN) return hipErrorInvalidValue;
   if (!E_tiled == !E8_tiled) return hipErrorInvalidValue;  // exactly one table form
-  static bool attr = false;
-  if (!attr) {
-    const void *fns[4] = {reinterpret_cast<const void *>(lm_head_es_kernel<false, false>),
-                          reinterpret_cast<const void *>(lm_head_es_kernel<true, false>),
-                          reinterpret_cast<const void *>(lm_head_es_kernel<false, true>),
-                          reinterpret_cast<const void *>(lm_head_es_kernel<true, true>)};
-    for (const void *f : fns)
-      if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess)
-        return hipErrorInvalidValue;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr{0};
+  if (once_per_device(attr, [] {
+        const void *fns[4] = {reinterpret_cast<const void *>(lm_head_es_kernel<false, false>),
+                              reinterpret_cast<const void *>(lm_head_es_kernel<true, false>),
+                              reinterpret_cast<const void *>(lm_head_es_kernel<false, true>),
+                              reinterpret_cast<const void *>(lm_head_es_kernel<true, true>)};
+        for (const void *f : fns) {
+          const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes());
+          if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+      }) != hipSuccess)
+    return hipErrorInvalidValue;
   const int M = B * N, nblk = (M + ES_BM - 1) / ES_BM;
   const int items = (V / ES_BN) * nblk;
   const dim3 grid(B == 1 ? items : (items + 7) / 8 * 8);
@@ -461,19 +463,21 @@ hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *E
   if (B < 1 || B > ES_MAX_BATCH || M > ES_BM || K % 64 || N % 4 || ksplit < 1 || ksplit > K / ES_BK)
     return hipErrorInvalidValue;
   if (!Et_tiled == !Et8_tiled) return hipErrorInvalidValue;  // exactly one table form
-  static bool attr = false;
-  if (!attr) {
+  static std::atomic<uint64_t> attr{0};
+  if (once_per_device(attr, [] {
 #define DG_SC_FN(SC, MD, Q8) reinterpret_cast<const void *>(selfcond_es_kernel<SC, MD, Q8>)
-    const void *fns[12] = {DG_SC_FN(false, 0, false), DG_SC_FN(true, 0, false), DG_SC_FN(false, 1, false),
-                           DG_SC_FN(true, 1, false),  DG_SC_FN(false, 2, false), DG_SC_FN(true, 2, false),
-                           DG_SC_FN(false, 0, true),  DG_SC_FN(true, 0, true),  DG_SC_FN(false, 1, true),
-                           DG_SC_FN(true, 1, true),   DG_SC_FN(false, 2, true), DG_SC_FN(true, 2, true)};
+        const void *fns[12] = {DG_SC_FN(false, 0, false), DG_SC_FN(true, 0, false), DG_SC_FN(false, 1, false),
+                               DG_SC_FN(true, 1, false),  DG_SC_FN(false, 2, false), DG_SC_FN(true, 2, false),
+                               DG_SC_FN(false, 0, true),  DG_SC_FN(true, 0, true),  DG_SC_FN(false, 1, true),
+                               DG_SC_FN(true, 1, true),   DG_SC_FN(false, 2, true), DG_SC_FN(true, 2, true)};
 #undef DG_SC_FN
-    for (const void *f : fns)
-      if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes()) != hipSuccess)
-        return hipErrorInvalidValue;
-    attr = true;
-  }
+        for (const void *f : fns) {
+          const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes());
+          if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+      }) != hipSuccess)
+    return hipErrorInvalidValue;
   const int mode = B == 1 ? 0 : (M <= ES_BM / 2 ? 2 : 1);
   const int ntn = (N + ES_BN - 1) / ES_BN;
   const int items = ntn * ksplit * (mode == 2 ? (B + 1) / 2 : B);

@@ -387,13 +387,12 @@ hipError_t gemm_split_launch(const SplitGemm &g, hipStream_t s, bool partials_on
   if (g.ksplit < 1 || (g.ksplit > 1 && !g.part) || g.K % PG_BK) return hipErrorInvalidValue;
   for (int i = 0; i < g.count; ++i)
     if (g.N[i] % 4) return hipErrorInvalidValue;
-  static bool attr = false;
-  if (!attr) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_split_kernel<BM, BN, STAGES>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS) != hipSuccess)
-      return hipErrorInvalidValue;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr{0};
+  if (once_per_device(attr, [] {
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_split_kernel<BM, BN, STAGES>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+      }) != hipSuccess)
+    return hipErrorInvalidValue;
   int maxN = 0, P = 0;
   for (int i = 0; i < g.count; ++i) {
     maxN = g.N[i] > maxN ? g.N[i] : maxN;

@@ -8,6 +8,9 @@
 // within the threshold, and the first failure ends the walk.  [P5] states
 // the plain running sum (rule CUMSUM).  Every rejected position is
 // re-noised with a fresh uniform token; accepted ones take the candidate.
+// [P3] §5.3 / [P5] adaptive stop: the flags say whether every entropy is
+// below the confidence threshold and count the steps in a row whose
+// predictions (or, by the configured rule, the canvas) did not change.
 // Masked sampler ([P1] §1, [P3] §3.1): only positions holding [MASK] are
 // walked, rejected ones keep [MASK] and decided ones are never revisited.
 //
@@ -40,11 +43,15 @@ hipError_t canvas_init(int32_t *tokens, int32_t *status, int N, int log2v, uint6
   return hipGetLastError();
 }
 
+// pred: each position's prediction (the most likely token, as the int bits
+// of top[i].x); pred_prev: the previous step's, replaced by this step's.
 __device__ __forceinline__ void select_body(const float *__restrict__ entropy, const int32_t *__restrict__ argmax,
                                             int32_t *__restrict__ tokens, uint8_t *__restrict__ accept,
                                             int32_t *__restrict__ status, int N, int log2v, uint64_t limit,
                                             int rule, float conf_eps, uint64_t seed, uint32_t canvas_id,
-                                            uint32_t step, int mask_id, int32_t *host_status) {
+                                            uint32_t step, int mask_id, int32_t *host_status,
+                                            const float2 *__restrict__ pred, int32_t *__restrict__ pred_prev,
+                                            int stable_rule) {
   __shared__ __align__(16) uint64_t keys[256];
   __shared__ __align__(16) uint64_t fix[256];
   __shared__ float fmin_s[4], fmax_s[4], fsum_s[4];
@@ -91,10 +98,15 @@ __device__ __forceinline__ void select_body(const float *__restrict__ entropy, c
   const int acc_here = (finite && test <= limit) ? 1 : 0;
 
   // re-noise, new canvas, flags
-  int changed = 0, conf = 1, acc = 0, isnan_ = 0;
+  int changed = 0, conf = 1, acc = 0, isnan_ = 0, pchanged = 0;
   float hmin = INFINITY, hmax = -INFINITY, hsum = 0.f;
   int masked = 0;
   if (i < N) {
+    // [P3] §5.3 / [P5]: is this position's prediction the previous step's?
+    // (no previous step at step 0; a NaN entropy has no prediction to compare)
+    const int32_t p = __float_as_int(pred[i].x);
+    pchanged = step == 0u || p != pred_prev[i] || h != h;
+    pred_prev[i] = p;
     acc = acc_here;
     const int32_t t = acc ? argmax[i]
                           : (mask_id >= 0 ? old : uniform_token(seed, (uint32_t)i, step, canvas_id, 1u, log2v));
@@ -109,6 +121,7 @@ __device__ __forceinline__ void select_body(const float *__restrict__ entropy, c
     hsum = isnan_ ? 0.f : h;
   }
   const int any_changed = __syncthreads_or(changed);
+  const int any_pchanged = __syncthreads_or(pchanged);
   const int all_conf = __syncthreads_and(conf);
   const int n_acc = __syncthreads_count(acc);
   const int n_nan = __syncthreads_count(isnan_);
@@ -135,7 +148,8 @@ __device__ __forceinline__ void select_body(const float *__restrict__ entropy, c
     const int stable_old = status[DG_ST_STABLE];
     status[DG_ST_ALLCONF] = all_conf;
     status[DG_ST_CHANGED] = any_changed;
-    status[DG_ST_STABLE] = any_changed ? 0 : stable_old + 1;
+    status[DG_ST_PRED_CHANGED] = any_pchanged;
+    status[DG_ST_STABLE] = (stable_rule == DG_STABLE_CANVAS ? any_changed : any_pchanged) ? 0 : stable_old + 1;
     status[DG_ST_ACCEPTED] = n_acc;
     status[DG_ST_NAN] = n_nan;
     status[DG_ST_STEP] = (int32_t)step;
@@ -155,10 +169,11 @@ __device__ __forceinline__ void select_body(const float *__restrict__ entropy, c
 
 // One workgroup per canvas (a single canvas is a batch of one).
 __global__ void __launch_bounds__(256) select_batch_kernel(SelectBatch bt, int N, int log2v, uint64_t limit,
-                                                           int rule, float conf_eps, int mask_id) {
+                                                           int rule, float conf_eps, int mask_id, int stable_rule) {
   const int c = blockIdx.x;
   select_body(bt.entropy[c], bt.argmax[c], bt.tokens[c], bt.accept[c], bt.status[c], N, log2v, limit, rule,
-              conf_eps, bt.seed[c], bt.canvas_id[c], bt.step[c], mask_id, bt.host_status[c]);
+              conf_eps, bt.seed[c], bt.canvas_id[c], bt.step[c], mask_id, bt.host_status[c], bt.pred[c],
+              bt.pred_prev[c], stable_rule);
 }
 
 // gamma (nats) -> the 2^-32-nat fixed-point limit, saturating
@@ -172,10 +187,12 @@ static uint64_t select_limit(double gamma) {
 }
 
 hipError_t select_step_batch(const SelectBatch &bt, int B, int N, int log2v, double gamma, int rule,
-                             float conf_eps, int mask_id, hipStream_t s) {
+                             float conf_eps, int mask_id, int stable_rule, hipStream_t s) {
   if (B < 1 || B > ES_MAX_BATCH || N < 1 || N > 256) return hipErrorInvalidValue;
+  for (int c = 0; c < B; ++c)
+    if (!bt.pred[c] || !bt.pred_prev[c]) return hipErrorInvalidValue;
   hipLaunchKernelGGL(select_batch_kernel, dim3(B), dim3(256), 0, s, bt, N, log2v, select_limit(gamma), rule,
-                     conf_eps, mask_id);
+                     conf_eps, mask_id, stable_rule);
   return hipGetLastError();
 }
 
