@@ -316,6 +316,29 @@ dg_status dg_denoise_step(const dg_config *cfg, const dg_weights *w, const dg_kv
                           dg_canvas *canvas, float temperature, float accept_threshold_nats,
                           void *ws, size_t ws_bytes, void *stream);
 
+/* dg_denoise_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, semantics and kernels as dg_denoise_step,
+ * minus the workspace: the step's scratch is a device array inside the
+ * library, DG_STATIC_SCRATCH_BYTES (160 MiB) on every device the library
+ * is loaded on, held until the process ends.  The call allocates nothing
+ * (no hipMalloc, hipFree or event creation; the profiling switch and the
+ * logits dump do not apply to it).  The device current on the calling
+ * thread must be the device of `stream`; its array's address is looked up
+ * once per device, on the device's first call.
+ * Every call on one device shares that device's array, whose contents are
+ * whatever the last call left (the step needs none of it cleared): calls
+ * that overlap on one device -- other streams, other host threads -- race
+ * and must be ordered by the caller.
+ * Errors: as dg_denoise_step; DG_ERR_WORKSPACE when the configuration's
+ * dg_workspace_bytes(cfg, 0) exceeds DG_STATIC_SCRATCH_BYTES (checked
+ * before anything else runs); DG_ERR_HIP if the array's address cannot be
+ * obtained. */
+#define DG_STATIC_SCRATCH_BYTES ((size_t)160 << 20)
+dg_status dg_denoise_step_static(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache,
+                                 dg_canvas *canvas, float temperature, float accept_threshold_nats,
+                                 void *stream);
+
 /* Batched canvases.  [P5] (current limitations) notes that several users
  * cannot share one denoising pass the way autoregressive decoding shares a
  * batch: each user's canvas runs its own loop.  This call steps n_canvases

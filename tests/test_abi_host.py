@@ -166,6 +166,33 @@ def test_denoise_step_validation(lib):
     assert (cv.step, cv.has_prev) == (3, 1)
 
 
+def test_static_scratch_step_validation(lib):
+    """The entry point that allocates nothing rejects, before any device work:
+    a configuration whose scratch need exceeds the library's array, and every
+    argument error of dg_denoise_step."""
+    def call(cfg, w, cache, cv, T, g):
+        return B.lib().dg_denoise_step_static(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache),
+                                              ctypes.byref(cv), T, g, None)
+    cache = B.dg_kv_cache(FAKE, FAKE, 512, 512)
+    cv, w = fake_canvas(), fake_weights()
+    big = cfg_of(3, d=4096, F=65536)
+    assert B.dg_validate_config(big) == B.DG_OK
+    assert B.dg_workspace_bytes(big, 0) > B.DG_STATIC_SCRATCH_BYTES
+    assert call(big, w, cache, cv, 1.0, 8.0) == B.DG_ERR_WORKSPACE
+    for i in range(1, 6):   # the shipped configurations fit
+        assert B.dg_workspace_bytes(cfg_of(i), 0) <= B.DG_STATIC_SCRATCH_BYTES
+    cfg = cfg_of(2)
+    for T, g in [(0.0, 8.0), (float("nan"), 8.0), (1.0, -1.0), (1.0, float("nan"))]:
+        assert call(cfg, w, cache, cv, T, g) == B.DG_ERR_INVALID_ARG
+    cv2 = fake_canvas()
+    cv2.status = None
+    assert call(cfg, w, cache, cv2, 1.0, 8.0) == B.DG_ERR_INVALID_ARG
+    bad = cfg_of(2)
+    bad.canvas_len = 0
+    assert call(bad, w, cache, cv, 1.0, 8.0) == B.DG_ERR_INVALID_ARG
+    assert (cv.step, cv.has_prev) == (3, 1)
+
+
 def test_prefill_validation(lib):
     cfg = cfg_of(5)
     w = fake_weights()

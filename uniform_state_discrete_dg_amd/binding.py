@@ -81,6 +81,8 @@ SIGNATURES = {
                                   c_sz, vp]),
     "dg_denoise_step": (c_i32, [P(dg_config), P(dg_weights), P(dg_kv_cache), P(dg_canvas), c_f32,
                                 c_f32, vp, c_sz, vp]),
+    "dg_denoise_step_static": (c_i32, [P(dg_config), P(dg_weights), P(dg_kv_cache), P(dg_canvas), c_f32,
+                                       c_f32, vp]),
     "dg_workspace_bytes_batch": (c_sz, [P(dg_config), c_i32]),
     "dg_denoise_step_batch": (c_i32, [P(dg_config), P(dg_weights), P(dg_kv_cache), P(dg_canvas), c_i32,
                                       c_f32, c_f32, vp, c_sz, vp]),
@@ -191,6 +193,17 @@ def dg_denoise_step(cfg: dg_config, w: dg_weights, cache: dg_kv_cache, canvas: d
         ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), ctypes.byref(canvas),
         temperature, accept_threshold_nats, _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+DG_STATIC_SCRATCH_BYTES = 160 << 20
+
+
+def dg_denoise_step_static(cfg: dg_config, w: dg_weights, cache: dg_kv_cache, canvas: dg_canvas,
+                           temperature: float, accept_threshold_nats: float, stream=None) -> None:
+    """dg_denoise_step with the library's own device scratch (no workspace)."""
+    _check("dg_denoise_step_static", lib().dg_denoise_step_static(
+        ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(cache), ctypes.byref(canvas), temperature,
+        accept_threshold_nats, _stream(stream)))
 
 
 def dg_workspace_bytes_batch(cfg: dg_config, n_canvases: int) -> int:

@@ -220,8 +220,9 @@ struct ProfScope {
   std::vector<std::pair<hipEvent_t, hipEvent_t>> *vec = nullptr;
   hipEvent_t e0{}, e1{};
   hipStream_t s;
-  ProfScope(std::vector<std::pair<hipEvent_t, hipEvent_t>> &v, hipStream_t st) : s(st) {
-    if (!(g_prof_mask.load(std::memory_order_relaxed) & (&v == &g_prof_lm ? 1 : 2))) return;
+  // enabled = false: records nothing (the entry point that allocates nothing)
+  ProfScope(std::vector<std::pair<hipEvent_t, hipEvent_t>> &v, hipStream_t st, bool enabled = true) : s(st) {
+    if (!enabled || !(g_prof_mask.load(std::memory_order_relaxed) & (&v == &g_prof_lm ? 1 : 2))) return;
     if (!prof_take(&e0)) return;
     if (!prof_take(&e1)) {
       (void)hipEventDestroy(e0);
@@ -504,17 +505,25 @@ dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cac
 //   SC_DONE    it was launched ahead: launch the rest of the step.
 enum ScMode { SC_INLINE = 0, SC_AHEAD = 1, SC_DONE = 2 };
 
-static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache, dg_canvas *cv,
-                              float temperature, float gamma, void *ws, size_t ws_bytes, void *stream,
-                              bool logits_dump, ScMode sc_mode = SC_INLINE, int32_t stable_steps = 0,
-                              int32_t *host_status = nullptr) {
-  dg_status st = check_config(cfg);
+// The arguments of one step, short of the workspace.
+static dg_status check_step_args(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache,
+                                 const dg_canvas *cv, float temperature, float gamma) {
+  const dg_status st = check_config(cfg);
   if (st != DG_OK) return st;
   if (!weights_ok(cfg, w) || !cache || !cache->k || !cache->v || !canvas_ok(cv)) return DG_ERR_INVALID_ARG;
   if (cache->length < 0 || cache->length > cache->capacity) return DG_ERR_INVALID_ARG;
   if (!(std::isfinite(temperature) && temperature > 0.f)) return DG_ERR_INVALID_ARG;
   if (std::isnan(gamma) || gamma < 0.f) return DG_ERR_INVALID_ARG;
   if (cv->step < 0) return DG_ERR_INVALID_ARG;
+  return DG_OK;
+}
+
+static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache, dg_canvas *cv,
+                              float temperature, float gamma, void *ws, size_t ws_bytes, void *stream,
+                              bool logits_dump, ScMode sc_mode = SC_INLINE, int32_t stable_steps = 0,
+                              int32_t *host_status = nullptr, bool profile = true) {
+  const dg_status st = check_step_args(cfg, w, cache, cv, temperature, gamma);
+  if (st != DG_OK) return st;
   const bool bf = cfg->dtype == DG_BF16;
   const bool dump = logits_dump && bf;
   const Layout L = layout(cfg, 0, dump);
@@ -560,7 +569,7 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
       const int ks = selfcond_ksplit(cfg);
       float *part = reinterpret_cast<float *>(base + L.sc_part);
       if (sc_mode != SC_DONE) {
-        ProfScope ps(g_prof_sc, s);
+        ProfScope ps(g_prof_sc, s, profile);
         const dg::SelfcondGuard guard{sc_mode == SC_AHEAD ? cv->status : nullptr, stable_steps};
         const TableRef tt = table_ref(cfg, w, true);
         dg::EsCanvasesIn cin{};
@@ -649,7 +658,7 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
   float *logits = reinterpret_cast<float *>(base + L.logits);
   if (bf) {
     {
-      ProfScope ps(g_prof_lm, s);
+      ProfScope ps(g_prof_lm, s, profile);
       const TableRef te = table_ref(cfg, w, false);
       dg::EsCanvases ec{};
       ec.probs[0] = static_cast<uint16_t *>(cv->probs);
@@ -874,6 +883,49 @@ dg_status dg_denoise_step(const dg_config *cfg, const dg_weights *w, const dg_kv
                           float temperature, float accept_threshold_nats, void *ws, size_t ws_bytes, void *stream) {
   return denoise_impl(cfg, w, cache, cv, temperature, accept_threshold_nats, ws, ws_bytes, stream,
                       g_logits_dump.load());
+}
+
+// ---- the step without a caller workspace ---------------------------------------
+// For callers that cannot allocate (graph capture, tight serving loops,
+// harnesses that forbid hipMalloc): the step's scratch lives in this
+// file-scope device array, one copy per device the library is loaded on,
+// held until the process ends.  Host code never names the array itself (its
+// host-side symbol is a stand-in, not a device address): each device's
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and is what the kernels receive.
+static __device__ __align__(256) char scratch[DG_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (looked up on the device's first call).
+dg_status scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DG_ERR_HIP;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // idempotent: two threads racing here both get the same address
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DG_ERR_HIP;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return DG_OK;
+}
+}  // namespace
+
+dg_status dg_denoise_step_static(const dg_config *cfg, const dg_weights *w, const dg_kv_cache *cache, dg_canvas *cv,
+                                 float temperature, float accept_threshold_nats, void *stream) {
+  dg_status st = check_config(cfg);
+  if (st != DG_OK) return st;
+  if (layout(cfg, 0, false).total > DG_STATIC_SCRATCH_BYTES) return DG_ERR_WORKSPACE;
+  st = check_step_args(cfg, w, cache, cv, temperature, accept_threshold_nats);
+  if (st != DG_OK) return st;
+  void *ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != DG_OK) return st;
+  return denoise_impl(cfg, w, cache, cv, temperature, accept_threshold_nats, ws, DG_STATIC_SCRATCH_BYTES, stream,
+                      /*logits_dump=*/false, SC_INLINE, 0, nullptr, /*profile=*/false);
 }
 
 // The batch's stacked layout; at least the single step's (the fp32 path steps
