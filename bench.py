@@ -41,6 +41,40 @@ def step_flops(c: dict, selfcond: bool = True) -> float:
     return float(f)
 
 
+def step_bytes(c: dict, selfcond: bool = True) -> float:
+    """Algorithmic HBM bytes of one step: the embedding table streamed by the
+    LM head and (self-conditioned steps) by the self-conditioning
+    contraction, each in bf16; the bf16 probability numerators written by the
+    LM head and read back by the next contraction; the per-(row, 64-column
+    tile) statistics written and read; every projection weight once (bf16);
+    the prefix keys and values once (fp32 as stored).  Activations of the
+    canvas rows (a few MB) are left out."""
+    N, V, d, F, Hq, Hkv, hd, L = c["N"], c["V"], c["d"], c["F"], c["Hq"], c["Hkv"], c["hd"], c["L"]
+    b = V * d * 2 + N * V * 2 + 2 * N * (V // 64) * 16
+    b += (Hq + 2 * Hkv) * hd * d * 2 + d * Hq * hd * 2 + 2 * Hkv * L * hd * 4
+    if selfcond:
+        b += V * d * 2 + N * V * 2 + 2 * d * F * 2
+    return float(b)
+
+
+def cpu_info() -> dict:
+    """The host the oracle baseline ran on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
 def lm_head_bytes(c: dict) -> float:
     """Algorithmic HBM bytes of one LM-head launch: E once (bf16), the
     normalised hidden rows, the bf16 probability numerators written once and
@@ -78,41 +112,45 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(c: dict, inp: dict, rows=(16, 176), sc_rows: int = 24) -> dict:
-    """The oracle timed on a bounded sample: one step at rows[0] and rows[1]
-    evaluated canvas rows (embedding and canvas K/V always use every row),
-    plus self-conditioning rows, extrapolated linearly to all rows."""
+def cpu_baseline(c: dict, inp: dict, rows=(16, 48)) -> dict:
+    """The oracle timed on whole self-conditioned steps (self-conditioning
+    contraction and FFN, attention, output projection, LM head, softmax and
+    entropy of every row), as it stands.  With rows[1] >= N one full step is
+    timed; otherwise steps over canvases of rows[0] and rows[1] tokens (same
+    model, prefix and vocabulary) are timed and the step time is extrapolated
+    linearly in the canvas length to N rows (every part of the step but the
+    fixed prefix handling grows with the rows)."""
     import numpy as np
 
     import oracle
-    om = oracle.model_from_inputs(inp)
+    N, V = c["N"], c["V"]
     kp = inp["k_prefix"].double().numpy()
     vp = inp["v_prefix"].double().numpy()
-    N, V = c["N"], c["V"]
-    tok = oracle.canvas_init(1, 0, N, V)
-    times = []
-    t_start = time.perf_counter()
-    for r in rows:
-        sel = np.zeros(N, np.uint8)
-        sel[:r] = 1
+
+    def one_step(n):
+        om = oracle.model_from_inputs(inp, N=n)
+        tok = oracle.canvas_init(1, 0, n, V)
+        p_prev = np.full((n, V), 1.0 / V)
         t0 = time.perf_counter()
-        om.denoise_forward(tok, None, kp, vp, c["L"], 1.0, row_sel=sel, want_logits=False,
-                           want_probs=False)
-        times.append(time.perf_counter() - t0)
-    per_row = (times[1] - times[0]) / (rows[1] - rows[0])
-    fixed = max(times[0] - per_row * rows[0], 0.0)
-    p = np.full(V, 1.0 / V)
-    t0 = time.perf_counter()
-    for _ in range(sc_rows):
-        om.selfcond_row(p)
-    sc_row = (time.perf_counter() - t0) / sc_rows
+        om.denoise_forward(tok, p_prev, kp, vp, c["L"], 1.0, want_logits=False, want_probs=False)
+        return time.perf_counter() - t0
+
+    t_start = time.perf_counter()
+    if rows[1] >= N:
+        t_step = one_step(N)
+        how = f"one full self-conditioned oracle step of {N} rows"
+    else:
+        t0, t1 = one_step(rows[0]), one_step(rows[1])
+        per_row = (t1 - t0) / (rows[1] - rows[0])
+        t_step = t0 + per_row * (N - rows[0])
+        how = (f"self-conditioned oracle steps over canvases of {rows[0]} and {rows[1]} rows "
+               f"({t0:.2f} s, {t1:.2f} s), extrapolated linearly to {N} rows")
     sample_s = time.perf_counter() - t_start
-    t_step = fixed + N * (per_row + sc_row)
-    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": (f"{c['name']}: oracle step with {rows[0]} and {rows[1]} of {N} rows through "
-                       f"attention/LM head plus {sc_rows} self-conditioning rows ({sample_s:.1f} s of oracle "
-                       f"time), extrapolated linearly to {N} rows (s/step = {t_step:.2f})")}
+    out = {"value": 1.0 / t_step, "unit": "steps/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"{c['name']}: {how}; {sample_s:.1f} s of oracle time; s/step = {t_step:.2f}",
+           "canvas_tokens_per_s": N / t_step, "s_per_step": t_step}
+    out.update(cpu_info())
+    return out
 
 
 def batched_canvases(c: dict, inp: dict, w, cfg, sizes, steps: int, warmup: int) -> dict:
@@ -174,6 +212,59 @@ def batched_canvases(c: dict, inp: dict, w, cfg, sizes, steps: int, warmup: int)
     torch.cuda.empty_cache()
     return {"workload": f"batched canvases, {c['name']}, one prefix cache of {c['L']} per canvas",
             "steps": steps, "warmup": warmup, "by_canvases": res}
+
+
+def native_loop_config(cfg_id: int, steps: int, warmup: int, with_cpu: bool) -> dict:
+    """Another configuration of the workload table through the same native
+    canvas loop as the headline (dg_run_canvas, the stop test kept but unable
+    to fire, so every step but the first is self-conditioned): steps/s,
+    canvas tokens/s, the step's MFMA and algorithmic-HBM fractions, the two
+    table-streaming kernels' HIP-event times (a second loop), where the
+    configured adaptive stop fires, and the oracle baseline of the same
+    configuration."""
+    import torch
+
+    from uniform_state_discrete_dg_amd import binding as B
+    from uniform_state_discrete_dg_amd import driver as D
+    from uniform_state_discrete_dg_amd import workloads as W
+    c = W.config(cfg_id)
+    inp = W.make_inputs(c)
+    den = D.Denoiser(c, inp)
+    seed = W.canvas_seed(cfg_id)
+    probe = den.run_canvas_native(seed, 0, c["steps"], c["sched"], c["T0"], c["T1"], c["gamma"], True, c["stable_n"])
+    den.cfg.conf_eps = 0.0
+    temps = [D.temperature(c["sched"], c["T0"], c["T1"], s % c["steps"], c["steps"]) for s in
+             range(max(steps, warmup))]
+
+    def run(n, cid):
+        k, stopped = B.dg_run_canvas(den.cfg, den.w.s, den.cache.s, den.canvas.s, seed, cid, temps[:n], c["gamma"],
+                                     True, 0, den.ws)
+        assert k == n and not stopped
+        torch.cuda.synchronize()
+
+    run(warmup, 1)
+    t0 = time.perf_counter()
+    run(steps, 2)
+    dt = time.perf_counter() - t0
+    B.dg_profile_enable(3)
+    run(steps, 3)
+    B.dg_profile_enable(0)
+    lm_ms, lm_n, sc_ms, sc_n = B.dg_profile_read()
+    flops = step_flops(c, True) * (steps - 1) + step_flops(c, False)
+    nbytes = step_bytes(c, True) * (steps - 1) + step_bytes(c, False)
+    sps = steps / dt
+    res = {"workload": c["name"], "steps": steps, "warmup": warmup, "steps_per_s": sps, "ms_per_step": dt / steps * 1e3,
+           "canvas_tokens_per_s": sps * c["N"], "mfma_frac_of_bf16_peak": flops / dt / PEAK_BF16_FLOPS,
+           "hbm_GBps_algorithmic": nbytes / dt / 1e9, "hbm_frac_algorithmic": nbytes / dt / PEAK_HBM_BYTES,
+           "bytes_per_selfcond_step": step_bytes(c, True), "flops_per_selfcond_step": step_flops(c, True),
+           "lm_head_us": lm_ms / max(lm_n, 1) * 1e3, "selfcond_us": sc_ms / max(sc_n, 1) * 1e3,
+           "adaptive_stop": {"fires_at_step": probe.steps if probe.stop_reason != "budget" else None,
+                             "reason": probe.stop_reason, "budget": c["steps"]}}
+    if with_cpu:   # a full step where it takes seconds, else two reduced canvases
+        res["cpu_baseline"] = cpu_baseline(c, inp, rows=(c["N"], c["N"]) if c["V"] * c["d"] <= 2 ** 25 else (16, 48))
+    del den
+    torch.cuda.empty_cache()
+    return res
 
 
 def fp8_table(c: dict, inp: dict, steps: int, warmup: int) -> dict:
@@ -263,6 +354,9 @@ def main() -> int:
                          "prefix (the latency-sensitive shapes; empty: skip it)")
     ap.add_argument("--no-fp8-table", action="store_true",
                     help="skip the run with the fp8 (quantised) packed table")
+    ap.add_argument("--other-configs", default="1,2,4",
+                    help="workload table entries also run through the native loop, each with its own "
+                         "oracle baseline (empty: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run the library's plain copy kernel over 1 GiB three times "
                          "(reference for memory-traffic counters)")
@@ -364,6 +458,7 @@ def main() -> int:
             _, _, sc_ms, sc_n = B.dg_profile_read()
     # every timed step but the first of the canvas uses self-conditioning
     flops = step_flops(c, True) * (args.steps - 1) + step_flops(c, False)
+    nbytes = step_bytes(c, True) * (args.steps - 1) + step_bytes(c, False)
     lm_avg_s = lm_ms / 1e3 / max(lm_n, 1)
     lm_gbs = lm_head_bytes(c) / lm_avg_s / 1e9
     sc_avg_s = sc_ms / 1e3 / max(sc_n, 1)
@@ -380,6 +475,12 @@ def main() -> int:
         "repeats": {"steps_per_s": repeats, "median": sorted(repeats)[len(repeats) // 2],
                     "note": "the timed loop run five times back to back; value is the first"},
         "mfma_frac_of_bf16_peak": flops / dt / PEAK_BF16_FLOPS,
+        "step_roofline": {"mfma_frac": flops / dt / PEAK_BF16_FLOPS, "target_mfma_frac": 0.5,
+                          "met": flops / dt / PEAK_BF16_FLOPS >= 0.5,
+                          "hbm_GBps_algorithmic": nbytes / dt / 1e9, "hbm_frac_algorithmic": nbytes / dt / PEAK_HBM_BYTES,
+                          "flops_per_selfcond_step": step_flops(c, True),
+                          "bytes_per_selfcond_step": step_bytes(c, True),
+                          "note": "whole step over the timed loop; 'roofline' below is the LM-head kernel alone"},
         "roofline": {"bound": "hbm", "kernel": "lm_head (tied head + softmax/entropy epilogue)",
                      "achieved": lm_gbs, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                      "frac": lm_gbs * 1e9 / PEAK_HBM_BYTES, "traffic": measured_traffic(),
@@ -411,6 +512,13 @@ def main() -> int:
         del den
         torch.cuda.empty_cache()
         out["block_diffusion"] = block_diffusion()
+    else:
+        del den
+        torch.cuda.empty_cache()
+    others = [int(x) for x in args.other_configs.split(",") if x.strip()]
+    if others:
+        out["other_configs"] = {str(i): native_loop_config(i, args.steps, 10, not args.no_cpu_baseline)
+                                for i in others}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(c, inp)
     print(json.dumps(out), flush=True)
