@@ -127,7 +127,8 @@ typedef enum { DG_STABLE_PREDICTIONS = 0, DG_STABLE_CANVAS = 1 } dg_stable_rule;
  * Supported: 1 <= canvas_len <= 256; vocab a power of two in [256, 2^24];
  * n_q_heads a multiple of n_kv_heads.  DG_BF16 additionally needs head_dim ==
  * 128, d_model <= 4096 and d_model, ffn_hidden multiples of 64; DG_F32 needs
- * head_dim <= 128. */
+ * head_dim <= 128 and a multiple of 16 (its contractions and attention run on
+ * the 16x16x4 fp32 matrix-core instruction). */
 typedef struct {
   int32_t canvas_len;   /* N: tokens per canvas ([P1]: 256; [P5] table: 128) */
   int32_t vocab;        /* V */

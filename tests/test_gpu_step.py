@@ -106,6 +106,20 @@ def test_config1_fp32_lockstep():
     print(rep)
 
 
+@pytest.mark.usefixtures("logits_dump")
+@pytest.mark.parametrize("shape", [
+    dict(N=37, V=1024, d=96, Hq=6, Hkv=3, hd=32, F=200, L=45),     # ragged rows, columns and keys, GQA
+    dict(N=70, V=2048, d=256, Hq=2, Hkv=1, hd=128, F=96, L=130),   # the largest fp32 head, MQA
+])
+def test_fp32_matrix_core_path_ragged_lockstep(shape):
+    """The fp32 configuration's contractions and attention run on the fp32
+    matrix cores (16x16x4 tiles); shapes that are multiples of none of the
+    tile sizes, head dims 32 and 128, three steps in lock-step with the
+    oracle at 1e-4."""
+    c = W.config(1, **shape)
+    lockstep(c, W.make_inputs(c, seed=19), 3)
+
+
 def test_config1_fp32_independent_decisions():
     """fp32 config: the oracle's own decisions equal the GPU's when no two
     entropies (or a prefix sum and the threshold) are within float error."""
@@ -338,12 +352,14 @@ def test_cache_untouched_by_denoise():
     assert den.cache.length == c["L"]
 
 
-@pytest.mark.parametrize("dtype,masked", [("bf16", False), ("f32", False), ("bf16", True)])
+@pytest.mark.parametrize("dtype,masked", [("bf16", False), ("f32", False), ("bf16", True), ("f32hd64", False)])
 def test_prefill_append_incremental(dtype, masked):
     """Causal prefill of 300 tokens then 77 more (ragged), against the oracle;
     masked: the masked sampler's [MASK] id V among them reads its own row."""
     if dtype == "bf16":
         c = W.config(2, L=0, V=8192, d=1024, F=1024, Hq=8, Hkv=4)
+    elif dtype == "f32hd64":
+        c = W.config(1, L=0, d=128, Hq=4, Hkv=2, hd=64)
     else:
         c = W.config(1, L=0)
     cap = 400

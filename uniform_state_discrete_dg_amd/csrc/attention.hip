@@ -330,23 +330,33 @@ hipError_t attention_mfma(const AttnArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path (small head dims): one thread per (query, head), online softmax.
+// fp32 path (the fp32 configuration) on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: products exact in fp32, fp32 accumulation).  One
+// wave owns 16 queries of one query head and walks the keys 16 at a time:
+// S = Q K^T (hd / 4 MFMAs), a running max and sum per query row, P = exp(S
+// - max), then O += P V (4 MFMAs per 16 output dims).  Lane l holds rows
+// 4 (l / 16) + r, r = 0..3, of a 16 x 16 result at column l % 16, so a
+// query row's scores sit in the 16 lanes of one lane group and its running
+// statistics are reduced there; P goes through LDS to become the A operand.
 // ---------------------------------------------------------------------------
-__global__ void attn_f32_kernel(AttnArgs a) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= a.nq * a.Hq) return;
-  const int q = t / a.Hq, h = t % a.Hq;
-  const int g = h / (a.Hq / a.Hkv);
-  const int hd = a.hd;
-  const float *Q = static_cast<const float *>(a.q) + ((int64_t)h * a.nq + q) * hd;
+constexpr int F32_HDMAX = 128;
+
+__global__ void __launch_bounds__(64) attn_f32_kernel(AttnArgs a) {
+  __shared__ float Ps[16][17];
+  const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4;
+  const int h = blockIdx.y, g = h / (a.Hq / a.Hkv), hd = a.hd;
+  const int q0 = blockIdx.x * 16;
   const int nk = a.nA + a.nB;
-  const int lim = a.causal ? min(nk, a.q_pos0 + q + 1) : nk;
+  const float *Q = static_cast<const float *>(a.q) + (int64_t)h * a.nq * hd;
   const float scale = rsqrtf((float)hd);
-  float acc[128];
-  for (int e = 0; e < hd; ++e) acc[e] = 0.f;
-  float m = -INFINITY, l = 0.f;
-  for (int j = 0; j < lim; ++j) {
-    const float *kp, *vp;
+  // A operand of S = Q K^T: lane supplies Q[q0 + col][4 s + grp]
+  float qa[F32_HDMAX / 4];
+#pragma unroll
+  for (int s4 = 0; s4 < F32_HDMAX / 4; ++s4) {
+    const int k = 4 * s4 + grp;
+    qa[s4] = (s4 < hd / 4 && q0 + col < a.nq) ? Q[(int64_t)(q0 + col) * hd + k] : 0.f;
+  }
+  auto key_row = [&](int j, const float *&kp, const float *&vp) {
     if (j < a.nA) {
       kp = static_cast<const float *>(a.kA) + ((int64_t)g * a.capA + j) * hd;
       vp = static_cast<const float *>(a.vA) + ((int64_t)g * a.capA + j) * hd;
@@ -354,23 +364,89 @@ __global__ void attn_f32_kernel(AttnArgs a) {
       kp = static_cast<const float *>(a.kB) + ((int64_t)g * a.capB + (j - a.nA)) * hd;
       vp = static_cast<const float *>(a.vB) + ((int64_t)g * a.capB + (j - a.nA)) * hd;
     }
-    float s = 0.f;
-    for (int e = 0; e < hd; ++e) s = fmaf(Q[e], kp[e], s);
-    s *= scale;
-    const float mn = fmaxf(m, s);
-    const float al = expf(m - mn);
-    const float p = expf(s - mn);
-    l = l * al + p;
-    for (int e = 0; e < hd; ++e) acc[e] = acc[e] * al + p * vp[e];
-    m = mn;
+  };
+  f32x4_t o[F32_HDMAX / 16];
+#pragma unroll
+  for (int t = 0; t < F32_HDMAX / 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
   }
-  float *o = static_cast<float *>(a.out) + (int64_t)q * a.Hq * hd + (int64_t)h * hd;
-  for (int e = 0; e < hd; ++e) o[e] = acc[e] / l;
+  for (int k0 = 0; k0 < nk; k0 += 16) {
+    // S block: key k0 + col for this lane's B operand
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    {
+      const int j = k0 + col;
+      const float *kp = nullptr, *vp = nullptr;
+      if (j < nk) key_row(j, kp, vp);
+#pragma unroll
+      for (int s4 = 0; s4 < F32_HDMAX / 4; ++s4) {
+        if (s4 >= hd / 4) break;
+        const float kb = j < nk ? kp[4 * s4 + grp] : 0.f;
+        sc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[s4], kb, sc, 0, 0, 0);
+      }
+    }
+    // scale, mask, running max/sum per query row 4 grp + r (over the 16 lanes of the group)
+    float p[4], alpha[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qi = q0 + 4 * grp + r, j = k0 + col;
+      float v = sc[r] * scale;
+      if (j >= nk || (a.causal && j > a.q_pos0 + qi)) v = -INFINITY;
+      float mx = v;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float m_new = fmaxf(m_run[r], mx);
+      const float msub = m_new == -INFINITY ? 0.f : m_new;  // a row with no visible key yet
+      alpha[r] = m_new == -INFINITY ? 1.f : expf(m_run[r] - m_new);
+      p[r] = expf(v - msub);
+      float ps = p[r];
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) ps += __shfl_xor(ps, off);
+      l_run[r] = l_run[r] * alpha[r] + ps;
+      m_run[r] = m_new;
+      Ps[4 * grp + r][col] = p[r];
+    }
+#pragma unroll
+    for (int t = 0; t < F32_HDMAX / 16; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[t][r] *= alpha[r];
+    __syncthreads();
+    // O += P V: A operand P[col][4 s + grp] (query col, key 4 s + grp), B operand V[key][dim 16 t + col]
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const float pa = Ps[col][4 * s4 + grp];
+      const int j = k0 + 4 * s4 + grp;
+      const float *kp = nullptr, *vp = nullptr;
+      if (j < nk) key_row(j, kp, vp);
+#pragma unroll
+      for (int t = 0; t < F32_HDMAX / 16; ++t) {
+        if (t >= hd / 16) break;
+        const float vb = j < nk ? vp[16 * t + col] : 0.f;
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vb, o[t], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  float *out = static_cast<float *>(a.out);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int qi = q0 + 4 * grp + r;
+    if (qi >= a.nq) continue;
+#pragma unroll
+    for (int t = 0; t < F32_HDMAX / 16; ++t) {
+      if (t >= hd / 16) break;
+      out[(int64_t)qi * a.Hq * hd + (int64_t)h * hd + 16 * t + col] = o[t][r] / l_run[r];
+    }
+  }
 }
 
 hipError_t attention_f32(const AttnArgs &a, hipStream_t s) {
-  const int n = a.nq * a.Hq;
-  hipLaunchKernelGGL(attn_f32_kernel, dim3((n + 63) / 64), dim3(64), 0, s, a);
+  if (a.hd > F32_HDMAX || a.hd % 16) return hipErrorInvalidValue;
+  if (a.nq <= 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_f32_kernel, dim3((a.nq + 15) / 16, a.Hq), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -64,7 +64,7 @@ dg_status check_config(const dg_config *c) {
     if (c->head_dim != 128 || c->d_model % 64 != 0 || c->ffn_hidden % 64 != 0 || c->d_model > 4096)
       return DG_ERR_UNSUPPORTED;
   } else {
-    if (c->head_dim > 128) return DG_ERR_UNSUPPORTED;
+    if (c->head_dim > 128 || c->head_dim % 16) return DG_ERR_UNSUPPORTED;  // fp32 MFMA tiles of 16
   }
   return DG_OK;
 }

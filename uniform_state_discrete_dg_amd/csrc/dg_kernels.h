@@ -121,7 +121,7 @@ struct SelfcondGuard {
 };
 hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partials, int ksplit, hipStream_t s,
                          SelfcondGuard guard = SelfcondGuard{nullptr, 0});
-// fp32 SIMT GEMM: C[m][n] = sum_k A[m*sam + k*sak] * B[n*sbn + k*sbk].
+// fp32 GEMM on the fp32 MFMA: C[m][n] = sum_k A[m*sam + k*sak] * B[n*sbn + k*sbk].
 struct GemmShapeF32 {
   const float *A;
   int64_t sam, sak;
@@ -241,6 +241,7 @@ struct AttnArgs {
 };
 // head_dim 128 on the MFMA (split-bf16 products), split-KV + merge
 hipError_t attention_mfma(const AttnArgs &a, hipStream_t s);
+// fp32 path (head_dim <= 128, a multiple of 16) on the fp32 MFMA
 hipError_t attention_f32(const AttnArgs &a, hipStream_t s);
 void attention_plan(int nq, int Hq, int nk, int *splits, int *keys_per_split);
 

@@ -2,7 +2,8 @@
 //
 // The small contractions of the step (QKV, output projection, the
 // self-conditioning FFN) on the gfx950 32x32x16 bf16 MFMA with fp32
-// accumulation, plus the fp32 SIMT GEMM of the fp32 configuration.  (The
+// accumulation, plus the fp32 GEMM of the fp32 configuration on the
+// 16x16x4 fp32 MFMA.  (The
 // two table-streaming contractions live in estream.hip.)
 // All operands are K-contiguous ("NT"): A[M][K] and B[N][K].
 #include "dg_device.h"
@@ -429,37 +430,54 @@ hipError_t gemm_split_norm(const SplitGemm &g, const RowNorm &rn, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
-// fp32 SIMT GEMM (the fp32 configuration): 16x16 outputs per workgroup,
-// K staged through LDS in slices of 16, generic strides on both operands.
+// fp32 GEMM (the fp32 configuration) on the fp32 matrix cores: every product
+// exact in fp32, accumulated in fp32 by v_mfma_f32_16x16x4_f32.  A
+// workgroup of 4 waves owns a 32 x 32 output tile (a 16 x 16 tile per wave);
+// K is staged through LDS 32 at a time.  Generic strides on both operands
+// (the self-conditioning contraction reads E as its transpose).
+// MFMA lane layout (16x16x4): lane l supplies A[l % 16][l / 16] and
+// B^T[l % 16][l / 16] and holds D[4 (l / 16) + r][l % 16], r = 0..3.
 // ---------------------------------------------------------------------------
+namespace {
+constexpr int F32_BM = 32, F32_BN = 32, F32_BK = 32;
+}
+
 __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmShapeF32 g, Epi e) {
-  __shared__ float sa[16][17];
-  __shared__ float sb[16][17];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int m = blockIdx.y * 16 + ty, n = blockIdx.x * 16 + tx;
-  float acc = 0.f;
-  for (int k0 = 0; k0 < g.K; k0 += 16) {
-    {
-      const int am = blockIdx.y * 16 + ty, ak = k0 + tx;
-      float v = 0.f;
-      if (am < g.M && ak < g.K) {
-        v = g.A[(int64_t)am * g.sam + (int64_t)ak * g.sak];
-        if (g.a_scale) v *= g.a_scale[(int64_t)am * g.a_scale_ld + (ak >> 6)];
+  __shared__ float sa[F32_BM][F32_BK + 1];
+  __shared__ float sb[F32_BN][F32_BK + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.y * F32_BM, n0 = blockIdx.x * F32_BN;
+  const int wm = (wave >> 1) * 16, wn = (wave & 1) * 16;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < g.K; k0 += F32_BK) {
+    for (int t = tid; t < F32_BM * F32_BK; t += 256) {
+      const int r = t / F32_BK, k = t % F32_BK, gk = k0 + k;
+      float va = 0.f, vb = 0.f;
+      if (m0 + r < g.M && gk < g.K) {
+        va = g.A[(int64_t)(m0 + r) * g.sam + (int64_t)gk * g.sak];
+        if (g.a_scale) va *= g.a_scale[(int64_t)(m0 + r) * g.a_scale_ld + (gk >> 6)];
       }
-      sa[ty][tx] = v;
-      const int bn = blockIdx.x * 16 + ty, bk = k0 + tx;
-      sb[ty][tx] = (bn < g.N && bk < g.K) ? g.B[(int64_t)bn * g.sbn + (int64_t)bk * g.sbk] : 0.f;
+      if (n0 + r < g.N && gk < g.K) vb = g.B[(int64_t)(n0 + r) * g.sbn + (int64_t)gk * g.sbk];
+      sa[r][k] = va;
+      sb[r][k] = vb;
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) acc = fmaf(sa[ty][kk], sb[tx][kk], acc);
+    for (int kk = 0; kk < F32_BK; kk += 4)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[wm + (lane & 15)][kk + (lane >> 4)],
+                                                 sb[wn + (lane & 15)][kk + (lane >> 4)], acc, 0, 0, 0);
     __syncthreads();
   }
-  if (m < g.M && n < g.N) epi_store(e, m, n, acc);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = m0 + wm + 4 * (lane >> 4) + r, n = n0 + wn + (lane & 15);
+    if (m < g.M && n < g.N) epi_store(e, m, n, acc[r]);
+  }
 }
 
 hipError_t gemm_f32(const GemmShapeF32 &g, const Epi &e, hipStream_t s) {
-  dim3 grid((g.N + 15) / 16, (g.M + 15) / 16, 1);
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  dim3 grid((g.N + F32_BN - 1) / F32_BN, (g.M + F32_BM - 1) / F32_BM, 1);
   hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, g, e);
   return hipGetLastError();
 }
