@@ -58,11 +58,14 @@ __device__ __forceinline__ void select_body(const float *__restrict__ entropy, c
   const int i = threadIdx.x;
 
   float h = 0.f;
-  int32_t old = 0;
-  if (i < N) {
+  int32_t old = 0, p = 0, p_prev = 0, cand = 0;
+  if (i < N) {  // every load up front, so their latencies overlap
     h = entropy[i];
     if (h <= 0.f) h = 0.f;  // clamp; NaN passes through
     old = tokens[i];
+    cand = argmax[i];
+    p = __float_as_int(pred[i].x);
+    p_prev = pred_prev[i];
   }
   // masked sampler: a decided (locked) position takes no part in the walk;
   // its key sorts after every walked one and it adds nothing to their sums
@@ -104,11 +107,10 @@ __device__ __forceinline__ void select_body(const float *__restrict__ entropy, c
   if (i < N) {
     // [P3] §5.3 / [P5]: is this position's prediction the previous step's?
     // (no previous step at step 0; a NaN entropy has no prediction to compare)
-    const int32_t p = __float_as_int(pred[i].x);
-    pchanged = step == 0u || p != pred_prev[i] || h != h;
+    pchanged = step == 0u || p != p_prev || h != h;
     pred_prev[i] = p;
     acc = acc_here;
-    const int32_t t = acc ? argmax[i]
+    const int32_t t = acc ? cand
                           : (mask_id >= 0 ? old : uniform_token(seed, (uint32_t)i, step, canvas_id, 1u, log2v));
     tokens[i] = t;
     masked = mask_id >= 0 && t == mask_id;
