@@ -267,10 +267,12 @@ def native_loop_config(cfg_id: int, steps: int, warmup: int, with_cpu: bool) -> 
     return res
 
 
-def fp8_table(c: dict, inp: dict, steps: int, warmup: int) -> dict:
-    """The same workload with the quantised table: E replaced by its fp8 e4m3
-    grid (q = E * 2^8, saturated, nearest even) and the streaming kernels
-    reading the fp8 packed copy (half the table bytes).  A model variant,
+def quantised_table(c: dict, inp: dict, steps: int, warmup: int, table: str) -> dict:
+    """The same workload with a quantised table: E replaced by its fp8 e4m3
+    grid (table "fp8": q = E * 2^8, saturated, nearest even; half the table
+    bytes) or its block-scaled fp4 e2m1 grid (table "fp4": a power-of-two
+    scale per 32 x 32 block; a quarter of the table bytes plus the scale
+    bytes), the streaming kernels reading the packed copy.  A model variant,
     timed with the same native loop as the headline (the stop test kept,
     unable to fire); the bf16 path on this table gives the same results bit
     for bit."""
@@ -279,10 +281,10 @@ def fp8_table(c: dict, inp: dict, steps: int, warmup: int) -> dict:
     from uniform_state_discrete_dg_amd import binding as B
     from uniform_state_discrete_dg_amd import driver as D
     from uniform_state_discrete_dg_amd import workloads as W
-    c8 = dict(c, table="fp8", table_exp=8)
-    inp8 = dict(inp)
-    inp8["E"] = W.fp8_grid(inp["E"], 8)
-    den = D.Denoiser(c8, inp8)
+    cq = dict(c, table=table, table_exp=8 if table == "fp8" else 0)
+    inpq = dict(inp)
+    inpq["E"] = W.fp8_grid(inp["E"], 8) if table == "fp8" else W.fp4_grid(inp["E"])
+    den = D.Denoiser(cq, inpq)
     den.cfg.conf_eps = 0.0
     temps = [D.temperature(c["sched"], c["T0"], c["T1"], s % c["steps"], c["steps"]) for s in
              range(max(steps, warmup))]
@@ -300,13 +302,15 @@ def fp8_table(c: dict, inp: dict, steps: int, warmup: int) -> dict:
     lm_ms, lm_n, sc_ms, sc_n = B.dg_profile_read()
     N, V, d = c["N"], c["V"], c["d"]
     lm_us = lm_ms / max(lm_n, 1) * 1e3
-    lm_bytes = V * d + N * d * 2 + N * V * 2 + N * (V // 64) * 16
-    res = {"table": "fp8 e4m3, q = E * 2^8", "steps": n, "steps_per_s": n / dt,
+    tbytes = V * d if table == "fp8" else V * d // 2 + V * d // 1024  # one copy of the table
+    lm_bytes = tbytes + N * d * 2 + N * V * 2 + N * (V // 64) * 16
+    name = "fp8 e4m3, q = E * 2^8" if table == "fp8" else "fp4 e2m1, one power-of-two scale per 32 x 32 block"
+    res = {"table": name, "steps": n, "steps_per_s": n / dt,
            "canvas_tokens_per_s": n / dt * N,
            "mfma_frac_of_bf16_peak": (step_flops(c, True) * (n - 1) + step_flops(c, False)) / dt / PEAK_BF16_FLOPS,
            "lm_head_us": lm_us, "lm_head_algorithmic_GBps": lm_bytes / (lm_us * 1e-6) / 1e9,
            "selfcond_us": sc_ms / max(sc_n, 1) * 1e3,
-           "table_bytes_per_step": 2 * V * d}
+           "table_bytes_per_step": 2 * tbytes}
     del den
     torch.cuda.empty_cache()
     return res
@@ -354,6 +358,8 @@ def main() -> int:
                          "prefix (the latency-sensitive shapes; empty: skip it)")
     ap.add_argument("--no-fp8-table", action="store_true",
                     help="skip the run with the fp8 (quantised) packed table")
+    ap.add_argument("--no-fp4-table", action="store_true",
+                    help="skip the run with the block-scaled fp4 packed table")
     ap.add_argument("--other-configs", default="1,2,4",
                     help="workload table entries also run through the native loop, each with its own "
                          "oracle baseline (empty: skip)")
@@ -507,7 +513,9 @@ def main() -> int:
         assert all(c4[k] == c[k] for k in ("V", "d", "Hq", "Hkv", "hd", "F", "dtype"))
         out["batched_small_canvases"] = batched_canvases(c4, inp, den.w, B.make_config(c4), small, nb_steps, 3)
     if not args.no_fp8_table:
-        out["fp8_table"] = fp8_table(c, inp, args.steps, 3)
+        out["fp8_table"] = quantised_table(c, inp, args.steps, 3, "fp8")
+    if not args.no_fp4_table:
+        out["fp4_table"] = quantised_table(c, inp, args.steps, 3, "fp4")
     if not args.no_block_diffusion:
         del den
         torch.cuda.empty_cache()

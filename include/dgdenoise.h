@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define DG_ABI_VERSION 6
+#define DG_ABI_VERSION 7
 
 typedef enum {
   DG_OK = 0,
@@ -96,8 +96,8 @@ typedef enum { DG_SAMPLER_UNIFORM = 0, DG_SAMPLER_MASKED = 1 } dg_sampler;
 
 /* Storage of the packed table the two table-streaming contractions read
  * (DG_BF16 only; DG_F32 ignores it).  [P2] (local-deployment numbers) runs
- * the model quantised (NVFP4) to fit a consumer GPU; the MI355X counterpart
- * kept here is OCP fp8 e4m3.
+ * the model quantised (NVFP4) to fit a consumer GPU; the MI355X counterparts
+ * kept here are OCP fp8 e4m3 and block-scaled fp4 e2m1.
  * BF16: E_pack holds E and E^T in bf16.
  * FP8:  E_pack holds q = E * 2^table_exp and its transpose as fp8 e4m3
  *       (dg_pack_embedding rounds to nearest even and saturates at +-448).
@@ -107,8 +107,20 @@ typedef enum { DG_SAMPLER_UNIFORM = 0, DG_SAMPLER_MASKED = 1 } dg_sampler;
  *       gathers and the exact top-logit recompute read it) must hold the
  *       same values, i.e. lie on that grid (E = fp8(E * 2^table_exp) *
  *       2^-table_exp), or the two copies disagree.  The table's bytes halve
- *       (E_pack 2 V d bytes instead of 4 V d). */
-typedef enum { DG_TABLE_BF16 = 0, DG_TABLE_FP8 = 1 } dg_table_format;
+ *       (E_pack 2 V d bytes instead of 4 V d).
+ * FP4:  E_pack holds E and E^T as e2m1 codes (values 0, 0.5, 1, 1.5, 2, 3,
+ *       4, 6 and their negatives) with one power-of-two scale byte u per
+ *       32 x 32 block of E (value = code * 2^(u - 127), an E8M0 exponent as
+ *       in the OCP microscaling formats, over a square block so that E and
+ *       E^T hold the same values).  dg_pack_embedding sets u = floor(log2
+ *       of the block's largest magnitude) - 2 + 127, clamped to [2, 252]
+ *       (127 for an all-zero block), and rounds each value divided by the
+ *       scale to the nearest code (ties to the even code, saturated at 6; a
+ *       value rounded to zero is +0).  table_exp must be 0.  As with FP8 the
+ *       kernels widen each fragment to bf16 exactly, and E must lie on that
+ *       grid.  E_pack is V d + V d / 512 bytes (codes, then the scale bytes of
+ *       E's blocks and of E^T's). */
+typedef enum { DG_TABLE_BF16 = 0, DG_TABLE_FP8 = 1, DG_TABLE_FP4 = 2 } dg_table_format;
 
 /* What the adaptive stop's stability counter counts ([P3] §5.3 adaptive
  * stop: the most likely token predictions unchanged over the last N steps;
@@ -145,7 +157,7 @@ typedef struct {
   dg_candidate_rule candidate_rule;
   dg_sampler sampler;
   dg_table_format table_format;
-  int32_t table_exp;    /* DG_TABLE_FP8: q = E * 2^table_exp, in [-32, 32] */
+  int32_t table_exp;    /* DG_TABLE_FP8: q = E * 2^table_exp, in [-32, 32]; 0 for DG_TABLE_FP4 */
   dg_stable_rule stable_rule;
 } dg_config;
 
@@ -268,8 +280,9 @@ size_t dg_probs_bytes(const dg_config *cfg);
 
 /* Writes E_pack (device, caller-allocated dg_embedding_pack_bytes(cfg)
  * bytes): E [V][d] in the tiled layout, followed by E^T [d][V] in the tiled
- * layout (padding rows zero).  A layout copy only: the same values as E.
- * Does nothing for DG_F32. */
+ * layout (padding rows zero).  DG_TABLE_BF16: a layout copy only, the same
+ * values as E; DG_TABLE_FP8 / DG_TABLE_FP4: the rounded codes (and scale
+ * bytes) described at dg_table_format.  Does nothing for DG_F32. */
 dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_pack, void *stream);
 
 /* [P3] §5.4 canvas initialisation: tokens[i] = the top log2(V) bits of word 0

@@ -38,7 +38,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert B.dg_abi_version() == 6
+    assert B.dg_abi_version() == 7
     for s in range(6):
         assert lib.dg_status_string(s)
 
@@ -359,7 +359,7 @@ def test_fp8_table_config_and_sizes(lib):
     assert B.dg_validate_config(c8) == B.DG_ERR_INVALID_ARG
     c8.table_exp = -32
     assert B.dg_validate_config(c8) == B.DG_OK
-    c8.table_format = 2
+    c8.table_format = 3
     assert B.dg_validate_config(c8) == B.DG_ERR_INVALID_ARG
     # the fp32 configuration ignores the table format (it reads E directly)
     c1 = cfg_of(1, table="fp8", table_exp=8)
@@ -380,3 +380,63 @@ def test_fp8_grid_quantiser():
     assert (Q.float() - E.float()).abs().max().item() <= 0.0625 * E.float().abs().max().item() + 2 ** -17
     big = torch.tensor([[1e6, -1e6, 0.0, 3.0]], dtype=torch.bfloat16)
     assert W.fp8_grid(big, 0).float().tolist() == [[448.0, -448.0, 0.0, 3.0]]
+
+
+def test_fp4_table_config_and_sizes(lib):
+    """The fp4 packed table: accepted for DG_BF16 with table_exp 0 (its
+    scales are per block); codes are half a byte per element and every
+    1024 elements add one scale byte; same workspace and canvas buffers."""
+    for i in (2, 3, 4):
+        cfg = cfg_of(i)
+        c4 = cfg_of(i, table="fp4")
+        assert c4.table_format == B.DG_TABLE_FP4 and c4.table_exp == 0
+        assert B.dg_validate_config(c4) == B.DG_OK
+        n = cfg.vocab * cfg.d_model  # d multiple of 256 here: no padding rows
+        assert B.dg_embedding_pack_bytes(c4) == n + 2 * n // 1024
+        assert B.dg_workspace_bytes(c4, 0) == B.dg_workspace_bytes(cfg, 0)
+        assert B.dg_probs_bytes(c4) == B.dg_probs_bytes(cfg)
+    c4 = cfg_of(2, table="fp4")
+    c4.table_exp = 1
+    assert B.dg_validate_config(c4) == B.DG_ERR_INVALID_ARG
+    c1 = cfg_of(1, table="fp4")
+    assert B.dg_validate_config(c1) == B.DG_OK
+    assert B.dg_embedding_pack_bytes(c1) == 0
+
+
+def test_fp4_grid_quantiser():
+    """The block-scaled fp4 input: each 32 x 32 block holds code values
+    times one power of two, the block's largest magnitude maps into
+    [4, 6] (saturating above 6), rounding is to the nearest value with ties
+    to the even code, the grid is idempotent and exact in bf16."""
+    import torch
+    g = torch.Generator().manual_seed(5)
+    E = (torch.randn(64, 96, generator=g) * 0.05).to(torch.bfloat16)
+    Q = W.fp4_grid(E)
+    u = W.fp4_scale_bytes(E)
+    assert u.shape == (2, 3)
+    full = u.repeat_interleave(32, 0).repeat_interleave(32, 1)
+    y = Q.float() * torch.pow(2.0, (127 - full).float())
+    assert set(y.abs().unique().tolist()) <= set(W.FP4_VALUES)
+    amax = E.float().abs().view(2, 32, 3, 32).amax(dim=(1, 3))
+    r = amax * torch.pow(2.0, (127 - u).float())
+    assert bool(((r >= 4) & (r < 8)).all())
+    assert torch.equal(W.fp4_grid(Q), Q)
+    assert torch.equal(W.fp4_scale_bytes(Q), u)
+    # error bound: half the largest gap (2 units of 2^(u-127)) or the saturation
+    err = (Q.float() - E.float()).abs() * torch.pow(2.0, (127 - full).float())
+    assert err.max().item() <= 2.0
+    # hand-worked block: scale byte 127 (largest magnitude 4.5, floor(log2) = 2)
+    blk = torch.zeros(32, 32)
+    vals = [4.5, 0.25, 0.26, -0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 5.5, -7.9, -0.1, 0.74]
+    blk[0, :len(vals)] = torch.tensor(vals)
+    want = [4.0, 0.0, 0.5, -1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0, -6.0, 0.0, 0.5]
+    got = W.fp4_grid(blk.to(torch.bfloat16)).float()[0, :len(vals)].tolist()
+    assert W.fp4_scale_bytes(blk).item() == 127
+    assert got == want
+    codes = W.fp4_codes(blk)[0, :len(vals)].tolist()
+    assert codes == [6, 0, 1, 8 | 2, 2, 4, 4, 6, 6, 7, 8 | 7, 0, 1]   # -0.1 -> +0
+    # an all-zero block has scale byte 127; tiny and huge blocks clamp
+    z = torch.zeros(32, 32)
+    assert W.fp4_scale_bytes(z).item() == 127
+    assert W.fp4_scale_bytes(torch.full((32, 32), 2.0 ** -130)).item() == 2
+    assert W.fp4_scale_bytes(torch.full((32, 32), 2.0 ** 126)).item() == 126 - 2 + 127

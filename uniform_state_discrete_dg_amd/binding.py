@@ -25,7 +25,7 @@ DG_F32, DG_BF16 = 0, 1
 DG_ACCEPT_SUM_MINUS_MAX, DG_ACCEPT_CUMSUM = 0, 1
 DG_CANDIDATE_ARGMAX, DG_CANDIDATE_MULTINOMIAL = 0, 1
 DG_SAMPLER_UNIFORM, DG_SAMPLER_MASKED = 0, 1
-DG_TABLE_BF16, DG_TABLE_FP8 = 0, 1
+DG_TABLE_BF16, DG_TABLE_FP8, DG_TABLE_FP4 = 0, 1, 2
 DG_STABLE_PREDICTIONS, DG_STABLE_CANVAS = 0, 1
 DG_STATUS_WORDS = 16
 DG_MAX_BATCH = 16
@@ -317,13 +317,13 @@ def make_config(c: dict, accept_rule: int = DG_ACCEPT_SUM_MINUS_MAX,
                 conf_eps: float = 0.005, candidate_rule: int = DG_CANDIDATE_ARGMAX,
                 sampler: int = DG_SAMPLER_UNIFORM, stable_rule: int = DG_STABLE_PREDICTIONS) -> dg_config:
     """The C config of a workload dict; c["table"] == "fp8" selects the fp8
-    packed table with scale exponent c["table_exp"]; c["stable_rule"], when
-    present, overrides stable_rule."""
-    fp8 = c.get("table") == "fp8"
+    packed table with scale exponent c["table_exp"], "fp4" the block-scaled
+    fp4 table; c["stable_rule"], when present, overrides stable_rule."""
+    table = {"fp8": DG_TABLE_FP8, "fp4": DG_TABLE_FP4}.get(c.get("table"), DG_TABLE_BF16)
     return dg_config(c["N"], c["V"], c["d"], c["Hq"], c["Hkv"], c["hd"], c["F"],
                      DG_BF16 if c["dtype"] == "bf16" else DG_F32, c.get("rms_eps", 1e-6),
                      conf_eps, accept_rule, candidate_rule, sampler,
-                     DG_TABLE_FP8 if fp8 else DG_TABLE_BF16, c.get("table_exp", 0) if fp8 else 0,
+                     table, c.get("table_exp", 0) if table == DG_TABLE_FP8 else 0,
                      c.get("stable_rule", stable_rule))
 
 

@@ -48,10 +48,11 @@ dg_status check_config(const dg_config *c) {
       !in_range(enum_value(c->accept_rule), DG_ACCEPT_SUM_MINUS_MAX, DG_ACCEPT_CUMSUM) ||
       !in_range(enum_value(c->candidate_rule), DG_CANDIDATE_ARGMAX, DG_CANDIDATE_MULTINOMIAL) ||
       !in_range(enum_value(c->sampler), DG_SAMPLER_UNIFORM, DG_SAMPLER_MASKED) ||
-      !in_range(enum_value(c->table_format), DG_TABLE_BF16, DG_TABLE_FP8) ||
+      !in_range(enum_value(c->table_format), DG_TABLE_BF16, DG_TABLE_FP4) ||
       !in_range(enum_value(c->stable_rule), DG_STABLE_PREDICTIONS, DG_STABLE_CANVAS))
     return DG_ERR_INVALID_ARG;
   if (c->table_format == DG_TABLE_FP8 && (c->table_exp < -32 || c->table_exp > 32)) return DG_ERR_INVALID_ARG;
+  if (c->table_format == DG_TABLE_FP4 && c->table_exp != 0) return DG_ERR_INVALID_ARG;  // scales are per block
   if (c->canvas_len < 1 || c->vocab < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
       c->head_dim < 1 || c->ffn_hidden < 1)
     return DG_ERR_INVALID_ARG;
@@ -75,20 +76,26 @@ dg_status check_config(const dg_config *c) {
 size_t pack_te_elems(const dg_config *c) { return dg::tl_elems(c->vocab, c->d_model); }
 size_t pack_elems(const dg_config *c) { return pack_te_elems(c) + dg::tl_elems(c->d_model, c->vocab); }
 bool table_fp8(const dg_config *c) { return c->dtype == DG_BF16 && c->table_format == DG_TABLE_FP8; }
+bool table_fp4(const dg_config *c) { return c->dtype == DG_BF16 && c->table_format == DG_TABLE_FP4; }
+// fp4: the codes of E and E^T (half a byte per element), then the scale
+// bytes of E's blocks and of E^T's (one per 1024 elements)
+size_t pack4_codes(const dg_config *c) { return pack_elems(c) / 2; }
+size_t pack4_scales(const dg_config *c) { return pack_elems(c) / 1024; }
 
-// The packed table one streaming contraction reads: bf16 (elements) or fp8
-// (one byte per element, E = q * scale).
+// The packed table one streaming contraction reads: bf16 (elements), or a
+// quantised form (fp8: one byte per element, E = q * scale; fp4: codes and
+// block scale bytes).
 struct TableRef {
   const uint16_t *bf;
-  const uint8_t *q8;
-  float scale;
+  dg::QTable qt;
 };
 // E (the LM head's operand) or, with transposed, E^T (the self-conditioning one)
 TableRef table_ref(const dg_config *c, const dg_weights *w, bool transposed) {
   const size_t off = transposed ? pack_te_elems(c) : 0;
-  if (table_fp8(c))
-    return {nullptr, static_cast<const uint8_t *>(w->E_pack) + off, std::ldexp(1.f, -c->table_exp)};
-  return {static_cast<const uint16_t *>(w->E_pack) + off, nullptr, 1.f};
+  const uint8_t *p8 = static_cast<const uint8_t *>(w->E_pack);
+  if (table_fp8(c)) return {nullptr, {1, p8 + off, nullptr, std::ldexp(1.f, -c->table_exp)}};
+  if (table_fp4(c)) return {nullptr, {2, p8 + off / 2, p8 + pack4_codes(c) + off / 1024, 1.f}};
+  return {static_cast<const uint16_t *>(w->E_pack) + off, {0, nullptr, nullptr, 1.f}};
 }
 
 int selfcond_ksplit(const dg_config *c) {
@@ -387,6 +394,7 @@ size_t dg_stats_bytes(const dg_config *cfg) {
 
 size_t dg_embedding_pack_bytes(const dg_config *cfg) {
   if (check_config(cfg) != DG_OK || cfg->dtype != DG_BF16) return 0;
+  if (table_fp4(cfg)) return pack4_codes(cfg) + pack4_scales(cfg);
   return pack_elems(cfg) * (table_fp8(cfg) ? 1 : 2);
 }
 
@@ -409,6 +417,14 @@ dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_pack, v
     const uint16_t *Eb = static_cast<const uint16_t *>(E);
     DG_TRY(dg::tile_fp8(Eb, V, d, d, false, sc, q, s));
     DG_TRY(dg::tile_fp8(Eb, d, V, d, true, sc, q + pack_te_elems(cfg), s));
+    return DG_OK;
+  }
+  if (table_fp4(cfg)) {  // e2m1 codes with 32 x 32 block scales: E [V][d], then E^T [d][V]
+    uint8_t *q = static_cast<uint8_t *>(E_pack), *sc = q + pack4_codes(cfg);
+    const uint16_t *Eb = static_cast<const uint16_t *>(E);
+    const size_t te = pack_te_elems(cfg);
+    DG_TRY(dg::tile_fp4(Eb, V, d, d, false, q, sc, s));
+    DG_TRY(dg::tile_fp4(Eb, d, V, d, true, q + te / 2, sc + te / 1024, s));
     return DG_OK;
   }
   bf16 *te = static_cast<bf16 *>(E_pack), *tet = te + pack_te_elems(cfg);
@@ -575,7 +591,7 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
         dg::EsCanvasesIn cin{};
         cin.probs[0] = static_cast<const uint16_t *>(cv->probs);
         cin.shift[0] = shift;
-        DG_TRY(dg::selfcond_bf16_batch(cin, 1, tt.bf, N, d, V, true, part, ks, s, guard, tt.q8, tt.scale));
+        DG_TRY(dg::selfcond_bf16_batch(cin, 1, tt.bf, N, d, V, true, part, ks, s, guard, tt.qt));
       }
       if (sc_mode == SC_AHEAD) return DG_OK;
       DG_TRY(dg::selfcond_reduce(part, ks, N, d, top, static_cast<const uint16_t *>(cv->probs), V, rscale, shift,
@@ -663,8 +679,7 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
       dg::EsCanvases ec{};
       ec.probs[0] = static_cast<uint16_t *>(cv->probs);
       ec.tile_stats[0] = tstats;
-      DG_TRY(dg::lm_head_bf16_batch(nrm16, 1, N, d, te.bf, V, inv_T, ec, dump ? logits : nullptr, s, te.q8,
-                                    te.scale));
+      DG_TRY(dg::lm_head_bf16_batch(nrm16, 1, N, d, te.bf, V, inv_T, ec, dump ? logits : nullptr, s, te.qt));
     }
     // the numerators stay as stored: the next step's contraction applies the
     // power-of-two tile exponents and the row factor (the batch launch with
@@ -765,7 +780,7 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
     {
       ProfScope ps(g_prof_sc, s);
       DG_TRY(dg::selfcond_bf16_batch(cin, B, tt.bf, N, d, V, true, part, ks, s, dg::SelfcondGuard{nullptr, 0},
-                                     tt.q8, tt.scale));
+                                     tt.qt));
     }
     for (int b = 0; b < B; ++b)
       DG_TRY(dg::selfcond_reduce(part + (size_t)b * ks * N * d, ks, N, d,
@@ -837,7 +852,7 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
     }
     ProfScope ps(g_prof_lm, s);
     const TableRef te = table_ref(cfg, w, false);
-    DG_TRY(dg::lm_head_bf16_batch(nrm16, B, N, d, te.bf, V, inv_T, ec, nullptr, s, te.q8, te.scale));
+    DG_TRY(dg::lm_head_bf16_batch(nrm16, B, N, d, te.bf, V, inv_T, ec, nullptr, s, te.qt));
   }
   {  // row statistics of every canvas in one launch, then its candidates, then one selection launch
     dg::RowCombineBatch rc{};
@@ -1122,7 +1137,7 @@ static hipError_t selfcond_vector(const dg_config *cfg, const dg_weights *w, con
     cin.probs[0] = static_cast<const uint16_t *>(probs);
     cin.shift[0] = shift;
     hipError_t e = dg::selfcond_bf16_batch(cin, 1, tt.bf, N, d, V, true, part, ks, s, dg::SelfcondGuard{nullptr, 0},
-                                           tt.q8, tt.scale);
+                                           tt.qt);
     if (e != hipSuccess) return e;
     return dg::selfcond_reduce(part, ks, N, d, top, static_cast<const uint16_t *>(probs), V, rscale, shift,
                                static_cast<const uint16_t *>(w->E), S, nullptr, s);

@@ -153,12 +153,21 @@ struct EsCanvases {
   uint16_t *probs[ES_MAX_BATCH];
   float4 *tile_stats[ES_MAX_BATCH];
 };
-// The table comes in one of two forms: E_tiled (bf16) or E8_tiled (fp8
-// e4m3 in the 8-byte-chunk tiled layout, values q with E = q * e8_scale);
-// exactly one is non-null.
+// A quantised form of the table operand (dg_tiled.h): tf = 1, fp8 e4m3
+// codes q in the 8-byte-chunk layout with E = q * scale; tf = 2, fp4 e2m1
+// codes in the 4-byte-chunk layout with one scale byte per 32 x 32 block
+// at s4 (scale is unused).  tf = 0: none (the bf16 operand is used).
+struct QTable {
+  int tf;
+  const uint8_t *q;
+  const uint8_t *s4;
+  float scale;
+};
+// The table comes in one of three forms: E_tiled (bf16) or a quantised
+// form qt; exactly one is given (E_tiled non-null or qt.tf != 0).
 hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, const uint16_t *E_tiled, int V,
                               float inv_T, const EsCanvases &cv, float *logits_dump, hipStream_t s,
-                              const uint8_t *E8_tiled = nullptr, float e8_scale = 1.f);
+                              const QTable &qt = QTable{0, nullptr, nullptr, 1.f});
 // The self-conditioning contraction of B canvases at once: canvas c's
 // operand cin.probs[c] (its exponents cin.shift[c] when scaled), partials at
 // partials + c * ksplit * M * N (the single-canvas layout per canvas).
@@ -171,8 +180,8 @@ struct EsCanvasesIn {
 };
 hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *Et_tiled, int M, int N, int K,
                                bool scaled, float *partials, int ksplit, hipStream_t s,
-                               SelfcondGuard guard = SelfcondGuard{nullptr, 0}, const uint8_t *Et8_tiled = nullptr,
-                               float e8_scale = 1.f);
+                               SelfcondGuard guard = SelfcondGuard{nullptr, 0},
+                               const QTable &qt = QTable{0, nullptr, nullptr, 1.f});
 // Same statistics from fp32 logits already in memory (fp32 path).
 hipError_t tile_stats_f32(const float *logits, int M, int V, float inv_T, float *probs,
                           float4 *tile_stats, hipStream_t s);
@@ -286,6 +295,14 @@ hipError_t copy_bytes(const void *src, void *dst, size_t bytes, hipStream_t s);
 // (X [R][K]) or Y = X^T (trans: X [K][R]), leading dimension ldx: each value
 // times scale, clamped to +-448, rounded to nearest even; rows past R zero.
 hipError_t tile_fp8(const uint16_t *X, int R, int K, int64_t ldx, bool trans, float scale, uint8_t *out,
+                    hipStream_t s);
+// fp4 e2m1 copy in the 4-byte-chunk tiled layout (dg_tiled.h) of Y = X or
+// Y = X^T as for tile_fp8, with the scale bytes of its 32 x 32 blocks: per
+// block u = clamp(floor(log2 amax) - 2 + 127, 2, 252) (127 for an all-zero
+// block), codes = y * 2^(127 - u) rounded to the nearest e2m1 value (ties
+// to the even code, saturated at +-6; a code rounded to zero is +0); rows
+// past R are zero codes with scale byte 127.
+hipError_t tile_fp4(const uint16_t *X, int R, int K, int64_t ldx, bool trans, uint8_t *codes, uint8_t *scales,
                     hipStream_t s);
 
 // Selection and canvas.  mask_id >= 0: the masked sampler (the canvas starts

@@ -48,4 +48,25 @@ __host__ __device__ inline int64_t tl8_index(int row, int col, int K) {
   return (((int64_t)b * (K >> 5) + s) * TL_CHUNKS + tl8_pos(r, k >> 3)) * 8 + (k & 7);
 }
 
+// The fp4 form (e2m1, two values per byte): the same blocks of 256 rows x 32
+// columns, 4 KB each, with 4-byte chunks of 8 values: chunk p holds
+// X[256 b + r][32 s + 8 c .. + 7], r = p / 4, c = (p % 4) ^ ((r / 8) % 4),
+// value 8 c + 2 i in the low nibble of byte i and 8 c + 2 i + 1 in its high
+// nibble.  A fragment is one 4-byte LDS read per lane; its 32 rows x 2 chunk
+// columns fall on 64 distinct banks.  Each 32 x 32 sub-block (rows 32 g ..
+// 32 g + 31 of the block) has one scale byte u (value = code * 2^(u - 127)),
+// stored apart from the codes: byte g of 8 per block, blocks in the same
+// order.
+constexpr int TL4_BYTES = 4096;  // bytes of codes per block
+constexpr int TL4_SCALES = 8;    // scale bytes per block
+__host__ __device__ inline int tl4_pos(int r, int c) { return r * 4 + (c ^ ((r >> 3) & 3)); }
+// byte holding X[row][col] (low nibble for even col) and that value's scale byte
+__host__ __device__ inline int64_t tl4_index(int row, int col, int K) {
+  const int b = row >> 8, r = row & 255, s = col >> 5, k = col & 31;
+  return (((int64_t)b * (K >> 5) + s) * TL_CHUNKS + tl4_pos(r, k >> 3)) * 4 + ((k & 7) >> 1);
+}
+__host__ __device__ inline int64_t tl4_scale_index(int row, int col, int K) {
+  return ((int64_t)(row >> 8) * (K >> 5) + (col >> 5)) * TL4_SCALES + ((row & 255) >> 5);
+}
+
 }  // namespace dg

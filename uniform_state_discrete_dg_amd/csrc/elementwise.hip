@@ -233,6 +233,71 @@ hipError_t tile_fp8(const uint16_t *X, int R, int K, int64_t ldx, bool trans, fl
   return hipGetLastError();
 }
 
+// fp4 e2m1 copy of a bf16 matrix in the 4-byte-chunk tiled layout
+// (dg_tiled.h), Y = X or Y = X^T as in tile_fp8_kernel, with a scale byte per
+// 32 x 32 block.  One workgroup per 256 x 32 block; thread t finds the
+// largest magnitude of row t, threads 0..7 that of a 32-row group.
+__device__ inline uint32_t fp4_code(float y) {  // nearest e2m1 code, ties to even, saturated; zero is +0
+  const float a = fabsf(y);
+  const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.f ? 6u : 7u;
+  return (c != 0u && signbit(y)) ? c | 8u : c;
+}
+__global__ void __launch_bounds__(256) tile_fp4_kernel(const bf16 *__restrict__ X, int R, int K, int64_t ldx,
+                                                       int trans, uint8_t *__restrict__ codes,
+                                                       uint8_t *__restrict__ scales) {
+  __shared__ float tile[256][33];
+  __shared__ float rowmax[256];
+  __shared__ float gmul[8];
+  const int nks = K / TL_K;
+  const int b = blockIdx.x / nks, s = blockIdx.x % nks;
+  const int t = threadIdx.x;
+  for (int i = 0; i < 32; ++i) {
+    const int idx = t + 256 * i;
+    int r, k;
+    float v = 0.f;
+    if (trans) {
+      k = idx >> 8;
+      r = idx & 255;
+      if (256 * b + r < R) v = bf16_to_f32(X[(int64_t)(32 * s + k) * ldx + 256 * b + r]);
+    } else {
+      r = idx >> 5;
+      k = idx & 31;
+      if (256 * b + r < R) v = bf16_to_f32(X[(int64_t)(256 * b + r) * ldx + 32 * s + k]);
+    }
+    tile[r][k] = v;
+  }
+  __syncthreads();
+  float m = 0.f;
+  for (int k = 0; k < 32; ++k) m = fmaxf(m, fabsf(tile[t][k]));  // NaN entries are passed over
+  rowmax[t] = m;
+  __syncthreads();
+  if (t < 8) {
+    float a = 0.f;
+    for (int r = 0; r < 32; ++r) a = fmaxf(a, rowmax[32 * t + r]);
+    const int ef = (int)((__float_as_uint(a) >> 23) & 0xFF);  // floor(log2 a) + 127 for normal a
+    const int u = a == 0.f ? 127 : min(max(ef - 2, 2), 252);
+    scales[(int64_t)blockIdx.x * TL4_SCALES + t] = (uint8_t)u;
+    gmul[t] = __uint_as_float((uint32_t)(254 - u) << 23);  // 2^(127 - u), exact
+  }
+  __syncthreads();
+  for (int j = 0; j < 4; ++j) {
+    const int p = t + 256 * j, r = p >> 2, c = (p & 3) ^ ((r >> 3) & 3);  // slot p holds chunk c
+    const float mul = gmul[r >> 5];
+    uint32_t w = 0u;
+    for (int e = 0; e < 8; ++e) w |= fp4_code(tile[r][8 * c + e] * mul) << (4 * e);
+    *reinterpret_cast<uint32_t *>(codes + (int64_t)blockIdx.x * TL4_BYTES + (int64_t)p * 4) = w;
+  }
+}
+
+hipError_t tile_fp4(const uint16_t *X, int R, int K, int64_t ldx, bool trans, uint8_t *codes, uint8_t *scales,
+                    hipStream_t s) {
+  if (R < 1 || K % TL_K) return hipErrorInvalidValue;
+  const int blocks = (R + TL_ROWS - 1) / TL_ROWS * (K / TL_K);
+  hipLaunchKernelGGL(tile_fp4_kernel, dim3(blocks), dim3(256), 0, s, X, R, K, ldx, trans ? 1 : 0, codes, scales);
+  return hipGetLastError();
+}
+
 hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top, const uint16_t *probs,
                            int V, const float *row_scale, const uint8_t *shift, const uint16_t *E, float *out,
                            uint16_t *out_split, hipStream_t s, int64_t lo_off) {

@@ -72,17 +72,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 // (positive values; anything scaled below the normal range becomes zero or
 // a denormal).
 //
-// B8: the table operand is fp8 e4m3 (q = E * 2^e) in the 8-byte-chunk tiled
-// layout (8 KB per slice, one DMA instruction per wave); each table fragment
-// is read as 8 bytes and turned into bf16 q * b8_scale (b8_scale = 2^-e:
-// exact) before the MFMAs, so the accumulation is that of the bf16 table
-// holding the same values.
-template <bool SCALED, bool PAIR = false, bool B8 = false>
+// TF (the table's storage) = TF_FP8: the table operand is fp8 e4m3
+// (q = E * 2^e) in the 8-byte-chunk tiled layout (8 KB per slice, one DMA
+// instruction per wave); each table fragment is read as 8 bytes and turned
+// into bf16 q * b8_scale (b8_scale = 2^-e: exact) before the MFMAs, so the
+// accumulation is that of the bf16 table holding the same values.
+// TF = TF_FP4: fp4 e2m1 with a power-of-two scale per 32 x 32 block
+// (dg_tiled.h), 4 KB per slice copied by the low 32 lanes of every wave; a
+// fragment is one 4-byte LDS read widened to bf16 exactly by four
+// v_cvt_scalef32_pk_bf16_fp4.  Bt8 carries the fp8 or fp4
+// blocks, Bs4 the fp4 scale bytes (slice s of this block at Bs4 + 8 s); the
+// 8 scale bytes of slice s are copied beside it by wave s % 8.
+enum { TF_BF16 = 0, TF_FP8 = 1, TF_FP4 = 2 };
+template <bool SCALED, bool PAIR = false, int TF = TF_BF16>
 __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const bf16 *__restrict__ Bt,
                                              const uint8_t *__restrict__ shift, int sb, int se, char *lds,
                                              f32x16_t (&acc)[2][4], const bf16 *__restrict__ At2 = nullptr,
                                              const uint8_t *__restrict__ shift2 = nullptr,
-                                             const uint8_t *__restrict__ Bt8 = nullptr, float b8_scale = 1.f) {
+                                             const uint8_t *__restrict__ Bt8 = nullptr, float b8_scale = 1.f,
+                                             const uint8_t *__restrict__ Bs4 = nullptr) {
+  constexpr bool B8 = TF == TF_FP8, B4 = TF == TF_FP4, BQ = B8 || B4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r32 = lane & 31, g = lane >> 5;
@@ -104,28 +113,38 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   const bf16 *asrc = (PAIR && wave >= 4) ? At2 + (int64_t)sb * TL_ELEMS + ((wave - 4) * 2 * 64 + lane) * 8
                                          : At + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
   const uint8_t *ssrc = !SCALED ? nullptr : (PAIR && lane >= 32) ? shift2 + (lane - 32) * 4 : shift + lane * 4;
-  const bf16 *bsrc = B8 ? nullptr : Bt + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
-  const uint8_t *bsrc8 = B8 ? Bt8 + (int64_t)sb * TL8_BYTES + (wave * 64 + lane) * 16 : nullptr;
+  const bf16 *bsrc = BQ ? nullptr : Bt + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
+  const uint8_t *bsrc8 = B8 ? Bt8 + (int64_t)sb * TL8_BYTES + (wave * 64 + lane) * 16
+                            : B4 ? Bt8 + (int64_t)sb * TL4_BYTES + (wave * 32 + (lane & 31)) * 16 : nullptr;
   char *lds_shift = lds + ES_STAGES * 2 * ES_SLICE;  // SCALED: [stage][256] bytes
+  char *lds_s4 = lds_shift + ES_STAGES * 256;         // B4: [stage][16] bytes, the slice's 8 scales
   auto issue = [&](int slice, int stage) {
     const int64_t off = (int64_t)min(slice, nk - 1) * TL_ELEMS;  // past the end: a repeat, never read
     char *st = lds + stage * 2 * ES_SLICE;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       __builtin_amdgcn_global_load_lds(asrc + off + u * 512, st + (wave * 2 + u) * 1024, 16, 0, 0);
-      if (!B8)
+      if (!BQ)
         __builtin_amdgcn_global_load_lds(bsrc + off + u * 512, st + ES_SLICE + (wave * 2 + u) * 1024, 16, 0, 0);
     }
     if (B8)  // 8 KB of fp8 table: 1 KB per wave
       __builtin_amdgcn_global_load_lds(bsrc8 + (int64_t)min(slice, nk - 1) * TL8_BYTES, st + ES_SLICE + wave * 1024,
                                        16, 0, 0);
+    if (B4 && lane < 32)  // 4 KB of fp4 table: 512 bytes per wave, lanes 0..31
+      __builtin_amdgcn_global_load_lds(bsrc8 + (int64_t)min(slice, nk - 1) * TL4_BYTES, st + ES_SLICE + wave * 512,
+                                       16, 0, 0);
     if (SCALED && wave == (slice & 7))  // the slice tile's 256 row exponents, 4 bytes per lane
       __builtin_amdgcn_global_load_lds(ssrc + (int64_t)((sb + min(slice, nk - 1)) >> 1) * 256,
                                        lds_shift + stage * 256, 4, 0, 0);
+    if (B4 && wave == (slice & 7) && lane < 2)  // the slice's 8 block scales, 4 bytes per lane
+      __builtin_amdgcn_global_load_lds(Bs4 + (int64_t)(sb + min(slice, nk - 1)) * 8 + lane * 4, lds_s4 + stage * 16,
+                                       4, 0, 0);
   };
-  // DMA instructions per slice per wave: 4 (3 with the fp8 table), plus the
-  // exponents of slice s for wave s % 8 when SCALED
-  constexpr int PER = B8 ? 3 : 4;
+  // DMA instructions per slice per wave: 4 (3 with an fp8 or fp4 table),
+  // plus XTRA more for wave s % 8 on slice s (exponents when SCALED, fp4
+  // block scales)
+  constexpr int PER = BQ ? 3 : 4;
+  constexpr int XTRA = (SCALED ? 1 : 0) + (B4 ? 1 : 0);
 
   // Fragment f of one 16-wide k step as stored: f < 2 a canvas fragment
   // (rows wm*64 + 32f), else table fragment f - 2 (rows wn*128 + 32(f-2)).
@@ -138,6 +157,24 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   auto frag8 = [&](int stage, int kk, int j) -> uint2 {
     const uint2 *sl = reinterpret_cast<const uint2 *>(lds + stage * 2 * ES_SLICE + ES_SLICE);
     return sl[tl8_pos(wn * 128 + j * 32 + r32, kk * 2 + g)];
+  };
+  // B4: the 4 bytes (8 fp4 values) of table fragment j, its block's scale
+  // (rows wn*128 + 32j: scale byte 4 wn + j of the slice), and the bf16 form
+  auto frag4 = [&](int stage, int kk, int j) -> uint32_t {
+    const uint32_t *sl = reinterpret_cast<const uint32_t *>(lds + stage * 2 * ES_SLICE + ES_SLICE);
+    return sl[tl4_pos(wn * 128 + j * 32 + r32, kk * 2 + g)];
+  };
+  // the scale bytes of this wave's four table fragments (rows wn*128 + 32j:
+  // byte j), one broadcast read; fragment j's scale 2^(byte - 127)
+  auto scales4 = [&](int stage) -> uint32_t {
+    return *reinterpret_cast<const uint32_t *>(lds_s4 + stage * 16 + wn * 4);
+  };
+  auto scale4 = [](uint32_t w, int j) -> float { return __uint_as_float(((w >> (8 * j)) & 0xFFu) << 23); };
+  auto widen4 = [&](uint32_t q, float sc) -> uint4 {
+    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 0)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 2)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 3)));
   };
   auto widen = [&](uint2 q) -> uint4 {
     return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, b8_scale, false)),
@@ -163,6 +200,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   auto half = [&](const uint4 (&cur)[6], uint4 (&nxt)[6], int nstage, int nkk, bool ex, u16x2_t (&e)[2]) {
     uint32_t sh[2];
     uint2 q8[4];
+    uint32_t q4[4], s4 = 0;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int i = m >> 2, j = m & 3;
@@ -170,12 +208,16 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
                                                           __builtin_bit_cast(bf16x8_t, cur[i]), acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (m < 3) {
-        if (!B8 || m == 0) {
+        if (!BQ || m == 0) {
           nxt[2 * m] = frag(nstage, nkk, 2 * m);
           nxt[2 * m + 1] = frag(nstage, nkk, 2 * m + 1);
-        } else {
+        } else if (B8) {
           q8[2 * m - 2] = frag8(nstage, nkk, 2 * m - 2);
           q8[2 * m - 1] = frag8(nstage, nkk, 2 * m - 1);
+        } else {
+          q4[2 * m - 2] = frag4(nstage, nkk, 2 * m - 2);
+          q4[2 * m - 1] = frag4(nstage, nkk, 2 * m - 1);
+          if (m == 1) s4 = scales4(nstage);
         }
         if (SCALED && ex && m == 0) {
           sh[0] = expo(nstage, 0);
@@ -187,6 +229,11 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
     if (B8) {  // while the last MFMAs run
 #pragma unroll
       for (int j = 0; j < 4; ++j) nxt[2 + j] = widen(q8[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (B4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nxt[2 + j] = widen4(q4[j], scale4(s4, j));
       __builtin_amdgcn_sched_barrier(0);
     }
     if (SCALED) {  // while the last MFMAs run
@@ -211,13 +258,17 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   issue(2, 2);
   uint4 F0[6], F1[6];
   u16x2_t ex[2];
-  if (SCALED && (wave == 1 || wave == 2))
-    wait_vmcnt<2 * PER + 1>();
+  if (XTRA && (wave == 1 || wave == 2))
+    wait_vmcnt<2 * PER + XTRA>();
   else
     wait_vmcnt<2 * PER>();
   __builtin_amdgcn_s_barrier();
+  const uint32_t s40 = B4 ? scales4(0) : 0u;
 #pragma unroll
-  for (int f = 0; f < 6; ++f) F0[f] = (B8 && f >= 2) ? widen(frag8(0, 0, f - 2)) : frag(0, 0, f);
+  for (int f = 0; f < 6; ++f)
+    F0[f] = (B8 && f >= 2) ? widen(frag8(0, 0, f - 2))
+            : (B4 && f >= 2) ? widen4(frag4(0, 0, f - 2), scale4(s40, f - 2))
+                             : frag(0, 0, f);
   if (SCALED) {
     ex[0] = packed(expo(0, 0));
     ex[1] = packed(expo(0, 1));
@@ -226,8 +277,8 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   }
   for (int it = 0; it < nk; ++it) {
     half(F0, F1, it & 3, 1, false, ex);  // second half of slice it, same exponents
-    if (SCALED && wave == ((it + 2) & 7))  // this wave's copies of slice it+1 landed ...
-      wait_vmcnt<PER + 1>();
+    if (XTRA && wave == ((it + 2) & 7))  // this wave's copies of slice it+1 landed ...
+      wait_vmcnt<PER + XTRA>();
     else
       wait_vmcnt<PER>();
     __builtin_amdgcn_s_barrier();  // ... every wave's; every wave is done with slice it-1
@@ -253,12 +304,13 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
 // run back to back on one XCD, so the table tile comes from HBM once and from
 // that XCD's L2 for the other blocks.
 // ---------------------------------------------------------------------------
-template <bool BATCH, bool B8>
+template <bool BATCH, int TF>
 __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__restrict__ At, int M, int N, int K,
                                                               const bf16 *__restrict__ Et, int V, float inv_T,
                                                               EsCanvases cv, int nblk, int items,
                                                               float *__restrict__ logits,
-                                                              const uint8_t *__restrict__ Et8, float b8_scale) {
+                                                              const uint8_t *__restrict__ Et8, float b8_scale,
+                                                              const uint8_t *__restrict__ Es4) {
   extern __shared__ __align__(16) char lds[];
   int item = blockIdx.x;
   if (BATCH) item = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;  // grid: a multiple of 8
@@ -269,9 +321,11 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
   const int ksl = K / ES_BK;
   f32x16_t acc[2][4];
-  estream_tile<false, false, B8>(At + (int64_t)bb * ksl * TL_ELEMS, B8 ? nullptr : Et + (int64_t)jt * ksl * TL_ELEMS,
-                                 nullptr, 0, ksl, lds, acc, nullptr, nullptr,
-                                 B8 ? Et8 + (int64_t)jt * ksl * TL8_BYTES : nullptr, b8_scale);
+  estream_tile<false, false, TF>(
+      At + (int64_t)bb * ksl * TL_ELEMS, TF != TF_BF16 ? nullptr : Et + (int64_t)jt * ksl * TL_ELEMS, nullptr, 0, ksl,
+      lds, acc, nullptr, nullptr,
+      TF == TF_FP8 ? Et8 + (int64_t)jt * ksl * TL8_BYTES : TF == TF_FP4 ? Et8 + (int64_t)jt * ksl * TL4_BYTES : nullptr,
+      b8_scale, TF == TF_FP4 ? Es4 + (int64_t)jt * ksl * 8 : nullptr);
   const int ntiles = V / 64;
 
 #pragma unroll
@@ -348,19 +402,28 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
 
 int estream_bm(int) { return ES_BM; }
 
-static size_t es_lds_bytes() { return (size_t)ES_STAGES * (2 * ES_SLICE + 256); }
+static size_t es_lds_bytes() { return (size_t)ES_STAGES * (2 * ES_SLICE + 256 + 16); }
+
+// exactly one table form: bf16, or a quantised form with its codes (and scales)
+static bool one_table_form(const void *bf, const QTable &qt) {
+  if (qt.tf == TF_BF16) return bf != nullptr;
+  if (bf || !qt.q) return false;
+  return qt.tf == TF_FP8 || (qt.tf == TF_FP4 && qt.s4);
+}
 
 hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, const uint16_t *E_tiled, int V,
                               float inv_T, const EsCanvases &cv, float *logits_dump, hipStream_t s,
-                              const uint8_t *E8_tiled, float e8_scale) {
+                              const QTable &qt) {
   if (B < 1 || B > ES_MAX_BATCH || N < 1 || N > ES_BM || K % ES_BK || V % ES_BN) return hipErrorInvalidValue;
-  if (!E_tiled == !E8_tiled) return hipErrorInvalidValue;  // exactly one table form
+  if (!one_table_form(E_tiled, qt)) return hipErrorInvalidValue;
   static std::atomic<uint64_t> attr{0};
   if (once_per_device(attr, [] {
-        const void *fns[4] = {reinterpret_cast<const void *>(lm_head_es_kernel<false, false>),
-                              reinterpret_cast<const void *>(lm_head_es_kernel<true, false>),
-                              reinterpret_cast<const void *>(lm_head_es_kernel<false, true>),
-                              reinterpret_cast<const void *>(lm_head_es_kernel<true, true>)};
+        const void *fns[6] = {reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_BF16>),
+                              reinterpret_cast<const void *>(lm_head_es_kernel<true, TF_BF16>),
+                              reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_FP8>),
+                              reinterpret_cast<const void *>(lm_head_es_kernel<true, TF_FP8>),
+                              reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_FP4>),
+                              reinterpret_cast<const void *>(lm_head_es_kernel<true, TF_FP4>)};
         for (const void *f : fns) {
           const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes());
           if (e != hipSuccess) return e;
@@ -371,17 +434,19 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
   const int M = B * N, nblk = (M + ES_BM - 1) / ES_BM;
   const int items = (V / ES_BN) * nblk;
   const dim3 grid(B == 1 ? items : (items + 7) / 8 * 8);
-#define DG_LM_LAUNCH(BT, Q8)                                                                                   \
-  hipLaunchKernelGGL((lm_head_es_kernel<BT, Q8>), grid, dim3(ES_NT), es_lds_bytes(), s, A_tiled, M, N, K,      \
-                     reinterpret_cast<const bf16 *>(E_tiled), V, inv_T, cv, nblk, items, logits_dump, E8_tiled, \
-                     e8_scale)
-  if (B == 1) {
-    if (E8_tiled) DG_LM_LAUNCH(false, true);
-    else DG_LM_LAUNCH(false, false);
-  } else {
-    if (E8_tiled) DG_LM_LAUNCH(true, true);
-    else DG_LM_LAUNCH(true, false);
-  }
+#define DG_LM_LAUNCH(BT, TF)                                                                                   \
+  hipLaunchKernelGGL((lm_head_es_kernel<BT, TF>), grid, dim3(ES_NT), es_lds_bytes(), s, A_tiled, M, N, K,      \
+                     reinterpret_cast<const bf16 *>(E_tiled), V, inv_T, cv, nblk, items, logits_dump, qt.q,     \
+                     qt.scale, qt.s4)
+#define DG_LM_FORMS(BT)                                  \
+  do {                                                   \
+    if (qt.tf == TF_FP8) DG_LM_LAUNCH(BT, TF_FP8);       \
+    else if (qt.tf == TF_FP4) DG_LM_LAUNCH(BT, TF_FP4);  \
+    else DG_LM_LAUNCH(BT, TF_BF16);                      \
+  } while (0)
+  if (B == 1) DG_LM_FORMS(false);
+  else DG_LM_FORMS(true);
+#undef DG_LM_FORMS
 #undef DG_LM_LAUNCH
   return hipGetLastError();
 }
@@ -391,7 +456,7 @@ hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E
   EsCanvases cv{};
   cv.probs[0] = probs_tiled;
   cv.tile_stats[0] = tile_stats;
-  return lm_head_bf16_batch(A_tiled, 1, M, K, E_tiled, V, inv_T, cv, logits_dump, s, nullptr, 1.f);
+  return lm_head_bf16_batch(A_tiled, 1, M, K, E_tiled, V, inv_T, cv, logits_dump, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -406,12 +471,12 @@ hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E
 // MODE: 0 one canvas; 1 a batch, one canvas per 256-row block; 2 a batch of
 // canvases of at most 128 rows, two per block (canvas 2p in rows 0..127,
 // canvas 2p + 1 in rows 128..255, read from its own buffers).
-template <bool SCALED, int MODE, bool B8>
+template <bool SCALED, int MODE, int TF>
 __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin, const bf16 *__restrict__ Bt,
                                                                int M, int N, int K, float *__restrict__ part,
                                                                int ksplit, int ntn, int nb, int items,
                                                                SelfcondGuard guard, const uint8_t *__restrict__ Bt8,
-                                                               float b8_scale) {
+                                                               float b8_scale, const uint8_t *__restrict__ Bs4) {
   extern __shared__ __align__(16) char lds[];
   const int b = blockIdx.x, ng = gridDim.x;
   const int per_xcd = ng / 8;  // grid is a multiple of 8
@@ -424,17 +489,20 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin,
   const int sb = (int)((int64_t)ksl * kc / ksplit), se = (int)((int64_t)ksl * (kc + 1) / ksplit);
   const int n0 = nt * ES_BN;
   f32x16_t acc[2][4];
-  const bf16 *Bn = B8 ? nullptr : Bt + (int64_t)nt * ksl * TL_ELEMS;
-  const uint8_t *Bn8 = B8 ? Bt8 + (int64_t)nt * ksl * TL8_BYTES : nullptr;
+  const bf16 *Bn = TF != TF_BF16 ? nullptr : Bt + (int64_t)nt * ksl * TL_ELEMS;
+  const uint8_t *Bn8 = TF == TF_FP8   ? Bt8 + (int64_t)nt * ksl * TL8_BYTES
+                       : TF == TF_FP4 ? Bt8 + (int64_t)nt * ksl * TL4_BYTES
+                                      : nullptr;
+  const uint8_t *Bn4 = TF == TF_FP4 ? Bs4 + (int64_t)nt * ksl * TL4_SCALES : nullptr;
   if (MODE == 2) {
     const int c0 = 2 * blk, c1 = c0 + 1;
     // an odd batch's last block: its upper half is the canvas's own padding rows
     const bf16 *A2 = c1 < nb ? cin.probs[c1] : cin.probs[c0] + 512 * 8;
     const uint8_t *s2 = c1 < nb ? cin.shift[c1] : cin.shift[c0] + 128;
-    estream_tile<SCALED, true, B8>(cin.probs[c0], Bn, cin.shift[c0], sb, se, lds, acc, A2, s2, Bn8, b8_scale);
+    estream_tile<SCALED, true, TF>(cin.probs[c0], Bn, cin.shift[c0], sb, se, lds, acc, A2, s2, Bn8, b8_scale, Bn4);
   } else {
-    estream_tile<SCALED, false, B8>(cin.probs[blk], Bn, cin.shift[blk], sb, se, lds, acc, nullptr, nullptr, Bn8,
-                                    b8_scale);
+    estream_tile<SCALED, false, TF>(cin.probs[blk], Bn, cin.shift[blk], sb, se, lds, acc, nullptr, nullptr, Bn8,
+                                    b8_scale, Bn4);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -459,17 +527,18 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin,
 
 hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *Et_tiled, int M, int N, int K,
                                bool scaled, float *partials, int ksplit, hipStream_t s, SelfcondGuard guard,
-                               const uint8_t *Et8_tiled, float e8_scale) {
+                               const QTable &qt) {
   if (B < 1 || B > ES_MAX_BATCH || M > ES_BM || K % 64 || N % 4 || ksplit < 1 || ksplit > K / ES_BK)
     return hipErrorInvalidValue;
-  if (!Et_tiled == !Et8_tiled) return hipErrorInvalidValue;  // exactly one table form
+  if (!one_table_form(Et_tiled, qt)) return hipErrorInvalidValue;
   static std::atomic<uint64_t> attr{0};
   if (once_per_device(attr, [] {
-#define DG_SC_FN(SC, MD, Q8) reinterpret_cast<const void *>(selfcond_es_kernel<SC, MD, Q8>)
-        const void *fns[12] = {DG_SC_FN(false, 0, false), DG_SC_FN(true, 0, false), DG_SC_FN(false, 1, false),
-                               DG_SC_FN(true, 1, false),  DG_SC_FN(false, 2, false), DG_SC_FN(true, 2, false),
-                               DG_SC_FN(false, 0, true),  DG_SC_FN(true, 0, true),  DG_SC_FN(false, 1, true),
-                               DG_SC_FN(true, 1, true),   DG_SC_FN(false, 2, true), DG_SC_FN(true, 2, true)};
+#define DG_SC_FN(SC, MD, TF) reinterpret_cast<const void *>(selfcond_es_kernel<SC, MD, TF>)
+#define DG_SC_FN6(TF) \
+  DG_SC_FN(false, 0, TF), DG_SC_FN(true, 0, TF), DG_SC_FN(false, 1, TF), DG_SC_FN(true, 1, TF), \
+      DG_SC_FN(false, 2, TF), DG_SC_FN(true, 2, TF)
+        const void *fns[18] = {DG_SC_FN6(TF_BF16), DG_SC_FN6(TF_FP8), DG_SC_FN6(TF_FP4)};
+#undef DG_SC_FN6
 #undef DG_SC_FN
         for (const void *f : fns) {
           const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes());
@@ -483,22 +552,24 @@ hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *E
   const int items = ntn * ksplit * (mode == 2 ? (B + 1) / 2 : B);
   const dim3 grid((items + 7) / 8 * 8);
   const bf16 *Bt = reinterpret_cast<const bf16 *>(Et_tiled);
-#define DG_SC_LAUNCH(SC, MD, Q8)                                                                                 \
-  hipLaunchKernelGGL((selfcond_es_kernel<SC, MD, Q8>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Bt, M, N, K,   \
-                     partials, ksplit, ntn, B, items, guard, Et8_tiled, e8_scale)
-#define DG_SC_MODES(SC, Q8)                  \
-  do {                                       \
-    if (mode == 0) DG_SC_LAUNCH(SC, 0, Q8);  \
-    else if (mode == 1) DG_SC_LAUNCH(SC, 1, Q8); \
-    else DG_SC_LAUNCH(SC, 2, Q8);            \
+#define DG_SC_LAUNCH(SC, MD, TF)                                                                                 \
+  hipLaunchKernelGGL((selfcond_es_kernel<SC, MD, TF>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Bt, M, N, K,   \
+                     partials, ksplit, ntn, B, items, guard, qt.q, qt.scale, qt.s4)
+#define DG_SC_MODES(SC, TF)                      \
+  do {                                           \
+    if (mode == 0) DG_SC_LAUNCH(SC, 0, TF);      \
+    else if (mode == 1) DG_SC_LAUNCH(SC, 1, TF); \
+    else DG_SC_LAUNCH(SC, 2, TF);                \
   } while (0)
-  if (Et8_tiled) {
-    if (scaled) DG_SC_MODES(true, true);
-    else DG_SC_MODES(false, true);
-  } else {
-    if (scaled) DG_SC_MODES(true, false);
-    else DG_SC_MODES(false, false);
-  }
+#define DG_SC_FORMS(SC)                                \
+  do {                                                 \
+    if (qt.tf == TF_FP8) DG_SC_MODES(SC, TF_FP8);      \
+    else if (qt.tf == TF_FP4) DG_SC_MODES(SC, TF_FP4); \
+    else DG_SC_MODES(SC, TF_BF16);                     \
+  } while (0)
+  if (scaled) DG_SC_FORMS(true);
+  else DG_SC_FORMS(false);
+#undef DG_SC_FORMS
 #undef DG_SC_MODES
 #undef DG_SC_LAUNCH
   return hipGetLastError();
@@ -509,8 +580,7 @@ hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partia
   EsCanvasesIn cin{};
   cin.probs[0] = reinterpret_cast<const bf16 *>(g.A);
   cin.shift[0] = shift;
-  return selfcond_bf16_batch(cin, 1, g.B, g.M, g.N, g.K, shift != nullptr, partials, ksplit, s, guard, nullptr,
-                             1.f);
+  return selfcond_bf16_batch(cin, 1, g.B, g.M, g.N, g.K, shift != nullptr, partials, ksplit, s, guard);
 }
 
 }  // namespace dg

@@ -97,6 +97,8 @@ def make_inputs(cfg: dict, seed: int | None = None) -> dict:
     out["E"] = w(V, d)
     if c.get("table") == "fp8":
         out["E"] = fp8_grid(out["E"], c["table_exp"])
+    elif c.get("table") == "fp4":
+        out["E"] = fp4_grid(out["E"])
     out["w1"] = w(F, d)
     out["w2"] = w(d, F)
     out["wq"] = w(Hq * hd, d)
@@ -124,6 +126,52 @@ def fp8_grid(E: torch.Tensor, exp: int) -> torch.Tensor:
     either side sees it."""
     q = (E.float() * (2.0 ** exp)).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).float()
     return (q * (2.0 ** -exp)).to(E.dtype)
+
+
+FP4_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)  # e2m1 magnitudes, codes 0..7
+
+
+def fp4_scale_bytes(E: torch.Tensor) -> torch.Tensor:
+    """The scale byte u of each 32 x 32 block of E [R][K] (R, K multiples of
+    32): floor(log2 of the block's largest magnitude) - 2 + 127 read off the
+    float32 exponent field, clamped to [2, 252]; 127 for an all-zero block.
+    Returns int64 [R/32][K/32]."""
+    R, K = E.shape
+    a = E.float().abs().view(R // 32, 32, K // 32, 32).amax(dim=(1, 3)).contiguous()
+    ef = (a.view(torch.int32) >> 23) & 0xFF
+    u = (ef.to(torch.int64) - 2).clamp(2, 252)
+    return torch.where(a == 0, torch.full_like(u, 127), u)
+
+
+def fp4_codes(E: torch.Tensor) -> torch.Tensor:
+    """The e2m1 code (sign in bit 3) of every entry of E [R][K] under its
+    block's scale: the magnitude over 2^(u - 127) rounded to the nearest
+    value of FP4_VALUES, ties to the even code, saturated at 6; a value
+    rounded to zero is +0.  Returns uint8 [R][K]."""
+    R, K = E.shape
+    u = fp4_scale_bytes(E).repeat_interleave(32, 0).repeat_interleave(32, 1)
+    y = E.float() * torch.pow(2.0, (127 - u).float())
+    a = y.abs()
+    # thresholds are the midpoints; a midpoint goes to the even code
+    code = torch.full(a.shape, 7, dtype=torch.int64)
+    for c, (hi, incl) in reversed(list(enumerate(((0.25, True), (0.75, False), (1.25, True), (1.75, False),
+                                                  (2.5, True), (3.5, False), (5.0, True))))):
+        code = torch.where((a <= hi) if incl else (a < hi), torch.full_like(code, c), code)
+    neg = torch.signbit(y) & (code != 0)
+    return (code | (neg.to(torch.int64) << 3)).to(torch.uint8)
+
+
+def fp4_grid(E: torch.Tensor) -> torch.Tensor:
+    """A block-scaled fp4 table: every entry replaced by code value x
+    2^(u - 127) (fp4_codes, fp4_scale_bytes), returned in E's dtype (exactly:
+    such values are bf16 numbers).  An input of the fp4-table
+    configurations, drawn before either side sees it."""
+    R, K = E.shape
+    q = fp4_codes(E).to(torch.int64)
+    mag = torch.tensor(FP4_VALUES, dtype=torch.float32)[q & 7]
+    val = torch.where((q & 8) != 0, -mag, mag)
+    u = fp4_scale_bytes(E).repeat_interleave(32, 0).repeat_interleave(32, 1)
+    return (val * torch.pow(2.0, (u - 127).float())).to(E.dtype)
 
 
 def random_row_weights(N: int, V: int, seed: int) -> torch.Tensor:
