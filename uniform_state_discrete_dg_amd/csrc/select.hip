@@ -15,13 +15,12 @@
 // walked, rejected ones keep [MASK] and decided ones are never revisited.
 //
 // The walk is evaluated in parallel: each position's key (entropy bits << 32
-// | position) orders it among the others, its entropy is turned into
-// 2^-32-nat fixed point, and each thread sums, in 64-bit integers, the
-// fixed-point entropies of every key below its own -- the prefix sum of its
-// rank in the ascending order, without sorting.  A position is accepted iff
-// its prefix test holds: the tests are monotone in the rank, so this equals
-// the sequential walk, and integer sums make the result independent of
-// summation order.
+// | position; unique, so the order is total) is sorted ascending by a
+// bitonic network over the workgroup's 256 threads, each ranked entropy is
+// turned into 2^-32-nat fixed point and prefix-summed in 64-bit integers
+// (exact, so independent of summation order), and a rank is accepted iff its
+// prefix test holds: the tests are monotone in the rank, so this equals the
+// sequential walk with its first failure ending it.
 #include "dg_device.h"
 #include "dg_kernels.h"
 #include "dgdenoise.h"
@@ -53,7 +52,8 @@ __device__ __forceinline__ void select_body(const float *__restrict__ entropy, c
                                             const float2 *__restrict__ pred, int32_t *__restrict__ pred_prev,
                                             int stable_rule) {
   __shared__ __align__(16) uint64_t keys[256];
-  __shared__ __align__(16) uint64_t fix[256];
+  __shared__ uint64_t fix[4];
+  __shared__ int acc_s[256];
   __shared__ float fmin_s[4], fmax_s[4], fsum_s[4];
   const int i = threadIdx.x;
 
@@ -73,32 +73,51 @@ __device__ __forceinline__ void select_body(const float *__restrict__ entropy, c
   const uint64_t key = walked ? (((uint64_t)__float_as_uint(h) << 32) | (uint32_t)i) : ~0ull;
   // h >= +0 or NaN, so the float bits order the finite entropies; NaN, inf
   // and absurd values sort after every finite one and end the walk
-  const bool finite = walked && h < 1048576.0f;
-  const uint64_t q = finite ? (uint64_t)((double)h * 4294967296.0) : 0ull;
-  keys[i] = key;
-  fix[i] = q;
-  __syncthreads();
+  acc_s[i] = 0;
 
-  // sum of the fixed-point entropies ranked below this position (only finite
-  // keys can be below a finite one)
-  // (eight keys per step, loaded before use; the padding keys ~0 are never below)
-  uint64_t below = 0;
-  for (int j0 = 0; j0 < N; j0 += 8) {
-    ulonglong2 kk[4], ff[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      kk[u] = reinterpret_cast<const ulonglong2 *>(keys + j0)[u];
-      ff[u] = reinterpret_cast<const ulonglong2 *>(fix + j0)[u];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      below += ff[u].x & (0ull - (uint64_t)(kk[u].x < key));  // masks, not branches
-      below += ff[u].y & (0ull - (uint64_t)(kk[u].y < key));
+  // Bitonic sort of the 256 keys, ascending, thread t ending with the key of
+  // rank t: exchanges at distances below 64 go through the wavefront's lane
+  // shuffles, the distances 64 and 128 through LDS.
+  uint64_t k = key;
+  for (int size = 2; size <= 256; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      uint64_t other;
+      if (stride >= 64) {
+        __syncthreads();  // the previous exchange's reads are done
+        keys[i] = k;
+        __syncthreads();
+        other = keys[i ^ stride];
+      } else {
+        other = shfl_xor_u64(k, stride);
+      }
+      // a lower-index element keeps the smaller key in an ascending run
+      const bool keep_min = ((i & stride) == 0) == ((i & size) == 0);
+      k = keep_min ? (k < other ? k : other) : (k < other ? other : k);
     }
   }
-  const uint64_t incl = below + q;
-  const uint64_t test = (rule == DG_ACCEPT_CUMSUM) ? incl : below;  // below = incl - this (the max so far)
-  const int acc_here = (finite && test <= limit) ? 1 : 0;
+  // rank t's fixed-point entropy and the inclusive prefix sum over ranks
+  // (64-bit integers: exact, the same in any order)
+  const float hr = __uint_as_float((uint32_t)(k >> 32));
+  const bool finite_r = k != ~0ull && hr < 1048576.0f;
+  const uint64_t qr = finite_r ? (uint64_t)((double)hr * 4294967296.0) : 0ull;
+  uint64_t incl = qr;
+  const int lane = i & 63, wave = i >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t v = shfl_up_u64(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) fix[wave] = incl;  // the wavefront's total
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) incl += fix[w];
+  // below = the entropies ranked before this one; with SUM_MINUS_MAX the
+  // test drops the current (largest so far) term.  The tests grow with the
+  // rank, so accepting every rank whose test holds is the sequential walk.
+  const uint64_t below = incl - qr;
+  const uint64_t test = (rule == DG_ACCEPT_CUMSUM) ? incl : below;
+  if (finite_r && test <= limit) acc_s[(uint32_t)k] = 1;  // finite keys carry their position
+  __syncthreads();
+  const int acc_here = acc_s[i];
 
   // re-noise, new canvas, flags
   int changed = 0, conf = 1, acc = 0, isnan_ = 0, pchanged = 0;
