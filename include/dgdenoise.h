@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define DG_ABI_VERSION 7
+#define DG_ABI_VERSION 8
 
 typedef enum {
   DG_OK = 0,
@@ -94,32 +94,33 @@ typedef enum { DG_CANDIDATE_ARGMAX = 0, DG_CANDIDATE_MULTINOMIAL = 1 } dg_candid
  *   the loop also stops when no [MASK] is left. */
 typedef enum { DG_SAMPLER_UNIFORM = 0, DG_SAMPLER_MASKED = 1 } dg_sampler;
 
-/* Storage of the packed table the two table-streaming contractions read
- * (DG_BF16 only; DG_F32 ignores it).  [P2] (local-deployment numbers) runs
- * the model quantised (NVFP4) to fit a consumer GPU; the MI355X counterparts
- * kept here are OCP fp8 e4m3 and block-scaled fp4 e2m1.
- * BF16: E_pack holds E and E^T in bf16.
- * FP8:  E_pack holds q = E * 2^table_exp and its transpose as fp8 e4m3
- *       (dg_pack_embedding rounds to nearest even and saturates at +-448).
- *       The kernels turn each fragment back into bf16 as q * 2^-table_exp,
- *       exactly, so the arithmetic is that of the bf16 path on a table whose
- *       entries are those values; E itself (row-major bf16: the embedding
- *       gathers and the exact top-logit recompute read it) must hold the
- *       same values, i.e. lie on that grid (E = fp8(E * 2^table_exp) *
- *       2^-table_exp), or the two copies disagree.  The table's bytes halve
- *       (E_pack 2 V d bytes instead of 4 V d).
- * FP4:  E_pack holds E and E^T as e2m1 codes (values 0, 0.5, 1, 1.5, 2, 3,
- *       4, 6 and their negatives) with one power-of-two scale byte u per
- *       32 x 32 block of E (value = code * 2^(u - 127), an E8M0 exponent as
- *       in the OCP microscaling formats, over a square block so that E and
- *       E^T hold the same values).  dg_pack_embedding sets u = floor(log2
- *       of the block's largest magnitude) - 2 + 127, clamped to [2, 252]
- *       (127 for an all-zero block), and rounds each value divided by the
- *       scale to the nearest code (ties to the even code, saturated at 6; a
- *       value rounded to zero is +0).  table_exp must be 0.  As with FP8 the
- *       kernels widen each fragment to bf16 exactly, and E must lie on that
- *       grid.  E_pack is V d + V d / 512 bytes (codes, then the scale bytes of
- *       E's blocks and of E^T's). */
+/* Storage of the packed table (DG_BF16 only; DG_F32 ignores it).  The
+ * library keeps E once: the LM head streams it as it is, the
+ * self-conditioning contraction streams the same bytes and transposes them
+ * in LDS, and the row gathers (embeddings, the exact top-token terms) read
+ * single rows of it.  [P2] (local-deployment numbers) runs the model
+ * quantised (NVFP4) to fit a consumer GPU; the MI355X counterparts kept here
+ * are OCP fp8 e4m3 and block-scaled fp4 e2m1.
+ * BF16: E_pack holds E in bf16, tiled (2 V d bytes).
+ * FP8:  E_pack holds q = E * 2^table_exp as fp8 e4m3, one byte per value in
+ *       the tiled order with 8-byte chunks (V d bytes; dg_pack_embedding
+ *       rounds to nearest even and saturates at +-448).  The kernels turn
+ *       each value back into bf16 as q * 2^-table_exp, exactly, so the
+ *       arithmetic is that of the bf16 path on a table whose entries are
+ *       those values: the model's table is E rounded to that grid
+ *       (fp8(E * 2^table_exp) * 2^-table_exp).
+ * FP4:  E_pack holds E as e2m1 codes (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+ *       their negatives) with one power-of-two scale byte u per 32 x 32 block
+ *       of E (value = code * 2^(u - 127), an E8M0 exponent as in the OCP
+ *       microscaling formats, over a square block so that the 8 values a
+ *       lane widens share one scale whether E is read along its rows or
+ *       along its columns).  dg_pack_embedding sets u = floor(log2 of the
+ *       block's largest magnitude) - 2 + 127, clamped to [2, 252] (127 for
+ *       an all-zero block), and rounds each value divided by the scale to the
+ *       nearest code (ties to the even code, saturated at 6; a value rounded
+ *       to zero is +0).  table_exp must be 0.  As with FP8 the kernels widen
+ *       each value to bf16 exactly: the model's table is E on that grid.
+ *       E_pack is V d / 2 + V d / 1024 bytes (codes, then the scale bytes). */
 typedef enum { DG_TABLE_BF16 = 0, DG_TABLE_FP8 = 1, DG_TABLE_FP4 = 2 } dg_table_format;
 
 /* What the adaptive stop's stability counter counts ([P3] §5.3 adaptive
@@ -162,11 +163,11 @@ typedef struct {
 } dg_config;
 
 /* Weights (device, dtype of the config, caller-owned, read-only).
- * E [V][d] is the token-embedding table, tied to the LM head ([P3] §4.1).
- * E_pack (DG_BF16; ignored for DG_F32) holds E twice in the tiled layout
- * below, written once by dg_pack_embedding(): E itself, then E^T (d rows,
- * V columns); the LM head streams the first, the self-conditioning
- * contraction the second.
+ * E [V][d] is the token-embedding table, tied to the LM head ([P3] §4.1):
+ * DG_F32 reads it row-major (fp32) in every step; DG_BF16 reads only E_pack,
+ * the one packed copy dg_pack_embedding() writes from it (tiled layout
+ * below, in the form of table_format), so E may be null in the weights a
+ * DG_BF16 step is given and its row-major copy freed once packed.
  * w_sc1 [F][d], w_sc2 [d][F]: self-conditioning FFN ([P3] §5.1).
  * wq [Hq*hd][d], wk/wv [Hkv*hd][d], wo [d][Hq*hd]: attention projections.
  * g_attn, g_final [d]: RMSNorm gains (pre-attention, pre-LM-head).
@@ -279,10 +280,10 @@ size_t dg_embedding_pack_bytes(const dg_config *cfg);
 size_t dg_probs_bytes(const dg_config *cfg);
 
 /* Writes E_pack (device, caller-allocated dg_embedding_pack_bytes(cfg)
- * bytes): E [V][d] in the tiled layout, followed by E^T [d][V] in the tiled
- * layout (padding rows zero).  DG_TABLE_BF16: a layout copy only, the same
- * values as E; DG_TABLE_FP8 / DG_TABLE_FP4: the rounded codes (and scale
- * bytes) described at dg_table_format.  Does nothing for DG_F32. */
+ * bytes) from E (row-major bf16 [V][d]): E in the tiled layout.
+ * DG_TABLE_BF16: a layout copy only, the same values as E; DG_TABLE_FP8 /
+ * DG_TABLE_FP4: the rounded codes (and scale bytes) described at
+ * dg_table_format.  Does nothing for DG_F32. */
 dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_pack, void *stream);
 
 /* [P3] §5.4 canvas initialisation: tokens[i] = the top log2(V) bits of word 0

@@ -38,7 +38,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert B.dg_abi_version() == 7
+    assert B.dg_abi_version() == 8
     for s in range(6):
         assert lib.dg_status_string(s)
 
@@ -149,6 +149,16 @@ def test_denoise_step_validation(lib):
     w2 = fake_weights()
     w2.E_pack = None
     assert call_step(cfg, w2, cache, cv, 1.0, 8.0, need) == B.DG_ERR_INVALID_ARG
+    # the bf16 step reads only the packed copy: a null row-major E passes
+    # validation (the call then fails only on the workspace, checked after)
+    w4 = fake_weights()
+    w4.E = None
+    assert call_step(cfg, w4, cache, cv, 1.0, 8.0, need - 1) == B.DG_ERR_WORKSPACE
+    # the fp32 step reads the row-major table
+    cfg1 = cfg_of(1)
+    w5 = fake_weights()
+    w5.E = None
+    assert call_step(cfg1, w5, cache, cv, 1.0, 8.0, B.dg_workspace_bytes(cfg1, 0)) == B.DG_ERR_INVALID_ARG
     cv2 = fake_canvas()
     cv2.status = None
     assert call_step(cfg, w, cache, cv2, 1.0, 8.0, need) == B.DG_ERR_INVALID_ARG
@@ -240,15 +250,15 @@ def test_other_entry_point_validation(lib):
 
 
 def test_pack_and_probs_bytes(lib):
-    """Packed table = E and E^T, each tiled (rows padded to 256); bf16 probs
-    are one tiled block of 256 rows; fp32 probs are row-major; unsupported
+    """Packed table = E once, tiled (rows padded to 256); bf16 probs are one
+    tiled block of 256 rows; fp32 probs are row-major; unsupported
     configurations give 0."""
     def tl(R, K):
         return (R + 255) // 256 * 256 * K
     for i in (2, 3):
         cfg = cfg_of(i)
         V, d = cfg.vocab, cfg.d_model
-        assert B.dg_embedding_pack_bytes(cfg) == 2 * (tl(V, d) + tl(d, V))
+        assert B.dg_embedding_pack_bytes(cfg) == 2 * tl(V, d)
         assert B.dg_probs_bytes(cfg) == 2 * tl(cfg.canvas_len, V)
     cfg = cfg_of(1)
     assert B.dg_embedding_pack_bytes(cfg) == 0
@@ -350,7 +360,7 @@ def test_fp8_table_config_and_sizes(lib):
         assert c8.table_format == B.DG_TABLE_FP8 and c8.table_exp == 8
         assert B.dg_validate_config(c8) == B.DG_OK
         assert 2 * B.dg_embedding_pack_bytes(c8) == B.dg_embedding_pack_bytes(cfg)
-        assert B.dg_embedding_pack_bytes(c8) == 2 * cfg.vocab * cfg.d_model
+        assert B.dg_embedding_pack_bytes(c8) == cfg.vocab * cfg.d_model
         assert B.dg_workspace_bytes(c8, 0) == B.dg_workspace_bytes(cfg, 0)
         assert B.dg_probs_bytes(c8) == B.dg_probs_bytes(cfg)
     c8 = cfg_of(2, table="fp8", table_exp=33)
@@ -384,7 +394,7 @@ def test_fp8_grid_quantiser():
 
 def test_fp4_table_config_and_sizes(lib):
     """The fp4 packed table: accepted for DG_BF16 with table_exp 0 (its
-    scales are per block); codes are half a byte per element and every
+    scales are per block); codes are half a byte per element of E and every
     1024 elements add one scale byte; same workspace and canvas buffers."""
     for i in (2, 3, 4):
         cfg = cfg_of(i)
@@ -392,7 +402,7 @@ def test_fp4_table_config_and_sizes(lib):
         assert c4.table_format == B.DG_TABLE_FP4 and c4.table_exp == 0
         assert B.dg_validate_config(c4) == B.DG_OK
         n = cfg.vocab * cfg.d_model  # d multiple of 256 here: no padding rows
-        assert B.dg_embedding_pack_bytes(c4) == n + 2 * n // 1024
+        assert B.dg_embedding_pack_bytes(c4) == n // 2 + n // 1024
         assert B.dg_workspace_bytes(c4, 0) == B.dg_workspace_bytes(cfg, 0)
         assert B.dg_probs_bytes(c4) == B.dg_probs_bytes(cfg)
     c4 = cfg_of(2, table="fp4")

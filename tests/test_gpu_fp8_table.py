@@ -49,9 +49,10 @@ def tiled8_positions(R: int, K: int) -> torch.Tensor:
 
 @pytest.mark.parametrize("exp", [8, 5])
 def test_pack_bytes_match_torch_e4m3(exp):
-    """dg_pack_embedding (fp8): both halves byte-exact against torch's
-    float8_e4m3fn of E * 2^exp (saturated at 448) in the tiled layout, for a
-    table on the grid and one that is not (rounding to nearest even)."""
+    """dg_pack_embedding (fp8): the one packed copy byte-exact against
+    torch's float8_e4m3fn of E * 2^exp (saturated at 448) in the tiled
+    layout, for a table on the grid and one that is not (rounding to
+    nearest even)."""
     V, d = 4096, 1024
     g = torch.Generator().manual_seed(11)
     E = (torch.randn(V, d, generator=g) * 0.08).to(torch.bfloat16)
@@ -63,9 +64,8 @@ def test_pack_bytes_match_torch_e4m3(exp):
     torch.cuda.synchronize()
     got = packed.cpu()
     q = (E.float() * 2.0 ** exp).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
-    want = torch.zeros(2 * V * d, dtype=torch.uint8)
+    want = torch.zeros(V * d, dtype=torch.uint8)
     want[tiled8_positions(V, d).reshape(-1)] = q.reshape(-1)
-    want[V * d + tiled8_positions(d, V).reshape(-1)] = q.t().contiguous().reshape(-1)
     assert torch.equal(got, want)
 
 

@@ -244,3 +244,21 @@ def test_copy_kernel():
     b = torch.zeros_like(a)
     B.dg_test_copy(a, b, n * 4)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("V,d", [(4096, 1024), (2048, 320)])
+def test_bf16_pack_is_the_one_tiled_copy(V, d):
+    """dg_pack_embedding (bf16): E_pack is E once in the documented tiled
+    layout (the host formula of rows_to_tiled), nothing else; d = 320 leaves
+    a partial set of 32-column slices per block row."""
+    g = torch.Generator().manual_seed(21)
+    E = (torch.randn(V, d, generator=g) * 0.05).to(torch.bfloat16)
+    cfg = B.make_config(W.config(2, V=V, d=d))
+    nb = B.dg_embedding_pack_bytes(cfg)
+    assert nb == V * d * 2
+    packed = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    B.dg_pack_embedding(cfg, E.cuda(), packed)
+    torch.cuda.synchronize()
+    got = packed.cpu().view(torch.bfloat16)
+    assert torch.equal(got, B.rows_to_tiled(E))
+    assert torch.equal(B.tiled_to_rows(got, V, d), E)

@@ -375,17 +375,26 @@ def tiled_to_rows(T: torch.Tensor, R: int, K: int) -> torch.Tensor:
 
 
 class DeviceWeights:
-    """Moves a workload's weights to the GPU and packs the tiled tables once."""
+    """Moves a workload's weights to the GPU and packs the table once.  The
+    bf16 configuration keeps only the packed copy of E (the row-major one is
+    freed once packed and the step is given a null E); the fp32 one keeps E
+    row-major."""
 
     def __init__(self, cfg: dg_config, inp: dict, device="cuda", stream=None):
         dt = torch_dtype(cfg)
         t = {k: inp[k].to(device=device, dtype=dt).contiguous()
              for k in ("E", "w1", "w2", "wq", "wk", "wv", "wo", "g_attn", "g_final", "mask_emb") if k in inp}
         nb = dg_embedding_pack_bytes(cfg)
-        t["E_pack"] = torch.empty(max(nb, 1), dtype=torch.uint8, device=device)
-        dg_pack_embedding(cfg, t["E"], t["E_pack"] if nb else None, stream)
+        if nb:
+            t["E_pack"] = torch.empty(nb, dtype=torch.uint8, device=device)
+            dg_pack_embedding(cfg, t["E"], t["E_pack"], stream)
+            if stream is None:
+                torch.cuda.current_stream(device).synchronize()
+            else:
+                stream.synchronize()
+            del t["E"]
         self.t = t
-        self.s = dg_weights(*(t[k].data_ptr() if k in t and (k != "E_pack" or nb) else None
+        self.s = dg_weights(*(t[k].data_ptr() if k in t else None
                               for k in ("E", "E_pack", "w1", "w2", "wq", "wk", "wv", "wo", "g_attn",
                                         "g_final", "mask_emb")))
 

@@ -72,30 +72,21 @@ dg_status check_config(const dg_config *c) {
 
 // Self-conditioning split of K = V over workgroups (bf16 path): about one
 // work item per CU.
-// The packed table (DG_BF16): E tiled ([V][d]) followed by E^T tiled ([d][V]).
-size_t pack_te_elems(const dg_config *c) { return dg::tl_elems(c->vocab, c->d_model); }
-size_t pack_elems(const dg_config *c) { return pack_te_elems(c) + dg::tl_elems(c->d_model, c->vocab); }
+// The packed table (DG_BF16): E [V][d] once, tiled, in the configured
+// form; both contractions and every row gather read it.
+size_t pack_elems(const dg_config *c) { return dg::tl_elems(c->vocab, c->d_model); }
 bool table_fp8(const dg_config *c) { return c->dtype == DG_BF16 && c->table_format == DG_TABLE_FP8; }
 bool table_fp4(const dg_config *c) { return c->dtype == DG_BF16 && c->table_format == DG_TABLE_FP4; }
-// fp4: the codes of E and E^T (half a byte per element), then the scale
-// bytes of E's blocks and of E^T's (one per 1024 elements)
+// fp4: the codes (half a byte per element), then the blocks' scale bytes
+// (one per 1024 elements)
 size_t pack4_codes(const dg_config *c) { return pack_elems(c) / 2; }
 size_t pack4_scales(const dg_config *c) { return pack_elems(c) / 1024; }
 
-// The packed table one streaming contraction reads: bf16 (elements), or a
-// quantised form (fp8: one byte per element, E = q * scale; fp4: codes and
-// block scale bytes).
-struct TableRef {
-  const uint16_t *bf;
-  dg::QTable qt;
-};
-// E (the LM head's operand) or, with transposed, E^T (the self-conditioning one)
-TableRef table_ref(const dg_config *c, const dg_weights *w, bool transposed) {
-  const size_t off = transposed ? pack_te_elems(c) : 0;
+dg::PackedTable packed_table(const dg_config *c, const dg_weights *w) {
   const uint8_t *p8 = static_cast<const uint8_t *>(w->E_pack);
-  if (table_fp8(c)) return {nullptr, {1, p8 + off, nullptr, std::ldexp(1.f, -c->table_exp)}};
-  if (table_fp4(c)) return {nullptr, {2, p8 + off / 2, p8 + pack4_codes(c) + off / 1024, 1.f}};
-  return {static_cast<const uint16_t *>(w->E_pack) + off, {0, nullptr, nullptr, 1.f}};
+  if (table_fp8(c)) return {dg::TF_FP8, p8, nullptr, std::ldexp(1.f, -c->table_exp), c->d_model};
+  if (table_fp4(c)) return {dg::TF_FP4, p8, p8 + pack4_codes(c), 1.f, c->d_model};
+  return {dg::TF_BF16, p8, nullptr, 1.f, c->d_model};
 }
 
 int selfcond_ksplit(const dg_config *c) {
@@ -263,10 +254,9 @@ dg::Epi epi_store(void *out, bool f32, int64_t rstride, int cdiv, int64_t chi) {
 }
 
 bool weights_ok(const dg_config *c, const dg_weights *w) {
-  if (!w || !w->E || !w->w_sc1 || !w->w_sc2 || !w->wq || !w->wk || !w->wv || !w->wo || !w->g_attn ||
-      !w->g_final)
+  if (!w || !w->w_sc1 || !w->w_sc2 || !w->wq || !w->wk || !w->wv || !w->wo || !w->g_attn || !w->g_final)
     return false;
-  if (c->dtype == DG_BF16 && !w->E_pack) return false;
+  if (c->dtype == DG_BF16 ? !w->E_pack : !w->E) return false;  // DG_BF16 reads only the packed copy
   if (c->sampler == DG_SAMPLER_MASKED && (!w->mask_emb || reinterpret_cast<uintptr_t>(w->mask_emb) % 16))
     return false;
   return true;
@@ -395,7 +385,7 @@ size_t dg_stats_bytes(const dg_config *cfg) {
 size_t dg_embedding_pack_bytes(const dg_config *cfg) {
   if (check_config(cfg) != DG_OK || cfg->dtype != DG_BF16) return 0;
   if (table_fp4(cfg)) return pack4_codes(cfg) + pack4_scales(cfg);
-  return pack_elems(cfg) * (table_fp8(cfg) ? 1 : 2);
+  return pack_elems(cfg) * (table_fp8(cfg) ? 1 : 2);  // fp8: a byte per element, bf16: two
 }
 
 size_t dg_probs_bytes(const dg_config *cfg) {
@@ -411,27 +401,15 @@ dg_status dg_pack_embedding(const dg_config *cfg, const void *E, void *E_pack, v
   if (!E || !E_pack) return DG_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int V = cfg->vocab, d = cfg->d_model;
-  if (table_fp8(cfg)) {  // q = E * 2^table_exp as fp8: E [V][d], then E^T [d][V]
-    uint8_t *q = static_cast<uint8_t *>(E_pack);
-    const float sc = std::ldexp(1.f, cfg->table_exp);
-    const uint16_t *Eb = static_cast<const uint16_t *>(E);
-    DG_TRY(dg::tile_fp8(Eb, V, d, d, false, sc, q, s));
-    DG_TRY(dg::tile_fp8(Eb, d, V, d, true, sc, q + pack_te_elems(cfg), s));
-    return DG_OK;
+  const uint16_t *Eb = static_cast<const uint16_t *>(E);
+  uint8_t *q = static_cast<uint8_t *>(E_pack);
+  if (table_fp8(cfg)) {  // q = E * 2^table_exp as fp8
+    DG_TRY(dg::tile_fp8(Eb, V, d, d, false, std::ldexp(1.f, cfg->table_exp), q, s));
+  } else if (table_fp4(cfg)) {  // e2m1 codes, then the 32 x 32 blocks' scale bytes
+    DG_TRY(dg::tile_fp4(Eb, V, d, d, false, q, q + pack4_codes(cfg), s));
+  } else {
+    DG_TRY(dg::tile_rows(Eb, V, d, d, static_cast<uint16_t *>(E_pack), s));
   }
-  if (table_fp4(cfg)) {  // e2m1 codes with 32 x 32 block scales: E [V][d], then E^T [d][V]
-    uint8_t *q = static_cast<uint8_t *>(E_pack), *sc = q + pack4_codes(cfg);
-    const uint16_t *Eb = static_cast<const uint16_t *>(E);
-    const size_t te = pack_te_elems(cfg);
-    DG_TRY(dg::tile_fp4(Eb, V, d, d, false, q, sc, s));
-    DG_TRY(dg::tile_fp4(Eb, d, V, d, true, q + te / 2, sc + te / 1024, s));
-    return DG_OK;
-  }
-  bf16 *te = static_cast<bf16 *>(E_pack), *tet = te + pack_te_elems(cfg);
-  // E^T row-major goes through the first region (V*d elements) as scratch
-  DG_TRY(dg::transpose<bf16>(static_cast<const bf16 *>(E), V, d, te, V, s));
-  DG_TRY(dg::tile_rows(te, d, V, V, tet, s));
-  DG_TRY(dg::tile_rows(static_cast<const bf16 *>(E), V, d, d, te, s));
   return DG_OK;
 }
 
@@ -469,11 +447,11 @@ dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cac
   float *nrm = reinterpret_cast<float *>(base + L.p_nrm);
 
   if (bf) {  // nrm holds the split pair
-    DG_TRY(dg::gather_rows<bf16>(static_cast<const bf16 *>(w->E), tokens, n, d, V, mask_row<bf16>(cfg, w), x, s));
+    DG_TRY(dg::gather_rows(packed_table(cfg, w), tokens, n, V, mask_row<uint16_t>(cfg, w), x, s));
     DG_TRY(dg::rmsnorm_rows<bf16>(x, static_cast<const bf16 *>(w->g_attn), n, d, cfg->rms_eps, nullptr, nullptr,
                                   reinterpret_cast<bf16 *>(nrm), s));
   } else {
-    DG_TRY(dg::gather_rows<float>(static_cast<const float *>(w->E), tokens, n, d, V, mask_row<float>(cfg, w), x, s));
+    DG_TRY(dg::gather_rows(static_cast<const float *>(w->E), tokens, n, d, V, mask_row<float>(cfg, w), x, s));
     DG_TRY(dg::rmsnorm_rows<float>(x, static_cast<const float *>(w->g_attn), n, d, cfg->rms_eps, nrm, nullptr,
                                    nullptr, s));
   }
@@ -575,11 +553,9 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
   // by the FFN's output merge (its residual), so h0 is written once
   const bool fused_embed = bf && cv->has_prev;
   if (bf && !fused_embed)
-    DG_TRY(dg::gather_rows<bf16>(static_cast<const bf16 *>(w->E), cv->tokens, N, d, V, mask_row<bf16>(cfg, w), h0,
-                                 s));
+    DG_TRY(dg::gather_rows(packed_table(cfg, w), cv->tokens, N, V, mask_row<uint16_t>(cfg, w), h0, s));
   else if (!bf)
-    DG_TRY(dg::gather_rows<float>(static_cast<const float *>(w->E), cv->tokens, N, d, V, mask_row<float>(cfg, w),
-                                  h0, s));
+    DG_TRY(dg::gather_rows(static_cast<const float *>(w->E), cv->tokens, N, d, V, mask_row<float>(cfg, w), h0, s));
   if (cv->has_prev) {
     if (bf) {
       const int ks = selfcond_ksplit(cfg);
@@ -587,15 +563,14 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
       if (sc_mode != SC_DONE) {
         ProfScope ps(g_prof_sc, s, profile);
         const dg::SelfcondGuard guard{sc_mode == SC_AHEAD ? cv->status : nullptr, stable_steps};
-        const TableRef tt = table_ref(cfg, w, true);
         dg::EsCanvasesIn cin{};
         cin.probs[0] = static_cast<const uint16_t *>(cv->probs);
         cin.shift[0] = shift;
-        DG_TRY(dg::selfcond_bf16_batch(cin, 1, tt.bf, N, d, V, true, part, ks, s, guard, tt.qt));
+        DG_TRY(dg::selfcond_bf16_batch(cin, 1, packed_table(cfg, w), N, d, V, true, part, ks, s, guard));
       }
       if (sc_mode == SC_AHEAD) return DG_OK;
       DG_TRY(dg::selfcond_reduce(part, ks, N, d, top, static_cast<const uint16_t *>(cv->probs), V, rscale, shift,
-                                 static_cast<const uint16_t *>(w->E), sc, sc_s, s));
+                                 packed_table(cfg, w), sc, sc_s, s));
     } else {
       dg::GemmShapeF32 g{static_cast<const float *>(cv->probs), V, 1, static_cast<const float *>(w->E), 1, d,
                          N, d, V, nullptr, 0};
@@ -609,10 +584,9 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     dg::Epi ea = epi_store(h0, true, d, d, 0);
     if (fused_embed) {  // h0 = E[tokens] + W2 G
       ea.kind = dg::EPI_ADD_ROW;
-      ea.gtab = static_cast<const uint16_t *>(w->E);
+      ea.gtab = packed_table(cfg, w);
       ea.gtok = cv->tokens;
       ea.gV = V;
-      ea.gld = d;
       ea.gmask = mask_row<uint16_t>(cfg, w);
     } else {
       ea.kind = dg::EPI_ADD;
@@ -675,11 +649,10 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
   if (bf) {
     {
       ProfScope ps(g_prof_lm, s, profile);
-      const TableRef te = table_ref(cfg, w, false);
       dg::EsCanvases ec{};
       ec.probs[0] = static_cast<uint16_t *>(cv->probs);
       ec.tile_stats[0] = tstats;
-      DG_TRY(dg::lm_head_bf16_batch(nrm16, 1, N, d, te.bf, V, inv_T, ec, dump ? logits : nullptr, s, te.qt));
+      DG_TRY(dg::lm_head_bf16_batch(nrm16, 1, N, d, packed_table(cfg, w), V, inv_T, ec, dump ? logits : nullptr, s));
     }
     // the numerators stay as stored: the next step's contraction applies the
     // power-of-two tile exponents and the row factor (the batch launch with
@@ -691,13 +664,13 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
     rc.row_scale[0] = rscale;
     rc.shift[0] = shift;
     rc.top[0] = top;
-    DG_TRY(dg::row_combine_batch(rc, 1, N, ntiles, inv_T, nrm, static_cast<const uint16_t *>(w->E), d, s));
+    DG_TRY(dg::row_combine_batch(rc, 1, N, ntiles, inv_T, nrm, packed_table(cfg, w), s));
   } else {
     dg::GemmShapeF32 g{nrm, d, 1, static_cast<const float *>(w->E), d, 1, N, V, d, nullptr, 0};
     DG_TRY(dg::gemm_f32(g, epi_store(logits, true, V, V, 0), s));
     DG_TRY(dg::tile_stats_f32(logits, N, V, inv_T, static_cast<float *>(cv->probs), tstats, s));
     DG_TRY(dg::row_combine(tstats, N, ntiles, inv_T, cv->entropy, cv->argmax, tscale, nullptr, nullptr, nullptr,
-                           nullptr, d, top, s));
+                           dg::PackedTable{}, top, s));
     DG_TRY(dg::normalize_probs_f32(static_cast<float *>(cv->probs), tscale, N, V, s));
   }
   // [P3] §5.3 multinomial candidates, drawn from the probabilities as kept
@@ -762,16 +735,15 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
   int32_t *tok = reinterpret_cast<int32_t *>(base + L.tok);
   const StatsLayout SL = stats_layout(cfg);
   auto st_of = [&](int b, size_t off) { return static_cast<char *>(cvs[b].stats) + off; };
-  const uint16_t *Eb = static_cast<const uint16_t *>(w->E);
+  const dg::PackedTable tab = packed_table(cfg, w);
 
   dg::TokenPtrs tp{};
   for (int b = 0; b < B; ++b) tp.p[b] = cvs[b].tokens;
   DG_TRY(dg::stack_tokens(tp, B, N, tok, s));
   if (cvs[0].has_prev) {
-    // S = p_prev E for every canvas in one pass over E^T, then the merges
+    // S = p_prev E for every canvas in one pass over the table, then the merges
     const int ks = selfcond_ksplit(cfg);
     float *part = reinterpret_cast<float *>(base + L.sc_part);
-    const TableRef tt = table_ref(cfg, w, true);
     dg::EsCanvasesIn cin{};
     for (int b = 0; b < B; ++b) {
       cin.probs[b] = static_cast<const uint16_t *>(cvs[b].probs);
@@ -779,13 +751,12 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
     }
     {
       ProfScope ps(g_prof_sc, s);
-      DG_TRY(dg::selfcond_bf16_batch(cin, B, tt.bf, N, d, V, true, part, ks, s, dg::SelfcondGuard{nullptr, 0},
-                                     tt.qt));
+      DG_TRY(dg::selfcond_bf16_batch(cin, B, tab, N, d, V, true, part, ks, s));
     }
     for (int b = 0; b < B; ++b)
       DG_TRY(dg::selfcond_reduce(part + (size_t)b * ks * N * d, ks, N, d,
                                  reinterpret_cast<const float2 *>(st_of(b, SL.top)), cin.probs[b], V,
-                                 reinterpret_cast<const float *>(st_of(b, SL.rscale)), cin.shift[b], Eb,
+                                 reinterpret_cast<const float *>(st_of(b, SL.rscale)), cin.shift[b], tab,
                                  sc + (size_t)b * N * d, sc_s + (size_t)b * N * d, s, (int64_t)BN * d));
     dg::Epi eg = epi_store(G, false, F, F, 0);
     eg.kind = dg::EPI_GELU;
@@ -793,14 +764,13 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
     DG_TRY(proj1(cfg, sc_s, BN, d, w->w_sc1, F, eg, gpart, s));
     dg::Epi ea = epi_store(h0, true, d, d, 0);  // h0 = E[tokens] + W2 G
     ea.kind = dg::EPI_ADD_ROW;
-    ea.gtab = Eb;
+    ea.gtab = tab;
     ea.gtok = tok;
     ea.gV = V;
-    ea.gld = d;
     ea.gmask = mask_row<uint16_t>(cfg, w);
     DG_TRY(proj1_norm(cfg, G, BN, F, w->w_sc2, d, ea, gpart, w->g_attn, nullptr, nullptr, nrm_s, s));
   } else {
-    DG_TRY(dg::gather_rows<bf16>(static_cast<const bf16 *>(w->E), tok, BN, d, V, mask_row<bf16>(cfg, w), h0, s));
+    DG_TRY(dg::gather_rows(tab, tok, BN, V, mask_row<uint16_t>(cfg, w), h0, s));
     DG_TRY(dg::rmsnorm_rows<bf16>(h0, static_cast<const bf16 *>(w->g_attn), BN, d, cfg->rms_eps, nullptr, nullptr,
                                   nrm_s, s));
   }
@@ -851,8 +821,7 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
       ec.tile_stats[b] = reinterpret_cast<float4 *>(st_of(b, SL.tstats));
     }
     ProfScope ps(g_prof_lm, s);
-    const TableRef te = table_ref(cfg, w, false);
-    DG_TRY(dg::lm_head_bf16_batch(nrm16, B, N, d, te.bf, V, inv_T, ec, nullptr, s, te.qt));
+    DG_TRY(dg::lm_head_bf16_batch(nrm16, B, N, d, tab, V, inv_T, ec, nullptr, s));
   }
   {  // row statistics of every canvas in one launch, then its candidates, then one selection launch
     dg::RowCombineBatch rc{};
@@ -876,7 +845,7 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
       sel.pred[b] = reinterpret_cast<const float2 *>(st_of(b, SL.top));
       sel.pred_prev[b] = reinterpret_cast<int32_t *>(st_of(b, SL.pred));
     }
-    DG_TRY(dg::row_combine_batch(rc, B, N, ntiles, inv_T, nrm, Eb, d, s));
+    DG_TRY(dg::row_combine_batch(rc, B, N, ntiles, inv_T, nrm, tab, s));
     if (cfg->candidate_rule == DG_CANDIDATE_MULTINOMIAL)
       for (int b = 0; b < B; ++b) {
         dg_canvas *cv = &cvs[b];
@@ -1132,15 +1101,14 @@ static hipError_t selfcond_vector(const dg_config *cfg, const dg_weights *w, con
   const int N = cfg->canvas_len, V = cfg->vocab, d = cfg->d_model;
   if (cfg->dtype == DG_BF16) {
     const int ks = selfcond_ksplit(cfg);
-    const TableRef tt = table_ref(cfg, w, true);
+    const dg::PackedTable tab = packed_table(cfg, w);
     dg::EsCanvasesIn cin{};
     cin.probs[0] = static_cast<const uint16_t *>(probs);
     cin.shift[0] = shift;
-    hipError_t e = dg::selfcond_bf16_batch(cin, 1, tt.bf, N, d, V, true, part, ks, s, dg::SelfcondGuard{nullptr, 0},
-                                           tt.qt);
+    hipError_t e = dg::selfcond_bf16_batch(cin, 1, tab, N, d, V, true, part, ks, s);
     if (e != hipSuccess) return e;
-    return dg::selfcond_reduce(part, ks, N, d, top, static_cast<const uint16_t *>(probs), V, rscale, shift,
-                               static_cast<const uint16_t *>(w->E), S, nullptr, s);
+    return dg::selfcond_reduce(part, ks, N, d, top, static_cast<const uint16_t *>(probs), V, rscale, shift, tab, S,
+                               nullptr, s);
   }
   dg::GemmShapeF32 g{static_cast<const float *>(probs), V, 1, static_cast<const float *>(w->E), 1, d, N, d, V,
                      nullptr, 0};

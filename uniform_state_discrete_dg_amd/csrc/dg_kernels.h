@@ -8,6 +8,7 @@
 #include <atomic>
 
 #include "dgdenoise.h"
+#include "dg_tiled.h"
 
 namespace dg {
 
@@ -33,9 +34,9 @@ hipError_t once_per_device(std::atomic<uint64_t> &done, F &&set_up) {
 // layouts of Q/K/V ([head][row][hd]: cdiv = hd, chi = head stride).
 // A bf16 output with lo_off != 0 is a split pair: hi = bf16(v) at the index,
 // lo = bf16(v - hi) at index + lo_off (the operand format of SplitGemm).
-// EPI_ADD_ROW: out = acc + gtab[tok[row]][col] (bf16 table rows, leading
-// dimension gld, token ids clamped to [0, gV)): a residual gathered on the fly;
-// with gmask (the [MASK] row of the masked sampler) ids >= gV read gmask.
+// EPI_ADD_ROW: out = acc + E[tok[row]][col] (rows of the packed table gtab,
+// token ids clamped to [0, gV)): a residual gathered on the fly; with gmask
+// (the [MASK] row of the masked sampler, bf16) ids >= gV read gmask.
 enum EpiKind { EPI_STORE = 0, EPI_GELU = 1, EPI_ADD = 2, EPI_ADD_ROW = 3 };
 struct Epi {
   int kind;
@@ -46,20 +47,10 @@ struct Epi {
   int64_t chi;
   const float *resid;    // EPI_ADD: out = resid + acc (f32, same index)
   int64_t lo_off;        // bf16 output: offset of the lo term (0: plain bf16)
-  const uint16_t *gtab;  // EPI_ADD_ROW
+  PackedTable gtab;  // EPI_ADD_ROW
   const int32_t *gtok;
   int gV;
-  int64_t gld;
   const uint16_t *gmask;  // EPI_ADD_ROW: row of token ids >= gV (nullable)
-};
-
-// Operands of a table-streaming contraction in the tiled layout of
-// dg_tiled.h: A = one block of (up to) 256 canvas rows, B = ceil(N/256)
-// blocks of table rows, both with K columns.  C[M][N] = A B^T.
-struct TiledGemm {
-  const uint16_t *A;
-  const uint16_t *B;
-  int M, N, K;
 };
 
 // fp32 activation x bf16 weight GEMM on the bf16 MFMA.  The activation
@@ -119,8 +110,6 @@ struct SelfcondGuard {
            status[DG_ST_MASKED] == 0;
   }
 };
-hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partials, int ksplit, hipStream_t s,
-                         SelfcondGuard guard = SelfcondGuard{nullptr, 0});
 // fp32 GEMM on the fp32 MFMA: C[m][n] = sum_k A[m*sam + k*sak] * B[n*sbn + k*sbk].
 struct GemmShapeF32 {
   const float *A;
@@ -140,48 +129,33 @@ hipError_t gemm_f32(const GemmShapeF32 &g, const Epi &e, hipStream_t s);
 // f_t = 2^(m_t log2e - r_t), r_t = ceil(m_t log2e): numerators relative to
 // a power-of-two reference 2^r_t.
 // tile_stats: float4 [M][V/64] = (zmax, l, s, argmax as int bits).
-// A_tiled: the normalised canvas rows (M <= 256, one tiled block); E_tiled:
-// E in the tiled layout; probs_tiled: the numerators, tiled ([M][V]).
-hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E_tiled, int V, float inv_T,
-                        uint16_t *probs_tiled, float4 *tile_stats, float *logits_dump, hipStream_t s);
 // A batch of B canvases of N rows each (B * N rows stacked in A_tiled, row r
-// = row r % N of canvas r / N): canvas c's numerators and statistics go to
-// cv.probs[c] and cv.tile_stats[c].  Each row's results are those of the
-// single-canvas launch bit for bit.
+// = row r % N of canvas r / N; the normalised rows, tiled): canvas c's
+// numerators (tiled [N][V]) and statistics go to cv.probs[c] and
+// cv.tile_stats[c].  Each row's results are those of the single-canvas
+// launch bit for bit.  tab: the packed table E [V][K] (tab.d == K).
 constexpr int ES_MAX_BATCH = DG_MAX_BATCH;
 struct EsCanvases {
   uint16_t *probs[ES_MAX_BATCH];
   float4 *tile_stats[ES_MAX_BATCH];
 };
-// A quantised form of the table operand (dg_tiled.h): tf = 1, fp8 e4m3
-// codes q in the 8-byte-chunk layout with E = q * scale; tf = 2, fp4 e2m1
-// codes in the 4-byte-chunk layout with one scale byte per 32 x 32 block
-// at s4 (scale is unused).  tf = 0: none (the bf16 operand is used).
-struct QTable {
-  int tf;
-  const uint8_t *q;
-  const uint8_t *s4;
-  float scale;
-};
-// The table comes in one of three forms: E_tiled (bf16) or a quantised
-// form qt; exactly one is given (E_tiled non-null or qt.tf != 0).
-hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, const uint16_t *E_tiled, int V,
-                              float inv_T, const EsCanvases &cv, float *logits_dump, hipStream_t s,
-                              const QTable &qt = QTable{0, nullptr, nullptr, 1.f});
-// The self-conditioning contraction of B canvases at once: canvas c's
-// operand cin.probs[c] (its exponents cin.shift[c] when scaled), partials at
-// partials + c * ksplit * M * N (the single-canvas layout per canvas).
-// Canvases of M <= 128 rows are paired in one 256-row block (the second
-// canvas's rows read from its own buffers).  Each row's partials are those
-// of the single-canvas launch bit for bit (same K ranges, same MFMA order).
+hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, const PackedTable &tab, int V,
+                              float inv_T, const EsCanvases &cv, float *logits_dump, hipStream_t s);
+// The self-conditioning contraction S = P E of B canvases at once, K = V:
+// canvas c's operand cin.probs[c] (its exponents cin.shift[c] when scaled),
+// partials at partials + c * ksplit * M * N (the single-canvas layout per
+// canvas).  tab: the same packed table E [K][N] the LM head reads
+// (tab.d == N), transposed in LDS.  Canvases of M <= 128 rows are paired in
+// one 256-row block (the second canvas's rows read from its own buffers).
+// Each row's partials are those of the single-canvas launch bit for bit
+// (same K ranges, same MFMA order).
 struct EsCanvasesIn {
   const uint16_t *probs[ES_MAX_BATCH];
   const uint8_t *shift[ES_MAX_BATCH];
 };
-hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *Et_tiled, int M, int N, int K,
+hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const PackedTable &tab, int M, int N, int K,
                                bool scaled, float *partials, int ksplit, hipStream_t s,
-                               SelfcondGuard guard = SelfcondGuard{nullptr, 0},
-                               const QTable &qt = QTable{0, nullptr, nullptr, 1.f});
+                               SelfcondGuard guard = SelfcondGuard{nullptr, 0});
 // Same statistics from fp32 logits already in memory (fp32 path).
 hipError_t tile_stats_f32(const float *logits, int M, int V, float inv_T, float *probs,
                           float4 *tile_stats, hipStream_t s);
@@ -198,12 +172,13 @@ struct DrawArgs {
 // tile_scale[row][t] = exp(m_t - M_row) / L_row.  shift given (numerators
 // relative to 2^r_t, M <= 256): p = stored * 2^-shift[t][row] * row_scale[row]
 // and tile_scale (nullable) = 2^-shift * row_scale.  With n2 (fp32 [M][d],
-// d <= 4096) and E given, the argmax token's logit is recomputed exactly and
-// top[row] = (argmax as int bits, its exact probability).  cand receives
-// the argmax (the candidate token unless a multinomial draw follows).
+// d <= 4096, the packed table E [V][d]) given, the argmax token's logit is
+// recomputed exactly and top[row] = (argmax as int bits, its exact
+// probability).  cand receives the argmax (the candidate token unless a
+// multinomial draw follows).
 hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,
                        int32_t *cand, float *tile_scale, float *row_scale, uint8_t *shift, const float *n2,
-                       const uint16_t *E, int d, float2 *top, hipStream_t s);
+                       const PackedTable &E, float2 *top, hipStream_t s);
 // The row combine of B canvases (bf16 path, N <= 256 rows each) in one
 // launch: canvas c's statistics, entropy, candidates, row factors, exponents
 // and top tokens at the c-th pointers; n2 the stacked normalised rows
@@ -218,7 +193,7 @@ struct RowCombineBatch {
   float2 *top[ES_MAX_BATCH];
 };
 hipError_t row_combine_batch(const RowCombineBatch &bt, int B, int N, int ntiles, float inv_T, const float *n2,
-                             const uint16_t *E, int d, hipStream_t s);
+                             const PackedTable &E, hipStream_t s);
 // Multinomial draw of the candidate tokens (two Gumbel-max levels over the
 // tile statistics and the stored weights, dg_device.h), run once the step's
 // probabilities are final; cand holds the argmax and keeps it for a row with
@@ -257,9 +232,12 @@ void attention_plan(int nq, int Hq, int nk, int *splits, int *keys_per_split);
 // Small ops.
 // out[i] = E[tokens[i]] (fp32 [n][d]); ids clamped to [0, V), except that with
 // mask_row (the [MASK] embedding, id V, masked sampler) ids >= V read mask_row.
-template <typename T>
-hipError_t gather_rows(const T *E, const int32_t *tokens, int n, int d, int V, const T *mask_row, float *out,
-                       hipStream_t s);
+// The fp32 path's row-major table, and the packed table of the bf16 path
+// (mask_row bf16, 8-byte aligned; d % 4 == 0).
+hipError_t gather_rows(const float *E, const int32_t *tokens, int n, int d, int V, const float *mask_row,
+                       float *out, hipStream_t s);
+hipError_t gather_rows(const PackedTable &E, const int32_t *tokens, int n, int V, const uint16_t *mask_row,
+                       float *out, hipStream_t s);
 // out (fp32 [n][d], nullable), out_tiled (bf16, tiled block(s) of the
 // rows, the rows past n up to the block end written as zeros; nullable)
 // and/or out_split (split pair [n][d], lo term at + n * d; nullable).
@@ -274,7 +252,8 @@ hipError_t rmsnorm_rows(const float *x, const T *g, int n, int d, float eps, flo
 // term at + lo_off (0: + N * d).
 hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top,
                            const uint16_t *probs_tiled, int V, const float *row_scale, const uint8_t *shift,
-                           const uint16_t *E, float *out, uint16_t *out_split, hipStream_t s, int64_t lo_off = 0);
+                           const PackedTable &E, float *out, uint16_t *out_split, hipStream_t s,
+                           int64_t lo_off = 0);
 // The token ids of B canvases (src.p[c], N each) copied into one array
 // out[B * N], canvas after canvas.
 struct TokenPtrs {

@@ -50,16 +50,18 @@ __host__ __device__ inline int64_t tl8_index(int row, int col, int K) {
 
 // The fp4 form (e2m1, two values per byte): the same blocks of 256 rows x 32
 // columns, 4 KB each, with 4-byte chunks of 8 values: chunk p holds
-// X[256 b + r][32 s + 8 c .. + 7], r = p / 4, c = (p % 4) ^ ((r / 8) % 4),
+// X[256 b + r][32 s + 8 c .. + 7], r = p / 4, c = (p % 4) ^ (2 (bit 4 of r)),
 // value 8 c + 2 i in the low nibble of byte i and 8 c + 2 i + 1 in its high
-// nibble.  A fragment is one 4-byte LDS read per lane; its 32 rows x 2 chunk
-// columns fall on 64 distinct banks.  Each 32 x 32 sub-block (rows 32 g ..
-// 32 g + 31 of the block) has one scale byte u (value = code * 2^(u - 127)),
-// stored apart from the codes: byte g of 8 per block, blocks in the same
-// order.
+// nibble.  The swizzle keeps chunks 2q and 2q + 1 adjacent and in order, so
+// 16 consecutive values of a row are one aligned 8-byte word (the unit of
+// the transposing LDS read); a row-fragment read (4 bytes per lane, 32 rows
+// x 2 chunk columns) falls on 64 distinct banks.  Each 32 x 32 sub-block
+// (rows 32 g .. 32 g + 31 of the block) has one scale byte u (value = code *
+// 2^(u - 127)), stored apart from the codes: byte g of 8 per block, blocks
+// in the same order.
 constexpr int TL4_BYTES = 4096;  // bytes of codes per block
 constexpr int TL4_SCALES = 8;    // scale bytes per block
-__host__ __device__ inline int tl4_pos(int r, int c) { return r * 4 + (c ^ ((r >> 3) & 3)); }
+__host__ __device__ inline int tl4_pos(int r, int c) { return r * 4 + (c ^ (((r >> 4) & 1) << 1)); }
 // byte holding X[row][col] (low nibble for even col) and that value's scale byte
 __host__ __device__ inline int64_t tl4_index(int row, int col, int K) {
   const int b = row >> 8, r = row & 255, s = col >> 5, k = col & 31;
@@ -68,5 +70,47 @@ __host__ __device__ inline int64_t tl4_index(int row, int col, int K) {
 __host__ __device__ inline int64_t tl4_scale_index(int row, int col, int K) {
   return ((int64_t)(row >> 8) * (K >> 5) + (col >> 5)) * TL4_SCALES + ((row & 255) >> 5);
 }
+
+// The tied table E [V][d] as the library keeps it: one copy, in one of the
+// three tiled forms.  The LM head streams it as it is; the self-conditioning
+// contraction streams the same bytes and transposes them in LDS; the row
+// gathers (embeddings, the exact top-token terms) read single rows.
+enum TableForm { TF_BF16 = 0, TF_FP8 = 1, TF_FP4 = 2 };
+struct PackedTable {
+  int tf;             // TableForm
+  const void *p;      // bf16 values, fp8 codes or fp4 codes (tiled)
+  const uint8_t *s4;  // TF_FP4: the blocks' scale bytes
+  float scale;        // TF_FP8: value = code * scale
+  int d;              // columns
+};
+
+#if defined(__HIPCC__)
+// 4 consecutive values of one row (col % 4 == 0) as floats, exactly.
+__device__ inline float4 table_get4(const PackedTable &t, int row, int col) {
+  uint32_t w0, w1;  // two packed bf16 pairs
+  if (t.tf == TF_BF16) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(t.p) + tl_index(row, col, t.d));
+    w0 = v.x;
+    w1 = v.y;
+  } else if (t.tf == TF_FP8) {
+    const uint32_t q = *reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(t.p) + tl8_index(row, col, t.d));
+    w0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, t.scale, false));
+    w1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, t.scale, true));
+  } else {
+    const uint32_t q = *reinterpret_cast<const uint16_t *>(static_cast<const uint8_t *>(t.p) + tl4_index(row, col, t.d));
+    const float sc = __uint_as_float((uint32_t)t.s4[tl4_scale_index(row, col, t.d)] << 23);
+    w0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 0));
+    w1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1));
+  }
+  return make_float4(__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xffff0000u), __uint_as_float(w1 << 16),
+                     __uint_as_float(w1 & 0xffff0000u));
+}
+// One value.
+__device__ inline float table_get(const PackedTable &t, int row, int col) {
+  const float4 v = table_get4(t, row, col & ~3);
+  const int k = col & 3;
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+#endif
 
 }  // namespace dg

@@ -44,38 +44,41 @@ __global__ void gather_kernel(const T *__restrict__ E, const int32_t *__restrict
   for (int k = threadIdx.x; k < d; k += blockDim.x) out[(int64_t)i * d + k] = Elem<T>::load(row, k);
 }
 
-// bf16 rows, d % 8 == 0: eight values (16 bytes) per thread
-__global__ void gather8_kernel(const bf16 *__restrict__ E, const int32_t *__restrict__ tokens, int d, int V,
-                               const bf16 *__restrict__ mask_row, float *__restrict__ out) {
-  const int i = blockIdx.x;
-  const uint4 *src = reinterpret_cast<const uint4 *>(embed_row(E, tokens[i], d, V, mask_row));
+hipError_t gather_rows(const float *E, const int32_t *tokens, int n, int d, int V, const float *mask_row,
+                       float *out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_kernel<float>, dim3(n), dim3(256), 0, s, E, tokens, d, V, mask_row, out);
+  return hipGetLastError();
+}
+
+// Rows of the packed table (any form), four values per thread.
+__global__ void gather_table_kernel(PackedTable E, const int32_t *__restrict__ tokens, int V,
+                                    const bf16 *__restrict__ mask_row, float *__restrict__ out) {
+  const int i = blockIdx.x, d = E.d;
+  int t = tokens[i];
+  const bool masked = t >= V && mask_row;
+  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
   float4 *dst = reinterpret_cast<float4 *>(out + (int64_t)i * d);
-  for (int k = threadIdx.x; k < d / 8; k += blockDim.x) {
-    const uint4 v = src[k];
-    dst[2 * k] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                             __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
-    dst[2 * k + 1] = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xffff0000u),
-                                 __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xffff0000u));
+  for (int k = threadIdx.x; k < d / 4; k += blockDim.x) {
+    float4 v;
+    if (masked) {
+      const uint2 r = reinterpret_cast<const uint2 *>(mask_row)[k];
+      v = make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
+                      __uint_as_float(r.y & 0xffff0000u));
+    } else {
+      v = table_get4(E, t, 4 * k);
+    }
+    dst[k] = v;
   }
 }
 
-template <typename T>
-hipError_t gather_rows(const T *E, const int32_t *tokens, int n, int d, int V, const T *mask_row, float *out,
-                       hipStream_t s) {
+hipError_t gather_rows(const PackedTable &E, const int32_t *tokens, int n, int V, const uint16_t *mask_row,
+                       float *out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  if constexpr (sizeof(T) == 2) {
-    if (d % 8 == 0 && (reinterpret_cast<uintptr_t>(mask_row) & 15) == 0) {
-      hipLaunchKernelGGL(gather8_kernel, dim3(n), dim3(256), 0, s, E, tokens, d, V, mask_row, out);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL(gather_kernel<T>, dim3(n), dim3(256), 0, s, E, tokens, d, V, mask_row, out);
+  if (E.d % 4 || (reinterpret_cast<uintptr_t>(mask_row) & 7)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_table_kernel, dim3(n), dim3(256), 0, s, E, tokens, V, mask_row, out);
   return hipGetLastError();
 }
-template hipError_t gather_rows<float>(const float *, const int32_t *, int, int, int, const float *, float *,
-                                       hipStream_t);
-template hipError_t gather_rows<bf16>(const bf16 *, const int32_t *, int, int, int, const bf16 *, float *,
-                                      hipStream_t);
 
 // RMSNorm: out = x / sqrt(mean(x^2) + eps) * g, written in fp32 and/or, when
 // requested, rounded to bf16 (the operand of the tied LM head) and as a
@@ -129,8 +132,8 @@ template hipError_t rmsnorm_rows<bf16>(const float *, const bf16 *, int, int, fl
 __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int ksplit, int N, int d,
                                        const float2 *__restrict__ top, const bf16 *__restrict__ probs, int V,
                                        const float *__restrict__ row_scale, const uint8_t *__restrict__ shift,
-                                       const bf16 *__restrict__ E, float *__restrict__ out,
-                                       bf16 *__restrict__ out_split, int64_t lo_off) {
+                                       PackedTable E, float *__restrict__ out, bf16 *__restrict__ out_split,
+                                       int64_t lo_off) {
   // one thread per 4 consecutive columns of one row; d % 4 == 0
   const int row = blockIdx.y;
   const int k = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -154,11 +157,11 @@ __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int kspli
     int bits = probs[tl_index(row, a, V)];
     if (shift) bits = max(bits - ((int)shift[(int64_t)(a >> 6) * 256 + row] << 7), 0);
     const float c = tp.y - g * bf16_to_f32((bf16)bits);
-    const bf16 *e = E + (int64_t)a * d + k;
-    acc.x += c * bf16_to_f32(e[0]);
-    acc.y += c * bf16_to_f32(e[1]);
-    acc.z += c * bf16_to_f32(e[2]);
-    acc.w += c * bf16_to_f32(e[3]);
+    const float4 e = table_get4(E, a, k);
+    acc.x += c * e.x;
+    acc.y += c * e.y;
+    acc.z += c * e.z;
+    acc.w += c * e.w;
   }
   *reinterpret_cast<float4 *>(out + i) = acc;
   if (out_split) {
@@ -282,7 +285,7 @@ __global__ void __launch_bounds__(256) tile_fp4_kernel(const bf16 *__restrict__ 
   }
   __syncthreads();
   for (int j = 0; j < 4; ++j) {
-    const int p = t + 256 * j, r = p >> 2, c = (p & 3) ^ ((r >> 3) & 3);  // slot p holds chunk c
+    const int p = t + 256 * j, r = p >> 2, c = (p & 3) ^ (tl4_pos(r, 0) & 3);  // slot p holds chunk c
     const float mul = gmul[r >> 5];
     uint32_t w = 0u;
     for (int e = 0; e < 8; ++e) w |= fp4_code(tile[r][8 * c + e] * mul) << (4 * e);
@@ -299,9 +302,9 @@ hipError_t tile_fp4(const uint16_t *X, int R, int K, int64_t ldx, bool trans, ui
 }
 
 hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top, const uint16_t *probs,
-                           int V, const float *row_scale, const uint8_t *shift, const uint16_t *E, float *out,
+                           int V, const float *row_scale, const uint8_t *shift, const PackedTable &E, float *out,
                            uint16_t *out_split, hipStream_t s, int64_t lo_off) {
-  if (d % 4) return hipErrorInvalidValue;
+  if (d % 4 || (top && (!E.p || E.d != d))) return hipErrorInvalidValue;
   hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((d / 4 + 255) / 256, N), dim3(256), 0, s, part, ksplit, N, d,
                      top, probs, V, row_scale, shift, E, out, out_split, lo_off ? lo_off : (int64_t)N * d);
   return hipGetLastError();
@@ -541,8 +544,9 @@ __device__ __forceinline__ void row_combine_row(const int row, const float4 *__r
                                                 float inv_T, float *__restrict__ entropy,
                                                 int32_t *__restrict__ cand, float *__restrict__ tile_scale,
                                                 float *__restrict__ row_scale, uint8_t *__restrict__ shift,
-                                                const float *__restrict__ n2, const bf16 *__restrict__ E, int d,
+                                                const float *__restrict__ n2, const PackedTable &E,
                                                 float2 *__restrict__ top, float *shv, int *shi) {
+  const int d = E.d;
   // the normalised row for the exact top logit, loaded before the argmax is known
   float nv[RC_D];
   const bool fix = n2 != nullptr;
@@ -592,7 +596,7 @@ __device__ __forceinline__ void row_combine_row(const int row, const float4 *__r
 #pragma unroll
     for (int i = 0; i < RC_D; ++i) {
       const int k = threadIdx.x + RC_NT * i;
-      if (k < d) part += nv[i] * bf16_to_f32(E[(int64_t)amax * d + k]);
+      if (k < d) part += nv[i] * table_get(E, amax, k);
     }
     const float z_exact = rc_sum<RC_NW>(part, shv);
     d_top = z_exact * inv_T - My;
@@ -653,13 +657,13 @@ __global__ void __launch_bounds__(RC_NT) row_combine_kernel(const float4 *__rest
                                                           int32_t *__restrict__ cand,
                                                           float *__restrict__ tile_scale,
                                                           float *__restrict__ row_scale, uint8_t *__restrict__ shift,
-                                                          const float *__restrict__ n2, const bf16 *__restrict__ E,
-                                                          int d, float2 *__restrict__ top) {
+                                                          const float *__restrict__ n2, PackedTable E,
+                                                          float2 *__restrict__ top) {
   __shared__ float shv[2 * RC_NW];
   __shared__ int shi[RC_NW];
   const int row = blockIdx.x;
   row_combine_row<CACHED>(row, stats, ntiles, inv_T, entropy, cand, tile_scale, row_scale, shift,
-                          n2 ? n2 + (int64_t)row * d : nullptr, E, d, top, shv, shi);
+                          n2 ? n2 + (int64_t)row * E.d : nullptr, E, top, shv, shi);
 }
 
 // A batch: workgroup r is row r % N of canvas r / N (the bf16 path's
@@ -667,36 +671,35 @@ __global__ void __launch_bounds__(RC_NT) row_combine_kernel(const float4 *__rest
 template <bool CACHED>
 __global__ void __launch_bounds__(RC_NT) row_combine_batch_kernel(RowCombineBatch bt, int N, int ntiles,
                                                                 float inv_T, const float *__restrict__ n2,
-                                                                const bf16 *__restrict__ E, int d) {
+                                                                PackedTable E) {
   __shared__ float shv[2 * RC_NW];
   __shared__ int shi[RC_NW];
   const int c = blockIdx.x / N, row = blockIdx.x - c * N;
   row_combine_row<CACHED>(row, bt.stats[c], ntiles, inv_T, bt.entropy[c], bt.cand[c], nullptr, bt.row_scale[c],
-                          bt.shift[c], n2 + (int64_t)blockIdx.x * d, E, d, bt.top[c], shv, shi);
+                          bt.shift[c], n2 + (int64_t)blockIdx.x * E.d, E, bt.top[c], shv, shi);
 }
 
 hipError_t row_combine_batch(const RowCombineBatch &bt, int B, int N, int ntiles, float inv_T, const float *n2,
-                             const uint16_t *E, int d, hipStream_t s) {
-  if (B < 1 || B > ES_MAX_BATCH || N < 1 || N > 256 || !n2 || d > RC_NT * RC_D) return hipErrorInvalidValue;
+                             const PackedTable &E, hipStream_t s) {
+  if (B < 1 || B > ES_MAX_BATCH || N < 1 || N > 256 || !n2 || !E.p || E.d % 4 || E.d > RC_NT * RC_D)
+    return hipErrorInvalidValue;
   if (ntiles <= RC_NT * RC_CACHE)
-    hipLaunchKernelGGL(row_combine_batch_kernel<true>, dim3(B * N), dim3(RC_NT), 0, s, bt, N, ntiles, inv_T, n2, E,
-                       d);
+    hipLaunchKernelGGL(row_combine_batch_kernel<true>, dim3(B * N), dim3(RC_NT), 0, s, bt, N, ntiles, inv_T, n2, E);
   else
-    hipLaunchKernelGGL(row_combine_batch_kernel<false>, dim3(B * N), dim3(RC_NT), 0, s, bt, N, ntiles, inv_T, n2,
-                       E, d);
+    hipLaunchKernelGGL(row_combine_batch_kernel<false>, dim3(B * N), dim3(RC_NT), 0, s, bt, N, ntiles, inv_T, n2, E);
   return hipGetLastError();
 }
 
 hipError_t row_combine(const float4 *tile_stats, int M, int ntiles, float inv_T, float *entropy,
                        int32_t *cand, float *tile_scale, float *row_scale, uint8_t *shift, const float *n2,
-                       const uint16_t *E, int d, float2 *top, hipStream_t s) {
-  if ((shift && M > 256) || (n2 && d > RC_NT * RC_D)) return hipErrorInvalidValue;
+                       const PackedTable &E, float2 *top, hipStream_t s) {
+  if ((shift && M > 256) || (n2 && (!E.p || E.d % 4 || E.d > RC_NT * RC_D))) return hipErrorInvalidValue;
   if (ntiles <= RC_NT * RC_CACHE)
     hipLaunchKernelGGL(row_combine_kernel<true>, dim3(M), dim3(RC_NT), 0, s, tile_stats, ntiles, inv_T, entropy,
-                       cand, tile_scale, row_scale, shift, n2, E, d, top);
+                       cand, tile_scale, row_scale, shift, n2, E, top);
   else
     hipLaunchKernelGGL(row_combine_kernel<false>, dim3(M), dim3(RC_NT), 0, s, tile_stats, ntiles, inv_T, entropy,
-                       cand, tile_scale, row_scale, shift, n2, E, d, top);
+                       cand, tile_scale, row_scale, shift, n2, E, top);
   return hipGetLastError();
 }
 

@@ -79,19 +79,34 @@ __device__ __forceinline__ void wait_vmcnt() {
 // accumulation is that of the bf16 table holding the same values.
 // TF = TF_FP4: fp4 e2m1 with a power-of-two scale per 32 x 32 block
 // (dg_tiled.h), 4 KB per slice copied by the low 32 lanes of every wave; a
-// fragment is one 4-byte LDS read widened to bf16 exactly by four
-// v_cvt_scalef32_pk_bf16_fp4.  Bt8 carries the fp8 or fp4
-// blocks, Bs4 the fp4 scale bytes (slice s of this block at Bs4 + 8 s); the
-// 8 scale bytes of slice s are copied beside it by wave s % 8.
-enum { TF_BF16 = 0, TF_FP8 = 1, TF_FP4 = 2 };
-template <bool SCALED, bool PAIR = false, int TF = TF_BF16>
-__device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const bf16 *__restrict__ Bt,
+// fragment is 8 codes widened to bf16 exactly by four
+// v_cvt_scalef32_pk_bf16_fp4.  The 8 scale bytes of slice s (one per
+// 32-row group of the table operand) are copied beside it by wave s % 8.
+//
+// TR: the table operand is read from E [K][...] itself, whose tiled blocks
+// run along the table operand's k (the self-conditioning contraction,
+// K = V): Bt is the table's base, the workgroup's 256 operand rows are the
+// E columns of blocks tr_d0 .. tr_d0 + 7 (tr_ksd blocks per 256 E rows,
+// indices past the last clamped: those columns are never stored), and
+// slice s is rows 32 s .. 32 s + 31 of those 8 blocks, 8 runs of
+// consecutive bytes (wave w copies block tr_d0 + w).  The fragments are
+// transposed on the way out of LDS by the gfx950 transposing reads
+// (ds_read_b64_tr_b16 / _b8 / _b4): within each 16-lane group, lane i gets
+// element i + 16 e (e = 0, 1, ...) of the group's 16 consecutive 8-byte
+// loads, so each lane addresses a short run of one E row and receives one
+// E column.  Without TR, Bt is the workgroup's block row of the table (slice
+// s at s blocks on) and Bs4 its scale bytes (slice s at Bs4 + 8 s); with TR
+// Bs4 is the table's whole scale array.
+template <bool SCALED, bool PAIR = false, int TF = TF_BF16, bool TR = false>
+__device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const uint8_t *__restrict__ Bt,
                                              const uint8_t *__restrict__ shift, int sb, int se, char *lds,
                                              f32x16_t (&acc)[2][4], const bf16 *__restrict__ At2 = nullptr,
-                                             const uint8_t *__restrict__ shift2 = nullptr,
-                                             const uint8_t *__restrict__ Bt8 = nullptr, float b8_scale = 1.f,
-                                             const uint8_t *__restrict__ Bs4 = nullptr) {
+                                             const uint8_t *__restrict__ shift2 = nullptr, float b8_scale = 1.f,
+                                             const uint8_t *__restrict__ Bs4 = nullptr, int tr_ksd = 0,
+                                             int tr_d0 = 0) {
   constexpr bool B8 = TF == TF_FP8, B4 = TF == TF_FP4, BQ = B8 || B4;
+  // bytes of one 256 x 32 block of the table, and of one of its rows
+  constexpr int BLK = B8 ? TL8_BYTES : B4 ? TL4_BYTES : TL_ELEMS * 2, ROWB = BLK / 256;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r32 = lane & 31, g = lane >> 5;
@@ -113,32 +128,41 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   const bf16 *asrc = (PAIR && wave >= 4) ? At2 + (int64_t)sb * TL_ELEMS + ((wave - 4) * 2 * 64 + lane) * 8
                                          : At + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
   const uint8_t *ssrc = !SCALED ? nullptr : (PAIR && lane >= 32) ? shift2 + (lane - 32) * 4 : shift + lane * 4;
-  const bf16 *bsrc = BQ ? nullptr : Bt + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
-  const uint8_t *bsrc8 = B8 ? Bt8 + (int64_t)sb * TL8_BYTES + (wave * 64 + lane) * 16
-                            : B4 ? Bt8 + (int64_t)sb * TL4_BYTES + (wave * 32 + (lane & 31)) * 16 : nullptr;
+  // this lane's 16 bytes of each DMA instruction of the table slice: bf16
+  // 2 instructions of 64 lanes per wave, fp8 1, fp4 1 of 32 lanes
+  const int blane = (B4 ? (lane & 31) : lane) * 16;
+  const uint8_t *bsrc = TR ? Bt + (int64_t)min(tr_d0 + wave, tr_ksd - 1) * BLK + blane
+                           : Bt + (int64_t)sb * BLK + wave * (BLK / 8) + blane;
   char *lds_shift = lds + ES_STAGES * 2 * ES_SLICE;  // SCALED: [stage][256] bytes
-  char *lds_s4 = lds_shift + ES_STAGES * 256;         // B4: [stage][16] bytes, the slice's 8 scales
+  char *lds_s4 = lds_shift + ES_STAGES * 256;         // B4: [stage][32] bytes, the slice's 8 scales
   auto issue = [&](int slice, int stage) {
     const int64_t off = (int64_t)min(slice, nk - 1) * TL_ELEMS;  // past the end: a repeat, never read
     char *st = lds + stage * 2 * ES_SLICE;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       __builtin_amdgcn_global_load_lds(asrc + off + u * 512, st + (wave * 2 + u) * 1024, 16, 0, 0);
-      if (!BQ)
-        __builtin_amdgcn_global_load_lds(bsrc + off + u * 512, st + ES_SLICE + (wave * 2 + u) * 1024, 16, 0, 0);
     }
-    if (B8)  // 8 KB of fp8 table: 1 KB per wave
-      __builtin_amdgcn_global_load_lds(bsrc8 + (int64_t)min(slice, nk - 1) * TL8_BYTES, st + ES_SLICE + wave * 1024,
-                                       16, 0, 0);
-    if (B4 && lane < 32)  // 4 KB of fp4 table: 512 bytes per wave, lanes 0..31
-      __builtin_amdgcn_global_load_lds(bsrc8 + (int64_t)min(slice, nk - 1) * TL4_BYTES, st + ES_SLICE + wave * 512,
-                                       16, 0, 0);
+    // the table slice: BLK / 8 bytes per wave (rows 32 sg .. + 31 of a block
+    // with TR, 32 of its 256 rows otherwise)
+    const int sg = sb + min(slice, nk - 1);
+    const uint8_t *bs = TR ? bsrc + (int64_t)(sg >> 3) * tr_ksd * BLK + (sg & 7) * 32 * ROWB
+                           : bsrc + (int64_t)min(slice, nk - 1) * BLK;
+    char *bd = st + ES_SLICE + wave * (BLK / 8);
+    if (!BQ) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) __builtin_amdgcn_global_load_lds(bs + u * 1024, bd + u * 1024, 16, 0, 0);
+    } else if (B8 || lane < 32) {
+      __builtin_amdgcn_global_load_lds(bs, bd, 16, 0, 0);
+    }
     if (SCALED && wave == (slice & 7))  // the slice tile's 256 row exponents, 4 bytes per lane
       __builtin_amdgcn_global_load_lds(ssrc + (int64_t)((sb + min(slice, nk - 1)) >> 1) * 256,
                                        lds_shift + stage * 256, 4, 0, 0);
-    if (B4 && wave == (slice & 7) && lane < 2)  // the slice's 8 block scales, 4 bytes per lane
-      __builtin_amdgcn_global_load_lds(Bs4 + (int64_t)(sb + min(slice, nk - 1)) * 8 + lane * 4, lds_s4 + stage * 16,
-                                       4, 0, 0);
+    if (B4 && !TR && wave == (slice & 7) && lane < 2)  // the slice's 8 block scales, 4 bytes per lane
+      __builtin_amdgcn_global_load_lds(Bs4 + (int64_t)sg * 8 + lane * 4, lds_s4 + stage * 32, 4, 0, 0);
+    if (B4 && TR && wave == (slice & 7) && lane < 8)  // lane l: the 4 bytes holding block tr_d0 + l's scale
+      __builtin_amdgcn_global_load_lds(
+          Bs4 + (((int64_t)(sg >> 3) * tr_ksd + min(tr_d0 + lane, tr_ksd - 1)) * TL4_SCALES + ((sg & 7) & ~3)),
+          lds_s4 + stage * 32, 4, 0, 0);
   };
   // DMA instructions per slice per wave: 4 (3 with an fp8 or fp4 table),
   // plus XTRA more for wave s % 8 on slice s (exponents when SCALED, fp4
@@ -148,26 +172,70 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
 
   // Fragment f of one 16-wide k step as stored: f < 2 a canvas fragment
   // (rows wm*64 + 32f), else table fragment f - 2 (rows wn*128 + 32(f-2)).
+  // TR: table fragment j's E rows (slice rows v) and block (wn * 4 + j) in
+  // LDS; the lane's place in its 16-lane group
+  typedef short v4s_t __attribute__((ext_vector_type(4)));
+  typedef int v2i_t __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+  typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  auto tblk = [&](int stage, int j) -> const char * {
+    return lds + stage * 2 * ES_SLICE + ES_SLICE + (wn * 4 + j) * (BLK / 8);
+  };
   auto frag = [&](int stage, int kk, int f) -> uint4 {
+    if (TR && f >= 2) {  // two 4-row reads: lane i16 gets column 16 (g16 & 1) + i16, rows 8 (g16 >> 1) + 0..7
+      const char *b = tblk(stage, f - 2);
+      const int c = 2 * (g16 & 1) + ((i16 >> 1) & 1), hf = i16 & 1;  // 4 columns 4 (i16 & 3) of the 16
+      uint2 r[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int v = kk * 16 + 8 * (g16 >> 1) + 4 * u + (i16 >> 2);
+        const v4s_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4s_t *)(b + v * ROWB + (c ^ ((v >> 2) & 3)) * 16 + hf * 8));
+        r[u] = __builtin_bit_cast(uint2, t);
+      }
+      return make_uint4(r[0].x, r[0].y, r[1].x, r[1].y);
+    }
     const uint4 *sl = reinterpret_cast<const uint4 *>(lds + stage * 2 * ES_SLICE + (f < 2 ? 0 : ES_SLICE));
     const int row = f < 2 ? wm * 64 + f * 32 + r32 : wn * 128 + (f - 2) * 32 + r32;
     return sl[tl_pos(row, kk * 2 + g)];
   };
   // B8: the 8 fp8 bytes of table fragment j (rows wn*128 + 32j), and their bf16 form
   auto frag8 = [&](int stage, int kk, int j) -> uint2 {
+    if (TR) {  // one read: lane i16 gets column 16 (g16 & 1) + i16, rows 8 (g16 >> 1) + 0..7
+      const int v = kk * 16 + 8 * (g16 >> 1) + (i16 >> 1), c = 2 * (g16 & 1) + (i16 & 1);
+      const v2i_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (lds_v2i_t *)(tblk(stage, j) + (v * 4 + (c ^ (tl8_pos(v, 0) & 3))) * 8));
+      return __builtin_bit_cast(uint2, t);
+    }
     const uint2 *sl = reinterpret_cast<const uint2 *>(lds + stage * 2 * ES_SLICE + ES_SLICE);
     return sl[tl8_pos(wn * 128 + j * 32 + r32, kk * 2 + g)];
   };
   // B4: the 4 bytes (8 fp4 values) of table fragment j, its block's scale
   // (rows wn*128 + 32j: scale byte 4 wn + j of the slice), and the bf16 form
   auto frag4 = [&](int stage, int kk, int j) -> uint32_t {
+    if (TR) {  // one read of both k halves: lane i16 gets column 16 (g16 & 1) + i16,
+               // rows kk * 16 + 8 (g16 >> 1) + 0..7 in word kk
+      const int h = g16 >> 1, v = i16 < 8 ? 8 * h + i16 : 16 + 8 * h + (i16 - 8), c = 2 * (g16 & 1);
+      const v2i_t t = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+          (lds_v2i_t *)(tblk(stage, j) + (v * 4 + (c ^ (tl4_pos(v, 0) & 3))) * 4));
+      return (uint32_t)(kk ? t.y : t.x);
+    }
     const uint32_t *sl = reinterpret_cast<const uint32_t *>(lds + stage * 2 * ES_SLICE + ES_SLICE);
     return sl[tl4_pos(wn * 128 + j * 32 + r32, kk * 2 + g)];
   };
-  // the scale bytes of this wave's four table fragments (rows wn*128 + 32j:
-  // byte j), one broadcast read; fragment j's scale 2^(byte - 127)
-  auto scales4 = [&](int stage) -> uint32_t {
-    return *reinterpret_cast<const uint32_t *>(lds_s4 + stage * 16 + wn * 4);
+  // the scale bytes of this wave's four table fragments (byte j for the
+  // fragment of rows wn*128 + 32j), broadcast reads of the stage holding
+  // slice `slice`; fragment j's scale 2^(byte - 127).  TR: dword 4 wn + j
+  // holds the fragment's byte at position (sg & 3).
+  auto scales4 = [&](int stage, int slice) -> uint32_t {
+    if (TR) {
+      const uint4 w = *reinterpret_cast<const uint4 *>(lds_s4 + stage * 32 + wn * 16);
+      const int sh = 8 * ((sb + min(slice, nk - 1)) & 3);
+      return ((w.x >> sh) & 0xFFu) | (((w.y >> sh) & 0xFFu) << 8) | (((w.z >> sh) & 0xFFu) << 16) |
+             (((w.w >> sh) & 0xFFu) << 24);
+    }
+    return *reinterpret_cast<const uint32_t *>(lds_s4 + stage * 32 + wn * 4);
   };
   auto scale4 = [](uint32_t w, int j) -> float { return __uint_as_float(((w >> (8 * j)) & 0xFFu) << 23); };
   auto widen4 = [&](uint32_t q, float sc) -> uint4 {
@@ -197,7 +265,8 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   // interleaved (two after each of the first three MFMAs), each step pinned
   // in place, so a fragment is read a full k half before its first use.
   // With ex, the next half's exponents are read too (a new slice).
-  auto half = [&](const uint4 (&cur)[6], uint4 (&nxt)[6], int nstage, int nkk, bool ex, u16x2_t (&e)[2]) {
+  // nsl: the slice the next k half belongs to
+  auto half = [&](const uint4 (&cur)[6], uint4 (&nxt)[6], int nstage, int nkk, bool ex, u16x2_t (&e)[2], int nsl) {
     uint32_t sh[2];
     uint2 q8[4];
     uint32_t q4[4], s4 = 0;
@@ -217,7 +286,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
         } else {
           q4[2 * m - 2] = frag4(nstage, nkk, 2 * m - 2);
           q4[2 * m - 1] = frag4(nstage, nkk, 2 * m - 1);
-          if (m == 1) s4 = scales4(nstage);
+          if (m == 1) s4 = scales4(nstage, nsl);
         }
         if (SCALED && ex && m == 0) {
           sh[0] = expo(nstage, 0);
@@ -263,7 +332,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   else
     wait_vmcnt<2 * PER>();
   __builtin_amdgcn_s_barrier();
-  const uint32_t s40 = B4 ? scales4(0) : 0u;
+  const uint32_t s40 = B4 ? scales4(0, 0) : 0u;
 #pragma unroll
   for (int f = 0; f < 6; ++f)
     F0[f] = (B8 && f >= 2) ? widen(frag8(0, 0, f - 2))
@@ -276,7 +345,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
     scale(F0[1], ex[1]);
   }
   for (int it = 0; it < nk; ++it) {
-    half(F0, F1, it & 3, 1, false, ex);  // second half of slice it, same exponents
+    half(F0, F1, it & 3, 1, false, ex, it);  // second half of slice it, same exponents
     if (XTRA && wave == ((it + 2) & 7))  // this wave's copies of slice it+1 landed ...
       wait_vmcnt<PER + XTRA>();
     else
@@ -284,7 +353,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
     __builtin_amdgcn_s_barrier();  // ... every wave's; every wave is done with slice it-1
     issue(it + 3, (it + 3) & 3);
     __builtin_amdgcn_sched_barrier(0);
-    half(F1, F0, (it + 1) & 3, 0, true, ex);  // past the last slice: a repeat, unused
+    half(F1, F0, (it + 1) & 3, 0, true, ex, it + 1);  // past the last slice: a repeat, unused
   }
   wait_vmcnt<0>();  // retire the trailing (unused) prefetches before LDS is reused
   __builtin_amdgcn_s_barrier();
@@ -306,11 +375,8 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
 // ---------------------------------------------------------------------------
 template <bool BATCH, int TF>
 __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__restrict__ At, int M, int N, int K,
-                                                              const bf16 *__restrict__ Et, int V, float inv_T,
-                                                              EsCanvases cv, int nblk, int items,
-                                                              float *__restrict__ logits,
-                                                              const uint8_t *__restrict__ Et8, float b8_scale,
-                                                              const uint8_t *__restrict__ Es4) {
+                                                              PackedTable tab, int V, float inv_T, EsCanvases cv,
+                                                              int nblk, int items, float *__restrict__ logits) {
   extern __shared__ __align__(16) char lds[];
   int item = blockIdx.x;
   if (BATCH) item = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;  // grid: a multiple of 8
@@ -321,11 +387,11 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
   const int ksl = K / ES_BK;
   f32x16_t acc[2][4];
-  estream_tile<false, false, TF>(
-      At + (int64_t)bb * ksl * TL_ELEMS, TF != TF_BF16 ? nullptr : Et + (int64_t)jt * ksl * TL_ELEMS, nullptr, 0, ksl,
-      lds, acc, nullptr, nullptr,
-      TF == TF_FP8 ? Et8 + (int64_t)jt * ksl * TL8_BYTES : TF == TF_FP4 ? Et8 + (int64_t)jt * ksl * TL4_BYTES : nullptr,
-      b8_scale, TF == TF_FP4 ? Es4 + (int64_t)jt * ksl * 8 : nullptr);
+  constexpr int BLK = TF == TF_FP8 ? TL8_BYTES : TF == TF_FP4 ? TL4_BYTES : TL_ELEMS * 2;
+  estream_tile<false, false, TF>(At + (int64_t)bb * ksl * TL_ELEMS,
+                                 static_cast<const uint8_t *>(tab.p) + (int64_t)jt * ksl * BLK, nullptr, 0, ksl, lds,
+                                 acc, nullptr, nullptr, tab.scale,
+                                 TF == TF_FP4 ? tab.s4 + (int64_t)jt * ksl * TL4_SCALES : nullptr);
   const int ntiles = V / 64;
 
 #pragma unroll
@@ -402,20 +468,16 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
 
 int estream_bm(int) { return ES_BM; }
 
-static size_t es_lds_bytes() { return (size_t)ES_STAGES * (2 * ES_SLICE + 256 + 16); }
+static size_t es_lds_bytes() { return (size_t)ES_STAGES * (2 * ES_SLICE + 256 + 32); }
 
-// exactly one table form: bf16, or a quantised form with its codes (and scales)
-static bool one_table_form(const void *bf, const QTable &qt) {
-  if (qt.tf == TF_BF16) return bf != nullptr;
-  if (bf || !qt.q) return false;
-  return qt.tf == TF_FP8 || (qt.tf == TF_FP4 && qt.s4);
+static bool table_ok(const PackedTable &t, int d) {
+  return t.p && t.d == d && (t.tf == TF_BF16 || t.tf == TF_FP8 || (t.tf == TF_FP4 && t.s4));
 }
 
-hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, const uint16_t *E_tiled, int V,
-                              float inv_T, const EsCanvases &cv, float *logits_dump, hipStream_t s,
-                              const QTable &qt) {
+hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, const PackedTable &tab, int V,
+                              float inv_T, const EsCanvases &cv, float *logits_dump, hipStream_t s) {
   if (B < 1 || B > ES_MAX_BATCH || N < 1 || N > ES_BM || K % ES_BK || V % ES_BN) return hipErrorInvalidValue;
-  if (!one_table_form(E_tiled, qt)) return hipErrorInvalidValue;
+  if (!table_ok(tab, K)) return hipErrorInvalidValue;
   static std::atomic<uint64_t> attr{0};
   if (once_per_device(attr, [] {
         const void *fns[6] = {reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_BF16>),
@@ -434,29 +496,20 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
   const int M = B * N, nblk = (M + ES_BM - 1) / ES_BM;
   const int items = (V / ES_BN) * nblk;
   const dim3 grid(B == 1 ? items : (items + 7) / 8 * 8);
-#define DG_LM_LAUNCH(BT, TF)                                                                                   \
-  hipLaunchKernelGGL((lm_head_es_kernel<BT, TF>), grid, dim3(ES_NT), es_lds_bytes(), s, A_tiled, M, N, K,      \
-                     reinterpret_cast<const bf16 *>(E_tiled), V, inv_T, cv, nblk, items, logits_dump, qt.q,     \
-                     qt.scale, qt.s4)
-#define DG_LM_FORMS(BT)                                  \
-  do {                                                   \
-    if (qt.tf == TF_FP8) DG_LM_LAUNCH(BT, TF_FP8);       \
-    else if (qt.tf == TF_FP4) DG_LM_LAUNCH(BT, TF_FP4);  \
-    else DG_LM_LAUNCH(BT, TF_BF16);                      \
+#define DG_LM_LAUNCH(BT, TF)                                                                              \
+  hipLaunchKernelGGL((lm_head_es_kernel<BT, TF>), grid, dim3(ES_NT), es_lds_bytes(), s, A_tiled, M, N, K, tab, \
+                     V, inv_T, cv, nblk, items, logits_dump)
+#define DG_LM_FORMS(BT)                                   \
+  do {                                                    \
+    if (tab.tf == TF_FP8) DG_LM_LAUNCH(BT, TF_FP8);       \
+    else if (tab.tf == TF_FP4) DG_LM_LAUNCH(BT, TF_FP4);  \
+    else DG_LM_LAUNCH(BT, TF_BF16);                       \
   } while (0)
   if (B == 1) DG_LM_FORMS(false);
   else DG_LM_FORMS(true);
 #undef DG_LM_FORMS
 #undef DG_LM_LAUNCH
   return hipGetLastError();
-}
-
-hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E_tiled, int V, float inv_T,
-                        uint16_t *probs_tiled, float4 *tile_stats, float *logits_dump, hipStream_t s) {
-  EsCanvases cv{};
-  cv.probs[0] = probs_tiled;
-  cv.tile_stats[0] = tile_stats;
-  return lm_head_bf16_batch(A_tiled, 1, M, K, E_tiled, V, inv_T, cv, logits_dump, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -472,11 +525,9 @@ hipError_t lm_head_bf16(const uint16_t *A_tiled, int M, int K, const uint16_t *E
 // canvases of at most 128 rows, two per block (canvas 2p in rows 0..127,
 // canvas 2p + 1 in rows 128..255, read from its own buffers).
 template <bool SCALED, int MODE, int TF>
-__global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin, const bf16 *__restrict__ Bt,
-                                                               int M, int N, int K, float *__restrict__ part,
-                                                               int ksplit, int ntn, int nb, int items,
-                                                               SelfcondGuard guard, const uint8_t *__restrict__ Bt8,
-                                                               float b8_scale, const uint8_t *__restrict__ Bs4) {
+__global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin, PackedTable tab, int M, int N,
+                                                               int K, float *__restrict__ part, int ksplit, int ntn,
+                                                               int nb, int items, SelfcondGuard guard) {
   extern __shared__ __align__(16) char lds[];
   const int b = blockIdx.x, ng = gridDim.x;
   const int per_xcd = ng / 8;  // grid is a multiple of 8
@@ -489,20 +540,19 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin,
   const int sb = (int)((int64_t)ksl * kc / ksplit), se = (int)((int64_t)ksl * (kc + 1) / ksplit);
   const int n0 = nt * ES_BN;
   f32x16_t acc[2][4];
-  const bf16 *Bn = TF != TF_BF16 ? nullptr : Bt + (int64_t)nt * ksl * TL_ELEMS;
-  const uint8_t *Bn8 = TF == TF_FP8   ? Bt8 + (int64_t)nt * ksl * TL8_BYTES
-                       : TF == TF_FP4 ? Bt8 + (int64_t)nt * ksl * TL4_BYTES
-                                      : nullptr;
-  const uint8_t *Bn4 = TF == TF_FP4 ? Bs4 + (int64_t)nt * ksl * TL4_SCALES : nullptr;
+  // the table E [K][N] read transposed: columns n0 .. n0 + 255 are its blocks 8 nt .. 8 nt + 7
+  const uint8_t *Bt = static_cast<const uint8_t *>(tab.p);
+  const int ksd = N / ES_BK;
   if (MODE == 2) {
     const int c0 = 2 * blk, c1 = c0 + 1;
     // an odd batch's last block: its upper half is the canvas's own padding rows
     const bf16 *A2 = c1 < nb ? cin.probs[c1] : cin.probs[c0] + 512 * 8;
     const uint8_t *s2 = c1 < nb ? cin.shift[c1] : cin.shift[c0] + 128;
-    estream_tile<SCALED, true, TF>(cin.probs[c0], Bn, cin.shift[c0], sb, se, lds, acc, A2, s2, Bn8, b8_scale, Bn4);
+    estream_tile<SCALED, true, TF, true>(cin.probs[c0], Bt, cin.shift[c0], sb, se, lds, acc, A2, s2, tab.scale,
+                                         tab.s4, ksd, 8 * nt);
   } else {
-    estream_tile<SCALED, false, TF>(cin.probs[blk], Bn, cin.shift[blk], sb, se, lds, acc, nullptr, nullptr, Bn8,
-                                    b8_scale, Bn4);
+    estream_tile<SCALED, false, TF, true>(cin.probs[blk], Bt, cin.shift[blk], sb, se, lds, acc, nullptr, nullptr,
+                                          tab.scale, tab.s4, ksd, 8 * nt);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -525,12 +575,11 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin,
   }
 }
 
-hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *Et_tiled, int M, int N, int K,
-                               bool scaled, float *partials, int ksplit, hipStream_t s, SelfcondGuard guard,
-                               const QTable &qt) {
-  if (B < 1 || B > ES_MAX_BATCH || M > ES_BM || K % 64 || N % 4 || ksplit < 1 || ksplit > K / ES_BK)
+hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const PackedTable &tab, int M, int N, int K,
+                               bool scaled, float *partials, int ksplit, hipStream_t s, SelfcondGuard guard) {
+  if (B < 1 || B > ES_MAX_BATCH || M > ES_BM || K % 256 || N % ES_BK || ksplit < 1 || ksplit > K / ES_BK)
     return hipErrorInvalidValue;
-  if (!one_table_form(Et_tiled, qt)) return hipErrorInvalidValue;
+  if (!table_ok(tab, N)) return hipErrorInvalidValue;
   static std::atomic<uint64_t> attr{0};
   if (once_per_device(attr, [] {
 #define DG_SC_FN(SC, MD, TF) reinterpret_cast<const void *>(selfcond_es_kernel<SC, MD, TF>)
@@ -551,10 +600,9 @@ hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *E
   const int ntn = (N + ES_BN - 1) / ES_BN;
   const int items = ntn * ksplit * (mode == 2 ? (B + 1) / 2 : B);
   const dim3 grid((items + 7) / 8 * 8);
-  const bf16 *Bt = reinterpret_cast<const bf16 *>(Et_tiled);
-#define DG_SC_LAUNCH(SC, MD, TF)                                                                                 \
-  hipLaunchKernelGGL((selfcond_es_kernel<SC, MD, TF>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, Bt, M, N, K,   \
-                     partials, ksplit, ntn, B, items, guard, qt.q, qt.scale, qt.s4)
+#define DG_SC_LAUNCH(SC, MD, TF)                                                                                \
+  hipLaunchKernelGGL((selfcond_es_kernel<SC, MD, TF>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, tab, M, N, K, \
+                     partials, ksplit, ntn, B, items, guard)
 #define DG_SC_MODES(SC, TF)                      \
   do {                                           \
     if (mode == 0) DG_SC_LAUNCH(SC, 0, TF);      \
@@ -563,8 +611,8 @@ hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *E
   } while (0)
 #define DG_SC_FORMS(SC)                                \
   do {                                                 \
-    if (qt.tf == TF_FP8) DG_SC_MODES(SC, TF_FP8);      \
-    else if (qt.tf == TF_FP4) DG_SC_MODES(SC, TF_FP4); \
+    if (tab.tf == TF_FP8) DG_SC_MODES(SC, TF_FP8);      \
+    else if (tab.tf == TF_FP4) DG_SC_MODES(SC, TF_FP4); \
     else DG_SC_MODES(SC, TF_BF16);                     \
   } while (0)
   if (scaled) DG_SC_FORMS(true);
@@ -573,14 +621,6 @@ hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const uint16_t *E
 #undef DG_SC_MODES
 #undef DG_SC_LAUNCH
   return hipGetLastError();
-}
-
-hipError_t selfcond_bf16(const TiledGemm &g, const uint8_t *shift, float *partials, int ksplit, hipStream_t s,
-                         SelfcondGuard guard) {
-  EsCanvasesIn cin{};
-  cin.probs[0] = reinterpret_cast<const bf16 *>(g.A);
-  cin.shift[0] = shift;
-  return selfcond_bf16_batch(cin, 1, g.B, g.M, g.N, g.K, shift != nullptr, partials, ksplit, s, guard);
 }
 
 }  // namespace dg

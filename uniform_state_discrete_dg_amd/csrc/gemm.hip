@@ -12,11 +12,16 @@
 
 namespace dg {
 
-__device__ __forceinline__ const uint16_t *epi_row(const Epi &e, int row) {
+// EPI_ADD_ROW: columns col .. col + 3 (col % 4 == 0) of the row's table entry
+__device__ __forceinline__ float4 epi_row4(const Epi &e, int row, int col) {
   int t = e.gtok[row];
-  if (t >= e.gV && e.gmask) return e.gmask;  // [MASK] (masked sampler)
+  if (t >= e.gV && e.gmask) {  // [MASK] (masked sampler)
+    const uint2 r = *reinterpret_cast<const uint2 *>(e.gmask + col);
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
+                       __uint_as_float(r.y & 0xffff0000u));
+  }
   t = t < 0 ? 0 : (t >= e.gV ? e.gV - 1 : t);
-  return e.gtab + (int64_t)t * e.gld;
+  return table_get4(e.gtab, t, col);
 }
 
 __device__ __forceinline__ void epi_store(const Epi &e, int row, int col, float v) {
@@ -24,7 +29,12 @@ __device__ __forceinline__ void epi_store(const Epi &e, int row, int col, float 
   switch (e.kind) {
     case EPI_GELU: v = gelu_erf(v); break;
     case EPI_ADD: v += e.resid[idx]; break;
-    case EPI_ADD_ROW: v += bf16_to_f32(epi_row(e, row)[col]); break;
+    case EPI_ADD_ROW: {
+      const float4 r = epi_row4(e, row, col & ~3);
+      const int k = col & 3;
+      v += k == 0 ? r.x : k == 1 ? r.y : k == 2 ? r.z : r.w;
+      break;
+    }
     default: break;
   }
   if (e.out_f32) {
@@ -270,9 +280,8 @@ __global__ void __launch_bounds__(256) gemm_splitk_epilogue_kernel(SplitGemm g) 
     const float4 r = *reinterpret_cast<const float4 *>(e.resid + idx);
     v = make_float4(v.x + r.x, v.y + r.y, v.z + r.z, v.w + r.w);
   } else if (e.kind == EPI_ADD_ROW) {
-    const uint16_t *r = epi_row(e, row) + col;
-    v = make_float4(v.x + bf16_to_f32(r[0]), v.y + bf16_to_f32(r[1]), v.z + bf16_to_f32(r[2]),
-                    v.w + bf16_to_f32(r[3]));
+    const float4 r = epi_row4(e, row, col);
+    v = make_float4(v.x + r.x, v.y + r.y, v.z + r.z, v.w + r.w);
   }
   if (e.out_f32) {
     *reinterpret_cast<float4 *>(static_cast<float *>(e.out) + idx) = v;
@@ -323,11 +332,11 @@ __global__ void __launch_bounds__(256) gemm_splitk_norm_kernel(SplitGemm g, RowN
         v.z += r.z;
         v.w += r.w;
       } else if (e.kind == EPI_ADD_ROW) {
-        const uint2 r = *reinterpret_cast<const uint2 *>(epi_row(e, row) + c);
-        v.x += __uint_as_float(r.x << 16);
-        v.y += __uint_as_float(r.x & 0xffff0000u);
-        v.z += __uint_as_float(r.y << 16);
-        v.w += __uint_as_float(r.y & 0xffff0000u);
+        const float4 r = epi_row4(e, row, c);
+        v.x += r.x;
+        v.y += r.y;
+        v.z += r.z;
+        v.w += r.w;
       }
       *reinterpret_cast<float4 *>(o) = v;
       ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
@@ -419,7 +428,7 @@ hipError_t gemm_split_norm(const SplitGemm &g, const RowNorm &rn, hipStream_t s)
   const Epi &e = g.e[0];
   if (g.count != 1 || g.ksplit < 2 || !g.part || !e.out_f32 || e.cdiv < g.N[0] || g.N[0] % 4 ||
       g.N[0] > 256 * 4 * RN_MAXQ || (e.kind != EPI_STORE && e.kind != EPI_ADD && e.kind != EPI_ADD_ROW) ||
-      e.rstride % 4 || (e.kind == EPI_ADD_ROW && e.gld % 4) ||
+      e.rstride % 4 || (e.kind == EPI_ADD_ROW && (e.gtab.d != g.N[0] || !e.gtab.p)) ||
       (rn.out_tiled && g.N[0] % TL_K))
     return hipErrorInvalidValue;
   hipError_t err = gemm_split_kernel_launch(g, s);  // partials only; the merge applies the epilogue
