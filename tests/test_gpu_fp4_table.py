@@ -38,10 +38,11 @@ def logits_dump():
 
 def packed_fp4(X: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
     """X [R][K] (R a multiple of 32) in the fp4 tiled layout: the code bytes
-    (blocks of 256 x 32 at (b * K/32 + s) * 4096, 4-byte chunk c of row r at
-    slot 4 r + (c ^ 2 (bit 4 of r)), value 8c + 2i in the low nibble of
-    byte i) and the scale bytes (8 per block, one per 32-row group), rows
-    past R zero codes with scale 127."""
+    (blocks of 256 x 32 at (b * K/32 + s) * 4096; block row r stored as row
+    q = r with bits 3 and 4 swapped, the 4 bytes of its columns 8c .. 8c + 7
+    at unit 4 q + 2 ((c % 2) xor (bit 3 xor bit 4 of q)) + c / 2, value
+    8c + 2i in the low nibble of byte i) and the scale bytes (8 per block,
+    one per 32-row group), rows past R zero codes with scale 127."""
     R, K = X.shape
     Rp = (R + 255) // 256 * 256
     codes = torch.zeros(Rp, K, dtype=torch.int64)
@@ -51,7 +52,9 @@ def packed_fp4(X: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
     r = torch.arange(Rp).view(Rp, 1)
     k = torch.arange(K).view(1, K)
     b, rr, s, kk = r // 256, r % 256, k // 32, k % 32
-    slot = rr * 4 + ((kk // 8) ^ (((rr >> 4) & 1) << 1))
+    c = kk // 8
+    q = (rr & ~0x18) | ((rr >> 1) & 0x8) | ((rr << 1) & 0x10)
+    slot = q * 4 + 2 * ((c % 2) ^ (((q >> 3) ^ (q >> 4)) & 1)) + c // 2
     byte = ((b * (K // 32) + s) * 1024 + slot) * 4 + (kk % 8) // 2
     out = torch.zeros(Rp * K // 2, dtype=torch.int64)
     even = (kk % 2 == 0).expand(Rp, K)

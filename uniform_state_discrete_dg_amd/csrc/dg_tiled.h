@@ -49,19 +49,32 @@ __host__ __device__ inline int64_t tl8_index(int row, int col, int K) {
 }
 
 // The fp4 form (e2m1, two values per byte): the same blocks of 256 rows x 32
-// columns, 4 KB each, with 4-byte chunks of 8 values: chunk p holds
-// X[256 b + r][32 s + 8 c .. + 7], r = p / 4, c = (p % 4) ^ (2 (bit 4 of r)),
-// value 8 c + 2 i in the low nibble of byte i and 8 c + 2 i + 1 in its high
-// nibble.  The swizzle keeps chunks 2q and 2q + 1 adjacent and in order, so
-// 16 consecutive values of a row are one aligned 8-byte word (the unit of
-// the transposing LDS read); a row-fragment read (4 bytes per lane, 32 rows
-// x 2 chunk columns) falls on 64 distinct banks.  Each 32 x 32 sub-block
-// (rows 32 g .. 32 g + 31 of the block) has one scale byte u (value = code *
-// 2^(u - 127)), stored apart from the codes: byte g of 8 per block, blocks
-// in the same order.
+// columns, 4 KB each.  A row is 16 bytes: two 8-byte words, word w holding
+// the 8 values of columns 8 w .. 8 w + 7 (4 bytes) and then those of columns
+// 16 + 8 w .. 16 + 8 w + 7, value 2 i in the low nibble of byte i.  Block
+// row r is stored as row rho(r) = r with bits 3 and 4 swapped, its word w at
+// position w ^ ((bit 3 xor bit 4) of rho(r)).  One 8-byte read gives a
+// row-fragment lane both 16-wide k halves of its columns (the LM head), and
+// is the unit of the transposing LDS read (the self-conditioning
+// contraction), whose 32-lane halves read rows 0-7 with 16-23 and 8-15 with
+// 24-31: rho makes each such set 16 consecutive stored rows, and the word
+// swizzle keeps the rows of a row-fragment read off each other's banks.
+// Each 32 x 32 sub-block (rows 32 g .. 32 g + 31 of the block) has one scale
+// byte u (value = code * 2^(u - 127)), stored apart from the codes: byte g of
+// 8 per block, blocks in the same order.
 constexpr int TL4_BYTES = 4096;  // bytes of codes per block
 constexpr int TL4_SCALES = 8;    // scale bytes per block
-__host__ __device__ inline int tl4_pos(int r, int c) { return r * 4 + (c ^ (((r >> 4) & 1) << 1)); }
+// rho (an involution: stored row <-> block row) and the word swizzle of a stored row
+__host__ __device__ inline int tl4_row(int r) { return (r & ~0x18) | ((r >> 1) & 0x8) | ((r << 1) & 0x10); }
+__host__ __device__ inline int tl4_swz(int sr) { return ((sr >> 3) ^ (sr >> 4)) & 1; }
+// position (in 4-byte units from the block's start) of the 8 values of
+// columns 8 c .. 8 c + 7 of block row r, and the inverse: which columns unit
+// u of stored row sr holds
+__host__ __device__ inline int tl4_pos(int r, int c) {
+  const int sr = tl4_row(r);
+  return sr * 4 + 2 * ((c & 1) ^ tl4_swz(sr)) + (c >> 1);
+}
+__host__ __device__ inline int tl4_chunk_at(int sr, int u) { return ((u >> 1) ^ tl4_swz(sr)) + 2 * (u & 1); }
 // byte holding X[row][col] (low nibble for even col) and that value's scale byte
 __host__ __device__ inline int64_t tl4_index(int row, int col, int K) {
   const int b = row >> 8, r = row & 255, s = col >> 5, k = col & 31;

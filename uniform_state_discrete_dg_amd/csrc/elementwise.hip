@@ -285,7 +285,8 @@ __global__ void __launch_bounds__(256) tile_fp4_kernel(const bf16 *__restrict__ 
   }
   __syncthreads();
   for (int j = 0; j < 4; ++j) {
-    const int p = t + 256 * j, r = p >> 2, c = (p & 3) ^ (tl4_pos(r, 0) & 3);  // slot p holds chunk c
+    // slot p: stored row p / 4 = block row r, columns 8c .. 8c + 7
+    const int p = t + 256 * j, r = tl4_row(p >> 2), c = tl4_chunk_at(p >> 2, p & 3);
     const float mul = gmul[r >> 5];
     uint32_t w = 0u;
     for (int e = 0; e < 8; ++e) w |= fp4_code(tile[r][8 * c + e] * mul) << (4 * e);

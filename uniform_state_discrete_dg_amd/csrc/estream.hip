@@ -211,18 +211,23 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
     const uint2 *sl = reinterpret_cast<const uint2 *>(lds + stage * 2 * ES_SLICE + ES_SLICE);
     return sl[tl8_pos(wn * 128 + j * 32 + r32, kk * 2 + g)];
   };
-  // B4: the 4 bytes (8 fp4 values) of table fragment j, its block's scale
-  // (rows wn*128 + 32j: scale byte 4 wn + j of the slice), and the bf16 form
-  auto frag4 = [&](int stage, int kk, int j) -> uint32_t {
-    if (TR) {  // one read of both k halves: lane i16 gets column 16 (g16 & 1) + i16,
-               // rows kk * 16 + 8 (g16 >> 1) + 0..7 in word kk
-      const int h = g16 >> 1, v = i16 < 8 ? 8 * h + i16 : 16 + 8 * h + (i16 - 8), c = 2 * (g16 & 1);
+  // B4: the 8 bytes holding table fragment j's 8 fp4 values for both k
+  // halves of the slice (x: k half 0, y: k half 1).  Row fragment: row
+  // wn*128 + 32j + r32, word g.  TR: one transposing read; lane i16 gets
+  // rows kk * 16 + 8 (g16 >> 1) + 0..7 in word kk of E column
+  // 8 w + i16 (i16 < 8) or 16 + 8 w + i16 - 8 (w = g16 & 1): the fragment's
+  // 8-column groups 1 and 2 trade places (undone where the results are
+  // stored).  Rows are stored at tl4_row (dg_tiled.h).
+  auto frag4w = [&](int stage, int j) -> uint2 {
+    if (TR) {
+      const int h = g16 >> 1, v = tl4_row(i16 < 8 ? 8 * h + i16 : 16 + 8 * h + (i16 - 8)), w = g16 & 1;
       const v2i_t t = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
-          (lds_v2i_t *)(tblk(stage, j) + (v * 4 + (c ^ (tl4_pos(v, 0) & 3))) * 4));
-      return (uint32_t)(kk ? t.y : t.x);
+          (lds_v2i_t *)(tblk(stage, j) + v * 16 + 8 * (w ^ tl4_swz(v))));
+      return __builtin_bit_cast(uint2, t);
     }
-    const uint32_t *sl = reinterpret_cast<const uint32_t *>(lds + stage * 2 * ES_SLICE + ES_SLICE);
-    return sl[tl4_pos(wn * 128 + j * 32 + r32, kk * 2 + g)];
+    const int row = tl4_row(wn * 128 + j * 32 + r32);
+    return *reinterpret_cast<const uint2 *>(lds + stage * 2 * ES_SLICE + ES_SLICE + row * 16 +
+                                            8 * (g ^ tl4_swz(row)));
   };
   // the scale bytes of this wave's four table fragments (byte j for the
   // fragment of rows wn*128 + 32j), broadcast reads of the stage holding
@@ -265,11 +270,12 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   // interleaved (two after each of the first three MFMAs), each step pinned
   // in place, so a fragment is read a full k half before its first use.
   // With ex, the next half's exponents are read too (a new slice).
+  uint32_t q4hi[4];  // B4: the second k half's codes of the current slice
   // nsl: the slice the next k half belongs to
   auto half = [&](const uint4 (&cur)[6], uint4 (&nxt)[6], int nstage, int nkk, bool ex, u16x2_t (&e)[2], int nsl) {
     uint32_t sh[2];
     uint2 q8[4];
-    uint32_t q4[4], s4 = 0;
+    uint32_t q4[4], s4 = 0;  // B4: this half's codes (the second half's kept in q4hi)
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int i = m >> 2, j = m & 3;
@@ -284,8 +290,16 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
           q8[2 * m - 2] = frag8(nstage, nkk, 2 * m - 2);
           q8[2 * m - 1] = frag8(nstage, nkk, 2 * m - 1);
         } else {
-          q4[2 * m - 2] = frag4(nstage, nkk, 2 * m - 2);
-          q4[2 * m - 1] = frag4(nstage, nkk, 2 * m - 1);
+#pragma unroll
+          for (int jj = 2 * m - 2; jj < 2 * m; ++jj) {
+            if (nkk == 0) {  // a new slice: both halves' codes in one read
+              const uint2 t = frag4w(nstage, jj);
+              q4[jj] = t.x;
+              q4hi[jj] = t.y;
+            } else {
+              q4[jj] = q4hi[jj];
+            }
+          }
           if (m == 1) s4 = scales4(nstage, nsl);
         }
         if (SCALED && ex && m == 0) {
@@ -334,10 +348,15 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   __builtin_amdgcn_s_barrier();
   const uint32_t s40 = B4 ? scales4(0, 0) : 0u;
 #pragma unroll
-  for (int f = 0; f < 6; ++f)
-    F0[f] = (B8 && f >= 2) ? widen(frag8(0, 0, f - 2))
-            : (B4 && f >= 2) ? widen4(frag4(0, 0, f - 2), scale4(s40, f - 2))
-                             : frag(0, 0, f);
+  for (int f = 0; f < 6; ++f) {
+    if (B4 && f >= 2) {
+      const uint2 t = frag4w(0, f - 2);
+      q4hi[f - 2] = t.y;
+      F0[f] = widen4(t.x, scale4(s40, f - 2));
+    } else {
+      F0[f] = (B8 && f >= 2) ? widen(frag8(0, 0, f - 2)) : frag(0, 0, f);
+    }
+  }
   if (SCALED) {
     ex[0] = packed(expo(0, 0));
     ex[1] = packed(expo(0, 1));
@@ -566,8 +585,10 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin,
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        // registers 4q..4q+3 are four consecutive columns
-        const int col = n0 + wn * 128 + j * 32 + 8 * q + 4 * (lane >> 5);
+        // registers 4q..4q+3 are four consecutive columns (the fp4 table's
+        // transposing read swaps the fragment's 8-column groups 1 and 2)
+        const int qc = TF == TF_FP4 ? ((q & 1) << 1) | (q >> 1) : q;
+        const int col = n0 + wn * 128 + j * 32 + 8 * qc + 4 * (lane >> 5);
         if (col < N)
           *reinterpret_cast<float4 *>(out + (int64_t)lrow * N + col) =
               make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
