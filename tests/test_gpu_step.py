@@ -217,6 +217,23 @@ def test_ragged_canvas_lockstep():
 
 
 @pytest.mark.usefixtures("logits_dump")
+@pytest.mark.parametrize("table", ["bf16", "fp8", "fp4"])
+def test_partial_column_tile_lockstep(table):
+    """A model width that is not a multiple of 256 (d = 320 = 10 column
+    blocks of 32): the self-conditioning contraction's last 256-column tile
+    reads E transposed with 6 of its 8 column blocks past the table (their
+    reads clamped, their columns never stored); lock-step against the oracle
+    over three steps (two self-conditioned), in each table form (the
+    quantised ones on their grids)."""
+    c = W.config(2, N=96, V=4096, d=320, F=448, Hq=4, Hkv=2, L=130)
+    if table != "bf16":
+        c = dict(c, table=table, table_exp=8 if table == "fp8" else 0)
+    inp = W.make_inputs(c, seed=91)
+    den, rep = lockstep(c, inp, 3)
+    print(rep)
+
+
+@pytest.mark.usefixtures("logits_dump")
 @pytest.mark.parametrize("cfg_id", [3, 4])
 def test_full_size_step_sampled(cfg_id):
     """Full vocabulary (262144) at the configuration's canvas and prefix:
