@@ -39,13 +39,24 @@ __device__ __forceinline__ int kswz(int row, int chunk) { return row * 16 + (chu
 // so the 16 rows a fragment read touches at one group fall on distinct banks.
 __device__ __forceinline__ int vswz(int hd, int u) { return hd * 8 + (u ^ ((hd >> 1) & 7)); }
 
+// The canvas of grid z-slice `z` of a batch launch (canvas c owns z-slices
+// zbase[c] .. zbase[c + 1] - 1: its own split plan) and that slice's split.
+__device__ __forceinline__ int attn_canvas(const AttnBatch &bt, int &z) {
+  int c = 0;
+  while (c + 1 < bt.B && z >= bt.zbase[c + 1]) ++c;
+  z -= bt.zbase[c];
+  return c;
+}
+
 template <int G>
-__global__ void __launch_bounds__(NTH * G) attn_split_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(NTH * G) attn_split_kernel(AttnBatch bt) {
   __shared__ uint4 Ks[2][KT * HD / 8];     // hi, lo: [64 keys][16 chunks of 8]
   __shared__ uint4 Vt[2][HD * KT / 8];     // hi, lo: [128 hd][8 chunks of 8 keys]
 
+  int z = blockIdx.z;
+  const AttnArgs &a = bt.c[attn_canvas(bt, z)];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 5;
-  const int h = blockIdx.y * G + (wave >> 2), z = blockIdx.z;
+  const int h = blockIdx.y * G + (wave >> 2);
   const int g = h / (a.Hq / a.Hkv);
   const int q = blockIdx.x * BQ + (wave & 3) * 32 + (lane & 31);
   const int nk = a.nA + a.nB;
@@ -272,11 +283,12 @@ __global__ void __launch_bounds__(NTH * G) attn_split_kernel(AttnArgs a) {
   }
 }
 
-// Merge of the split-KV partial results (both dtypes).
+// Merge of the split-KV partial results (both dtypes); canvas blockIdx.y of
+// a batch.
 template <typename T>
-__global__ void attn_combine_kernel(const float *__restrict__ part_o, const float *__restrict__ part_ml,
-                                    int splits, int nq, int Hq, int hd, T *__restrict__ out,
-                                    bf16 *__restrict__ out_split, int64_t lo_off) {
+__device__ __forceinline__ void attn_combine_body(const float *__restrict__ part_o, const float *__restrict__ part_ml,
+                                                  int splits, int nq, int Hq, int hd, T *__restrict__ out,
+                                                  bf16 *__restrict__ out_split, int64_t lo_off) {
   const int qh = blockIdx.x;
   const int q = qh / Hq, h = qh % Hq;
   const int e = threadIdx.x;
@@ -302,6 +314,13 @@ __global__ void attn_combine_kernel(const float *__restrict__ part_o, const floa
   }
 }
 
+template <typename T>
+__global__ void attn_combine_kernel(AttnBatch bt) {
+  const AttnArgs &a = bt.c[blockIdx.y];
+  attn_combine_body<T>(a.part_o, a.part_ml, a.splits, a.nq, a.Hq, HD, static_cast<T *>(a.out), a.out_split,
+                       a.out_lo_off ? a.out_lo_off : (int64_t)a.nq * a.Hq * HD);
+}
+
 void attention_plan(int nq, int Hq, int nk, int *splits, int *keys_per_split) {
   const int qb = (nq + BQ - 1) / BQ;
   int want = (512 + qb * Hq - 1) / (qb * Hq);  // aim for ~2 workgroups per CU
@@ -316,17 +335,33 @@ void attention_plan(int nq, int Hq, int nk, int *splits, int *keys_per_split) {
   if (*splits < 1) *splits = 1;
 }
 
-hipError_t attention_mfma(const AttnArgs &a, hipStream_t s) {
-  if ((a.Hq / a.Hkv) % 2 == 0)  // pairs of query heads share their KV head's tiles
-    hipLaunchKernelGGL(attn_split_kernel<2>, dim3((a.nq + BQ - 1) / BQ, a.Hq / 2, a.splits), dim3(NTH * 2), 0, s, a);
+hipError_t attention_mfma_batch(const AttnBatch &bt, hipStream_t s) {
+  if (bt.B < 1 || bt.B > ES_MAX_BATCH || bt.zbase[0] != 0) return hipErrorInvalidValue;
+  const AttnArgs &a0 = bt.c[0];
+  for (int c = 0; c < bt.B; ++c) {  // one grid: the same queries and heads for every canvas
+    const AttnArgs &a = bt.c[c];
+    if (a.nq != a0.nq || a.Hq != a0.Hq || a.Hkv != a0.Hkv || a.hd != HD || a.splits < 1 ||
+        bt.zbase[c + 1] - bt.zbase[c] != a.splits)
+      return hipErrorInvalidValue;
+  }
+  const int zt = bt.zbase[bt.B];
+  if ((a0.Hq / a0.Hkv) % 2 == 0)  // pairs of query heads share their KV head's tiles
+    hipLaunchKernelGGL(attn_split_kernel<2>, dim3((a0.nq + BQ - 1) / BQ, a0.Hq / 2, zt), dim3(NTH * 2), 0, s, bt);
   else
-    hipLaunchKernelGGL(attn_split_kernel<1>, dim3((a.nq + BQ - 1) / BQ, a.Hq, a.splits), dim3(NTH), 0, s, a);
+    hipLaunchKernelGGL(attn_split_kernel<1>, dim3((a0.nq + BQ - 1) / BQ, a0.Hq, zt), dim3(NTH), 0, s, bt);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(attn_combine_kernel<float>, dim3(a.nq * a.Hq), dim3(HD), 0, s, a.part_o,
-                     a.part_ml, a.splits, a.nq, a.Hq, HD, static_cast<float *>(a.out), a.out_split,
-                     a.out_lo_off ? a.out_lo_off : (int64_t)a.nq * a.Hq * HD);
+  hipLaunchKernelGGL(attn_combine_kernel<float>, dim3(a0.nq * a0.Hq, bt.B), dim3(HD), 0, s, bt);
   return hipGetLastError();
+}
+
+hipError_t attention_mfma(const AttnArgs &a, hipStream_t s) {
+  AttnBatch bt{};  // a batch of one: the same kernels, so a canvas's results do not depend on its batch
+  bt.c[0] = a;
+  bt.B = 1;
+  bt.zbase[0] = 0;
+  bt.zbase[1] = a.splits;
+  return attention_mfma_batch(bt, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -121,6 +121,7 @@ StatsLayout stats_layout(const dg_config *c) {
 
 struct Layout {
   size_t h0, h1, nrm, nrm16, nrm_s, sc, sc_s, g, q, kc, vc, o, o_s, ap_o, ap_ml, sc_part, gpart, logits, tok, total;
+  size_t ap_stride_o, ap_stride_ml;  // floats between canvases' attention partials (a batch)
   // prefill view (same region)
   size_t p_x, p_nrm, p_q, p_ap_o, p_ap_ml, p_gpart, p_total;
 };
@@ -160,8 +161,10 @@ Layout layout(const dg_config *c, int32_t nprefill, bool with_logits, int nb = 1
   int splits = 1, kps = 0;
   // the plan for any key count never uses more splits than for 2^20 keys
   dg::attention_plan(Nc, (int)Hq, 1 << 20, &splits, &kps);
-  L.ap_o = take((size_t)splits * Hq * Nc * hd * 4);
-  L.ap_ml = take((size_t)splits * Hq * Nc * 2 * 4);
+  L.ap_stride_o = (size_t)splits * Hq * Nc * hd;
+  L.ap_stride_ml = (size_t)splits * Hq * Nc * 2;
+  L.ap_o = take(nb * L.ap_stride_o * 4);
+  L.ap_ml = take(nb * L.ap_stride_ml * 4);
   L.sc_part = take(bf ? (size_t)selfcond_ksplit(c) * N * d * 4 : 0);
   if (bf) {  // K-split partials of the projections, the largest of the step's four
     const int nqkv[3] = {(int)(Hq * hd), (int)(Hkv * hd), (int)(Hkv * hd)};
@@ -753,11 +756,14 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
       ProfScope ps(g_prof_sc, s);
       DG_TRY(dg::selfcond_bf16_batch(cin, B, tab, N, d, V, true, part, ks, s));
     }
-    for (int b = 0; b < B; ++b)
-      DG_TRY(dg::selfcond_reduce(part + (size_t)b * ks * N * d, ks, N, d,
-                                 reinterpret_cast<const float2 *>(st_of(b, SL.top)), cin.probs[b], V,
-                                 reinterpret_cast<const float *>(st_of(b, SL.rscale)), cin.shift[b], tab,
-                                 sc + (size_t)b * N * d, sc_s + (size_t)b * N * d, s, (int64_t)BN * d));
+    dg::ReduceBatch rb{};
+    for (int b = 0; b < B; ++b) {
+      rb.top[b] = reinterpret_cast<const float2 *>(st_of(b, SL.top));
+      rb.probs[b] = cin.probs[b];
+      rb.row_scale[b] = reinterpret_cast<const float *>(st_of(b, SL.rscale));
+      rb.shift[b] = cin.shift[b];
+    }
+    DG_TRY(dg::selfcond_reduce_batch(part, ks, B, N, d, rb, V, tab, sc, sc_s, s, (int64_t)BN * d));
     dg::Epi eg = epi_store(G, false, F, F, 0);
     eg.kind = dg::EPI_GELU;
     eg.lo_off = (int64_t)BN * F;
@@ -782,8 +788,10 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
                            epi_store(vc, true, hd, hd, (int64_t)BN * hd)};
     DG_TRY(proj(cfg, nrm_s, BN, d, 3, W, No, E3, gpart, s));
   }
+  dg::AttnBatch ab{};  // every canvas's attention in one split launch and one merge launch
+  ab.B = B;
   for (int b = 0; b < B; ++b) {  // canvas b: its queries over [its cache || its own keys]
-    dg::AttnArgs a{};
+    dg::AttnArgs &a = ab.c[b];
     a.q = q + (size_t)b * N * hd;
     a.q_hstride = (int64_t)BN * hd;
     a.nq = N;
@@ -803,11 +811,12 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
     a.out = o + (size_t)b * N * Hq * hd;
     a.out_split = o_s + (size_t)b * N * Hq * hd;
     a.out_lo_off = (int64_t)BN * Hq * hd;
-    a.part_o = reinterpret_cast<float *>(base + L.ap_o);
-    a.part_ml = reinterpret_cast<float *>(base + L.ap_ml);
+    a.part_o = reinterpret_cast<float *>(base + L.ap_o) + (size_t)b * L.ap_stride_o;
+    a.part_ml = reinterpret_cast<float *>(base + L.ap_ml) + (size_t)b * L.ap_stride_ml;
     dg::attention_plan(N, Hq, caches[b].length + N, &a.splits, &a.keys_per_split);
-    DG_TRY(dg::attention_mfma(a, s));
+    ab.zbase[b + 1] = ab.zbase[b] + a.splits;
   }
+  DG_TRY(dg::attention_mfma_batch(ab, s));
   {
     dg::Epi ea = epi_store(h1, true, d, d, 0);
     ea.kind = dg::EPI_ADD;

@@ -225,6 +225,17 @@ struct AttnArgs {
 };
 // head_dim 128 on the MFMA (split-bf16 products), split-KV + merge
 hipError_t attention_mfma(const AttnArgs &a, hipStream_t s);
+// Several canvases' attention in one split launch and one merge launch:
+// canvas c (same nq, Hq, Hkv for all) with its own buffers, partials and
+// split plan, its splits at grid z-slices zbase[c] .. zbase[c + 1] - 1.  A
+// single canvas is a batch of one, so each canvas's results are those of
+// its own launch bit for bit.
+struct AttnBatch {
+  AttnArgs c[DG_MAX_BATCH];
+  int zbase[DG_MAX_BATCH + 1];
+  int B;
+};
+hipError_t attention_mfma_batch(const AttnBatch &bt, hipStream_t s);
 // fp32 path (head_dim <= 128, a multiple of 16) on the fp32 MFMA
 hipError_t attention_f32(const AttnArgs &a, hipStream_t s);
 void attention_plan(int nq, int Hq, int nk, int *splits, int *keys_per_split);
@@ -254,6 +265,18 @@ hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const fl
                            const uint16_t *probs_tiled, int V, const float *row_scale, const uint8_t *shift,
                            const PackedTable &E, float *out, uint16_t *out_split, hipStream_t s,
                            int64_t lo_off = 0);
+// The same for B canvases in one launch: canvas c's partials at
+// part + c * ksplit * N * d, its rows of out / out_split at c * N * d (lo
+// terms at + lo_off, 0: + B * N * d), its state at the c-th pointers.
+struct ReduceBatch {
+  const float2 *top[DG_MAX_BATCH];
+  const uint16_t *probs[DG_MAX_BATCH];
+  const float *row_scale[DG_MAX_BATCH];
+  const uint8_t *shift[DG_MAX_BATCH];
+};
+hipError_t selfcond_reduce_batch(const float *part, int ksplit, int B, int N, int d, const ReduceBatch &rb, int V,
+                                 const PackedTable &E, float *out, uint16_t *out_split, hipStream_t s,
+                                 int64_t lo_off = 0);
 // The token ids of B canvases (src.p[c], N each) copied into one array
 // out[B * N], canvas after canvas.
 struct TokenPtrs {

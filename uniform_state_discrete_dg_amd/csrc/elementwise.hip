@@ -129,21 +129,25 @@ template hipError_t rmsnorm_rows<bf16>(const float *, const bf16 *, int, int, fl
 // row's dominant token: the contraction used p~ = g * (the tiled value at
 // (row, a) scaled by 2^-shift of a's tile, as the contraction scaled it),
 // the previous step's exact probability of a is p_a, so S += (p_a - p~) E[a].
-__global__ void selfcond_reduce_kernel(const float *__restrict__ part, int ksplit, int N, int d,
-                                       const float2 *__restrict__ top, const bf16 *__restrict__ probs, int V,
-                                       const float *__restrict__ row_scale, const uint8_t *__restrict__ shift,
-                                       PackedTable E, float *__restrict__ out, bf16 *__restrict__ out_split,
+// Canvas blockIdx.z of a batch (a single canvas is a batch of one): its
+// partials at part + c * ksplit * N * d, its output rows at c * N * d.
+__global__ void selfcond_reduce_kernel(const float *__restrict__ part, int ksplit, int N, int d, ReduceBatch rb,
+                                       int V, PackedTable E, float *__restrict__ out, bf16 *__restrict__ out_split,
                                        int64_t lo_off) {
   // one thread per 4 consecutive columns of one row; d % 4 == 0
-  const int row = blockIdx.y;
+  const int row = blockIdx.y, c = blockIdx.z;
   const int k = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (k >= d) return;
-  const int64_t i = (int64_t)row * d + k;
   const int64_t count = (int64_t)N * d;
+  const int64_t i = (int64_t)row * d + k, io = c * count + i;
+  const float *pc = part + (int64_t)c * ksplit * count;
+  const float2 *top = rb.top[c];
+  const float *row_scale = rb.row_scale[c];
+  const uint8_t *shift = rb.shift[c];
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 8
   for (int z = 0; z < ksplit; ++z) {
-    const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)z * count + i);
+    const float4 v = *reinterpret_cast<const float4 *>(pc + (int64_t)z * count + i);
     acc.x += v.x;
     acc.y += v.y;
     acc.z += v.z;
@@ -154,21 +158,21 @@ __global__ void selfcond_reduce_kernel(const float *__restrict__ part, int kspli
   if (top) {
     const float2 tp = top[row];
     const int a = __float_as_int(tp.x);
-    int bits = probs[tl_index(row, a, V)];
+    int bits = rb.probs[c][tl_index(row, a, V)];
     if (shift) bits = max(bits - ((int)shift[(int64_t)(a >> 6) * 256 + row] << 7), 0);
-    const float c = tp.y - g * bf16_to_f32((bf16)bits);
+    const float cf = tp.y - g * bf16_to_f32((bf16)bits);
     const float4 e = table_get4(E, a, k);
-    acc.x += c * e.x;
-    acc.y += c * e.y;
-    acc.z += c * e.z;
-    acc.w += c * e.w;
+    acc.x += cf * e.x;
+    acc.y += cf * e.y;
+    acc.z += cf * e.z;
+    acc.w += cf * e.w;
   }
-  *reinterpret_cast<float4 *>(out + i) = acc;
+  *reinterpret_cast<float4 *>(out + io) = acc;
   if (out_split) {
     uint2 hi, lo;
     split4(acc, hi, lo);
-    *reinterpret_cast<uint2 *>(out_split + i) = hi;
-    *reinterpret_cast<uint2 *>(out_split + lo_off + i) = lo;
+    *reinterpret_cast<uint2 *>(out_split + io) = hi;
+    *reinterpret_cast<uint2 *>(out_split + lo_off + io) = lo;
   }
 }
 
@@ -302,13 +306,26 @@ hipError_t tile_fp4(const uint16_t *X, int R, int K, int64_t ldx, bool trans, ui
   return hipGetLastError();
 }
 
+hipError_t selfcond_reduce_batch(const float *part, int ksplit, int B, int N, int d, const ReduceBatch &rb, int V,
+                                 const PackedTable &E, float *out, uint16_t *out_split, hipStream_t s,
+                                 int64_t lo_off) {
+  if (B < 1 || B > ES_MAX_BATCH || d % 4) return hipErrorInvalidValue;
+  for (int c = 0; c < B; ++c)
+    if (rb.top[c] && (!E.p || E.d != d || !rb.probs[c])) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((d / 4 + 255) / 256, N, B), dim3(256), 0, s, part, ksplit, N, d,
+                     rb, V, E, out, out_split, lo_off ? lo_off : (int64_t)B * N * d);
+  return hipGetLastError();
+}
+
 hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const float2 *top, const uint16_t *probs,
                            int V, const float *row_scale, const uint8_t *shift, const PackedTable &E, float *out,
                            uint16_t *out_split, hipStream_t s, int64_t lo_off) {
-  if (d % 4 || (top && (!E.p || E.d != d))) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((d / 4 + 255) / 256, N), dim3(256), 0, s, part, ksplit, N, d,
-                     top, probs, V, row_scale, shift, E, out, out_split, lo_off ? lo_off : (int64_t)N * d);
-  return hipGetLastError();
+  ReduceBatch rb{};  // a batch of one: the same kernel, so a canvas's S does not depend on its batch
+  rb.top[0] = top;
+  rb.probs[0] = probs;
+  rb.row_scale[0] = row_scale;
+  rb.shift[0] = shift;
+  return selfcond_reduce_batch(part, ksplit, 1, N, d, rb, V, E, out, out_split, s, lo_off ? lo_off : (int64_t)N * d);
 }
 
 // Numerators -> probabilities, in place (fp32 path, row-major [N][V]).
