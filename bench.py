@@ -84,7 +84,7 @@ def lm_head_bytes(c: dict) -> float:
 
 
 def selfcond_bytes(c: dict) -> float:
-    """E^T once and the bf16 probabilities once."""
+    """The table once (read transposed) and the bf16 probabilities once."""
     N, V, d = c["N"], c["V"], c["d"]
     return float(V * d * 2 + N * V * 2)
 
@@ -93,18 +93,32 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lm_head_n256_v262k_d2816.
 KERNEL_SRC = os.path.join(ROOT, "uniform_state_discrete_dg_amd", "csrc", "estream.hip")
 
 
+def kernel_code_sha256() -> str:
+    """sha256 of the streaming kernels' source with its // comments, trailing
+    blanks and empty lines removed: a change to the code invalidates the
+    counter summary, a change to the comments does not."""
+    import hashlib
+    lines = []
+    for line in open(KERNEL_SRC).read().splitlines():
+        i = line.find("//")
+        if i >= 0:
+            line = line[:i]
+        line = line.rstrip()
+        if line:
+            lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per LM-head launch from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration),
-    or None when the kernel source has changed since it was taken."""
-    import hashlib
+    or None when the kernel code has changed since it was taken."""
     try:
         kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line)
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if kv.get("kernel_source_sha256") != src:
+    if kv.get("kernel_code_sha256") != kernel_code_sha256():
         return None
     try:
         return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])

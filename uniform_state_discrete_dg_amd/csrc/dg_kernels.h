@@ -94,10 +94,11 @@ struct RowNorm {
 hipError_t gemm_split_norm(const SplitGemm &g, const RowNorm &rn, hipStream_t s);
 // Canvas rows per workgroup of the two table-streaming kernels (128 or 256).
 int estream_bm(int M);
-// The self-conditioning contraction: A = probs (tiled bf16), B = E^T (tiled,
-// d rows), K = V split in ksplit ranges; writes f32 partials [ksplit][M][N].
-// shift (nullable; uint8 [K/64][256]): A's value at (row, k) is the stored
-// bf16 times 2^-shift[k / 64][row], applied exactly on the exponent field.
+// The self-conditioning contraction (selfcond_bf16_batch below): A = probs
+// (tiled bf16), B = the packed table E read transposed, K = V split in
+// ksplit ranges; writes f32 partials [ksplit][M][N].  shift (uint8
+// [K/64][256]): A's value at (row, k) is the stored bf16 times
+// 2^-shift[k / 64][row], applied exactly on the exponent field.
 // guard: a launch made before the host knows whether the canvas loop stops
 // after the previous step; every workgroup returns at once when the status
 // words (written by that step's selection) say stop.

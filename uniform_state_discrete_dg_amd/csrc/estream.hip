@@ -3,9 +3,10 @@
 //   * the tied LM head z = RMSNorm(h1) E^T, with the softmax/entropy
 //     statistics fused into its epilogue (the logits never reach memory; the
 //     probability numerators are written once in bf16), and
-//   * the self-conditioning contraction S = p_prev E, streaming E^T and
-//     split over V, with the probability numerators' power-of-two tile
-//     exponents applied as they are read.
+//   * the self-conditioning contraction S = p_prev E, streaming the same
+//     copy of E (transposed on its way out of LDS) split over V, with the
+//     probability numerators' power-of-two tile exponents applied as they
+//     are read.
 // At a 256-row canvas both sit at the chip's ridge point (256 flop per byte
 // of the table: HBM and matrix cores would finish together), and with both
 // busy the chip runs at its power limit (the shader clock drops to about
@@ -23,7 +24,8 @@
 // block is 16 KB of consecutive memory already in LDS order (chunk c of row
 // r at position c ^ ((r >> 2) & 3), which keeps the 32 rows a fragment read
 // touches, 16 lanes at a time, on distinct banks), so every DMA instruction
-// copies 1 KB of consecutive bytes.
+// copies 1 KB of consecutive bytes (the self-conditioning contraction's
+// table slice: 8 runs of 2 KB, see TR below).
 //
 // The MFMA takes the table fragment as its first operand, so a lane's
 // accumulators hold one canvas row and 16 of the 32 table rows of a
