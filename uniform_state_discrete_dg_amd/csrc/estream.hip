@@ -46,6 +46,8 @@ constexpr int ES_BK = 32;         // k per slice
 constexpr int ES_STAGES = 4;      // LDS stages (3 slices in flight)
 constexpr int ES_SLICE = ES_BM * ES_BK * 2;  // bytes of one operand slice (16 KB)
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int ES_STAGE_NUM = 8 * ES_SLICE;             // LM head staging: 8 slices of numerators ...
+constexpr int ES_STAGE_LDS = ES_STAGE_NUM + ES_BM * 64;  // ... then 256 rows x 4 tiles of statistics
 static_assert(ES_BM == TL_ROWS && ES_BN == TL_ROWS && ES_BK == TL_K, "slices are tiled-layout blocks");
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= n, no wait on exp/lgkm.
@@ -414,14 +416,20 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
                                  acc, nullptr, nullptr, tab.scale,
                                  TF == TF_FP4 ? tab.s4 + (int64_t)jt * ksl * TL4_SCALES : nullptr);
   const int ntiles = V / 64;
+  // The numerators and statistics are staged in LDS (free once the ring has
+  // drained) and leave as contiguous runs: each canvas row's 64 bytes of a
+  // 32-column slice, and its 4 tiles' statistics, are consecutive in the
+  // canvas's buffers, so a wave stores 1 KB runs instead of 8-byte pieces
+  // of 64-byte lines.  Staging: slice ls (0..7) at ls * 16 KB, row r's
+  // chunks at r * 64 in stored order (tl_pos of the canvas's own row);
+  // statistics at ES_STAGE_NUM + r * 64 + 16 * (local tile).
+  char *stage_num = lds, *stage_st = lds + ES_STAGE_NUM;
 
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = wm * 64 + i * 32 + (lane & 31);
     const int grow = bb * ES_BM + row;  // stacked row
     const int c = BATCH ? min(grow, M - 1) / N : 0, lrow = grow - c * N;  // c < M / N even past the last row
-    bf16 *__restrict__ probs = cv.probs[c];
-    float4 *__restrict__ tile_stats = cv.tile_stats[c];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int tile = (n0 + wn * 128 + h * 64) / 64;
@@ -450,8 +458,10 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
       }
       const float m = best * inv_T;
       // stored numerators are exp(y - m) * f = 2^(y log2e - r), r = ceil(m log2e):
-      // the tile's reference is a power of two (see row_combine)
-      const float f = exp2f(m * LOG2E - ceilf(m * LOG2E));
+      // the tile's reference is a power of two (see row_combine).  The
+      // hardware exp2 serves every term: it returns no denormals, so a term
+      // below 2^-126 of the tile's largest counts as zero.
+      const float f = __builtin_amdgcn_exp2f(m * LOG2E - ceilf(m * LOG2E));
       float l = 0.f, sacc = 0.f;
       uint32_t pk[2][8];
 #pragma unroll
@@ -459,37 +469,60 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const float t0 = acc[i][2 * h + jj][r] * inv_T - m, t1 = acc[i][2 * h + jj][r + 1] * inv_T - m;
-          const float e0 = exp2f(t0 * LOG2E), e1 = exp2f(t1 * LOG2E);
+          const float e0 = __builtin_amdgcn_exp2f(t0 * LOG2E), e1 = __builtin_amdgcn_exp2f(t1 * LOG2E);
           l += e0 + e1;
           sacc += e0 * t0 + e1 * t1;
           pk[jj][r >> 1] = pack_bf16x2(e0 * f, e1 * f);
         }
       l += __shfl_xor(l, 32);
       sacc += __shfl_xor(sacc, 32);
-      if (grow < M) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          // slice 2 tile + jj; the lane's four values of chunk q are elements 4g..4g+3
-          bf16 *blk = probs + (int64_t)(2 * tile + jj) * TL_ELEMS + 4 * g;
+      for (int jj = 0; jj < 2; ++jj) {
+        // local slice wn * 4 + 2h + jj; the lane's four values of chunk q are elements 4g..4g+3
+        char *sl = stage_num + (wn * 4 + 2 * h + jj) * ES_SLICE + row * 64 + g * 8;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<uint2 *>(blk + tl_pos(lrow, q) * 8) = make_uint2(pk[jj][2 * q], pk[jj][2 * q + 1]);
-            if (logits) {
-              const f32x16_t &z = acc[i][2 * h + jj];
-              *reinterpret_cast<float4 *>(logits + (int64_t)grow * V + cbase + 32 * jj + 8 * q) =
-                  make_float4(z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]);
-            }
+        for (int q = 0; q < 4; ++q) {
+          *reinterpret_cast<uint2 *>(sl + (q ^ ((lrow >> 2) & 3)) * 16) = make_uint2(pk[jj][2 * q], pk[jj][2 * q + 1]);
+          if (logits && grow < M) {
+            const f32x16_t &z = acc[i][2 * h + jj];
+            *reinterpret_cast<float4 *>(logits + (int64_t)grow * V + cbase + 32 * jj + 8 * q) =
+                make_float4(z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]);
           }
         }
-        if (g == 0) tile_stats[(int64_t)lrow * ntiles + tile] = make_float4(best, l, sacc, __int_as_float(bcol));
       }
+      if (g == 0)
+        *reinterpret_cast<float4 *>(stage_st + row * 64 + (wn * 2 + h) * 16) =
+            make_float4(best, l, sacc, __int_as_float(bcol));
     }
   }
+  __syncthreads();
+  // copy out: thread t moves the 16-byte chunk t % 4 of rows t / 4 and
+  // t / 4 + 128, in each of the 8 slices and of the statistics
+  const int u4 = threadIdx.x & 3;
+#pragma unroll
+  for (int rh = 0; rh < 2; ++rh) {
+    const int row = (threadIdx.x >> 2) + rh * 128;
+    const int grow = bb * ES_BM + row;
+    if (grow >= M) continue;
+    const int c = BATCH ? grow / N : 0, lrow = grow - c * N;
+    char *dst = reinterpret_cast<char *>(cv.probs[c]) + (int64_t)(n0 / 32) * ES_SLICE + lrow * 64 + u4 * 16;
+    const char *src = stage_num + row * 64 + u4 * 16;
+#pragma unroll
+    for (int ls = 0; ls < 8; ++ls)
+      *reinterpret_cast<uint4 *>(dst + ls * ES_SLICE) = *reinterpret_cast<const uint4 *>(src + ls * ES_SLICE);
+    reinterpret_cast<uint4 *>(cv.tile_stats[c] + (int64_t)lrow * ntiles + n0 / 64)[u4] =
+        *reinterpret_cast<const uint4 *>(stage_st + row * 64 + u4 * 16);
+  }
 }
+
 
 int estream_bm(int) { return ES_BM; }
 
 static size_t es_lds_bytes() { return (size_t)ES_STAGES * (2 * ES_SLICE + 256 + 32); }
+// the LM head also stages its 256 x 256 numerators and statistics
+static size_t es_lds_bytes_lm() {
+  return es_lds_bytes() > (size_t)ES_STAGE_LDS ? es_lds_bytes() : (size_t)ES_STAGE_LDS;
+}
 
 static bool table_ok(const PackedTable &t, int d) {
   return t.p && t.d == d && (t.tf == TF_BF16 || t.tf == TF_FP8 || (t.tf == TF_FP4 && t.s4));
@@ -508,7 +541,7 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
                               reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_FP4>),
                               reinterpret_cast<const void *>(lm_head_es_kernel<true, TF_FP4>)};
         for (const void *f : fns) {
-          const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes());
+          const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes_lm());
           if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -518,7 +551,7 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
   const int items = (V / ES_BN) * nblk;
   const dim3 grid(B == 1 ? items : (items + 7) / 8 * 8);
 #define DG_LM_LAUNCH(BT, TF)                                                                              \
-  hipLaunchKernelGGL((lm_head_es_kernel<BT, TF>), grid, dim3(ES_NT), es_lds_bytes(), s, A_tiled, M, N, K, tab, \
+  hipLaunchKernelGGL((lm_head_es_kernel<BT, TF>), grid, dim3(ES_NT), es_lds_bytes_lm(), s, A_tiled, M, N, K, tab, \
                      V, inv_T, cv, nblk, items, logits_dump)
 #define DG_LM_FORMS(BT)                                   \
   do {                                                    \
