@@ -46,6 +46,7 @@ constexpr int ES_BK = 32;         // k per slice
 constexpr int ES_STAGES = 4;      // LDS stages (3 slices in flight)
 constexpr int ES_SLICE = ES_BM * ES_BK * 2;  // bytes of one operand slice (16 KB)
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 constexpr int ES_STAGE_NUM = 8 * ES_SLICE;             // LM head staging: 8 slices of numerators ...
 constexpr int ES_STAGE_LDS = ES_STAGE_NUM + ES_BM * 64;  // ... then 256 rows x 4 tiles of statistics
 static_assert(ES_BM == TL_ROWS && ES_BN == TL_ROWS && ES_BK == TL_K, "slices are tiled-layout blocks");
@@ -457,25 +458,29 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
         }
       }
       const float m = best * inv_T;
-      // stored numerators are exp(y - m) * f = 2^(y log2e - r), r = ceil(m log2e):
-      // the tile's reference is a power of two (see row_combine).  The
-      // hardware exp2 serves every term: it returns no denormals, so a term
-      // below 2^-126 of the tile's largest counts as zero.
-      const float f = __builtin_amdgcn_exp2f(m * LOG2E - ceilf(m * LOG2E));
-      float l = 0.f, sacc = 0.f;
+      // stored numerators are 2^(y log2e - r) = exp(y - m) * f with
+      // r = ceil(m log2e) and f = 2^-(r - m log2e): the tile's reference is
+      // a power of two (see row_combine).  Each is one fma and one exp2,
+      // x = z (log2e / T) - r; l = sum exp(y - m) and s = sum exp(y - m)(y - m)
+      // follow from the sums of n = 2^x and n x, since y - m = (x + dl) / log2e
+      // with dl = r - m log2e.  The hardware exp2 returns no denormals: a
+      // term below 2^-126 of the tile's largest counts as zero.
+      const float r = ceilf(m * LOG2E), dl = r - m * LOG2E, c1 = inv_T * LOG2E;
+      float ln = 0.f, sn = 0.f;
       uint32_t pk[2][8];
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float t0 = acc[i][2 * h + jj][r] * inv_T - m, t1 = acc[i][2 * h + jj][r + 1] * inv_T - m;
-          const float e0 = __builtin_amdgcn_exp2f(t0 * LOG2E), e1 = __builtin_amdgcn_exp2f(t1 * LOG2E);
-          l += e0 + e1;
-          sacc += e0 * t0 + e1 * t1;
-          pk[jj][r >> 1] = pack_bf16x2(e0 * f, e1 * f);
+        for (int v = 0; v < 16; v += 2) {
+          const float x0 = fmaf(acc[i][2 * h + jj][v], c1, -r), x1 = fmaf(acc[i][2 * h + jj][v + 1], c1, -r);
+          const float n0 = __builtin_amdgcn_exp2f(x0), n1 = __builtin_amdgcn_exp2f(x1);
+          ln += n0 + n1;
+          sn = fmaf(n0, x0, fmaf(n1, x1, sn));
+          pk[jj][v >> 1] = pack_bf16x2(n0, n1);
         }
-      l += __shfl_xor(l, 32);
-      sacc += __shfl_xor(sacc, 32);
+      ln += __shfl_xor(ln, 32);
+      sn += __shfl_xor(sn, 32);
+      const float inv_f = __builtin_amdgcn_exp2f(dl), l = ln * inv_f, sacc = fmaf(dl, ln, sn) * (inv_f * LN2);
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         // local slice wn * 4 + 2h + jj; the lane's four values of chunk q are elements 4g..4g+3
