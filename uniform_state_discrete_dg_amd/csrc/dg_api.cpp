@@ -165,7 +165,7 @@ Layout layout(const dg_config *c, int32_t nprefill, bool with_logits, int nb = 1
   L.ap_stride_ml = (size_t)splits * Hq * Nc * 2;
   L.ap_o = take(nb * L.ap_stride_o * 4);
   L.ap_ml = take(nb * L.ap_stride_ml * 4);
-  L.sc_part = take(bf ? (size_t)selfcond_ksplit(c) * N * d * 4 : 0);
+  L.sc_part = take(bf ? dg::selfcond_part_bytes(nb, Nc, (int)d, selfcond_ksplit(c)) : 0);
   if (bf) {  // K-split partials of the projections, the largest of the step's four
     const int nqkv[3] = {(int)(Hq * hd), (int)(Hkv * hd), (int)(Hkv * hd)};
     const int nd[1] = {(int)d}, nf[1] = {(int)F};

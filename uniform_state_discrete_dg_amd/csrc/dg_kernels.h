@@ -96,9 +96,23 @@ hipError_t gemm_split_norm(const SplitGemm &g, const RowNorm &rn, hipStream_t s)
 int estream_bm(int M);
 // The self-conditioning contraction (selfcond_bf16_batch below): A = probs
 // (tiled bf16), B = the packed table E read transposed, K = V split in
-// ksplit ranges; writes f32 partials [ksplit][M][N].  shift (uint8
-// [K/64][256]): A's value at (row, k) is the stored bf16 times
-// 2^-shift[k / 64][row], applied exactly on the exponent field.
+// ksplit ranges.  shift (uint8 [K/64][256]): A's value at (row, k) is the
+// stored bf16 times 2^-shift[k / 64][row], applied exactly on the exponent
+// field.
+// The f32 partials are stored in register order, one 256 x 256 block per
+// (operand block b, K range kc, column tile nt) at float offset
+// ((b * ksplit + kc) * ceil(N / 256) + nt) * 65536; inside it the float4
+// at slot s = (((w * 2 + i) * 4 + j) * 4 + q) * 64 + l holds block row
+// 64 (w / 2) + 32 i + l % 32 and columns 256 nt + 128 (w % 2) + 32 j +
+// 8 q + 4 (l / 32) .. + 3 (so one store instruction writes 1 KB).  Operand
+// block b is canvas b, or (selfcond_paired) canvases 2b (rows 0..127) and
+// 2b + 1 (rows 128..255).  Slots of rows or columns past the canvas are not
+// written.
+inline bool selfcond_paired(int B, int M) { return B > 1 && 2 * M <= 256; }
+inline int selfcond_blocks(int B, int M) { return selfcond_paired(B, M) ? (B + 1) / 2 : B; }
+inline size_t selfcond_part_bytes(int B, int M, int N, int ksplit) {
+  return (size_t)selfcond_blocks(B, M) * ksplit * ((N + 255) / 256) * 65536 * 4;
+}
 // guard: a launch made before the host knows whether the canvas loop stops
 // after the previous step; every workgroup returns at once when the status
 // words (written by that step's selection) say stop.
@@ -257,7 +271,7 @@ template <typename T>
 hipError_t rmsnorm_rows(const float *x, const T *g, int n, int d, float eps, float *out, bf16 *out_tiled,
                         bf16 *out_split, hipStream_t s);
 // S (fp32 [N][d]) = row_scale[row] (1 when null) * the sum of the ksplit
-// partials + exact correction of each row's dominant token (top = (token
+// partials (the contraction's register-order blocks) + exact correction of each row's dominant token (top = (token
 // bits, exact p); nullable): the contraction used the value of probs
 // (tiled) at (row, a), scaled by 2^-shift of a's tile when shift is given,
 // times row_scale.  out_split (nullable): S also as a split pair [N][d], lo
@@ -266,9 +280,9 @@ hipError_t selfcond_reduce(const float *part, int ksplit, int N, int d, const fl
                            const uint16_t *probs_tiled, int V, const float *row_scale, const uint8_t *shift,
                            const PackedTable &E, float *out, uint16_t *out_split, hipStream_t s,
                            int64_t lo_off = 0);
-// The same for B canvases in one launch: canvas c's partials at
-// part + c * ksplit * N * d, its rows of out / out_split at c * N * d (lo
-// terms at + lo_off, 0: + B * N * d), its state at the c-th pointers.
+// The same for B canvases in one launch (the partials of the batched
+// contraction): canvas c's rows of out / out_split at c * N * d (lo terms
+// at + lo_off, 0: + B * N * d), its state at the c-th pointers.
 struct ReduceBatch {
   const float2 *top[DG_MAX_BATCH];
   const uint16_t *probs[DG_MAX_BATCH];

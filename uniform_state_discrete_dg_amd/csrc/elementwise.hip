@@ -129,25 +129,33 @@ template hipError_t rmsnorm_rows<bf16>(const float *, const bf16 *, int, int, fl
 // row's dominant token: the contraction used p~ = g * (the tiled value at
 // (row, a) scaled by 2^-shift of a's tile, as the contraction scaled it),
 // the previous step's exact probability of a is p_a, so S += (p_a - p~) E[a].
-// Canvas blockIdx.z of a batch (a single canvas is a batch of one): its
-// partials at part + c * ksplit * N * d, its output rows at c * N * d.
-__global__ void selfcond_reduce_kernel(const float *__restrict__ part, int ksplit, int N, int d, ReduceBatch rb,
-                                       int V, PackedTable E, float *__restrict__ out, bf16 *__restrict__ out_split,
-                                       int64_t lo_off) {
-  // one thread per 4 consecutive columns of one row; d % 4 == 0
-  const int row = blockIdx.y, c = blockIdx.z;
-  const int k = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (k >= d) return;
+// One thread per float4 slot of the contraction's register-order blocks
+// (selfcond_part_bytes): slot blockIdx.x * 256 + thread of column tile
+// blockIdx.y of operand block blockIdx.z, so the ksplit partial reads are
+// contiguous across a wave; the slot's canvas row and 4 columns follow from
+// its index.  Canvas c of a batch (a single canvas is a batch of one) has
+// its output rows at c * N * d.
+__global__ void __launch_bounds__(256) selfcond_reduce_kernel(const float *__restrict__ part, int ksplit, int B, int N,
+                                                            int d, int paired, ReduceBatch rb, int V, PackedTable E,
+                                                            float *__restrict__ out, bf16 *__restrict__ out_split,
+                                                            int64_t lo_off) {
+  const int sl = blockIdx.x * 256 + threadIdx.x, nt = blockIdx.y, blk = blockIdx.z, ntn = gridDim.y;
+  const int l = sl & 63, q = (sl >> 6) & 3, j = (sl >> 8) & 3, ii = (sl >> 10) & 1, w = sl >> 11;
+  const int brow = (w >> 1) * 64 + 32 * ii + (l & 31);
+  const int k = nt * 256 + (w & 1) * 128 + 32 * j + 8 * q + 4 * (l >> 5);
+  const int c = paired ? 2 * blk + (brow >> 7) : blk, row = paired ? brow & 127 : brow;
+  if (c >= B || row >= N || k >= d) return;  // slots the contraction did not write
   const int64_t count = (int64_t)N * d;
   const int64_t i = (int64_t)row * d + k, io = c * count + i;
-  const float *pc = part + (int64_t)c * ksplit * count;
+  const float *pc = part + (((int64_t)blk * ksplit * ntn + nt) << 16) + (sl << 2);
+  const int64_t zstride = (int64_t)ntn << 16;
   const float2 *top = rb.top[c];
   const float *row_scale = rb.row_scale[c];
   const uint8_t *shift = rb.shift[c];
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 8
   for (int z = 0; z < ksplit; ++z) {
-    const float4 v = *reinterpret_cast<const float4 *>(pc + (int64_t)z * count + i);
+    const float4 v = *reinterpret_cast<const float4 *>(pc + z * zstride);
     acc.x += v.x;
     acc.y += v.y;
     acc.z += v.z;
@@ -312,8 +320,10 @@ hipError_t selfcond_reduce_batch(const float *part, int ksplit, int B, int N, in
   if (B < 1 || B > ES_MAX_BATCH || d % 4) return hipErrorInvalidValue;
   for (int c = 0; c < B; ++c)
     if (rb.top[c] && (!E.p || E.d != d || !rb.probs[c])) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(selfcond_reduce_kernel, dim3((d / 4 + 255) / 256, N, B), dim3(256), 0, s, part, ksplit, N, d,
-                     rb, V, E, out, out_split, lo_off ? lo_off : (int64_t)B * N * d);
+  if (N > 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(selfcond_reduce_kernel, dim3(64, (d + 255) / 256, selfcond_blocks(B, N)), dim3(256), 0, s, part,
+                     ksplit, B, N, d, selfcond_paired(B, N) ? 1 : 0, rb, V, E, out, out_split,
+                     lo_off ? lo_off : (int64_t)B * N * d);
   return hipGetLastError();
 }
 

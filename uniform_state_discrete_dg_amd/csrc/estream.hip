@@ -615,22 +615,25 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin,
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  // the block of partials in register order (selfcond_part_bytes): each
+  // store instruction writes 64 lanes x 16 consecutive bytes
+  float *out = part + ((((int64_t)blk * ksplit + kc) * ntn + nt) << 16);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = wm * 64 + i * 32 + (lane & 31);
     const int c = MODE == 2 ? 2 * blk + (row >> 7) : blk, lrow = MODE == 2 ? row & 127 : row;
     if (lrow >= M || c >= nb) continue;
-    float *out = part + ((int64_t)c * ksplit + kc) * M * N;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        // registers 4q..4q+3 are four consecutive columns (the fp4 table's
-        // transposing read swaps the fragment's 8-column groups 1 and 2)
+        // registers 4q..4q+3 are four consecutive columns, 8-column group qc
+        // of the fragment (the fp4 table's transposing read swaps groups 1
+        // and 2); the slot is that of group qc
         const int qc = TF == TF_FP4 ? ((q & 1) << 1) | (q >> 1) : q;
         const int col = n0 + wn * 128 + j * 32 + 8 * qc + 4 * (lane >> 5);
         if (col < N)
-          *reinterpret_cast<float4 *>(out + (int64_t)lrow * N + col) =
+          *reinterpret_cast<float4 *>(out + (((((wave * 2 + i) * 4 + j) * 4 + qc) * 64 + lane) << 2)) =
               make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
       }
   }
@@ -657,7 +660,7 @@ hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const PackedTable
         return hipSuccess;
       }) != hipSuccess)
     return hipErrorInvalidValue;
-  const int mode = B == 1 ? 0 : (M <= ES_BM / 2 ? 2 : 1);
+  const int mode = B == 1 ? 0 : (selfcond_paired(B, M) ? 2 : 1);
   const int ntn = (N + ES_BN - 1) / ES_BN;
   const int items = ntn * ksplit * (mode == 2 ? (B + 1) / 2 : B);
   const dim3 grid((items + 7) / 8 * 8);
