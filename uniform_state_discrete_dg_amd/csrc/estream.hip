@@ -102,7 +102,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // E column.  Without TR, Bt is the workgroup's block row of the table (slice
 // s at s blocks on) and Bs4 its scale bytes (slice s at Bs4 + 8 s); with TR
 // Bs4 is the table's whole scale array.
-template <bool SCALED, bool PAIR = false, int TF = TF_BF16, bool TR = false>
+template <bool SCALED, bool PAIR = false, int TF = TF_BF16, bool TR = false, int NW = 8>
 __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const uint8_t *__restrict__ Bt,
                                              const uint8_t *__restrict__ shift, int sb, int se, char *lds,
                                              f32x16_t (&acc)[2][4], const bf16 *__restrict__ At2 = nullptr,
@@ -110,8 +110,11 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
                                              const uint8_t *__restrict__ Bs4 = nullptr, int tr_ksd = 0,
                                              int tr_d0 = 0) {
   constexpr bool B8 = TF == TF_FP8, B4 = TF == TF_FP4, BQ = B8 || B4;
+  static_assert(NW == 8 || (NW == 4 && !PAIR), "8 waves (256 canvas rows) or 4 (128 rows, one canvas)");
   // bytes of one 256 x 32 block of the table, and of one of its rows
   constexpr int BLK = B8 ? TL8_BYTES : B4 ? TL4_BYTES : TL_ELEMS * 2, ROWB = BLK / 256;
+  // the table slice is copied in 8 parts of BLK / 8 bytes, part p by wave p % NW
+  constexpr int NPART = 8 / NW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r32 = lane & 31, g = lane >> 5;
@@ -125,19 +128,24 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
 
   const int nk = se - sb;
   if (nk <= 0) return;
-  // DMA: this wave copies 2 KB of each operand slice (2 instructions of 64
-  // lanes x 16 bytes), chunks p = (2 wave + u) * 64 + lane.
+  // DMA: this wave copies 2 KB of the canvas operand's slice (2 instructions
+  // of 64 lanes x 16 bytes), chunks p = (2 wave + u) * 64 + lane: rows
+  // 0 .. 32 NW - 1.
   // PAIR: rows 128..255 of the canvas operand (chunks 512..1023, copied by
   // waves 4..7) are rows 0..127 of a second block At2, and their exponents
   // (bytes 128..255 of a tile's row, lanes 32..63) rows 0..127 of shift2.
   const bf16 *asrc = (PAIR && wave >= 4) ? At2 + (int64_t)sb * TL_ELEMS + ((wave - 4) * 2 * 64 + lane) * 8
                                          : At + (int64_t)sb * TL_ELEMS + (wave * 2 * 64 + lane) * 8;
   const uint8_t *ssrc = !SCALED ? nullptr : (PAIR && lane >= 32) ? shift2 + (lane - 32) * 4 : shift + lane * 4;
-  // this lane's 16 bytes of each DMA instruction of the table slice: bf16
-  // 2 instructions of 64 lanes per wave, fp8 1, fp4 1 of 32 lanes
+  // this lane's 16 bytes of each DMA instruction of a table part: bf16
+  // 2 instructions of 64 lanes per part, fp8 1, fp4 1 of 32 lanes
   const int blane = (B4 ? (lane & 31) : lane) * 16;
-  const uint8_t *bsrc = TR ? Bt + (int64_t)min(tr_d0 + wave, tr_ksd - 1) * BLK + blane
-                           : Bt + (int64_t)sb * BLK + wave * (BLK / 8) + blane;
+  const uint8_t *bsrc[NPART];
+#pragma unroll
+  for (int v = 0; v < NPART; ++v) {
+    const int pt = wave + NW * v;
+    bsrc[v] = TR ? Bt + (int64_t)min(tr_d0 + pt, tr_ksd - 1) * BLK + blane : Bt + (int64_t)sb * BLK + pt * (BLK / 8) + blane;
+  }
   char *lds_shift = lds + ES_STAGES * 2 * ES_SLICE;  // SCALED: [stage][256] bytes
   char *lds_s4 = lds_shift + ES_STAGES * 256;         // B4: [stage][32] bytes, the slice's 8 scales
   auto issue = [&](int slice, int stage) {
@@ -147,32 +155,35 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
     for (int u = 0; u < 2; ++u) {
       __builtin_amdgcn_global_load_lds(asrc + off + u * 512, st + (wave * 2 + u) * 1024, 16, 0, 0);
     }
-    // the table slice: BLK / 8 bytes per wave (rows 32 sg .. + 31 of a block
-    // with TR, 32 of its 256 rows otherwise)
+    // the table slice: BLK / 8 bytes per part (rows 32 sg .. + 31 of column
+    // block tr_d0 + p with TR, rows 32 p .. + 31 of the block otherwise)
     const int sg = sb + min(slice, nk - 1);
-    const uint8_t *bs = TR ? bsrc + (int64_t)(sg >> 3) * tr_ksd * BLK + (sg & 7) * 32 * ROWB
-                           : bsrc + (int64_t)min(slice, nk - 1) * BLK;
-    char *bd = st + ES_SLICE + wave * (BLK / 8);
-    if (!BQ) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) __builtin_amdgcn_global_load_lds(bs + u * 1024, bd + u * 1024, 16, 0, 0);
-    } else if (B8 || lane < 32) {
-      __builtin_amdgcn_global_load_lds(bs, bd, 16, 0, 0);
+    for (int v = 0; v < NPART; ++v) {
+      const uint8_t *bs = TR ? bsrc[v] + (int64_t)(sg >> 3) * tr_ksd * BLK + (sg & 7) * 32 * ROWB
+                             : bsrc[v] + (int64_t)min(slice, nk - 1) * BLK;
+      char *bd = st + ES_SLICE + (wave + NW * v) * (BLK / 8);
+      if (!BQ) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) __builtin_amdgcn_global_load_lds(bs + u * 1024, bd + u * 1024, 16, 0, 0);
+      } else if (B8 || lane < 32) {
+        __builtin_amdgcn_global_load_lds(bs, bd, 16, 0, 0);
+      }
     }
-    if (SCALED && wave == (slice & 7))  // the slice tile's 256 row exponents, 4 bytes per lane
+    if (SCALED && wave == (slice & (NW - 1)))  // the slice tile's 256 row exponents, 4 bytes per lane
       __builtin_amdgcn_global_load_lds(ssrc + (int64_t)((sb + min(slice, nk - 1)) >> 1) * 256,
                                        lds_shift + stage * 256, 4, 0, 0);
-    if (B4 && !TR && wave == (slice & 7) && lane < 2)  // the slice's 8 block scales, 4 bytes per lane
+    if (B4 && !TR && wave == (slice & (NW - 1)) && lane < 2)  // the slice's 8 block scales, 4 bytes per lane
       __builtin_amdgcn_global_load_lds(Bs4 + (int64_t)sg * 8 + lane * 4, lds_s4 + stage * 32, 4, 0, 0);
-    if (B4 && TR && wave == (slice & 7) && lane < 8)  // lane l: the 4 bytes holding block tr_d0 + l's scale
+    if (B4 && TR && wave == (slice & (NW - 1)) && lane < 8)  // lane l: the 4 bytes holding block tr_d0 + l's scale
       __builtin_amdgcn_global_load_lds(
           Bs4 + (((int64_t)(sg >> 3) * tr_ksd + min(tr_d0 + lane, tr_ksd - 1)) * TL4_SCALES + ((sg & 7) & ~3)),
           lds_s4 + stage * 32, 4, 0, 0);
   };
-  // DMA instructions per slice per wave: 4 (3 with an fp8 or fp4 table),
-  // plus XTRA more for wave s % 8 on slice s (exponents when SCALED, fp4
-  // block scales)
-  constexpr int PER = BQ ? 3 : 4;
+  // DMA instructions per slice per wave: 2 for the canvas operand plus 2
+  // (bf16) or 1 (fp8, fp4) per table part, plus XTRA more for wave s % NW
+  // on slice s (exponents when SCALED, fp4 block scales)
+  constexpr int PER = 2 + NPART * (BQ ? 1 : 2);
   constexpr int XTRA = (SCALED ? 1 : 0) + (B4 ? 1 : 0);
 
   // Fragment f of one 16-wide k step as stored: f < 2 a canvas fragment
@@ -370,7 +381,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   }
   for (int it = 0; it < nk; ++it) {
     half(F0, F1, it & 3, 1, false, ex, it);  // second half of slice it, same exponents
-    if (XTRA && wave == ((it + 2) & 7))  // this wave's copies of slice it+1 landed ...
+    if (XTRA && wave == ((it + 2) & (NW - 1)))  // this wave's copies of slice it+1 landed ...
       wait_vmcnt<PER + XTRA>();
     else
       wait_vmcnt<PER>();
@@ -397,8 +408,8 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
 // run back to back on one XCD, so the table tile comes from HBM once and from
 // that XCD's L2 for the other blocks.
 // ---------------------------------------------------------------------------
-template <bool BATCH, int TF>
-__global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__restrict__ At, int M, int N, int K,
+template <bool BATCH, int TF, int NW = 8>
+__global__ void __launch_bounds__(NW * 64, 1) lm_head_es_kernel(const bf16 *__restrict__ At, int M, int N, int K,
                                                               PackedTable tab, int V, float inv_T, EsCanvases cv,
                                                               int nblk, int items, float *__restrict__ logits) {
   extern __shared__ __align__(16) char lds[];
@@ -412,7 +423,7 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
   const int ksl = K / ES_BK;
   f32x16_t acc[2][4];
   constexpr int BLK = TF == TF_FP8 ? TL8_BYTES : TF == TF_FP4 ? TL4_BYTES : TL_ELEMS * 2;
-  estream_tile<false, false, TF>(At + (int64_t)bb * ksl * TL_ELEMS,
+  estream_tile<false, false, TF, false, NW>(At + (int64_t)bb * ksl * TL_ELEMS,
                                  static_cast<const uint8_t *>(tab.p) + (int64_t)jt * ksl * BLK, nullptr, 0, ksl, lds,
                                  acc, nullptr, nullptr, tab.scale,
                                  TF == TF_FP4 ? tab.s4 + (int64_t)jt * ksl * TL4_SCALES : nullptr);
@@ -506,7 +517,7 @@ __global__ void __launch_bounds__(ES_NT, 1) lm_head_es_kernel(const bf16 *__rest
   const int u4 = threadIdx.x & 3;
 #pragma unroll
   for (int rh = 0; rh < 2; ++rh) {
-    const int row = (threadIdx.x >> 2) + rh * 128;
+    const int row = (threadIdx.x >> 2) + rh * NW * 16;  // rows 0 .. 32 NW - 1
     const int grow = bb * ES_BM + row;
     if (grow >= M) continue;
     const int c = BATCH ? grow / N : 0, lrow = grow - c * N;
@@ -539,12 +550,15 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
   if (!table_ok(tab, K)) return hipErrorInvalidValue;
   static std::atomic<uint64_t> attr{0};
   if (once_per_device(attr, [] {
-        const void *fns[6] = {reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_BF16>),
+        const void *fns[9] = {reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_BF16>),
                               reinterpret_cast<const void *>(lm_head_es_kernel<true, TF_BF16>),
                               reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_FP8>),
                               reinterpret_cast<const void *>(lm_head_es_kernel<true, TF_FP8>),
                               reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_FP4>),
-                              reinterpret_cast<const void *>(lm_head_es_kernel<true, TF_FP4>)};
+                              reinterpret_cast<const void *>(lm_head_es_kernel<true, TF_FP4>),
+                              reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_BF16, 4>),
+                              reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_FP8, 4>),
+                              reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_FP4, 4>)};
         for (const void *f : fns) {
           const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes_lm());
           if (e != hipSuccess) return e;
@@ -555,17 +569,20 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
   const int M = B * N, nblk = (M + ES_BM - 1) / ES_BM;
   const int items = (V / ES_BN) * nblk;
   const dim3 grid(B == 1 ? items : (items + 7) / 8 * 8);
-#define DG_LM_LAUNCH(BT, TF)                                                                              \
-  hipLaunchKernelGGL((lm_head_es_kernel<BT, TF>), grid, dim3(ES_NT), es_lds_bytes_lm(), s, A_tiled, M, N, K, tab, \
-                     V, inv_T, cv, nblk, items, logits_dump)
-#define DG_LM_FORMS(BT)                                   \
-  do {                                                    \
-    if (tab.tf == TF_FP8) DG_LM_LAUNCH(BT, TF_FP8);       \
-    else if (tab.tf == TF_FP4) DG_LM_LAUNCH(BT, TF_FP4);  \
-    else DG_LM_LAUNCH(BT, TF_BF16);                       \
+  // one canvas of at most 128 rows: 4 waves over its 128 rows, not 8 over
+  // 256 with half of them padding
+#define DG_LM_LAUNCH(BT, TF, NW)                                                                      \
+  hipLaunchKernelGGL((lm_head_es_kernel<BT, TF, NW>), grid, dim3(NW * 64), es_lds_bytes_lm(), s, A_tiled, M, N, K, \
+                     tab, V, inv_T, cv, nblk, items, logits_dump)
+#define DG_LM_FORMS(BT, NW)                                   \
+  do {                                                        \
+    if (tab.tf == TF_FP8) DG_LM_LAUNCH(BT, TF_FP8, NW);       \
+    else if (tab.tf == TF_FP4) DG_LM_LAUNCH(BT, TF_FP4, NW);  \
+    else DG_LM_LAUNCH(BT, TF_BF16, NW);                       \
   } while (0)
-  if (B == 1) DG_LM_FORMS(false);
-  else DG_LM_FORMS(true);
+  if (B == 1 && 2 * N <= ES_BM) DG_LM_FORMS(false, 4);
+  else if (B == 1) DG_LM_FORMS(false, 8);
+  else DG_LM_FORMS(true, 8);
 #undef DG_LM_FORMS
 #undef DG_LM_LAUNCH
   return hipGetLastError();
@@ -582,9 +599,10 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
 // ---------------------------------------------------------------------------
 // MODE: 0 one canvas; 1 a batch, one canvas per 256-row block; 2 a batch of
 // canvases of at most 128 rows, two per block (canvas 2p in rows 0..127,
-// canvas 2p + 1 in rows 128..255, read from its own buffers).
+// canvas 2p + 1 in rows 128..255, read from its own buffers); 3 one canvas
+// of at most 128 rows, 4 waves over its 128 rows.
 template <bool SCALED, int MODE, int TF>
-__global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin, PackedTable tab, int M, int N,
+__global__ void __launch_bounds__(MODE == 3 ? ES_NT / 2 : ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin, PackedTable tab, int M, int N,
                                                                int K, float *__restrict__ part, int ksplit, int ntn,
                                                                int nb, int items, SelfcondGuard guard) {
   extern __shared__ __align__(16) char lds[];
@@ -593,7 +611,8 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin,
   const int item = (b % 8) * per_xcd + b / 8;
   if (item >= items || guard.stopped()) return;
   const int nblk = MODE == 2 ? (nb + 1) / 2 : nb;  // canvas operand blocks
-  const int blk = MODE == 0 ? 0 : item % nblk, kn = MODE == 0 ? item : item / nblk;
+  constexpr bool ONE = MODE == 0 || MODE == 3;
+  const int blk = ONE ? 0 : item % nblk, kn = ONE ? item : item / nblk;
   const int kc = kn / ntn, nt = kn % ntn;
   const int ksl = K / ES_BK;
   const int sb = (int)((int64_t)ksl * kc / ksplit), se = (int)((int64_t)ksl * (kc + 1) / ksplit);
@@ -610,8 +629,8 @@ __global__ void __launch_bounds__(ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin,
     estream_tile<SCALED, true, TF, true>(cin.probs[c0], Bt, cin.shift[c0], sb, se, lds, acc, A2, s2, tab.scale,
                                          tab.s4, ksd, 8 * nt);
   } else {
-    estream_tile<SCALED, false, TF, true>(cin.probs[blk], Bt, cin.shift[blk], sb, se, lds, acc, nullptr, nullptr,
-                                          tab.scale, tab.s4, ksd, 8 * nt);
+    estream_tile<SCALED, false, TF, true, MODE == 3 ? 4 : 8>(cin.probs[blk], Bt, cin.shift[blk], sb, se, lds, acc,
+                                                            nullptr, nullptr, tab.scale, tab.s4, ksd, 8 * nt);
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -647,11 +666,11 @@ hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const PackedTable
   static std::atomic<uint64_t> attr{0};
   if (once_per_device(attr, [] {
 #define DG_SC_FN(SC, MD, TF) reinterpret_cast<const void *>(selfcond_es_kernel<SC, MD, TF>)
-#define DG_SC_FN6(TF) \
+#define DG_SC_FN8(TF) \
   DG_SC_FN(false, 0, TF), DG_SC_FN(true, 0, TF), DG_SC_FN(false, 1, TF), DG_SC_FN(true, 1, TF), \
-      DG_SC_FN(false, 2, TF), DG_SC_FN(true, 2, TF)
-        const void *fns[18] = {DG_SC_FN6(TF_BF16), DG_SC_FN6(TF_FP8), DG_SC_FN6(TF_FP4)};
-#undef DG_SC_FN6
+      DG_SC_FN(false, 2, TF), DG_SC_FN(true, 2, TF), DG_SC_FN(false, 3, TF), DG_SC_FN(true, 3, TF)
+        const void *fns[24] = {DG_SC_FN8(TF_BF16), DG_SC_FN8(TF_FP8), DG_SC_FN8(TF_FP4)};
+#undef DG_SC_FN8
 #undef DG_SC_FN
         for (const void *f : fns) {
           const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes());
@@ -660,18 +679,19 @@ hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const PackedTable
         return hipSuccess;
       }) != hipSuccess)
     return hipErrorInvalidValue;
-  const int mode = B == 1 ? 0 : (selfcond_paired(B, M) ? 2 : 1);
+  const int mode = B == 1 ? (2 * M <= ES_BM ? 3 : 0) : (selfcond_paired(B, M) ? 2 : 1);
   const int ntn = (N + ES_BN - 1) / ES_BN;
   const int items = ntn * ksplit * (mode == 2 ? (B + 1) / 2 : B);
   const dim3 grid((items + 7) / 8 * 8);
-#define DG_SC_LAUNCH(SC, MD, TF)                                                                                \
-  hipLaunchKernelGGL((selfcond_es_kernel<SC, MD, TF>), grid, dim3(ES_NT), es_lds_bytes(), s, cin, tab, M, N, K, \
-                     partials, ksplit, ntn, B, items, guard)
+#define DG_SC_LAUNCH(SC, MD, TF)                                                                                 \
+  hipLaunchKernelGGL((selfcond_es_kernel<SC, MD, TF>), grid, dim3(MD == 3 ? ES_NT / 2 : ES_NT), es_lds_bytes(), s, \
+                     cin, tab, M, N, K, partials, ksplit, ntn, B, items, guard)
 #define DG_SC_MODES(SC, TF)                      \
   do {                                           \
     if (mode == 0) DG_SC_LAUNCH(SC, 0, TF);      \
     else if (mode == 1) DG_SC_LAUNCH(SC, 1, TF); \
-    else DG_SC_LAUNCH(SC, 2, TF);                \
+    else if (mode == 2) DG_SC_LAUNCH(SC, 2, TF); \
+    else DG_SC_LAUNCH(SC, 3, TF);                \
   } while (0)
 #define DG_SC_FORMS(SC)                                \
   do {                                                 \
