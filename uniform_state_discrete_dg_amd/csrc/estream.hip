@@ -43,19 +43,33 @@ constexpr int ES_NT = 512;        // 8 waves
 constexpr int ES_BM = 256;        // canvas rows per workgroup
 constexpr int ES_BN = 256;        // table rows per workgroup
 constexpr int ES_BK = 32;         // k per slice
-constexpr int ES_STAGES = 4;      // LDS stages (3 slices in flight)
 constexpr int ES_SLICE = ES_BM * ES_BK * 2;  // bytes of one operand slice (16 KB)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-constexpr int ES_STAGE_NUM = 8 * ES_SLICE;             // LM head staging: 8 slices of numerators ...
-constexpr int ES_STAGE_LDS = ES_STAGE_NUM + ES_BM * 64;  // ... then 256 rows x 4 tiles of statistics
+// LDS of a workgroup of NW waves (32 NW canvas rows) and STG stages: each
+// stage holds the canvas operand's slice (NW * 2 KB) then the table's
+// (16 KB), then come the exponents ([stage][256]) and fp4 scales
+// ([stage][32]).  Four stages keep three slices in flight; so do three, by
+// refilling the stage of the slice just read (its LDS reads are waited for
+// before the barrier), in less LDS: the 4-wave LM head uses three, so that
+// two of its workgroups share a CU.  The LM head stages its numerators
+// (8 slices of NW * 2 KB) and statistics (32 NW rows x 64 bytes) in the
+// same memory afterwards.
+constexpr int es_abytes(int NW) { return NW * 2048; }
+constexpr int es_stage_bytes(int NW) { return es_abytes(NW) + ES_SLICE; }
+constexpr int es_lds(int NW, int STG) { return STG * (es_stage_bytes(NW) + 256 + 32); }
+constexpr int es_lm_stages(int NW) { return NW == 8 ? 4 : 3; }
+constexpr int es_lds_lm(int NW) {
+  return es_lds(NW, es_lm_stages(NW)) > 9 * es_abytes(NW) ? es_lds(NW, es_lm_stages(NW)) : 9 * es_abytes(NW);
+}
 static_assert(ES_BM == TL_ROWS && ES_BN == TL_ROWS && ES_BK == TL_K, "slices are tiled-layout blocks");
 
-// s_waitcnt immediate (gfx9 encoding): vmcnt <= n, no wait on exp/lgkm.
-template <int n>
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= n, no wait on exp, and on
+// lgkm only with lgkm0 (then every LDS read issued has returned).
+template <int n, bool lgkm0 = false>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | ((lgkm0 ? 0 : 0xF) << 8));
 }
 
 }  // namespace
@@ -102,7 +116,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // E column.  Without TR, Bt is the workgroup's block row of the table (slice
 // s at s blocks on) and Bs4 its scale bytes (slice s at Bs4 + 8 s); with TR
 // Bs4 is the table's whole scale array.
-template <bool SCALED, bool PAIR = false, int TF = TF_BF16, bool TR = false, int NW = 8>
+template <bool SCALED, bool PAIR = false, int TF = TF_BF16, bool TR = false, int NW = 8, int STG = 4>
 __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const uint8_t *__restrict__ Bt,
                                              const uint8_t *__restrict__ shift, int sb, int se, char *lds,
                                              f32x16_t (&acc)[2][4], const bf16 *__restrict__ At2 = nullptr,
@@ -111,6 +125,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
                                              int tr_d0 = 0) {
   constexpr bool B8 = TF == TF_FP8, B4 = TF == TF_FP4, BQ = B8 || B4;
   static_assert(NW == 8 || (NW == 4 && !PAIR), "8 waves (256 canvas rows) or 4 (128 rows, one canvas)");
+  static_assert(STG == 3 || STG == 4, "three or four LDS stages");
   // bytes of one 256 x 32 block of the table, and of one of its rows
   constexpr int BLK = B8 ? TL8_BYTES : B4 ? TL4_BYTES : TL_ELEMS * 2, ROWB = BLK / 256;
   // the table slice is copied in 8 parts of BLK / 8 bytes, part p by wave p % NW
@@ -146,11 +161,12 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
     const int pt = wave + NW * v;
     bsrc[v] = TR ? Bt + (int64_t)min(tr_d0 + pt, tr_ksd - 1) * BLK + blane : Bt + (int64_t)sb * BLK + pt * (BLK / 8) + blane;
   }
-  char *lds_shift = lds + ES_STAGES * 2 * ES_SLICE;  // SCALED: [stage][256] bytes
-  char *lds_s4 = lds_shift + ES_STAGES * 256;         // B4: [stage][32] bytes, the slice's 8 scales
+  constexpr int AB = es_abytes(NW), SB = es_stage_bytes(NW);
+  char *lds_shift = lds + STG * SB;          // SCALED: [stage][256] bytes
+  char *lds_s4 = lds_shift + STG * 256;      // B4: [stage][32] bytes, the slice's 8 scales
   auto issue = [&](int slice, int stage) {
     const int64_t off = (int64_t)min(slice, nk - 1) * TL_ELEMS;  // past the end: a repeat, never read
-    char *st = lds + stage * 2 * ES_SLICE;
+    char *st = lds + stage * SB;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       __builtin_amdgcn_global_load_lds(asrc + off + u * 512, st + (wave * 2 + u) * 1024, 16, 0, 0);
@@ -162,7 +178,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
     for (int v = 0; v < NPART; ++v) {
       const uint8_t *bs = TR ? bsrc[v] + (int64_t)(sg >> 3) * tr_ksd * BLK + (sg & 7) * 32 * ROWB
                              : bsrc[v] + (int64_t)min(slice, nk - 1) * BLK;
-      char *bd = st + ES_SLICE + (wave + NW * v) * (BLK / 8);
+      char *bd = st + AB + (wave + NW * v) * (BLK / 8);
       if (!BQ) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) __builtin_amdgcn_global_load_lds(bs + u * 1024, bd + u * 1024, 16, 0, 0);
@@ -196,7 +212,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
   typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
   const int g16 = lane >> 4, i16 = lane & 15;
   auto tblk = [&](int stage, int j) -> const char * {
-    return lds + stage * 2 * ES_SLICE + ES_SLICE + (wn * 4 + j) * (BLK / 8);
+    return lds + stage * SB + AB + (wn * 4 + j) * (BLK / 8);
   };
   auto frag = [&](int stage, int kk, int f) -> uint4 {
     if (TR && f >= 2) {  // two 4-row reads: lane i16 gets column 16 (g16 & 1) + i16, rows 8 (g16 >> 1) + 0..7
@@ -212,7 +228,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
       }
       return make_uint4(r[0].x, r[0].y, r[1].x, r[1].y);
     }
-    const uint4 *sl = reinterpret_cast<const uint4 *>(lds + stage * 2 * ES_SLICE + (f < 2 ? 0 : ES_SLICE));
+    const uint4 *sl = reinterpret_cast<const uint4 *>(lds + stage * SB + (f < 2 ? 0 : AB));
     const int row = f < 2 ? wm * 64 + f * 32 + r32 : wn * 128 + (f - 2) * 32 + r32;
     return sl[tl_pos(row, kk * 2 + g)];
   };
@@ -224,7 +240,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
           (lds_v2i_t *)(tblk(stage, j) + (v * 4 + (c ^ (tl8_pos(v, 0) & 3))) * 8));
       return __builtin_bit_cast(uint2, t);
     }
-    const uint2 *sl = reinterpret_cast<const uint2 *>(lds + stage * 2 * ES_SLICE + ES_SLICE);
+    const uint2 *sl = reinterpret_cast<const uint2 *>(lds + stage * SB + AB);
     return sl[tl8_pos(wn * 128 + j * 32 + r32, kk * 2 + g)];
   };
   // B4: the 8 bytes holding table fragment j's 8 fp4 values for both k
@@ -242,7 +258,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
       return __builtin_bit_cast(uint2, t);
     }
     const int row = tl4_row(wn * 128 + j * 32 + r32);
-    return *reinterpret_cast<const uint2 *>(lds + stage * 2 * ES_SLICE + ES_SLICE + row * 16 +
+    return *reinterpret_cast<const uint2 *>(lds + stage * SB + AB + row * 16 +
                                             8 * (g ^ tl4_swz(row)));
   };
   // the scale bytes of this wave's four table fragments (byte j for the
@@ -380,15 +396,17 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
     scale(F0[1], ex[1]);
   }
   for (int it = 0; it < nk; ++it) {
-    half(F0, F1, it & 3, 1, false, ex, it);  // second half of slice it, same exponents
-    if (XTRA && wave == ((it + 2) & (NW - 1)))  // this wave's copies of slice it+1 landed ...
-      wait_vmcnt<PER + XTRA>();
+    half(F0, F1, it % STG, 1, false, ex, it);  // second half of slice it, same exponents
+    // this wave's copies of slice it+1 landed (with 3 stages also its LDS
+    // reads of slice it returned) ...
+    if (XTRA && wave == ((it + 2) & (NW - 1)))
+      wait_vmcnt<PER + XTRA, STG == 3>();
     else
-      wait_vmcnt<PER>();
-    __builtin_amdgcn_s_barrier();  // ... every wave's; every wave is done with slice it-1
-    issue(it + 3, (it + 3) & 3);
+      wait_vmcnt<PER, STG == 3>();
+    __builtin_amdgcn_s_barrier();  // ... every wave's; every wave is done with slice it-1 (3 stages: it)
+    issue(it + 3, (it + 3) % STG);
     __builtin_amdgcn_sched_barrier(0);
-    half(F1, F0, (it + 1) & 3, 0, true, ex, it + 1);  // past the last slice: a repeat, unused
+    half(F1, F0, (it + 1) % STG, 0, true, ex, it + 1);  // past the last slice: a repeat, unused
   }
   wait_vmcnt<0>();  // retire the trailing (unused) prefetches before LDS is reused
   __builtin_amdgcn_s_barrier();
@@ -409,7 +427,7 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
 // that XCD's L2 for the other blocks.
 // ---------------------------------------------------------------------------
 template <bool BATCH, int TF, int NW = 8>
-__global__ void __launch_bounds__(NW * 64, 1) lm_head_es_kernel(const bf16 *__restrict__ At, int M, int N, int K,
+__global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) lm_head_es_kernel(const bf16 *__restrict__ At, int M, int N, int K,
                                                               PackedTable tab, int V, float inv_T, EsCanvases cv,
                                                               int nblk, int items, float *__restrict__ logits) {
   extern __shared__ __align__(16) char lds[];
@@ -423,7 +441,7 @@ __global__ void __launch_bounds__(NW * 64, 1) lm_head_es_kernel(const bf16 *__re
   const int ksl = K / ES_BK;
   f32x16_t acc[2][4];
   constexpr int BLK = TF == TF_FP8 ? TL8_BYTES : TF == TF_FP4 ? TL4_BYTES : TL_ELEMS * 2;
-  estream_tile<false, false, TF, false, NW>(At + (int64_t)bb * ksl * TL_ELEMS,
+  estream_tile<false, false, TF, false, NW, es_lm_stages(NW)>(At + (int64_t)bb * ksl * TL_ELEMS,
                                  static_cast<const uint8_t *>(tab.p) + (int64_t)jt * ksl * BLK, nullptr, 0, ksl, lds,
                                  acc, nullptr, nullptr, tab.scale,
                                  TF == TF_FP4 ? tab.s4 + (int64_t)jt * ksl * TL4_SCALES : nullptr);
@@ -434,8 +452,9 @@ __global__ void __launch_bounds__(NW * 64, 1) lm_head_es_kernel(const bf16 *__re
   // canvas's buffers, so a wave stores 1 KB runs instead of 8-byte pieces
   // of 64-byte lines.  Staging: slice ls (0..7) at ls * 16 KB, row r's
   // chunks at r * 64 in stored order (tl_pos of the canvas's own row);
-  // statistics at ES_STAGE_NUM + r * 64 + 16 * (local tile).
-  char *stage_num = lds, *stage_st = lds + ES_STAGE_NUM;
+  // statistics at 8 * (NW * 2 KB) + r * 64 + 16 * (local tile).
+  constexpr int AB = es_abytes(NW);
+  char *stage_num = lds, *stage_st = lds + 8 * AB;
 
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -495,7 +514,7 @@ __global__ void __launch_bounds__(NW * 64, 1) lm_head_es_kernel(const bf16 *__re
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         // local slice wn * 4 + 2h + jj; the lane's four values of chunk q are elements 4g..4g+3
-        char *sl = stage_num + (wn * 4 + 2 * h + jj) * ES_SLICE + row * 64 + g * 8;
+        char *sl = stage_num + (wn * 4 + 2 * h + jj) * AB + row * 64 + g * 8;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           *reinterpret_cast<uint2 *>(sl + (q ^ ((lrow >> 2) & 3)) * 16) = make_uint2(pk[jj][2 * q], pk[jj][2 * q + 1]);
@@ -525,7 +544,7 @@ __global__ void __launch_bounds__(NW * 64, 1) lm_head_es_kernel(const bf16 *__re
     const char *src = stage_num + row * 64 + u4 * 16;
 #pragma unroll
     for (int ls = 0; ls < 8; ++ls)
-      *reinterpret_cast<uint4 *>(dst + ls * ES_SLICE) = *reinterpret_cast<const uint4 *>(src + ls * ES_SLICE);
+      *reinterpret_cast<uint4 *>(dst + ls * ES_SLICE) = *reinterpret_cast<const uint4 *>(src + ls * AB);
     reinterpret_cast<uint4 *>(cv.tile_stats[c] + (int64_t)lrow * ntiles + n0 / 64)[u4] =
         *reinterpret_cast<const uint4 *>(stage_st + row * 64 + u4 * 16);
   }
@@ -534,11 +553,10 @@ __global__ void __launch_bounds__(NW * 64, 1) lm_head_es_kernel(const bf16 *__re
 
 int estream_bm(int) { return ES_BM; }
 
-static size_t es_lds_bytes() { return (size_t)ES_STAGES * (2 * ES_SLICE + 256 + 32); }
-// the LM head also stages its 256 x 256 numerators and statistics
-static size_t es_lds_bytes_lm() {
-  return es_lds_bytes() > (size_t)ES_STAGE_LDS ? es_lds_bytes() : (size_t)ES_STAGE_LDS;
-}
+// the self-conditioning contraction: four stages (one workgroup per CU)
+static size_t es_lds_bytes(int NW = 8) { return (size_t)(NW == 8 ? es_lds(8, 4) : es_lds(4, 4)); }
+// the LM head also stages its numerators and statistics
+static size_t es_lds_bytes_lm(int NW = 8) { return (size_t)(NW == 8 ? es_lds_lm(8) : es_lds_lm(4)); }
 
 static bool table_ok(const PackedTable &t, int d) {
   return t.p && t.d == d && (t.tf == TF_BF16 || t.tf == TF_FP8 || (t.tf == TF_FP4 && t.s4));
@@ -572,7 +590,7 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
   // one canvas of at most 128 rows: 4 waves over its 128 rows, not 8 over
   // 256 with half of them padding
 #define DG_LM_LAUNCH(BT, TF, NW)                                                                      \
-  hipLaunchKernelGGL((lm_head_es_kernel<BT, TF, NW>), grid, dim3(NW * 64), es_lds_bytes_lm(), s, A_tiled, M, N, K, \
+  hipLaunchKernelGGL((lm_head_es_kernel<BT, TF, NW>), grid, dim3(NW * 64), es_lds_bytes_lm(NW), s, A_tiled, M, N, K, \
                      tab, V, inv_T, cv, nblk, items, logits_dump)
 #define DG_LM_FORMS(BT, NW)                                   \
   do {                                                        \
@@ -684,7 +702,8 @@ hipError_t selfcond_bf16_batch(const EsCanvasesIn &cin, int B, const PackedTable
   const int items = ntn * ksplit * (mode == 2 ? (B + 1) / 2 : B);
   const dim3 grid((items + 7) / 8 * 8);
 #define DG_SC_LAUNCH(SC, MD, TF)                                                                                 \
-  hipLaunchKernelGGL((selfcond_es_kernel<SC, MD, TF>), grid, dim3(MD == 3 ? ES_NT / 2 : ES_NT), es_lds_bytes(), s, \
+  hipLaunchKernelGGL((selfcond_es_kernel<SC, MD, TF>), grid, dim3(MD == 3 ? ES_NT / 2 : ES_NT),                   \
+                     es_lds_bytes(MD == 3 ? 4 : 8), s, \
                      cin, tab, M, N, K, partials, ksplit, ntn, B, items, guard)
 #define DG_SC_MODES(SC, TF)                      \
   do {                                           \
