@@ -189,8 +189,8 @@ Layout layout(const dg_config *c, int32_t nprefill, bool with_logits, int nb = 1
   L.p_ap_ml = take((size_t)splits * Hq * n * 2 * 4);
   if (bf && n) {
     const int nkvq[3] = {(int)(Hkv * hd), (int)(Hkv * hd), (int)(Hq * hd)};
-    L.p_gpart = take(std::max(dg::gemm_split_part_bytes((int)n, (int)d, nkvq, 3),
-                              dg::gemm_split_part_bytes((int)n, (int)d, nkvq, 2)));
+    L.p_gpart = take(std::max(dg::gemm_split_part_bytes((int)n, (int)d, nkvq, 2),
+                              dg::gemm_split_part_bytes((int)n, (int)d, nkvq + 2, 1)));
   }
   L.p_total = off;
   return L;
@@ -467,7 +467,12 @@ dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cac
   const dg::Epi E3[3] = {epi_store(kbase, true, hd, hd, (int64_t)cap * hd),
                          epi_store(vbase, true, hd, hd, (int64_t)cap * hd),
                          epi_store(q, true, hd, hd, (int64_t)n * hd)};
-  DG_TRY(proj(cfg, nrm, n, d, attn_out ? 3 : 2, W, No, E3, reinterpret_cast<float *>(base + L.p_gpart), s));
+  // K and V in one launch whether or not the prompt's attention output is
+  // wanted (the split of K follows the launch's shape, so the cache's bits do
+  // not depend on that choice); Q in a launch of its own
+  float *gp = reinterpret_cast<float *>(base + L.p_gpart);
+  DG_TRY(proj(cfg, nrm, n, d, 2, W, No, E3, gp, s));
+  if (attn_out) DG_TRY(proj(cfg, nrm, n, d, 1, W + 2, No + 2, E3 + 2, gp, s));
   if (attn_out) {
     dg::AttnArgs a{};
     a.q = q;
