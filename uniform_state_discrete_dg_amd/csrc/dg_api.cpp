@@ -169,10 +169,10 @@ Layout layout(const dg_config *c, int32_t nprefill, bool with_logits, int nb = 1
   if (bf) {  // K-split partials of the projections, the largest of the step's four
     const int nqkv[3] = {(int)(Hq * hd), (int)(Hkv * hd), (int)(Hkv * hd)};
     const int nd[1] = {(int)d}, nf[1] = {(int)F};
-    size_t m = dg::gemm_split_part_bytes((int)N, (int)d, nqkv, 3);
-    m = std::max(m, dg::gemm_split_part_bytes((int)N, (int)(Hq * hd), nd, 1));
-    m = std::max(m, dg::gemm_split_part_bytes((int)N, (int)d, nf, 1));
-    m = std::max(m, dg::gemm_split_part_bytes((int)N, (int)F, nd, 1));
+    size_t m = dg::gemm_split_part_bytes((int)N, Nc, (int)d, nqkv, 3);
+    m = std::max(m, dg::gemm_split_part_bytes((int)N, Nc, (int)(Hq * hd), nd, 1));
+    m = std::max(m, dg::gemm_split_part_bytes((int)N, Nc, (int)d, nf, 1));
+    m = std::max(m, dg::gemm_split_part_bytes((int)N, Nc, (int)F, nd, 1));
     L.gpart = take(m);
   }
   L.logits = take(nb == 1 && (!bf || with_logits) ? N * V * 4 : 0);
@@ -189,8 +189,8 @@ Layout layout(const dg_config *c, int32_t nprefill, bool with_logits, int nb = 1
   L.p_ap_ml = take((size_t)splits * Hq * n * 2 * 4);
   if (bf && n) {
     const int nkvq[3] = {(int)(Hkv * hd), (int)(Hkv * hd), (int)(Hq * hd)};
-    L.p_gpart = take(std::max(dg::gemm_split_part_bytes((int)n, (int)d, nkvq, 2),
-                              dg::gemm_split_part_bytes((int)n, (int)d, nkvq + 2, 1)));
+    L.p_gpart = take(std::max(dg::gemm_split_part_bytes((int)n, Nc, (int)d, nkvq, 2),
+                              dg::gemm_split_part_bytes((int)n, Nc, (int)d, nkvq + 2, 1)));
   }
   L.p_total = off;
   return L;
@@ -309,7 +309,7 @@ hipError_t proj(const dg_config *c, const void *A, int M, int K, int count, cons
       g.e[i] = e[i];
     }
     g.part = part;
-    g.ksplit = dg::gemm_split_plan(M, K, Nout, count);
+    g.ksplit = dg::gemm_split_plan(c->canvas_len, K, Nout, count);
     return dg::gemm_split(g, s);
   }
   for (int i = 0; i < count; ++i) {
@@ -333,14 +333,14 @@ hipError_t proj1(const dg_config *c, const void *A, int M, int K, const void *W,
 hipError_t proj1_norm(const dg_config *c, const void *A, int M, int K, const void *W, int Nout, const dg::Epi &e,
                       float *part, const void *gain, float *norm_out, bf16 *norm_tiled, bf16 *norm_split,
                       hipStream_t s) {
-  if (c->dtype == DG_BF16 && dg::gemm_split_plan(M, K, &Nout, 1) > 1) {
+  if (c->dtype == DG_BF16 && dg::gemm_split_plan(c->canvas_len, K, &Nout, 1) > 1) {
     dg::SplitGemm g = split_gemm(A, M, K);
     g.count = 1;
     g.B[0] = W;
     g.N[0] = Nout;
     g.e[0] = e;
     g.part = part;
-    g.ksplit = dg::gemm_split_plan(M, K, &Nout, 1);
+    g.ksplit = dg::gemm_split_plan(c->canvas_len, K, &Nout, 1);
     const dg::RowNorm rn{static_cast<const uint16_t *>(gain), c->rms_eps, norm_out, norm_tiled, norm_split};
     return dg::gemm_split_norm(g, rn, s);
   }

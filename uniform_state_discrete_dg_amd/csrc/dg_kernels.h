@@ -72,10 +72,13 @@ struct SplitGemm {
   float *part;
   int ksplit;
 };
-// K-split the planner picks for a shape (a function of K only).
-int gemm_split_plan(int M, int K, const int *N, int count);
-// Bytes of partials gemm_split needs for that plan (0 when ksplit == 1).
-size_t gemm_split_part_bytes(int M, int K, const int *N, int count);
+// K-split the planner picks for a weight shape (K, N[0..count)) and rows_ref,
+// the configuration's canvas length: the same for every launch of one
+// configuration (single or batched step, prefill of any length), never a
+// launch's own row count.
+int gemm_split_plan(int rows_ref, int K, const int *N, int count);
+// Bytes of partials gemm_split needs for that plan at M rows (0 when ksplit == 1).
+size_t gemm_split_part_bytes(int M, int rows_ref, int K, const int *N, int count);
 hipError_t gemm_split(const SplitGemm &g, hipStream_t s);
 // RMSNorm of a projection's output rows, fused into its split-K merge:
 // y = epilogue(sum of partials) (EPI_STORE, EPI_ADD or EPI_ADD_ROW, fp32,

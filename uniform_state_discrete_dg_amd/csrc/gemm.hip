@@ -369,30 +369,35 @@ __global__ void __launch_bounds__(256) gemm_splitk_norm_kernel(SplitGemm g, RowN
   }
 }
 
-// The K ranges depend on the weights' shape alone (K and the launch's column
-// tiles P), never on M: a row's result then does not depend on how many rows
-// are computed with it, which keeps an incremental prefill bitwise equal to a
-// one-shot one and a batched step equal to its single steps.  At least one
-// range per 44 slices (1408 k), and at least 40 / P ranges, so that a launch
-// of few column tiles still spreads its chains over the chip; no range
-// shorter than 4 slices.  Measured at M = 256 (split count against time,
-// merge included): 2816 x 2816 and 2816 -> 4096 best at 2; 1024 -> 3072 at
-// 2 (19.2 -> 15.2 us against 1), 1024 -> 2048 at 2-3, 2048 -> 1024 at 4-6
-// (16.5 -> 13.4 us against 2), 1024 -> 1024 at 4-5 (18.4 -> 11.5 us).
-int gemm_split_plan(int M, int K, const int *N, int count) {
-  (void)M;
+// The K ranges depend on the weights' shape (K and the launch's column tiles
+// P) and on the configuration's canvas length (its R = ceil(rows_ref / 64)
+// row tiles), never on a launch's own row count M: a row's result then does
+// not depend on how many rows are computed with it, which keeps an
+// incremental prefill bitwise equal to a one-shot one and a batched step
+// equal to its single steps.  At least one range per 44 slices (1408 k), and
+// at least 160 / (R P) ranges, so that a launch of few tiles still spreads
+// its chains over the chip; no range shorter than 4 slices.  Measured (split
+// count against time, merge included): at 256 rows, 2816 x 2816 and
+// 2816 -> 4096 best at 2; 1024 -> 3072 at 2 (19.2 -> 15.2 us against 1),
+// 1024 -> 2048 at 2-3, 2048 -> 1024 at 4-6 (16.5 -> 13.4 us against 2),
+// 1024 -> 1024 at 4-5 (18.4 -> 11.5 us); at 128 rows, 2816 x 2816 at 4-5
+// (21.0 -> 16.4 us against 2), 2816 -> 4096 at 3-4 (21.7 -> 18.4 / 16.9 us),
+// 2048 -> 2816 at 4 (17.0 -> 14.3 us).
+int gemm_split_plan(int rows_ref, int K, const int *N, int count) {
   const int nsl = K / PG_BK;
+  const int R = rows_ref > 0 ? (rows_ref + PG_BM - 1) / PG_BM : 1;
   int P = 0;
   for (int i = 0; i < count; ++i) P += (N[i] + PG_BN - 1) / PG_BN;
   int ks = (nsl + 43) / 44;
-  const int spread = (40 + P - 1) / (P > 0 ? P : 1);
+  const int want = R * (P > 0 ? P : 1);
+  const int spread = (160 + want - 1) / want;
   if (spread > ks) ks = spread;
   if (ks > nsl / 4) ks = nsl / 4;
   return ks > 1 ? ks : 1;
 }
 
-size_t gemm_split_part_bytes(int M, int K, const int *N, int count) {
-  const int ks = gemm_split_plan(M, K, N, count);
+size_t gemm_split_part_bytes(int M, int rows_ref, int K, const int *N, int count) {
+  const int ks = gemm_split_plan(rows_ref, K, N, count);
   if (ks <= 1) return 0;
   size_t n = 0;
   for (int i = 0; i < count; ++i) n += (size_t)ks * M * N[i];
