@@ -9,16 +9,19 @@
 //     are read.
 // At a 256-row canvas both sit at the chip's ridge point (256 flop per byte
 // of the table: HBM and matrix cores would finish together), and with both
-// busy the chip runs at its power limit (the shader clock drops to about
-// 1.4 GHz), so the design keeps bytes in flight and spends as few
-// instructions and LDS bytes per MFMA as it can.  A workgroup owns all
-// canvas rows x 256 table rows.  k advances in 32-wide slices; each slice of
-// both operands (16 KB + 16 KB) is copied global -> LDS by the DMA form of
-// the vector load (global_load_lds_dwordx4, no registers involved) into one
-// of four LDS stages, three slices ahead of the MFMAs.  The waits are
-// explicit (s_waitcnt vmcnt + s_barrier, one barrier per slice): a plain
-// __syncthreads would carry a release fence that drains every DMA in flight.
-// 8 waves (2 per SIMD), each 64 canvas rows x 128 table rows.
+// busy the chip runs at its power limit (the engine clock drops to about
+// 2 GHz in the step, lower back to back), so the design keeps bytes in
+// flight and spends as few instructions and LDS bytes per MFMA as it can.
+// A workgroup owns all canvas rows x 256 table rows.  k advances in 32-wide
+// slices; each slice of both operands (16 KB + 16 KB) is copied global ->
+// LDS by the DMA form of the vector load (global_load_lds_dwordx4, no
+// registers involved) into one of four LDS stages, three slices ahead of
+// the MFMAs.  The waits are explicit (s_waitcnt vmcnt + s_barrier, one
+// barrier per slice): a plain __syncthreads would carry a release fence
+// that drains every DMA in flight.  8 waves (2 per SIMD), each 64 canvas
+// rows x 128 table rows; a single canvas of at most 128 rows runs 4 waves
+// over its 128 rows instead (the same wave tile), the LM head then in a
+// compact 3-stage ring so that two workgroups share a CU.
 //
 // Both operands are in the tiled layout of dg_tiled.h: a slice of a 256-row
 // block is 16 KB of consecutive memory already in LDS order (chunk c of row
