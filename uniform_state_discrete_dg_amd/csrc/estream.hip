@@ -46,6 +46,7 @@ constexpr int ES_NT = 512;        // 8 waves
 constexpr int ES_BM = 256;        // canvas rows per workgroup
 constexpr int ES_BN = 256;        // table rows per workgroup
 constexpr int ES_BK = 32;         // k per slice
+constexpr int ES_CUS = 256;       // compute units of the part (a launch-shape choice only)
 constexpr int ES_SLICE = ES_BM * ES_BK * 2;  // bytes of one operand slice (16 KB)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -434,17 +435,21 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) lm_head_es_kernel(co
                                                               PackedTable tab, int V, float inv_T, EsCanvases cv,
                                                               int nblk, int items, float *__restrict__ logits) {
   extern __shared__ __align__(16) char lds[];
+  // 4 waves: the canvas's rows in nh = ceil(M / 128) halves, item = (table
+  // tile, half), the halves of a tile back to back on one XCD
+  const int nh = NW == 8 ? 1 : (M + 127) / 128;
   int item = blockIdx.x;
-  if (BATCH) item = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;  // grid: a multiple of 8
-  if (BATCH && item >= items) return;
-  const int jt = BATCH ? item / nblk : item, bb = BATCH ? item % nblk : 0;
+  if (BATCH || nh > 1) item = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;  // grid: a multiple of 8
+  if ((BATCH || nh > 1) && item >= items) return;
+  const int jt = BATCH ? item / nblk : item / nh, bb = BATCH ? item % nblk : 0;
+  const int r0 = NW == 8 ? 0 : (item % nh) * 128;  // the workgroup's first canvas row
   const int n0 = jt * ES_BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 5;
   const int ksl = K / ES_BK;
   f32x16_t acc[2][4];
   constexpr int BLK = TF == TF_FP8 ? TL8_BYTES : TF == TF_FP4 ? TL4_BYTES : TL_ELEMS * 2;
-  estream_tile<false, false, TF, false, NW, es_lm_stages(NW)>(At + (int64_t)bb * ksl * TL_ELEMS,
+  estream_tile<false, false, TF, false, NW, es_lm_stages(NW)>(At + (int64_t)bb * ksl * TL_ELEMS + r0 * ES_BK,
                                  static_cast<const uint8_t *>(tab.p) + (int64_t)jt * ksl * BLK, nullptr, 0, ksl, lds,
                                  acc, nullptr, nullptr, tab.scale,
                                  TF == TF_FP4 ? tab.s4 + (int64_t)jt * ksl * TL4_SCALES : nullptr);
@@ -462,7 +467,7 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) lm_head_es_kernel(co
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = wm * 64 + i * 32 + (lane & 31);
-    const int grow = bb * ES_BM + row;  // stacked row
+    const int grow = bb * ES_BM + r0 + row;  // stacked row
     const int c = BATCH ? min(grow, M - 1) / N : 0, lrow = grow - c * N;  // c < M / N even past the last row
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -540,7 +545,7 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) lm_head_es_kernel(co
 #pragma unroll
   for (int rh = 0; rh < 2; ++rh) {
     const int row = (threadIdx.x >> 2) + rh * NW * 16;  // rows 0 .. 32 NW - 1
-    const int grow = bb * ES_BM + row;
+    const int grow = bb * ES_BM + r0 + row;
     if (grow >= M) continue;
     const int c = BATCH ? grow / N : 0, lrow = grow - c * N;
     char *dst = reinterpret_cast<char *>(cv.probs[c]) + (int64_t)(n0 / 32) * ES_SLICE + lrow * 64 + u4 * 16;
@@ -588,8 +593,13 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
       }) != hipSuccess)
     return hipErrorInvalidValue;
   const int M = B * N, nblk = (M + ES_BM - 1) / ES_BM;
-  const int items = (V / ES_BN) * nblk;
-  const dim3 grid(B == 1 ? items : (items + 7) / 8 * 8);
+  // one canvas runs 4-wave workgroups over 128-row halves when it has at
+  // most 128 rows, or when its table has fewer 256-row tiles than the chip
+  // has CUs (so 8-wave workgroups would leave CUs idle; with the CUs full,
+  // copying each table slice into LDS twice costs more than it returns)
+  const bool narrow = B == 1 && (2 * N <= ES_BM || V / ES_BN < ES_CUS);
+  const int items = (V / ES_BN) * (narrow ? (N + 127) / 128 : nblk);
+  const dim3 grid(B == 1 && 2 * N <= ES_BM ? items : (items + 7) / 8 * 8);
   // one canvas of at most 128 rows: 4 waves over its 128 rows, not 8 over
   // 256 with half of them padding
 #define DG_LM_LAUNCH(BT, TF, NW)                                                                      \
@@ -601,7 +611,7 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
     else if (tab.tf == TF_FP4) DG_LM_LAUNCH(BT, TF_FP4, NW);  \
     else DG_LM_LAUNCH(BT, TF_BF16, NW);                       \
   } while (0)
-  if (B == 1 && 2 * N <= ES_BM) DG_LM_FORMS(false, 4);
+  if (narrow) DG_LM_FORMS(false, 4);
   else if (B == 1) DG_LM_FORMS(false, 8);
   else DG_LM_FORMS(true, 8);
 #undef DG_LM_FORMS
