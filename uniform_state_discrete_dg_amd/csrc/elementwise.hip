@@ -507,6 +507,27 @@ __device__ __forceinline__ float2 rc_sum2(float a, float b, float *sh) {
   __syncthreads();
   return r;
 }
+template <int NW>
+__device__ __forceinline__ float3 rc_sum3(float a, float b, float c, float *sh) {
+  a = warp_sum(a);
+  b = warp_sum(b);
+  c = warp_sum(c);
+  if ((threadIdx.x & 63) == 0) {
+    sh[threadIdx.x >> 6] = a;
+    sh[NW + (threadIdx.x >> 6)] = b;
+    sh[2 * NW + (threadIdx.x >> 6)] = c;
+  }
+  __syncthreads();
+  float3 r = make_float3(sh[0], sh[NW], sh[2 * NW]);
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    r.x += sh[w];
+    r.y += sh[NW + w];
+    r.z += sh[2 * NW + w];
+  }
+  __syncthreads();
+  return r;
+}
 // max of (value, lowest index on ties)
 template <int NW>
 __device__ __forceinline__ void rc_argmax(float &v, int &i, float *shv, int *shi) {
@@ -616,21 +637,14 @@ __device__ __forceinline__ void row_combine_row(const int row, const float4 *__r
   const bool found = bidx < ntiles * TILE;
   const int amax = found ? bidx : 0;
   const float My = Mz * inv_T;
-  const int ta = amax / TILE;
-  // corrected terms of the argmax token inside its tile (reference m_ta = My)
-  float l_fix = 0.f, s_fix = 0.f, d_top = 0.f;
+  // the argmax token's table row, in flight while the tile sums are formed
+  float ev[RC_D];
   if (fix && found) {
-    float part = 0.f;
 #pragma unroll
     for (int i = 0; i < RC_D; ++i) {
       const int k = threadIdx.x + RC_NT * i;
-      if (k < d) part += nv[i] * table_get(E, amax, k);
+      ev[i] = k < d ? table_get(E, amax, k) : 0.f;
     }
-    const float z_exact = rc_sum<RC_NW>(part, shv);
-    d_top = z_exact * inv_T - My;
-    const float e = exp2f(d_top * LOG2E);
-    l_fix = e - 1.f;
-    s_fix = e * d_top;
   }
   float L = 0.f, S = 0.f;
 #pragma unroll
@@ -640,18 +654,29 @@ __device__ __forceinline__ void row_combine_row(const int row, const float4 *__r
     const float4 v = tile(i, t);
     const float dd = v.x * inv_T - My;
     const float w = exp2f(dd * LOG2E);
-    float l = v.y, sacc = v.z;
-    if (fix && t == ta) {
-      l += l_fix;
-      sacc += s_fix;
-    }
-    L += l * w;
-    S += w * (sacc + dd * l);
+    L += v.y * w;
+    S += w * (v.z + dd * v.y);
+  }
+  float part = 0.f;
+  if (fix && found) {
+#pragma unroll
+    for (int i = 0; i < RC_D; ++i) part += nv[i] * ev[i];
   }
   {
-    const float2 LS = rc_sum2<RC_NW>(L, S, shv);
-    L = LS.x;
-    S = LS.y;
+    const float3 r = rc_sum3<RC_NW>(part, L, S, shv);
+    L = r.y;
+    S = r.z;
+    part = r.x;
+  }
+  // the argmax token's term replaced by its exact one: its tile holds the
+  // row maximum, so that tile's weight is exactly 1 (dd = 0) and the
+  // correction adds e - 1 to L and e d_top to S (reference m_ta = My)
+  float d_top = 0.f;
+  if (fix && found) {
+    d_top = part * inv_T - My;
+    const float e = exp2f(d_top * LOG2E);
+    L += e - 1.f;
+    S += e * d_top;
   }
   const float invL = 1.f / L;
   const float R = ceilf(My * LOG2E);
@@ -687,7 +712,7 @@ __global__ void __launch_bounds__(RC_NT) row_combine_kernel(const float4 *__rest
                                                           float *__restrict__ row_scale, uint8_t *__restrict__ shift,
                                                           const float *__restrict__ n2, PackedTable E,
                                                           float2 *__restrict__ top) {
-  __shared__ float shv[2 * RC_NW];
+  __shared__ float shv[3 * RC_NW];
   __shared__ int shi[RC_NW];
   const int row = blockIdx.x;
   row_combine_row<CACHED>(row, stats, ntiles, inv_T, entropy, cand, tile_scale, row_scale, shift,
@@ -700,7 +725,7 @@ template <bool CACHED>
 __global__ void __launch_bounds__(RC_NT) row_combine_batch_kernel(RowCombineBatch bt, int N, int ntiles,
                                                                 float inv_T, const float *__restrict__ n2,
                                                                 PackedTable E) {
-  __shared__ float shv[2 * RC_NW];
+  __shared__ float shv[3 * RC_NW];
   __shared__ int shi[RC_NW];
   const int c = blockIdx.x / N, row = blockIdx.x - c * N;
   row_combine_row<CACHED>(row, bt.stats[c], ntiles, inv_T, bt.entropy[c], bt.cand[c], nullptr, bt.row_scale[c],
