@@ -460,7 +460,7 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) lm_head_es_kernel(co
   // canvas's buffers, so a wave stores 1 KB runs instead of 8-byte pieces
   // of 64-byte lines.  Staging: slice ls (0..7) at ls * 16 KB, row r's
   // chunks at r * 64 in stored order (tl_pos of the canvas's own row);
-  // statistics at 8 * (NW * 2 KB) + r * 64 + 16 * (local tile).
+  // statistics at 8 * (NW * 2 KB) + r * 64 + 16 * (local tile xor r / 4 mod 4).
   constexpr int AB = es_abytes(NW);
   char *stage_num = lds, *stage_st = lds + 8 * AB;
 
@@ -533,8 +533,8 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) lm_head_es_kernel(co
           }
         }
       }
-      if (g == 0)
-        *reinterpret_cast<float4 *>(stage_st + row * 64 + (wn * 2 + h) * 16) =
+      if (g == 0)  // local tile wn * 2 + h at slot (tile ^ (row / 4 mod 4)): 32 rows on distinct banks
+        *reinterpret_cast<float4 *>(stage_st + row * 64 + ((wn * 2 + h) ^ ((row >> 2) & 3)) * 16) =
             make_float4(best, l, sacc, __int_as_float(bcol));
     }
   }
@@ -554,7 +554,7 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) lm_head_es_kernel(co
     for (int ls = 0; ls < 8; ++ls)
       *reinterpret_cast<uint4 *>(dst + ls * ES_SLICE) = *reinterpret_cast<const uint4 *>(src + ls * AB);
     reinterpret_cast<uint4 *>(cv.tile_stats[c] + (int64_t)lrow * ntiles + n0 / 64)[u4] =
-        *reinterpret_cast<const uint4 *>(stage_st + row * 64 + u4 * 16);
+        *reinterpret_cast<const uint4 *>(stage_st + row * 64 + (u4 ^ ((row >> 2) & 3)) * 16);
   }
 }
 
