@@ -404,7 +404,8 @@ def test_prefill_append_incremental(dtype, masked):
         assert rel_frob(den.cache.v[:, :L].float().cpu().numpy(), vc[:, :L]) <= tol
         assert rel_frob(attn.float().cpu().numpy(), a_ref) <= tol
     assert not den.cache.k[:, L:].any()
-    # keys/values of a token depend on the token only: one-shot append is bitwise equal
+    # keys/values of a token depend on the token only: a one-shot append, with no attention output
+    # requested (the incremental one asked for it), is bitwise equal
     den2 = D.Denoiser(c, inp, capacity=cap, max_prefill=377, sampler=den.cfg.sampler)
     den2.prefill(toks.cuda())
     assert torch.equal(den2.cache.k, den.cache.k) and torch.equal(den2.cache.v, den.cache.v)
