@@ -93,20 +93,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_lm_head_n256_v262k_d2816.
 KERNEL_SRC = os.path.join(ROOT, "uniform_state_discrete_dg_amd", "csrc", "estream.hip")
 
 
-def kernel_code_sha256() -> str:
-    """sha256 of the streaming kernels' source with its // comments, trailing
-    blanks and empty lines removed: a change to the code invalidates the
-    counter summary, a change to the comments does not."""
+def kernel_code_sha256(text: str = None) -> str:
+    """sha256 of the streaming kernels' source with its // comments and all
+    whitespace removed: a change to the code invalidates the counter
+    summary, a change to the comments or the line breaks does not."""
     import hashlib
-    lines = []
-    for line in open(KERNEL_SRC).read().splitlines():
+    if text is None:
+        text = open(KERNEL_SRC).read()
+    code = []
+    for line in text.splitlines():
         i = line.find("//")
-        if i >= 0:
-            line = line[:i]
-        line = line.rstrip()
-        if line:
-            lines.append(line)
-    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+        code.append(line[:i] if i >= 0 else line)
+    return hashlib.sha256("".join("".join(code).split()).encode()).hexdigest()
 
 
 def measured_traffic():

@@ -163,7 +163,8 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
 #pragma unroll
   for (int v = 0; v < NPART; ++v) {
     const int pt = wave + NW * v;
-    bsrc[v] = TR ? Bt + (int64_t)min(tr_d0 + pt, tr_ksd - 1) * BLK + blane : Bt + (int64_t)sb * BLK + pt * (BLK / 8) + blane;
+    bsrc[v] = TR ? Bt + (int64_t)min(tr_d0 + pt, tr_ksd - 1) * BLK + blane
+                 : Bt + (int64_t)sb * BLK + pt * (BLK / 8) + blane;
   }
   constexpr int AB = es_abytes(NW), SB = es_stage_bytes(NW);
   char *lds_shift = lds + STG * SB;          // SCALED: [stage][256] bytes
@@ -431,9 +432,9 @@ __device__ __forceinline__ void estream_tile(const bf16 *__restrict__ At, const 
 // that XCD's L2 for the other blocks.
 // ---------------------------------------------------------------------------
 template <bool BATCH, int TF, int NW = 8>
-__global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) lm_head_es_kernel(const bf16 *__restrict__ At, int M, int N, int K,
-                                                              PackedTable tab, int V, float inv_T, EsCanvases cv,
-                                                              int nblk, int items, float *__restrict__ logits) {
+__global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : 2)
+    lm_head_es_kernel(const bf16 *__restrict__ At, int M, int N, int K, PackedTable tab, int V, float inv_T,
+                      EsCanvases cv, int nblk, int items, float *__restrict__ logits) {
   extern __shared__ __align__(16) char lds[];
   // 4 waves: the canvas's rows in nh = ceil(M / 128) halves, item = (table
   // tile, half), the halves of a tile back to back on one XCD
@@ -586,7 +587,8 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
                               reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_FP8, 4>),
                               reinterpret_cast<const void *>(lm_head_es_kernel<false, TF_FP4, 4>)};
         for (const void *f : fns) {
-          const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes_lm());
+          const hipError_t e =
+              hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)es_lds_bytes_lm());
           if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -633,9 +635,9 @@ hipError_t lm_head_bf16_batch(const uint16_t *A_tiled, int B, int N, int K, cons
 // canvas 2p + 1 in rows 128..255, read from its own buffers); 3 one canvas
 // of at most 128 rows, 4 waves over its 128 rows.
 template <bool SCALED, int MODE, int TF>
-__global__ void __launch_bounds__(MODE == 3 ? ES_NT / 2 : ES_NT, 1) selfcond_es_kernel(EsCanvasesIn cin, PackedTable tab, int M, int N,
-                                                               int K, float *__restrict__ part, int ksplit, int ntn,
-                                                               int nb, int items, SelfcondGuard guard) {
+__global__ void __launch_bounds__(MODE == 3 ? ES_NT / 2 : ES_NT, 1)
+    selfcond_es_kernel(EsCanvasesIn cin, PackedTable tab, int M, int N, int K, float *__restrict__ part, int ksplit,
+                       int ntn, int nb, int items, SelfcondGuard guard) {
   extern __shared__ __align__(16) char lds[];
   const int b = blockIdx.x, ng = gridDim.x;
   const int per_xcd = ng / 8;  // grid is a multiple of 8
