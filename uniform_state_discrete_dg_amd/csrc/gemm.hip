@@ -310,12 +310,15 @@ __global__ void __launch_bounds__(256) gemm_splitk_norm_kernel(SplitGemm g, RowN
   const int64_t stride = (int64_t)M * N;
   const float *p0 = g.part + (int64_t)row * N;
   float4 y[RN_MAXQ];
+  uint2 gw[RN_MAXQ];  // the gain's four bf16 values per float4, loaded with the partials
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < RN_MAXQ; ++k) {
     const int c = (threadIdx.x + 256 * k) * 4;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    gw[k] = make_uint2(0u, 0u);
     if (c < N) {
+      gw[k] = *reinterpret_cast<const uint2 *>(rn.gain + c);
       v = *reinterpret_cast<const float4 *>(p0 + c);
       for (int z = 1; z < g.ksplit; ++z) {
         const float4 w = *reinterpret_cast<const float4 *>(p0 + z * stride + c);
@@ -352,8 +355,10 @@ __global__ void __launch_bounds__(256) gemm_splitk_norm_kernel(SplitGemm g, RowN
   for (int k = 0; k < RN_MAXQ; ++k) {
     const int c = (threadIdx.x + 256 * k) * 4;
     if (c >= N) continue;
-    const float q[4] = {y[k].x * inv * bf16_to_f32(rn.gain[c]), y[k].y * inv * bf16_to_f32(rn.gain[c + 1]),
-                        y[k].z * inv * bf16_to_f32(rn.gain[c + 2]), y[k].w * inv * bf16_to_f32(rn.gain[c + 3])};
+    const float q[4] = {y[k].x * inv * __uint_as_float(gw[k].x << 16),
+                        y[k].y * inv * __uint_as_float(gw[k].x & 0xffff0000u),
+                        y[k].z * inv * __uint_as_float(gw[k].y << 16),
+                        y[k].w * inv * __uint_as_float(gw[k].y & 0xffff0000u)};
     if (rn.out) *reinterpret_cast<float4 *>(rn.out + (int64_t)row * N + c) = make_float4(q[0], q[1], q[2], q[3]);
     if (rn.out_split) {
       uint2 hi, lo;
