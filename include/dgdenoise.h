@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define DG_ABI_VERSION 8
+#define DG_ABI_VERSION 9
 
 typedef enum {
   DG_OK = 0,
@@ -178,9 +178,12 @@ typedef struct {
 } dg_weights;
 
 /* Prefix KV cache ([P1]/[P4]: written causally by prefill, read by denoise).
- * k, v: device float32 [Hkv][capacity][hd] for both dtypes (a bf16 model's
- * keys/values are kept at full precision; the attention kernel splits them
- * into bf16 pairs for the matrix cores).  Positions
+ * k, v: device buffers of Hkv * capacity * hd * 4 bytes each.  DG_F32:
+ * float32 [Hkv][capacity][hd].  DG_BF16: split pairs, bf16
+ * [2][Hkv][capacity][hd]: the hi terms, then the lo terms, value =
+ * hi + lo with hi = bf16(x) and lo = bf16(x - hi) (16 significant bits),
+ * the form the attention kernel copies to the matrix cores unconverted;
+ * a caller filling a cache itself writes that form.  Positions
  * [0, length) are valid.  dg_denoise_step never writes the cache
  * ([P3] §4.2); dg_prefill_append writes [length, length+n) and then
  * advances `length` (host field) by n. */

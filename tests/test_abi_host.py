@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from uniform_state_discrete_dg_amd import binding as B
 from uniform_state_discrete_dg_amd import workloads as W
@@ -38,7 +39,7 @@ def test_header_symbols_exported(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert B.dg_abi_version() == 8
+    assert B.dg_abi_version() == 9
     for s in range(6):
         assert lib.dg_status_string(s)
 
@@ -450,3 +451,20 @@ def test_fp4_grid_quantiser():
     assert W.fp4_scale_bytes(z).item() == 127
     assert W.fp4_scale_bytes(torch.full((32, 32), 2.0 ** -130)).item() == 2
     assert W.fp4_scale_bytes(torch.full((32, 32), 2.0 ** 126)).item() == 126 - 2 + 127
+
+
+def test_cache_split_pair_roundtrip():
+    """The host's split-pair form of a bf16 model's KV cache: hi = bf16(x)
+    (round to nearest even), lo = bf16(x - hi); hi + lo keeps 16
+    significant bits, and a bf16 value has lo = 0."""
+    g = torch.Generator().manual_seed(7)
+    x = torch.randn(3, 17, 128, generator=g) * torch.exp(torch.randn(3, 17, 128, generator=g) * 4)
+    p = B.split_pair(x)
+    assert p.shape == (2, 3, 17, 128) and p.dtype == torch.bfloat16
+    assert torch.equal(p[0], x.to(torch.bfloat16))
+    assert torch.equal(p[1], (x - p[0].float()).to(torch.bfloat16))
+    y = B.join_pair(p)
+    assert ((y - x).abs() <= x.abs() * 2.0 ** -16).all()
+    xb = x.to(torch.bfloat16).float()
+    pb = B.split_pair(xb)
+    assert not pb[1].float().any() and torch.equal(B.join_pair(pb), xb)

@@ -141,8 +141,8 @@ def test_block_diffusion_full_size_floats():
     den.prefill(prompt.cuda(), attn)
     torch.cuda.synchronize()
     a_ref = om.prefill_append(prompt.numpy(), kc, vc, 0)
-    assert rel_frob(den.cache.k[:, :P].cpu().numpy(), kc[:, :P]) <= 1e-4
-    assert rel_frob(den.cache.v[:, :P].cpu().numpy(), vc[:, :P]) <= 1e-4
+    assert rel_frob(den.cache.k_f32()[:, :P].cpu().numpy(), kc[:, :P]) <= 1e-4
+    assert rel_frob(den.cache.v_f32()[:, :P].cpu().numpy(), vc[:, :P]) <= 1e-4
     assert rel_frob(attn.cpu().numpy(), a_ref) <= 1e-4
     rows = sorted({0, 5, N // 2, N - 1})
     sel = np.zeros(N, np.uint8)
@@ -166,5 +166,5 @@ def test_block_diffusion_full_size_floats():
     om.prefill_append(fin.cpu().numpy(), kc, vc, P, want_attn=False)
     L1 = P + N
     assert den.cache.length == L1
-    assert rel_frob(den.cache.k[:, P:L1].cpu().numpy(), kc[:, P:L1]) <= 1e-4
-    assert rel_frob(den.cache.v[:, P:L1].cpu().numpy(), vc[:, P:L1]) <= 1e-4
+    assert rel_frob(den.cache.k_f32()[:, P:L1].cpu().numpy(), kc[:, P:L1]) <= 1e-4
+    assert rel_frob(den.cache.v_f32()[:, P:L1].cpu().numpy(), vc[:, P:L1]) <= 1e-4

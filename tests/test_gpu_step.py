@@ -400,10 +400,10 @@ def test_prefill_append_incremental(dtype, masked):
         a_ref = om.prefill_append(toks[lo:hi].numpy(), kc, vc, L)
         L += n
         assert den.cache.length == L
-        assert rel_frob(den.cache.k[:, :L].float().cpu().numpy(), kc[:, :L]) <= tol
-        assert rel_frob(den.cache.v[:, :L].float().cpu().numpy(), vc[:, :L]) <= tol
+        assert rel_frob(den.cache.k_f32()[:, :L].cpu().numpy(), kc[:, :L]) <= tol
+        assert rel_frob(den.cache.v_f32()[:, :L].cpu().numpy(), vc[:, :L]) <= tol
         assert rel_frob(attn.float().cpu().numpy(), a_ref) <= tol
-    assert not den.cache.k[:, L:].any()
+    assert not den.cache.k_f32()[:, L:].any()
     # keys/values of a token depend on the token only: a one-shot append, with no attention output
     # requested (the incremental one asked for it), is bitwise equal
     den2 = D.Denoiser(c, inp, capacity=cap, max_prefill=377, sampler=den.cfg.sampler)
@@ -445,8 +445,8 @@ def test_block_diffusion_reduced_vocab():
         om.prefill_append(fin.cpu().numpy(), kc, vc, L0, want_attn=False)
         L1 = den.cache.length
         assert L1 == L0 + 256
-        assert rel_frob(den.cache.k[:, :L1].float().cpu().numpy(), kc[:, :L1]) <= 1e-2
-        assert rel_frob(den.cache.v[:, :L1].float().cpu().numpy(), vc[:, :L1]) <= 1e-2
+        assert rel_frob(den.cache.k_f32()[:, :L1].cpu().numpy(), kc[:, :L1]) <= 1e-2
+        assert rel_frob(den.cache.v_f32()[:, :L1].cpu().numpy(), vc[:, :L1]) <= 1e-2
 
 
 def test_block_diffusion_full_size_short():

@@ -399,19 +399,49 @@ class DeviceWeights:
                                         "g_final", "mask_emb")))
 
 
+def split_pair(x: torch.Tensor) -> torch.Tensor:
+    """fp32 values -> [2, *x.shape] bf16: hi = bf16(x), lo = bf16(x - hi)
+    (round to nearest even, as the library writes them)."""
+    x = x.to(torch.float32)
+    hi = x.to(torch.bfloat16)
+    lo = (x - hi.to(torch.float32)).to(torch.bfloat16)
+    return torch.stack((hi, lo))
+
+
+def join_pair(p: torch.Tensor) -> torch.Tensor:
+    """[2, ...] bf16 split pair -> the fp32 values hi + lo (exact)."""
+    return p[0].to(torch.float32) + p[1].to(torch.float32)
+
+
 class DeviceCache:
-    """fp32 [Hkv][capacity][hd] keys and values (both dtypes)."""
+    """Keys and values of the prefix, [Hkv][capacity][hd] each: fp32 for a
+    DG_F32 model; for DG_BF16 split pairs, bf16 [2][Hkv][capacity][hd] (the
+    hi terms, then the lo terms; the same bytes as fp32).  k_f32() / v_f32()
+    give the values as fp32 [Hkv][capacity][hd] either way."""
 
     def __init__(self, cfg: dg_config, capacity: int, device="cuda", k_prefix=None, v_prefix=None):
-        dt = torch.float32
-        self.k = torch.zeros((cfg.n_kv_heads, capacity, cfg.head_dim), dtype=dt, device=device)
+        self.pair = cfg.dtype == DG_BF16
+        shape = (cfg.n_kv_heads, capacity, cfg.head_dim)
+        if self.pair:
+            self.k = torch.zeros((2,) + shape, dtype=torch.bfloat16, device=device)
+        else:
+            self.k = torch.zeros(shape, dtype=torch.float32, device=device)
         self.v = torch.zeros_like(self.k)
         L = 0
         if k_prefix is not None:
             L = k_prefix.shape[1]
-            self.k[:, :L] = k_prefix.to(device=device, dtype=dt)
-            self.v[:, :L] = v_prefix.to(device=device, dtype=dt)
+            for dst, src in ((self.k, k_prefix), (self.v, v_prefix)):
+                if self.pair:
+                    dst[:, :, :L] = split_pair(src.to(device=device))
+                else:
+                    dst[:, :L] = src.to(device=device, dtype=torch.float32)
         self.s = dg_kv_cache(self.k.data_ptr(), self.v.data_ptr(), L, capacity)
+
+    def k_f32(self) -> torch.Tensor:
+        return join_pair(self.k) if self.pair else self.k
+
+    def v_f32(self) -> torch.Tensor:
+        return join_pair(self.v) if self.pair else self.v
 
     @property
     def length(self) -> int:

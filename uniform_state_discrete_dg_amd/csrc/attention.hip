@@ -6,8 +6,11 @@
 // segments, the committed cache [0, nA) and the step's own canvas keys
 // [0, nB), so the cache is never written by a denoising step.
 //
-// Queries, keys and values are fp32 in memory.  While they are staged, each
-// value is split into two bf16 terms (hi + lo), and every product of two
+// Queries are fp32 in memory and split into two bf16 terms (hi + lo) as
+// they are loaded; keys and values are stored as such split pairs already
+// (the projection that produces them writes both terms: the KV cache of a
+// bf16 model and the step's own canvas keys), so a tile of them reaches LDS
+// by the DMA form of the vector load, unconverted.  Every product of two
 // split operands is formed from three bf16 MFMAs (hi*hi + hi*lo + lo*hi),
 // which keeps the scores and the output within ~1e-5 of fp32.
 //
@@ -15,12 +18,13 @@
 // KV head (G = 2 when the group size is even, else 1; 4 waves of 32
 // queries per head) and a contiguous range of keys (split-KV, partial
 // results merged by a second kernel), so each 64-key tile of K and V is
-// staged through LDS once for G heads.  The wave
-// computes S^T = K Q^T so that each lane ends up holding one query's scores,
-// keeps the running max / sum per lane, and computes O^T = V^T P^T with the
-// probabilities taken straight from registers; V is transposed while it is
-// staged into LDS.  Grouped-query attention maps query head h to KV head
-// h / (Hq / Hkv).
+// staged through LDS once for G heads, in a two-tile ring (the next tile
+// is in flight while the current one is used).  The wave computes
+// S^T = K Q^T so that each lane ends up holding one query's scores, keeps
+// the running max / sum per lane, and computes O^T = V^T P^T with the
+// probabilities taken straight from registers; the V^T fragments come out
+// of the row-major V tile through the gfx950 transposing LDS read.
+// Grouped-query attention maps query head h to KV head h / (Hq / Hkv).
 #include "dg_device.h"
 #include "dg_kernels.h"
 
@@ -32,12 +36,20 @@ constexpr int BQ = 128;   // queries per workgroup
 constexpr int KT = 64;    // keys per tile
 constexpr int NTH = 256;  // 4 waves
 constexpr float LOG2E = 1.4426950408889634f;
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
 }  // namespace
 
+// K tile in LDS: [64 keys][16 chunks of 8], chunk c of key r at c ^ (r & 15),
+// so the 32 keys one fragment read touches at one chunk fall on distinct banks.
 __device__ __forceinline__ int kswz(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
-// V^T in LDS: [128 hd][8 groups of 8 keys], group u of row hd at u ^ ((hd >> 1) & 7),
-// so the 16 rows a fragment read touches at one group fall on distinct banks.
-__device__ __forceinline__ int vswz(int hd, int u) { return hd * 8 + (u ^ ((hd >> 1) & 7)); }
+// V tile in LDS: [64 keys][16 chunks of 8 hd], chunk c of key r at
+// c ^ 4 (r & 3): a transposing read covers 4 consecutive keys x 16 hd
+// (two chunks per key) for each of two 16-hd halves, 16 distinct chunks.
+__device__ __forceinline__ int vswz(int row, int chunk) { return row * 16 + (chunk ^ (4 * (row & 3))); }
+constexpr int ATT_TERM = KT * HD * 2;     // bytes of one term (hi or lo) of a K or V tile
+constexpr int ATT_STAGE = 4 * ATT_TERM;   // K hi, K lo, V hi, V lo
+constexpr int ATT_LDS = 2 * ATT_STAGE;    // two stages
 
 // The canvas of grid z-slice `z` of a batch launch (canvas c owns z-slices
 // zbase[c] .. zbase[c + 1] - 1: its own split plan) and that slice's split.
@@ -48,131 +60,81 @@ __device__ __forceinline__ int attn_canvas(const AttnBatch &bt, int &z) {
   return c;
 }
 
+template <int n>
+__device__ __forceinline__ void att_wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// DMA of the 64-key tile at kt0 into a stage: four 16 KB terms (K hi, K lo,
+// V hi, V lo) in 1 KB parts (4 keys x 16 chunks), PERW per wave, all of a
+// wave's parts in one term.  Each lane copies one 16-byte chunk, the
+// swizzle applied to its source, from the cache or the canvas segment by
+// its own key; a key past the range copies the range's last key (its
+// scores are masked and its probabilities are 0).
 template <int G>
-__global__ void __launch_bounds__(NTH * G) attn_split_kernel(AttnBatch bt) {
-  __shared__ uint4 Ks[2][KT * HD / 8];     // hi, lo: [64 keys][16 chunks of 8]
-  __shared__ uint4 Vt[2][HD * KT / 8];     // hi, lo: [128 hd][8 chunks of 8 keys]
-
-  int z = blockIdx.z;
-  const AttnArgs &a = bt.c[attn_canvas(bt, z)];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 5;
-  const int h = blockIdx.y * G + (wave >> 2);
-  const int g = h / (a.Hq / a.Hkv);
-  const int q = blockIdx.x * BQ + (wave & 3) * 32 + (lane & 31);
-  const int nk = a.nA + a.nB;
-  const int kbeg = z * a.keys_per_split;
-  const int kend = min(nk, kbeg + a.keys_per_split);
-  const float *Q = static_cast<const float *>(a.q);
-  const int64_t qhs = a.q_hstride ? a.q_hstride : (int64_t)a.nq * HD;
-  const float *kA = static_cast<const float *>(a.kA), *vA = static_cast<const float *>(a.vA);
-  const float *kB = static_cast<const float *>(a.kB), *vB = static_cast<const float *>(a.vB);
-
-  // This lane's query fragments (B operand of S^T = K Q^T), hi and lo.
-  bf16x8_t qh[HD / 16], ql[HD / 16];
+__device__ __forceinline__ void att_issue(const bf16 *__restrict__ kA, const bf16 *__restrict__ vA,
+                                          const bf16 *__restrict__ kB, const bf16 *__restrict__ vB, int64_t loA,
+                                          int64_t loB, int nA, int kt0, int kend, char *__restrict__ st) {
+  constexpr int PERW = 64 / (4 * G);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int term = (wave * PERW) >> 4, part0 = (wave * PERW) & 15;
+  const bool isV = term >= 2, isLo = term & 1;
+  char *dst = st + term * ATT_TERM + part0 * 1024;
+  const int sl = lane & 15;
+  if (kt0 + KT <= kend && (kt0 + KT <= nA || kt0 >= nA)) {  // the tile lies in one segment: one base
+    const bool inA = kt0 < nA;
+    const bf16 *base = (isV ? (inA ? vA : vB) : (inA ? kA : kB)) + (int64_t)(inA ? kt0 : kt0 - nA) * HD +
+                       (isLo ? (inA ? loA : loB) : 0);
 #pragma unroll
-  for (int s = 0; s < HD / 16; ++s) {
-    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-    if (q < a.nq) {
-      const float4 *src = reinterpret_cast<const float4 *>(Q + (int64_t)h * qhs + (int64_t)q * HD + s * 16 + g4 * 8);
-      x0 = src[0];
-      x1 = src[1];
+    for (int u = 0; u < PERW; ++u) {
+      const int key = (part0 + u) * 4 + (lane >> 4);
+      const int ch = isV ? (sl ^ (4 * (key & 3))) : (sl ^ (key & 15));
+      __builtin_amdgcn_global_load_lds(base + key * HD + ch * 8, dst + u * 1024, 16, 0, 0);
     }
-    uint4 hi, lo;
-    split8(x0, x1, hi, lo);
-    qh[s] = __builtin_bit_cast(bf16x8_t, hi);
-    ql[s] = __builtin_bit_cast(bf16x8_t, lo);
+  } else {
+#pragma unroll
+    for (int u = 0; u < PERW; ++u) {
+      const int key = (part0 + u) * 4 + (lane >> 4);
+      const int ch = isV ? (sl ^ (4 * (key & 3))) : (sl ^ (key & 15));
+      const int kc = min(kt0 + key, kend - 1);
+      const bool inA = kc < nA;
+      const bf16 *base = isV ? (inA ? vA : vB) : (inA ? kA : kB);
+      const int64_t off = (int64_t)(inA ? kc : kc - nA) * HD + ch * 8 + (isLo ? (inA ? loA : loB) : 0);
+      __builtin_amdgcn_global_load_lds(base + off, dst + u * 1024, 16, 0, 0);
+    }
   }
+}
 
+// The key range [kbeg, kend) of one KV group against the wave's 32 queries
+// (fragments qh / ql): running max m_run, sum l_run and O^T accumulators.
+// The operands come in as restrict-qualified parameters, which tells the
+// compiler the LDS reads do not depend on the DMA copies in flight (the
+// wait / barrier pair before each tile orders them).
+template <int G>
+__device__ __forceinline__ void att_tiles(const bf16 *__restrict__ kA, const bf16 *__restrict__ vA,
+                                          const bf16 *__restrict__ kB, const bf16 *__restrict__ vB, int64_t loA,
+                                          int64_t loB, int nA, int kbeg, int kend, int qlimit, bool causal,
+                                          const bf16x8_t (&qh)[HD / 16], const bf16x8_t (&ql)[HD / 16],
+                                          char *__restrict__ lds, f32x16_t (&oacc)[HD / 32], float &m_run,
+                                          float &l_run) {
+  constexpr int PERW = 64 / (4 * G);
+  const int lane = threadIdx.x & 63, g4 = lane >> 5;
   const float sc = rsqrtf((float)HD) * LOG2E;
-  const int qlimit = a.causal ? a.q_pos0 + q : INT32_MAX;
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16_t oacc[HD / 32];
-#pragma unroll
-  for (int nb = 0; nb < HD / 32; ++nb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.f;
-
-  // A tile is 64 keys x 128.  K: 1024 chunks of 8 floats, 4 / G per thread
-  // (thread -> key idx / 16, chunk idx % 16).  V: thread -> DV = 4 / G dims
-  // (DV (tid % (32 G)) ..) x the 8 keys of group u = tid / (32 G), which it
-  // writes as 8-key vectors of V^T.  Group u holds, in MFMA k order, the keys
-  // that a lane's probabilities cover in the P^T fragment: with c = u / 2 and
-  // g = u % 2, keys 16 c + 4 g + {0..3} then 16 c + 8 + 4 g + {0..3}.
-  constexpr int KPT = 4 / G, DV = 4 / G;
-  typedef float fv_t __attribute__((ext_vector_type(DV)));
-  float4 rk[KPT][2];
-  fv_t rv[8];
-  auto kv_src = [&](int kabs, int col, const float *&kp, const float *&vp, int64_t &off) {
-    if (kabs < a.nA) {
-      off = ((int64_t)g * a.capA + kabs) * HD + col;
-      kp = kA;
-      vp = vA;
-    } else {
-      off = ((int64_t)g * a.capB + (kabs - a.nA)) * HD + col;
-      kp = kB;
-      vp = vB;
-    }
-  };
-  auto load = [&](int kt0) {
-#pragma unroll
-    for (int t = 0; t < KPT; ++t) {
-      const int idx = tid + t * NTH * G;
-      const int key = idx >> 4, ch = idx & 15;
-      const int kabs = kt0 + key;
-      float4 k0 = make_float4(0.f, 0.f, 0.f, 0.f), k1 = k0;
-      if (kabs < kend) {
-        int64_t off;
-        const float *kp, *vp;
-        kv_src(kabs, ch * 8, kp, vp, off);
-        k0 = *reinterpret_cast<const float4 *>(kp + off);
-        k1 = *reinterpret_cast<const float4 *>(kp + off + 4);
-      }
-      rk[t][0] = k0;
-      rk[t][1] = k1;
-    }
-    const int dv = tid & (32 * G - 1), kg = tid / (32 * G);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kabs = kt0 + 16 * (kg >> 1) + 4 * (kg & 1) + (j & 3) + 8 * (j >> 2);
-      fv_t v = {};
-      if (kabs < kend) {
-        int64_t off;
-        const float *kp, *vp;
-        kv_src(kabs, dv * DV, kp, vp, off);
-        v = *reinterpret_cast<const fv_t *>(vp + off);
-      }
-      rv[j] = v;
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int t = 0; t < KPT; ++t) {
-      const int idx = tid + t * NTH * G;
-      const int key = idx >> 4, ch = idx & 15;
-      uint4 hi, lo;
-      split8(rk[t][0], rk[t][1], hi, lo);
-      Ks[0][kswz(key, ch)] = hi;
-      Ks[1][kswz(key, ch)] = lo;
-    }
-    const int dv = tid & (32 * G - 1), kg = tid / (32 * G);
-#pragma unroll
-    for (int e = 0; e < DV; ++e) {
-      const float x[8] = {rv[0][e], rv[1][e], rv[2][e], rv[3][e], rv[4][e], rv[5][e], rv[6][e], rv[7][e]};
-      uint4 hi, lo;
-      split8(make_float4(x[0], x[1], x[2], x[3]), make_float4(x[4], x[5], x[6], x[7]), hi, lo);
-      Vt[0][vswz(dv * DV + e, kg)] = hi;
-      Vt[1][vswz(dv * DV + e, kg)] = lo;
-    }
-  };
-
-  if (kbeg < kend) {
-    load(kbeg);
-    store();
-    __syncthreads();
-  }
-  for (int kt0 = kbeg; kt0 < kend; kt0 += KT) {
-    const bool more = kt0 + KT < kend;
-    if (more) load(kt0 + KT);
+  const int ntile = (kend - kbeg + KT - 1) / KT;
+  if (ntile <= 0) return;
+  att_issue<G>(kA, vA, kB, vB, loA, loB, nA, kbeg, kend, lds);
+  if (ntile > 1) att_issue<G>(kA, vA, kB, vB, loA, loB, nA, kbeg + KT, kend, lds + ATT_STAGE);
+  for (int t = 0; t < ntile; ++t) {
+    const int kt0 = kbeg + t * KT;
+    if (t + 1 < ntile)
+      att_wait_vmcnt<PERW>();  // this wave's copies of tile t landed (tile t + 1's may be in flight)
+    else
+      att_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // ... and every wave's
+    const char *st = lds + (t & 1) * ATT_STAGE;
+    const uint4 *Kh = reinterpret_cast<const uint4 *>(st), *Kl = reinterpret_cast<const uint4 *>(st + ATT_TERM);
+    const char *Vh = st + 2 * ATT_TERM, *Vl = st + 3 * ATT_TERM;
 
     // S^T for two 32-key blocks: K_hi Q_hi + K_lo Q_hi + K_hi Q_lo.
     f32x16_t sacc[2];
@@ -183,8 +145,8 @@ __global__ void __launch_bounds__(NTH * G) attn_split_kernel(AttnBatch bt) {
 #pragma unroll
       for (int s = 0; s < HD / 16; ++s) {
         const int li = kswz(b * 32 + (lane & 31), 2 * s + g4);
-        const bf16x8_t kh = __builtin_bit_cast(bf16x8_t, Ks[0][li]);
-        const bf16x8_t kl = __builtin_bit_cast(bf16x8_t, Ks[1][li]);
+        const bf16x8_t kh = __builtin_bit_cast(bf16x8_t, Kh[li]);
+        const bf16x8_t kl = __builtin_bit_cast(bf16x8_t, Kl[li]);
         sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qh[s], sacc[b], 0, 0, 0);
         sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, ql[s], sacc[b], 0, 0, 0);
         sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[s], sacc[b], 0, 0, 0);
@@ -192,7 +154,7 @@ __global__ void __launch_bounds__(NTH * G) attn_split_kernel(AttnBatch bt) {
     }
     // mask (only a partial tile or causal mode needs it), scale, running max
     float tmax = -INFINITY;
-    if (kt0 + KT > kend || a.causal) {
+    if (kt0 + KT > kend || causal) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -236,7 +198,15 @@ __global__ void __launch_bounds__(NTH * G) attn_split_kernel(AttnBatch bt) {
         for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
     }
 
-    // O^T += V^T P^T over the four 16-key steps of the tile (3 products each).
+    // O^T += V^T P^T over the four 16-key steps of the tile (3 products
+    // each).  A lane's probabilities of step (b, hh) are those of keys
+    // K0 + {0..3} and K0 + 8 + {0..3}, K0 = 32 b + 16 hh + 4 g4; its V^T
+    // fragment (hd row nb * 32 + lane % 32, the same keys) comes from two
+    // transposing reads: within each 16-lane group lane i receives element
+    // i + 16 e of the group's 16 8-byte loads, so lane L of the group loads
+    // key K0 + 8 u + L / 4 at hd c0 + 4 (L % 4) .. + 3 and lane i gets hd
+    // c0 + i of keys K0 + 8 u + {0..3}.
+    const int Lg = lane & 15;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -247,23 +217,81 @@ __global__ void __launch_bounds__(NTH * G) attn_split_kernel(AttnBatch bt) {
                ph4, pl4);
         const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, ph4);
         const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, pl4);
-        const int u = 4 * b + 2 * hh + g4;  // the lane's 8 keys of this 16-key step
+        const int K0 = b * 32 + 16 * hh + 4 * g4;
 #pragma unroll
         for (int nb = 0; nb < HD / 32; ++nb) {
-          const int hd = nb * 32 + (lane & 31);
-          const bf16x8_t vh = __builtin_bit_cast(bf16x8_t, Vt[0][vswz(hd, u)]);
-          const bf16x8_t vl = __builtin_bit_cast(bf16x8_t, Vt[1][vswz(hd, u)]);
+          const int c0 = nb * 32 + 16 * ((lane >> 4) & 1);
+          uint2 rh[2], rl[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int key = K0 + 8 * u + (Lg >> 2), hd = c0 + 4 * (Lg & 3);
+            const int addr = vswz(key, hd >> 3) * 16 + ((hd >> 2) & 1) * 8;
+            rh[u] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t *)(Vh + addr)));
+            rl[u] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t *)(Vl + addr)));
+          }
+          const bf16x8_t vh = __builtin_bit_cast(bf16x8_t, make_uint4(rh[0].x, rh[0].y, rh[1].x, rh[1].y));
+          const bf16x8_t vl = __builtin_bit_cast(bf16x8_t, make_uint4(rl[0].x, rl[0].y, rl[1].x, rl[1].y));
           oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, ph, oacc[nb], 0, 0, 0);
           oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pl, oacc[nb], 0, 0, 0);
           oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, ph, oacc[nb], 0, 0, 0);
         }
       }
-    __syncthreads();
-    if (more) {
-      store();
-      __syncthreads();
+    if (t + 2 < ntile) {
+      __builtin_amdgcn_s_barrier();  // every wave is done with this stage
+      att_issue<G>(kA, vA, kB, vB, loA, loB, nA, kt0 + 2 * KT, kend, lds + (t & 1) * ATT_STAGE);
     }
   }
+}
+
+template <int G>
+__global__ void __launch_bounds__(NTH * G) attn_split_kernel(AttnBatch bt) {
+  extern __shared__ __align__(16) char lds[];  // ATT_LDS: two stages of K and V
+  int z = blockIdx.z;
+  const AttnArgs &a = bt.c[attn_canvas(bt, z)];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), g4 = lane >> 5;
+  const int h = blockIdx.y * G + (wave >> 2);
+  const int g = h / (a.Hq / a.Hkv);
+  const int q = blockIdx.x * BQ + (wave & 3) * 32 + (lane & 31);
+  const int nk = a.nA + a.nB;
+  const int kbeg = z * a.keys_per_split;
+  const int kend = min(nk, kbeg + a.keys_per_split);
+  const float *Q = static_cast<const float *>(a.q);
+  const int64_t qhs = a.q_hstride ? a.q_hstride : (int64_t)a.nq * HD;
+
+  // This lane's query fragments (B operand of S^T = K Q^T), hi and lo.
+  bf16x8_t qh[HD / 16], ql[HD / 16];
+#pragma unroll
+  for (int s = 0; s < HD / 16; ++s) {
+    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+    if (q < a.nq) {
+      const float4 *src = reinterpret_cast<const float4 *>(Q + (int64_t)h * qhs + (int64_t)q * HD + s * 16 + g4 * 8);
+      x0 = src[0];
+      x1 = src[1];
+    }
+    uint4 hi, lo;
+    split8(x0, x1, hi, lo);
+    qh[s] = __builtin_bit_cast(bf16x8_t, hi);
+    ql[s] = __builtin_bit_cast(bf16x8_t, lo);
+  }
+  // the split fragments exist before the first DMA copy is issued, so the
+  // wait for the query loads cannot land after the copies (a wait there
+  // would also wait for the copies of both prologue tiles)
+#pragma unroll
+  for (int s = 0; s < HD / 16; ++s) asm volatile("" ::"v"(qh[s]), "v"(ql[s]));
+
+  const int qlimit = a.causal ? a.q_pos0 + q : INT32_MAX;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16_t oacc[HD / 32];
+#pragma unroll
+  for (int nb = 0; nb < HD / 32; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.f;
+  const bf16 *kA = static_cast<const bf16 *>(a.kA), *vA = static_cast<const bf16 *>(a.vA);
+  const bf16 *kB = static_cast<const bf16 *>(a.kB), *vB = static_cast<const bf16 *>(a.vB);
+  const int64_t gA = (int64_t)g * a.capA * HD, gB = (int64_t)g * a.capB * HD;
+  att_tiles<G>(kA + gA, vA + gA, kB ? kB + gB : kB, vB ? vB + gB : vB, (int64_t)a.Hkv * a.capA * HD,
+               (int64_t)a.Hkv * a.capB * HD, a.nA, kbeg, kend, qlimit, a.causal != 0, qh, ql, lds, oacc, m_run,
+               l_run);
 
   if (q < a.nq) {
     float *po = a.part_o + (((int64_t)z * a.Hq + h) * a.nq + q) * HD;
@@ -344,11 +372,21 @@ hipError_t attention_mfma_batch(const AttnBatch &bt, hipStream_t s) {
         bt.zbase[c + 1] - bt.zbase[c] != a.splits)
       return hipErrorInvalidValue;
   }
+  static std::atomic<uint64_t> attr{0};
+  if (once_per_device(attr, [] {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(attn_split_kernel<2>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, ATT_LDS);
+        if (e != hipSuccess) return e;
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(attn_split_kernel<1>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, ATT_LDS);
+      }) != hipSuccess)
+    return hipErrorInvalidValue;
   const int zt = bt.zbase[bt.B];
   if ((a0.Hq / a0.Hkv) % 2 == 0)  // pairs of query heads share their KV head's tiles
-    hipLaunchKernelGGL(attn_split_kernel<2>, dim3((a0.nq + BQ - 1) / BQ, a0.Hq / 2, zt), dim3(NTH * 2), 0, s, bt);
+    hipLaunchKernelGGL(attn_split_kernel<2>, dim3((a0.nq + BQ - 1) / BQ, a0.Hq / 2, zt), dim3(NTH * 2), ATT_LDS, s,
+                       bt);
   else
-    hipLaunchKernelGGL(attn_split_kernel<1>, dim3((a0.nq + BQ - 1) / BQ, a0.Hq, zt), dim3(NTH), 0, s, bt);
+    hipLaunchKernelGGL(attn_split_kernel<1>, dim3((a0.nq + BQ - 1) / BQ, a0.Hq, zt), dim3(NTH), ATT_LDS, s, bt);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(attn_combine_kernel<float>, dim3(a0.nq * a0.Hq, bt.B), dim3(HD), 0, s, bt);

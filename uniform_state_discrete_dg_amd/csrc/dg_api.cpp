@@ -256,6 +256,17 @@ dg::Epi epi_store(void *out, bool f32, int64_t rstride, int cdiv, int64_t chi) {
   return e;
 }
 
+// Keys or values written by their projection ([head][row][hd], head stride
+// head_stride): fp32 for DG_F32; for DG_BF16 a split pair, hi = bf16(v)
+// and lo = bf16(v - hi) `plane` elements further on, the form the attention
+// kernel copies into LDS unconverted.
+dg::Epi epi_kv(const dg_config *c, void *out, int64_t head_stride, int64_t plane) {
+  const bool bf = c->dtype == DG_BF16;
+  dg::Epi e = epi_store(out, !bf, c->head_dim, c->head_dim, head_stride);
+  if (bf) e.lo_off = plane;
+  return e;
+}
+
 bool weights_ok(const dg_config *c, const dg_weights *w) {
   if (!w || !w->w_sc1 || !w->w_sc2 || !w->wq || !w->wk || !w->wv || !w->wo || !w->g_attn || !w->g_final)
     return false;
@@ -458,14 +469,18 @@ dg_status dg_prefill_append(const dg_config *cfg, const dg_weights *w, dg_kv_cac
     DG_TRY(dg::rmsnorm_rows<float>(x, static_cast<const float *>(w->g_attn), n, d, cfg->rms_eps, nrm, nullptr,
                                    nullptr, s));
   }
-  // keys/values of the new tokens straight into the (fp32) cache at [length, length+n)
-  float *kbase = static_cast<float *>(cache->k) + (size_t)Lp * hd;
-  float *vbase = static_cast<float *>(cache->v) + (size_t)Lp * hd;
+  // keys/values of the new tokens straight into the cache at [length, length+n)
+  // (fp32, or the split pair of a bf16 model)
+  const size_t row0 = (size_t)Lp * hd;
+  void *kbase = bf ? static_cast<void *>(static_cast<bf16 *>(cache->k) + row0)
+                   : static_cast<void *>(static_cast<float *>(cache->k) + row0);
+  void *vbase = bf ? static_cast<void *>(static_cast<bf16 *>(cache->v) + row0)
+                   : static_cast<void *>(static_cast<float *>(cache->v) + row0);
   float *q = reinterpret_cast<float *>(base + L.p_q);
   const void *W[3] = {w->wk, w->wv, w->wq};
   const int No[3] = {Hkv * hd, Hkv * hd, Hq * hd};
-  const dg::Epi E3[3] = {epi_store(kbase, true, hd, hd, (int64_t)cap * hd),
-                         epi_store(vbase, true, hd, hd, (int64_t)cap * hd),
+  const int64_t plane = (int64_t)Hkv * cap * hd;
+  const dg::Epi E3[3] = {epi_kv(cfg, kbase, (int64_t)cap * hd, plane), epi_kv(cfg, vbase, (int64_t)cap * hd, plane),
                          epi_store(q, true, hd, hd, (int64_t)n * hd)};
   // K and V in one launch whether or not the prompt's attention output is
   // wanted (the split of K follows the launch's shape, so the cache's bits do
@@ -616,8 +631,9 @@ static dg_status denoise_impl(const dg_config *cfg, const dg_weights *w, const d
   {
     const void *W[3] = {w->wq, w->wk, w->wv};
     const int No[3] = {Hq * hd, Hkv * hd, Hkv * hd};
-    const dg::Epi E3[3] = {epi_store(q, true, hd, hd, (int64_t)N * hd), epi_store(kc, true, hd, hd, (int64_t)N * hd),
-                           epi_store(vc, true, hd, hd, (int64_t)N * hd)};
+    const int64_t plane = (int64_t)Hkv * N * hd;
+    const dg::Epi E3[3] = {epi_store(q, true, hd, hd, (int64_t)N * hd), epi_kv(cfg, kc, (int64_t)N * hd, plane),
+                           epi_kv(cfg, vc, (int64_t)N * hd, plane)};
     DG_TRY(proj(cfg, bf ? static_cast<const void *>(nrm_s) : nrm, N, d, 3, W, No, E3, gpart, s));
   }
   // 3. bidirectional attention over [cache || canvas], output projection
@@ -789,8 +805,8 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
     const void *W[3] = {w->wq, w->wk, w->wv};
     const int No[3] = {Hq * hd, Hkv * hd, Hkv * hd};
     const dg::Epi E3[3] = {epi_store(q, true, hd, hd, (int64_t)BN * hd),
-                           epi_store(kc, true, hd, hd, (int64_t)BN * hd),
-                           epi_store(vc, true, hd, hd, (int64_t)BN * hd)};
+                           epi_kv(cfg, kc, (int64_t)BN * hd, (int64_t)Hkv * BN * hd),
+                           epi_kv(cfg, vc, (int64_t)BN * hd, (int64_t)Hkv * BN * hd)};
     DG_TRY(proj(cfg, nrm_s, BN, d, 3, W, No, E3, gpart, s));
   }
   dg::AttnBatch ab{};  // every canvas's attention in one split launch and one merge launch
@@ -807,8 +823,8 @@ static dg_status denoise_batch_bf16(const dg_config *cfg, const dg_weights *w, c
     a.vA = caches[b].v;
     a.nA = caches[b].length;
     a.capA = caches[b].capacity;
-    a.kB = kc + (size_t)b * N * hd;
-    a.vB = vc + (size_t)b * N * hd;
+    a.kB = reinterpret_cast<bf16 *>(kc) + (size_t)b * N * hd;  // split pairs (the batch is bf16)
+    a.vB = reinterpret_cast<bf16 *>(vc) + (size_t)b * N * hd;
     a.nB = N;
     a.capB = BN;
     a.causal = 0;
