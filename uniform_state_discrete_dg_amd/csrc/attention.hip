@@ -320,15 +320,37 @@ __device__ __forceinline__ void attn_combine_body(const float *__restrict__ part
   const int qh = blockIdx.x;
   const int q = qh / Hq, h = qh % Hq;
   const int e = threadIdx.x;
+  // the ranges' (m, l) pairs and output columns, CH ranges' loads issued
+  // together; the sums run over the ranges in order, as one at a time
+  constexpr int CH = 8;
+  const int64_t zs = (int64_t)Hq * nq;
+  const float2 *ml = reinterpret_cast<const float2 *>(part_ml) + (int64_t)h * nq + q;
+  const float *po = part_o + ((int64_t)h * nq + q) * hd + (e < hd ? e : 0);
   float M = -INFINITY;
-  for (int z = 0; z < splits; ++z) M = fmaxf(M, part_ml[(((int64_t)z * Hq + h) * nq + q) * 2]);
+  for (int z0 = 0; z0 < splits; z0 += CH) {
+    float mv[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) mv[j] = z0 + j < splits ? ml[(z0 + j) * zs].x : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) M = fmaxf(M, mv[j]);
+  }
   float num = 0.f, den = 0.f;
-  for (int z = 0; z < splits; ++z) {
-    const float m = part_ml[(((int64_t)z * Hq + h) * nq + q) * 2];
-    const float l = part_ml[(((int64_t)z * Hq + h) * nq + q) * 2 + 1];
-    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-    den += w * l;
-    if (e < hd) num += w * part_o[(((int64_t)z * Hq + h) * nq + q) * hd + e];
+  for (int z0 = 0; z0 < splits; z0 += CH) {
+    float2 mlv[CH];
+    float ov[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const bool in = z0 + j < splits;
+      mlv[j] = in ? ml[(z0 + j) * zs] : make_float2(-INFINITY, 0.f);
+      ov[j] = in ? po[(z0 + j) * zs * hd] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (z0 + j >= splits) break;
+      const float w = (mlv[j].x == -INFINITY) ? 0.f : exp2f(mlv[j].x - M);
+      den += w * mlv[j].y;
+      num += w * ov[j];
+    }
   }
   if (e < hd) {
     const int64_t i = (int64_t)q * Hq * hd + (int64_t)h * hd + e;
