@@ -56,18 +56,20 @@ __device__ __forceinline__ void epi_store(const Epi &e, int row, int col, float 
 // At a 256-row canvas these contractions are small (M = 256, N and K a few
 // thousand), so the work is cut into 64 x 128 output tiles and, along K,
 // into ranges of about 1408 (a 256 x 2816 x 2816 product: 88 tiles x 2
-// ranges = 176 workgroups).  Each workgroup
-// (4 waves, wave tile 32 rows x 64 columns) streams its A rows (both bf16
-// terms) and B rows (bf16) through a 4-stage LDS ring fed by the DMA form of
-// the vector load, 32 k per slice, three slices ahead of the MFMAs.  The
-// MFMA takes the weight fragment first, so a lane's accumulators are one
-// output row and runs of four consecutive output columns.
+// ranges = 176 workgroups).  Each workgroup (8 waves, 2 x 4, wave tile 32 x
+// 32: two waves per SIMD, so one's MFMAs run while the other waits on LDS
+// or the barrier) streams its A rows (both bf16 terms) and B rows (bf16)
+// through a 4-stage LDS ring fed by the DMA form of the vector load, 32 k
+// per slice, three slices ahead of the MFMAs.  The MFMA takes the weight
+// fragment first, so a lane's accumulators are one output row and runs of
+// four consecutive output columns.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int PG_NT = 256;
 constexpr int PG_BK = 32;
-// default tile: rows x columns per workgroup, LDS stages
+// default tile: rows x columns per workgroup, LDS stages; waves as a
+// PG_WM x PG_WN grid over the tile
 constexpr int PG_BM = 64, PG_BN = 128, PG_STAGES = 4;
+constexpr int PG_WM = 2, PG_WN = 4, PG_NT = 64 * PG_WM * PG_WN;
 
 template <int n>
 __device__ __forceinline__ void pg_wait_vmcnt() {
@@ -84,16 +86,19 @@ struct PgCfg {
   static constexpr int BSLICE = BN * PG_BK * 2;  // bf16 B slice
   static constexpr int STAGE = ASLICE + BSLICE;
   static constexpr int LDS = STAGES * STAGE;
-  static constexpr int UA = BM / 32, UB = BN / 64;  // DMA instructions per wave per slice
+  static constexpr int NW = PG_WM * PG_WN;
+  static constexpr int UA = BM / 8 / NW, UB = BN / 16 / NW;  // DMA instructions per wave per slice
   static constexpr int PER = UA + UB;
-  static constexpr int FM = BM / 64, FN = BN / 64;  // 32-wide fragments per wave (2 x 2 waves)
-  static_assert(BM % 64 == 0 && BN % 64 == 0 && STAGES >= 3, "tile");
+  static constexpr int TM = BM / PG_WM, TN = BN / PG_WN;  // wave tile
+  static constexpr int FM = TM / 32, FN = TN / 32;         // 32-wide fragments per wave
+  static_assert(UA >= 1 && UB >= 1 && UA * NW * 8 == BM && UB * NW * 16 == BN && STAGES >= 3, "tile");
+  static_assert(FM >= 1 && FN >= 1 && FM * 32 == TM && FN * 32 == TN, "wave tile");
   static_assert((STAGES - 2) * PER < 64, "vmcnt range");
 };
 }  // namespace
 
-// Accumulates acc[i][j] (wave tile rows wm*BM/2 + 32 i + [0, 32), columns
-// wn*BN/2 + 32 j + [0, 32)) over the slices [sb, sb + nk) of K.  The
+// Accumulates acc[i][j] (wave tile rows wm*TM + 32 i + [0, 32), columns
+// wn*TN + 32 j + [0, 32)) over the slices [sb, sb + nk) of K.  The
 // operands come in as restrict-qualified parameters: that tells the
 // compiler the LDS reads do not depend on the DMA copies in flight (the
 // s_waitcnt / s_barrier pair before each slice orders them), so it adds no
@@ -101,10 +106,10 @@ struct PgCfg {
 template <int BM, int BN, int STAGES>
 __device__ __forceinline__ void pg_tile(const bf16 *__restrict__ A, int64_t lda, int64_t lo_off, int M, int m0,
                                         const bf16 *__restrict__ B, int K, int N, int n0, int sb, int nk, char *lds,
-                                        f32x16_t (&acc)[BM / 64][BN / 64]) {
+                                        f32x16_t (&acc)[PgCfg<BM, BN, STAGES>::FM][PgCfg<BM, BN, STAGES>::FN]) {
   using C = PgCfg<BM, BN, STAGES>;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, gq = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / PG_WN, wn = wave % PG_WN, r32 = lane & 31, gq = lane >> 5;
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -158,14 +163,14 @@ __device__ __forceinline__ void pg_tile(const bf16 *__restrict__ A, int64_t lda,
       bf16x8_t fh[C::FM], fl[C::FM];
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
-        const int arow = wm * (BM / 2) + 32 * i + r32;
+        const int arow = wm * C::TM + 32 * i + r32;
         fh[i] = __builtin_bit_cast(bf16x8_t, sa[b_slot(arow, 2 * kk + gq)]);
         fl[i] = __builtin_bit_cast(bf16x8_t, sa[BM * 4 + b_slot(arow, 2 * kk + gq)]);
       }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
         const bf16x8_t fb =
-            __builtin_bit_cast(bf16x8_t, sbq[b_slot(wn * (BN / 2) + 32 * j + r32, 2 * kk + gq)]);
+            __builtin_bit_cast(bf16x8_t, sbq[b_slot(wn * C::TN + 32 * j + r32, 2 * kk + gq)]);
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fl[i], acc[i][j], 0, 0, 0);
@@ -204,22 +209,22 @@ __global__ void __launch_bounds__(PG_NT) gemm_split_kernel(SplitGemm g) {
   }
   const int N = g.N[seg], n0 = p * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, r32 = lane & 31, gq = lane >> 5;
+  const int wm = wave / PG_WN, wn = wave % PG_WN, r32 = lane & 31, gq = lane >> 5;
   const int nsl = K / PG_BK;
   const int sb = (int)((int64_t)nsl * kc / g.ksplit), se = (int)((int64_t)nsl * (kc + 1) / g.ksplit);
   f32x16_t acc[C::FM][C::FN];
   pg_tile<BM, BN, STAGES>(g.A, g.lda, g.lo_off, M, m0, static_cast<const bf16 *>(g.B[seg]), K, N, n0, sb, se - sb, lds,
                           acc);
 
-  // lane: output rows m0 + wm*BM/2 + 32 i + r32; register r of fragment j is
-  // column n0 + wn*BN/2 + 32 j + 8 (r >> 2) + 4 gq + (r & 3)
+  // lane: output rows m0 + wm*TM + 32 i + r32; register r of fragment j is
+  // column n0 + wn*TN + 32 j + 8 (r >> 2) + 4 gq + (r & 3)
   size_t base = 0;
   if (g.ksplit > 1)
     for (int t = 0; t < seg; ++t) base += (size_t)g.ksplit * M * g.N[t];
   const Epi e = g.e[seg];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
-    const int row = m0 + wm * (BM / 2) + 32 * i + r32;
+    const int row = m0 + wm * C::TM + 32 * i + r32;
     if (row >= M) continue;
     if (g.ksplit > 1) {
       float *out = g.part + base + ((size_t)kc * M + row) * N;
@@ -227,7 +232,7 @@ __global__ void __launch_bounds__(PG_NT) gemm_split_kernel(SplitGemm g) {
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * (BN / 2) + 32 * j + 8 * q + 4 * gq;
+          const int col = n0 + wn * C::TN + 32 * j + 8 * q + 4 * gq;
           if (col < N)
             *reinterpret_cast<float4 *>(out + col) =
                 make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
@@ -237,7 +242,7 @@ __global__ void __launch_bounds__(PG_NT) gemm_split_kernel(SplitGemm g) {
       for (int j = 0; j < C::FN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int col = n0 + wn * (BN / 2) + 32 * j + 8 * (r >> 2) + 4 * gq + (r & 3);
+          const int col = n0 + wn * C::TN + 32 * j + 8 * (r >> 2) + 4 * gq + (r & 3);
           if (col < N) epi_store(e, row, col, acc[i][j][r]);
         }
     }
