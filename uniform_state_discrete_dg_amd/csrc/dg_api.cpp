@@ -129,10 +129,12 @@ struct Layout {
 // Activations are fp32 in the workspace for both dtypes; the bf16 path also
 // keeps each projection operand as a split pair (hi and lo bf16 terms, the
 // lo array after the hi array, 4 bytes per value: nrm_s, sc_s, o_s, and g,
-// which holds only that form there); nrm16 is the bf16 copy of the final
-// normalised state used by the LM head.  nb > 1: a batch of nb canvases,
-// whose rows are stacked (N = nb * canvas_len rows) in every activation; the
-// attention partials serve one canvas at a time; tok holds the stacked ids.
+// which holds only that form there) and the canvas keys and values kc / vc
+// only as split pairs ([Hkv][N][hd] hi terms, then the lo terms); nrm16 is
+// the bf16 copy of the final normalised state used by the LM head.  nb > 1:
+// a batch of nb canvases, whose rows are stacked (N = nb * canvas_len rows)
+// in every activation; the attention partials serve one canvas at a time;
+// tok holds the stacked ids.
 Layout layout(const dg_config *c, int32_t nprefill, bool with_logits, int nb = 1) {
   Layout L{};
   const size_t N = (size_t)nb * c->canvas_len, V = c->vocab, d = c->d_model, F = c->ffn_hidden;
