@@ -59,6 +59,15 @@ constexpr float LN2 = 0.6931471805599453f;
 // two of its workgroups share a CU.  The LM head stages its numerators
 // (8 slices of NW * 2 KB) and statistics (32 NW rows x 64 bytes) in the
 // same memory afterwards.
+// A 16-byte store written through the L2 (system scope, sc0 sc1): the line
+// is not left dirty in this XCD's L2 for the write-back at the kernel's end,
+// which the next kernel would wait for.  The s_nop keeps the store's data
+// registers from being rewritten in the cycle after it issues.
+typedef int es_v4i_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_through(void *p, es_v4i_t v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1\n\ts_nop 1" ::"v"(p), "v"(v));
+}
+
 constexpr int es_abytes(int NW) { return NW * 2048; }
 constexpr int es_stage_bytes(int NW) { return es_abytes(NW) + ES_SLICE; }
 constexpr int es_lds(int NW, int STG) { return STG * (es_stage_bytes(NW) + 256 + 32); }
@@ -551,9 +560,11 @@ __global__ void __launch_bounds__(NW * 64, NW == 8 ? 1 : 2)
     const int c = BATCH ? grow / N : 0, lrow = grow - c * N;
     char *dst = reinterpret_cast<char *>(cv.probs[c]) + (int64_t)(n0 / 32) * ES_SLICE + lrow * 64 + u4 * 16;
     const char *src = stage_num + row * 64 + u4 * 16;
+    es_v4i_t v[8];
 #pragma unroll
-    for (int ls = 0; ls < 8; ++ls)
-      *reinterpret_cast<uint4 *>(dst + ls * ES_SLICE) = *reinterpret_cast<const uint4 *>(src + ls * AB);
+    for (int ls = 0; ls < 8; ++ls) v[ls] = *reinterpret_cast<const es_v4i_t *>(src + ls * AB);
+#pragma unroll
+    for (int ls = 0; ls < 8; ++ls) store_through(dst + ls * ES_SLICE, v[ls]);
     reinterpret_cast<uint4 *>(cv.tile_stats[c] + (int64_t)lrow * ntiles + n0 / 64)[u4] =
         *reinterpret_cast<const uint4 *>(stage_st + row * 64 + (u4 ^ ((row >> 2) & 3)) * 16);
   }
@@ -685,8 +696,9 @@ __global__ void __launch_bounds__(MODE == 3 ? ES_NT / 2 : ES_NT, 1)
         const int qc = TF == TF_FP4 ? ((q & 1) << 1) | (q >> 1) : q;
         const int col = n0 + wn * 128 + j * 32 + 8 * qc + 4 * (lane >> 5);
         if (col < N)
-          *reinterpret_cast<float4 *>(out + (((((wave * 2 + i) * 4 + j) * 4 + qc) * 64 + lane) << 2)) =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          store_through(out + (((((wave * 2 + i) * 4 + j) * 4 + qc) * 64 + lane) << 2),
+                        es_v4i_t{__float_as_int(acc[i][j][4 * q]), __float_as_int(acc[i][j][4 * q + 1]),
+                                 __float_as_int(acc[i][j][4 * q + 2]), __float_as_int(acc[i][j][4 * q + 3])});
       }
   }
 }
